@@ -1,0 +1,45 @@
+"""CPU oracle for the QLoRA frozen-base linear layer -- TEST INFRASTRUCTURE ONLY.
+
+This package is the plain, slow, obviously-correct reference that the HIP
+library is checked against.  Only the test suite, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import it.  The product path
+(the C-ABI library and its Python binding) never imports, links or calls
+anything here, and this package imports nothing from the product.
+
+What it computes (numpy, fp64 unless a step fixes another precision):
+
+* ``nf4``   -- the 16 NF4 levels and their decision thresholds, the blockwise
+  absmax quantiser (blocks of 64, two 4-bit codes per byte), the 8-bit
+  double quantisation of the block scales (groups of 256) and the bit-exact
+  dequantisation to bf16.
+* ``lora_linear`` -- the layer y = x.W'^T + (alpha/r).(x.A^T).B^T and its
+  gradients dX, dA, dB on the decoded weight W'.
+
+Sources are cited by page title and section.  The pages state the format in
+words only; every reading taken where they are silent is written at the
+function that takes it.
+
+Parity status: every function here is pinned by a CPU test in ``tests/``
+against something other than itself (closed forms, brute force on tiny
+inputs, library routines for special cases, adjoint identities, the pages'
+storage figures).  The exact numeric values of the NF4 levels are fixed by
+the construction reading, not by a table on the pages.
+"""
+
+from .nf4 import (  # noqa: F401
+    P_MAX,
+    BLOCK,
+    GROUP,
+    nf4_levels_f64,
+    nf4_levels_f32,
+    nf4_thresholds_f32,
+    bf16_rne_bits,
+    bf16_bits_to_f64,
+    quantize_nf4,
+    unpack_codes,
+    double_quant,
+    dequant_scales,
+    dequant_nf4_bits,
+    storage_bits_per_weight,
+)
+from .lora_linear import lora_linear_fwd, lora_linear_bwd, lora_scale  # noqa: F401
