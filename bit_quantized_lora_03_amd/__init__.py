@@ -1,0 +1,27 @@
+"""QLoRA frozen-base linear layer for MI355X (gfx950).
+
+The base weight is stored as packed 4-bit NF4 codes with double-quantised
+block scales and is dequantised to bf16 tile by tile inside hand-written
+HIP GEMMs; the LoRA path y += (alpha/r).(x.A^T).B^T rides on the same
+MFMA accumulators.  The work sits behind the C ABI in include/qlora.h
+(``libqlora.so``); this package is its thin Python binding plus the seeded
+synthetic input generators.
+"""
+
+from . import workloads  # noqa: F401
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    Nf4Weight,
+    PackedWeight,
+    QloraError,
+    dequantize,
+    double_quant,
+    lib,
+    linear_bwd,
+    linear_fwd,
+    nf4_levels,
+    quantize_nf4,
+    quantize_weight,
+    workspace_bytes,
+)

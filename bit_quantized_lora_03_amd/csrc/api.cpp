@@ -1,0 +1,324 @@
+// C ABI of the QLoRA linear layer: argument validation, workspace layout and
+// kernel dispatch.  Every argument is checked before the first HIP call, so
+// invalid calls return a status without touching the GPU.  No C++
+// exception crosses the ABI.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/qlora.h"
+#include "launch.h"
+#include "nf4_table.h"
+
+namespace {
+
+using qlora::Nf4Levels;
+using qlora::Nf4Thresholds;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges; empty ranges never overlap)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+Nf4Levels levels_arg() {
+  Nf4Levels L;
+  std::memcpy(L.v, qlora::nf4_table().level, sizeof(L.v));
+  return L;
+}
+Nf4Thresholds thresholds_arg() {
+  Nf4Thresholds T;
+  std::memcpy(T.t, qlora::nf4_table().threshold, sizeof(T.t));
+  return T;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Validate the packed-weight descriptor for a GEMM of the given M.
+int check_weight(const qlora_nf4_weight* w) {
+  if (!w || !w->codes || !w->qscale || !w->dq_step) return QLORA_EINVAL;
+  if (w->N <= 0 || w->K <= 0) return QLORA_EINVAL;
+  if (w->N % 64 || w->K % 64) return QLORA_ESHAPE;
+  if (!aligned16(w->codes) || !aligned16(w->qscale) || !aligned16(w->dq_step)) return QLORA_EALIGN;
+  return QLORA_OK;
+}
+
+int check_rank(int32_t r) {
+  if (r < 0) return QLORA_EINVAL;
+  if (r > QLORA_MAX_RANK || r % 8) return QLORA_ESHAPE;
+  return QLORA_OK;
+}
+
+// ---- workspace layout --------------------------------------------------
+struct FwdWs {
+  size_t p_off, xs_off, total;
+  int splits;
+};
+FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+  (void)N;
+  FwdWs L{};
+  if (r == 0 || M == 0) return L;
+  L.splits = qlora::lora_down_splits(M, K, r);
+  L.p_off = 0;
+  L.xs_off = round_up(L.p_off + (size_t)L.splits * M * r * sizeof(float), 256);
+  L.total = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+  return L;
+}
+
+struct BwdWs {
+  size_t pa_off, bt_off, pg_off, xs_off, gs_off, total;
+  int splits_a, splits_g;
+};
+BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+  BwdWs L{};
+  if (r == 0 || M == 0) return L;
+  L.splits_a = qlora::lora_down_splits(M, K, r);
+  L.splits_g = qlora::lora_down_splits(M, N, r);
+  L.pa_off = 0;
+  L.bt_off = round_up(L.pa_off + (size_t)L.splits_a * M * r * sizeof(float), 256);
+  L.pg_off = round_up(L.bt_off + (size_t)r * N * sizeof(uint16_t), 256);
+  L.xs_off = round_up(L.pg_off + (size_t)L.splits_g * M * r * sizeof(float), 256);
+  L.gs_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+  L.total = round_up(L.gs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+  return L;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_EINVAL: return "invalid argument (null pointer, negative size or aliasing)";
+    case QLORA_ESHAPE: return "unsupported shape (N, K must be multiples of 64; r a multiple of 8 <= 256)";
+    case QLORA_EALIGN: return "device pointer not 16-byte aligned";
+    case QLORA_ENOTSUP: return "unsupported block size (64 / 256 only)";
+    case QLORA_EWORKSPACE: return "workspace missing or too small";
+    case QLORA_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int qlora_nf4_levels(float* levels, float* thresholds) {
+  try {
+    const qlora::Nf4Table& t = qlora::nf4_table();
+    if (levels) std::memcpy(levels, t.level, sizeof(t.level));
+    if (thresholds) std::memcpy(thresholds, t.threshold, sizeof(t.threshold));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_EINVAL;
+  }
+}
+
+size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64 || check_rank(r) != QLORA_OK) return 0;
+  if (op == 0) return fwd_layout(M, N, K, r).total;
+  if (op == 1) return bwd_layout(M, N, K, r).total;
+  return 0;
+}
+
+int qlora_quantize_nf4(const float* w, int64_t n_elems, int32_t blocksize, uint8_t* codes,
+                       float* absmax, void* stream) {
+  try {
+    if (n_elems < 0) return QLORA_EINVAL;
+    if (blocksize != QLORA_BLOCK) return QLORA_ENOTSUP;
+    if (n_elems == 0) return QLORA_OK;
+    if (!w || !codes || !absmax) return QLORA_EINVAL;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax)) return QLORA_EALIGN;
+    const size_t nw = (size_t)n_elems * 4, nc = (size_t)(n_elems + 1) / 2,
+                 na = (size_t)((n_elems + 63) / 64) * 4;
+    if (overlap(w, nw, codes, nc) || overlap(w, nw, absmax, na) || overlap(codes, nc, absmax, na))
+      return QLORA_EINVAL;
+    return hip_status(qlora::launch_quantize(w, n_elems, codes, absmax, thresholds_arg(),
+                                             as_stream(stream)));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
+int qlora_double_quant(const float* absmax, int64_t n_blocks, int32_t blocksize2,
+                       uint8_t* qscale, float* dq_step, void* stream) {
+  try {
+    if (n_blocks < 0) return QLORA_EINVAL;
+    if (blocksize2 != QLORA_GROUP) return QLORA_ENOTSUP;
+    if (n_blocks == 0) return QLORA_OK;
+    if (!absmax || !qscale || !dq_step) return QLORA_EINVAL;
+    if (!aligned16(absmax) || !aligned16(qscale) || !aligned16(dq_step)) return QLORA_EALIGN;
+    const size_t na = (size_t)n_blocks * 4, nq = (size_t)n_blocks,
+                 ns = (size_t)((n_blocks + 255) / 256) * 4;
+    if (overlap(absmax, na, qscale, nq) || overlap(absmax, na, dq_step, ns) ||
+        overlap(qscale, nq, dq_step, ns))
+      return QLORA_EINVAL;
+    return hip_status(qlora::launch_double_quant(absmax, n_blocks, qscale, dq_step,
+                                                 as_stream(stream)));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
+int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream) {
+  try {
+    if (!w || !w->codes || !w->qscale || !w->dq_step || !out) return QLORA_EINVAL;
+    if (w->N <= 0 || w->K <= 0) return QLORA_EINVAL;
+    const int64_t n = w->N * w->K;
+    if (n % 64) return QLORA_ESHAPE;
+    if (!aligned16(w->codes) || !aligned16(w->qscale) || !aligned16(w->dq_step) ||
+        !aligned16(out))
+      return QLORA_EALIGN;
+    const size_t no = (size_t)n * 2;
+    if (overlap(out, no, w->codes, (size_t)n / 2) || overlap(out, no, w->qscale, (size_t)n / 64))
+      return QLORA_EINVAL;
+    return hip_status(qlora::launch_dequant(w->codes, w->qscale, w->dq_step, n / 64, out,
+                                            levels_arg(), as_stream(stream)));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
+int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha, uint16_t* y, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  try {
+    int st = check_weight(w);
+    if (st != QLORA_OK) return st;
+    if ((st = check_rank(r)) != QLORA_OK) return st;
+    if (M < 0) return QLORA_EINVAL;
+    const int64_t N = w->N, K = w->K;
+    if (M == 0) return QLORA_OK;
+    if (!x || !y) return QLORA_EINVAL;
+    if (r > 0 && (!A || !B)) return QLORA_EINVAL;
+    if (!aligned16(x) || !aligned16(y) || (r > 0 && (!aligned16(A) || !aligned16(B))))
+      return QLORA_EALIGN;
+    const FwdWs ws = fwd_layout(M, N, K, r);
+    if (ws.total > 0) {
+      if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
+    }
+    const size_t ny = (size_t)M * N * 2;
+    if (overlap(y, ny, x, (size_t)M * K * 2) || overlap(y, ny, w->codes, (size_t)N * K / 2) ||
+        (r > 0 && (overlap(y, ny, A, (size_t)r * K * 2) || overlap(y, ny, B, (size_t)N * r * 2))) ||
+        (ws.total > 0 && overlap(y, ny, workspace, ws.total)))
+      return QLORA_EINVAL;
+
+    hipStream_t s = as_stream(stream);
+    const Nf4Levels L = levels_arg();
+    uint16_t* xs = nullptr;
+    if (r > 0) {
+      float* P = at<float>(workspace, ws.p_off);
+      xs = at<uint16_t>(workspace, ws.xs_off);
+      if ((st = hip_status(qlora::launch_lora_down(x, A, M, K, r, ws.splits, P, s))) != QLORA_OK)
+        return st;
+      const float scale = alpha / static_cast<float>(r);
+      if ((st = hip_status(qlora::launch_lora_split(P, ws.splits, M, r, scale, xs, s))) != QLORA_OK)
+        return st;
+    }
+    return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->dq_step, x, xs, B, y, M, N,
+                                             K, r, L, s));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* dx,
+                     float* dA, float* dB, int32_t accumulate, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  try {
+    int st = check_weight(w);
+    if (st != QLORA_OK) return st;
+    if ((st = check_rank(r)) != QLORA_OK) return st;
+    if (M < 0) return QLORA_EINVAL;
+    const int64_t N = w->N, K = w->K;
+    if (M == 0) {
+      // a sum over no tokens: dA = dB = 0 (or unchanged when accumulating)
+      if (r == 0) return QLORA_OK;
+      if (!dA || !dB) return QLORA_EINVAL;
+      if (!aligned16(dA) || !aligned16(dB)) return QLORA_EALIGN;
+      if (overlap(dA, (size_t)r * K * 4, dB, (size_t)N * r * 4)) return QLORA_EINVAL;
+      hipStream_t s0 = as_stream(stream);
+      if ((st = hip_status(qlora::launch_tn_gemm(nullptr, nullptr, N, nullptr, nullptr, r, 0, N,
+                                                 r, dB, accumulate, s0))) != QLORA_OK)
+        return st;
+      return hip_status(qlora::launch_tn_gemm(nullptr, nullptr, r, nullptr, nullptr, K, 0, r, K,
+                                              dA, accumulate, s0));
+    }
+    if (!dy) return QLORA_EINVAL;
+    if (r > 0 && (!A || !B || !x || !dA || !dB)) return QLORA_EINVAL;
+    if (!aligned16(dy) || (dx && !aligned16(dx)) ||
+        (r > 0 && (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
+                   !aligned16(dB))))
+      return QLORA_EALIGN;
+    const BwdWs ws = bwd_layout(M, N, K, r);
+    if (ws.total > 0) {
+      if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
+    }
+    // outputs must not overlap inputs, the workspace or each other
+    const size_t nxb = (size_t)M * K * 2, nyb = (size_t)M * N * 2, nab = (size_t)r * K * 4,
+                 nbb = (size_t)N * r * 4;
+    const void* ins[] = {x, dy, A, B, w->codes, workspace};
+    const size_t in_sz[] = {nxb, nyb, (size_t)r * K * 2, (size_t)N * r * 2, (size_t)N * K / 2,
+                            ws.total};
+    void* outs[] = {dx, r > 0 ? dA : nullptr, r > 0 ? dB : nullptr};
+    const size_t out_sz[] = {nxb, nab, nbb};
+    for (int o = 0; o < 3; ++o) {
+      for (int i = 0; i < 6; ++i)
+        if (overlap(outs[o], out_sz[o], ins[i], in_sz[i])) return QLORA_EINVAL;
+      for (int o2 = o + 1; o2 < 3; ++o2)
+        if (overlap(outs[o], out_sz[o], outs[o2], out_sz[o2])) return QLORA_EINVAL;
+    }
+    hipStream_t s = as_stream(stream);
+
+    const Nf4Levels L = levels_arg();
+    uint16_t* gs = nullptr;
+    if (r > 0) {
+      float* Pa = at<float>(workspace, ws.pa_off);
+      uint16_t* Bt = at<uint16_t>(workspace, ws.bt_off);
+      float* Pg = at<float>(workspace, ws.pg_off);
+      uint16_t* xs = at<uint16_t>(workspace, ws.xs_off);
+      gs = at<uint16_t>(workspace, ws.gs_off);
+      const float scale = alpha / static_cast<float>(r);
+      if ((st = hip_status(qlora::launch_lora_down(x, A, M, K, r, ws.splits_a, Pa, s))) != QLORA_OK)
+        return st;
+      if ((st = hip_status(qlora::launch_transpose_bf16(B, N, r, Bt, s))) != QLORA_OK) return st;
+      if ((st = hip_status(qlora::launch_lora_down(dy, Bt, M, N, r, ws.splits_g, Pg, s))) != QLORA_OK)
+        return st;
+      if ((st = hip_status(qlora::launch_lora_split(Pa, ws.splits_a, M, r, scale, xs, s))) != QLORA_OK)
+        return st;
+      if ((st = hip_status(qlora::launch_lora_split(Pg, ws.splits_g, M, r, scale, gs, s))) != QLORA_OK)
+        return st;
+      // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x
+      if ((st = hip_status(qlora::launch_tn_gemm(dy, dy, N, xs, xs + r, 2 * r, M, N, r, dB,
+                                                 accumulate, s))) != QLORA_OK)
+        return st;
+      if ((st = hip_status(qlora::launch_tn_gemm(gs, gs + r, 2 * r, x, x, K, M, r, K, dA,
+                                                 accumulate, s))) != QLORA_OK)
+        return st;
+    }
+    if (dx) {
+      if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->dq_step, dy, gs, A, dx,
+                                                 M, N, K, r, L, s))) != QLORA_OK)
+        return st;
+    }
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16 packing,
+// byte permutes, and the NF4 decode (a per-block 16-entry bf16 table looked
+// up with v_perm_b32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// The 16 fp32 NF4 levels, passed to kernels by value (lands in SGPRs).
+struct Nf4Levels {
+  float v[16];
+};
+struct Nf4Thresholds {
+  float t[15];
+};
+
+// v_perm_b32: result byte i = byte sel.byte[i] of the 8-byte value
+// {hi:lo}; selector 0..3 picks lo's bytes, 4..7 hi's bytes, 12 gives 0x00
+// and 13..15 give 0xFF.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Two fp32 -> packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// ---------------------------------------------------------------------------
+// NF4 decode.  A block's 16 decoded values e[c] = bf16_rne(fp32(L[c] * s'))
+// are held as two 16-byte planes: lo[j] holds the low bytes of entries
+// 4j..4j+3, hi[j] their high bytes.  One v_perm picks 4 bytes out of 8, so
+// a 4-bit code is resolved with one perm into entries 0..7, one into 8..15,
+// and a third perm that keeps the right one (chosen by the code's bit 3).
+// ---------------------------------------------------------------------------
+struct Nf4Lut {
+  uint32_t lo[4];
+  uint32_t hi[4];
+};
+
+__device__ __forceinline__ Nf4Lut nf4_make_lut(const Nf4Levels& L, float scale) {
+  uint32_t p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // one fp32 product per level, then round-to-nearest-even to bf16
+    const float a = L.v[2 * i] * scale;
+    const float b = L.v[2 * i + 1] * scale;
+    p[i] = pack_bf16x2(a, b);
+  }
+  Nf4Lut t;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t.lo[j] = perm(p[2 * j + 1], p[2 * j], 0x06040200u);
+    t.hi[j] = perm(p[2 * j + 1], p[2 * j], 0x07050301u);
+  }
+  return t;
+}
+
+// 4 codes, one per byte (values 0..15) -> two bf16 pairs, in byte order.
+__device__ __forceinline__ void nf4_lookup4(const Nf4Lut& t, uint32_t n,
+                                            uint32_t& o01, uint32_t& o23) {
+  const uint32_t n_hi = n & 0x07070707u;                          // index in 8..15
+  const uint32_t pick = ((n >> 1) & 0x04040404u) | 0x03020100u;   // j or j+4
+  const uint32_t lo = perm(perm(t.lo[3], t.lo[2], n_hi), perm(t.lo[1], t.lo[0], n), pick);
+  const uint32_t hi = perm(perm(t.hi[3], t.hi[2], n_hi), perm(t.hi[1], t.hi[0], n), pick);
+  o01 = perm(hi, lo, 0x05010400u);
+  o23 = perm(hi, lo, 0x07030602u);
+}
+
+// 8 packed codes (byte j = c[2j] | c[2j+1] << 4) -> 8 bf16 in element order
+// as four pairs: out[i] = e[c(2i)] | e[c(2i+1)] << 16.
+__device__ __forceinline__ u32x4_t nf4_decode8(const Nf4Lut& t, uint32_t v) {
+  const uint32_t ev = v & 0x0F0F0F0Fu;          // c0 c2 c4 c6
+  const uint32_t od = (v >> 4) & 0x0F0F0F0Fu;   // c1 c3 c5 c7
+  const uint32_t n0 = perm(od, ev, 0x05010400u);  // c0 c1 c2 c3
+  const uint32_t n1 = perm(od, ev, 0x07030602u);  // c4 c5 c6 c7
+  uint32_t o0, o1, o2, o3;
+  nf4_lookup4(t, n0, o0, o1);
+  nf4_lookup4(t, n1, o2, o3);
+  const u32x4_t out = {o0, o1, o2, o3};
+  return out;
+}
+
+// Decoded block scale s' = fp32(q * step): q (0..255) converts exactly and
+// the single fp32 product is rounded once.
+__device__ __forceinline__ float nf4_block_scale(uint32_t q, float step) {
+  return static_cast<float>(q) * step;
+}
+
+// MFMA wrappers (gfx950 bf16, fp32 accumulate).
+__device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+}  // namespace qlora

@@ -1,0 +1,168 @@
+// NF4 blockwise quantiser, 8-bit double quantisation of the block scales,
+// and the standalone dequantiser (gfx950).
+//
+// [QLoRA / infivelines.com]: 16 NF4 levels at normal quantiles; one scale
+// per block of 64 weights; the block scales quantised again in blocks of
+// 256.  [QLoRA -- Module 12.4, "Design Details That Matter"]: NF4 and double
+// quant.  The arithmetic of every step is fixed so that results are
+// reproducible bit for bit: IEEE correctly rounded fp32 division, a
+// round-half-even rint, one fp32 product per decoded value and a
+// round-to-nearest-even bf16 conversion.  These kernels are HBM-bound
+// streaming passes: every lane owns whole contiguous pieces so that loads
+// and stores are wide and coalesced.
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace qlora {
+
+// ---------------------------------------------------------------------------
+// Quantiser: each lane owns 8 consecutive weights (two 16-byte loads), so 8
+// lanes cover one 64-weight block and a wave covers 8 blocks.  The block's
+// absmax is a max over the 8 lanes (xor shuffles inside the 8-lane group).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(
+    const float* __restrict__ w, int64_t n, uint8_t* __restrict__ codes,
+    float* __restrict__ absmax, Nf4Thresholds T) {
+  const int64_t lanes_total = (n + 7) >> 3;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+       g - (threadIdx.x & 7) < lanes_total;  // whole 8-lane groups iterate together
+       g += stride) {
+    const int64_t e0 = g << 3;
+    float v[8];
+    if (e0 + 8 <= n) {
+      const float4* p = reinterpret_cast<const float4*>(w + e0);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (e0 + i < n) ? w[e0 + i] : 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 8));
+    m = fmaxf(m, __shfl_xor(m, 2, 8));
+    m = fmaxf(m, __shfl_xor(m, 4, 8));
+
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t c = 7;
+      if (m > 0.0f && e0 + i < n) {
+        const float u = __fdiv_rn(v[i], m);  // IEEE correctly rounded
+        c = 0;
+#pragma unroll
+        for (int k = 0; k < 15; ++k) c += (u > T.t[k]) ? 1u : 0u;
+      }
+      packed |= c << (4 * i);
+    }
+    if (e0 < n) {
+      if (e0 + 8 <= n) {
+        *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = packed;
+      } else {
+        const int64_t nbytes = (n + 1) >> 1;
+        for (int i = 0; i < 4; ++i)
+          if ((e0 >> 1) + i < nbytes) codes[(e0 >> 1) + i] = (uint8_t)(packed >> (8 * i));
+      }
+      if ((threadIdx.x & 7) == 0) absmax[e0 >> 6] = m;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Double quantisation: one wave per group of 256 scales, 4 scales per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void double_quant_kernel(
+    const float* __restrict__ absmax, int64_t nb, uint8_t* __restrict__ qscale,
+    float* __restrict__ step_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t groups = (nb + 255) >> 8;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t wstride = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t gidx = wave0; gidx < groups; gidx += wstride) {
+    const int64_t b0 = (gidx << 8) + 4 * lane;
+    float s[4];
+    if (b0 + 4 <= nb) {
+      const float4 a = *reinterpret_cast<const float4*>(absmax + b0);
+      s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (b0 + i < nb) ? absmax[b0 + i] : 0.0f;
+    }
+    float m = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float st = __fdiv_rn(m, 255.0f);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t q = 0;
+      if (st > 0.0f) q = (uint32_t)fminf(rintf(__fdiv_rn(s[i], st)), 255.0f);
+      packed |= q << (8 * i);
+    }
+    if (b0 + 4 <= nb) {
+      *reinterpret_cast<uint32_t*>(qscale + b0) = packed;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (b0 + i < nb) qscale[b0 + i] = (uint8_t)(packed >> (8 * i));
+    }
+    if (lane == 0) step_out[gidx] = st;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Standalone dequantiser: one lane per 64-weight block (the decode routine
+// the GEMMs run on their tiles), 32 code bytes in, 128 bf16 bytes out.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void nf4_dequant_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ qscale,
+    const float* __restrict__ step, int64_t nb, uint16_t* __restrict__ out,
+    Nf4Levels L) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+    const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(codes + (b << 5));
+    const u32x4_t c0 = cp[0], c1 = cp[1];
+    const Nf4Lut lut = nf4_make_lut(L, nf4_block_scale(qscale[b], step[b >> 8]));
+    u32x4_t* op = reinterpret_cast<u32x4_t*>(out + (b << 6));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[i] = nf4_decode8(lut, c0[i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[4 + i] = nf4_decode8(lut, c1[i]);
+  }
+}
+
+static int grid_for(int64_t work_items, int per_block, int cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+hipError_t launch_quantize(const float* w, int64_t n, uint8_t* codes, float* absmax,
+                           const Nf4Thresholds& T, hipStream_t s) {
+  const int64_t lanes = (n + 7) >> 3;
+  const int grid = grid_for(lanes, 256, 256 * 32);
+  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid), dim3(256), 0, s, w, n, codes, absmax, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* qscale,
+                               float* step, hipStream_t s) {
+  const int64_t groups = (nb + 255) >> 8;
+  const int grid = grid_for(groups, 4, 256 * 16);
+  hipLaunchKernelGGL(double_quant_kernel, dim3(grid), dim3(256), 0, s, absmax, nb, qscale, step);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
+                          int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s) {
+  const int grid = grid_for(nb, 256, 256 * 16);
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid), dim3(256), 0, s, codes, qscale, step, nb,
+                     out, L);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -1,0 +1,163 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) QLoRA frozen-base linear layer.
+ *
+ * The layer keeps a frozen base weight in 4-bit NF4 with double-quantised
+ * block scales and adds a full-precision LoRA path:
+ *
+ *     y = x . deq(W)^T + (alpha/r) . (x . A^T) . B^T
+ *
+ * Sources, cited by page title and section:
+ *   [QLoRA / infivelines.com]  NF4 levels at normal quantiles; one scale per
+ *       block of 64 weights; the scales quantised again in blocks of 256
+ *       (~0.127 bits/weight); dequantised to bf16 one block at a time
+ *       inside the matrix multiply; gradients pass through the frozen base.
+ *   [QLoRA -- the democratization event, the recipe]  4-bit NF4 frozen
+ *       base, 16-bit adapters, dequantised on the fly, gradients into the
+ *       adapters only; double quantisation of the block scale factors.
+ *   [QLoRA -- Module 12.4, "Design Details That Matter" / "Hugging Face +
+ *       BitsAndBytes"]  NF4, double quant; LoraConfig(r, lora_alpha).
+ *   [QLoRA, and fine-tuning a 7B model on a free GPU, "What each setting is
+ *       doing"]  stored in 4 bits, computed in bfloat16, dequantised for
+ *       each matrix multiply.
+ *   The pages defer the LoRA equation; the form above with s = alpha/r is
+ *   the standard LoRA layer the pages configure.
+ *
+ * Conventions (all entry points)
+ *   - Plain C types only.  bf16 tensors are passed as uint16_t bit patterns.
+ *     `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Every pointer argument except where noted is a DEVICE pointer, owned
+ *     and allocated by the caller, 16-byte aligned, row-major and densely
+ *     packed.  The library allocates no device memory and keeps no state
+ *     between calls except its constant NF4 table.
+ *   - Inputs are never written.  Outputs are fully overwritten (dA/dB are
+ *     accumulated into when `accumulate` is nonzero).  Outputs must not
+ *     alias inputs or each other.
+ *   - Return value: QLORA_OK (0) means the work was enqueued on `stream`;
+ *     a negative status means nothing was enqueued.  Argument validation
+ *     happens before any HIP call.  Device-side faults surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI.
+ *   - Inputs must be finite (no NaN/Inf); this is not checked.
+ *   - Calls on the same stream are ordered; the workspace of a call may be
+ *     reused by the next call on the same stream.  Concurrent calls on
+ *     different streams need separate workspaces.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+#define QLORA_OK          0
+#define QLORA_EINVAL     (-1) /* null pointer, negative size, aliasing        */
+#define QLORA_ESHAPE     (-2) /* K or N not a multiple of 64, r > 256 or r%8  */
+#define QLORA_EALIGN     (-3) /* a device pointer is not 16-byte aligned      */
+#define QLORA_ENOTSUP    (-4) /* blocksize != 64 or blocksize2 != 256         */
+#define QLORA_EWORKSPACE (-5) /* workspace NULL or smaller than required      */
+#define QLORA_EHIP       (-6) /* a HIP launch or runtime call failed          */
+
+#define QLORA_BLOCK   64   /* weights per absmax block                       */
+#define QLORA_GROUP   256  /* block scales per double-quantisation group      */
+#define QLORA_MAX_RANK 256
+
+/* A frozen NF4 base weight W [N, K] (out_features x in_features, row-major).
+ * All pointers are device pointers owned by the caller.
+ *   codes   [N*K/2]           byte j = code(2j) | code(2j+1) << 4
+ *   qscale  [N*K/64]          8-bit double-quantised block absmax
+ *   dq_step [ceil(N*K/16384)] fp32 step of each group of 256 block scales
+ * Block b covers flattened elements [64b, 64b+64) and decodes with scale
+ * s'_b = fp32(qscale[b] * dq_step[b/256]).                                  */
+typedef struct qlora_nf4_weight {
+  const uint8_t* codes;
+  const uint8_t* qscale;
+  const float*   dq_step;
+  int64_t        N;
+  int64_t        K;
+} qlora_nf4_weight;
+
+/* Blockwise NF4 quantisation.  [QLoRA / infivelines.com]: 16 levels at
+ * normal quantiles; each block of 64 weights carries its own scale.
+ *   w       [n_elems] fp32 input, flattened row-major (an [N, K] weight).
+ *   codes   [ceil(n_elems/2)] packed 4-bit codes, even element in the low
+ *           nibble; an odd tail is padded with code 7 (the zero level).
+ *   absmax  [ceil(n_elems/64)] fp32 exact max |w| of each block (the last
+ *           block may be partial).
+ * A code is the index of the NF4 level nearest to fp32(w / absmax) (IEEE
+ * correctly rounded quotient), ties to the lower level; a block whose
+ * absmax is 0 gets code 7 everywhere.  blocksize must be 64 (ENOTSUP).
+ * n_elems may be 0 (nothing is enqueued).                                   */
+int qlora_quantize_nf4(const float* w, int64_t n_elems, int32_t blocksize,
+                       uint8_t* codes, float* absmax, void* stream);
+
+/* Double quantisation of block scales.  [QLoRA / infivelines.com]: the
+ * block scales are quantised again in blocks of 256; [QLoRA -- Module 12.4,
+ * "Double quant"]: quantise the quantisation constants.
+ *   absmax  [n_blocks] fp32 block scales (>= 0), e.g. from the quantiser.
+ *   qscale  [n_blocks] uint8: q = min(255, rint(fp32(absmax / step))).
+ *   dq_step [ceil(n_blocks/256)] fp32: step = fp32(group max / 255);
+ *           a group whose step is 0 stores q = 0.
+ * Divisions are IEEE correctly rounded; rint is round-half-to-even.
+ * blocksize2 must be 256 (ENOTSUP).                                         */
+int qlora_double_quant(const float* absmax, int64_t n_blocks, int32_t blocksize2,
+                       uint8_t* qscale, float* dq_step, void* stream);
+
+/* Standalone dequantisation to bf16 (the same device function the GEMMs
+ * use): out[i] = bf16_rne(fp32(L[code_i] * fp32(qscale[b] * dq_step[b/256]))).
+ * [QLoRA / infivelines.com]: the base is dequantised to bf16.
+ *   out  [N*K] bf16 (uint16_t patterns), row-major [N, K].
+ * Requires N*K to be a multiple of 64.                                      */
+int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream);
+
+/* Forward pass.  [QLoRA / infivelines.com]: dequantised to bf16 one block
+ * at a time inside the matrix multiply; adapters in full precision.
+ *   x  [M, K] bf16        A [r, K] bf16        B [N, r] bf16
+ *   y  [M, N] bf16 output: y = x.deq(W)^T + (alpha/r).(x.A^T).B^T,
+ *      accumulated in fp32 and rounded once to bf16 (nearest-even).
+ * M >= 1 is arbitrary; N and K must be multiples of 64 (ESHAPE); r is 0 or
+ * a multiple of 8 up to 256 (r = 0: base only, A and B may be NULL).
+ * workspace: device scratch of at least
+ * qlora_linear_workspace_bytes(0, M, N, K, r) bytes, 256-byte aligned.      */
+int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
+                     const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                     uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* Backward pass through the frozen base.  [QLoRA -- the democratization
+ * event, the recipe]: gradients flow through the frozen 4-bit base into the
+ * adapters; the base gets no gradient.
+ *   dy [M, N] bf16 upstream gradient; x, A, B as in the forward pass.
+ *   dx [M, K] bf16 output (may be NULL to skip):
+ *        dx = dy.deq(W) + (alpha/r).(dy.B).A
+ *   dA [r, K] fp32 output:  dA = (alpha/r).(dy.B)^T.x
+ *   dB [N, r] fp32 output:  dB = (alpha/r).dy^T.(x.A^T)
+ *   accumulate != 0 adds the new dA/dB to the existing contents.
+ * r = 0: only dx is produced (A, B, dA, dB may be NULL).
+ * workspace: at least qlora_linear_workspace_bytes(1, M, N, K, r) bytes.    */
+int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
+                     int64_t M, const uint16_t* A, const uint16_t* B, int32_t r,
+                     float alpha, uint16_t* dx, float* dA, float* dB,
+                     int32_t accumulate, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Workspace bytes for op 0 (forward) or 1 (backward) at the given shape;
+ * 0 for an invalid shape.  Host-only; never touches the GPU.               */
+size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
+                                    int32_t r);
+
+/* The library's own fp32 NF4 table (16 levels, ascending) and its 15 fp32
+ * decision thresholds (level midpoints rounded towards -infinity), built on
+ * the host from the library's own normal quantile function.  `levels` and
+ * `thresholds` are HOST pointers; either may be NULL.  Never touches the GPU. */
+int qlora_nf4_levels(float* levels, float* thresholds);
+
+/* Static string for a status code (host only).                             */
+const char* qlora_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H */

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/qlora.h declares, its own NF4 table equals the oracle's bit for bit,
+and invalid arguments are rejected before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import bit_quantized_lora_03_amd as q
+from bit_quantized_lora_03_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q.LIB_PATH),
+                                reason="libqlora.so not built")
+
+# fake but well-aligned, non-null device addresses: every call below must be
+# rejected by validation before any of them is dereferenced or launched on
+P0 = 1 << 20
+P1 = 2 << 20
+P2 = 3 << 20
+P3 = 4 << 20
+P4 = 5 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    L = q.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_library_table_equals_oracle_bitwise():
+    lv, th = q.nf4_levels()
+    assert np.array_equal(lv.view(np.uint32), oracle.nf4_levels_f32().view(np.uint32))
+    assert np.array_equal(th.view(np.uint32), oracle.nf4_thresholds_f32().view(np.uint32))
+
+
+def test_status_strings():
+    L = q.lib()
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert len(L.qlora_status_string(code)) >= 2
+    assert L.qlora_status_string(-99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    ws = q.workspace_bytes
+    assert ws(0, 512, 4096, 4096, 0) == 0
+    assert ws(1, 512, 4096, 4096, 0) == 0
+    f = ws(0, 512, 4096, 4096, 16)
+    b = ws(1, 512, 4096, 4096, 16)
+    assert f > 0 and b > f and f % 256 == 0 and b % 256 == 0
+    assert f >= 512 * 32 * 2                      # at least the hi/lo split of x.A^T
+    assert ws(0, 16, 100, 4096, 16) == 0          # N % 64
+    assert ws(0, 16, 4096, 100, 16) == 0          # K % 64
+    assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
+    assert ws(0, 16, 4096, 4096, 264) == 0        # r > 256
+    assert ws(2, 16, 4096, 4096, 16) == 0         # bad op
+
+
+def _weight(N=128, K=128, codes=P0, qs=P1, st=P2):
+    return _lib.Nf4Weight(codes, qs, st, N, K)
+
+
+def test_quantize_validation():
+    L = q.lib()
+    assert L.qlora_quantize_nf4(P0, -1, 64, P1, P2, None) == -1
+    assert L.qlora_quantize_nf4(P0, 128, 32, P1, P2, None) == -4
+    assert L.qlora_quantize_nf4(P0, 0, 64, None, None, None) == 0      # empty: no-op
+    assert L.qlora_quantize_nf4(None, 128, 64, P1, P2, None) == -1
+    assert L.qlora_quantize_nf4(P0 + 4, 128, 64, P1, P2, None) == -3
+    assert L.qlora_quantize_nf4(P0, 128, 64, P0 + 256, P2, None) == -1  # codes inside w
+
+
+def test_double_quant_validation():
+    L = q.lib()
+    assert L.qlora_double_quant(P0, -5, 256, P1, P2, None) == -1
+    assert L.qlora_double_quant(P0, 512, 128, P1, P2, None) == -4
+    assert L.qlora_double_quant(P0, 0, 256, None, None, None) == 0
+    assert L.qlora_double_quant(P0, 512, 256, None, P2, None) == -1
+    assert L.qlora_double_quant(P0, 512, 256, P1 + 8, P2, None) == -3
+    assert L.qlora_double_quant(P0, 512, 256, P0 + 16, P2, None) == -1
+
+
+def test_dequant_validation():
+    L = q.lib()
+    w = _weight()
+    assert L.qlora_dequantize_nf4(ctypes.byref(w), None, None) == -1
+    bad = _weight(N=3, K=5)
+    assert L.qlora_dequantize_nf4(ctypes.byref(bad), P3, None) == -2
+    assert L.qlora_dequantize_nf4(ctypes.byref(w), P3 + 2, None) == -3
+    assert L.qlora_dequantize_nf4(ctypes.byref(w), P0, None) == -1     # out over codes
+
+
+def test_fwd_validation():
+    L = q.lib()
+    w = _weight(256, 256)
+    ws_need = q.workspace_bytes(0, 16, 256, 256, 8)
+    call = lambda **kw: L.qlora_linear_fwd(
+        ctypes.byref(kw.get("w", w)), kw.get("x", P3), kw.get("M", 16), kw.get("A", P4),
+        kw.get("B", P4 + 8192), kw.get("r", 8), 16.0, kw.get("y", P4 + 65536),
+        kw.get("ws", P4 + (1 << 19)), kw.get("wsb", ws_need), None)
+    assert L.qlora_linear_fwd(None, P3, 16, P4, P4, 8, 16.0, P1, None, 0, None) == -1
+    assert call(w=_weight(250, 256)) == -2
+    assert call(w=_weight(256, 250)) == -2
+    assert call(w=_weight(256, 256, codes=P0 + 1)) == -3
+    assert call(r=12) == -2
+    assert call(r=264) == -2
+    assert call(r=-8) == -1
+    assert call(M=-1) == -1
+    assert call(x=None) == -1
+    assert call(A=None) == -1
+    assert call(x=P3 + 2) == -3
+    assert call(ws=None) == -5
+    assert call(wsb=ws_need - 1) == -5
+    assert call(ws=P4 + (1 << 19) + 16) == -3                 # workspace 256-B alignment
+    assert call(y=P3) == -1                                   # y aliases x
+    assert call(M=0) == 0                                     # empty: no-op
+
+
+def test_bwd_validation():
+    L = q.lib()
+    w = _weight(256, 256)
+    need = q.workspace_bytes(1, 16, 256, 256, 8)
+    base = dict(w=w, x=P3, dy=P3 + 16384, M=16, A=P4, B=P4 + 8192, r=8, dx=P4 + 65536,
+                dA=P4 + 131072, dB=P4 + 196608, acc=0, ws=P4 + (1 << 19), wsb=need)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.qlora_linear_bwd(ctypes.byref(a["w"]), a["x"], a["dy"], a["M"], a["A"], a["B"],
+                                  a["r"], 16.0, a["dx"], a["dA"], a["dB"], a["acc"], a["ws"],
+                                  a["wsb"], None)
+    assert call(dy=None) == -1
+    assert call(dA=None) == -1
+    assert call(x=None) == -1
+    assert call(r=4) == -2
+    assert call(dB=P4 + 196608 + 4) == -3
+    assert call(ws=None) == -5
+    assert call(dx=P3) == -1                                  # dx aliases x
+    assert call(dA=P4 + 65536) == -1                          # dA overlaps dx
+    assert call(dB=P4 + (1 << 19)) == -1                      # dB inside workspace
