@@ -1,0 +1,352 @@
+#!/usr/bin/env python
+"""Benchmark of the QLoRA frozen-base linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: NF4-quantise the fp32 base weight, double-quantise
+its block scales, run the fused forward (dequant-in-GEMM + LoRA) and the
+backward (dX through the frozen base, dA, dB).  The step is captured once
+in a HIP graph and replayed; K replays are timed between device
+synchronisations.  Rank 0 prints one JSON line.
+
+value = algorithmic fwd+bwd flops per step / step time, in TFLOP/s.  The
+`roofline` object is for the dominant kernel, timed alone with HIP events
+on its stream; `cpu_baseline` is the fp64 CPU oracle timed on the host on
+the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+DEFAULT_WORKLOAD = "q_proj4096_m512_r16"
+
+
+def packed_weight_bytes(N, K):
+    n = N * K
+    return n // 2 + n // 64 + 4 * math.ceil(n / 16384)
+
+
+def fwd_flops(M, N, K, r):
+    return 2 * M * N * K + 2 * M * r * (K + N)
+
+
+def bwd_flops(M, N, K, r):
+    return 2 * M * N * K + 4 * M * r * (N + K) + 2 * M * K * r
+
+
+def fwd_bytes(M, N, K, r):
+    return packed_weight_bytes(N, K) + 2 * M * K + 2 * r * K + 2 * N * r + 2 * M * N
+
+
+def bwd_bytes(M, N, K, r):
+    return (packed_weight_bytes(N, K) + 2 * M * N + 4 * M * K + 2 * r * K + 2 * N * r
+            + 4 * (r * K + N * r))
+
+
+def quant_bytes(N, K):
+    n = N * K
+    nb = n // 64
+    return 4 * n + n // 2 + 4 * nb + (4 * nb + nb + 4 * math.ceil(nb / 256))
+
+
+def make_layer(name):
+    from bit_quantized_lora_03_amd import workloads as wl
+    if name == "linear256_m16_r8":
+        return wl.tiny_256(), "fwd+bwd+quant"
+    if name == "q_proj4096_m512_r16":
+        return wl.q_proj_4096(), "fwd+bwd+quant"
+    if name in ("mlp_gate", "mlp_up", "mlp_down"):
+        return wl.mlp_7b()[["mlp_gate", "mlp_up", "mlp_down"].index(name)], "fwd+bwd"
+    if name.startswith("decode8192_m"):
+        return wl.decode_8192(int(name[len("decode8192_m"):])), "fwd"
+    if name == "up65b_m4096_r64":
+        return wl.layer_65b(), "fwd+bwd+quant"
+    raise SystemExit(f"unknown workload {name}")
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        blas = [i for i in info if i.get("user_api") == "blas"]
+        if blas:
+            return int(blas[0]["num_threads"]), blas[0].get("internal_api", "?")
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0)), "?"
+
+
+def run_cpu_baseline(L, kind, budget_s):
+    """Time the fp64 oracle on the host on this workload (test infrastructure,
+    used here only as the CPU reference)."""
+    import oracle
+    t0 = time.perf_counter()
+    flops = 0.0
+    w = L.w
+    x = L.f32("x")
+    A = L.f32("A") if L.r else None
+    B = L.f32("B") if L.r else None
+    _, packed, absmax = oracle.quantize_nf4(w)
+    q, step = oracle.double_quant(absmax)
+    t_q = time.perf_counter()
+    wd = oracle.bf16_bits_to_f64(oracle.dequant_nf4_bits(packed, q, step, w.size)).reshape(w.shape)
+    # the layer on a bounded token sample if the full batch would exceed the budget
+    M = L.M
+    rows = M
+    est = (fwd_flops(M, L.N, L.K, L.r) + (bwd_flops(M, L.N, L.K, L.r) if "bwd" in kind else 0)) / 50e9
+    if est > budget_s:
+        rows = max(1, int(M * budget_s / est))
+    t1 = time.perf_counter()
+    oracle.lora_linear_fwd(x[:rows], wd, A, B, L.alpha)
+    flops += fwd_flops(rows, L.N, L.K, L.r)
+    if "bwd" in kind:
+        oracle.lora_linear_bwd(x[:rows], L.f32("dy")[:rows], wd, A, B, L.alpha)
+        flops += bwd_flops(rows, L.N, L.K, L.r)
+    t2 = time.perf_counter()
+    # scale to a full step: quantise/dequantise once, the layer for M tokens
+    layer_s = (t2 - t1) * (M / rows)
+    step_s = (t_q - t0) + (t1 - t_q) + layer_s
+    full_flops = fwd_flops(M, L.N, L.K, L.r) + (bwd_flops(M, L.N, L.K, L.r) if "bwd" in kind else 0)
+    threads, blas = cpu_threads()
+    sample = (f"quantise + double-quant + dequant of the full {L.N}x{L.K} weight; "
+              f"layer on {rows} of {M} tokens, scaled linearly to {M} "
+              f"(quant {t_q - t0:.2f}s, dequant {t1 - t_q:.2f}s, layer {t2 - t1:.2f}s; "
+              f"blas={blas})")
+    return {"value": full_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": sample, "step_s": step_s}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle CPU work to aim for")
+    ap.add_argument("--eager", action="store_true", help="time eager calls, no graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_lora_03_amd as q
+    from bit_quantized_lora_03_amd import _lib
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, kind = make_layer(args.workload)
+    M, N, K, r, alpha = L.M, L.N, L.K, L.r, L.alpha
+    lib = q.lib()
+    stream = torch.cuda.current_stream()
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    # ---- inputs resident in HBM ----
+    w_d = to_dev(L.w)
+    x_d = to_dev(L.x_bits)
+    A_d = to_dev(L.A_bits) if r else None
+    B_d = to_dev(L.B_bits) if r else None
+    dy_d = to_dev(L.dy_bits) if "bwd" in kind else None
+    n = N * K
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    absmax = torch.empty(n // 64, dtype=torch.float32, device=dev)
+    qs = torch.empty(n // 64, dtype=torch.uint8, device=dev)
+    st = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=dev)
+    rot = 16 if kind == "fwd" else 1          # decode: rotate 16 weight copies
+    y = torch.empty((M, N), dtype=torch.int16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.int16, device=dev) if "bwd" in kind else None
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev) if ("bwd" in kind and r) else None
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev) if ("bwd" in kind and r) else None
+    ws_f = q.workspace_bytes(0, M, N, K, r)
+    ws_b = q.workspace_bytes(1, M, N, K, r)
+    ws = torch.empty(max(ws_f, ws_b, 256), dtype=torch.uint8, device=dev)
+
+    P = lambda t: None if t is None else t.data_ptr()
+    sp = lambda: torch.cuda.current_stream().cuda_stream
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {lib.qlora_status_string(rc).decode()}")
+
+    def quantize():
+        check(lib.qlora_quantize_nf4(P(w_d), n, 64, P(codes), P(absmax), sp()), "quantize")
+        check(lib.qlora_double_quant(P(absmax), n // 64, 256, P(qs), P(st), sp()), "double_quant")
+
+    quantize()
+    torch.cuda.synchronize()
+    weights = []
+    for j in range(rot):
+        c, qq, ss = (codes, qs, st) if j == 0 else (codes.clone(), qs.clone(), st.clone())
+        weights.append((c, qq, ss, _lib.Nf4Weight(c.data_ptr(), qq.data_ptr(), ss.data_ptr(), N, K)))
+
+    def fwd(j=0, rr=r):
+        wt = weights[j][3]
+        check(lib.qlora_linear_fwd(ctypes.byref(wt), P(x_d), M, P(A_d) if rr else None,
+                                   P(B_d) if rr else None, rr, alpha, P(y), P(ws), ws.numel(),
+                                   sp()), "fwd")
+
+    def bwd(rr=r, with_dx=True):
+        wt = weights[0][3]
+        check(lib.qlora_linear_bwd(ctypes.byref(wt), P(x_d), P(dy_d), M, P(A_d) if rr else None,
+                                   P(B_d) if rr else None, rr, alpha, P(dx) if with_dx else None,
+                                   P(dA) if rr else None, P(dB) if rr else None, 0, P(ws),
+                                   ws.numel(), sp()), "bwd")
+
+    def step(i=0):
+        if "quant" in kind:
+            quantize()
+        fwd(i % rot)
+        if "bwd" in kind:
+            bwd()
+
+    # ---- capture one step per rotation slot in a HIP graph ----
+    graphs = []
+    if not args.eager:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(2):
+                step(0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for j in range(rot):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(j)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs:
+            graphs[i % rot].replay()
+        else:
+            step(i)
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    flops = fwd_flops(M, N, K, r) + (bwd_flops(M, N, K, r) if "bwd" in kind else 0)
+    wbytes = packed_weight_bytes(N, K) * (2 if "bwd" in kind else 1)
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # ---- per-op breakdown (eager, events on the launch stream) ----
+    def timed(fn, reps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    reps = max(10, args.steps)
+    ops = {}
+    if "quant" in kind:
+        ops["quantize_ms"] = timed(lambda i: quantize(), reps)
+    ops["fwd_ms"] = timed(lambda i: fwd(i % rot), reps)
+    if "bwd" in kind:
+        ops["bwd_ms"] = timed(lambda i: bwd(), reps)
+    # the two big fused GEMMs alone (base-only calls launch exactly one kernel)
+    k_fwd = timed(lambda i: fwd(i % rot, 0), reps)
+    k_dx = timed(lambda i: bwd(0, True), reps) if "bwd" in kind else 0.0
+    ops["fwd_gemm_alone_ms"] = k_fwd
+    if "bwd" in kind:
+        ops["dx_gemm_alone_ms"] = k_dx
+
+    if M <= 64:
+        # decode: HBM-bound; algorithmic bytes of the base-only launch
+        kb = packed_weight_bytes(N, K) + 2 * M * K + 2 * M * N
+        ach = kb / (k_fwd * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBPS, "traffic": None,
+                "kernel": "fwd_gemm_kernel (base only)", "per_launch": kb}
+    else:
+        name, t_k, fl = ("fwd_gemm_kernel", k_fwd, 2 * M * N * K)
+        if "bwd" in kind and k_dx > k_fwd:
+            name, t_k, fl = ("dx_gemm_kernel", k_dx, 2 * M * N * K)
+        ach = fl / (t_k * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": name + " (base only)",
+                "per_launch": fl}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = run_cpu_baseline(L, kind, args.cpu_budget)
+
+    out = {
+        "metric": "fused NF4-dequant+LoRA linear fwd+bwd TFLOP/s and weight GB/s vs roofline",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "r": r, "alpha": alpha,
+                   "step": kind.replace("+", " + "), "graph": not args.eager,
+                   "weight_rotation": rot},
+        "weight_GBps": round(wbytes / (ms_step * 1e-3) / 1e9, 2),
+        "roofline": roof,
+        "ops": {k: round(v, 5) for k, v in ops.items()},
+        "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "step_s"},
+        "wall_s": round(wall, 4),
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
