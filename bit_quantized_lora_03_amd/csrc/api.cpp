@@ -60,17 +60,30 @@ int check_rank(int32_t r) {
 
 // ---- workspace layout --------------------------------------------------
 struct FwdWs {
-  size_t p_off, xs_off, total;
-  int splits;
+  size_t p_off, xs_off, part_off, total;
+  int splits, dsplits;
+  bool decode;  // few tokens: split-K decode path
 };
 FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
-  (void)N;
   FwdWs L{};
-  if (r == 0 || M == 0) return L;
-  L.splits = qlora::lora_down_splits(M, K, r);
-  L.p_off = 0;
-  L.xs_off = round_up(L.p_off + (size_t)L.splits * M * r * sizeof(float), 256);
-  L.total = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+  L.decode = M <= qlora::kDecodeMaxM;
+  if (M == 0) return L;
+  size_t off = 0;
+  if (r > 0) {
+    L.splits = qlora::lora_down_splits(M, K, r);
+    L.p_off = 0;
+    off = round_up((size_t)L.splits * M * r * sizeof(float), 256);
+    if (!L.decode) {
+      L.xs_off = off;
+      off = round_up(off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+    }
+  }
+  if (L.decode) {
+    L.dsplits = qlora::decode_splits(N, K);
+    L.part_off = off;
+    off = round_up(off + (size_t)L.dsplits * M * N * sizeof(float), 256);
+  }
+  L.total = off;
   return L;
 }
 
@@ -217,13 +230,21 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
 
     hipStream_t s = as_stream(stream);
     const Nf4Levels L = levels_arg();
-    uint16_t* xs = nullptr;
+    const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+    float* P = r > 0 ? at<float>(workspace, ws.p_off) : nullptr;
     if (r > 0) {
-      float* P = at<float>(workspace, ws.p_off);
-      xs = at<uint16_t>(workspace, ws.xs_off);
       if ((st = hip_status(qlora::launch_lora_down(x, A, M, K, r, ws.splits, P, s))) != QLORA_OK)
         return st;
-      const float scale = alpha / static_cast<float>(r);
+    }
+    if (ws.decode) {
+      return hip_status(qlora::launch_decode_fwd(w->codes, w->qscale, w->dq_step, x, P,
+                                                 ws.splits, B, r, scale,
+                                                 at<float>(workspace, ws.part_off), ws.dsplits, y,
+                                                 M, N, K, L, s));
+    }
+    uint16_t* xs = nullptr;
+    if (r > 0) {
+      xs = at<uint16_t>(workspace, ws.xs_off);
       if ((st = hip_status(qlora::launch_lora_split(P, ws.splits, M, r, scale, xs, s))) != QLORA_OK)
         return st;
     }

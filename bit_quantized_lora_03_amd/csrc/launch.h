@@ -42,6 +42,15 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
                            uint16_t* y, int64_t M, int64_t N, int64_t K, int r,
                            const Nf4Levels& L, hipStream_t s);
 
+// gemm_decode.hip -- forward for M <= 32: split-K partials part[S][M][N],
+// then y = bf16(sum part + scale . (sum_z P[z]) . B^T)
+constexpr int kDecodeMaxM = 32;
+int decode_splits(int64_t N, int64_t K);
+hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const float* step,
+                             const uint16_t* x, const float* P, int psplits, const uint16_t* B,
+                             int r, float scale, float* part, int splits, uint16_t* y, int64_t M,
+                             int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s);
+
 // gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,

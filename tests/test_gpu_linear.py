@@ -170,3 +170,41 @@ def test_empty_token_batch(cuda):
                               dev(L.A_bits), dev(L.B_bits), 16.0, dA=dev(dA0))
     torch.cuda.synchronize()
     assert np.all(host(dA) == 0) and np.all(host(dB) == 0)
+
+
+@pytest.mark.parametrize("shape", [(300, 320, 448, 16, 32.0), (8, 256, 512, 64, 16.0)],
+                         ids=["main", "decode"])
+def test_graph_replay_matches_eager(cuda, shape):
+    """The whole fwd + bwd captured in one HIP graph: every replay (with
+    eager work and synchronisations between replays) equals the eager run
+    bit for bit."""
+    import torch
+    L = _layer(*shape)
+    ol = OracleLayer(L.w)
+    pw = ol.to_device()
+    x, dy, A, B = dev(L.x_bits), dev(L.dy_bits), dev(L.A_bits), dev(L.B_bits)
+    y0 = q.linear_fwd(pw, x, A, B, L.alpha)
+    dx0, dA0, dB0 = q.linear_bwd(pw, x, dy, A, B, L.alpha)
+    torch.cuda.synchronize()
+    eager = [host(t) for t in (y0, dx0, dA0, dB0)]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        q.linear_fwd(pw, x, A, B, L.alpha)
+        q.linear_bwd(pw, x, dy, A, B, L.alpha)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y = q.linear_fwd(pw, x, A, B, L.alpha)
+        dx, dA, dB = q.linear_bwd(pw, x, dy, A, B, L.alpha)
+    for rep in range(4):
+        for t in (y, dx, dA, dB):
+            t.zero_()                                  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t) for t in (y, dx, dA, dB)]
+        for a, b in zip(got, eager):
+            assert np.array_equal(a, b), f"replay {rep} differs from eager"
