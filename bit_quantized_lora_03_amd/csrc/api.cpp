@@ -61,47 +61,65 @@ int check_rank(int32_t r) {
 // ---- workspace layout --------------------------------------------------
 struct FwdWs {
   size_t p_off, xs_off, part_off, total;
-  int splits, dsplits;
-  bool decode;  // few tokens: split-K decode path
+  int splits;    // k splits of the adapter down-projection partials
+  int dsplits;   // k splits of the decode path
+  int gsplits;   // k splits of the fused GEMM (1: no partials)
+  bool decode;   // few tokens: split-K decode path
 };
 FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdWs L{};
   L.decode = M <= qlora::kDecodeMaxM;
+  L.gsplits = 1;
   if (M == 0) return L;
+  if (L.decode) {
+    // split-K partials of x . W'^T and x . A^T: [S][M][N + r] fp32
+    L.dsplits = qlora::decode_splits(M, N, K);
+    L.part_off = 0;
+    L.total = round_up((size_t)L.dsplits * M * (N + r) * sizeof(float), 256);
+    return L;
+  }
   size_t off = 0;
   if (r > 0) {
     L.splits = qlora::lora_down_splits(M, K, r);
     L.p_off = 0;
-    off = round_up((size_t)L.splits * M * r * sizeof(float), 256);
-    if (!L.decode) {
-      L.xs_off = off;
-      off = round_up(off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
-    }
+    L.xs_off = round_up((size_t)L.splits * M * r * sizeof(float), 256);
+    off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
   }
-  if (L.decode) {
-    L.dsplits = qlora::decode_splits(N, K);
+  L.gsplits = qlora::gemm_splits(M, N, K);
+  if (L.gsplits > 1) {
     L.part_off = off;
-    off = round_up(off + (size_t)L.dsplits * M * N * sizeof(float), 256);
+    off = round_up(off + (size_t)L.gsplits * M * N * sizeof(float), 256);
   }
   L.total = off;
   return L;
 }
 
 struct BwdWs {
-  size_t pa_off, bt_off, pg_off, xs_off, gs_off, total;
+  size_t pa_off, bt_off, pg_off, xs_off, gs_off, part_off, total;
   int splits_a, splits_g;
+  int gsplits;  // reduction splits of the dX GEMM (1: no partials)
 };
 BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs L{};
-  if (r == 0 || M == 0) return L;
-  L.splits_a = qlora::lora_down_splits(M, K, r);
-  L.splits_g = qlora::lora_down_splits(M, N, r);
-  L.pa_off = 0;
-  L.bt_off = round_up(L.pa_off + (size_t)L.splits_a * M * r * sizeof(float), 256);
-  L.pg_off = round_up(L.bt_off + (size_t)r * N * sizeof(uint16_t), 256);
-  L.xs_off = round_up(L.pg_off + (size_t)L.splits_g * M * r * sizeof(float), 256);
-  L.gs_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
-  L.total = round_up(L.gs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+  L.gsplits = 1;
+  if (M == 0) return L;
+  size_t off = 0;
+  if (r > 0) {
+    L.splits_a = qlora::lora_down_splits(M, K, r);
+    L.splits_g = qlora::lora_down_splits(M, N, r);
+    L.pa_off = 0;
+    L.bt_off = round_up(L.pa_off + (size_t)L.splits_a * M * r * sizeof(float), 256);
+    L.pg_off = round_up(L.bt_off + (size_t)r * N * sizeof(uint16_t), 256);
+    L.xs_off = round_up(L.pg_off + (size_t)L.splits_g * M * r * sizeof(float), 256);
+    L.gs_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+    off = round_up(L.gs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+  }
+  L.gsplits = qlora::gemm_splits(M, K, N);
+  if (L.gsplits > 1) {
+    L.part_off = off;
+    off = round_up(off + (size_t)L.gsplits * M * K * sizeof(float), 256);
+  }
+  L.total = off;
   return L;
 }
 
@@ -231,25 +249,23 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
     hipStream_t s = as_stream(stream);
     const Nf4Levels L = levels_arg();
     const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-    float* P = r > 0 ? at<float>(workspace, ws.p_off) : nullptr;
-    if (r > 0) {
-      if ((st = hip_status(qlora::launch_lora_down(x, A, M, K, r, ws.splits, P, s))) != QLORA_OK)
-        return st;
-    }
     if (ws.decode) {
-      return hip_status(qlora::launch_decode_fwd(w->codes, w->qscale, w->dq_step, x, P,
-                                                 ws.splits, B, r, scale,
-                                                 at<float>(workspace, ws.part_off), ws.dsplits, y,
-                                                 M, N, K, L, s));
+      return hip_status(qlora::launch_decode_fwd(w->codes, w->qscale, w->dq_step, x, A, B, r,
+                                                 scale, at<float>(workspace, ws.part_off),
+                                                 ws.dsplits, y, M, N, K, L, s));
     }
     uint16_t* xs = nullptr;
     if (r > 0) {
+      float* P = at<float>(workspace, ws.p_off);
       xs = at<uint16_t>(workspace, ws.xs_off);
+      if ((st = hip_status(qlora::launch_lora_down(x, A, M, K, r, ws.splits, P, s))) != QLORA_OK)
+        return st;
       if ((st = hip_status(qlora::launch_lora_split(P, ws.splits, M, r, scale, xs, s))) != QLORA_OK)
         return st;
     }
-    return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->dq_step, x, xs, B, y, M, N,
-                                             K, r, L, s));
+    float* part = ws.gsplits > 1 ? at<float>(workspace, ws.part_off) : nullptr;
+    return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->dq_step, x, xs, B, y, part,
+                                             ws.gsplits, M, N, K, r, L, s));
   } catch (...) {
     return QLORA_EHIP;
   }
@@ -332,8 +348,9 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
         return st;
     }
     if (dx) {
+      float* part = ws.gsplits > 1 ? at<float>(workspace, ws.part_off) : nullptr;
       if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->dq_step, dy, gs, A, dx,
-                                                 M, N, K, r, L, s))) != QLORA_OK)
+                                                 part, ws.gsplits, M, N, K, r, L, s))) != QLORA_OK)
         return st;
     }
     return QLORA_OK;

@@ -105,6 +105,17 @@ __device__ __forceinline__ float nf4_block_scale(uint32_t q, float step) {
   return static_cast<float>(q) * step;
 }
 
+// Raw buffer access (gfx9 descriptor: untyped dwords, DATA_FORMAT 32).
+// Loads at byte offsets at or past `bytes` return zero, which the GEMMs use
+// for rows beyond the tensor instead of branching.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // MFMA wrappers (gfx950 bf16, fp32 accumulate).
 __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);

@@ -17,6 +17,11 @@
 //
 // Block tile 256 (k) x 256 (m), 64 reduction rows per stage; 4 waves in a
 // 2 x 2 grid of 128 x 128; two LDS stages of (W^T tile, dy tile), 128 KiB.
+// As in the forward pass, the next slab is decoded while the current one
+// multiplies (a quarter after each quarter of the MFMAs), codes are fetched
+// two slabs ahead, out-of-range rows are clamped rather than branched
+// around, and small outputs split the reduction over gridDim.z blocks that
+// write fp32 partials.
 
 #include "device_common.h"
 #include "launch.h"
@@ -37,11 +42,15 @@ struct DxParams {
   const uint16_t* dy;
   const uint16_t* gs;
   const uint16_t* A;
-  uint16_t* dx;
+  uint16_t* dx;    // bf16 output (splits == 1)
+  float* part;     // fp32 partials [splits][M][K] (splits > 1)
   int64_t M, N, K;
   int r;
+  int splits;
   Nf4Levels L;
 };
+
+__device__ __forceinline__ int64_t clamp_row(int64_t v, int64_t hi) { return v < hi ? v : hi - 1; }
 
 // dy tile: [256 m][64 n], rows 128 B, chunk swizzled by row.
 __device__ __forceinline__ int rk(int row, int chunk) { return row * ROW_CHUNKS + (chunk ^ (row & 7)); }
@@ -77,112 +86,130 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // this thread decodes reduction row (t >> 2) of the slab, k quarter (t & 3)
+  const int z = blockIdx.z;
+  const int64_t nst = N / RT;
+  const int64_t st0 = nst * z / p.splits, st1 = nst * (z + 1) / p.splits;
+
+  // this thread decodes reduction row (t >> 2) of the slab, k quarter (t & 3);
+  // a quarter past K is clamped to the last block (never stored)
   const int wr = t >> 2;
   const int kq = t & 3;
-  const int64_t kcol = k0 + 64 * kq;
-  const bool kcol_ok = kcol < K;
+  const int64_t kcol_raw = k0 + 64 * kq;
+  const bool kcol_ok = kcol_raw < K;
+  const int64_t kcol = kcol_ok ? kcol_raw : K - 64;
+  // dy rows m0 + (t >> 3) + 32 j through a buffer descriptor: rows past M
+  // read as zero
+  const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.dy, (uint32_t)(M * N * 2));
+  const uint32_t yoff = (uint32_t)(((m0 + (t >> 3)) * N + 8 * (t & 7)) * 2);
+  const uint32_t yrow_step = (uint32_t)(32 * N * 2);
 
-  u32x4_t yr[8];
-  u32x4_t cr[2];
-  float wscale;
-
-  auto load_tile = [&](int64_t st) {
-    const int64_t nb = st * RT;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t m = m0 + (t >> 3) + 32 * j;
-      yr[j] = (m < M) ? *reinterpret_cast<const u32x4_t*>(p.dy + m * N + nb + 8 * (t & 7)) : zero;
-    }
-    const int64_t n = nb + wr;
-    if (kcol_ok) {
-      const int64_t idx = n * K + kcol;  // first element of the block
-      const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
-      cr[0] = cp[0];
-      cr[1] = cp[1];
-      wscale = nf4_block_scale(p.qscale[idx >> 6], p.step[idx >> 14]);
-    } else {
-      cr[0] = zero;
-      cr[1] = zero;
-      wscale = 0.0f;
-    }
+  struct Codes {
+    u32x4_t c0, c1;
+    float s;
   };
-  // scatter 64 consecutive-k bf16 values of reduction row `wr` into W^T
-  auto scatter_row = [&](int stage, const u32x4_t* v8) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pr = v8[c][e];
-        const int kl = 64 * kq + 8 * c + 2 * e;
-        wt[stage][wt_off(kl, wr)] = (uint16_t)pr;
-        wt[stage][wt_off(kl + 1, wr)] = (uint16_t)(pr >> 16);
-      }
-    }
+  auto load_codes = [&](int64_t st, Codes& c) {
+    const int64_t idx = (st * RT + wr) * K + kcol;  // first element of the block
+    const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
+    c.c0 = cp[0];
+    c.c1 = cp[1];
+    c.s = nf4_block_scale(p.qscale[idx >> 6], p.step[idx >> 14]);
   };
-  auto store_tile = [&](int stage) {
+  auto load_dy = [&](int64_t st, u32x4_t (&yr)[8]) {
+    const uint32_t o = yoff + (uint32_t)(st * RT * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) yr[j] = buffer_load16(yres, o + j * yrow_step);
+  };
+  auto store_dy = [&](int stage, const u32x4_t (&yr)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) dyt[stage][rk((t >> 3) + 32 * j, t & 7)] = yr[j];
-    const Nf4Lut lut = nf4_make_lut(p.L, wscale);
-    u32x4_t v8[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) v8[c] = nf4_decode8(lut, cr[c >> 2][c & 3]);
-    scatter_row(stage, v8);
   };
-  auto compute = [&](int stage) {
+  // scatter 8 consecutive-k bf16 values (chunk c of this thread's 64) of
+  // reduction row `wr` into W^T
+  auto scatter8 = [&](int stage, int c, const u32x4_t v) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 2 * kk + lg;
-      u32x4_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const u32x4_t*>(&wt[stage][wt_off(128 * wk + 32 * i + lr, 8 * ch)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = dyt[stage][rk(128 * wm + 32 * j + lr, ch)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t pr = v[e];
+      const int kl = 64 * kq + 8 * c + 2 * e;
+      wt[stage][wt_off(kl, wr)] = (uint16_t)pr;
+      wt[stage][wt_off(kl + 1, wr)] = (uint16_t)(pr >> 16);
     }
   };
+  auto mfma_step = [&](int stage, int kk) {
+    const int ch = 2 * kk + lg;
+    u32x4_t a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const u32x4_t*>(&wt[stage][wt_off(128 * wk + 32 * i + lr, 8 * ch)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = dyt[stage][rk(128 * wm + 32 * j + lr, ch)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+  };
 
-  const int64_t nst = N / RT;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int64_t st = 0; st < nst; ++st) {
-    const int cur = (int)(st & 1);
-    if (st + 1 < nst) load_tile(st + 1);
-    compute(cur);
-    if (st + 1 < nst) store_tile(cur ^ 1);
+  if (st0 < st1) {
+    const int64_t last = st1 - 1;
+    auto cl = [&](int64_t v) { return v < last ? v : last; };
+    Codes cn, cnn;
+    u32x4_t yr[8];
+    load_codes(st0, cn);
+    load_dy(st0, yr);
+    store_dy(0, yr);
+    {
+      const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) scatter8(0, c, nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]));
+    }
+    load_codes(cl(st0 + 1), cn);
+    load_dy(cl(st0 + 1), yr);
+    load_codes(cl(st0 + 2), cnn);
     __syncthreads();
+
+    for (int64_t st = st0; st < st1; ++st) {
+      const int cur = (int)((st - st0) & 1), nxt = cur ^ 1;
+      const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        mfma_step(cur, kk);
+#pragma unroll
+        for (int c = 2 * kk; c < 2 * kk + 2; ++c)
+          scatter8(nxt, c, nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]));
+        if (kk == 3) store_dy(nxt, yr);
+      }
+      load_dy(cl(st + 2), yr);
+      cn = cnn;
+      load_codes(cl(st + 3), cnn);
+      __syncthreads();
+    }
   }
 
-  // --- adapter rows: gs [M, 2r] against [A ; A] ---
+  // --- adapter rows: gs [M, 2r] against [A ; A] (last split only) ---
   const int r = p.r;
-  const int ext_tiles = (2 * r + RT - 1) / RT;
-  for (int e = 0; e < ext_tiles; ++e) {
-    // W^T side: reduction row c = e*64 + wr is A's row (c mod r), zero past 2r
-    const int c = e * RT + wr;
-    u32x4_t v8[8];
-    const bool row_ok = c < 2 * r && kcol_ok;
-    const int arow = c < r ? c : c - r;
+  if (z == p.splits - 1) {
+    const int ext_tiles = (2 * r + RT - 1) / RT;
+    const int64_t m = clamp_row(m0 + t, M);
+    for (int e = 0; e < ext_tiles; ++e) {
+      // W^T side: reduction row c = e*64 + wr is A's row (c mod r), zero past 2r
+      const int c = e * RT + wr;
+      const bool row_ok = c < 2 * r;
+      const int arow = c < r ? c : c - r;
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      v8[q] = row_ok ? *reinterpret_cast<const u32x4_t*>(p.A + (int64_t)arow * K + kcol + 8 * q) : zero;
-    scatter_row(0, v8);
-    // dy side: rows m, columns c of gs
-    const int64_t m = m0 + t;
+      for (int q = 0; q < 8; ++q)
+        scatter8(0, q, row_ok ? *reinterpret_cast<const u32x4_t*>(p.A + (int64_t)arow * K + kcol + 8 * q)
+                              : zero);
+      // dy side: rows m, columns c of gs
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int col = e * RT + 8 * q;
-      dyt[0][rk(t, q)] = (m < M && col < 2 * r)
-                             ? *reinterpret_cast<const u32x4_t*>(p.gs + m * 2 * r + col)
-                             : zero;
+      for (int q = 0; q < 8; ++q) {
+        const int col = e * RT + 8 * q;
+        dyt[0][rk(t, q)] =
+            col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.gs + m * 2 * r + col) : zero;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) mfma_step(0, kk);
+      __syncthreads();
     }
-    __syncthreads();
-    compute(0);
-    __syncthreads();
   }
 
   // --- epilogue: D[k][m]; lane holds m = lr, k = 8(v/4) + 4 lg + v%4 ---
@@ -195,11 +222,16 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t k = k0 + 128 * wk + 32 * i + 8 * q + 4 * lg;
-        if (k < K) {
+        if (k >= K) continue;
+        if (p.splits == 1) {
           u32x2_t o;
           o[0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
           o[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           *reinterpret_cast<u32x2_t*>(p.dx + m * K + k) = o;
+        } else {
+          f32x4_t o = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                       acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4_t*>(p.part + ((int64_t)z * M + m) * K + k) = o;
         }
       }
     }
@@ -208,8 +240,8 @@ void dx_gemm_kernel(DxParams p) {
 
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
-                          uint16_t* dx, int64_t M, int64_t N, int64_t K, int r,
-                          const Nf4Levels& L, hipStream_t s) {
+                          uint16_t* dx, float* part, int splits, int64_t M, int64_t N, int64_t K,
+                          int r, const Nf4Levels& L, hipStream_t s) {
   DxParams p;
   p.codes = codes;
   p.qscale = qscale;
@@ -218,14 +250,19 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.gs = gs;
   p.A = A;
   p.dx = dx;
+  p.part = part;
   p.M = M;
   p.N = N;
   p.K = K;
   p.r = r;
+  p.splits = splits;
   p.L = L;
-  dim3 grid((unsigned)((K + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE));
+  dim3 grid((unsigned)((K + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE),
+            (unsigned)splits);
   hipLaunchKernelGGL(dx_gemm_kernel, grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(part, splits, M * K, dx, s);
 }
 
 }  // namespace qlora

@@ -2,21 +2,31 @@
 //
 // [QLoRA / infivelines.com]: the 4-bit base is dequantised to bf16 one block
 // at a time inside the matrix multiply, and the adapters stay in full
-// precision.  Here one 64-wide k tile of a weight row is exactly one NF4
-// block, so each thread decodes one block per k tile into LDS with that
-// block's own 16-entry table, and the tile feeds bf16 MFMA (32x32x16,
-// fp32 accumulate) with the activation tile.
+// precision.  One 64-wide k tile of a weight row is exactly one NF4 block,
+// so each thread decodes one block per k tile into LDS with that block's own
+// 16-entry table, and the tile feeds bf16 MFMA (32x32x16, fp32 accumulate)
+// together with the activation tile.
 //
 // The adapter term rides on the same accumulators: with xs = [hi | lo] the
 // bf16 split of s . x . A^T (hi + lo equals the fp32 value to 2^-17), the
-// product xs . [B | B]^T is run as 2r extra reduction columns after the
-// base reduction, so y is rounded to bf16 exactly once.
+// product xs . [B | B]^T runs as 2r extra reduction columns after the base
+// reduction, so y is rounded to bf16 exactly once.
 //
 // Block tile 256 (n) x 256 (m) x 64 (k); 4 waves in a 2 x 2 grid, each a
-// 128 x 128 sub-tile as 4 x 4 MFMA tiles (256 accumulators per lane, one
-// wave per SIMD).  LDS holds two stages of (W tile, x tile), 128 KiB; the
-// next tile's global loads are in flight while the current one is
-// multiplied.
+// 128 x 128 sub-tile of 4 x 4 MFMA tiles (256 fp32 accumulators per lane,
+// one wave per SIMD).  Two LDS stages of (W tile, x tile), 128 KiB.
+//
+// Pipeline per k tile: the MFMAs of tile t run from LDS stage t&1 while the
+// same waves decode tile t+1's codes (loaded one tile earlier) into the
+// other stage, one quarter of the decode after each quarter of the MFMAs,
+// so the matrix cores and the vector ALUs work at the same time.  Codes are
+// fetched two tiles ahead and x one tile ahead.  Out-of-range rows are
+// clamped to the last valid row instead of branched around, so the loop
+// body is a single basic block; their results are never stored.
+//
+// When the output has too few tiles to fill the chip, the k range is split
+// over gridDim.z blocks that write fp32 partials; fwd_reduce adds them in a
+// fixed order and rounds once.
 
 #include "device_common.h"
 #include "launch.h"
@@ -37,9 +47,11 @@ struct FwdParams {
   const uint16_t* x;
   const uint16_t* xs;
   const uint16_t* B;
-  uint16_t* y;
+  uint16_t* y;     // bf16 output (splits == 1)
+  float* part;     // fp32 partials [splits][M][N] (splits > 1)
   int64_t M, N, K;
   int r;
+  int splits;
   Nf4Levels L;
 };
 
@@ -47,6 +59,8 @@ struct FwdParams {
 // so that 8 consecutive rows read at the same logical chunk hit 8 distinct
 // chunk positions (all banks).
 __device__ __forceinline__ int rk(int row, int chunk) { return row * ROW_CHUNKS + (chunk ^ (row & 7)); }
+
+__device__ __forceinline__ int64_t clamp_row(int64_t v, int64_t hi) { return v < hi ? v : hi - 1; }
 
 }  // namespace
 
@@ -58,8 +72,13 @@ void fwd_gemm_kernel(FwdParams p) {
   const int wn = wave & 1, wm = wave >> 1;
   const int64_t n0 = (int64_t)blockIdx.x * TILE;
   const int64_t m0 = (int64_t)blockIdx.y * TILE;
+  const int z = blockIdx.z;
   const int64_t M = p.M, N = p.N, K = p.K;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  // k tiles of this split
+  const int64_t nkt = K / KT;
+  const int64_t kt0 = nkt * z / p.splits, kt1 = nkt * (z + 1) / p.splits;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -69,87 +88,116 @@ void fwd_gemm_kernel(FwdParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // --- per-thread staging registers for one k tile ---
-  u32x4_t xr[8];
-  u32x4_t cr[2];
-  float wscale;
-  const int64_t wrow = n0 + t;          // this thread decodes W row n0 + t
-  const bool wrow_ok = wrow < N;
+  // this thread decodes weight row n0 + t (clamped) and stages x rows
+  // m0 + (t >> 3) + 32 j, chunk t & 7
+  const int64_t wrow = clamp_row(n0 + t, N);
+  const uint8_t* wcodes = p.codes + ((wrow * K) >> 1);
+  const int64_t wblk0 = (wrow * K) >> 6;
+  // x rows m0 + (t >> 3) + 32 j through a buffer descriptor: rows past M
+  // read as zero
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(p.x, (uint32_t)(M * K * 2));
+  const uint32_t xoff = (uint32_t)(((m0 + (t >> 3)) * K + 8 * (t & 7)) * 2);
+  const uint32_t xrow_step = (uint32_t)(32 * K * 2);
 
-  auto load_tile = [&](int64_t kt) {
-    const int64_t k0 = kt * KT;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t m = m0 + (t >> 3) + 32 * j;
-      xr[j] = (m < M) ? *reinterpret_cast<const u32x4_t*>(p.x + m * K + k0 + 8 * (t & 7)) : zero;
-    }
-    if (wrow_ok) {
-      const int64_t idx = wrow * K + k0;  // first element of the block
-      const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
-      cr[0] = cp[0];
-      cr[1] = cp[1];
-      wscale = nf4_block_scale(p.qscale[idx >> 6], p.step[idx >> 14]);
-    } else {
-      cr[0] = zero;
-      cr[1] = zero;
-      wscale = 0.0f;
-    }
+  struct Codes {
+    u32x4_t c0, c1;
+    float s;
   };
-  auto store_tile = [&](int stage) {
+  auto load_codes = [&](int64_t kt, Codes& c) {
+    const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(wcodes + kt * (KT / 2));
+    c.c0 = cp[0];
+    c.c1 = cp[1];
+    const int64_t b = wblk0 + kt;
+    c.s = nf4_block_scale(p.qscale[b], p.step[b >> 8]);
+  };
+  auto load_x = [&](int64_t kt, u32x4_t (&xr)[8]) {
+    const uint32_t o = xoff + (uint32_t)(kt * KT * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xr[j] = buffer_load16(xres, o + j * xrow_step);
+  };
+  auto store_x = [&](int stage, const u32x4_t (&xr)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) lds[stage][1][rk((t >> 3) + 32 * j, t & 7)] = xr[j];
-    const Nf4Lut lut = nf4_make_lut(p.L, wscale);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) lds[stage][0][rk(t, c)] = nf4_decode8(lut, cr[c >> 2][c & 3]);
   };
-  auto compute = [&](int stage) {
+  auto mfma_step = [&](int stage, int kk) {
+    const int ch = 2 * kk + lg;
+    u32x4_t a[4], b[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 2 * kk + lg;
-      u32x4_t a[4], b[4];
+    for (int i = 0; i < 4; ++i) a[i] = lds[stage][0][rk(128 * wn + 32 * i + lr, ch)];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds[stage][0][rk(128 * wn + 32 * i + lr, ch)];
+    for (int j = 0; j < 4; ++j) b[j] = lds[stage][1][rk(128 * wm + 32 * j + lr, ch)];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lds[stage][1][rk(128 * wm + 32 * j + lr, ch)];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
-    }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
   };
 
-  const int64_t nkt = K / KT;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nkt; ++kt) {
-    const int cur = (int)(kt & 1);
-    if (kt + 1 < nkt) load_tile(kt + 1);
-    compute(cur);
-    if (kt + 1 < nkt) store_tile(cur ^ 1);
+  if (kt0 < kt1) {
+    // prologue: tile kt0 into stage 0; x of kt0+1 and codes of kt0+1, kt0+2
+    // in flight.  Prefetch indices are clamped into the split, so the loop
+    // issues its loads unconditionally (past the end they re-read the last
+    // tile and their results are never used).
+    const int64_t last = kt1 - 1;
+    auto cl = [&](int64_t v) { return v < last ? v : last; };
+    Codes cn, cnn;
+    u32x4_t xr[8];
+    load_codes(kt0, cn);
+    load_x(kt0, xr);
+    store_x(0, xr);
+    {
+      const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        lds[0][0][rk(t, c)] = nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]);
+    }
+    load_codes(cl(kt0 + 1), cn);
+    load_x(cl(kt0 + 1), xr);
+    load_codes(cl(kt0 + 2), cnn);
     __syncthreads();
+
+    for (int64_t kt = kt0; kt < kt1; ++kt) {
+      const int cur = (int)((kt - kt0) & 1), nxt = cur ^ 1;
+      // tile kt+1 is decoded into the other stage while tile kt multiplies;
+      // on the last tile this decodes a repeat into a stage nobody reads
+      const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        mfma_step(cur, kk);
+#pragma unroll
+        for (int c = 2 * kk; c < 2 * kk + 2; ++c)
+          lds[nxt][0][rk(t, c)] = nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]);
+        if (kk == 3) store_x(nxt, xr);
+      }
+      load_x(cl(kt + 2), xr);
+      cn = cnn;
+      load_codes(cl(kt + 3), cnn);
+      __syncthreads();
+    }
   }
 
-  // --- adapter columns: xs [M, 2r] against [B | B] ---
+  // --- adapter columns: xs [M, 2r] against [B | B] (last split only) ---
   const int r = p.r;
-  const int ext_tiles = (2 * r + KT - 1) / KT;
-  for (int e = 0; e < ext_tiles; ++e) {
-    const int64_t m = m0 + t;
+  if (z == p.splits - 1) {
+    const int ext_tiles = (2 * r + KT - 1) / KT;
+    const int64_t m = clamp_row(m0 + t, M);
+    for (int e = 0; e < ext_tiles; ++e) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int col = e * KT + 8 * c;
-      u32x4_t wv = zero, xv = zero;
-      if (col < 2 * r) {
-        const int j = col < r ? col : col - r;
-        if (wrow_ok) wv = *reinterpret_cast<const u32x4_t*>(p.B + wrow * r + j);
-        if (m < M) xv = *reinterpret_cast<const u32x4_t*>(p.xs + m * 2 * r + col);
+      for (int c = 0; c < 8; ++c) {
+        const int col = e * KT + 8 * c;
+        u32x4_t wv = zero, xv = zero;
+        if (col < 2 * r) {
+          const int j = col < r ? col : col - r;
+          wv = *reinterpret_cast<const u32x4_t*>(p.B + wrow * r + j);
+          xv = *reinterpret_cast<const u32x4_t*>(p.xs + m * 2 * r + col);
+        }
+        lds[0][0][rk(t, c)] = wv;
+        lds[0][1][rk(t, c)] = xv;
       }
-      lds[0][0][rk(t, c)] = wv;
-      lds[0][1][rk(t, c)] = xv;
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) mfma_step(0, kk);
+      __syncthreads();
     }
-    __syncthreads();
-    compute(0);
-    __syncthreads();
   }
 
   // --- epilogue: D[n][m]; lane holds m = lr, n = 8(v/4) + 4 lg + v%4 ---
@@ -162,21 +210,69 @@ void fwd_gemm_kernel(FwdParams p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t n = n0 + 128 * wn + 32 * i + 8 * q + 4 * lg;
-        if (n < N) {
+        if (n >= N) continue;
+        if (p.splits == 1) {
           u32x2_t o;
           o[0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
           o[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
           *reinterpret_cast<u32x2_t*>(p.y + m * N + n) = o;
+        } else {
+          f32x4_t o = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                       acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4_t*>(p.part + ((int64_t)z * M + m) * N + n) = o;
         }
       }
     }
   }
 }
 
+// out[i] = bf16(sum_z part[z][i]), i over M*N (4 per thread), fixed order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, int64_t count,
+                                                            uint16_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < count; i += stride) {
+    f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + i);
+    for (int z = 1; z < splits; ++z) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + (int64_t)z * count + i);
+      s[0] += v[0];
+      s[1] += v[1];
+      s[2] += v[2];
+      s[3] += v[3];
+    }
+    u32x2_t o;
+    o[0] = pack_bf16x2(s[0], s[1]);
+    o[1] = pack_bf16x2(s[2], s[3]);
+    *reinterpret_cast<u32x2_t*>(out + i) = o;
+  }
+}
+
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, uint16_t* out,
+                                hipStream_t s) {
+  int64_t g = (count / 4 + 255) / 256;
+  if (g > 8192) g = 8192;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)g), dim3(256), 0, s, part, splits,
+                     count, out);
+  return hipGetLastError();
+}
+
+// Split the k range when the output tiles alone cannot fill the chip:
+// aim for ~256 blocks, at least 4 k tiles per split.
+int gemm_splits(int64_t M, int64_t N, int64_t Kred) {
+  const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
+  const int64_t nkt = Kred / KT;
+  if (tiles >= 192) return 1;
+  int64_t s = 256 / tiles;
+  if (s > nkt / 4) s = nkt / 4;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : (int)s;
+}
+
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                            const uint16_t* x, const uint16_t* xs, const uint16_t* B,
-                           uint16_t* y, int64_t M, int64_t N, int64_t K, int r,
-                           const Nf4Levels& L, hipStream_t s) {
+                           uint16_t* y, float* part, int splits, int64_t M, int64_t N, int64_t K,
+                           int r, const Nf4Levels& L, hipStream_t s) {
   FwdParams p;
   p.codes = codes;
   p.qscale = qscale;
@@ -185,14 +281,19 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.xs = xs;
   p.B = B;
   p.y = y;
+  p.part = part;
   p.M = M;
   p.N = N;
   p.K = K;
   p.r = r;
+  p.splits = splits;
   p.L = L;
-  dim3 grid((unsigned)((N + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE));
+  dim3 grid((unsigned)((N + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE),
+            (unsigned)splits);
   hipLaunchKernelGGL(fwd_gemm_kernel, grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_splitk_reduce(part, splits, M * N, y, s);
 }
 
 }  // namespace qlora

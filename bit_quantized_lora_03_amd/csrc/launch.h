@@ -36,25 +36,32 @@ hipError_t launch_tn_gemm(const uint16_t* U0, const uint16_t* U1, int64_t ldu,
                           const uint16_t* V0, const uint16_t* V1, int64_t ldv, int64_t M,
                           int64_t P, int64_t Q, float* C, int accumulate, hipStream_t s);
 
-// gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T
+// gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T.  With splits > 1 the
+// k range is split over blocks writing fp32 partials part[splits][M][N],
+// reduced to bf16 y by a second kernel.
+int gemm_splits(int64_t M, int64_t N, int64_t Kred);
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                            const uint16_t* x, const uint16_t* xs, const uint16_t* B,
-                           uint16_t* y, int64_t M, int64_t N, int64_t K, int r,
-                           const Nf4Levels& L, hipStream_t s);
+                           uint16_t* y, float* part, int splits, int64_t M, int64_t N, int64_t K,
+                           int r, const Nf4Levels& L, hipStream_t s);
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, uint16_t* out,
+                                hipStream_t s);
 
-// gemm_decode.hip -- forward for M <= 32: split-K partials part[S][M][N],
-// then y = bf16(sum part + scale . (sum_z P[z]) . B^T)
+// gemm_decode.hip -- forward for M <= 32: split-K partials
+// part[S][M][N + r] (columns N.. hold x . A^T), then
+// y = bf16(sum part + scale . xa . B^T)
 constexpr int kDecodeMaxM = 32;
-int decode_splits(int64_t N, int64_t K);
+int decode_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                             const uint16_t* x, const float* P, int psplits, const uint16_t* B,
-                             int r, float scale, float* part, int splits, uint16_t* y, int64_t M,
+                             const uint16_t* x, const uint16_t* A, const uint16_t* B, int r,
+                             float scale, float* part, int splits, uint16_t* y, int64_t M,
                              int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s);
 
-// gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]
+// gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]; splits > 1 as in the
+// forward GEMM (partials [splits][M][K])
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
-                          uint16_t* dx, int64_t M, int64_t N, int64_t K, int r,
-                          const Nf4Levels& L, hipStream_t s);
+                          uint16_t* dx, float* part, int splits, int64_t M, int64_t N, int64_t K,
+                          int r, const Nf4Levels& L, hipStream_t s);
 
 }  // namespace qlora

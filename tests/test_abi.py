@@ -57,12 +57,18 @@ def test_status_strings():
 
 def test_workspace_sizes():
     ws = q.workspace_bytes
-    assert ws(0, 512, 4096, 4096, 0) == 0
-    assert ws(1, 512, 4096, 4096, 0) == 0
+    # many output tiles, no adapter: one kernel, no scratch
+    assert ws(0, 4096, 22016, 8192, 0) == 0
+    assert ws(1, 4096, 22016, 8192, 0) == 0
+    # few output tiles: fp32 split-K partials even without an adapter
+    assert ws(0, 512, 4096, 4096, 0) >= 512 * 4096 * 4 * 2
     f = ws(0, 512, 4096, 4096, 16)
     b = ws(1, 512, 4096, 4096, 16)
-    assert f > 0 and b > f and f % 256 == 0 and b % 256 == 0
-    assert f >= 512 * 32 * 2                      # at least the hi/lo split of x.A^T
+    assert f > 0 and b > 0 and f % 256 == 0 and b % 256 == 0
+    assert f >= 512 * 32 * 2 + ws(0, 512, 4096, 4096, 0)   # + the hi/lo split of x.A^T
+    # few tokens: the decode path keeps k-split partials of x.W'^T and x.A^T
+    d = ws(0, 16, 8192, 8192, 64)
+    assert d >= 16 * (8192 + 64) * 4 and d % 256 == 0
     assert ws(0, 16, 100, 4096, 16) == 0          # N % 64
     assert ws(0, 16, 4096, 100, 16) == 0          # K % 64
     assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
