@@ -116,6 +116,33 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint3
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// Block-to-tile mapping for a 1-D grid of `total` blocks.  Consecutive
+// workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2),
+// so id i is first turned into a rank that is contiguous within its XCD;
+// ranks are then walked in groups of `group_m` row tiles (column tiles
+// fastest within a group), so the blocks resident on one XCD share a few
+// activation tiles and a few weight tiles at every k step.
+struct TileCoord {
+  int64_t m, n, z;
+};
+__device__ __forceinline__ TileCoord xcd_tile(int64_t id, int64_t total, int64_t m_tiles,
+                                              int64_t n_tiles, int group_m) {
+  constexpr int kXcd = 8;
+  const int64_t xcd = id % kXcd, slot = id / kXcd;
+  const int64_t per = total / kXcd, extra = total % kXcd;
+  const int64_t rank = xcd * per + (xcd < extra ? xcd : extra) + slot;
+  const int64_t tiles = m_tiles * n_tiles;
+  TileCoord c;
+  c.z = rank / tiles;
+  const int64_t tr = rank - c.z * tiles;
+  const int64_t span = (int64_t)group_m * n_tiles;
+  const int64_t g = tr / span, w = tr - g * span;
+  const int64_t gm = (m_tiles - g * group_m) < group_m ? (m_tiles - g * group_m) : group_m;
+  c.m = g * group_m + w % gm;
+  c.n = w / gm;
+  return c;
+}
+
 // MFMA wrappers (gfx950 bf16, fp32 accumulate).
 __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);

@@ -23,6 +23,8 @@
 // around, and small outputs split the reduction over gridDim.z blocks that
 // write fp32 partials.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -73,9 +75,11 @@ void dx_gemm_kernel(DxParams p) {
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int wk = wave & 1, wm = wave >> 1;
-  const int64_t k0 = (int64_t)blockIdx.x * TILE;
-  const int64_t m0 = (int64_t)blockIdx.y * TILE;
   const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t m_tiles = (M + TILE - 1) / TILE, k_tiles = (K + TILE - 1) / TILE;
+  const TileCoord tc = xcd_tile(blockIdx.x, (int64_t)gridDim.x, m_tiles, k_tiles, 4);
+  const int64_t k0 = tc.n * TILE;
+  const int64_t m0 = tc.m * TILE;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   f32x16_t acc[4][4];
@@ -86,7 +90,7 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int z = blockIdx.z;
+  const int z = (int)tc.z;
   const int64_t nst = N / RT;
   const int64_t st0 = nst * z / p.splits, st1 = nst * (z + 1) / p.splits;
 
@@ -149,25 +153,32 @@ void dx_gemm_kernel(DxParams p) {
   };
 
   if (st0 < st1) {
+    // Register sets indexed by slab parity (relative to st0), loaded at the
+    // top of the iteration two slabs ahead into the set that was just
+    // consumed; the loop is unrolled by two so the parity is a constant and
+    // no register holding an in-flight load is copied.
     const int64_t last = st1 - 1;
     auto cl = [&](int64_t v) { return v < last ? v : last; };
-    Codes cn, cnn;
-    u32x4_t yr[8];
-    load_codes(st0, cn);
-    load_dy(st0, yr);
-    store_dy(0, yr);
+    Codes C[2];
+    u32x4_t Y[2][8];
+    load_codes(st0, C[0]);
+    load_dy(st0, Y[0]);
+    store_dy(0, Y[0]);
     {
-      const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
+      const Nf4Lut lut = nf4_make_lut(p.L, C[0].s);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) scatter8(0, c, nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]));
+      for (int c = 0; c < 8; ++c)
+        scatter8(0, c, nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]));
     }
-    load_codes(cl(st0 + 1), cn);
-    load_dy(cl(st0 + 1), yr);
-    load_codes(cl(st0 + 2), cnn);
+    load_dy(cl(st0 + 1), Y[1]);
+    load_codes(cl(st0 + 1), C[1]);
     __syncthreads();
 
-    for (int64_t st = st0; st < st1; ++st) {
-      const int cur = (int)((st - st0) & 1), nxt = cur ^ 1;
+    auto iteration = [&](int64_t st, auto parity) {
+      constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
+      load_dy(cl(st + 2), Y[cur]);
+      load_codes(cl(st + 2), C[cur]);
+      const Codes& cn = C[nxt];
       const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -175,12 +186,13 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
         for (int c = 2 * kk; c < 2 * kk + 2; ++c)
           scatter8(nxt, c, nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]));
-        if (kk == 3) store_dy(nxt, yr);
+        if (kk == 3) store_dy(nxt, Y[nxt]);
       }
-      load_dy(cl(st + 2), yr);
-      cn = cnn;
-      load_codes(cl(st + 3), cnn);
       __syncthreads();
+    };
+    for (int64_t st = st0; st < st1; st += 2) {
+      iteration(st, std::integral_constant<int, 0>());
+      if (st + 1 < st1) iteration(st + 1, std::integral_constant<int, 1>());
     }
   }
 
@@ -257,9 +269,8 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.r = r;
   p.splits = splits;
   p.L = L;
-  dim3 grid((unsigned)((K + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE),
-            (unsigned)splits);
-  hipLaunchKernelGGL(dx_gemm_kernel, grid, dim3(256), 0, s, p);
+  const int64_t blocks = ((K + TILE - 1) / TILE) * ((M + TILE - 1) / TILE) * splits;
+  hipLaunchKernelGGL(dx_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, M * K, dx, s);

@@ -28,6 +28,8 @@
 // over gridDim.z blocks that write fp32 partials; fwd_reduce adds them in a
 // fixed order and rounds once.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -70,10 +72,12 @@ void fwd_gemm_kernel(FwdParams p) {
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int wn = wave & 1, wm = wave >> 1;
-  const int64_t n0 = (int64_t)blockIdx.x * TILE;
-  const int64_t m0 = (int64_t)blockIdx.y * TILE;
-  const int z = blockIdx.z;
   const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t m_tiles = (M + TILE - 1) / TILE, n_tiles = (N + TILE - 1) / TILE;
+  const TileCoord tc = xcd_tile(blockIdx.x, (int64_t)gridDim.x, m_tiles, n_tiles, 4);
+  const int64_t n0 = tc.n * TILE;
+  const int64_t m0 = tc.m * TILE;
+  const int z = (int)tc.z;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   // k tiles of this split
@@ -133,45 +137,123 @@ void fwd_gemm_kernel(FwdParams p) {
   };
 
   if (kt0 < kt1) {
-    // prologue: tile kt0 into stage 0; x of kt0+1 and codes of kt0+1, kt0+2
-    // in flight.  Prefetch indices are clamped into the split, so the loop
-    // issues its loads unconditionally (past the end they re-read the last
-    // tile and their results are never used).
+    // Register sets are indexed by tile parity (relative to kt0): X[q] and
+    // C[q] hold the x rows and codes of a tile with parity q.  At the top of
+    // iteration kt the set of parity(kt) is free (tile kt already sits in
+    // LDS), so tile kt+2 is loaded into it there; tile kt+1's set, loaded an
+    // iteration earlier, is decoded and written into the other LDS stage.
+    // The loop is unrolled by two so the parity is a constant and no
+    // register holding an in-flight load is ever copied (a copy would make
+    // the compiler wait for the load).  Prefetch indices are clamped into
+    // the split, so loads are unconditional.
     const int64_t last = kt1 - 1;
     auto cl = [&](int64_t v) { return v < last ? v : last; };
-    Codes cn, cnn;
-    u32x4_t xr[8];
-    load_codes(kt0, cn);
-    load_x(kt0, xr);
-    store_x(0, xr);
+    Codes C[2];
+    u32x4_t X[2][8];
+    load_codes(kt0, C[0]);
+    load_x(kt0, X[0]);
+    store_x(0, X[0]);
     {
-      const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
+      const Nf4Lut lut = nf4_make_lut(p.L, C[0].s);
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        lds[0][0][rk(t, c)] = nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]);
+        lds[0][0][rk(t, c)] = nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]);
     }
-    load_codes(cl(kt0 + 1), cn);
-    load_x(cl(kt0 + 1), xr);
-    load_codes(cl(kt0 + 2), cnn);
+    load_x(cl(kt0 + 1), X[1]);
+    load_codes(cl(kt0 + 1), C[1]);
     __syncthreads();
 
-    for (int64_t kt = kt0; kt < kt1; ++kt) {
-      const int cur = (int)((kt - kt0) & 1), nxt = cur ^ 1;
-      // tile kt+1 is decoded into the other stage while tile kt multiplies;
-      // on the last tile this decodes a repeat into a stage nobody reads
-      const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
+    // Hand-scheduled iteration.  Issue is in order, so back-to-back MFMAs
+    // would hold everything behind them; instead each of the 64 MFMAs of a
+    // tile is followed by one small unit of other work and a scheduling
+    // fence: the next k-step's operand reads, a slice of the decode of tile
+    // kt+1 into the other stage, its LDS writes.  The vector work then
+    // executes while the matrix core is busy.
+    auto iteration = [&](int64_t kt, auto parity) {
+      constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
+      // tile kt+2 into the free set (loads issued first, used an iteration later)
+      load_x(cl(kt + 2), X[cur]);
+      load_codes(cl(kt + 2), C[cur]);
+      const Codes& cn = C[nxt];
+      u32x4_t op[2][2][4];  // [buffer][a|b][i]
+      auto read_ops = [&](int kk, int buf, int which, int i) {
+        const int ch = 2 * kk + lg;
+        if (which == 0)
+          op[buf][0][i] = lds[cur][0][rk(128 * wn + 32 * i + lr, ch)];
+        else
+          op[buf][1][i] = lds[cur][1][rk(128 * wm + 32 * i + lr, ch)];
+      };
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        read_ops(0, 0, 0, i);
+        read_ops(0, 0, 1, i);
+      }
+      uint32_t pk[8];
+      Nf4Lut lut;
+      uint32_t dn1 = 0;
+      u32x4_t dv = zero;
+      auto unit = [&](int kk, int s) {
+        // operand reads for step kk+1 in slots 8..15
+        if (kk < 3 && s >= 8) read_ops(kk + 1, (kk + 1) & 1, (s - 8) >> 2, (s - 8) & 3);
+        if (kk == 0) {
+          // the 16-entry table of tile kt+1's block (slots 0..7)
+          if (s < 4) {
+            pk[2 * s] = pack_bf16x2(p.L.v[4 * s] * cn.s, p.L.v[4 * s + 1] * cn.s);
+            pk[2 * s + 1] = pack_bf16x2(p.L.v[4 * s + 2] * cn.s, p.L.v[4 * s + 3] * cn.s);
+          } else if (s < 8) {
+            const int j = s - 4;
+            lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
+            lut.hi[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
+          }
+        }
+        // decode chunks 2kk, 2kk+1 of tile kt+1: three units each
+        const int base = kk == 0 ? 8 : 0;
+        const int u = s - base;
+        if (u >= 0 && u < 6) {
+          const int c = 2 * kk + u / 3;
+          const uint32_t v = (c < 4 ? cn.c0 : cn.c1)[c & 3];
+          switch (u % 3) {
+            case 0: {
+              const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
+              const uint32_t dn0 = perm(od, ev, 0x05010400u);
+              dn1 = perm(od, ev, 0x07030602u);
+              uint32_t o0, o1;
+              nf4_lookup4(lut, dn0, o0, o1);
+              dv[0] = o0;
+              dv[1] = o1;
+              break;
+            }
+            case 1: {
+              uint32_t o2, o3;
+              nf4_lookup4(lut, dn1, o2, o3);
+              dv[2] = o2;
+              dv[3] = o3;
+              break;
+            }
+            default:
+              lds[nxt][0][rk(t, c)] = dv;
+              break;
+          }
+        }
+        // tile kt+1's x rows into the other stage
+        if (kk == 3 && s >= 6 && s < 14)
+          lds[nxt][1][rk((t >> 3) + 32 * (s - 6), t & 7)] = X[nxt][s - 6];
+      };
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        mfma_step(cur, kk);
 #pragma unroll
-        for (int c = 2 * kk; c < 2 * kk + 2; ++c)
-          lds[nxt][0][rk(t, c)] = nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]);
-        if (kk == 3) store_x(nxt, xr);
+        for (int s = 0; s < 16; ++s) {
+          const int i = s >> 2, j = s & 3;
+          acc[i][j] = mfma32x32x16(op[kk & 1][0][i], op[kk & 1][1][j], acc[i][j]);
+          unit(kk, s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      load_x(cl(kt + 2), xr);
-      cn = cnn;
-      load_codes(cl(kt + 3), cnn);
       __syncthreads();
+    };
+    for (int64_t kt = kt0; kt < kt1; kt += 2) {
+      iteration(kt, std::integral_constant<int, 0>());
+      if (kt + 1 < kt1) iteration(kt + 1, std::integral_constant<int, 1>());
     }
   }
 
@@ -288,9 +370,8 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.r = r;
   p.splits = splits;
   p.L = L;
-  dim3 grid((unsigned)((N + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE),
-            (unsigned)splits);
-  hipLaunchKernelGGL(fwd_gemm_kernel, grid, dim3(256), 0, s, p);
+  const int64_t blocks = ((N + TILE - 1) / TILE) * ((M + TILE - 1) / TILE) * splits;
+  hipLaunchKernelGGL(fwd_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, M * N, y, s);
