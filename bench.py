@@ -81,6 +81,46 @@ def make_layer(name):
     raise SystemExit(f"unknown workload {name}")
 
 
+def _gemm_splits(M, N, Kred):
+    """Mirror of the library's k-split choice for the fused GEMMs (for naming
+    the launches in the roofline line only)."""
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    nkt = Kred // 64
+    if tiles >= 192:
+        return 1
+    s = min(256 // tiles, nkt // 4, 16)
+    return max(1, s)
+
+
+def _source_digest(key):
+    """Hash of the kernel sources a recorded traffic figure was taken with."""
+    import hashlib
+    files = {"fwd": ["gemm_fwd.hip"], "dx": ["gemm_bwd.hip", "gemm_fwd.hip"],
+             "decode": ["gemm_decode.hip"]}[key] + ["device_common.h"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "bit_quantized_lora_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _recorded_traffic(workload, key):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (profiles/traffic.md), or None when absent or taken with kernel
+    sources that differ from the current ones."""
+    path = os.path.join(ROOT, "profiles", "traffic.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("TRAFFIC "):
+            rec = json.loads(line[len("TRAFFIC "):])
+            if rec.get("workload") == workload and rec.get("key") == key:
+                if rec.get("src") != _source_digest(key):
+                    return None
+                return rec.get("bytes_per_launch")
+    return None
+
+
 def cpu_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -303,21 +343,32 @@ def main():
     if "bwd" in kind:
         ops["dx_gemm_alone_ms"] = k_dx
 
-    if M <= 64:
+    # the unit the roofline line is about: one base-only fused-GEMM call (the
+    # GEMM kernel, plus its split-K reduce kernel when the output is small)
+    fsplit = _gemm_splits(M, N, K)
+    dsplit = _gemm_splits(M, K, N)
+    if M <= 32:
         # decode: HBM-bound; algorithmic bytes of the base-only launch
         kb = packed_weight_bytes(N, K) + 2 * M * K + 2 * M * N
         ach = kb / (k_fwd * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBPS, "traffic": None,
-                "kernel": "fwd_gemm_kernel (base only)", "per_launch": kb}
+                "kernel": "decode_main_kernel + decode_reduce_kernel (base only)",
+                "per_launch": kb, "duration_ms": k_fwd}
+        key = "decode"
     else:
-        name, t_k, fl = ("fwd_gemm_kernel", k_fwd, 2 * M * N * K)
+        name, t_k, fl, sp = ("fwd_gemm_kernel", k_fwd, 2 * M * N * K, fsplit)
+        key = "fwd"
         if "bwd" in kind and k_dx > k_fwd:
-            name, t_k, fl = ("dx_gemm_kernel", k_dx, 2 * M * N * K)
+            name, t_k, fl, sp = ("dx_gemm_kernel", k_dx, 2 * M * N * K, dsplit)
+            key = "dx"
+        if sp > 1:
+            name += f" + splitk_reduce_kernel (k split {sp})"
         ach = fl / (t_k * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": name + " (base only)",
-                "per_launch": fl}
+                "per_launch": fl, "duration_ms": t_k}
+    roof["traffic"] = _recorded_traffic(args.workload, key)
 
     cpu = None
     if not args.no_cpu_baseline:
