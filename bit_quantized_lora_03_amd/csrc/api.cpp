@@ -61,7 +61,7 @@ int check_rank(int32_t r) {
 // ---- workspace layout --------------------------------------------------
 struct FwdWs {
   size_t p_off, xs_off, part_off, total;
-  int splits;    // k splits of the adapter down-projection partials
+  int psplits;   // k splits of the adapter down-projection (1: no partials)
   int dsplits;   // k splits of the decode path
   int gsplits;   // k splits of the fused GEMM (1: no partials)
   bool decode;   // few tokens: split-K decode path
@@ -80,9 +80,10 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   }
   size_t off = 0;
   if (r > 0) {
-    L.splits = qlora::lora_down_splits(M, K, r);
+    // fp32 k-split partials of x . A^T, then xs = [hi | lo] of s . x . A^T: [M][2r] bf16
+    L.psplits = qlora::lora_proj_splits(M, K, r, 1);
     L.p_off = 0;
-    L.xs_off = round_up((size_t)L.splits * M * r * sizeof(float), 256);
+    L.xs_off = L.psplits > 1 ? round_up((size_t)L.psplits * M * r * sizeof(float), 256) : 0;
     off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
   }
   L.gsplits = qlora::gemm_splits(M, N, K);
@@ -95,8 +96,9 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t pa_off, bt_off, pg_off, xs_off, gs_off, part_off, total;
-  int splits_a, splits_g;
+  size_t pa_off, pg_off, xs_off, gs_off, cb_off, ca_off, part_off, total;
+  int psplits;  // k splits of the two down-projections (1: no partials)
+  int tsplits;  // token splits of the dA / dB reductions (1: no partials)
   int gsplits;  // reduction splits of the dX GEMM (1: no partials)
 };
 BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
@@ -105,14 +107,24 @@ BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M == 0) return L;
   size_t off = 0;
   if (r > 0) {
-    L.splits_a = qlora::lora_down_splits(M, K, r);
-    L.splits_g = qlora::lora_down_splits(M, N, r);
-    L.pa_off = 0;
-    L.bt_off = round_up(L.pa_off + (size_t)L.splits_a * M * r * sizeof(float), 256);
-    L.pg_off = round_up(L.bt_off + (size_t)r * N * sizeof(uint16_t), 256);
-    L.xs_off = round_up(L.pg_off + (size_t)L.splits_g * M * r * sizeof(float), 256);
+    // fp32 partials of x . A^T and dy . B; xs = [hi | lo] of s . x . A^T and
+    // gs = [hi | lo] of s . dy . B, [M][2r] bf16 each; fp32 token-split
+    // partials of dB [N][r] and dA [r][K]
+    L.psplits = qlora::lora_proj_splits(M, K < N ? K : N, r, 2);
+    if (L.psplits > 1) {
+      L.pa_off = off;
+      L.pg_off = round_up(off + (size_t)L.psplits * M * r * sizeof(float), 256);
+      off = round_up(L.pg_off + (size_t)L.psplits * M * r * sizeof(float), 256);
+    }
+    L.xs_off = off;
     L.gs_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
     off = round_up(L.gs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+    L.tsplits = qlora::lora_grad_splits(M, N, K);
+    if (L.tsplits > 1) {
+      L.cb_off = off;
+      L.ca_off = round_up(off + (size_t)L.tsplits * N * r * sizeof(float), 256);
+      off = round_up(L.ca_off + (size_t)L.tsplits * r * K * sizeof(float), 256);
+    }
   }
   L.gsplits = qlora::gemm_splits(M, K, N);
   if (L.gsplits > 1) {
@@ -256,11 +268,11 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
     }
     uint16_t* xs = nullptr;
     if (r > 0) {
-      float* P = at<float>(workspace, ws.p_off);
       xs = at<uint16_t>(workspace, ws.xs_off);
-      if ((st = hip_status(qlora::launch_lora_down(x, A, M, K, r, ws.splits, P, s))) != QLORA_OK)
-        return st;
-      if ((st = hip_status(qlora::launch_lora_split(P, ws.splits, M, r, scale, xs, s))) != QLORA_OK)
+      float* P = ws.psplits > 1 ? at<float>(workspace, ws.p_off) : nullptr;
+      const qlora::LoraProjJob jx{x, A, xs, P, K, 0};
+      if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, ws.psplits, s))) !=
+          QLORA_OK)
         return st;
     }
     float* part = ws.gsplits > 1 ? at<float>(workspace, ws.part_off) : nullptr;
@@ -287,12 +299,10 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
       if (!dA || !dB) return QLORA_EINVAL;
       if (!aligned16(dA) || !aligned16(dB)) return QLORA_EALIGN;
       if (overlap(dA, (size_t)r * K * 4, dB, (size_t)N * r * 4)) return QLORA_EINVAL;
-      hipStream_t s0 = as_stream(stream);
-      if ((st = hip_status(qlora::launch_tn_gemm(nullptr, nullptr, N, nullptr, nullptr, r, 0, N,
-                                                 r, dB, accumulate, s0))) != QLORA_OK)
-        return st;
-      return hip_status(qlora::launch_tn_gemm(nullptr, nullptr, r, nullptr, nullptr, K, 0, r, K,
-                                              dA, accumulate, s0));
+      // the gradient kernel with no tokens writes zeros (or adds nothing)
+      const qlora::LoraGradJob jb{nullptr, nullptr, dB, nullptr, N, 0},
+          ja{nullptr, nullptr, dA, nullptr, K, 1};
+      return hip_status(qlora::launch_lora_grad(jb, ja, 0, r, accumulate, 1, as_stream(stream)));
     }
     if (!dy) return QLORA_EINVAL;
     if (r > 0 && (!A || !B || !x || !dA || !dB)) return QLORA_EINVAL;
@@ -324,27 +334,22 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
     const Nf4Levels L = levels_arg();
     uint16_t* gs = nullptr;
     if (r > 0) {
-      float* Pa = at<float>(workspace, ws.pa_off);
-      uint16_t* Bt = at<uint16_t>(workspace, ws.bt_off);
-      float* Pg = at<float>(workspace, ws.pg_off);
       uint16_t* xs = at<uint16_t>(workspace, ws.xs_off);
       gs = at<uint16_t>(workspace, ws.gs_off);
       const float scale = alpha / static_cast<float>(r);
-      if ((st = hip_status(qlora::launch_lora_down(x, A, M, K, r, ws.splits_a, Pa, s))) != QLORA_OK)
-        return st;
-      if ((st = hip_status(qlora::launch_transpose_bf16(B, N, r, Bt, s))) != QLORA_OK) return st;
-      if ((st = hip_status(qlora::launch_lora_down(dy, Bt, M, N, r, ws.splits_g, Pg, s))) != QLORA_OK)
-        return st;
-      if ((st = hip_status(qlora::launch_lora_split(Pa, ws.splits_a, M, r, scale, xs, s))) != QLORA_OK)
-        return st;
-      if ((st = hip_status(qlora::launch_lora_split(Pg, ws.splits_g, M, r, scale, gs, s))) != QLORA_OK)
+      // xs = split(s . x . A^T), gs = split(s . dy . B) in one launch
+      const bool pp = ws.psplits > 1;
+      const qlora::LoraProjJob jx{x, A, xs, pp ? at<float>(workspace, ws.pa_off) : nullptr, K, 0},
+          jg{dy, B, gs, pp ? at<float>(workspace, ws.pg_off) : nullptr, N, 1};
+      if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, ws.psplits, s))) !=
+          QLORA_OK)
         return st;
       // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x
-      if ((st = hip_status(qlora::launch_tn_gemm(dy, dy, N, xs, xs + r, 2 * r, M, N, r, dB,
-                                                 accumulate, s))) != QLORA_OK)
-        return st;
-      if ((st = hip_status(qlora::launch_tn_gemm(gs, gs + r, 2 * r, x, x, K, M, r, K, dA,
-                                                 accumulate, s))) != QLORA_OK)
+      const bool tp = ws.tsplits > 1;
+      const qlora::LoraGradJob jb{dy, xs, dB, tp ? at<float>(workspace, ws.cb_off) : nullptr, N, 0},
+          ja{x, gs, dA, tp ? at<float>(workspace, ws.ca_off) : nullptr, K, 1};
+      if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, ws.tsplits, s))) !=
+          QLORA_OK)
         return st;
     }
     if (dx) {

@@ -18,23 +18,42 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* qscale,
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s);
 
-// lora_kernels.hip -- rank-r helper GEMMs
-// Partial products P[z][m][j] = sum over the z-th share of the k range of
-// X[m][k] * Y[j][k]; X [M, K] and Y [R, K] bf16 row-major.
-int lora_down_splits(int64_t M, int64_t K, int R);
-hipError_t launch_lora_down(const uint16_t* X, const uint16_t* Y, int64_t M, int64_t K, int R,
-                            int splits, float* P, hipStream_t s);
-// out[m][c], c in [0, 2R): hi / lo bf16 split of v = scale * sum_z P[z][m][c mod R]
-hipError_t launch_lora_split(const float* P, int splits, int64_t M, int R, float scale,
-                             uint16_t* out, hipStream_t s);
-// dst [C, R] = transpose of src [R, C] (bf16)
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst,
-                                 hipStream_t s);
-// C[p][q] (+)= sum_h sum_m U_h[m][p] * V_h[m][q] for h in {0, 1}; U_h has
-// leading dimension ldu, V_h ldv; C [P, Q] fp32 row-major.
-hipError_t launch_tn_gemm(const uint16_t* U0, const uint16_t* U1, int64_t ldu,
-                          const uint16_t* V0, const uint16_t* V1, int64_t ldv, int64_t M,
-                          int64_t P, int64_t Q, float* C, int accumulate, hipStream_t s);
+// lora_kernels.hip -- rank-r kernels of the adapter path
+// lora_proj: out[m][j] = hi, out[m][r + j] = lo, the bf16 pair of
+// v = scale * sum_k X[m][k] * Y(j, k), with Y(j, k) = Y[j * Kred + k]
+// (kmajor == 0, A [r, Kred]) or Y[k * r + j] (kmajor == 1, B [Kred, r]).
+// With splits > 1 the k range is split over blocks writing fp32 partials
+// P [splits][M][r], added in split order by a second kernel.
+constexpr int kProjMaxSplits = 16;
+struct LoraProjJob {
+  const uint16_t* X;  // [M, Kred] bf16
+  const uint16_t* Y;
+  uint16_t* out;      // [M, 2r] bf16
+  float* P;           // [splits][M][r] fp32 (splits > 1)
+  int64_t Kred;
+  int kmajor;
+};
+// splits for njobs jobs whose reduction lengths are all >= Kred
+int lora_proj_splits(int64_t M, int64_t Kred, int r, int njobs);
+// one job, or two in one launch (j1 non-null)
+hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
+                            float scale, int splits, hipStream_t s);
+// lora_grad: C (+)= sum_m G[m][g] * (S[m][j] + S[m][r + j]), C [ldg, r]
+// (transposed == 0) or [r, ldg] (transposed == 1); both jobs in one launch.
+// With splits > 1 the tokens are split over blocks writing fp32 partials
+// Cp [splits][C's layout], added to C in split order by a second kernel.
+constexpr int kGradMaxSplits = 16;
+struct LoraGradJob {
+  const uint16_t* G;  // [M, ldg] bf16, ldg a multiple of 64
+  const uint16_t* S;  // [M, 2r] bf16 (hi | lo)
+  float* C;
+  float* Cp;          // [splits][ldg * r] fp32 (splits > 1)
+  int64_t ldg;
+  int transposed;
+};
+int lora_grad_splits(int64_t M, int64_t ldg0, int64_t ldg1);
+hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
+                            int accumulate, int splits, hipStream_t s);
 
 // gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T.  With splits > 1 the
 // k range is split over blocks writing fp32 partials part[splits][M][N],

@@ -1,260 +1,397 @@
-// Rank-r helper GEMMs of the LoRA path (gfx950, bf16 MFMA, fp32 accumulate).
+// Rank-r kernels of the LoRA path (gfx950, bf16 MFMA, fp32 accumulate).
 //
-// The adapter path y += s . (x . A^T) . B^T and its gradients are skinny
-// GEMMs with one dimension equal to the rank r ("QLoRA -- Module 12.4",
+// The adapter term y += s . (x . A^T) . B^T and its gradients are skinny
+// products with one side equal to the rank r ("QLoRA -- Module 12.4",
 // "Hugging Face + BitsAndBytes": LoraConfig(r, lora_alpha); s = alpha / r).
 //
-//  * lora_down: P[z] = X . Y^T over the z-th share of the reduction, for
-//    x . A^T (forward) and dy . B (backward, with B transposed first).  The
-//    reduction is long (K or N) and the output thin, so the work is split
-//    over the reduction into fp32 partials summed later in a fixed order.
-//  * lora_split: v = s . sum_z P[z] rounded to a bf16 pair (hi, lo) with
-//    hi + lo = v to 2^-17 relative, so that the rank-r product can ride on
-//    bf16 MFMA in the big GEMMs' epilogues without losing the fp32 value.
-//  * tn_gemm: dB = dy^T . xs and dA = gs^T . x, reductions over the tokens.
+//  * lora_proj: out = split(s . X . Y^T), X [M, Kred] bf16 and Y either
+//    [r, Kred] (A, for x . A^T) or [Kred, r] (B, for dy . B).  split(v)
+//    stores hi = bf16(v) and lo = bf16(v - hi) as out[m][j] and
+//    out[m][r + j]; hi + lo equals the fp32 value to 2^-17 relative, so the
+//    rank-r product can ride on bf16 MFMA inside the fused GEMMs.
+//  * lora_grad: C (+)= G^T . (S_hi + S_lo) with the reduction over the
+//    tokens: dB [N, r] = dy^T . xs and dA [r, K] = gs^T . x.
+//
+// Both are latency-bound at the shapes of the layer (a few MB per call), so
+// the reduction is spread over many small blocks: the waves of a block take
+// interleaved shares of its range and are added in LDS in wave order; when
+// a range is split over blocks, each block writes an fp32 partial and a
+// finalize kernel adds the partials in split order.  Results are therefore
+// deterministic.  Each wave keeps its next share's global loads in flight
+// while it works on the current one, and two jobs share one launch.
 
 #include "device_common.h"
 #include "launch.h"
 
 namespace qlora {
 
-// ---------------------------------------------------------------------------
-// lora_down: grid (ceil(M/64), splits, ceil(R/64)), 256 threads.  Each wave
-// takes every 4th 64-wide k tile of the block's share and computes a 64x64
-// (m x j) tile with 32x32x16 MFMA straight from global memory (X rows and
-// Y rows are both k-contiguous).  The four waves' tiles are summed in LDS.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void lora_down_kernel(const uint16_t* __restrict__ X,
-                                                        const uint16_t* __restrict__ Y,
-                                                        int64_t M, int64_t K, int R, int splits,
-                                                        float* __restrict__ P) {
-  __shared__ float red[4][64][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane & 31, lg = lane >> 5;
-  const int64_t m0 = (int64_t)blockIdx.x * 64;
-  const int z = blockIdx.y;
-  const int j0 = blockIdx.z * 64;
-  const int64_t nkt = K >> 6;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  for (int64_t kt = z + (int64_t)splits * wave; kt < nkt; kt += (int64_t)splits * 4) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int64_t k = kt * 64 + kk * 16 + 8 * lg;
-      u32x4_t a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t m = m0 + 32 * i + lr;
-        a[i] = (m < M) ? *reinterpret_cast<const u32x4_t*>(X + m * K + k) : zero;
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int jr = j0 + 32 * j + lr;
-        b[j] = (jr < R) ? *reinterpret_cast<const u32x4_t*>(Y + (int64_t)jr * K + k) : zero;
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
-    }
-  }
-  // D = X . Y^T: lane holds column j = lr, rows m = 8(v/4) + 4 lg + v%4.
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        red[wave][32 * i + 8 * (v >> 2) + 4 * lg + (v & 3)][32 * j + lr] = acc[i][j][v];
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int mm = e >> 6, jj = e & 63;
-    const float s = red[0][mm][jj] + red[1][mm][jj] + red[2][mm][jj] + red[3][mm][jj];
-    const int64_t m = m0 + mm;
-    const int j = j0 + jj;
-    if (m < M && j < R) P[((int64_t)z * M + m) * R + j] = s;
-  }
-}
-
-int lora_down_splits(int64_t M, int64_t K, int R) {
-  const int64_t mt = (M + 63) / 64, jt = (R + 63) / 64;
-  const int64_t nkt = K / 64;
-  int64_t cap = nkt / 4;
-  if (cap < 1) cap = 1;
-  int64_t s = (512 + mt * jt - 1) / (mt * jt);
-  if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  return (int)s;
-}
-
-hipError_t launch_lora_down(const uint16_t* X, const uint16_t* Y, int64_t M, int64_t K, int R,
-                            int splits, float* P, hipStream_t s) {
-  dim3 grid((unsigned)((M + 63) / 64), (unsigned)splits, (unsigned)((R + 63) / 64));
-  hipLaunchKernelGGL(lora_down_kernel, grid, dim3(256), 0, s, X, Y, M, K, R, splits, P);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// lora_split: out[m][j] = hi, out[m][R + j] = lo with v = scale * sum_z P,
-// hi = bf16(v), lo = bf16(v - hi) (v - hi is exact in fp32).
-// ---------------------------------------------------------------------------
 __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
-__global__ __launch_bounds__(256) void lora_split_kernel(const float* __restrict__ P, int splits,
-                                                         int64_t M, int R, float scale,
-                                                         uint16_t* __restrict__ out) {
-  const int64_t total = M * R;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-    float acc = 0.0f;
-    for (int z = 0; z < splits; ++z) acc += P[(int64_t)z * total + e];
-    const float v = scale * acc;
-    const uint16_t hi = bf16_rne_bits(v);
-    const uint16_t lo = bf16_rne_bits(v - bf16_bits_to_f32(hi));
-    const int64_t m = e / R;
-    const int j = (int)(e - m * R);
-    out[m * 2 * R + j] = hi;
-    out[m * 2 * R + R + j] = lo;
-  }
-}
-
-hipError_t launch_lora_split(const float* P, int splits, int64_t M, int R, float scale,
-                             uint16_t* out, hipStream_t s) {
-  const int64_t total = M * R;
-  int64_t g = (total + 255) / 256;
-  if (g > 4096) g = 4096;
-  if (g < 1) g = 1;
-  hipLaunchKernelGGL(lora_split_kernel, dim3((unsigned)g), dim3(256), 0, s, P, splits, M, R,
-                     scale, out);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
-// transpose (bf16): dst[c][r] = src[r][c], 64x64 tiles through LDS.
+// lora_proj: grid (njobs * ceil(M/16) * ceil(r/16) * splits), 256 threads.
+// A block owns 16 tokens x 16 rank columns of one job and the z-th share of
+// the reduction; wave w takes the 32-wide k steps w, w + 4, ... of that
+// share and runs 16x16x32 MFMA straight from global memory: the token
+// operand is one 16-byte load per lane (8 consecutive k of a row), and so is
+// A's operand; B ([Kred, r]) is gathered as 8 two-byte loads per lane.  With
+// one split the block writes the bf16 pair itself; otherwise it writes an
+// fp32 partial P[z][m][j] and lora_proj_finalize adds the shares in order.
+// Many small blocks keep enough loads in flight across the chip; a few big
+// ones would leave the reduction latency-bound.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
-                                                             int64_t R, int64_t C,
-                                                             uint16_t* __restrict__ dst) {
-  __shared__ uint16_t tile[64][65];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int rr = e >> 6, cc = e & 63;
-    const int64_t r = r0 + rr, c = c0 + cc;
-    tile[rr][cc] = (r < R && c < C) ? src[r * C + c] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int cc = e >> 6, rr = e & 63;
-    const int64_t r = r0 + rr, c = c0 + cc;
-    if (r < R && c < C) dst[c * R + r] = tile[rr][cc];
-  }
-}
+constexpr int kProjWaves = 4;
+constexpr int kProjBatch = 4;  // k steps per register set
 
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst,
-                                 hipStream_t s) {
-  dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, src, R, C, dst);
-  return hipGetLastError();
-}
+__global__ __launch_bounds__(kProjWaves * 64) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
+                                                                    int64_t blocks_per_job,
+                                                                    int64_t M, int r, float scale,
+                                                                    int splits) {
+  __shared__ float red[kProjWaves][16][17];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool second = (int64_t)blockIdx.x >= blocks_per_job;
+  const uint16_t* X = second ? j1.X : j0.X;
+  const uint16_t* Y = second ? j1.Y : j0.Y;
+  uint16_t* out = second ? j1.out : j0.out;
+  const int64_t Kred = second ? j1.Kred : j0.Kred;
+  const int kmajor = second ? j1.kmajor : j0.kmajor;
+  float* P = second ? j1.P : j0.P;
 
-// ---------------------------------------------------------------------------
-// tn_gemm: C[p][q] (+)= sum_h sum_m U_h[m][p] V_h[m][q].  The reduction runs
-// over the tokens m, the slow dimension of both operands, so each 64-token
-// step is stored transposed in LDS (tokens contiguous) and read back as
-// MFMA operands.  grid (ceil(P/64), ceil(Q/64)), 256 threads; wave (wp, wq)
-// owns a 32x32 quadrant.  Each output tile is reduced by one block over all
-// tokens, in a fixed order.
-// ---------------------------------------------------------------------------
-// LDS tile [64 rows][64 tokens] bf16, rows 128 B; 16-byte token chunks are
-// swizzled by the row so that both the transposing 2-byte writes (8 rows
-// at once) and the 16-byte operand reads (8 consecutive rows) spread over
-// all banks.
-__device__ __forceinline__ int tn_off(int row, int tok) {
-  const int chunk = (tok >> 3) ^ (row & 7) ^ ((row >> 3) & 7);
-  return row * 64 + chunk * 8 + (tok & 7);
-}
-
-__global__ __launch_bounds__(256) void tn_gemm_kernel(
-    const uint16_t* __restrict__ U0, const uint16_t* __restrict__ U1, int64_t ldu,
-    const uint16_t* __restrict__ V0, const uint16_t* __restrict__ V1, int64_t ldv, int64_t M,
-    int64_t P, int64_t Q, float* __restrict__ C, int accumulate) {
-  __shared__ uint16_t ut[2][64 * 64];
-  __shared__ uint16_t vt[2][64 * 64];
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
-  const int wp = wave & 1, wq = wave >> 1;
-  const int64_t p0 = (int64_t)blockIdx.x * 64, q0 = (int64_t)blockIdx.y * 64;
+  const int jblocks = (r + 15) / 16;
+  const int64_t b0 = second ? (int64_t)blockIdx.x - blocks_per_job : (int64_t)blockIdx.x;
+  const int z = (int)(b0 % splits);
+  const int64_t bb = b0 / splits;
+  const int64_t m0 = (bb / jblocks) * 16;
+  const int jc = (int)(bb % jblocks) * 16;
+  const int i = lane & 15, kg = lane >> 4;
+  const int64_t m = m0 + i;
+  const bool mok = m < M;
+  const int jj = jc + i;
+  const bool jok = jj < r;
+  const int64_t nsteps = Kred / 32;
+  const int64_t st0 = nsteps * z / splits, st1 = nsteps * (z + 1) / splits;
+  const int64_t ns = st1 - st0 > wave ? (st1 - st0 - wave + kProjWaves - 1) / kProjWaves : 0;
+  const uint16_t* xrow = X + (mok ? m : 0) * Kred + 8 * kg;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
-  f32x16_t acc;
+  // operands of this wave's s-th k step
+  auto load = [&](int64_t s, u32x4_t& xv, u32x4_t& yv) {
+    const int64_t k0 = 32 * (st0 + wave + (int64_t)kProjWaves * s);
+    xv = mok ? *reinterpret_cast<const u32x4_t*>(xrow + k0) : zero;
+    if (!kmajor) {
+      yv = jok ? *reinterpret_cast<const u32x4_t*>(Y + (int64_t)jj * Kred + k0 + 8 * kg) : zero;
+    } else {
+      const uint16_t* yc = Y + (k0 + 8 * kg) * r + (jok ? jj : 0);
+      uint32_t h[8];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+      for (int e = 0; e < 8; ++e) h[e] = jok ? (uint32_t)yc[(int64_t)e * r] : 0u;
+      yv[0] = h[0] | (h[1] << 16);
+      yv[1] = h[2] | (h[3] << 16);
+      yv[2] = h[4] | (h[5] << 16);
+      yv[3] = h[6] | (h[7] << 16);
+    }
+  };
+  const int64_t nb = (ns + kProjBatch - 1) / kProjBatch;
+  auto load_batch = [&](int64_t bi, u32x4_t (&xv)[kProjBatch], u32x4_t (&yv)[kProjBatch]) {
+#pragma unroll
+    for (int u = 0; u < kProjBatch; ++u) {
+      const int64_t s = bi * kProjBatch + u;
+      if (s < ns) {
+        load(s, xv[u], yv[u]);
+      } else {
+        xv[u] = zero;
+        yv[u] = zero;
+      }
+    }
+  };
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto mma_batch = [&](const u32x4_t (&xv)[kProjBatch], const u32x4_t (&yv)[kProjBatch]) {
+#pragma unroll
+    for (int u = 0; u < kProjBatch; ++u) acc = mfma16x16x32(xv[u], yv[u], acc);
+  };
 
-  const int chunk = t & 7;  // 8 columns (p or q) per thread per row
-  for (int64_t m0 = 0; m0 < M; m0 += 64) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint16_t* U = h ? U1 : U0;
-      const uint16_t* V = h ? V1 : V0;
-#pragma unroll
-      for (int rep = 0; rep < 2; ++rep) {
-        const int tok = (t >> 3) + 32 * rep;
-        const int64_t m = m0 + tok;
-        const int64_t p = p0 + 8 * chunk, q = q0 + 8 * chunk;
-        const u32x4_t u = (m < M && p < P) ? *reinterpret_cast<const u32x4_t*>(U + m * ldu + p) : zero;
-        const u32x4_t v = (m < M && q < Q) ? *reinterpret_cast<const u32x4_t*>(V + m * ldv + q) : zero;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t uw = u[e >> 1], vw = v[e >> 1];
-          ut[h][tn_off(8 * chunk + e, tok)] = (uint16_t)((e & 1) ? (uw >> 16) : uw);
-          vt[h][tn_off(8 * chunk + e, tok)] = (uint16_t)((e & 1) ? (vw >> 16) : vw);
-        }
-      }
+  // two register sets: batch b + 1 loads while batch b multiplies
+  u32x4_t X0[kProjBatch], Y0[kProjBatch], X1[kProjBatch], Y1[kProjBatch];
+  if (nb > 0) load_batch(0, X0, Y0);
+  for (int64_t bi = 0; bi < nb; bi += 2) {
+    if (bi + 1 < nb) load_batch(bi + 1, X1, Y1);
+    mma_batch(X0, Y0);
+    if (bi + 1 < nb) {
+      if (bi + 2 < nb) load_batch(bi + 2, X0, Y0);
+      mma_batch(X1, Y1);
     }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int tc = 2 * kk + lg;  // token chunk
-        const int pr = 32 * wp + lr, qr = 32 * wq + lr;
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&ut[h][tn_off(pr, 8 * tc)]);
-        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&vt[h][tn_off(qr, 8 * tc)]);
-        acc = mfma32x32x16(a, b, acc);
-      }
-    }
-    __syncthreads();
   }
-  // D[p][q]: lane holds column q = 32 wq + lr, rows p = 32 wp + 8(v/4) + 4 lg + v%4.
-  const int64_t q = q0 + 32 * wq + lr;
-  if (q < Q) {
+
+  // D[token][j]: lane holds column j = lane % 16, rows 4 (lane / 16) + v
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t p = p0 + 32 * wp + 8 * (v >> 2) + 4 * lg + (v & 3);
-      if (p < P) {
-        float* c = C + p * Q + q;
-        *c = accumulate ? (*c + acc[v]) : acc[v];
+  for (int v = 0; v < 4; ++v) red[wave][4 * kg + v][i] = acc[v];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int mm = threadIdx.x >> 4, j = threadIdx.x & 15;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kProjWaves; ++w) sum += red[w][mm][j];
+    const int64_t mo = m0 + mm;
+    const int jo = jc + j;
+    if (mo < M && jo < r) {
+      if (splits == 1) {
+        const float v = scale * sum;
+        const uint16_t hi = bf16_rne_bits(v);
+        const uint16_t lo = bf16_rne_bits(v - bf16_bits_to_f32(hi));  // v - hi is exact
+        out[mo * 2 * r + jo] = hi;
+        out[mo * 2 * r + r + jo] = lo;
+      } else {
+        P[((int64_t)z * M + mo) * r + jo] = sum;
       }
     }
   }
 }
 
-hipError_t launch_tn_gemm(const uint16_t* U0, const uint16_t* U1, int64_t ldu,
-                          const uint16_t* V0, const uint16_t* V1, int64_t ldv, int64_t M,
-                          int64_t P, int64_t Q, float* C, int accumulate, hipStream_t s) {
-  dim3 grid((unsigned)((P + 63) / 64), (unsigned)((Q + 63) / 64));
-  hipLaunchKernelGGL(tn_gemm_kernel, grid, dim3(256), 0, s, U0, U1, ldu, V0, V1, ldv, M, P, Q,
-                     C, accumulate);
+// out = bf16 pair of scale * sum_z P[z] (z in order); grid-stride over both
+// jobs' M x r values.
+__global__ __launch_bounds__(256) void lora_proj_finalize_kernel(LoraProjJob j0, LoraProjJob j1,
+                                                                 int njobs, int64_t M, int r,
+                                                                 float scale, int splits) {
+  const int64_t per = M * r, total = per * njobs;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const bool second = e >= per;
+    const float* P = second ? j1.P : j0.P;
+    uint16_t* out = second ? j1.out : j0.out;
+    const int64_t ee = second ? e - per : e;
+    float v[16];
+#pragma unroll
+    for (int z = 0; z < 16; ++z) v[z] = z < splits ? P[(int64_t)z * per + ee] : 0.0f;
+    float sum = v[0];
+#pragma unroll
+    for (int z = 1; z < 16; ++z)
+      if (z < splits) sum += v[z];
+    const float t = scale * sum;
+    const uint16_t hi = bf16_rne_bits(t);
+    const uint16_t lo = bf16_rne_bits(t - bf16_bits_to_f32(hi));
+    const int64_t m = ee / r;
+    const int j = (int)(ee - m * r);
+    out[m * 2 * r + j] = hi;
+    out[m * 2 * r + r + j] = lo;
+  }
+}
+
+int lora_proj_splits(int64_t M, int64_t Kred, int r, int njobs) {
+  const int64_t tiles = ((M + 15) / 16) * ((r + 15) / 16) * njobs;
+  int64_t s = (1024 + tiles - 1) / tiles;
+  const int64_t cap = Kred / 256;  // at least 8 k steps (2 per wave) per block
+  if (s > cap) s = cap;
+  if (s > kProjMaxSplits) s = kProjMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
+                            float scale, int splits, hipStream_t s) {
+  const int njobs = j1 ? 2 : 1;
+  const int64_t per_job = ((M + 15) / 16) * ((r + 15) / 16) * splits;
+  if (per_job == 0) return hipSuccess;
+  hipLaunchKernelGGL(lora_proj_kernel, dim3((unsigned)(per_job * njobs)), dim3(kProjWaves * 64), 0,
+                     s, j0, j1 ? *j1 : j0, per_job, M, r, scale, splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  int64_t g = (M * r * njobs + 255) / 256;
+  if (g > 2048) g = 2048;
+  hipLaunchKernelGGL(lora_proj_finalize_kernel, dim3((unsigned)g), dim3(256), 0, s, j0,
+                     j1 ? *j1 : j0, njobs, M, r, scale, splits);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// lora_grad: grid ((ldg0 / 64 + ldg1 / 64) * splits), 256 threads.  A block
+// owns 64 columns g of the big operand G (dy for dB, x for dA), all r
+// columns of the small operand S = [hi | lo] (in chunks of 64) and the z-th
+// share of the tokens.  Wave w takes the 32-token steps w, w + 4, ... of
+// that share: it loads the step's G and S rows, stores them transposed
+// (tokens contiguous) in its own LDS tile, and reads 16-byte MFMA operands
+// back (16x16x32: G columns as rows, S columns as columns; hi and lo are two
+// MFMAs on the same G operand).  No barrier is needed inside the loop: a
+// wave's LDS accesses are executed in order and no other wave touches its
+// tile.  With one split the block writes C itself; otherwise it writes the
+// partial Cp[z] (C's layout) and lora_grad_finalize adds them in order.
+// ---------------------------------------------------------------------------
+constexpr int kGradRow = 40;                  // LDS row: 32 tokens + 8 pad (bf16), 80 bytes
+constexpr int kGradTile = 192 * kGradRow;     // rows 0..63 G, 64..127 S hi, 128..191 S lo
+constexpr int kGradRed = 68;                  // fp32 row stride of the cross-wave reduction
+
+__global__ __launch_bounds__(256) void lora_grad_kernel(LoraGradJob j0, LoraGradJob j1,
+                                                        int64_t blocks0, int64_t M, int r,
+                                                        int accumulate, int splits) {
+  __shared__ __align__(16) uint16_t smem[2 * 4 * 64 * kGradRed];  // 69632 B
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool second = (int64_t)blockIdx.x >= blocks0;
+  const uint16_t* G = second ? j1.G : j0.G;
+  const uint16_t* S = second ? j1.S : j0.S;
+  const int64_t ldg = second ? j1.ldg : j0.ldg;
+  const int transposed = second ? j1.transposed : j0.transposed;
+  const int64_t bb = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
+  const int z = (int)(bb % splits);
+  const int64_t g0 = 64 * (bb / splits);
+  float* C = splits == 1 ? (second ? j1.C : j0.C)
+                         : (second ? j1.Cp : j0.Cp) + (int64_t)z * ldg * r;
+  const int acc_out = splits == 1 ? accumulate : 0;
+
+  uint16_t* tile = smem + wave * kGradTile;
+  float* red = reinterpret_cast<float*>(smem);  // [4][64][kGradRed], after the token loop
+  const int tk = lane & 31, ch = lane >> 5;     // token of a step, chunk parity
+  const int i = lane & 15, kg = lane >> 4;      // MFMA operand lane coordinates
+  const int64_t nst = (M + 31) / 32;
+  const int64_t st0 = nst * z / splits, st1 = nst * (z + 1) / splits;
+  const int64_t ns = st1 - st0 > wave ? (st1 - st0 - wave + 3) / 4 : 0;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  for (int jc = 0; jc < r; jc += 64) {
+    const int R = r - jc < 64 ? r - jc : 64;  // multiple of 8
+    const int R8 = R / 8;
+
+    // step s of this wave: tokens 32 (st0 + wave + 4 s) + tk; G chunk c = ch + 2u
+    // (8 columns), S chunk cc = ch + 2u (hi chunks first, then lo chunks)
+    auto load_step = [&](int64_t s, u32x4_t (&gv)[4], u32x4_t (&sv)[8]) {
+      const int64_t m = 32 * (st0 + wave + 4 * s) + tk;
+      const bool ok = m < M;
+      const uint16_t* grow = G + (ok ? m : 0) * ldg + g0;
+      const uint16_t* srow = S + (ok ? m : 0) * 2 * r;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        gv[u] = ok ? *reinterpret_cast<const u32x4_t*>(grow + 8 * (ch + 2 * u)) : zero;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u < R8) {
+          const int cc = ch + 2 * u;
+          const int col = cc < R8 ? jc + 8 * cc : r + jc + 8 * (cc - R8);
+          sv[u] = ok ? *reinterpret_cast<const u32x4_t*>(srow + col) : zero;
+        }
+      }
+    };
+    auto put8 = [&](int row, const u32x4_t& v) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        tile[(row + e) * kGradRow + tk] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    };
+    auto store_step = [&](const u32x4_t (&gv)[4], const u32x4_t (&sv)[8]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) put8(8 * (ch + 2 * u), gv[u]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u < R8) {
+          const int cc = ch + 2 * u;
+          put8(cc < R8 ? 64 + 8 * cc : 128 + 8 * (cc - R8), sv[u]);
+        }
+      }
+    };
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mma_step = [&]() {
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const u32x4_t a =
+            *reinterpret_cast<const u32x4_t*>(tile + (16 * gi + i) * kGradRow + 8 * kg);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          if (16 * jt < R) {
+            const u32x4_t bh =
+                *reinterpret_cast<const u32x4_t*>(tile + (64 + 16 * jt + i) * kGradRow + 8 * kg);
+            const u32x4_t bl =
+                *reinterpret_cast<const u32x4_t*>(tile + (128 + 16 * jt + i) * kGradRow + 8 * kg);
+            acc[gi][jt] = mfma16x16x32(a, bh, acc[gi][jt]);
+            acc[gi][jt] = mfma16x16x32(a, bl, acc[gi][jt]);
+          }
+        }
+      }
+    };
+
+    u32x4_t G0[4], S0[8], G1[4], S1[8];
+    if (ns > 0) load_step(0, G0, S0);
+    for (int64_t s = 0; s < ns; s += 2) {
+      if (s + 1 < ns) load_step(s + 1, G1, S1);
+      store_step(G0, S0);
+      mma_step();
+      if (s + 1 < ns) {
+        if (s + 2 < ns) load_step(s + 2, G0, S0);
+        store_step(G1, S1);
+        mma_step();
+      }
+    }
+
+    __syncthreads();  // every wave is done with its tile; reuse LDS for the sums
+    // D[g][j]: lane holds column j = lane % 16, rows 4 (lane / 16) + v
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt)
+        if (16 * jt < R)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            red[(wave * 64 + 16 * gi + 4 * kg + v) * kGradRed + 16 * jt + i] = acc[gi][jt][v];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * R; e += 256) {
+      // consecutive threads write consecutive addresses of C
+      const int gl = transposed ? (e & 63) : e / R;
+      const int j = transposed ? (e >> 6) : e % R;
+      const float sum = ((red[(0 * 64 + gl) * kGradRed + j] + red[(1 * 64 + gl) * kGradRed + j]) +
+                         red[(2 * 64 + gl) * kGradRed + j]) +
+                        red[(3 * 64 + gl) * kGradRed + j];
+      const int64_t g = g0 + gl;
+      const int jo = jc + j;
+      float* c = transposed ? C + (int64_t)jo * ldg + g : C + g * r + jo;
+      *c = acc_out ? *c + sum : sum;
+    }
+    __syncthreads();  // before the next chunk overwrites the tiles
+  }
+}
+
+// C (+)= sum_z Cp[z] (z in order), grid-stride over both jobs' outputs
+__global__ __launch_bounds__(256) void lora_grad_finalize_kernel(LoraGradJob j0, LoraGradJob j1,
+                                                                 int r, int accumulate,
+                                                                 int splits) {
+  const int64_t n0 = j0.ldg * r, total = n0 + j1.ldg * r;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const bool second = e >= n0;
+    const float* Cp = second ? j1.Cp : j0.Cp;
+    float* C = second ? j1.C : j0.C;
+    const int64_t n = second ? total - n0 : n0;
+    const int64_t ee = second ? e - n0 : e;
+    float v[16];
+#pragma unroll
+    for (int z = 0; z < 16; ++z) v[z] = z < splits ? Cp[(int64_t)z * n + ee] : 0.0f;
+    float sum = v[0];
+#pragma unroll
+    for (int z = 1; z < 16; ++z)
+      if (z < splits) sum += v[z];
+    C[ee] = accumulate ? C[ee] + sum : sum;
+  }
+}
+
+int lora_grad_splits(int64_t M, int64_t ldg0, int64_t ldg1) {
+  const int64_t blocks = ldg0 / 64 + ldg1 / 64;
+  const int64_t nst = (M + 31) / 32;
+  int64_t s = blocks > 0 ? (512 + blocks - 1) / blocks : 1;
+  if (s > nst / 4) s = nst / 4;  // at least one 32-token step per wave
+  if (s > kGradMaxSplits) s = kGradMaxSplits;
+  return s < 1 ? 1 : (int)s;
+}
+
+hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
+                            int accumulate, int splits, hipStream_t s) {
+  const int64_t b0 = j0.ldg / 64, b1 = j1.ldg / 64;
+  if (b0 + b1 == 0 || r == 0) return hipSuccess;
+  hipLaunchKernelGGL(lora_grad_kernel, dim3((unsigned)((b0 + b1) * splits)), dim3(256), 0, s, j0,
+                     j1, b0 * splits, M, r, accumulate, splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  int64_t g = ((j0.ldg + j1.ldg) * r + 255) / 256;
+  if (g > 2048) g = 2048;
+  hipLaunchKernelGGL(lora_grad_finalize_kernel, dim3((unsigned)g), dim3(256), 0, s, j0, j1, r,
+                     accumulate, splits);
   return hipGetLastError();
 }
 
