@@ -7,6 +7,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <stdexcept>
 
 #include "../../include/qlora.h"
 #include "launch.h"
@@ -15,7 +16,6 @@
 namespace {
 
 using qlora::Nf4Levels;
-using qlora::Nf4Thresholds;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -31,10 +31,22 @@ Nf4Levels levels_arg() {
   std::memcpy(L.v, qlora::nf4_table().level, sizeof(L.v));
   return L;
 }
-Nf4Thresholds thresholds_arg() {
-  Nf4Thresholds T;
-  std::memcpy(T.t, qlora::nf4_table().threshold, sizeof(T.t));
-  return T;
+// The quantiser's bin table (see Nf4CodeBins), built from the thresholds with
+// the same fp32 bin function the kernel uses.
+qlora::Nf4CodeBins code_bins_arg() {
+  const qlora::Nf4Table& t = qlora::nf4_table();
+  qlora::Nf4CodeBins B;
+  for (int b = 0; b < 64; ++b) {
+    B.thr[b] = 2.0f;
+    B.base[b] = 0;
+  }
+  for (int i = 0; i < 15; ++i) {
+    const uint32_t b = qlora::nf4_bin(t.threshold[i]);
+    if (B.thr[b] != 2.0f) throw std::logic_error("two NF4 thresholds in one bin");
+    B.thr[b] = t.threshold[i];
+    for (int c = (int)b + 1; c < 64; ++c) B.base[c] += 1;
+  }
+  return B;
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -42,6 +54,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+int64_t pad32(int64_t M) { return (M + 31) / 32 * 32; }
 
 // Validate the packed-weight descriptor for a GEMM of the given M.
 int check_weight(const qlora_nf4_weight* w) {
@@ -60,7 +73,7 @@ int check_rank(int32_t r) {
 
 // ---- workspace layout --------------------------------------------------
 struct FwdWs {
-  size_t p_off, xs_off, part_off, total;
+  size_t p_off, xs_off, xst_off, part_off, total;
   int psplits;   // k splits of the adapter down-projection (1: no partials)
   int dsplits;   // k splits of the decode path
   int gsplits;   // k splits of the fused GEMM (1: no partials)
@@ -84,7 +97,8 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
     L.psplits = qlora::lora_proj_splits(M, K, r, 1);
     L.p_off = 0;
     L.xs_off = L.psplits > 1 ? round_up((size_t)L.psplits * M * r * sizeof(float), 256) : 0;
-    off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+    L.xst_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+    off = round_up(L.xst_off + (size_t)pad32(M) * 2 * r * sizeof(uint16_t), 256);
   }
   L.gsplits = qlora::gemm_splits(M, N, K);
   if (L.gsplits > 1) {
@@ -96,7 +110,7 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t pa_off, pg_off, xs_off, gs_off, cb_off, ca_off, part_off, total;
+  size_t pa_off, pg_off, xs_off, gs_off, xst_off, gst_off, cb_off, ca_off, part_off, total;
   int psplits;  // k splits of the two down-projections (1: no partials)
   int tsplits;  // token splits of the dA / dB reductions (1: no partials)
   int gsplits;  // reduction splits of the dX GEMM (1: no partials)
@@ -116,9 +130,13 @@ BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
       L.pg_off = round_up(off + (size_t)L.psplits * M * r * sizeof(float), 256);
       off = round_up(L.pg_off + (size_t)L.psplits * M * r * sizeof(float), 256);
     }
+    const size_t pair = (size_t)M * 2 * r * sizeof(uint16_t),
+                 pairT = (size_t)pad32(M) * 2 * r * sizeof(uint16_t);
     L.xs_off = off;
-    L.gs_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
-    off = round_up(L.gs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+    L.gs_off = round_up(L.xs_off + pair, 256);
+    L.xst_off = round_up(L.gs_off + pair, 256);
+    L.gst_off = round_up(L.xst_off + pairT, 256);
+    off = round_up(L.gst_off + pairT, 256);
     L.tsplits = qlora::lora_grad_splits(M, N, K);
     if (L.tsplits > 1) {
       L.cb_off = off;
@@ -187,7 +205,7 @@ int qlora_quantize_nf4(const float* w, int64_t n_elems, int32_t blocksize, uint8
                  na = (size_t)((n_elems + 63) / 64) * 4;
     if (overlap(w, nw, codes, nc) || overlap(w, nw, absmax, na) || overlap(codes, nc, absmax, na))
       return QLORA_EINVAL;
-    return hip_status(qlora::launch_quantize(w, n_elems, codes, absmax, thresholds_arg(),
+    return hip_status(qlora::launch_quantize(w, n_elems, codes, absmax, code_bins_arg(),
                                              as_stream(stream)));
   } catch (...) {
     return QLORA_EHIP;
@@ -270,7 +288,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
     if (r > 0) {
       xs = at<uint16_t>(workspace, ws.xs_off);
       float* P = ws.psplits > 1 ? at<float>(workspace, ws.p_off) : nullptr;
-      const qlora::LoraProjJob jx{x, A, xs, P, K, 0};
+      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), P, K, 0};
       if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, ws.psplits, s))) !=
           QLORA_OK)
         return st;
@@ -339,15 +357,17 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
       const float scale = alpha / static_cast<float>(r);
       // xs = split(s . x . A^T), gs = split(s . dy . B) in one launch
       const bool pp = ws.psplits > 1;
-      const qlora::LoraProjJob jx{x, A, xs, pp ? at<float>(workspace, ws.pa_off) : nullptr, K, 0},
-          jg{dy, B, gs, pp ? at<float>(workspace, ws.pg_off) : nullptr, N, 1};
+      uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
+      uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
+      const qlora::LoraProjJob jx{x, A, xs, xsT, pp ? at<float>(workspace, ws.pa_off) : nullptr, K, 0},
+          jg{dy, B, gs, gsT, pp ? at<float>(workspace, ws.pg_off) : nullptr, N, 1};
       if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, ws.psplits, s))) !=
           QLORA_OK)
         return st;
       // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x
       const bool tp = ws.tsplits > 1;
-      const qlora::LoraGradJob jb{dy, xs, dB, tp ? at<float>(workspace, ws.cb_off) : nullptr, N, 0},
-          ja{x, gs, dA, tp ? at<float>(workspace, ws.ca_off) : nullptr, K, 1};
+      const qlora::LoraGradJob jb{dy, xsT, dB, tp ? at<float>(workspace, ws.cb_off) : nullptr, N, 0},
+          ja{x, gsT, dA, tp ? at<float>(workspace, ws.ca_off) : nullptr, K, 1};
       if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, ws.tsplits, s))) !=
           QLORA_OK)
         return st;

@@ -23,6 +23,21 @@ struct Nf4Thresholds {
   float t[15];
 };
 
+// Code lookup for the quantiser.  bin(u) = min(63, trunc(32 * fl32(u + 1)))
+// is monotone in u, so for |u| <= 1 the code #{i : u > t[i]} equals
+// base[bin] + (u > thr[bin]), where base[b] counts the thresholds whose bin
+// is below b and thr[b] is the threshold inside bin b (+2, above every u,
+// if there is none; no bin holds two).
+struct Nf4CodeBins {
+  float thr[64];
+  uint32_t base[64];
+};
+__host__ __device__ __forceinline__ uint32_t nf4_bin(float u) {
+  const float t = (u + 1.0f) * 32.0f;  // the product is exact (power of two)
+  const uint32_t b = (uint32_t)t;
+  return b < 63u ? b : 63u;
+}
+
 // v_perm_b32: result byte i = byte sel.byte[i] of the 8-byte value
 // {hi:lo}; selector 0..3 picks lo's bytes, 4..7 hi's bytes, 12 gives 0x00
 // and 13..15 give 0xFF.
@@ -141,6 +156,53 @@ __device__ __forceinline__ TileCoord xcd_tile(int64_t id, int64_t total, int64_t
   c.m = g * group_m + w % gm;
   c.n = w / gm;
   return c;
+}
+
+// Epilogue of the fused GEMMs.  A wave holds a 128 (rows: n or k) x 128
+// (columns: tokens m) fp32 tile as 4 x 4 MFMA 32x32 tiles; lane l holds
+// column 32 j + l % 32 and rows 32 i + 8 (v / 4) + 4 (l / 32) + v % 4.  The
+// output is token-major (out[m][row]), so storing straight from registers
+// would give every store instruction 32 rows of 16 bytes.  Instead each
+// 32-column slice goes through the wave's own LDS area (32 x 132 fp32, the
+// 4-float pad spreads the rows over the banks) and comes back row-contiguous:
+// one store instruction then writes two whole 128-row runs.  `part` selects
+// fp32 partials, otherwise values are rounded to bf16.
+constexpr int kEpiStride = 132;
+constexpr int kEpiFloats = 32 * kEpiStride;  // per wave
+__device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[4][4], float* scratch,
+                                               int64_t row0, int64_t col0, int64_t nrows,
+                                               int64_t ncols, bool part, float* outf,
+                                               uint16_t* outh, int64_t ld, int lane) {
+  const int lr = lane & 31, lg = lane >> 5;
+  const int64_t row = row0 + 4 * lr;  // the 4 rows this lane stores
+  const bool row_ok = row < nrows;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                           acc[i][j][4 * q + 3]};
+        *reinterpret_cast<f32x4_t*>(scratch + lr * kEpiStride + 32 * i + 8 * q + 4 * lg) = v;
+      }
+#pragma unroll
+    for (int pp = 0; pp < 16; ++pp) {
+      const int c = 2 * pp + lg;  // column within the slice
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(scratch + c * kEpiStride + 4 * lr);
+      const int64_t m = col0 + 32 * j + c;
+      if (m < ncols && row_ok) {
+        if (part) {
+          *reinterpret_cast<f32x4_t*>(outf + m * ld + row) = v;
+        } else {
+          u32x2_t o;
+          o[0] = pack_bf16x2(v[0], v[1]);
+          o[1] = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<u32x2_t*>(outh + m * ld + row) = o;
+        }
+      }
+    }
+  }
 }
 
 // MFMA wrappers (gfx950 bf16, fp32 accumulate).

@@ -224,30 +224,13 @@ void dx_gemm_kernel(DxParams p) {
     }
   }
 
-  // --- epilogue: D[k][m]; lane holds m = lr, k = 8(v/4) + 4 lg + v%4 ---
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + 128 * wm + 32 * j + lr;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t k = k0 + 128 * wk + 32 * i + 8 * q + 4 * lg;
-        if (k >= K) continue;
-        if (p.splits == 1) {
-          u32x2_t o;
-          o[0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-          o[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<u32x2_t*>(p.dx + m * K + k) = o;
-        } else {
-          f32x4_t o = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                       acc[i][j][4 * q + 3]};
-          *reinterpret_cast<f32x4_t*>(p.part + ((int64_t)z * M + m) * K + k) = o;
-        }
-      }
-    }
-  }
+  // --- epilogue: D[k][m] -> dx[m][k] (or the split's fp32 partial) ---
+  __syncthreads();  // the LDS stages are free from here on
+  float* scratch = (wave < 2 ? reinterpret_cast<float*>(&wt[0][0])
+                             : reinterpret_cast<float*>(&dyt[0][0])) +
+                   (wave & 1) * kEpiFloats;
+  store_acc_tile(acc, scratch, k0 + 128 * wk, m0 + 128 * wm, K, M, p.splits > 1,
+                 p.splits > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
 }
 
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,

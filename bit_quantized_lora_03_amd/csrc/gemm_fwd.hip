@@ -282,30 +282,11 @@ void fwd_gemm_kernel(FwdParams p) {
     }
   }
 
-  // --- epilogue: D[n][m]; lane holds m = lr, n = 8(v/4) + 4 lg + v%4 ---
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + 128 * wm + 32 * j + lr;
-    if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + 128 * wn + 32 * i + 8 * q + 4 * lg;
-        if (n >= N) continue;
-        if (p.splits == 1) {
-          u32x2_t o;
-          o[0] = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-          o[1] = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<u32x2_t*>(p.y + m * N + n) = o;
-        } else {
-          f32x4_t o = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                       acc[i][j][4 * q + 3]};
-          *reinterpret_cast<f32x4_t*>(p.part + ((int64_t)z * M + m) * N + n) = o;
-        }
-      }
-    }
-  }
+  // --- epilogue: D[n][m] -> y[m][n] (or the split's fp32 partial) ---
+  __syncthreads();  // the LDS stages are free from here on
+  float* scratch = reinterpret_cast<float*>(&lds[0][0][0]) + wave * kEpiFloats;
+  store_acc_tile(acc, scratch, n0 + 128 * wn, m0 + 128 * wm, N, M, p.splits > 1,
+                 p.splits > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
 }
 
 // out[i] = bf16(sum_z part[z][i]), i over M*N (4 per thread), fixed order.

@@ -12,7 +12,7 @@ namespace qlora {
 
 // quant_kernels.hip
 hipError_t launch_quantize(const float* w, int64_t n, uint8_t* codes, float* absmax,
-                           const Nf4Thresholds& T, hipStream_t s);
+                           const Nf4CodeBins& bins, hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* qscale,
                                float* step, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
@@ -21,14 +21,17 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const flo
 // lora_kernels.hip -- rank-r kernels of the adapter path
 // lora_proj: out[m][j] = hi, out[m][r + j] = lo, the bf16 pair of
 // v = scale * sum_k X[m][k] * Y(j, k), with Y(j, k) = Y[j * Kred + k]
-// (kmajor == 0, A [r, Kred]) or Y[k * r + j] (kmajor == 1, B [Kred, r]).
-// With splits > 1 the k range is split over blocks writing fp32 partials
-// P [splits][M][r], added in split order by a second kernel.
+// (kmajor == 0, A [r, Kred]) or Y[k * r + j] (kmajor == 1, B [Kred, r]);
+// also outT[j][m] = hi, outT[r + j][m] = lo with rows of Mp = M rounded up
+// to 32 (zero past M).  With splits > 1 the k range is split over blocks
+// writing fp32 partials P [splits][M][r], added in split order by a second
+// kernel.
 constexpr int kProjMaxSplits = 16;
 struct LoraProjJob {
   const uint16_t* X;  // [M, Kred] bf16
   const uint16_t* Y;
   uint16_t* out;      // [M, 2r] bf16
+  uint16_t* outT;     // [2r, Mp] bf16
   float* P;           // [splits][M][r] fp32 (splits > 1)
   int64_t Kred;
   int kmajor;
@@ -38,14 +41,14 @@ int lora_proj_splits(int64_t M, int64_t Kred, int r, int njobs);
 // one job, or two in one launch (j1 non-null)
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                             float scale, int splits, hipStream_t s);
-// lora_grad: C (+)= sum_m G[m][g] * (S[m][j] + S[m][r + j]), C [ldg, r]
+// lora_grad: C (+)= sum_m G[m][g] * (ST[j][m] + ST[r + j][m]), C [ldg, r]
 // (transposed == 0) or [r, ldg] (transposed == 1); both jobs in one launch.
 // With splits > 1 the tokens are split over blocks writing fp32 partials
 // Cp [splits][C's layout], added to C in split order by a second kernel.
 constexpr int kGradMaxSplits = 16;
 struct LoraGradJob {
-  const uint16_t* G;  // [M, ldg] bf16, ldg a multiple of 64
-  const uint16_t* S;  // [M, 2r] bf16 (hi | lo)
+  const uint16_t* G;   // [M, ldg] bf16, ldg a multiple of 64
+  const uint16_t* ST;  // [2r, Mp] bf16 (hi rows, then lo rows), zero past M
   float* C;
   float* Cp;          // [splits][ldg * r] fp32 (splits > 1)
   int64_t ldg;

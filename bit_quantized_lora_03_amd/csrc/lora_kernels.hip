@@ -8,7 +8,9 @@
 //    [r, Kred] (A, for x . A^T) or [Kred, r] (B, for dy . B).  split(v)
 //    stores hi = bf16(v) and lo = bf16(v - hi) as out[m][j] and
 //    out[m][r + j]; hi + lo equals the fp32 value to 2^-17 relative, so the
-//    rank-r product can ride on bf16 MFMA inside the fused GEMMs.
+//    rank-r product can ride on bf16 MFMA inside the fused GEMMs.  A second
+//    copy, outT [2r][Mp] (tokens contiguous, Mp = M rounded up to 32, zero
+//    past M), feeds lora_grad.
 //  * lora_grad: C (+)= G^T . (S_hi + S_lo) with the reduction over the
 //    tokens: dB [N, r] = dy^T . xs and dA [r, K] = gs^T . x.
 //
@@ -29,34 +31,49 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+__host__ __device__ __forceinline__ int64_t pad32(int64_t M) { return (M + 31) / 32 * 32; }
+
+// Store the bf16 pair of v for (m, j) in both layouts (m < Mp; rows past M
+// only get zeros in the transposed copy).
+__device__ __forceinline__ void put_split(const LoraProjJob& J, int64_t M, int r, int64_t m,
+                                          int j, float v) {
+  const int64_t Mp = pad32(M);
+  uint16_t hi = 0, lo = 0;
+  if (m < M) {
+    hi = bf16_rne_bits(v);
+    lo = bf16_rne_bits(v - bf16_bits_to_f32(hi));  // v - hi is exact
+    J.out[m * 2 * r + j] = hi;
+    J.out[m * 2 * r + r + j] = lo;
+  }
+  J.outT[(int64_t)j * Mp + m] = hi;
+  J.outT[(int64_t)(r + j) * Mp + m] = lo;
+}
+
 // ---------------------------------------------------------------------------
-// lora_proj: grid (njobs * ceil(M/16) * ceil(r/16) * splits), 256 threads.
-// A block owns 16 tokens x 16 rank columns of one job and the z-th share of
+// lora_proj: grid (njobs * Mp/16 * ceil(r/16) * splits), 256 threads.  A
+// block owns 16 tokens x 16 rank columns of one job and the z-th share of
 // the reduction; wave w takes the 32-wide k steps w, w + 4, ... of that
-// share and runs 16x16x32 MFMA straight from global memory: the token
-// operand is one 16-byte load per lane (8 consecutive k of a row), and so is
-// A's operand; B ([Kred, r]) is gathered as 8 two-byte loads per lane.  With
-// one split the block writes the bf16 pair itself; otherwise it writes an
-// fp32 partial P[z][m][j] and lora_proj_finalize adds the shares in order.
-// Many small blocks keep enough loads in flight across the chip; a few big
-// ones would leave the reduction latency-bound.
+// share and runs 16x16x32 MFMA.  The token operand is one 16-byte load per
+// lane (8 consecutive k of a row), and so is A's operand.  B ([Kred, r]) is
+// read as 16-byte row pieces (8 rank columns of one k) and turned around in
+// a small LDS tile of the wave's own.  With one split the block writes the
+// bf16 pairs itself; otherwise it writes an fp32 partial P[z][m][j] and
+// lora_proj_finalize adds the shares in order.  Many small blocks keep
+// enough loads in flight across the chip.
 // ---------------------------------------------------------------------------
 constexpr int kProjWaves = 4;
 constexpr int kProjBatch = 4;  // k steps per register set
+constexpr int kProjTRow = 40;  // transpose tile row: 32 k + 8 pad (bf16), 80 bytes
 
 __global__ __launch_bounds__(kProjWaves * 64) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
                                                                     int64_t blocks_per_job,
                                                                     int64_t M, int r, float scale,
                                                                     int splits) {
   __shared__ float red[kProjWaves][16][17];
+  __shared__ __align__(16) uint16_t tt[kProjWaves][16 * kProjTRow];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool second = (int64_t)blockIdx.x >= blocks_per_job;
-  const uint16_t* X = second ? j1.X : j0.X;
-  const uint16_t* Y = second ? j1.Y : j0.Y;
-  uint16_t* out = second ? j1.out : j0.out;
-  const int64_t Kred = second ? j1.Kred : j0.Kred;
-  const int kmajor = second ? j1.kmajor : j0.kmajor;
-  float* P = second ? j1.P : j0.P;
+  const LoraProjJob J = second ? j1 : j0;
 
   const int jblocks = (r + 15) / 16;
   const int64_t b0 = second ? (int64_t)blockIdx.x - blocks_per_job : (int64_t)blockIdx.x;
@@ -69,28 +86,25 @@ __global__ __launch_bounds__(kProjWaves * 64) void lora_proj_kernel(LoraProjJob 
   const bool mok = m < M;
   const int jj = jc + i;
   const bool jok = jj < r;
+  // B row pieces: lane loads k = k0 + lane / 2, columns jc + 8 (lane % 2) + e
+  const int bcol = jc + 8 * (lane & 1);
+  const bool bok = bcol < r;
+  const int64_t Kred = J.Kred;
   const int64_t nsteps = Kred / 32;
   const int64_t st0 = nsteps * z / splits, st1 = nsteps * (z + 1) / splits;
   const int64_t ns = st1 - st0 > wave ? (st1 - st0 - wave + kProjWaves - 1) / kProjWaves : 0;
-  const uint16_t* xrow = X + (mok ? m : 0) * Kred + 8 * kg;
+  const uint16_t* xrow = J.X + (mok ? m : 0) * Kred + 8 * kg;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  uint16_t* tile = tt[wave];
 
-  // operands of this wave's s-th k step
+  // operands of this wave's s-th k step (B: the raw row piece)
   auto load = [&](int64_t s, u32x4_t& xv, u32x4_t& yv) {
     const int64_t k0 = 32 * (st0 + wave + (int64_t)kProjWaves * s);
     xv = mok ? *reinterpret_cast<const u32x4_t*>(xrow + k0) : zero;
-    if (!kmajor) {
-      yv = jok ? *reinterpret_cast<const u32x4_t*>(Y + (int64_t)jj * Kred + k0 + 8 * kg) : zero;
-    } else {
-      const uint16_t* yc = Y + (k0 + 8 * kg) * r + (jok ? jj : 0);
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = jok ? (uint32_t)yc[(int64_t)e * r] : 0u;
-      yv[0] = h[0] | (h[1] << 16);
-      yv[1] = h[2] | (h[3] << 16);
-      yv[2] = h[4] | (h[5] << 16);
-      yv[3] = h[6] | (h[7] << 16);
-    }
+    if (!J.kmajor)
+      yv = jok ? *reinterpret_cast<const u32x4_t*>(J.Y + (int64_t)jj * Kred + k0 + 8 * kg) : zero;
+    else
+      yv = bok ? *reinterpret_cast<const u32x4_t*>(J.Y + (k0 + (lane >> 1)) * r + bcol) : zero;
   };
   const int64_t nb = (ns + kProjBatch - 1) / kProjBatch;
   auto load_batch = [&](int64_t bi, u32x4_t (&xv)[kProjBatch], u32x4_t (&yv)[kProjBatch]) {
@@ -108,7 +122,18 @@ __global__ __launch_bounds__(kProjWaves * 64) void lora_proj_kernel(LoraProjJob 
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   auto mma_batch = [&](const u32x4_t (&xv)[kProjBatch], const u32x4_t (&yv)[kProjBatch]) {
 #pragma unroll
-    for (int u = 0; u < kProjBatch; ++u) acc = mfma16x16x32(xv[u], yv[u], acc);
+    for (int u = 0; u < kProjBatch; ++u) {
+      u32x4_t b = yv[u];
+      if (J.kmajor) {
+        // row piece -> tile[col][k]; then lane (col i, k group kg) reads its 8 k
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          tile[(8 * (lane & 1) + e) * kProjTRow + (lane >> 1)] =
+              (uint16_t)(yv[u][e >> 1] >> (16 * (e & 1)));
+        b = *reinterpret_cast<const u32x4_t*>(tile + i * kProjTRow + 8 * kg);
+      }
+      acc = mfma16x16x32(xv[u], b, acc);
+    }
   };
 
   // two register sets: batch b + 1 loads while batch b multiplies
@@ -127,58 +152,49 @@ __global__ __launch_bounds__(kProjWaves * 64) void lora_proj_kernel(LoraProjJob 
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[wave][4 * kg + v][i] = acc[v];
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int mm = threadIdx.x >> 4, j = threadIdx.x & 15;
-    float sum = 0.0f;
+  const int mm = threadIdx.x >> 4, j = threadIdx.x & 15;
+  float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kProjWaves; ++w) sum += red[w][mm][j];
-    const int64_t mo = m0 + mm;
-    const int jo = jc + j;
-    if (mo < M && jo < r) {
-      if (splits == 1) {
-        const float v = scale * sum;
-        const uint16_t hi = bf16_rne_bits(v);
-        const uint16_t lo = bf16_rne_bits(v - bf16_bits_to_f32(hi));  // v - hi is exact
-        out[mo * 2 * r + jo] = hi;
-        out[mo * 2 * r + r + jo] = lo;
-      } else {
-        P[((int64_t)z * M + mo) * r + jo] = sum;
-      }
-    }
+  for (int w = 0; w < kProjWaves; ++w) sum += red[w][mm][j];
+  const int64_t mo = m0 + mm;
+  const int jo = jc + j;
+  if (jo < r) {
+    if (splits == 1)
+      put_split(J, M, r, mo, jo, scale * sum);
+    else if (mo < M)
+      J.P[((int64_t)z * M + mo) * r + jo] = sum;
   }
 }
 
-// out = bf16 pair of scale * sum_z P[z] (z in order); grid-stride over both
-// jobs' M x r values.
+// bf16 pairs of scale * sum_z P[z] (z in order); grid-stride over both
+// jobs' Mp x r values (rows past M get zeros in the transposed copy).
 __global__ __launch_bounds__(256) void lora_proj_finalize_kernel(LoraProjJob j0, LoraProjJob j1,
                                                                  int njobs, int64_t M, int r,
                                                                  float scale, int splits) {
-  const int64_t per = M * r, total = per * njobs;
+  const int64_t per = pad32(M) * r, total = per * njobs;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const bool second = e >= per;
-    const float* P = second ? j1.P : j0.P;
-    uint16_t* out = second ? j1.out : j0.out;
+    const LoraProjJob J = second ? j1 : j0;
     const int64_t ee = second ? e - per : e;
-    float v[16];
-#pragma unroll
-    for (int z = 0; z < 16; ++z) v[z] = z < splits ? P[(int64_t)z * per + ee] : 0.0f;
-    float sum = v[0];
-#pragma unroll
-    for (int z = 1; z < 16; ++z)
-      if (z < splits) sum += v[z];
-    const float t = scale * sum;
-    const uint16_t hi = bf16_rne_bits(t);
-    const uint16_t lo = bf16_rne_bits(t - bf16_bits_to_f32(hi));
     const int64_t m = ee / r;
     const int j = (int)(ee - m * r);
-    out[m * 2 * r + j] = hi;
-    out[m * 2 * r + r + j] = lo;
+    float sum = 0.0f;
+    if (m < M) {
+      float v[16];
+#pragma unroll
+      for (int z = 0; z < 16; ++z) v[z] = z < splits ? J.P[((int64_t)z * M + m) * r + j] : 0.0f;
+      sum = v[0];
+#pragma unroll
+      for (int z = 1; z < 16; ++z)
+        if (z < splits) sum += v[z];
+    }
+    put_split(J, M, r, m, j, scale * sum);
   }
 }
 
 int lora_proj_splits(int64_t M, int64_t Kred, int r, int njobs) {
-  const int64_t tiles = ((M + 15) / 16) * ((r + 15) / 16) * njobs;
+  const int64_t tiles = (pad32(M) / 16) * ((r + 15) / 16) * njobs;
   int64_t s = (1024 + tiles - 1) / tiles;
   const int64_t cap = Kred / 256;  // at least 8 k steps (2 per wave) per block
   if (s > cap) s = cap;
@@ -189,13 +205,15 @@ int lora_proj_splits(int64_t M, int64_t Kred, int r, int njobs) {
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                             float scale, int splits, hipStream_t s) {
   const int njobs = j1 ? 2 : 1;
-  const int64_t per_job = ((M + 15) / 16) * ((r + 15) / 16) * splits;
+  // Mp / 16 row blocks, so that the blocks (one split) or the finalize pass
+  // cover every row of the transposed copy
+  const int64_t per_job = (pad32(M) / 16) * ((r + 15) / 16) * splits;
   if (per_job == 0) return hipSuccess;
   hipLaunchKernelGGL(lora_proj_kernel, dim3((unsigned)(per_job * njobs)), dim3(kProjWaves * 64), 0,
                      s, j0, j1 ? *j1 : j0, per_job, M, r, scale, splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  int64_t g = (M * r * njobs + 255) / 256;
+  int64_t g = (pad32(M) * r * njobs + 255) / 256;
   if (g > 2048) g = 2048;
   hipLaunchKernelGGL(lora_proj_finalize_kernel, dim3((unsigned)g), dim3(256), 0, s, j0,
                      j1 ? *j1 : j0, njobs, M, r, scale, splits);
@@ -205,119 +223,109 @@ hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_
 // ---------------------------------------------------------------------------
 // lora_grad: grid ((ldg0 / 64 + ldg1 / 64) * splits), 256 threads.  A block
 // owns 64 columns g of the big operand G (dy for dB, x for dA), all r
-// columns of the small operand S = [hi | lo] (in chunks of 64) and the z-th
-// share of the tokens.  Wave w takes the 32-token steps w, w + 4, ... of
-// that share: it loads the step's G and S rows, stores them transposed
-// (tokens contiguous) in its own LDS tile, and reads 16-byte MFMA operands
-// back (16x16x32: G columns as rows, S columns as columns; hi and lo are two
-// MFMAs on the same G operand).  No barrier is needed inside the loop: a
-// wave's LDS accesses are executed in order and no other wave touches its
-// tile.  With one split the block writes C itself; otherwise it writes the
-// partial Cp[z] (C's layout) and lora_grad_finalize adds them in order.
+// columns of the small operand S (in chunks of 16 JT) and the z-th share of the
+// tokens.  Wave w takes the 32-token steps w, w + 4, ... of that share.  G
+// is token-major, so the wave stores each step's G rows transposed (tokens
+// contiguous) in its own LDS tile and reads 16-byte MFMA operands back; S
+// comes from the transposed copy ST [2r][Mp] as direct 16-byte loads.
+// 16x16x32 MFMA with G columns as rows and S columns as columns; hi and lo
+// are two MFMAs on the same G operand.  No barrier is needed inside the
+// loop: a wave's LDS accesses are executed in order and no other wave
+// touches its tile.  With one split the block writes C itself; otherwise it
+// writes the partial Cp[z] (C's layout) and lora_grad_finalize adds them in
+// order.
 // ---------------------------------------------------------------------------
-constexpr int kGradRow = 40;                  // LDS row: 32 tokens + 8 pad (bf16), 80 bytes
-constexpr int kGradTile = 192 * kGradRow;     // rows 0..63 G, 64..127 S hi, 128..191 S lo
-constexpr int kGradRed = 68;                  // fp32 row stride of the cross-wave reduction
+constexpr int kGradRow = 40;               // LDS row: 32 tokens + 8 pad (bf16), 80 bytes
+constexpr int kGradTile = 64 * kGradRow;   // one wave's transposed G step
+constexpr int kGradRed = 68;               // fp32 row stride of the cross-wave reduction
 
+// JT: 16-column groups of S held per step (1, 2 or 4), so small ranks keep
+// few registers and more blocks fit on a CU.
+template <int JT>
 __global__ __launch_bounds__(256) void lora_grad_kernel(LoraGradJob j0, LoraGradJob j1,
                                                         int64_t blocks0, int64_t M, int r,
                                                         int accumulate, int splits) {
-  __shared__ __align__(16) uint16_t smem[2 * 4 * 64 * kGradRed];  // 69632 B
+  __shared__ __align__(16) float red[4 * 64 * kGradRed];  // 69632 B; the tiles alias its start
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const bool second = (int64_t)blockIdx.x >= blocks0;
-  const uint16_t* G = second ? j1.G : j0.G;
-  const uint16_t* S = second ? j1.S : j0.S;
-  const int64_t ldg = second ? j1.ldg : j0.ldg;
-  const int transposed = second ? j1.transposed : j0.transposed;
+  const LoraGradJob J = second ? j1 : j0;
+  const int64_t ldg = J.ldg;
   const int64_t bb = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
   const int z = (int)(bb % splits);
   const int64_t g0 = 64 * (bb / splits);
-  float* C = splits == 1 ? (second ? j1.C : j0.C)
-                         : (second ? j1.Cp : j0.Cp) + (int64_t)z * ldg * r;
+  float* C = splits == 1 ? J.C : J.Cp + (int64_t)z * ldg * r;
   const int acc_out = splits == 1 ? accumulate : 0;
 
-  uint16_t* tile = smem + wave * kGradTile;
-  float* red = reinterpret_cast<float*>(smem);  // [4][64][kGradRed], after the token loop
-  const int tk = lane & 31, ch = lane >> 5;     // token of a step, chunk parity
-  const int i = lane & 15, kg = lane >> 4;      // MFMA operand lane coordinates
-  const int64_t nst = (M + 31) / 32;
+  uint16_t* tile = reinterpret_cast<uint16_t*>(red) + wave * kGradTile;
+  const int tk = lane & 31, ch = lane >> 5;  // token of a step, chunk parity
+  const int i = lane & 15, kg = lane >> 4;   // MFMA operand lane coordinates
+  const int64_t Mp = pad32(M);
+  const int64_t nst = Mp / 32;
   const int64_t st0 = nst * z / splits, st1 = nst * (z + 1) / splits;
   const int64_t ns = st1 - st0 > wave ? (st1 - st0 - wave + 3) / 4 : 0;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
-  for (int jc = 0; jc < r; jc += 64) {
-    const int R = r - jc < 64 ? r - jc : 64;  // multiple of 8
-    const int R8 = R / 8;
+  for (int jc = 0; jc < r; jc += 16 * JT) {
+    const int R = r - jc < 16 * JT ? r - jc : 16 * JT;  // multiple of 8
 
-    // step s of this wave: tokens 32 (st0 + wave + 4 s) + tk; G chunk c = ch + 2u
-    // (8 columns), S chunk cc = ch + 2u (hi chunks first, then lo chunks)
-    auto load_step = [&](int64_t s, u32x4_t (&gv)[4], u32x4_t (&sv)[8]) {
-      const int64_t m = 32 * (st0 + wave + 4 * s) + tk;
+    // step s of this wave: tokens t0 + tk with t0 = 32 (st0 + wave + 4 s);
+    // G chunk c = ch + 2u (8 columns); S operands of the 16-column groups
+    auto load_step = [&](int64_t s, u32x4_t (&gv)[4], u32x4_t (&sh)[JT], u32x4_t (&sl)[JT]) {
+      const int64_t t0 = 32 * (st0 + wave + 4 * s);
+      const int64_t m = t0 + tk;
       const bool ok = m < M;
-      const uint16_t* grow = G + (ok ? m : 0) * ldg + g0;
-      const uint16_t* srow = S + (ok ? m : 0) * 2 * r;
+      const uint16_t* grow = J.G + (ok ? m : 0) * ldg + g0;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         gv[u] = ok ? *reinterpret_cast<const u32x4_t*>(grow + 8 * (ch + 2 * u)) : zero;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (u < R8) {
-          const int cc = ch + 2 * u;
-          const int col = cc < R8 ? jc + 8 * cc : r + jc + 8 * (cc - R8);
-          sv[u] = ok ? *reinterpret_cast<const u32x4_t*>(srow + col) : zero;
+      for (int jt = 0; jt < JT; ++jt) {
+        if (16 * jt < R) {
+          const int col = jc + 16 * jt + i;
+          const bool cok = col < r;
+          const int64_t off = t0 + 8 * kg;
+          sh[jt] = cok ? *reinterpret_cast<const u32x4_t*>(J.ST + (int64_t)col * Mp + off) : zero;
+          sl[jt] = cok ? *reinterpret_cast<const u32x4_t*>(J.ST + (int64_t)(r + col) * Mp + off)
+                       : zero;
+        } else {
+          sh[jt] = zero;
+          sl[jt] = zero;
         }
       }
     };
-    auto put8 = [&](int row, const u32x4_t& v) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        tile[(row + e) * kGradRow + tk] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-    };
-    auto store_step = [&](const u32x4_t (&gv)[4], const u32x4_t (&sv)[8]) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) put8(8 * (ch + 2 * u), gv[u]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (u < R8) {
-          const int cc = ch + 2 * u;
-          put8(cc < R8 ? 64 + 8 * cc : 128 + 8 * (cc - R8), sv[u]);
-        }
-      }
-    };
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][JT];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    auto mma_step = [&]() {
+      for (int b = 0; b < JT; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto mma_step = [&](const u32x4_t (&gv)[4], const u32x4_t (&sh)[JT], const u32x4_t (&sl)[JT]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          tile[(8 * (ch + 2 * u) + e) * kGradRow + tk] = (uint16_t)(gv[u][e >> 1] >> (16 * (e & 1)));
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const u32x4_t a =
             *reinterpret_cast<const u32x4_t*>(tile + (16 * gi + i) * kGradRow + 8 * kg);
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < JT; ++jt) {
           if (16 * jt < R) {
-            const u32x4_t bh =
-                *reinterpret_cast<const u32x4_t*>(tile + (64 + 16 * jt + i) * kGradRow + 8 * kg);
-            const u32x4_t bl =
-                *reinterpret_cast<const u32x4_t*>(tile + (128 + 16 * jt + i) * kGradRow + 8 * kg);
-            acc[gi][jt] = mfma16x16x32(a, bh, acc[gi][jt]);
-            acc[gi][jt] = mfma16x16x32(a, bl, acc[gi][jt]);
+            acc[gi][jt] = mfma16x16x32(a, sh[jt], acc[gi][jt]);
+            acc[gi][jt] = mfma16x16x32(a, sl[jt], acc[gi][jt]);
           }
         }
       }
     };
 
-    u32x4_t G0[4], S0[8], G1[4], S1[8];
-    if (ns > 0) load_step(0, G0, S0);
+    u32x4_t G0[4], H0[JT], L0[JT], G1[4], H1[JT], L1[JT];
+    if (ns > 0) load_step(0, G0, H0, L0);
     for (int64_t s = 0; s < ns; s += 2) {
-      if (s + 1 < ns) load_step(s + 1, G1, S1);
-      store_step(G0, S0);
-      mma_step();
+      if (s + 1 < ns) load_step(s + 1, G1, H1, L1);
+      mma_step(G0, H0, L0);
       if (s + 1 < ns) {
-        if (s + 2 < ns) load_step(s + 2, G0, S0);
-        store_step(G1, S1);
-        mma_step();
+        if (s + 2 < ns) load_step(s + 2, G0, H0, L0);
+        mma_step(G1, H1, L1);
       }
     }
 
@@ -326,7 +334,7 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(LoraGradJob j0, LoraGrad
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt)
+      for (int jt = 0; jt < JT; ++jt)
         if (16 * jt < R)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
@@ -334,14 +342,14 @@ __global__ __launch_bounds__(256) void lora_grad_kernel(LoraGradJob j0, LoraGrad
     __syncthreads();
     for (int e = threadIdx.x; e < 64 * R; e += 256) {
       // consecutive threads write consecutive addresses of C
-      const int gl = transposed ? (e & 63) : e / R;
-      const int j = transposed ? (e >> 6) : e % R;
+      const int gl = J.transposed ? (e & 63) : e / R;
+      const int j = J.transposed ? (e >> 6) : e % R;
       const float sum = ((red[(0 * 64 + gl) * kGradRed + j] + red[(1 * 64 + gl) * kGradRed + j]) +
                          red[(2 * 64 + gl) * kGradRed + j]) +
                         red[(3 * 64 + gl) * kGradRed + j];
       const int64_t g = g0 + gl;
       const int jo = jc + j;
-      float* c = transposed ? C + (int64_t)jo * ldg + g : C + g * r + jo;
+      float* c = J.transposed ? C + (int64_t)jo * ldg + g : C + g * r + jo;
       *c = acc_out ? *c + sum : sum;
     }
     __syncthreads();  // before the next chunk overwrites the tiles
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(256) void lora_grad_finalize_kernel(LoraGradJob j0,
 
 int lora_grad_splits(int64_t M, int64_t ldg0, int64_t ldg1) {
   const int64_t blocks = ldg0 / 64 + ldg1 / 64;
-  const int64_t nst = (M + 31) / 32;
+  const int64_t nst = pad32(M) / 32;
   int64_t s = blocks > 0 ? (512 + blocks - 1) / blocks : 1;
   if (s > nst / 4) s = nst / 4;  // at least one 32-token step per wave
   if (s > kGradMaxSplits) s = kGradMaxSplits;
@@ -384,8 +392,16 @@ hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_
                             int accumulate, int splits, hipStream_t s) {
   const int64_t b0 = j0.ldg / 64, b1 = j1.ldg / 64;
   if (b0 + b1 == 0 || r == 0) return hipSuccess;
-  hipLaunchKernelGGL(lora_grad_kernel, dim3((unsigned)((b0 + b1) * splits)), dim3(256), 0, s, j0,
-                     j1, b0 * splits, M, r, accumulate, splits);
+  const dim3 grid((unsigned)((b0 + b1) * splits));
+  if (r <= 16)
+    hipLaunchKernelGGL(lora_grad_kernel<1>, grid, dim3(256), 0, s, j0, j1, b0 * splits, M, r,
+                       accumulate, splits);
+  else if (r <= 32)
+    hipLaunchKernelGGL(lora_grad_kernel<2>, grid, dim3(256), 0, s, j0, j1, b0 * splits, M, r,
+                       accumulate, splits);
+  else
+    hipLaunchKernelGGL(lora_grad_kernel<4>, grid, dim3(256), 0, s, j0, j1, b0 * splits, M, r,
+                       accumulate, splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   int64_t g = ((j0.ldg + j1.ldg) * r + 255) / 256;

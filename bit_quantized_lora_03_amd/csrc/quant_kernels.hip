@@ -19,11 +19,25 @@ namespace qlora {
 // ---------------------------------------------------------------------------
 // Quantiser: each lane owns 8 consecutive weights (two 16-byte loads), so 8
 // lanes cover one 64-weight block and a wave covers 8 blocks.  The block's
-// absmax is a max over the 8 lanes (xor shuffles inside the 8-lane group).
+// absmax m is a max over the 8 lanes (xor shuffles inside the 8-lane group).
+//
+// u = fl32(w / m) is formed without a division per weight: with
+// y = fl32(1 / m), q = fl32(w * y) is within one ulp of w / m, the residual
+// w - q * m is exact in one fma, and fl32(q + residual * y) is the correctly
+// rounded quotient (Markstein's correction step; it needs no underflow, so
+// blocks with m outside [2^-60, 2^60] divide directly).  The code is then
+// base[bin(u)] + (u > thr[bin(u)]) from a 64-entry table in LDS: one
+// comparison per weight instead of fifteen.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void nf4_quantize_kernel(
     const float* __restrict__ w, int64_t n, uint8_t* __restrict__ codes,
-    float* __restrict__ absmax, Nf4Thresholds T) {
+    float* __restrict__ absmax, Nf4CodeBins bins) {
+#pragma clang fp contract(off)
+  __shared__ uint2 tab[64];
+  if (threadIdx.x < 64)
+    tab[threadIdx.x] = make_uint2(__float_as_uint(bins.thr[threadIdx.x]), bins.base[threadIdx.x]);
+  __syncthreads();
+
   const int64_t lanes_total = (n + 7) >> 3;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -47,16 +61,25 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(
     m = fmaxf(m, __shfl_xor(m, 2, 8));
     m = fmaxf(m, __shfl_xor(m, 4, 8));
 
+    float u[8];
+    if (m >= 0x1p-60f && m <= 0x1p60f) {
+      const float y = __fdiv_rn(1.0f, m);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q = v[i] * y;
+        const float res = __builtin_fmaf(-q, m, v[i]);  // exact
+        u[i] = __builtin_fmaf(res, y, q);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) u[i] = __fdiv_rn(v[i], m);
+    }
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t c = 7;
-      if (m > 0.0f && e0 + i < n) {
-        const float u = __fdiv_rn(v[i], m);  // IEEE correctly rounded
-        c = 0;
-#pragma unroll
-        for (int k = 0; k < 15; ++k) c += (u > T.t[k]) ? 1u : 0u;
-      }
+      const uint2 t = tab[nf4_bin(u[i])];
+      uint32_t c = t.y + (u[i] > __uint_as_float(t.x) ? 1u : 0u);
+      if (!(m > 0.0f) || e0 + i >= n) c = 7;  // zero block, padding
       packed |= c << (4 * i);
     }
     if (e0 < n) {
@@ -142,10 +165,10 @@ static int grid_for(int64_t work_items, int per_block, int cap) {
 }
 
 hipError_t launch_quantize(const float* w, int64_t n, uint8_t* codes, float* absmax,
-                           const Nf4Thresholds& T, hipStream_t s) {
+                           const Nf4CodeBins& bins, hipStream_t s) {
   const int64_t lanes = (n + 7) >> 3;
   const int grid = grid_for(lanes, 256, 256 * 32);
-  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid), dim3(256), 0, s, w, n, codes, absmax, T);
+  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid), dim3(256), 0, s, w, n, codes, absmax, bins);
   return hipGetLastError();
 }
 

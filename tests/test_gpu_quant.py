@@ -58,6 +58,36 @@ def test_quantize_special_values(cuda):
     _assert_bitexact(_special_weight(), "special")
 
 
+def _near_threshold_weight():
+    """Blocks whose absmax is not a power of two, filled with weights whose
+    quotient w / absmax lands on, or a few ulps either side of, each decision
+    threshold: the quotient's last bit decides the code."""
+    rng = np.random.default_rng(101)
+    L = oracle.nf4_levels_f32().astype(np.float64)
+    mids = ((L[:-1] + L[1:]) / 2).astype(np.float32)
+    blocks = []
+    for m in (rng.uniform(0.005, 0.2, 24).astype(np.float32).tolist() + [3.7e-10, 5.1e7]):
+        m = np.float32(m)
+        cand = []
+        for t in mids:
+            base = np.float32(t * m).view(np.int32)
+            for k in range(-3, 4):
+                cand.append(np.array(base + k, dtype=np.int32).view(np.float32))
+        cand = np.array(cand, dtype=np.float32)
+        cand = cand[np.abs(cand) <= m]
+        for i in range(0, cand.size, 63):
+            blk = np.full(64, 0.0, dtype=np.float32)
+            blk[0] = m if i % 2 == 0 else -m
+            chunk = cand[i:i + 63]
+            blk[1:1 + chunk.size] = chunk
+            blocks.append(blk)
+    return np.concatenate(blocks)
+
+
+def test_quantize_near_threshold_quotients(cuda):
+    _assert_bitexact(_near_threshold_weight(), "near-threshold")
+
+
 @pytest.mark.parametrize("n", [1, 7, 8, 63, 64, 65, 127, 1000, 64 * 257 + 13, 64 * 512])
 def test_quantize_ragged_lengths(cuda, n):
     w = workloads.normal_f32(7, n, (n,), 0.02)
