@@ -107,16 +107,21 @@ void dx_gemm_kernel(DxParams p) {
   const uint32_t yoff = (uint32_t)(((m0 + (t >> 3)) * N + 8 * (t & 7)) * 2);
   const uint32_t yrow_step = (uint32_t)(32 * N * 2);
 
+  // The scale byte and its step stay raw until the tile is decoded (an
+  // iteration later): forming s' here would make the wave wait for this
+  // prefetch -- and, since loads return in order, for every load before it.
   struct Codes {
     u32x4_t c0, c1;
-    float s;
+    uint32_t q;
+    float st;
   };
   auto load_codes = [&](int64_t st, Codes& c) {
     const int64_t idx = (st * RT + wr) * K + kcol;  // first element of the block
     const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
     c.c0 = cp[0];
     c.c1 = cp[1];
-    c.s = nf4_block_scale(p.qscale[idx >> 6], p.step[idx >> 14]);
+    c.q = p.qscale[idx >> 6];
+    c.st = p.step[idx >> 14];
   };
   auto load_dy = [&](int64_t st, u32x4_t (&yr)[8]) {
     const uint32_t o = yoff + (uint32_t)(st * RT * 2);
@@ -165,7 +170,7 @@ void dx_gemm_kernel(DxParams p) {
     load_dy(st0, Y[0]);
     store_dy(0, Y[0]);
     {
-      const Nf4Lut lut = nf4_make_lut(p.L, C[0].s);
+      const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(C[0].q, C[0].st));
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         scatter8(0, c, nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]));
@@ -179,7 +184,7 @@ void dx_gemm_kernel(DxParams p) {
       load_dy(cl(st + 2), Y[cur]);
       load_codes(cl(st + 2), C[cur]);
       const Codes& cn = C[nxt];
-      const Nf4Lut lut = nf4_make_lut(p.L, cn.s);
+      const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(cn.q, cn.st));
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         mfma_step(cur, kk);

@@ -103,16 +103,21 @@ void fwd_gemm_kernel(FwdParams p) {
   const uint32_t xoff = (uint32_t)(((m0 + (t >> 3)) * K + 8 * (t & 7)) * 2);
   const uint32_t xrow_step = (uint32_t)(32 * K * 2);
 
+  // The scale byte and its step stay raw until the tile is decoded (an
+  // iteration later): forming s' here would make the wave wait for this
+  // prefetch -- and, since loads return in order, for every load before it.
   struct Codes {
     u32x4_t c0, c1;
-    float s;
+    uint32_t q;
+    float st;
   };
   auto load_codes = [&](int64_t kt, Codes& c) {
     const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(wcodes + kt * (KT / 2));
     c.c0 = cp[0];
     c.c1 = cp[1];
     const int64_t b = wblk0 + kt;
-    c.s = nf4_block_scale(p.qscale[b], p.step[b >> 8]);
+    c.q = p.qscale[b];
+    c.st = p.step[b >> 8];
   };
   auto load_x = [&](int64_t kt, u32x4_t (&xr)[8]) {
     const uint32_t o = xoff + (uint32_t)(kt * KT * 2);
@@ -154,7 +159,7 @@ void fwd_gemm_kernel(FwdParams p) {
     load_x(kt0, X[0]);
     store_x(0, X[0]);
     {
-      const Nf4Lut lut = nf4_make_lut(p.L, C[0].s);
+      const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(C[0].q, C[0].st));
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         lds[0][0][rk(t, c)] = nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]);
@@ -198,8 +203,9 @@ void fwd_gemm_kernel(FwdParams p) {
         if (kk == 0) {
           // the 16-entry table of tile kt+1's block (slots 0..7)
           if (s < 4) {
-            pk[2 * s] = pack_bf16x2(p.L.v[4 * s] * cn.s, p.L.v[4 * s + 1] * cn.s);
-            pk[2 * s + 1] = pack_bf16x2(p.L.v[4 * s + 2] * cn.s, p.L.v[4 * s + 3] * cn.s);
+            const float sc = nf4_block_scale(cn.q, cn.st);
+            pk[2 * s] = pack_bf16x2(p.L.v[4 * s] * sc, p.L.v[4 * s + 1] * sc);
+            pk[2 * s + 1] = pack_bf16x2(p.L.v[4 * s + 2] * sc, p.L.v[4 * s + 3] * sc);
           } else if (s < 8) {
             const int j = s - 4;
             lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
