@@ -54,15 +54,20 @@ struct DxParams {
 
 __device__ __forceinline__ int64_t clamp_row(int64_t v, int64_t hi) { return v < hi ? v : hi - 1; }
 
-// dy tile: [256 m][64 n], rows 128 B, chunk swizzled by row.
-__device__ __forceinline__ int rk(int row, int chunk) { return row * ROW_CHUNKS + (chunk ^ (row & 7)); }
+// dy tile: [256 m][64 n], rows 128 B (an even row covers banks 0..31, an
+// odd one banks 32..63).  A 16-byte read serves 16 consecutive rows at one
+// logical chunk per LDS cycle; xor-swizzling the chunk with (row / 2) mod 8
+// gives each pair of rows its own chunk, so those 16 lanes hit all 64 banks.
+__device__ __forceinline__ int rk(int row, int chunk) {
+  return row * ROW_CHUNKS + (chunk ^ ((row >> 1) & 7));
+}
 
 // W^T tile: [256 k][64 n] bf16, element offset.  The 16-byte n-chunk is
-// swizzled by k's low 3 bits (8 consecutive k rows read at one chunk land
-// in 8 distinct chunks) and by k's 64-block index (the four threads that
+// swizzled by (k / 2) mod 8, as above (16 consecutive k rows read at one
+// chunk hit all banks), and by k's 64-block index (the four threads that
 // decode one weight row at k, k+64, k+128, k+192 write distinct chunks).
 __device__ __forceinline__ int wt_off(int k, int n) {
-  const int chunk = (n >> 3) ^ (k & 7) ^ (((k >> 6) & 3) << 1);
+  const int chunk = (n >> 3) ^ ((k >> 1) & 7) ^ (((k >> 6) & 3) << 1);
   return k * RT + chunk * 8 + (n & 7);
 }
 

@@ -57,10 +57,15 @@ struct FwdParams {
   Nf4Levels L;
 };
 
-// Tile rows are 128 B; the 16-byte chunk index is xor-swizzled with the row
-// so that 8 consecutive rows read at the same logical chunk hit 8 distinct
-// chunk positions (all banks).
-__device__ __forceinline__ int rk(int row, int chunk) { return row * ROW_CHUNKS + (chunk ^ (row & 7)); }
+// Tile rows are 128 B, so an even row covers banks 0..31 and an odd row
+// banks 32..63.  A 16-byte read serves 16 lanes per LDS cycle, here 16
+// consecutive rows at one logical chunk: xor-swizzling the chunk with
+// (row / 2) mod 8 puts each pair of rows at its own chunk, so the 16 lanes
+// cover all 64 banks once (swizzling with row mod 8 would map rows r and
+// r + 8 to the same banks).
+__device__ __forceinline__ int rk(int row, int chunk) {
+  return row * ROW_CHUNKS + (chunk ^ ((row >> 1) & 7));
+}
 
 __device__ __forceinline__ int64_t clamp_row(int64_t v, int64_t hi) { return v < hi ? v : hi - 1; }
 
@@ -193,57 +198,62 @@ void fwd_gemm_kernel(FwdParams p) {
         read_ops(0, 0, 0, i);
         read_ops(0, 0, 1, i);
       }
+      // The 64 MFMA slots of the tile carry, in order: the table of tile
+      // kt+1's block (slots 0..7), the decode of its 8 code words (6 slots
+      // each, about 5 vector ops per slot, then the 16-byte LDS write), and
+      // the LDS writes of its x rows (slots 56..63).  Each slot's vector work
+      // fits in the shadow of one MFMA (32 cycles); the operand reads of
+      // step kk+1 ride in slots 8..15 of step kk.
       uint32_t pk[8];
       Nf4Lut lut;
-      uint32_t dn1 = 0;
+      float sc = 0.0f;
+      uint32_t dn0 = 0, dn1 = 0, nh = 0, pick = 0, la = 0, lb = 0;
       u32x4_t dv = zero;
+      auto lookup_a = [&](uint32_t n) {  // low-byte planes of 4 codes
+        nh = n & 0x07070707u;
+        pick = ((n >> 1) & 0x04040404u) | 0x03020100u;
+        la = perm(lut.lo[1], lut.lo[0], n);
+        lb = perm(lut.lo[3], lut.lo[2], nh);
+      };
+      auto lookup_b = [&](uint32_t n, uint32_t& o01, uint32_t& o23) {  // high bytes, merge
+        const uint32_t lo = perm(lb, la, pick);
+        const uint32_t hi =
+            perm(perm(lut.hi[3], lut.hi[2], nh), perm(lut.hi[1], lut.hi[0], n), pick);
+        o01 = perm(hi, lo, 0x05010400u);
+        o23 = perm(hi, lo, 0x07030602u);
+      };
       auto unit = [&](int kk, int s) {
+        const int slot = 16 * kk + s;
         // operand reads for step kk+1 in slots 8..15
         if (kk < 3 && s >= 8) read_ops(kk + 1, (kk + 1) & 1, (s - 8) >> 2, (s - 8) & 3);
-        if (kk == 0) {
-          // the 16-entry table of tile kt+1's block (slots 0..7)
-          if (s < 4) {
-            const float sc = nf4_block_scale(cn.q, cn.st);
-            pk[2 * s] = pack_bf16x2(p.L.v[4 * s] * sc, p.L.v[4 * s + 1] * sc);
-            pk[2 * s + 1] = pack_bf16x2(p.L.v[4 * s + 2] * sc, p.L.v[4 * s + 3] * sc);
-          } else if (s < 8) {
-            const int j = s - 4;
-            lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
-            lut.hi[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
-          }
-        }
-        // decode chunks 2kk, 2kk+1 of tile kt+1: three units each
-        const int base = kk == 0 ? 8 : 0;
-        const int u = s - base;
-        if (u >= 0 && u < 6) {
-          const int c = 2 * kk + u / 3;
+        if (slot < 4) {
+          if (slot == 0) sc = nf4_block_scale(cn.q, cn.st);
+          pk[2 * slot] = pack_bf16x2(p.L.v[4 * slot] * sc, p.L.v[4 * slot + 1] * sc);
+          pk[2 * slot + 1] = pack_bf16x2(p.L.v[4 * slot + 2] * sc, p.L.v[4 * slot + 3] * sc);
+        } else if (slot < 8) {
+          const int j = slot - 4;
+          lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
+          lut.hi[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
+        } else if (slot < 56) {
+          const int c = (slot - 8) / 6, u = (slot - 8) % 6;
           const uint32_t v = (c < 4 ? cn.c0 : cn.c1)[c & 3];
-          switch (u % 3) {
+          switch (u) {
             case 0: {
               const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
-              const uint32_t dn0 = perm(od, ev, 0x05010400u);
-              dn1 = perm(od, ev, 0x07030602u);
-              uint32_t o0, o1;
-              nf4_lookup4(lut, dn0, o0, o1);
-              dv[0] = o0;
-              dv[1] = o1;
+              dn0 = perm(od, ev, 0x05010400u);  // codes 0..3 of the word, one per byte
+              dn1 = perm(od, ev, 0x07030602u);  // codes 4..7
               break;
             }
-            case 1: {
-              uint32_t o2, o3;
-              nf4_lookup4(lut, dn1, o2, o3);
-              dv[2] = o2;
-              dv[3] = o3;
-              break;
-            }
-            default:
-              lds[nxt][0][rk(t, c)] = dv;
-              break;
+            case 1: lookup_a(dn0); break;
+            case 2: { uint32_t o0, o1; lookup_b(dn0, o0, o1); dv[0] = o0; dv[1] = o1; break; }
+            case 3: lookup_a(dn1); break;
+            case 4: { uint32_t o2, o3; lookup_b(dn1, o2, o3); dv[2] = o2; dv[3] = o3; break; }
+            default: lds[nxt][0][rk(t, c)] = dv; break;
           }
+        } else {
+          // tile kt+1's x rows into the other stage
+          lds[nxt][1][rk((t >> 3) + 32 * (slot - 56), t & 7)] = X[nxt][slot - 56];
         }
-        // tile kt+1's x rows into the other stage
-        if (kk == 3 && s >= 6 && s < 14)
-          lds[nxt][1][rk((t >> 3) + 32 * (s - 6), t & 7)] = X[nxt][s - 6];
       };
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
