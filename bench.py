@@ -81,15 +81,32 @@ def make_layer(name):
     raise SystemExit(f"unknown workload {name}")
 
 
-def _gemm_splits(M, N, Kred):
-    """Mirror of the library's k-split choice for the fused GEMMs (for naming
-    the launches in the roofline line only)."""
-    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+def _fwd_config(M, N, Kred):
+    """Mirror of the library's tile/k-split choice for the fused forward GEMM
+    (for naming the launches in the roofline line only): (token tile, splits)."""
     nkt = Kred // 64
+    n_t = (N + 255) // 256
+    best, best_t = (256, 1), float("inf")
+    for tm in (256, 128):
+        tiles = ((M + tm - 1) // tm) * n_t
+        s = 1 if tiles >= 192 else 256 // tiles
+        s = max(1, min(s, nkt // 4, 16))
+        blocks = tiles * s
+        fill = 1.0 if blocks >= 256 else blocks / 256.0
+        rate = (1.1e15 if tm == 256 else 0.8e15) * fill
+        partial = 2.0 * s * M * N * 4 / 5.0e12 if s > 1 else 0.0
+        est = 2.0 * M * N * Kred / rate + partial
+        if est < best_t:
+            best, best_t = (tm, s), est
+    return best
+
+
+def _dx_splits(M, K, N):
+    """Mirror of the library's k-split choice for the dX GEMM (256 x 256 tiles)."""
+    tiles = ((M + 255) // 256) * ((K + 255) // 256)
     if tiles >= 192:
         return 1
-    s = min(256 // tiles, nkt // 4, 16)
-    return max(1, s)
+    return max(1, min(256 // tiles, (N // 64) // 4, 16))
 
 
 def _source_digest(key):
@@ -345,8 +362,8 @@ def main():
 
     # the unit the roofline line is about: one base-only fused-GEMM call (the
     # GEMM kernel, plus its split-K reduce kernel when the output is small)
-    fsplit = _gemm_splits(M, N, K)
-    dsplit = _gemm_splits(M, K, N)
+    fsplit = _fwd_config(M, N, K)[1]
+    dsplit = _dx_splits(M, K, N)
     if M <= 32:
         # decode: HBM-bound; algorithmic bytes of the base-only launch
         kb = packed_weight_bytes(N, K) + 2 * M * K + 2 * M * N

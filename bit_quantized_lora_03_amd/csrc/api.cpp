@@ -144,7 +144,7 @@ BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
       off = round_up(L.ca_off + (size_t)L.tsplits * r * K * sizeof(float), 256);
     }
   }
-  L.gsplits = qlora::gemm_splits(M, K, N);
+  L.gsplits = qlora::dx_gemm_splits(M, K, N);
   if (L.gsplits > 1) {
     L.part_off = off;
     off = round_up(off + (size_t)L.gsplits * M * K * sizeof(float), 256);

@@ -158,8 +158,8 @@ __device__ __forceinline__ TileCoord xcd_tile(int64_t id, int64_t total, int64_t
   return c;
 }
 
-// Epilogue of the fused GEMMs.  A wave holds a 128 (rows: n or k) x 128
-// (columns: tokens m) fp32 tile as 4 x 4 MFMA 32x32 tiles; lane l holds
+// Epilogue of the fused GEMMs.  A wave holds a 128 (rows: n or k) x 32 MS
+// (columns: tokens m) fp32 tile as 4 x MS MFMA 32x32 tiles; lane l holds
 // column 32 j + l % 32 and rows 32 i + 8 (v / 4) + 4 (l / 32) + v % 4.  The
 // output is token-major (out[m][row]), so storing straight from registers
 // would give every store instruction 32 rows of 16 bytes.  Instead each
@@ -169,7 +169,8 @@ __device__ __forceinline__ TileCoord xcd_tile(int64_t id, int64_t total, int64_t
 // fp32 partials, otherwise values are rounded to bf16.
 constexpr int kEpiStride = 132;
 constexpr int kEpiFloats = 32 * kEpiStride;  // per wave
-__device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[4][4], float* scratch,
+template <int MS>
+__device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[4][MS], float* scratch,
                                                int64_t row0, int64_t col0, int64_t nrows,
                                                int64_t ncols, bool part, float* outf,
                                                uint16_t* outh, int64_t ld, int lane) {
@@ -177,7 +178,7 @@ __device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[4][4], floa
   const int64_t row = row0 + 4 * lr;  // the 4 rows this lane stores
   const bool row_ok = row < nrows;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < MS; ++j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

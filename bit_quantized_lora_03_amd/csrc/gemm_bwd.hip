@@ -243,6 +243,18 @@ void dx_gemm_kernel(DxParams p) {
                  p.splits > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
 }
 
+// k splits of the dX GEMM (256 x 256 tiles): aim for ~256 blocks when the
+// output tiles alone cannot fill the chip, at least 4 reduction stages each.
+int dx_gemm_splits(int64_t M, int64_t K, int64_t N) {
+  const int64_t tiles = ((M + TILE - 1) / TILE) * ((K + TILE - 1) / TILE);
+  const int64_t nst = N / RT;
+  if (tiles >= 192) return 1;
+  int64_t s = 256 / tiles;
+  if (s > nst / 4) s = nst / 4;
+  if (s > 16) s = 16;
+  return s < 1 ? 1 : (int)s;
+}
+
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
                           uint16_t* dx, float* part, int splits, int64_t M, int64_t N, int64_t K,

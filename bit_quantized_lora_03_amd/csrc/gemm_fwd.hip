@@ -71,29 +71,42 @@ __device__ __forceinline__ int64_t clamp_row(int64_t v, int64_t hi) { return v <
 
 }  // namespace
 
+// MS: 32-wide token subtiles per wave.  MS = 4 is the 256 (n) x 256 (m)
+// block tile; MS = 2 halves the token extent (256 x 128), which doubles the
+// number of output tiles for small-M shapes and so halves the k splits (and
+// their fp32 partials) needed to fill the chip.
+template <int MS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(FwdParams p) {
-  __shared__ u32x4_t lds[2][2][TILE_CHUNKS];  // [stage][0 = W, 1 = x]
+  constexpr int TM = 64 * MS;             // token rows of the block tile
+  constexpr int XR = TM / 32;             // x rows staged per thread
+  constexpr int WCH = TILE * ROW_CHUNKS;  // W stage, u32x4
+  constexpr int XCH = TM * ROW_CHUNKS;    // x stage, u32x4
+  __shared__ u32x4_t lds[2][WCH + XCH];   // [stage][W tile | x tile]
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int wn = wave & 1, wm = wave >> 1;
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int64_t m_tiles = (M + TILE - 1) / TILE, n_tiles = (N + TILE - 1) / TILE;
+  const int64_t m_tiles = (M + TM - 1) / TM, n_tiles = (N + TILE - 1) / TILE;
   const TileCoord tc = xcd_tile(blockIdx.x, (int64_t)gridDim.x, m_tiles, n_tiles, 4);
   const int64_t n0 = tc.n * TILE;
-  const int64_t m0 = tc.m * TILE;
+  const int64_t m0 = tc.m * TM;
   const int z = (int)tc.z;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  auto W = [&](int stage, int row, int chunk) -> u32x4_t& { return lds[stage][rk(row, chunk)]; };
+  auto Xl = [&](int stage, int row, int chunk) -> u32x4_t& {
+    return lds[stage][WCH + rk(row, chunk)];
+  };
 
   // k tiles of this split
   const int64_t nkt = K / KT;
   const int64_t kt0 = nkt * z / p.splits, kt1 = nkt * (z + 1) / p.splits;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][MS];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < MS; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -124,26 +137,26 @@ void fwd_gemm_kernel(FwdParams p) {
     c.q = p.qscale[b];
     c.st = p.step[b >> 8];
   };
-  auto load_x = [&](int64_t kt, u32x4_t (&xr)[8]) {
+  auto load_x = [&](int64_t kt, u32x4_t (&xr)[XR]) {
     const uint32_t o = xoff + (uint32_t)(kt * KT * 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xr[j] = buffer_load16(xres, o + j * xrow_step);
+    for (int j = 0; j < XR; ++j) xr[j] = buffer_load16(xres, o + j * xrow_step);
   };
-  auto store_x = [&](int stage, const u32x4_t (&xr)[8]) {
+  auto store_x = [&](int stage, const u32x4_t (&xr)[XR]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) lds[stage][1][rk((t >> 3) + 32 * j, t & 7)] = xr[j];
+    for (int j = 0; j < XR; ++j) Xl(stage, (t >> 3) + 32 * j, t & 7) = xr[j];
   };
   auto mfma_step = [&](int stage, int kk) {
     const int ch = 2 * kk + lg;
-    u32x4_t a[4], b[4];
+    u32x4_t a[4], b[MS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = lds[stage][0][rk(128 * wn + 32 * i + lr, ch)];
+    for (int i = 0; i < 4; ++i) a[i] = W(stage, 128 * wn + 32 * i + lr, ch);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = lds[stage][1][rk(128 * wm + 32 * j + lr, ch)];
+    for (int j = 0; j < MS; ++j) b[j] = Xl(stage, 32 * MS * wm + 32 * j + lr, ch);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < MS; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
   };
 
   if (kt0 < kt1) {
@@ -159,51 +172,48 @@ void fwd_gemm_kernel(FwdParams p) {
     const int64_t last = kt1 - 1;
     auto cl = [&](int64_t v) { return v < last ? v : last; };
     Codes C[2];
-    u32x4_t X[2][8];
+    u32x4_t X[2][XR];
     load_codes(kt0, C[0]);
     load_x(kt0, X[0]);
     store_x(0, X[0]);
     {
       const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(C[0].q, C[0].st));
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        lds[0][0][rk(t, c)] = nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]);
+      for (int c = 0; c < 8; ++c) W(0, t, c) = nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]);
     }
     load_x(cl(kt0 + 1), X[1]);
     load_codes(cl(kt0 + 1), C[1]);
     __syncthreads();
 
     // Hand-scheduled iteration.  Issue is in order, so back-to-back MFMAs
-    // would hold everything behind them; instead each of the 64 MFMAs of a
-    // tile is followed by one small unit of other work and a scheduling
-    // fence: the next k-step's operand reads, a slice of the decode of tile
-    // kt+1 into the other stage, its LDS writes.  The vector work then
-    // executes while the matrix core is busy.
+    // would hold everything behind them; instead each MFMA of the tile is
+    // followed by a small, fixed amount of other work and a scheduling
+    // fence, so the vector work executes while the matrix core is busy.
     auto iteration = [&](int64_t kt, auto parity) {
       constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
+      constexpr int SPK = 4 * MS;       // MFMAs (slots) per k step
+      constexpr int NRD = 4 + MS;       // operand reads per k step
       // tile kt+2 into the free set (loads issued first, used an iteration later)
       load_x(cl(kt + 2), X[cur]);
       load_codes(cl(kt + 2), C[cur]);
       const Codes& cn = C[nxt];
       u32x4_t op[2][2][4];  // [buffer][a|b][i]
-      auto read_ops = [&](int kk, int buf, int which, int i) {
+      auto read_op = [&](int kk, int buf, int q) {
         const int ch = 2 * kk + lg;
-        if (which == 0)
-          op[buf][0][i] = lds[cur][0][rk(128 * wn + 32 * i + lr, ch)];
+        if (q < 4)
+          op[buf][0][q] = W(cur, 128 * wn + 32 * q + lr, ch);
         else
-          op[buf][1][i] = lds[cur][1][rk(128 * wm + 32 * i + lr, ch)];
+          op[buf][1][q - 4] = Xl(cur, 32 * MS * wm + 32 * (q - 4) + lr, ch);
       };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        read_ops(0, 0, 0, i);
-        read_ops(0, 0, 1, i);
-      }
-      // The 64 MFMA slots of the tile carry, in order: the table of tile
-      // kt+1's block (slots 0..7), the decode of its 8 code words (6 slots
-      // each, about 5 vector ops per slot, then the 16-byte LDS write), and
-      // the LDS writes of its x rows (slots 56..63).  Each slot's vector work
-      // fits in the shadow of one MFMA (32 cycles); the operand reads of
-      // step kk+1 ride in slots 8..15 of step kk.
+      for (int q = 0; q < NRD; ++q) read_op(0, 0, q);
+
+      // Work units of the tile, in order: the table of tile kt+1's block
+      // (units 0..7), the decode of its 8 code words (6 units each, about 5
+      // vector ops per unit, the last one the 16-byte LDS write), the LDS
+      // writes of its x rows (units 56..56+XR-1).  MS = 4 runs one unit per
+      // MFMA (each fits in the MFMA's 32-cycle shadow), MS = 2 two.  The
+      // operand reads of step kk+1 ride in the last slots of step kk.
       uint32_t pk[8];
       Nf4Lut lut;
       float sc = 0.0f;
@@ -222,22 +232,19 @@ void fwd_gemm_kernel(FwdParams p) {
         o01 = perm(hi, lo, 0x05010400u);
         o23 = perm(hi, lo, 0x07030602u);
       };
-      auto unit = [&](int kk, int s) {
-        const int slot = 16 * kk + s;
-        // operand reads for step kk+1 in slots 8..15
-        if (kk < 3 && s >= 8) read_ops(kk + 1, (kk + 1) & 1, (s - 8) >> 2, (s - 8) & 3);
-        if (slot < 4) {
-          if (slot == 0) sc = nf4_block_scale(cn.q, cn.st);
-          pk[2 * slot] = pack_bf16x2(p.L.v[4 * slot] * sc, p.L.v[4 * slot + 1] * sc);
-          pk[2 * slot + 1] = pack_bf16x2(p.L.v[4 * slot + 2] * sc, p.L.v[4 * slot + 3] * sc);
-        } else if (slot < 8) {
-          const int j = slot - 4;
+      auto unit = [&](int u) {
+        if (u < 4) {
+          if (u == 0) sc = nf4_block_scale(cn.q, cn.st);
+          pk[2 * u] = pack_bf16x2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
+          pk[2 * u + 1] = pack_bf16x2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
+        } else if (u < 8) {
+          const int j = u - 4;
           lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
           lut.hi[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
-        } else if (slot < 56) {
-          const int c = (slot - 8) / 6, u = (slot - 8) % 6;
+        } else if (u < 56) {
+          const int c = (u - 8) / 6, w = (u - 8) % 6;
           const uint32_t v = (c < 4 ? cn.c0 : cn.c1)[c & 3];
-          switch (u) {
+          switch (w) {
             case 0: {
               const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
               dn0 = perm(od, ev, 0x05010400u);  // codes 0..3 of the word, one per byte
@@ -248,20 +255,24 @@ void fwd_gemm_kernel(FwdParams p) {
             case 2: { uint32_t o0, o1; lookup_b(dn0, o0, o1); dv[0] = o0; dv[1] = o1; break; }
             case 3: lookup_a(dn1); break;
             case 4: { uint32_t o2, o3; lookup_b(dn1, o2, o3); dv[2] = o2; dv[3] = o3; break; }
-            default: lds[nxt][0][rk(t, c)] = dv; break;
+            default: W(nxt, t, c) = dv; break;
           }
-        } else {
+        } else if (u < 56 + XR) {
           // tile kt+1's x rows into the other stage
-          lds[nxt][1][rk((t >> 3) + 32 * (slot - 56), t & 7)] = X[nxt][slot - 56];
+          Xl(nxt, (t >> 3) + 32 * (u - 56), t & 7) = X[nxt][u - 56];
         }
       };
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          const int i = s >> 2, j = s & 3;
+        for (int s = 0; s < SPK; ++s) {
+          const int i = s / MS, j = s % MS;
           acc[i][j] = mfma32x32x16(op[kk & 1][0][i], op[kk & 1][1][j], acc[i][j]);
-          unit(kk, s);
+          const int slot = SPK * kk + s;
+          if (kk < 3 && s >= SPK - NRD) read_op(kk + 1, (kk + 1) & 1, s - (SPK - NRD));
+          constexpr int UPS = 16 / SPK;  // units per slot: 64 units over 4 SPK slots
+#pragma unroll
+          for (int e = 0; e < UPS; ++e) unit(UPS * slot + e);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -277,7 +288,7 @@ void fwd_gemm_kernel(FwdParams p) {
   const int r = p.r;
   if (z == p.splits - 1) {
     const int ext_tiles = (2 * r + KT - 1) / KT;
-    const int64_t m = clamp_row(m0 + t, M);
+    const int64_t m = clamp_row(m0 + (t % TM), M);
     for (int e = 0; e < ext_tiles; ++e) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -288,8 +299,8 @@ void fwd_gemm_kernel(FwdParams p) {
           wv = *reinterpret_cast<const u32x4_t*>(p.B + wrow * r + j);
           xv = *reinterpret_cast<const u32x4_t*>(p.xs + m * 2 * r + col);
         }
-        lds[0][0][rk(t, c)] = wv;
-        lds[0][1][rk(t, c)] = xv;
+        W(0, t, c) = wv;
+        if (t < TM) Xl(0, t, c) = xv;
       }
       __syncthreads();
 #pragma unroll
@@ -300,9 +311,9 @@ void fwd_gemm_kernel(FwdParams p) {
 
   // --- epilogue: D[n][m] -> y[m][n] (or the split's fp32 partial) ---
   __syncthreads();  // the LDS stages are free from here on
-  float* scratch = reinterpret_cast<float*>(&lds[0][0][0]) + wave * kEpiFloats;
-  store_acc_tile(acc, scratch, n0 + 128 * wn, m0 + 128 * wm, N, M, p.splits > 1,
-                 p.splits > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
+  float* scratch = reinterpret_cast<float*>(&lds[0][0]) + wave * kEpiFloats;
+  store_acc_tile<MS>(acc, scratch, n0 + 128 * wn, m0 + 32 * MS * wm, N, M, p.splits > 1,
+                     p.splits > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
 }
 
 // out[i] = bf16(sum_z part[z][i]), i over M*N (4 per thread), fixed order.
@@ -336,22 +347,45 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, ui
   return hipGetLastError();
 }
 
-// Split the k range when the output tiles alone cannot fill the chip:
-// aim for ~256 blocks, at least 4 k tiles per split.
-int gemm_splits(int64_t M, int64_t N, int64_t Kred) {
-  const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
+// Block tile and k splits for an output of M x N with a reduction of Kred.
+// For each token tile (256 or 128 rows) the k range is split until ~256
+// blocks fill the chip (at least 4 k tiles per split); the choice is the
+// smaller estimate of  flops / rate(tile) + the fp32 partials written and
+// read back.  The rates are the measured sustained throughputs of the two
+// tiles (the 256-row tile amortises each decoded weight over twice the
+// tokens, the 128-row one needs half the splits).
+GemmConfig gemm_config(int64_t M, int64_t N, int64_t Kred) {
   const int64_t nkt = Kred / KT;
-  if (tiles >= 192) return 1;
-  int64_t s = 256 / tiles;
-  if (s > nkt / 4) s = nkt / 4;
-  if (s > 16) s = 16;
-  return s < 1 ? 1 : (int)s;
+  const int64_t n_t = (N + TILE - 1) / TILE;
+  GemmConfig best{256, 1};
+  double best_t = 1e300;
+  for (int tm : {256, 128}) {
+    const int64_t tiles = ((M + tm - 1) / tm) * n_t;
+    int64_t s = tiles >= 192 ? 1 : 256 / tiles;
+    if (s > nkt / 4) s = nkt / 4;
+    if (s > 16) s = 16;
+    if (s < 1) s = 1;
+    const double blocks = (double)tiles * s;
+    const double fill = blocks >= 256 ? 1.0 : blocks / 256.0;
+    const double rate = (tm == 256 ? 1.1e15 : 0.8e15) * fill;  // flop/s
+    const double partial = s > 1 ? 2.0 * s * (double)M * N * 4 / 5.0e12 : 0.0;
+    const double est = 2.0 * M * N * Kred / rate + partial;
+    if (est < best_t) {
+      best_t = est;
+      best = GemmConfig{tm, (int)s};
+    }
+  }
+  return best;
 }
+
+int gemm_splits(int64_t M, int64_t N, int64_t Kred) { return gemm_config(M, N, Kred).splits; }
 
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                            const uint16_t* x, const uint16_t* xs, const uint16_t* B,
                            uint16_t* y, float* part, int splits, int64_t M, int64_t N, int64_t K,
                            int r, const Nf4Levels& L, hipStream_t s) {
+  const GemmConfig cfg = gemm_config(M, N, K);
+  if (cfg.splits != splits) return hipErrorInvalidValue;  // workspace laid out for another split
   FwdParams p;
   p.codes = codes;
   p.qscale = qscale;
@@ -367,8 +401,11 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.r = r;
   p.splits = splits;
   p.L = L;
-  const int64_t blocks = ((N + TILE - 1) / TILE) * ((M + TILE - 1) / TILE) * splits;
-  hipLaunchKernelGGL(fwd_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const int64_t blocks = ((N + TILE - 1) / TILE) * ((M + cfg.tm - 1) / cfg.tm) * splits;
+  if (cfg.tm == 256)
+    hipLaunchKernelGGL(fwd_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(fwd_gemm_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, M * N, y, s);

@@ -61,6 +61,11 @@ hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_
 // gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T.  With splits > 1 the
 // k range is split over blocks writing fp32 partials part[splits][M][N],
 // reduced to bf16 y by a second kernel.
+struct GemmConfig {
+  int tm;      // token rows of the block tile (256 or 128)
+  int splits;  // k splits (1: no partials)
+};
+GemmConfig gemm_config(int64_t M, int64_t N, int64_t Kred);
 int gemm_splits(int64_t M, int64_t N, int64_t Kred);
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                            const uint16_t* x, const uint16_t* xs, const uint16_t* B,
@@ -81,6 +86,7 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
 
 // gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]; splits > 1 as in the
 // forward GEMM (partials [splits][M][K])
+int dx_gemm_splits(int64_t M, int64_t K, int64_t N);
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
                           uint16_t* dx, float* part, int splits, int64_t M, int64_t N, int64_t K,
