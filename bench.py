@@ -102,7 +102,8 @@ def _fwd_config(M, N, Kred):
 
 
 def _dx_splits(M, K, N):
-    """Mirror of the library's k-split choice for the dX GEMM (256 x 256 tiles)."""
+    """Mirror of the library's reduction-split choice for the dX GEMM (256 x 256
+    tiles)."""
     tiles = ((M + 255) // 256) * ((K + 255) // 256)
     if tiles >= 192:
         return 1

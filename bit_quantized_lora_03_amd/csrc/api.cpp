@@ -94,7 +94,8 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   size_t off = 0;
   if (r > 0) {
     // fp32 k-split partials of x . A^T, then xs = [hi | lo] of s . x . A^T: [M][2r] bf16
-    L.psplits = qlora::lora_proj_splits(M, K, r, 1);
+    int unused = 1;
+    qlora::lora_proj_plan(M, r, K, 0, L.psplits, unused);
     L.p_off = 0;
     L.xs_off = L.psplits > 1 ? round_up((size_t)L.psplits * M * r * sizeof(float), 256) : 0;
     L.xst_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
@@ -111,7 +112,7 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
 
 struct BwdWs {
   size_t pa_off, pg_off, xs_off, gs_off, xst_off, gst_off, cb_off, ca_off, part_off, total;
-  int psplits;  // k splits of the two down-projections (1: no partials)
+  int psplits_a, psplits_g;  // k splits of x . A^T and dy . B (1: no partials)
   int tsplits;  // token splits of the dA / dB reductions (1: no partials)
   int gsplits;  // reduction splits of the dX GEMM (1: no partials)
 };
@@ -124,12 +125,11 @@ BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
     // fp32 partials of x . A^T and dy . B; xs = [hi | lo] of s . x . A^T and
     // gs = [hi | lo] of s . dy . B, [M][2r] bf16 each; fp32 token-split
     // partials of dB [N][r] and dA [r][K]
-    L.psplits = qlora::lora_proj_splits(M, K < N ? K : N, r, 2);
-    if (L.psplits > 1) {
-      L.pa_off = off;
-      L.pg_off = round_up(off + (size_t)L.psplits * M * r * sizeof(float), 256);
-      off = round_up(L.pg_off + (size_t)L.psplits * M * r * sizeof(float), 256);
-    }
+    qlora::lora_proj_plan(M, r, K, N, L.psplits_a, L.psplits_g);
+    L.pa_off = off;
+    if (L.psplits_a > 1) off = round_up(off + (size_t)L.psplits_a * M * r * sizeof(float), 256);
+    L.pg_off = off;
+    if (L.psplits_g > 1) off = round_up(off + (size_t)L.psplits_g * M * r * sizeof(float), 256);
     const size_t pair = (size_t)M * 2 * r * sizeof(uint16_t),
                  pairT = (size_t)pad32(M) * 2 * r * sizeof(uint16_t);
     L.xs_off = off;
@@ -288,8 +288,9 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
     if (r > 0) {
       xs = at<uint16_t>(workspace, ws.xs_off);
       float* P = ws.psplits > 1 ? at<float>(workspace, ws.p_off) : nullptr;
-      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), P, K, 0};
-      if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, ws.psplits, s))) !=
+      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), P, K, 0,
+                                  ws.psplits};
+      if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s))) !=
           QLORA_OK)
         return st;
     }
@@ -356,13 +357,14 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
       gs = at<uint16_t>(workspace, ws.gs_off);
       const float scale = alpha / static_cast<float>(r);
       // xs = split(s . x . A^T), gs = split(s . dy . B) in one launch
-      const bool pp = ws.psplits > 1;
       uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
       uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
-      const qlora::LoraProjJob jx{x, A, xs, xsT, pp ? at<float>(workspace, ws.pa_off) : nullptr, K, 0},
-          jg{dy, B, gs, gsT, pp ? at<float>(workspace, ws.pg_off) : nullptr, N, 1};
-      if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, ws.psplits, s))) !=
-          QLORA_OK)
+      const qlora::LoraProjJob jx{x, A, xs, xsT,
+                                  ws.psplits_a > 1 ? at<float>(workspace, ws.pa_off) : nullptr,
+                                  K, 0, ws.psplits_a},
+          jg{dy, B, gs, gsT, ws.psplits_g > 1 ? at<float>(workspace, ws.pg_off) : nullptr, N, 1,
+             ws.psplits_g};
+      if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, s))) != QLORA_OK)
         return st;
       // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x
       const bool tp = ws.tsplits > 1;

@@ -73,25 +73,33 @@ __device__ __forceinline__ int wt_off(int k, int n) {
 
 }  // namespace
 
+// MS: 32-wide token subtiles per wave (4: the 256 (k) x 256 (m) tile).
+template <int MS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
-  __shared__ uint16_t wt[2][TILE_ELEMS];
-  __shared__ u32x4_t dyt[2][TILE * ROW_CHUNKS];
+  constexpr int TM = 64 * MS;   // token rows of the block tile
+  constexpr int XR = TM / 32;   // dy rows staged per thread
+  // one LDS array: two W^T stages, then two dy stages (the epilogue reuses
+  // it from the start)
+  constexpr int WT_U4 = 2 * TILE_ELEMS * 2 / 16;
+  __shared__ u32x4_t lds[WT_U4 + 2 * TM * ROW_CHUNKS];
+  uint16_t(*wt)[TILE_ELEMS] = reinterpret_cast<uint16_t(*)[TILE_ELEMS]>(&lds[0]);
+  u32x4_t(*dyt)[TM * ROW_CHUNKS] = reinterpret_cast<u32x4_t(*)[TM * ROW_CHUNKS]>(&lds[WT_U4]);
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int wk = wave & 1, wm = wave >> 1;
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int64_t m_tiles = (M + TILE - 1) / TILE, k_tiles = (K + TILE - 1) / TILE;
+  const int64_t m_tiles = (M + TM - 1) / TM, k_tiles = (K + TILE - 1) / TILE;
   const TileCoord tc = xcd_tile(blockIdx.x, (int64_t)gridDim.x, m_tiles, k_tiles, 4);
   const int64_t k0 = tc.n * TILE;
-  const int64_t m0 = tc.m * TILE;
+  const int64_t m0 = tc.m * TM;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][MS];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < MS; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -128,14 +136,14 @@ void dx_gemm_kernel(DxParams p) {
     c.q = p.qscale[idx >> 6];
     c.st = p.step[idx >> 14];
   };
-  auto load_dy = [&](int64_t st, u32x4_t (&yr)[8]) {
+  auto load_dy = [&](int64_t st, u32x4_t (&yr)[XR]) {
     const uint32_t o = yoff + (uint32_t)(st * RT * 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) yr[j] = buffer_load16(yres, o + j * yrow_step);
+    for (int j = 0; j < XR; ++j) yr[j] = buffer_load16(yres, o + j * yrow_step);
   };
-  auto store_dy = [&](int stage, const u32x4_t (&yr)[8]) {
+  auto store_dy = [&](int stage, const u32x4_t (&yr)[XR]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dyt[stage][rk((t >> 3) + 32 * j, t & 7)] = yr[j];
+    for (int j = 0; j < XR; ++j) dyt[stage][rk((t >> 3) + 32 * j, t & 7)] = yr[j];
   };
   // scatter 8 consecutive-k bf16 values (chunk c of this thread's 64) of
   // reduction row `wr` into W^T
@@ -150,16 +158,16 @@ void dx_gemm_kernel(DxParams p) {
   };
   auto mfma_step = [&](int stage, int kk) {
     const int ch = 2 * kk + lg;
-    u32x4_t a[4], b[4];
+    u32x4_t a[4], b[MS];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       a[i] = *reinterpret_cast<const u32x4_t*>(&wt[stage][wt_off(128 * wk + 32 * i + lr, 8 * ch)]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = dyt[stage][rk(128 * wm + 32 * j + lr, ch)];
+    for (int j = 0; j < MS; ++j) b[j] = dyt[stage][rk(32 * MS * wm + 32 * j + lr, ch)];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < MS; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
   };
 
   if (st0 < st1) {
@@ -170,7 +178,7 @@ void dx_gemm_kernel(DxParams p) {
     const int64_t last = st1 - 1;
     auto cl = [&](int64_t v) { return v < last ? v : last; };
     Codes C[2];
-    u32x4_t Y[2][8];
+    u32x4_t Y[2][XR];
     load_codes(st0, C[0]);
     load_dy(st0, Y[0]);
     store_dy(0, Y[0]);
@@ -210,7 +218,7 @@ void dx_gemm_kernel(DxParams p) {
   const int r = p.r;
   if (z == p.splits - 1) {
     const int ext_tiles = (2 * r + RT - 1) / RT;
-    const int64_t m = clamp_row(m0 + t, M);
+    const int64_t m = clamp_row(m0 + (t % TM), M);
     for (int e = 0; e < ext_tiles; ++e) {
       // W^T side: reduction row c = e*64 + wr is A's row (c mod r), zero past 2r
       const int c = e * RT + wr;
@@ -224,8 +232,9 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int col = e * RT + 8 * q;
-        dyt[0][rk(t, q)] =
-            col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.gs + m * 2 * r + col) : zero;
+        if (t < TM)
+          dyt[0][rk(t, q)] =
+              col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.gs + m * 2 * r + col) : zero;
       }
       __syncthreads();
 #pragma unroll
@@ -236,24 +245,27 @@ void dx_gemm_kernel(DxParams p) {
 
   // --- epilogue: D[k][m] -> dx[m][k] (or the split's fp32 partial) ---
   __syncthreads();  // the LDS stages are free from here on
-  float* scratch = (wave < 2 ? reinterpret_cast<float*>(&wt[0][0])
-                             : reinterpret_cast<float*>(&dyt[0][0])) +
-                   (wave & 1) * kEpiFloats;
-  store_acc_tile(acc, scratch, k0 + 128 * wk, m0 + 128 * wm, K, M, p.splits > 1,
-                 p.splits > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
+  float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * kEpiFloats;
+  store_acc_tile<MS>(acc, scratch, k0 + 128 * wk, m0 + 32 * MS * wm, K, M, p.splits > 1,
+                     p.splits > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
 }
 
-// k splits of the dX GEMM (256 x 256 tiles): aim for ~256 blocks when the
-// output tiles alone cannot fill the chip, at least 4 reduction stages each.
-int dx_gemm_splits(int64_t M, int64_t K, int64_t N) {
+// Block tile and reduction splits of the dX GEMM (output M x K, reduction
+// N): 256 x 256 tiles, the reduction split until ~256 blocks fill the chip
+// (at least 4 stages per split).  (The 128-token tile does not pay here: the
+// decode of a W^T slab is not spread over the MFMAs as finely as in the
+// forward pass, so halving the MFMAs per slab exposes it.)
+GemmConfig dx_gemm_config(int64_t M, int64_t K, int64_t N) {
   const int64_t tiles = ((M + TILE - 1) / TILE) * ((K + TILE - 1) / TILE);
   const int64_t nst = N / RT;
-  if (tiles >= 192) return 1;
+  if (tiles >= 192) return GemmConfig{256, 1};
   int64_t s = 256 / tiles;
   if (s > nst / 4) s = nst / 4;
   if (s > 16) s = 16;
-  return s < 1 ? 1 : (int)s;
+  return GemmConfig{256, s < 1 ? 1 : (int)s};
 }
+
+int dx_gemm_splits(int64_t M, int64_t K, int64_t N) { return dx_gemm_config(M, K, N).splits; }
 
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
@@ -274,8 +286,10 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.r = r;
   p.splits = splits;
   p.L = L;
-  const int64_t blocks = ((K + TILE - 1) / TILE) * ((M + TILE - 1) / TILE) * splits;
-  hipLaunchKernelGGL(dx_gemm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const GemmConfig cfg = dx_gemm_config(M, K, N);
+  if (cfg.splits != splits) return hipErrorInvalidValue;  // workspace laid out for another split
+  const int64_t blocks = ((K + TILE - 1) / TILE) * ((M + cfg.tm - 1) / cfg.tm) * splits;
+  hipLaunchKernelGGL(dx_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, M * K, dx, s);

@@ -23,9 +23,9 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const flo
 // v = scale * sum_k X[m][k] * Y(j, k), with Y(j, k) = Y[j * Kred + k]
 // (kmajor == 0, A [r, Kred]) or Y[k * r + j] (kmajor == 1, B [Kred, r]);
 // also outT[j][m] = hi, outT[r + j][m] = lo with rows of Mp = M rounded up
-// to 32 (zero past M).  With splits > 1 the k range is split over blocks
-// writing fp32 partials P [splits][M][r], added in split order by a second
-// kernel.
+// to 32 (zero past M).  With splits > 1 the job's k range is split over
+// blocks writing fp32 partials P [splits][M][r], added in split order by a
+// second kernel.
 constexpr int kProjMaxSplits = 16;
 struct LoraProjJob {
   const uint16_t* X;  // [M, Kred] bf16
@@ -35,12 +35,13 @@ struct LoraProjJob {
   float* P;           // [splits][M][r] fp32 (splits > 1)
   int64_t Kred;
   int kmajor;
+  int splits;
 };
-// splits for njobs jobs whose reduction lengths are all >= Kred
-int lora_proj_splits(int64_t M, int64_t Kred, int r, int njobs);
+// splits of one job (K1 = 0) or of two jobs sharing a launch
+void lora_proj_plan(int64_t M, int r, int64_t K0, int64_t K1, int& s0, int& s1);
 // one job, or two in one launch (j1 non-null)
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
-                            float scale, int splits, hipStream_t s);
+                            float scale, hipStream_t s);
 // lora_grad: C (+)= sum_m G[m][g] * (ST[j][m] + ST[r + j][m]), C [ldg, r]
 // (transposed == 0) or [r, ldg] (transposed == 1); both jobs in one launch.
 // With splits > 1 the tokens are split over blocks writing fp32 partials
@@ -86,6 +87,7 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
 
 // gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]; splits > 1 as in the
 // forward GEMM (partials [splits][M][K])
+GemmConfig dx_gemm_config(int64_t M, int64_t K, int64_t N);
 int dx_gemm_splits(int64_t M, int64_t K, int64_t N);
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,

@@ -50,119 +50,186 @@ __device__ __forceinline__ void put_split(const LoraProjJob& J, int64_t M, int r
 }
 
 // ---------------------------------------------------------------------------
-// lora_proj: grid (njobs * Mp/16 * ceil(r/16) * splits), 256 threads.  A
-// block owns 16 tokens x 16 rank columns of one job and the z-th share of
-// the reduction; wave w takes the 32-wide k steps w, w + 4, ... of that
-// share and runs 16x16x32 MFMA.  The token operand is one 16-byte load per
-// lane (8 consecutive k of a row), and so is A's operand.  B ([Kred, r]) is
-// read as 16-byte row pieces (8 rank columns of one k) and turned around in
-// a small LDS tile of the wave's own.  With one split the block writes the
-// bf16 pairs itself; otherwise it writes an fp32 partial P[z][m][j] and
-// lora_proj_finalize adds the shares in order.  Many small blocks keep
-// enough loads in flight across the chip.
+// lora_proj: grid (sum over jobs of ceil(M/64) * ceil(r/(16 JT)) * splits),
+// 256 threads.  A block owns 64 tokens x 16 JT rank columns of one job and
+// the z-th share of that job's reduction (jobs split in proportion to their
+// reduction length, so their blocks carry equal work); wave w owns tokens
+// 16 w .. 16 w + 15 and runs the block's whole k share with 16x16x32 MFMA.
+// The token operand is one 16-byte load per lane (8 consecutive k of a
+// row), straight from global memory, and so is A's operand per 16-column
+// group (the four waves read the same A pieces, which stay in L1).  B
+// ([Kred, r]) has k as its slow index, so the block loads it as 16-byte row
+// pieces (8 rank columns of one k), turns them around once in a shared,
+// double-buffered LDS tile per batch of k steps, and every wave reads its
+// operands from there.  With one split the waves write the bf16 pairs
+// themselves; otherwise they write fp32 partials P[z][m][j] and
+// lora_proj_finalize adds the shares in order.
 // ---------------------------------------------------------------------------
-constexpr int kProjWaves = 4;
 constexpr int kProjBatch = 4;  // k steps per register set
-constexpr int kProjTRow = 40;  // transpose tile row: 32 k + 8 pad (bf16), 80 bytes
+constexpr int kProjTRow = 40;  // transposed B row: 32 k + 8 pad (bf16), 80 bytes
 
-__global__ __launch_bounds__(kProjWaves * 64) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
-                                                                    int64_t blocks_per_job,
-                                                                    int64_t M, int r, float scale,
-                                                                    int splits) {
-  __shared__ float red[kProjWaves][16][17];
-  __shared__ __align__(16) uint16_t tt[kProjWaves][16 * kProjTRow];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bool second = (int64_t)blockIdx.x >= blocks_per_job;
+template <int JT>
+__global__ __launch_bounds__(256) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
+                                                        int64_t blocks0, int64_t M, int r,
+                                                        float scale) {
+  __shared__ __align__(16) uint16_t tb[2][kProjBatch][16 * JT * kProjTRow];
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const bool second = (int64_t)blockIdx.x >= blocks0;
   const LoraProjJob J = second ? j1 : j0;
+  const int splits = J.splits;
 
-  const int jblocks = (r + 15) / 16;
-  const int64_t b0 = second ? (int64_t)blockIdx.x - blocks_per_job : (int64_t)blockIdx.x;
+  const int jblocks = (r + 16 * JT - 1) / (16 * JT);
+  const int64_t b0 = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
   const int z = (int)(b0 % splits);
   const int64_t bb = b0 / splits;
-  const int64_t m0 = (bb / jblocks) * 16;
-  const int jc = (int)(bb % jblocks) * 16;
+  const int64_t mblk = (bb / jblocks) * 64;
+  const int64_t m0 = mblk + 16 * wave;
+  const int jc = (int)(bb % jblocks) * 16 * JT;
   const int i = lane & 15, kg = lane >> 4;
   const int64_t m = m0 + i;
   const bool mok = m < M;
-  const int jj = jc + i;
-  const bool jok = jj < r;
-  // B row pieces: lane loads k = k0 + lane / 2, columns jc + 8 (lane % 2) + e
-  const int bcol = jc + 8 * (lane & 1);
-  const bool bok = bcol < r;
   const int64_t Kred = J.Kred;
   const int64_t nsteps = Kred / 32;
   const int64_t st0 = nsteps * z / splits, st1 = nsteps * (z + 1) / splits;
-  const int64_t ns = st1 - st0 > wave ? (st1 - st0 - wave + kProjWaves - 1) / kProjWaves : 0;
+  const int64_t ns = st1 - st0;
+  const int64_t nb = (ns + kProjBatch - 1) / kProjBatch;
   const uint16_t* xrow = J.X + (mok ? m : 0) * Kred + 8 * kg;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  uint16_t* tile = tt[wave];
 
-  // operands of this wave's s-th k step (B: the raw row piece)
-  auto load = [&](int64_t s, u32x4_t& xv, u32x4_t& yv) {
-    const int64_t k0 = 32 * (st0 + wave + (int64_t)kProjWaves * s);
-    xv = mok ? *reinterpret_cast<const u32x4_t*>(xrow + k0) : zero;
-    if (!J.kmajor)
-      yv = jok ? *reinterpret_cast<const u32x4_t*>(J.Y + (int64_t)jj * Kred + k0 + 8 * kg) : zero;
-    else
-      yv = bok ? *reinterpret_cast<const u32x4_t*>(J.Y + (k0 + (lane >> 1)) * r + bcol) : zero;
-  };
-  const int64_t nb = (ns + kProjBatch - 1) / kProjBatch;
-  auto load_batch = [&](int64_t bi, u32x4_t (&xv)[kProjBatch], u32x4_t (&yv)[kProjBatch]) {
+  f32x4_t acc[JT];
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto load_x = [&](int64_t bi, u32x4_t (&xv)[kProjBatch]) {
 #pragma unroll
     for (int u = 0; u < kProjBatch; ++u) {
       const int64_t s = bi * kProjBatch + u;
-      if (s < ns) {
-        load(s, xv[u], yv[u]);
-      } else {
-        xv[u] = zero;
-        yv[u] = zero;
-      }
-    }
-  };
-  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto mma_batch = [&](const u32x4_t (&xv)[kProjBatch], const u32x4_t (&yv)[kProjBatch]) {
-#pragma unroll
-    for (int u = 0; u < kProjBatch; ++u) {
-      u32x4_t b = yv[u];
-      if (J.kmajor) {
-        // row piece -> tile[col][k]; then lane (col i, k group kg) reads its 8 k
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          tile[(8 * (lane & 1) + e) * kProjTRow + (lane >> 1)] =
-              (uint16_t)(yv[u][e >> 1] >> (16 * (e & 1)));
-        b = *reinterpret_cast<const u32x4_t*>(tile + i * kProjTRow + 8 * kg);
-      }
-      acc = mfma16x16x32(xv[u], b, acc);
+      xv[u] = (mok && s < ns) ? *reinterpret_cast<const u32x4_t*>(xrow + 32 * (st0 + s)) : zero;
     }
   };
 
-  // two register sets: batch b + 1 loads while batch b multiplies
-  u32x4_t X0[kProjBatch], Y0[kProjBatch], X1[kProjBatch], Y1[kProjBatch];
-  if (nb > 0) load_batch(0, X0, Y0);
-  for (int64_t bi = 0; bi < nb; bi += 2) {
-    if (bi + 1 < nb) load_batch(bi + 1, X1, Y1);
-    mma_batch(X0, Y0);
-    if (bi + 1 < nb) {
-      if (bi + 2 < nb) load_batch(bi + 2, X0, Y0);
-      mma_batch(X1, Y1);
+  if (!J.kmajor) {
+    // A [r, Kred]: row pieces are MFMA operands as they are
+    auto load_a = [&](int64_t bi, u32x4_t (&yv)[kProjBatch][JT]) {
+#pragma unroll
+      for (int u = 0; u < kProjBatch; ++u) {
+        const int64_t s = bi * kProjBatch + u;
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          const int jj = jc + 16 * jt + i;
+          yv[u][jt] = (jj < r && s < ns)
+                          ? *reinterpret_cast<const u32x4_t*>(J.Y + (int64_t)jj * Kred +
+                                                              32 * (st0 + s) + 8 * kg)
+                          : zero;
+        }
+      }
+    };
+    auto mma = [&](const u32x4_t (&xv)[kProjBatch], const u32x4_t (&yv)[kProjBatch][JT]) {
+#pragma unroll
+      for (int u = 0; u < kProjBatch; ++u)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma16x16x32(xv[u], yv[u][jt], acc[jt]);
+    };
+    u32x4_t X0[kProjBatch], X1[kProjBatch], Y0[kProjBatch][JT], Y1[kProjBatch][JT];
+    if (nb > 0) {
+      load_x(0, X0);
+      load_a(0, Y0);
+    }
+    for (int64_t bi = 0; bi < nb; bi += 2) {
+      if (bi + 1 < nb) {
+        load_x(bi + 1, X1);
+        load_a(bi + 1, Y1);
+      }
+      mma(X0, Y0);
+      if (bi + 1 < nb) {
+        if (bi + 2 < nb) {
+          load_x(bi + 2, X0);
+          load_a(bi + 2, Y0);
+        }
+        mma(X1, Y1);
+      }
+    }
+  } else {
+    // B [Kred, r]: thread t loads JT row pieces per batch, piece p = t + 256 q:
+    // step p / (64 JT), k row (p mod 64 JT) / (2 JT), columns 8 (p mod 2 JT)
+    auto load_b = [&](int64_t bi, u32x4_t (&br)[JT]) {
+#pragma unroll
+      for (int q = 0; q < JT; ++q) {
+        const int pc = t + 256 * q;
+        const int u = pc / (64 * JT), w = pc % (64 * JT);
+        const int kr = w / (2 * JT), cp = w % (2 * JT);
+        const int64_t s = bi * kProjBatch + u;
+        const int col = jc + 8 * cp;
+        br[q] = (col < r && s < ns)
+                    ? *reinterpret_cast<const u32x4_t*>(J.Y + (32 * (st0 + s) + kr) * r + col)
+                    : zero;
+      }
+    };
+    auto put_b = [&](int buf, const u32x4_t (&br)[JT]) {
+#pragma unroll
+      for (int q = 0; q < JT; ++q) {
+        const int pc = t + 256 * q;
+        const int u = pc / (64 * JT), w = pc % (64 * JT);
+        const int kr = w / (2 * JT), cp = w % (2 * JT);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          tb[buf][u][(8 * cp + e) * kProjTRow + kr] = (uint16_t)(br[q][e >> 1] >> (16 * (e & 1)));
+      }
+    };
+    auto mma = [&](int buf, const u32x4_t (&xv)[kProjBatch]) {
+#pragma unroll
+      for (int u = 0; u < kProjBatch; ++u)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          const u32x4_t b =
+              *reinterpret_cast<const u32x4_t*>(&tb[buf][u][(16 * jt + i) * kProjTRow + 8 * kg]);
+          acc[jt] = mfma16x16x32(xv[u], b, acc[jt]);
+        }
+    };
+    // Batch b's pieces go into buffer b & 1 after the barrier of batch b - 1,
+    // which every wave reaches only once it is done reading batch b - 2 (the
+    // same buffer); all waves run the same number of batches.
+    u32x4_t X0[kProjBatch], X1[kProjBatch], B0[JT], B1[JT];
+    if (nb > 0) {
+      load_x(0, X0);
+      load_b(0, B0);
+    }
+    for (int64_t bi = 0; bi < nb; bi += 2) {
+      if (bi + 1 < nb) {
+        load_x(bi + 1, X1);
+        load_b(bi + 1, B1);
+      }
+      put_b(0, B0);
+      __syncthreads();
+      mma(0, X0);
+      if (bi + 1 < nb) {
+        if (bi + 2 < nb) {
+          load_x(bi + 2, X0);
+          load_b(bi + 2, B0);
+        }
+        put_b(1, B1);
+        __syncthreads();
+        mma(1, X1);
+      }
     }
   }
 
-  // D[token][j]: lane holds column j = lane % 16, rows 4 (lane / 16) + v
+  // D[token][j]: lane holds column j = lane % 16, tokens 4 (lane / 16) + v
+  const int64_t Mp = pad32(M);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) red[wave][4 * kg + v][i] = acc[v];
-  __syncthreads();
-  const int mm = threadIdx.x >> 4, j = threadIdx.x & 15;
-  float sum = 0.0f;
+  for (int jt = 0; jt < JT; ++jt) {
+    const int jo = jc + 16 * jt + i;
+    if (jo >= r) continue;
 #pragma unroll
-  for (int w = 0; w < kProjWaves; ++w) sum += red[w][mm][j];
-  const int64_t mo = m0 + mm;
-  const int jo = jc + j;
-  if (jo < r) {
-    if (splits == 1)
-      put_split(J, M, r, mo, jo, scale * sum);
-    else if (mo < M)
-      J.P[((int64_t)z * M + mo) * r + jo] = sum;
+    for (int v = 0; v < 4; ++v) {
+      const int64_t mo = m0 + 4 * kg + v;
+      if (splits == 1) {
+        if (mo < Mp) put_split(J, M, r, mo, jo, scale * acc[jt][v]);
+      } else if (mo < M) {
+        J.P[((int64_t)z * M + mo) * r + jo] = acc[jt][v];
+      }
+    }
   }
 }
 
@@ -170,12 +237,14 @@ __global__ __launch_bounds__(kProjWaves * 64) void lora_proj_kernel(LoraProjJob 
 // jobs' Mp x r values (rows past M get zeros in the transposed copy).
 __global__ __launch_bounds__(256) void lora_proj_finalize_kernel(LoraProjJob j0, LoraProjJob j1,
                                                                  int njobs, int64_t M, int r,
-                                                                 float scale, int splits) {
+                                                                 float scale) {
   const int64_t per = pad32(M) * r, total = per * njobs;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const bool second = e >= per;
     const LoraProjJob J = second ? j1 : j0;
+    const int splits = J.splits;
+    if (splits == 1) continue;  // the job's blocks wrote their results themselves
     const int64_t ee = second ? e - per : e;
     const int64_t m = ee / r;
     const int j = (int)(ee - m * r);
@@ -193,30 +262,50 @@ __global__ __launch_bounds__(256) void lora_proj_finalize_kernel(LoraProjJob j0,
   }
 }
 
-int lora_proj_splits(int64_t M, int64_t Kred, int r, int njobs) {
-  const int64_t tiles = (pad32(M) / 16) * ((r + 15) / 16) * njobs;
-  int64_t s = (1024 + tiles - 1) / tiles;
-  const int64_t cap = Kred / 256;  // at least 8 k steps (2 per wave) per block
-  if (s > cap) s = cap;
-  if (s > kProjMaxSplits) s = kProjMaxSplits;
-  return s < 1 ? 1 : (int)s;
+static int proj_jt(int r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
+
+// k splits of one or two jobs sharing a launch: about 512 blocks in all,
+// each job's splits in proportion to its reduction length (equal work per
+// block), at least 8 k steps per split.
+void lora_proj_plan(int64_t M, int r, int64_t K0, int64_t K1, int& s0, int& s1) {
+  const int jw = 16 * proj_jt(r);
+  const int64_t tiles = ((M + 63) / 64) * ((r + jw - 1) / jw);
+  const double total_k = (double)K0 + (double)K1;
+  auto pick = [&](int64_t Kred) {
+    if (Kred <= 0 || tiles == 0) return 1;
+    int64_t s = (int64_t)(512.0 * (double)Kred / (total_k * (double)tiles) + 0.5);
+    if (s > Kred / 256) s = Kred / 256;
+    if (s > kProjMaxSplits) s = kProjMaxSplits;
+    return s < 1 ? 1 : (int)s;
+  };
+  s0 = pick(K0);
+  s1 = pick(K1);
 }
 
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
-                            float scale, int splits, hipStream_t s) {
+                            float scale, hipStream_t s) {
   const int njobs = j1 ? 2 : 1;
-  // Mp / 16 row blocks, so that the blocks (one split) or the finalize pass
-  // cover every row of the transposed copy
-  const int64_t per_job = (pad32(M) / 16) * ((r + 15) / 16) * splits;
-  if (per_job == 0) return hipSuccess;
-  hipLaunchKernelGGL(lora_proj_kernel, dim3((unsigned)(per_job * njobs)), dim3(kProjWaves * 64), 0,
-                     s, j0, j1 ? *j1 : j0, per_job, M, r, scale, splits);
+  const int jt = proj_jt(r);
+  const int jw = 16 * jt;
+  // ceil(M/64) token blocks cover every row of the transposed copy (Mp =
+  // M rounded up to 32 <= the blocks' extent); rows past Mp are not written
+  const int64_t tiles = ((M + 63) / 64) * ((r + jw - 1) / jw);
+  const LoraProjJob jb = j1 ? *j1 : j0;
+  const int64_t blocks0 = tiles * j0.splits, blocks1 = j1 ? tiles * j1->splits : 0;
+  if (blocks0 + blocks1 == 0) return hipSuccess;
+  const dim3 grid((unsigned)(blocks0 + blocks1));
+  if (jt == 1)
+    hipLaunchKernelGGL(lora_proj_kernel<1>, grid, dim3(256), 0, s, j0, jb, blocks0, M, r, scale);
+  else if (jt == 2)
+    hipLaunchKernelGGL(lora_proj_kernel<2>, grid, dim3(256), 0, s, j0, jb, blocks0, M, r, scale);
+  else
+    hipLaunchKernelGGL(lora_proj_kernel<4>, grid, dim3(256), 0, s, j0, jb, blocks0, M, r, scale);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
+  if (e != hipSuccess || (j0.splits == 1 && (!j1 || j1->splits == 1))) return e;
   int64_t g = (pad32(M) * r * njobs + 255) / 256;
   if (g > 2048) g = 2048;
-  hipLaunchKernelGGL(lora_proj_finalize_kernel, dim3((unsigned)g), dim3(256), 0, s, j0,
-                     j1 ? *j1 : j0, njobs, M, r, scale, splits);
+  hipLaunchKernelGGL(lora_proj_finalize_kernel, dim3((unsigned)g), dim3(256), 0, s, j0, jb,
+                     njobs, M, r, scale);
   return hipGetLastError();
 }
 
