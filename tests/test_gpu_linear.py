@@ -27,6 +27,10 @@ SHAPES = [
     (33, 192, 1024, 128, 32.0),
     (5, 128, 192, 256, 8.0),
     (70, 448, 640, 0, 1.0),
+    # the two adapter down-projections of the backward (over K and over N)
+    # get different k splits: N >> K and N << K
+    (200, 4096, 512, 32, 64.0),
+    (96, 256, 4096, 16, 32.0),
 ]
 
 
