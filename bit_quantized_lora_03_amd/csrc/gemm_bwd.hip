@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
   constexpr int TM = 64 * MS;   // token rows of the block tile
   constexpr int XR = TM / 32;   // dy rows staged per thread
+  static_assert(MS == 4, "the hand-scheduled iteration assumes 256-token tiles");
   // one LDS array: two W^T stages, then two dy stages (the epilogue reuses
   // it from the start)
   constexpr int WT_U4 = 2 * TILE_ELEMS * 2 / 16;
@@ -192,19 +193,88 @@ void dx_gemm_kernel(DxParams p) {
     load_codes(cl(st0 + 1), C[1]);
     __syncthreads();
 
+    // Hand-scheduled iteration, as in the forward pass: each of the 64
+    // MFMAs of the slab is followed by one unit of other work and a
+    // scheduling fence -- the table of slab st+1's block (units 0..7), the
+    // decode of its 8 code words (6 units each, about 5 vector ops per
+    // unit; the last one scatters the 8 values into W^T), the LDS writes of
+    // its dy rows (units 56..63) -- and the operand reads of step kk+1 ride
+    // in slots 8..15 of step kk, so the vector work fits in the MFMAs' shadow.
     auto iteration = [&](int64_t st, auto parity) {
       constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
       load_dy(cl(st + 2), Y[cur]);
       load_codes(cl(st + 2), C[cur]);
       const Codes& cn = C[nxt];
-      const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(cn.q, cn.st));
+      u32x4_t op[2][2][4];  // [buffer][a|b][i]
+      auto read_op = [&](int kk, int buf, int q) {
+        const int ch = 2 * kk + lg;
+        if (q < 4)
+          op[buf][0][q] =
+              *reinterpret_cast<const u32x4_t*>(&wt[cur][wt_off(128 * wk + 32 * q + lr, 8 * ch)]);
+        else
+          op[buf][1][q - 4] = dyt[cur][rk(128 * wm + 32 * (q - 4) + lr, ch)];
+      };
+#pragma unroll
+      for (int q = 0; q < 8; ++q) read_op(0, 0, q);
+
+      uint32_t pk[8];
+      Nf4Lut lut;
+      float sc = 0.0f;
+      uint32_t dn0 = 0, dn1 = 0, nh = 0, pick = 0, la = 0, lb = 0;
+      u32x4_t dv = zero;
+      auto lookup_a = [&](uint32_t n) {  // low-byte planes of 4 codes
+        nh = n & 0x07070707u;
+        pick = ((n >> 1) & 0x04040404u) | 0x03020100u;
+        la = perm(lut.lo[1], lut.lo[0], n);
+        lb = perm(lut.lo[3], lut.lo[2], nh);
+      };
+      auto lookup_b = [&](uint32_t n, uint32_t& o01, uint32_t& o23) {  // high bytes, merge
+        const uint32_t lo = perm(lb, la, pick);
+        const uint32_t hi =
+            perm(perm(lut.hi[3], lut.hi[2], nh), perm(lut.hi[1], lut.hi[0], n), pick);
+        o01 = perm(hi, lo, 0x05010400u);
+        o23 = perm(hi, lo, 0x07030602u);
+      };
+      auto unit = [&](int u) {
+        if (u < 4) {
+          if (u == 0) sc = nf4_block_scale(cn.q, cn.st);
+          pk[2 * u] = pack_bf16x2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
+          pk[2 * u + 1] = pack_bf16x2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
+        } else if (u < 8) {
+          const int j = u - 4;
+          lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
+          lut.hi[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
+        } else if (u < 56) {
+          const int c = (u - 8) / 6, w = (u - 8) % 6;
+          const uint32_t v = (c < 4 ? cn.c0 : cn.c1)[c & 3];
+          switch (w) {
+            case 0: {
+              const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
+              dn0 = perm(od, ev, 0x05010400u);  // codes 0..3 of the word, one per byte
+              dn1 = perm(od, ev, 0x07030602u);  // codes 4..7
+              break;
+            }
+            case 1: lookup_a(dn0); break;
+            case 2: { uint32_t o0, o1; lookup_b(dn0, o0, o1); dv[0] = o0; dv[1] = o1; break; }
+            case 3: lookup_a(dn1); break;
+            case 4: { uint32_t o2, o3; lookup_b(dn1, o2, o3); dv[2] = o2; dv[3] = o3; break; }
+            default: scatter8(nxt, c, dv); break;
+          }
+        } else {
+          // slab st+1's dy rows into the other stage
+          dyt[nxt][rk((t >> 3) + 32 * (u - 56), t & 7)] = Y[nxt][u - 56];
+        }
+      };
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        mfma_step(cur, kk);
 #pragma unroll
-        for (int c = 2 * kk; c < 2 * kk + 2; ++c)
-          scatter8(nxt, c, nf4_decode8(lut, (c < 4 ? cn.c0 : cn.c1)[c & 3]));
-        if (kk == 3) store_dy(nxt, Y[nxt]);
+        for (int s2 = 0; s2 < 16; ++s2) {
+          const int i = s2 >> 2, j = s2 & 3;
+          acc[i][j] = mfma32x32x16(op[kk & 1][0][i], op[kk & 1][1][j], acc[i][j]);
+          if (kk < 3 && s2 >= 8) read_op(kk + 1, (kk + 1) & 1, s2 - 8);
+          unit(16 * kk + s2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       __syncthreads();
     };
