@@ -102,12 +102,9 @@ def _fwd_config(M, N, Kred):
 
 
 def _dx_splits(M, K, N):
-    """Mirror of the library's reduction-split choice for the dX GEMM (256 x 256
-    tiles)."""
-    tiles = ((M + 255) // 256) * ((K + 255) // 256)
-    if tiles >= 192:
-        return 1
-    return max(1, min(256 // tiles, (N // 64) // 4, 16))
+    """Mirror of the library's reduction-split choice for the dX GEMM (the same
+    rule as the forward GEMM's, over the M x K output)."""
+    return _fwd_config(M, K, N)[1]
 
 
 def _source_digest(key):

@@ -73,13 +73,14 @@ __device__ __forceinline__ int wt_off(int k, int n) {
 
 }  // namespace
 
-// MS: 32-wide token subtiles per wave (4: the 256 (k) x 256 (m) tile).
+// MS: 32-wide token subtiles per wave; MS = 4 is the 256 (k) x 256 (m)
+// tile, MS = 2 the 256 x 128 tile for small-M shapes (twice the output tiles,
+// so half the reduction splits and half their fp32 partials).
 template <int MS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
   constexpr int TM = 64 * MS;   // token rows of the block tile
   constexpr int XR = TM / 32;   // dy rows staged per thread
-  static_assert(MS == 4, "the hand-scheduled iteration assumes 256-token tiles");
   // one LDS array: two W^T stages, then two dy stages (the epilogue reuses
   // it from the start)
   constexpr int WT_U4 = 2 * TILE_ELEMS * 2 / 16;
@@ -205,17 +206,19 @@ void dx_gemm_kernel(DxParams p) {
       load_dy(cl(st + 2), Y[cur]);
       load_codes(cl(st + 2), C[cur]);
       const Codes& cn = C[nxt];
-      u32x4_t op[2][2][4];  // [buffer][a|b][i]
+      constexpr int SPK = 4 * MS;  // MFMAs (slots) per k step
+      constexpr int NRD = 4 + MS;  // operand reads per k step
+      u32x4_t op[2][2][4];         // [buffer][a|b][i]
       auto read_op = [&](int kk, int buf, int q) {
         const int ch = 2 * kk + lg;
         if (q < 4)
           op[buf][0][q] =
               *reinterpret_cast<const u32x4_t*>(&wt[cur][wt_off(128 * wk + 32 * q + lr, 8 * ch)]);
         else
-          op[buf][1][q - 4] = dyt[cur][rk(128 * wm + 32 * (q - 4) + lr, ch)];
+          op[buf][1][q - 4] = dyt[cur][rk(32 * MS * wm + 32 * (q - 4) + lr, ch)];
       };
 #pragma unroll
-      for (int q = 0; q < 8; ++q) read_op(0, 0, q);
+      for (int q = 0; q < NRD; ++q) read_op(0, 0, q);
 
       uint32_t pk[8];
       Nf4Lut lut;
@@ -260,7 +263,7 @@ void dx_gemm_kernel(DxParams p) {
             case 4: { uint32_t o2, o3; lookup_b(dn1, o2, o3); dv[2] = o2; dv[3] = o3; break; }
             default: scatter8(nxt, c, dv); break;
           }
-        } else {
+        } else if (u < 56 + XR) {
           // slab st+1's dy rows into the other stage
           dyt[nxt][rk((t >> 3) + 32 * (u - 56), t & 7)] = Y[nxt][u - 56];
         }
@@ -268,11 +271,13 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) {
-          const int i = s2 >> 2, j = s2 & 3;
+        for (int s2 = 0; s2 < SPK; ++s2) {
+          const int i = s2 / MS, j = s2 % MS;
           acc[i][j] = mfma32x32x16(op[kk & 1][0][i], op[kk & 1][1][j], acc[i][j]);
-          if (kk < 3 && s2 >= 8) read_op(kk + 1, (kk + 1) & 1, s2 - 8);
-          unit(16 * kk + s2);
+          if (kk < 3 && s2 >= SPK - NRD) read_op(kk + 1, (kk + 1) & 1, s2 - (SPK - NRD));
+          constexpr int UPS = 16 / SPK;  // units per slot: 64 units over 4 SPK slots
+#pragma unroll
+          for (int e = 0; e < UPS; ++e) unit(UPS * (SPK * kk + s2) + e);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -321,18 +326,32 @@ void dx_gemm_kernel(DxParams p) {
 }
 
 // Block tile and reduction splits of the dX GEMM (output M x K, reduction
-// N): 256 x 256 tiles, the reduction split until ~256 blocks fill the chip
-// (at least 4 stages per split).  (The 128-token tile does not pay here: the
-// decode of a W^T slab is not spread over the MFMAs as finely as in the
-// forward pass, so halving the MFMAs per slab exposes it.)
+// N): the same choice as the forward GEMM's -- for each token tile (256 or
+// 128 rows) split the reduction until ~256 blocks fill the chip (at least 4
+// stages per split) and keep the smaller estimate of flops / rate(tile) +
+// fp32 partial traffic.
 GemmConfig dx_gemm_config(int64_t M, int64_t K, int64_t N) {
-  const int64_t tiles = ((M + TILE - 1) / TILE) * ((K + TILE - 1) / TILE);
   const int64_t nst = N / RT;
-  if (tiles >= 192) return GemmConfig{256, 1};
-  int64_t s = 256 / tiles;
-  if (s > nst / 4) s = nst / 4;
-  if (s > 16) s = 16;
-  return GemmConfig{256, s < 1 ? 1 : (int)s};
+  const int64_t k_t = (K + TILE - 1) / TILE;
+  GemmConfig best{256, 1};
+  double best_t = 1e300;
+  for (int tm : {256, 128}) {
+    const int64_t tiles = ((M + tm - 1) / tm) * k_t;
+    int64_t s = tiles >= 192 ? 1 : 256 / tiles;
+    if (s > nst / 4) s = nst / 4;
+    if (s > 16) s = 16;
+    if (s < 1) s = 1;
+    const double blocks = (double)tiles * s;
+    const double fill = blocks >= 256 ? 1.0 : blocks / 256.0;
+    const double rate = (tm == 256 ? 1.1e15 : 0.8e15) * fill;
+    const double partial = s > 1 ? 2.0 * s * (double)M * K * 4 / 5.0e12 : 0.0;
+    const double est = 2.0 * M * K * N / rate + partial;
+    if (est < best_t) {
+      best_t = est;
+      best = GemmConfig{tm, (int)s};
+    }
+  }
+  return best;
 }
 
 int dx_gemm_splits(int64_t M, int64_t K, int64_t N) { return dx_gemm_config(M, K, N).splits; }
@@ -359,7 +378,10 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   const GemmConfig cfg = dx_gemm_config(M, K, N);
   if (cfg.splits != splits) return hipErrorInvalidValue;  // workspace laid out for another split
   const int64_t blocks = ((K + TILE - 1) / TILE) * ((M + cfg.tm - 1) / cfg.tm) * splits;
-  hipLaunchKernelGGL(dx_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  if (cfg.tm == 256)
+    hipLaunchKernelGGL(dx_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(dx_gemm_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, M * K, dx, s);
