@@ -158,39 +158,45 @@ __device__ __forceinline__ TileCoord xcd_tile(int64_t id, int64_t total, int64_t
   return c;
 }
 
-// Epilogue of the fused GEMMs.  A wave holds a 128 (rows: n or k) x 32 MS
-// (columns: tokens m) fp32 tile as 4 x MS MFMA 32x32 tiles; lane l holds
+// Epilogue of the fused GEMMs.  A wave holds a 32 NI (rows: n or k) x 32 NJ
+// (columns: tokens m) fp32 tile as NI x NJ MFMA 32x32 tiles; lane l holds
 // column 32 j + l % 32 and rows 32 i + 8 (v / 4) + 4 (l / 32) + v % 4.  The
 // output is token-major (out[m][row]), so storing straight from registers
 // would give every store instruction 32 rows of 16 bytes.  Instead each
-// 32-column slice goes through the wave's own LDS area (32 x 132 fp32, the
-// 4-float pad spreads the rows over the banks) and comes back row-contiguous:
-// one store instruction then writes two whole 128-row runs.  `part` selects
-// fp32 partials, otherwise values are rounded to bf16.
-constexpr int kEpiStride = 132;
-constexpr int kEpiFloats = 32 * kEpiStride;  // per wave
-template <int MS>
-__device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[4][MS], float* scratch,
+// 32-column slice goes through the wave's own LDS area (32 x (32 NI + 4)
+// fp32; the 4-float pad puts consecutive columns 4 banks apart) and comes
+// back row-contiguous: 8 NI lanes then store one column's 32 NI rows.
+// `part` selects fp32 partials, otherwise values are rounded to bf16.
+template <int NI>
+constexpr int epi_stride() { return 32 * NI + 4; }
+template <int NI>
+constexpr int epi_floats() { return 32 * epi_stride<NI>(); }  // per wave
+template <int NI, int NJ>
+__device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[NI][NJ], float* scratch,
                                                int64_t row0, int64_t col0, int64_t nrows,
                                                int64_t ncols, bool part, float* outf,
                                                uint16_t* outh, int64_t ld, int lane) {
+  constexpr int S = epi_stride<NI>();
+  constexpr int LPC = 8 * NI;      // lanes per column
+  constexpr int CPP = 64 / LPC;    // columns per pass
   const int lr = lane & 31, lg = lane >> 5;
-  const int64_t row = row0 + 4 * lr;  // the 4 rows this lane stores
+  const int rr = lane % LPC, cc = lane / LPC;
+  const int64_t row = row0 + 4 * rr;  // the 4 rows this lane stores
   const bool row_ok = row < nrows;
 #pragma unroll
-  for (int j = 0; j < MS; ++j) {
+  for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                            acc[i][j][4 * q + 3]};
-        *reinterpret_cast<f32x4_t*>(scratch + lr * kEpiStride + 32 * i + 8 * q + 4 * lg) = v;
+        *reinterpret_cast<f32x4_t*>(scratch + lr * S + 32 * i + 8 * q + 4 * lg) = v;
       }
 #pragma unroll
-    for (int pp = 0; pp < 16; ++pp) {
-      const int c = 2 * pp + lg;  // column within the slice
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(scratch + c * kEpiStride + 4 * lr);
+    for (int pp = 0; pp < 32 / CPP; ++pp) {
+      const int c = CPP * pp + cc;  // column within the slice
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(scratch + c * S + 4 * rr);
       const int64_t m = col0 + 32 * j + c;
       if (m < ncols && row_ok) {
         if (part) {

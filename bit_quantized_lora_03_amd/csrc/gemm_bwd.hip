@@ -320,8 +320,8 @@ void dx_gemm_kernel(DxParams p) {
 
   // --- epilogue: D[k][m] -> dx[m][k] (or the split's fp32 partial) ---
   __syncthreads();  // the LDS stages are free from here on
-  float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * kEpiFloats;
-  store_acc_tile<MS>(acc, scratch, k0 + 128 * wk, m0 + 32 * MS * wm, K, M, p.splits > 1,
+  float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<4>();
+  store_acc_tile<4, MS>(acc, scratch, k0 + 128 * wk, m0 + 32 * MS * wm, K, M, p.splits > 1,
                      p.splits > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
 }
 

@@ -3,30 +3,39 @@
 // [QLoRA / infivelines.com]: the 4-bit base is dequantised to bf16 one block
 // at a time inside the matrix multiply, and the adapters stay in full
 // precision.  One 64-wide k tile of a weight row is exactly one NF4 block,
-// so each thread decodes one block per k tile into LDS with that block's own
-// 16-entry table, and the tile feeds bf16 MFMA (32x32x16, fp32 accumulate)
-// together with the activation tile.
+// so each thread decodes one weight row's block per k tile with that block's
+// own 16-entry table, and the decoded values go straight into the MFMA
+// operand registers: the weight never passes through LDS.  Only the
+// activation tile, which all four waves share, is staged in LDS.
 //
 // The adapter term rides on the same accumulators: with xs = [hi | lo] the
 // bf16 split of s . x . A^T (hi + lo equals the fp32 value to 2^-17), the
 // product xs . [B | B]^T runs as 2r extra reduction columns after the base
 // reduction, so y is rounded to bf16 exactly once.
 //
-// Block tile 256 (n) x 256 (m) x 64 (k); 4 waves in a 2 x 2 grid, each a
-// 128 x 128 sub-tile of 4 x 4 MFMA tiles (256 fp32 accumulators per lane,
-// one wave per SIMD).  Two LDS stages of (W tile, x tile), 128 KiB.
+// Block tile 256 (n) x TM (m) x 64 (k), TM = 256 or 128; 4 waves, wave w
+// owning weight rows 64 w .. 64 w + 63 against all TM tokens (2 x TM/32
+// MFMA 32x32x16 tiles, fp32 accumulate, one wave per SIMD).  Thread t
+// decodes row 64 w + t of its wave into eight 8-value chunks.  MFMA step kk
+// of a k tile takes, in lanes 0..31, k chunk kk and, in lanes 32..63, chunk
+// 4 + kk (the reduction order inside a tile is free, as long as both
+// operands use the same one), so lane l needs chunk kk of row l % 32 and
+// lane l + 32 chunk 4 + kk of it: one v_permlane32_swap per register pair
+// exchanges the halves decoded by the other 32 lanes.
 //
-// Pipeline per k tile: the MFMAs of tile t run from LDS stage t&1 while the
-// same waves decode tile t+1's codes (loaded one tile earlier) into the
-// other stage, one quarter of the decode after each quarter of the MFMAs,
-// so the matrix cores and the vector ALUs work at the same time.  Codes are
-// fetched two tiles ahead and x one tile ahead.  Out-of-range rows are
-// clamped to the last valid row instead of branched around, so the loop
-// body is a single basic block; their results are never stored.
+// Pipeline: the activation tile goes through a 3-stage LDS ring, each chunk
+// loaded into a register one k tile before it is written, so one barrier
+// per k tile covers both hazards and the B operands of the next tile's
+// first step can be read before that barrier.  While the MFMAs of tile t
+// run, the same waves decode tile t+1's codes (loaded one tile earlier) in
+// small, fixed pieces placed between the MFMAs, so the matrix cores and the
+// vector ALUs work at the same time.  Out-of-range rows are clamped to the
+// last valid row instead of branched around, so the loop body is a single
+// basic block; their results are never stored.
 //
 // When the output has too few tiles to fill the chip, the k range is split
-// over gridDim.z blocks that write fp32 partials; fwd_reduce adds them in a
-// fixed order and rounds once.
+// over blocks that write fp32 partials; splitk_reduce adds them in a fixed
+// order and rounds once.
 
 #include <type_traits>
 
@@ -37,10 +46,10 @@ namespace qlora {
 
 namespace {
 
-constexpr int TILE = 256;   // n and m extent of a block tile
-constexpr int KT = 64;      // k extent of one stage (= one NF4 block)
-constexpr int ROW_CHUNKS = KT / 8;              // 16-byte chunks per tile row
-constexpr int TILE_CHUNKS = TILE * ROW_CHUNKS;  // u32x4 per tile
+constexpr int TILE_N = 256;  // n extent of a block tile
+constexpr int KT = 64;       // k extent of one tile (= one NF4 block)
+constexpr int ROW_CHUNKS = KT / 8;  // 16-byte chunks per tile row
+constexpr int NSTAGE = 4;           // activation ring depth
 
 struct FwdParams {
   const uint8_t* codes;
@@ -69,61 +78,96 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 
 __device__ __forceinline__ int64_t clamp_row(int64_t v, int64_t hi) { return v < hi ? v : hi - 1; }
 
+// s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS
+// operations of this wave are outstanding (expcnt left free).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
+// Register v of a and b becomes (lanes 0..31 of a, lanes 0..31 of b) and
+// (lanes 32..63 of a, lanes 32..63 of b).
+__device__ __forceinline__ void swap_halves(u32x4_t& a, u32x4_t& b, int v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a[v], b[v], false, false);
+  a[v] = r[0];
+  b[v] = r[1];
+}
+
 }  // namespace
 
-// MS: 32-wide token subtiles per wave.  MS = 4 is the 256 (n) x 256 (m)
-// block tile; MS = 2 halves the token extent (256 x 128), which doubles the
-// number of output tiles for small-M shapes and so halves the k splits (and
-// their fp32 partials) needed to fill the chip.
-template <int MS>
+// JT: 32-token MFMA tiles per wave; the block tile is 256 (n) x 32 JT (m).
+// JT = 8 amortises each decoded weight over 256 tokens; JT = 4 doubles the
+// number of output tiles for small-M shapes and so halves the k splits
+// (and their fp32 partials) needed to fill the chip.
+template <int JT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(FwdParams p) {
-  constexpr int TM = 64 * MS;             // token rows of the block tile
-  constexpr int XR = TM / 32;             // x rows staged per thread
-  constexpr int WCH = TILE * ROW_CHUNKS;  // W stage, u32x4
-  constexpr int XCH = TM * ROW_CHUNKS;    // x stage, u32x4
-  __shared__ u32x4_t lds[2][WCH + XCH];   // [stage][W tile | x tile]
+  constexpr int TM = 32 * JT;             // token rows of the block tile
+  constexpr int XR = TM / 32;             // x chunks staged per thread per tile
+  constexpr int XST = TM * ROW_CHUNKS;    // u32x4 per ring stage
+  constexpr int EPI = 4 * epi_floats<2>() / 4;  // epilogue scratch, u32x4
+  constexpr int LDS_U4 = NSTAGE * XST > EPI ? NSTAGE * XST : EPI;
+  __shared__ u32x4_t lds[LDS_U4];
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
-  const int wn = wave & 1, wm = wave >> 1;
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int64_t m_tiles = (M + TM - 1) / TM, n_tiles = (N + TILE - 1) / TILE;
+  const int64_t m_tiles = (M + TM - 1) / TM, n_tiles = (N + TILE_N - 1) / TILE_N;
   const TileCoord tc = xcd_tile(blockIdx.x, (int64_t)gridDim.x, m_tiles, n_tiles, 4);
-  const int64_t n0 = tc.n * TILE;
+  const int64_t n0 = tc.n * TILE_N;
   const int64_t m0 = tc.m * TM;
   const int z = (int)tc.z;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  auto W = [&](int stage, int row, int chunk) -> u32x4_t& { return lds[stage][rk(row, chunk)]; };
-  auto Xl = [&](int stage, int row, int chunk) -> u32x4_t& {
-    return lds[stage][WCH + rk(row, chunk)];
+  auto Xs = [&](int stage, int row, int chunk) -> u32x4_t& {
+    return lds[stage * XST + rk(row, chunk)];
+  };
+  // B operand of MFMA step kk, token tile j: chunk kk (lanes 0..31) or
+  // 4 + kk (lanes 32..63) of token 32 j + l % 32
+  auto read_b = [&](int stage, int kk, int j) -> u32x4_t {
+    return Xs(stage, 32 * j + lr, 4 * lg + kk);
   };
 
   // k tiles of this split
   const int64_t nkt = K / KT;
   const int64_t kt0 = nkt * z / p.splits, kt1 = nkt * (z + 1) / p.splits;
 
-  f32x16_t acc[4][MS];
+  f32x16_t acc[2][JT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < MS; ++j)
+    for (int j = 0; j < JT; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // this thread decodes weight row n0 + t (clamped) and stages x rows
-  // m0 + (t >> 3) + 32 j, chunk t & 7
+  // this thread decodes weight row n0 + t (clamped)
   const int64_t wrow = clamp_row(n0 + t, N);
   const uint8_t* wcodes = p.codes + ((wrow * K) >> 1);
   const int64_t wblk0 = (wrow * K) >> 6;
-  // x rows m0 + (t >> 3) + 32 j through a buffer descriptor: rows past M
-  // read as zero
-  const __amdgpu_buffer_rsrc_t xres = make_rsrc(p.x, (uint32_t)(M * K * 2));
-  const uint32_t xoff = (uint32_t)(((m0 + (t >> 3)) * K + 8 * (t & 7)) * 2);
-  const uint32_t xrow_step = (uint32_t)(32 * K * 2);
 
-  // The scale byte and its step stay raw until the tile is decoded (an
-  // iteration later): forming s' here would make the wave wait for this
-  // prefetch -- and, since loads return in order, for every load before it.
+  // The x tile reaches LDS by DMA (buffer loads that write LDS directly):
+  // instruction q of wave w fills the 1 KiB region R = XR w + q of a stage,
+  // lane i its 16 bytes at 16 i, i.e. tile row 8 R + i / 8 at physical
+  // chunk i % 8, which holds logical chunk (i % 8) ^ ((row / 2) % 8) -- the
+  // swizzled layout -- so each lane fetches that chunk.  The swizzle term
+  // is (4 (R % 2) + i / 16) % 8, so lanes need one offset for even and one
+  // for odd R.  Rows past M lie beyond the descriptor and read as zero.
+  // The bounds check covers the per-lane offset only (not the scalar one),
+  // so every row term goes into the lane offset and the scalar offset
+  // carries the k position alone.
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(p.x, (uint32_t)(M * K * 2));
+  uint32_t xvoff[2];
+#pragma unroll
+  for (int odd = 0; odd < 2; ++odd) {
+    const int c = (lane & 7) ^ ((4 * odd + (lane >> 4)) & 7);
+    xvoff[odd] = (uint32_t)((m0 + 8 * XR * wave + (lane >> 3)) * K * 2 + 16 * c);
+  }
+  auto dma_x = [&](u32x4_t* stage, int64_t kt, int q) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        xres, (__attribute__((address_space(3))) void*)(stage + 64 * (XR * wave + q)), 16,
+        xvoff[q & 1] + (uint32_t)(q * 8 * K * 2), (uint32_t)(kt * KT * 2), 0, 0);
+  };
+
+  // The scale byte and its step stay raw until the tile is decoded:
+  // forming s' at load time would make the wave wait for this prefetch --
+  // and, since loads return in order, for every load before it.
   struct Codes {
     u32x4_t c0, c1;
     uint32_t q;
@@ -137,183 +181,240 @@ void fwd_gemm_kernel(FwdParams p) {
     c.q = p.qscale[b];
     c.st = p.step[b >> 8];
   };
-  auto load_x = [&](int64_t kt, u32x4_t (&xr)[XR]) {
-    const uint32_t o = xoff + (uint32_t)(kt * KT * 2);
-#pragma unroll
-    for (int j = 0; j < XR; ++j) xr[j] = buffer_load16(xres, o + j * xrow_step);
-  };
-  auto store_x = [&](int stage, const u32x4_t (&xr)[XR]) {
-#pragma unroll
-    for (int j = 0; j < XR; ++j) Xl(stage, (t >> 3) + 32 * j, t & 7) = xr[j];
-  };
-  auto mfma_step = [&](int stage, int kk) {
-    const int ch = 2 * kk + lg;
-    u32x4_t a[4], b[MS];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = W(stage, 128 * wn + 32 * i + lr, ch);
-#pragma unroll
-    for (int j = 0; j < MS; ++j) b[j] = Xl(stage, 32 * MS * wm + 32 * j + lr, ch);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < MS; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+  auto store_x = [&](int stage, int q, const u32x4_t& v) {
+    Xs(stage, (t >> 3) + 32 * q, t & 7) = v;
   };
 
   if (kt0 < kt1) {
-    // Register sets are indexed by tile parity (relative to kt0): X[q] and
-    // C[q] hold the x rows and codes of a tile with parity q.  At the top of
-    // iteration kt the set of parity(kt) is free (tile kt already sits in
-    // LDS), so tile kt+2 is loaded into it there; tile kt+1's set, loaded an
-    // iteration earlier, is decoded and written into the other LDS stage.
-    // The loop is unrolled by two so the parity is a constant and no
-    // register holding an in-flight load is ever copied (a copy would make
-    // the compiler wait for the load).  Prefetch indices are clamped into
-    // the split, so loads are unconditional.
+    // Rings indexed by tile number mod 4 (relative to kt0): LDS stage q
+    // and code set C[q] belong to a tile with that residue.  x tiles are
+    // DMA'd three tiles ahead and codes loaded during step 3 of the
+    // iteration four tiles earlier: since vector loads complete in order, a
+    // wait for any load is also a wait for every older one, so every load
+    // gets two to three iterations (the first touch of a weight line comes
+    // from HBM).  The loop is unrolled by four so every ring index is a
+    // constant and no register holding an in-flight load is ever copied (a
+    // copy would make the compiler wait for the load).  Prefetch indices
+    // are clamped into the split, so loads are unconditional.
     const int64_t last = kt1 - 1;
     auto cl = [&](int64_t v) { return v < last ? v : last; };
-    Codes C[2];
-    u32x4_t X[2][XR];
+    Codes C[NSTAGE];
+    u32x4_t Ap[2][2];    // A operands of a step: [step parity][i]
+    u32x4_t op[2][JT];   // B operands, by step parity
+
+    // Decode state.  The weights are decoded just in time: during step kk
+    // the waves decode the chunk pair step kk+1 needs (pair 0 of the next
+    // tile, after that tile's table, during step 3), so only two steps of A
+    // operands are ever held.
+    uint32_t pk[8];
+    Nf4Lut lut;
+    float sc = 0.0f;
+    uint32_t dn0 = 0, dn1 = 0, nh = 0, pick = 0, la = 0, lb = 0;
+    u32x4_t dlo = zero, dhi = zero;
+    auto lookup_a = [&](uint32_t n) {  // low-byte planes of 4 codes
+      nh = n & 0x07070707u;
+      pick = ((n >> 1) & 0x04040404u) | 0x03020100u;
+      la = perm(lut.lo[1], lut.lo[0], n);
+      lb = perm(lut.lo[3], lut.lo[2], nh);
+    };
+    auto lookup_b = [&](uint32_t n, uint32_t& o01, uint32_t& o23) {  // high bytes, merge
+      const uint32_t lo = perm(lb, la, pick);
+      const uint32_t hi =
+          perm(perm(lut.hi[3], lut.hi[2], nh), perm(lut.hi[1], lut.hi[0], n), pick);
+      o01 = perm(hi, lo, 0x05010400u);
+      o23 = perm(hi, lo, 0x07030602u);
+    };
+    auto decode_part = [&](uint32_t v, int w, u32x4_t& d) {
+      switch (w) {
+        case 0: {
+          const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
+          dn0 = perm(od, ev, 0x05010400u);  // codes 0..3 of the word, one per byte
+          dn1 = perm(od, ev, 0x07030602u);  // codes 4..7
+          break;
+        }
+        case 1: lookup_a(dn0); break;
+        case 2: { uint32_t o0, o1; lookup_b(dn0, o0, o1); d[0] = o0; d[1] = o1; break; }
+        case 3: lookup_a(dn1); break;
+        default: { uint32_t o2, o3; lookup_b(dn1, o2, o3); d[2] = o2; d[3] = o3; break; }
+      }
+    };
+    // table unit u (0..7) of a block: four products-and-packs, four perms
+    auto table_unit = [&](const Codes& c, int u) {
+      if (u < 4) {
+        if (u == 0) sc = nf4_block_scale(c.q, c.st);
+        pk[2 * u] = pack_bf16x2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
+        pk[2 * u + 1] = pack_bf16x2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
+      } else {
+        const int j = u - 4;
+        lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
+        lut.hi[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
+      }
+    };
+    // pair unit w (0..11) of chunk pair pr: the decode of code words pr and
+    // 4 + pr (5 units each, about 5 vector ops per unit), then the
+    // lane-half exchange (2 units) that makes them step pr's A operands
+    auto pair_unit = [&](const Codes& c, int pr, int w, u32x4_t (&dst)[2]) {
+      if (w < 5) {
+        decode_part(c.c0[pr], w, dlo);
+      } else if (w < 10) {
+        decode_part(c.c1[pr], w - 5, dhi);
+      } else {
+        const int v = 2 * (w - 10);
+        swap_halves(dlo, dhi, v);
+        swap_halves(dlo, dhi, v + 1);
+        if (w == 11) {
+          dst[0] = dlo;
+          dst[1] = dhi;
+        }
+      }
+    };
+
+    // Prologue: codes of tiles kt0..kt0+3, x tiles kt0..kt0+2, the table
+    // and first pair of tile kt0; then wait for x tiles kt0 and kt0+1.
+    // (scheduling fences keep this issue order, which the wait below counts)
     load_codes(kt0, C[0]);
-    load_x(kt0, X[0]);
-    store_x(0, X[0]);
-    {
-      const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(C[0].q, C[0].st));
 #pragma unroll
-      for (int c = 0; c < 8; ++c) W(0, t, c) = nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]);
-    }
-    load_x(cl(kt0 + 1), X[1]);
+    for (int q = 0; q < XR; ++q) dma_x(&lds[0], kt0, q);
+#pragma unroll
+    for (int q = 0; q < XR; ++q) dma_x(&lds[XST], cl(kt0 + 1), q);
+    __builtin_amdgcn_sched_barrier(0);
     load_codes(cl(kt0 + 1), C[1]);
-    __syncthreads();
+    load_codes(cl(kt0 + 2), C[2]);
+    load_codes(cl(kt0 + 3), C[3]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < XR; ++q) dma_x(&lds[2 * XST], cl(kt0 + 2), q);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) table_unit(C[0], u);
+#pragma unroll
+    for (int w = 0; w < 12; ++w) pair_unit(C[0], 0, w, Ap[0]);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(12 + XR, 0));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 0; j < JT; ++j) op[0][j] = read_b(0, 0, j);
 
     // Hand-scheduled iteration.  Issue is in order, so back-to-back MFMAs
     // would hold everything behind them; instead each MFMA of the tile is
     // followed by a small, fixed amount of other work and a scheduling
     // fence, so the vector work executes while the matrix core is busy.
-    auto iteration = [&](int64_t kt, auto parity) {
-      constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
-      constexpr int SPK = 4 * MS;       // MFMAs (slots) per k step
-      constexpr int NRD = 4 + MS;       // operand reads per k step
-      // tile kt+2 into the free set (loads issued first, used an iteration later)
-      load_x(cl(kt + 2), X[cur]);
-      load_codes(cl(kt + 2), C[cur]);
-      const Codes& cn = C[nxt];
-      u32x4_t op[2][2][4];  // [buffer][a|b][i]
-      auto read_op = [&](int kk, int buf, int q) {
-        const int ch = 2 * kk + lg;
-        if (q < 4)
-          op[buf][0][q] = W(cur, 128 * wn + 32 * q + lr, ch);
-        else
-          op[buf][1][q - 4] = Xl(cur, 32 * MS * wm + 32 * (q - 4) + lr, ch);
-      };
-#pragma unroll
-      for (int q = 0; q < NRD; ++q) read_op(0, 0, q);
-
-      // Work units of the tile, in order: the table of tile kt+1's block
-      // (units 0..7), the decode of its 8 code words (6 units each, about 5
-      // vector ops per unit, the last one the 16-byte LDS write), the LDS
-      // writes of its x rows (units 56..56+XR-1).  MS = 4 runs one unit per
-      // MFMA (each fits in the MFMA's 32-cycle shadow), MS = 2 two.  The
-      // operand reads of step kk+1 ride in the last slots of step kk.
-      uint32_t pk[8];
-      Nf4Lut lut;
-      float sc = 0.0f;
-      uint32_t dn0 = 0, dn1 = 0, nh = 0, pick = 0, la = 0, lb = 0;
-      u32x4_t dv = zero;
-      auto lookup_a = [&](uint32_t n) {  // low-byte planes of 4 codes
-        nh = n & 0x07070707u;
-        pick = ((n >> 1) & 0x04040404u) | 0x03020100u;
-        la = perm(lut.lo[1], lut.lo[0], n);
-        lb = perm(lut.lo[3], lut.lo[2], nh);
-      };
-      auto lookup_b = [&](uint32_t n, uint32_t& o01, uint32_t& o23) {  // high bytes, merge
-        const uint32_t lo = perm(lb, la, pick);
-        const uint32_t hi =
-            perm(perm(lut.hi[3], lut.hi[2], nh), perm(lut.hi[1], lut.hi[0], n), pick);
-        o01 = perm(hi, lo, 0x05010400u);
-        o23 = perm(hi, lo, 0x07030602u);
-      };
-      auto unit = [&](int u) {
-        if (u < 4) {
-          if (u == 0) sc = nf4_block_scale(cn.q, cn.st);
-          pk[2 * u] = pack_bf16x2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
-          pk[2 * u + 1] = pack_bf16x2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
-        } else if (u < 8) {
-          const int j = u - 4;
-          lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
-          lut.hi[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
-        } else if (u < 56) {
-          const int c = (u - 8) / 6, w = (u - 8) % 6;
-          const uint32_t v = (c < 4 ? cn.c0 : cn.c1)[c & 3];
-          switch (w) {
-            case 0: {
-              const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
-              dn0 = perm(od, ev, 0x05010400u);  // codes 0..3 of the word, one per byte
-              dn1 = perm(od, ev, 0x07030602u);  // codes 4..7
-              break;
-            }
-            case 1: lookup_a(dn0); break;
-            case 2: { uint32_t o0, o1; lookup_b(dn0, o0, o1); dv[0] = o0; dv[1] = o1; break; }
-            case 3: lookup_a(dn1); break;
-            case 4: { uint32_t o2, o3; lookup_b(dn1, o2, o3); dv[2] = o2; dv[3] = o3; break; }
-            default: W(nxt, t, c) = dv; break;
-          }
-        } else if (u < 56 + XR) {
-          // tile kt+1's x rows into the other stage
-          Xl(nxt, (t >> 3) + 32 * (u - 56), t & 7) = X[nxt][u - 56];
-        }
+    // The stages are passed as restrict pointers: the ones read and the one
+    // being filled are distinct, which lets the compiler leave the DMA in
+    // flight across the reads.  The DMA's own completion is awaited by hand
+    // (s_waitcnt) before the barrier that publishes a stage.
+    auto iteration = [&](int64_t kt, auto phase, u32x4_t* __restrict__ rd0,
+                         u32x4_t* __restrict__ rd1, u32x4_t* __restrict__ fill) {
+      constexpr int ph = decltype(phase)::value;
+      constexpr int SPK = 2 * JT;  // MFMAs (slots) per k step
+      auto rb = [&](u32x4_t* st, int kk, int j) -> u32x4_t {
+        return st[rk(32 * j + lr, 4 * lg + kk)];
       };
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
+        // steps 0..2 decode pair kk+1 of this tile (12 units); step 3
+        // builds the next tile's table and decodes its pair 0 (20 units)
+        const int NU = kk < 3 ? 12 : 20;
 #pragma unroll
         for (int s = 0; s < SPK; ++s) {
-          const int i = s / MS, j = s % MS;
-          acc[i][j] = mfma32x32x16(op[kk & 1][0][i], op[kk & 1][1][j], acc[i][j]);
-          const int slot = SPK * kk + s;
-          if (kk < 3 && s >= SPK - NRD) read_op(kk + 1, (kk + 1) & 1, s - (SPK - NRD));
-          constexpr int UPS = 16 / SPK;  // units per slot: 64 units over 4 SPK slots
+          const int j = s >> 1, i = s & 1;
+          acc[i][j] = mfma32x32x16(Ap[kk & 1][i], op[kk & 1][j], acc[i][j]);
+          if (i == 1) {
+            // operand j of the next step: this tile's, or the next tile's
+            // first (its stage was completed before the last barrier)
+            if (kk < 3)
+              op[(kk + 1) & 1][j] = rb(rd0, kk + 1, j);
+            else
+              op[0][j] = rb(rd1, 0, j);
+          }
+          if (kk == 3 && s == 0) {
+            // tile kt's codes are consumed: tile kt+4's into their set
+            load_codes(cl(kt + 4), C[ph]);
+          }
 #pragma unroll
-          for (int e = 0; e < UPS; ++e) unit(UPS * slot + e);
+          for (int u = s * NU / SPK; u < (s + 1) * NU / SPK; ++u) {
+            if (kk < 3)
+              pair_unit(C[ph], kk + 1, u, Ap[(kk + 1) & 1]);
+            else if (u < 8)
+              table_unit(C[(ph + 1) % NSTAGE], u);
+            else
+              pair_unit(C[(ph + 1) % NSTAGE], 0, u - 8, Ap[0]);
+          }
+          const int slot = SPK * kk + s;
+          if (slot % 8 == 7) dma_x(fill, cl(kt + 3), slot / 8);  // x chunk of tile kt+3
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      __syncthreads();
+      // x tile kt+2 (DMA'd during the last iteration) is complete once at
+      // most this iteration's XR + 4 loads are outstanding
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(XR + 4, 0));
+      __builtin_amdgcn_s_barrier();
     };
-    for (int64_t kt = kt0; kt < kt1; kt += 2) {
-      iteration(kt, std::integral_constant<int, 0>());
-      if (kt + 1 < kt1) iteration(kt + 1, std::integral_constant<int, 1>());
+    u32x4_t* const S0 = &lds[0];
+    u32x4_t* const S1 = &lds[XST];
+    u32x4_t* const S2 = &lds[2 * XST];
+    u32x4_t* const S3 = &lds[3 * XST];
+    // Whole groups of four in the loop, the rest after it: the loop's back
+    // edge then only ever follows phase 3, so the compiler's wait analysis
+    // sees every load's true age at the loop head.
+    int64_t kt = kt0;
+    for (; kt + 4 <= kt1; kt += 4) {
+      iteration(kt, std::integral_constant<int, 0>(), S0, S1, S3);
+      iteration(kt + 1, std::integral_constant<int, 1>(), S1, S2, S0);
+      iteration(kt + 2, std::integral_constant<int, 2>(), S2, S3, S1);
+      iteration(kt + 3, std::integral_constant<int, 3>(), S3, S0, S2);
     }
+    if (kt < kt1) {
+      iteration(kt, std::integral_constant<int, 0>(), S0, S1, S3);
+      if (kt + 1 < kt1) {
+        iteration(kt + 1, std::integral_constant<int, 1>(), S1, S2, S0);
+        if (kt + 2 < kt1) iteration(kt + 2, std::integral_constant<int, 2>(), S2, S3, S1);
+      }
+    }
+    // the clamped prefetches past the split are still writing LDS
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   }
 
   // --- adapter columns: xs [M, 2r] against [B | B] (last split only) ---
   const int r = p.r;
   if (z == p.splits - 1) {
     const int ext_tiles = (2 * r + KT - 1) / KT;
-    const int64_t m = clamp_row(m0 + (t % TM), M);
     for (int e = 0; e < ext_tiles; ++e) {
+      __syncthreads();  // the ring is free
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int col = e * KT + 8 * c;
-        u32x4_t wv = zero, xv = zero;
-        if (col < 2 * r) {
-          const int j = col < r ? col : col - r;
-          wv = *reinterpret_cast<const u32x4_t*>(p.B + wrow * r + j);
-          xv = *reinterpret_cast<const u32x4_t*>(p.xs + m * 2 * r + col);
-        }
-        W(0, t, c) = wv;
-        if (t < TM) Xl(0, t, c) = xv;
+      for (int q = 0; q < XR; ++q) {
+        const int64_t m = clamp_row(m0 + (t >> 3) + 32 * q, M);
+        const int col = e * KT + 8 * (t & 7);
+        const u32x4_t v =
+            col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.xs + m * 2 * r + col) : zero;
+        store_x(0, q, v);
       }
+      u32x4_t a[2][4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int64_t row = clamp_row(n0 + 64 * wave + 32 * i + lr, N);
+          const int col = e * KT + 8 * (4 * lg + kk);
+          const int jj = col < r ? col : col - r;
+          a[i][kk] = col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.B + row * r + jj) : zero;
+        }
       __syncthreads();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) mfma_step(0, kk);
-      __syncthreads();
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+          const u32x4_t b = read_b(0, kk, j);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) acc[i][j] = mfma32x32x16(a[i][kk], b, acc[i][j]);
+        }
     }
   }
 
   // --- epilogue: D[n][m] -> y[m][n] (or the split's fp32 partial) ---
-  __syncthreads();  // the LDS stages are free from here on
-  float* scratch = reinterpret_cast<float*>(&lds[0][0]) + wave * kEpiFloats;
-  store_acc_tile<MS>(acc, scratch, n0 + 128 * wn, m0 + 32 * MS * wm, N, M, p.splits > 1,
-                     p.splits > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
+  __syncthreads();  // the LDS ring is free from here on
+  float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<2>();
+  store_acc_tile<2, JT>(acc, scratch, n0 + 64 * wave, m0, N, M, p.splits > 1,
+                        p.splits > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
 }
 
 // out[i] = bf16(sum_z part[z][i]), i over M*N (4 per thread), fixed order.
@@ -356,7 +457,7 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, ui
 // tokens, the 128-row one needs half the splits).
 GemmConfig gemm_config(int64_t M, int64_t N, int64_t Kred) {
   const int64_t nkt = Kred / KT;
-  const int64_t n_t = (N + TILE - 1) / TILE;
+  const int64_t n_t = (N + TILE_N - 1) / TILE_N;
   GemmConfig best{256, 1};
   double best_t = 1e300;
   for (int tm : {256, 128}) {
@@ -401,11 +502,11 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.r = r;
   p.splits = splits;
   p.L = L;
-  const int64_t blocks = ((N + TILE - 1) / TILE) * ((M + cfg.tm - 1) / cfg.tm) * splits;
+  const int64_t blocks = ((N + TILE_N - 1) / TILE_N) * ((M + cfg.tm - 1) / cfg.tm) * splits;
   if (cfg.tm == 256)
-    hipLaunchKernelGGL(fwd_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(fwd_gemm_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(fwd_gemm_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(fwd_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_splitk_reduce(part, splits, M * N, y, s);
