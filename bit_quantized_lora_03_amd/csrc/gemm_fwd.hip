@@ -188,11 +188,12 @@ void fwd_gemm_kernel(FwdParams p) {
   if (kt0 < kt1) {
     // Rings indexed by tile number mod 4 (relative to kt0): LDS stage q
     // and code set C[q] belong to a tile with that residue.  x tiles are
-    // DMA'd three tiles ahead and codes loaded during step 3 of the
-    // iteration four tiles earlier: since vector loads complete in order, a
-    // wait for any load is also a wait for every older one, so every load
-    // gets two to three iterations (the first touch of a weight line comes
-    // from HBM).  The loop is unrolled by four so every ring index is a
+    // DMA'd three tiles ahead and codes loaded at the end of the iteration
+    // four tiles earlier.  Vector loads complete in order, so a wait for
+    // any load is also a wait for every older one; the order (x chunks,
+    // then codes) and the one wait per iteration are arranged so that x
+    // gets one to two iterations and codes (whose first touch of a weight
+    // line comes from HBM) two.  The loop is unrolled by four so every ring index is a
     // constant and no register holding an in-flight load is ever copied (a
     // copy would make the compiler wait for the load).  Prefetch indices
     // are clamped into the split, so loads are unconditional.
@@ -270,8 +271,9 @@ void fwd_gemm_kernel(FwdParams p) {
     };
 
     // Prologue: codes of tiles kt0..kt0+3, x tiles kt0..kt0+2, the table
-    // and first pair of tile kt0; then wait for x tiles kt0 and kt0+1.
-    // (scheduling fences keep this issue order, which the wait below counts)
+    // and first pair of tile kt0; then wait for x tiles kt0 and kt0+1.  The
+    // issue order (kept by scheduling fences) ends like an iteration's: x
+    // tile kt0+2, then the codes of kt0+3, which the waits below count on.
     load_codes(kt0, C[0]);
 #pragma unroll
     for (int q = 0; q < XR; ++q) dma_x(&lds[0], kt0, q);
@@ -280,10 +282,11 @@ void fwd_gemm_kernel(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     load_codes(cl(kt0 + 1), C[1]);
     load_codes(cl(kt0 + 2), C[2]);
-    load_codes(cl(kt0 + 3), C[3]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < XR; ++q) dma_x(&lds[2 * XST], cl(kt0 + 2), q);
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(cl(kt0 + 3), C[3]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 8; ++u) table_unit(C[0], u);
@@ -326,10 +329,6 @@ void fwd_gemm_kernel(FwdParams p) {
             else
               op[0][j] = rb(rd1, 0, j);
           }
-          if (kk == 3 && s == 0) {
-            // tile kt's codes are consumed: tile kt+4's into their set
-            load_codes(cl(kt + 4), C[ph]);
-          }
 #pragma unroll
           for (int u = s * NU / SPK; u < (s + 1) * NU / SPK; ++u) {
             if (kk < 3)
@@ -344,9 +343,14 @@ void fwd_gemm_kernel(FwdParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // x tile kt+2 (DMA'd during the last iteration) is complete once at
-      // most this iteration's XR + 4 loads are outstanding
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(XR + 4, 0));
+      // tile kt's codes are consumed: tile kt+4's into their set, issued
+      // after this iteration's DMA so that the wait below (for the x tile
+      // DMA'd during the last iteration) does not also wait for them, nor
+      // for the codes issued at the end of the last iteration: x tile kt+2
+      // is complete once at most those 4 + XR + 4 loads are outstanding
+      load_codes(cl(kt + 4), C[ph]);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(XR + 8, 0));
       __builtin_amdgcn_s_barrier();
     };
     u32x4_t* const S0 = &lds[0];
