@@ -7,21 +7,25 @@
 //
 // The reduction here runs over the output features n, while the packed
 // weight is stored k-contiguous (row n holds blocks along k).  Each block
-// tile therefore decodes a 64 (n) x 256 (k) slab row by row -- one NF4
-// block per thread, the same decode as the forward pass -- and writes it
-// into LDS k-major (n contiguous), so that MFMA operands are again 16-byte
-// reads.  dy tiles go to LDS as in the forward pass.
+// tile decodes a 64 (n) x 256 (k) slab -- one NF4 block per thread, the same
+// decode as the forward pass -- and writes it to LDS as it is laid out in
+// memory (16-byte stores of 8 consecutive k).  The MFMA operand wants the
+// transpose (8 consecutive n of one k per lane), which the LDS transpose
+// read ds_read_b64_tr_b16 delivers: within each 16-lane group it hands lane
+// i element i % 4 of the 8-byte chunks addressed by lanes i/4, 4 + i/4,
+// 8 + i/4 and 12 + i/4, so pointing lane j at row n0 + j/4, column
+// k0 + 4 (j % 4) gives lane i the four values of column k0 + i at rows
+// n0..n0+3.  dy tiles go to LDS as in the forward pass.
 //
 // The adapter term uses the same accumulators: with gs = [hi | lo] the bf16
 // split of s . dy . B, gs . [A ; A] is run as 2r extra reduction rows.
 //
 // Block tile 256 (k) x 256 (m), 64 reduction rows per stage; 4 waves in a
-// 2 x 2 grid of 128 x 128; two LDS stages of (W^T tile, dy tile), 128 KiB.
-// As in the forward pass, the next slab is decoded while the current one
-// multiplies (a quarter after each quarter of the MFMAs), codes are fetched
-// two slabs ahead, out-of-range rows are clamped rather than branched
-// around, and small outputs split the reduction over gridDim.z blocks that
-// write fp32 partials.
+// 2 x 2 grid of 128 x 128; two LDS stages of (W slab, dy tile).  As in the
+// forward pass, the next slab is decoded while the current one multiplies,
+// codes are fetched two slabs ahead, out-of-range rows are clamped rather
+// than branched around, and small outputs split the reduction over blocks
+// that write fp32 partials.
 
 #include <type_traits>
 
@@ -35,7 +39,12 @@ namespace {
 constexpr int TILE = 256;
 constexpr int RT = 64;  // reduction rows per stage
 constexpr int ROW_CHUNKS = RT / 8;
-constexpr int TILE_ELEMS = TILE * RT;
+// W slab row stride in LDS, bytes: 512 of data plus 48 of pad.  140 dwords
+// = 12 mod 64 banks, so the 16 rows one store instruction writes per LDS
+// cycle start 12 banks apart (all 64 banks once), and the 4 rows one
+// transpose read touches (8 banks each) are disjoint.
+constexpr int WROW = 560;
+constexpr int WSTAGE = RT * WROW;  // bytes per W stage
 
 struct DxParams {
   const uint8_t* codes;
@@ -62,15 +71,6 @@ __device__ __forceinline__ int rk(int row, int chunk) {
   return row * ROW_CHUNKS + (chunk ^ ((row >> 1) & 7));
 }
 
-// W^T tile: [256 k][64 n] bf16, element offset.  The 16-byte n-chunk is
-// swizzled by (k / 2) mod 8, as above (16 consecutive k rows read at one
-// chunk hit all banks), and by k's 64-block index (the four threads that
-// decode one weight row at k, k+64, k+128, k+192 write distinct chunks).
-__device__ __forceinline__ int wt_off(int k, int n) {
-  const int chunk = (n >> 3) ^ ((k >> 1) & 7) ^ (((k >> 6) & 3) << 1);
-  return k * RT + chunk * 8 + (n & 7);
-}
-
 }  // namespace
 
 // MS: 32-wide token subtiles per wave; MS = 4 is the 256 (k) x 256 (m)
@@ -83,9 +83,9 @@ void dx_gemm_kernel(DxParams p) {
   constexpr int XR = TM / 32;   // dy rows staged per thread
   // one LDS array: two W^T stages, then two dy stages (the epilogue reuses
   // it from the start)
-  constexpr int WT_U4 = 2 * TILE_ELEMS * 2 / 16;
+  constexpr int WT_U4 = 2 * WSTAGE / 16;
   __shared__ u32x4_t lds[WT_U4 + 2 * TM * ROW_CHUNKS];
-  uint16_t(*wt)[TILE_ELEMS] = reinterpret_cast<uint16_t(*)[TILE_ELEMS]>(&lds[0]);
+  char* const wbase = reinterpret_cast<char*>(&lds[0]);
   u32x4_t(*dyt)[TM * ROW_CHUNKS] = reinterpret_cast<u32x4_t(*)[TM * ROW_CHUNKS]>(&lds[WT_U4]);
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
@@ -109,10 +109,11 @@ void dx_gemm_kernel(DxParams p) {
   const int64_t nst = N / RT;
   const int64_t st0 = nst * z / p.splits, st1 = nst * (z + 1) / p.splits;
 
-  // this thread decodes reduction row (t >> 2) of the slab, k quarter (t & 3);
-  // a quarter past K is clamped to the last block (never stored)
-  const int wr = t >> 2;
-  const int kq = t & 3;
+  // this thread decodes reduction row 16 wave + lane % 16 of the slab, k
+  // quarter lane / 16 (so the 16 lanes of one LDS store cycle write 16
+  // rows); a quarter past K is clamped to the last block (never stored)
+  const int wr = 16 * wave + (lane & 15);
+  const int kq = lane >> 4;
   const int64_t kcol_raw = k0 + 64 * kq;
   const bool kcol_ok = kcol_raw < K;
   const int64_t kcol = kcol_ok ? kcol_raw : K - 64;
@@ -147,23 +148,33 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
     for (int j = 0; j < XR; ++j) dyt[stage][rk((t >> 3) + 32 * j, t & 7)] = yr[j];
   };
-  // scatter 8 consecutive-k bf16 values (chunk c of this thread's 64) of
-  // reduction row `wr` into W^T
-  auto scatter8 = [&](int stage, int c, const u32x4_t v) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t pr = v[e];
-      const int kl = 64 * kq + 8 * c + 2 * e;
-      wt[stage][wt_off(kl, wr)] = (uint16_t)pr;
-      wt[stage][wt_off(kl + 1, wr)] = (uint16_t)(pr >> 16);
-    }
+  // store 8 consecutive-k bf16 values (chunk c of this thread's 64) of
+  // reduction row `wr` into the W slab
+  auto store8 = [&](int stage, int c, const u32x4_t v) {
+    *reinterpret_cast<u32x4_t*>(wbase + stage * WSTAGE + wr * WROW + (64 * kq + 8 * c) * 2) = v;
+  };
+  // A operand of MFMA step kk, k sub-tile i: lane l holds column
+  // 128 wk + 32 i + l % 32 at reduction rows 16 kk + 8 (l / 32) + 0..7, from
+  // two transpose reads (rows +0..3 and +4..7).  As provider, lane j of
+  // 16-lane group g points at row 8 (g / 2) + j / 4 (+ 4 for the second
+  // read), column 16 (g % 2) + 4 (j % 4).
+  const int tg = lane >> 4, tj = lane & 15;
+  const int a_off = (8 * (tg >> 1) + (tj >> 2)) * WROW + (128 * wk + 16 * (tg & 1) + 4 * (tj & 3)) * 2;
+  auto read_a = [&](int stage, int kk, int i) -> u32x4_t {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const int o = stage * WSTAGE + a_off + 16 * kk * WROW + 64 * i;
+    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o));
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o + 4 * WROW));
+    const u32x2_t h0 = __builtin_bit_cast(u32x2_t, r0), h1 = __builtin_bit_cast(u32x2_t, r1);
+    const u32x4_t v = {h0[0], h0[1], h1[0], h1[1]};
+    return v;
   };
   auto mfma_step = [&](int stage, int kk) {
     const int ch = 2 * kk + lg;
     u32x4_t a[4], b[MS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const u32x4_t*>(&wt[stage][wt_off(128 * wk + 32 * i + lr, 8 * ch)]);
+    for (int i = 0; i < 4; ++i) a[i] = read_a(stage, kk, i);
 #pragma unroll
     for (int j = 0; j < MS; ++j) b[j] = dyt[stage][rk(32 * MS * wm + 32 * j + lr, ch)];
 #pragma unroll
@@ -188,7 +199,7 @@ void dx_gemm_kernel(DxParams p) {
       const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(C[0].q, C[0].st));
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        scatter8(0, c, nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]));
+        store8(0, c, nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]));
     }
     load_dy(cl(st0 + 1), Y[1]);
     load_codes(cl(st0 + 1), C[1]);
@@ -198,7 +209,7 @@ void dx_gemm_kernel(DxParams p) {
     // MFMAs of the slab is followed by one unit of other work and a
     // scheduling fence -- the table of slab st+1's block (units 0..7), the
     // decode of its 8 code words (6 units each, about 5 vector ops per
-    // unit; the last one scatters the 8 values into W^T), the LDS writes of
+    // unit; the last one stores the 8 values into the W slab), the LDS writes of
     // its dy rows (units 56..63) -- and the operand reads of step kk+1 ride
     // in slots 8..15 of step kk, so the vector work fits in the MFMAs' shadow.
     auto iteration = [&](int64_t st, auto parity) {
@@ -212,8 +223,7 @@ void dx_gemm_kernel(DxParams p) {
       auto read_op = [&](int kk, int buf, int q) {
         const int ch = 2 * kk + lg;
         if (q < 4)
-          op[buf][0][q] =
-              *reinterpret_cast<const u32x4_t*>(&wt[cur][wt_off(128 * wk + 32 * q + lr, 8 * ch)]);
+          op[buf][0][q] = read_a(cur, kk, q);
         else
           op[buf][1][q - 4] = dyt[cur][rk(32 * MS * wm + 32 * (q - 4) + lr, ch)];
       };
@@ -261,7 +271,7 @@ void dx_gemm_kernel(DxParams p) {
             case 2: { uint32_t o0, o1; lookup_b(dn0, o0, o1); dv[0] = o0; dv[1] = o1; break; }
             case 3: lookup_a(dn1); break;
             case 4: { uint32_t o2, o3; lookup_b(dn1, o2, o3); dv[2] = o2; dv[3] = o3; break; }
-            default: scatter8(nxt, c, dv); break;
+            default: store8(nxt, c, dv); break;
           }
         } else if (u < 56 + XR) {
           // slab st+1's dy rows into the other stage
@@ -301,7 +311,7 @@ void dx_gemm_kernel(DxParams p) {
       const int arow = c < r ? c : c - r;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        scatter8(0, q, row_ok ? *reinterpret_cast<const u32x4_t*>(p.A + (int64_t)arow * K + kcol + 8 * q)
+        store8(0, q, row_ok ? *reinterpret_cast<const u32x4_t*>(p.A + (int64_t)arow * K + kcol + 8 * q)
                               : zero);
       // dy side: rows m, columns c of gs
 #pragma unroll
