@@ -81,30 +81,47 @@ def make_layer(name):
     raise SystemExit(f"unknown workload {name}")
 
 
-def _fwd_config(M, N, Kred):
-    """Mirror of the library's tile/k-split choice for the fused forward GEMM
-    (for naming the launches in the roofline line only): (token tile, splits)."""
+def _gemm_schedule(M, Nout, Kred):
+    """Mirror of the library's schedule for a fused GEMM with an M x Nout
+    output and a reduction of Kred (for naming the launches in the roofline
+    line only): (token tile, uniform splits, tail tiles, tail splits)."""
+    slots = 256
     nkt = Kred // 64
-    n_t = (N + 255) // 256
-    best, best_t = (256, 1), float("inf")
+    n_t = (Nout + 255) // 256
+    best, best_t = (256, 1, 0, 1), float("inf")
     for tm in (256, 128):
         tiles = ((M + tm - 1) // tm) * n_t
-        s = 1 if tiles >= 192 else 256 // tiles
-        s = max(1, min(s, nkt // 4, 16))
-        blocks = tiles * s
-        fill = 1.0 if blocks >= 256 else blocks / 256.0
-        rate = (1.1e15 if tm == 256 else 0.8e15) * fill
-        partial = 2.0 * s * M * N * 4 / 5.0e12 if s > 1 else 0.0
-        est = 2.0 * M * N * Kred / rate + partial
+        rate = 1.1e15 if tm == 256 else 0.8e15
+        t_tile = 2.0 * tm * 256 * Kred / (rate / slots)
+        if tiles < 192:
+            s = max(1, min(256 // tiles, nkt // 4, 16))
+            blocks = tiles * s
+            fill = 1.0 if blocks >= slots else blocks / slots
+            est = 2.0 * M * Nout * Kred / (rate * fill)
+            if s > 1:
+                est += 2.0 * s * M * Nout * 4 / 5.0e12
+            cfg = (tm, s, 0, 1)
+        else:
+            rounds, q = divmod(tiles, slots)
+            ts = min(slots // q if q else 1, nkt // 4, 8)
+            if q and ts >= 2:
+                est = (rounds + 1.0 / ts) * t_tile + 2.0 * ts * q * tm * 256 * 4 / 5.0e12
+                cfg = (tm, 1, q, ts)
+            else:
+                est = (rounds + (1 if q else 0)) * t_tile
+                cfg = (tm, 1, 0, 1)
         if est < best_t:
-            best, best_t = (tm, s), est
+            best, best_t = cfg, est
     return best
 
 
-def _dx_splits(M, K, N):
-    """Mirror of the library's reduction-split choice for the dX GEMM (the same
-    rule as the forward GEMM's, over the M x K output)."""
-    return _fwd_config(M, K, N)[1]
+def _schedule_label(cfg):
+    tm, s, q, ts = cfg
+    if q:
+        return f" + tail_reduce_kernel ({q} tail tiles split {ts})"
+    if s > 1:
+        return f" + splitk_reduce_kernel (k split {s})"
+    return ""
 
 
 def _source_digest(key):
@@ -360,8 +377,8 @@ def main():
 
     # the unit the roofline line is about: one base-only fused-GEMM call (the
     # GEMM kernel, plus its split-K reduce kernel when the output is small)
-    fsplit = _fwd_config(M, N, K)[1]
-    dsplit = _dx_splits(M, K, N)
+    fsched = _gemm_schedule(M, N, K)
+    dsched = _gemm_schedule(M, K, N)
     if M <= 32:
         # decode: HBM-bound; algorithmic bytes of the base-only launch
         kb = packed_weight_bytes(N, K) + 2 * M * K + 2 * M * N
@@ -372,13 +389,12 @@ def main():
                 "per_launch": kb, "duration_ms": k_fwd}
         key = "decode"
     else:
-        name, t_k, fl, sp = ("fwd_gemm_kernel", k_fwd, 2 * M * N * K, fsplit)
+        name, t_k, fl, sp = ("fwd_gemm_kernel", k_fwd, 2 * M * N * K, fsched)
         key = "fwd"
         if "bwd" in kind and k_dx > k_fwd:
-            name, t_k, fl, sp = ("dx_gemm_kernel", k_dx, 2 * M * N * K, dsplit)
+            name, t_k, fl, sp = ("dx_gemm_kernel", k_dx, 2 * M * N * K, dsched)
             key = "dx"
-        if sp > 1:
-            name += f" + splitk_reduce_kernel (k split {sp})"
+        name += _schedule_label(sp)
         ach = fl / (t_k * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": name + " (base only)",

@@ -76,13 +76,12 @@ struct FwdWs {
   size_t p_off, xs_off, xst_off, part_off, total;
   int psplits;   // k splits of the adapter down-projection (1: no partials)
   int dsplits;   // k splits of the decode path
-  int gsplits;   // k splits of the fused GEMM (1: no partials)
+  size_t gpart;  // fp32 partials of the fused GEMM's schedule (0: none)
   bool decode;   // few tokens: split-K decode path
 };
 FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdWs L{};
   L.decode = M <= qlora::kDecodeMaxM;
-  L.gsplits = 1;
   if (M == 0) return L;
   if (L.decode) {
     // split-K partials of x . W'^T and x . A^T: [S][M][N + r] fp32
@@ -101,10 +100,10 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
     L.xst_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
     off = round_up(L.xst_off + (size_t)pad32(M) * 2 * r * sizeof(uint16_t), 256);
   }
-  L.gsplits = qlora::gemm_splits(M, N, K);
-  if (L.gsplits > 1) {
+  L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, N, K), M, N);
+  if (L.gpart > 0) {
     L.part_off = off;
-    off = round_up(off + (size_t)L.gsplits * M * N * sizeof(float), 256);
+    off = round_up(off + L.gpart, 256);
   }
   L.total = off;
   return L;
@@ -114,11 +113,10 @@ struct BwdWs {
   size_t pa_off, pg_off, xs_off, gs_off, xst_off, gst_off, cb_off, ca_off, part_off, total;
   int psplits_a, psplits_g;  // k splits of x . A^T and dy . B (1: no partials)
   int tsplits;  // token splits of the dA / dB reductions (1: no partials)
-  int gsplits;  // reduction splits of the dX GEMM (1: no partials)
+  size_t gpart; // fp32 partials of the dX GEMM's schedule (0: none)
 };
 BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs L{};
-  L.gsplits = 1;
   if (M == 0) return L;
   size_t off = 0;
   if (r > 0) {
@@ -144,10 +142,10 @@ BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
       off = round_up(L.ca_off + (size_t)L.tsplits * r * K * sizeof(float), 256);
     }
   }
-  L.gsplits = qlora::dx_gemm_splits(M, K, N);
-  if (L.gsplits > 1) {
+  L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, K, N), M, K);
+  if (L.gpart > 0) {
     L.part_off = off;
-    off = round_up(off + (size_t)L.gsplits * M * K * sizeof(float), 256);
+    off = round_up(off + L.gpart, 256);
   }
   L.total = off;
   return L;
@@ -294,9 +292,9 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
           QLORA_OK)
         return st;
     }
-    float* part = ws.gsplits > 1 ? at<float>(workspace, ws.part_off) : nullptr;
+    float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
     return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->dq_step, x, xs, B, y, part,
-                                             ws.gsplits, M, N, K, r, L, s));
+                                             M, N, K, r, L, s));
   } catch (...) {
     return QLORA_EHIP;
   }
@@ -375,9 +373,9 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
         return st;
     }
     if (dx) {
-      float* part = ws.gsplits > 1 ? at<float>(workspace, ws.part_off) : nullptr;
+      float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
       if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->dq_step, dy, gs, A, dx,
-                                                 part, ws.gsplits, M, N, K, r, L, s))) != QLORA_OK)
+                                                 part, M, N, K, r, L, s))) != QLORA_OK)
         return st;
     }
     return QLORA_OK;

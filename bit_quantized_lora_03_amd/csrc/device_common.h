@@ -140,6 +140,15 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint3
 struct TileCoord {
   int64_t m, n, z;
 };
+// tile rank (0 .. m_tiles * n_tiles - 1) -> (m, n) in the grouped order
+__device__ __forceinline__ void tile_of_rank(int64_t tr, int64_t m_tiles, int64_t n_tiles,
+                                             int group_m, int64_t& m, int64_t& n) {
+  const int64_t span = (int64_t)group_m * n_tiles;
+  const int64_t g = tr / span, w = tr - g * span;
+  const int64_t gm = (m_tiles - g * group_m) < group_m ? (m_tiles - g * group_m) : group_m;
+  m = g * group_m + w % gm;
+  n = w / gm;
+}
 __device__ __forceinline__ TileCoord xcd_tile(int64_t id, int64_t total, int64_t m_tiles,
                                               int64_t n_tiles, int group_m) {
   constexpr int kXcd = 8;
@@ -149,13 +158,48 @@ __device__ __forceinline__ TileCoord xcd_tile(int64_t id, int64_t total, int64_t
   const int64_t tiles = m_tiles * n_tiles;
   TileCoord c;
   c.z = rank / tiles;
-  const int64_t tr = rank - c.z * tiles;
-  const int64_t span = (int64_t)group_m * n_tiles;
-  const int64_t g = tr / span, w = tr - g * span;
-  const int64_t gm = (m_tiles - g * group_m) < group_m ? (m_tiles - g * group_m) : group_m;
-  c.m = g * group_m + w % gm;
-  c.n = w / gm;
+  tile_of_rank(rank - c.z * tiles, m_tiles, n_tiles, group_m, c.m, c.n);
   return c;
+}
+
+// Work of one block of a fused GEMM grid.  Two schedules:
+//  - uniform split (tail_q == 0): every tile's reduction is split over
+//    `splits` blocks (1: none); block -> (tile, split z) by xcd_tile;
+//  - split tail (tail_q > 0): the first `full` blocks each own one whole
+//    tile (tile ranks 0 .. full-1); the last tail_q tiles, which would
+//    otherwise run as a partly filled last round, are split tail_s ways
+//    over the blocks after them, which write tile-local fp32 partials.
+struct BlockWork {
+  int64_t m, n;   // tile coordinates
+  int z, nz;      // split index and count of this block's tile
+  int64_t tail;   // tail tile index, or -1
+};
+__device__ __forceinline__ BlockWork block_work(int64_t id, int64_t total, int64_t m_tiles,
+                                                int64_t n_tiles, int splits, int64_t full,
+                                                int tail_q, int tail_s) {
+  BlockWork w;
+  if (tail_q == 0) {
+    const TileCoord c = xcd_tile(id, total, m_tiles, n_tiles, 4);
+    w.m = c.m;
+    w.n = c.n;
+    w.z = (int)c.z;
+    w.nz = splits;
+    w.tail = -1;
+  } else if (id < full) {
+    const TileCoord c = xcd_tile(id, full, m_tiles, n_tiles, 4);
+    w.m = c.m;
+    w.n = c.n;
+    w.z = 0;
+    w.nz = 1;
+    w.tail = -1;
+  } else {
+    const int64_t e = id - full;
+    w.tail = e % tail_q;
+    w.z = (int)(e / tail_q);
+    w.nz = tail_s;
+    tile_of_rank(full + w.tail, m_tiles, n_tiles, 4, w.m, w.n);
+  }
+  return w;
 }
 
 // Epilogue of the fused GEMMs.  A wave holds a 32 NI (rows: n or k) x 32 NJ

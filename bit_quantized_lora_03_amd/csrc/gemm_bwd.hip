@@ -53,11 +53,14 @@ struct DxParams {
   const uint16_t* dy;
   const uint16_t* gs;
   const uint16_t* A;
-  uint16_t* dx;    // bf16 output (splits == 1)
-  float* part;     // fp32 partials [splits][M][K] (splits > 1)
+  uint16_t* dx;    // bf16 output
+  float* part;     // fp32 partials: [splits][M][K] (uniform split) or
+                   // [tail_s][tail_q][TM][256] (split tail)
   int64_t M, N, K;
   int r;
-  int splits;
+  int splits;      // uniform schedule: reduction splits
+  int64_t full;    // split-tail schedule: whole tiles
+  int tail_q, tail_s;
   Nf4Levels L;
 };
 
@@ -92,9 +95,10 @@ void dx_gemm_kernel(DxParams p) {
   const int wk = wave & 1, wm = wave >> 1;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m_tiles = (M + TM - 1) / TM, k_tiles = (K + TILE - 1) / TILE;
-  const TileCoord tc = xcd_tile(blockIdx.x, (int64_t)gridDim.x, m_tiles, k_tiles, 4);
-  const int64_t k0 = tc.n * TILE;
-  const int64_t m0 = tc.m * TM;
+  const BlockWork bw = block_work(blockIdx.x, (int64_t)gridDim.x, m_tiles, k_tiles, p.splits,
+                                  p.full, p.tail_q, p.tail_s);
+  const int64_t k0 = bw.n * TILE;
+  const int64_t m0 = bw.m * TM;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   f32x16_t acc[4][MS];
@@ -105,9 +109,9 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int z = (int)tc.z;
+  const int z = bw.z, nz = bw.nz;
   const int64_t nst = N / RT;
-  const int64_t st0 = nst * z / p.splits, st1 = nst * (z + 1) / p.splits;
+  const int64_t st0 = nst * z / nz, st1 = nst * (z + 1) / nz;
 
   // this thread decodes reduction row 16 wave + lane % 16 of the slab, k
   // quarter lane / 16 (so the 16 lanes of one LDS store cycle write 16
@@ -301,7 +305,7 @@ void dx_gemm_kernel(DxParams p) {
 
   // --- adapter rows: gs [M, 2r] against [A ; A] (last split only) ---
   const int r = p.r;
-  if (z == p.splits - 1) {
+  if (z == nz - 1) {
     const int ext_tiles = (2 * r + RT - 1) / RT;
     const int64_t m = clamp_row(m0 + (t % TM), M);
     for (int e = 0; e < ext_tiles; ++e) {
@@ -331,45 +335,23 @@ void dx_gemm_kernel(DxParams p) {
   // --- epilogue: D[k][m] -> dx[m][k] (or the split's fp32 partial) ---
   __syncthreads();  // the LDS stages are free from here on
   float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<4>();
-  store_acc_tile<4, MS>(acc, scratch, k0 + 128 * wk, m0 + 32 * MS * wm, K, M, p.splits > 1,
-                     p.splits > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
+  if (bw.tail >= 0)  // tile-local [TM][256] partial
+    store_acc_tile<4, MS>(acc, scratch, 128 * wk, 32 * MS * wm, K - k0, M - m0, true,
+                          p.part + ((int64_t)z * p.tail_q + bw.tail) * TM * TILE, nullptr,
+                          TILE, lane);
+  else
+    store_acc_tile<4, MS>(acc, scratch, k0 + 128 * wk, m0 + 32 * MS * wm, K, M, nz > 1,
+                          nz > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
 }
-
-// Block tile and reduction splits of the dX GEMM (output M x K, reduction
-// N): the same choice as the forward GEMM's -- for each token tile (256 or
-// 128 rows) split the reduction until ~256 blocks fill the chip (at least 4
-// stages per split) and keep the smaller estimate of flops / rate(tile) +
-// fp32 partial traffic.
-GemmConfig dx_gemm_config(int64_t M, int64_t K, int64_t N) {
-  const int64_t nst = N / RT;
-  const int64_t k_t = (K + TILE - 1) / TILE;
-  GemmConfig best{256, 1};
-  double best_t = 1e300;
-  for (int tm : {256, 128}) {
-    const int64_t tiles = ((M + tm - 1) / tm) * k_t;
-    int64_t s = tiles >= 192 ? 1 : 256 / tiles;
-    if (s > nst / 4) s = nst / 4;
-    if (s > 16) s = 16;
-    if (s < 1) s = 1;
-    const double blocks = (double)tiles * s;
-    const double fill = blocks >= 256 ? 1.0 : blocks / 256.0;
-    const double rate = (tm == 256 ? 1.1e15 : 0.8e15) * fill;
-    const double partial = s > 1 ? 2.0 * s * (double)M * K * 4 / 5.0e12 : 0.0;
-    const double est = 2.0 * M * K * N / rate + partial;
-    if (est < best_t) {
-      best_t = est;
-      best = GemmConfig{tm, (int)s};
-    }
-  }
-  return best;
-}
-
-int dx_gemm_splits(int64_t M, int64_t K, int64_t N) { return dx_gemm_config(M, K, N).splits; }
 
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
-                          uint16_t* dx, float* part, int splits, int64_t M, int64_t N, int64_t K,
-                          int r, const Nf4Levels& L, hipStream_t s) {
+                          uint16_t* dx, float* part, int64_t M, int64_t N, int64_t K, int r,
+                          const Nf4Levels& L, hipStream_t s) {
+  // output M x K, reduction N: the forward GEMM's schedule with the roles
+  // of N and K exchanged
+  const GemmConfig cfg = gemm_config(M, K, N);
+  if (gemm_partial_bytes(cfg, M, K) > 0 && part == nullptr) return hipErrorInvalidValue;
   DxParams p;
   p.codes = codes;
   p.qscale = qscale;
@@ -383,18 +365,19 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.N = N;
   p.K = K;
   p.r = r;
-  p.splits = splits;
+  p.splits = cfg.splits;
+  p.full = cfg.full;
+  p.tail_q = cfg.tail_q;
+  p.tail_s = cfg.tail_s;
   p.L = L;
-  const GemmConfig cfg = dx_gemm_config(M, K, N);
-  if (cfg.splits != splits) return hipErrorInvalidValue;  // workspace laid out for another split
-  const int64_t blocks = ((K + TILE - 1) / TILE) * ((M + cfg.tm - 1) / cfg.tm) * splits;
+  const int64_t blocks = gemm_blocks(cfg, M, K);
   if (cfg.tm == 256)
     hipLaunchKernelGGL(dx_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(dx_gemm_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  return launch_splitk_reduce(part, splits, M * K, dx, s);
+  if (e != hipSuccess) return e;
+  return launch_gemm_reduce(cfg, part, M, K, dx, s);
 }
 
 }  // namespace qlora

@@ -58,11 +58,14 @@ struct FwdParams {
   const uint16_t* x;
   const uint16_t* xs;
   const uint16_t* B;
-  uint16_t* y;     // bf16 output (splits == 1)
-  float* part;     // fp32 partials [splits][M][N] (splits > 1)
+  uint16_t* y;     // bf16 output
+  float* part;     // fp32 partials: [splits][M][N] (uniform split) or
+                   // [tail_s][tail_q][TM][256] (split tail)
   int64_t M, N, K;
   int r;
-  int splits;
+  int splits;      // uniform schedule: reduction splits
+  int64_t full;    // split-tail schedule: whole tiles
+  int tail_q, tail_s;
   Nf4Levels L;
 };
 
@@ -111,10 +114,11 @@ void fwd_gemm_kernel(FwdParams p) {
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m_tiles = (M + TM - 1) / TM, n_tiles = (N + TILE_N - 1) / TILE_N;
-  const TileCoord tc = xcd_tile(blockIdx.x, (int64_t)gridDim.x, m_tiles, n_tiles, 4);
-  const int64_t n0 = tc.n * TILE_N;
-  const int64_t m0 = tc.m * TM;
-  const int z = (int)tc.z;
+  const BlockWork bw = block_work(blockIdx.x, (int64_t)gridDim.x, m_tiles, n_tiles, p.splits,
+                                  p.full, p.tail_q, p.tail_s);
+  const int64_t n0 = bw.n * TILE_N;
+  const int64_t m0 = bw.m * TM;
+  const int z = bw.z, nz = bw.nz;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   auto Xs = [&](int stage, int row, int chunk) -> u32x4_t& {
     return lds[stage * XST + rk(row, chunk)];
@@ -127,7 +131,7 @@ void fwd_gemm_kernel(FwdParams p) {
 
   // k tiles of this split
   const int64_t nkt = K / KT;
-  const int64_t kt0 = nkt * z / p.splits, kt1 = nkt * (z + 1) / p.splits;
+  const int64_t kt0 = nkt * z / nz, kt1 = nkt * (z + 1) / nz;
 
   f32x16_t acc[2][JT];
 #pragma unroll
@@ -380,7 +384,7 @@ void fwd_gemm_kernel(FwdParams p) {
 
   // --- adapter columns: xs [M, 2r] against [B | B] (last split only) ---
   const int r = p.r;
-  if (z == p.splits - 1) {
+  if (z == nz - 1) {
     const int ext_tiles = (2 * r + KT - 1) / KT;
     for (int e = 0; e < ext_tiles; ++e) {
       __syncthreads();  // the ring is free
@@ -414,11 +418,16 @@ void fwd_gemm_kernel(FwdParams p) {
     }
   }
 
-  // --- epilogue: D[n][m] -> y[m][n] (or the split's fp32 partial) ---
+  // --- epilogue: D[n][m] -> y[m][n], or the split's fp32 partial ---
   __syncthreads();  // the LDS ring is free from here on
   float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<2>();
-  store_acc_tile<2, JT>(acc, scratch, n0 + 64 * wave, m0, N, M, p.splits > 1,
-                        p.splits > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
+  if (bw.tail >= 0)  // tile-local [TM][256] partial
+    store_acc_tile<2, JT>(acc, scratch, 64 * wave, 0, N - n0, M - m0, true,
+                          p.part + ((int64_t)z * p.tail_q + bw.tail) * TM * TILE_N, nullptr,
+                          TILE_N, lane);
+  else
+    store_acc_tile<2, JT>(acc, scratch, n0 + 64 * wave, m0, N, M, nz > 1,
+                          nz > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
 }
 
 // out[i] = bf16(sum_z part[z][i]), i over M*N (4 per thread), fixed order.
@@ -452,45 +461,125 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, ui
   return hipGetLastError();
 }
 
-// Block tile and k splits for an output of M x N with a reduction of Kred.
-// For each token tile (256 or 128 rows) the k range is split until ~256
-// blocks fill the chip (at least 4 k tiles per split); the choice is the
-// smaller estimate of  flops / rate(tile) + the fp32 partials written and
-// read back.  The rates are the measured sustained throughputs of the two
-// tiles (the 256-row tile amortises each decoded weight over twice the
-// tokens, the 128-row one needs half the splits).
-GemmConfig gemm_config(int64_t M, int64_t N, int64_t Kred) {
+// Tail partials -> bf16 output: out[m0 + mi][n0 + ni] = bf16(sum_z
+// tpart[z][q][mi][ni]) for the tail tiles q, fixed split order; 4 elements
+// per thread.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ tpart,
+                                                          int tm, int64_t full, int tail_q,
+                                                          int tail_s, int64_t M, int64_t Nout,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t m_tiles = (M + tm - 1) / tm, n_tiles = (Nout + TILE_N - 1) / TILE_N;
+  const int64_t per_tile = (int64_t)tm * TILE_N / 4;
+  const int64_t count = per_tile * tail_q;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const int64_t q = i / per_tile, e = i - q * per_tile;
+    const int64_t mi = e / (TILE_N / 4), ni = 4 * (e % (TILE_N / 4));
+    int64_t mt, nt;
+    tile_of_rank(full + q, m_tiles, n_tiles, 4, mt, nt);
+    const int64_t m = mt * tm + mi, n = nt * TILE_N + ni;
+    if (m >= M || n >= Nout) continue;
+    const float* src = tpart + (q * tm + mi) * TILE_N + ni;
+    f32x4_t sum = *reinterpret_cast<const f32x4_t*>(src);
+    for (int z = 1; z < tail_s; ++z) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + (int64_t)z * tail_q * tm * TILE_N);
+      sum[0] += v[0];
+      sum[1] += v[1];
+      sum[2] += v[2];
+      sum[3] += v[3];
+    }
+    u32x2_t o;
+    o[0] = pack_bf16x2(sum[0], sum[1]);
+    o[1] = pack_bf16x2(sum[2], sum[3]);
+    *reinterpret_cast<u32x2_t*>(out + m * Nout + n) = o;
+  }
+}
+
+// Schedule of a fused GEMM: output Mout x Nout, reduction Kred (both GEMMs
+// tile the reduction by 64 and the non-token output dimension by 256).  For
+// each token tile (256 or 128 rows) the estimate is
+//   rounds * (time of one tile on one CU) + fp32 partial traffic,
+// where a round is 256 concurrent blocks (one per CU).  Few tiles: split
+// every tile's reduction until ~256 blocks run.  Otherwise the tiles run
+// whole, except that a last round filled less than half is split: its
+// tail_q tiles are split 256 / tail_q ways (at most 8, at least 4 k tiles
+// each), so it takes a fraction of a round.  The rates are the measured
+// sustained throughputs of the two tiles.
+GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred) {
+  constexpr int kSlots = 256;  // concurrent blocks: one per CU
   const int64_t nkt = Kred / KT;
-  const int64_t n_t = (N + TILE_N - 1) / TILE_N;
-  GemmConfig best{256, 1};
+  const int64_t n_t = (Nout + TILE_N - 1) / TILE_N;
+  GemmConfig best{256, 1, 0, 0, 1};
   double best_t = 1e300;
   for (int tm : {256, 128}) {
     const int64_t tiles = ((M + tm - 1) / tm) * n_t;
-    int64_t s = tiles >= 192 ? 1 : 256 / tiles;
-    if (s > nkt / 4) s = nkt / 4;
-    if (s > 16) s = 16;
-    if (s < 1) s = 1;
-    const double blocks = (double)tiles * s;
-    const double fill = blocks >= 256 ? 1.0 : blocks / 256.0;
-    const double rate = (tm == 256 ? 1.1e15 : 0.8e15) * fill;  // flop/s
-    const double partial = s > 1 ? 2.0 * s * (double)M * N * 4 / 5.0e12 : 0.0;
-    const double est = 2.0 * M * N * Kred / rate + partial;
+    const double rate = tm == 256 ? 1.1e15 : 0.8e15;  // flop/s, whole chip
+    const double t_tile = 2.0 * tm * TILE_N * (double)Kred / (rate / kSlots);
+    GemmConfig c{tm, 1, 0, 0, 1};
+    double est;
+    if (tiles < 192) {
+      int64_t sp = 256 / tiles;
+      if (sp > nkt / 4) sp = nkt / 4;
+      if (sp > 16) sp = 16;
+      if (sp < 1) sp = 1;
+      c.splits = (int)sp;
+      const double blocks = (double)tiles * sp;
+      const double fill = blocks >= kSlots ? 1.0 : blocks / kSlots;
+      est = 2.0 * M * Nout * (double)Kred / (rate * fill);
+      if (sp > 1) est += 2.0 * sp * (double)M * Nout * 4 / 5.0e12;
+    } else {
+      const int64_t rounds = tiles / kSlots, q = tiles % kSlots;
+      int64_t ts = q > 0 ? kSlots / q : 1;
+      if (ts > nkt / 4) ts = nkt / 4;
+      if (ts > 8) ts = 8;
+      if (q > 0 && ts >= 2) {
+        c.full = tiles - q;
+        c.tail_q = (int)q;
+        c.tail_s = (int)ts;
+        est = (rounds + 1.0 / ts) * t_tile + 2.0 * ts * q * tm * TILE_N * 4 / 5.0e12;
+      } else {
+        est = (rounds + (q > 0 ? 1 : 0)) * t_tile;
+      }
+    }
     if (est < best_t) {
       best_t = est;
-      best = GemmConfig{tm, (int)s};
+      best = c;
     }
   }
   return best;
 }
 
-int gemm_splits(int64_t M, int64_t N, int64_t Kred) { return gemm_config(M, N, Kred).splits; }
+int64_t gemm_blocks(const GemmConfig& c, int64_t M, int64_t Nout) {
+  if (c.tail_q > 0) return c.full + (int64_t)c.tail_q * c.tail_s;
+  return ((Nout + TILE_N - 1) / TILE_N) * ((M + c.tm - 1) / c.tm) * c.splits;
+}
+
+size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout) {
+  if (c.tail_q > 0) return (size_t)c.tail_s * c.tail_q * c.tm * TILE_N * sizeof(float);
+  if (c.splits > 1) return (size_t)c.splits * M * Nout * sizeof(float);
+  return 0;
+}
+
+hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M, int64_t Nout,
+                              uint16_t* out, hipStream_t s) {
+  if (c.tail_q > 0) {
+    const int64_t count = (int64_t)c.tail_q * c.tm * TILE_N / 4;
+    int64_t g = (count + 255) / 256;
+    if (g > 8192) g = 8192;
+    hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)g), dim3(256), 0, s, part, c.tm,
+                       c.full, c.tail_q, c.tail_s, M, Nout, out);
+    return hipGetLastError();
+  }
+  if (c.splits > 1) return launch_splitk_reduce(part, c.splits, M * Nout, out, s);
+  return hipSuccess;
+}
 
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                            const uint16_t* x, const uint16_t* xs, const uint16_t* B,
-                           uint16_t* y, float* part, int splits, int64_t M, int64_t N, int64_t K,
-                           int r, const Nf4Levels& L, hipStream_t s) {
+                           uint16_t* y, float* part, int64_t M, int64_t N, int64_t K, int r,
+                           const Nf4Levels& L, hipStream_t s) {
   const GemmConfig cfg = gemm_config(M, N, K);
-  if (cfg.splits != splits) return hipErrorInvalidValue;  // workspace laid out for another split
+  if (gemm_partial_bytes(cfg, M, N) > 0 && part == nullptr) return hipErrorInvalidValue;
   FwdParams p;
   p.codes = codes;
   p.qscale = qscale;
@@ -504,16 +593,19 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.N = N;
   p.K = K;
   p.r = r;
-  p.splits = splits;
+  p.splits = cfg.splits;
+  p.full = cfg.full;
+  p.tail_q = cfg.tail_q;
+  p.tail_s = cfg.tail_s;
   p.L = L;
-  const int64_t blocks = ((N + TILE_N - 1) / TILE_N) * ((M + cfg.tm - 1) / cfg.tm) * splits;
+  const int64_t blocks = gemm_blocks(cfg, M, N);
   if (cfg.tm == 256)
     hipLaunchKernelGGL(fwd_gemm_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(fwd_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  return launch_splitk_reduce(part, splits, M * N, y, s);
+  if (e != hipSuccess) return e;
+  return launch_gemm_reduce(cfg, part, M, N, y, s);
 }
 
 }  // namespace qlora

@@ -59,21 +59,33 @@ int lora_grad_splits(int64_t M, int64_t ldg0, int64_t ldg1);
 hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
                             int accumulate, int splits, hipStream_t s);
 
-// gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T.  With splits > 1 the
-// k range is split over blocks writing fp32 partials part[splits][M][N],
-// reduced to bf16 y by a second kernel.
+// gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T.
+// Schedule of a fused GEMM with an Mout x Nout output (Nout in tiles of 256)
+// and a reduction of Kred (in tiles of 64): either every tile's reduction is
+// split `splits` ways (fp32 partials part[splits][M][Nout], reduced by
+// splitk_reduce), or -- when the tiles fill at least one round of the chip
+// -- the `full` first tiles run whole and the last tail_q tiles are split
+// tail_s ways into tile-local fp32 partials tpart[tail_s][tail_q][tm][256],
+// reduced by tail_reduce.
 struct GemmConfig {
-  int tm;      // token rows of the block tile (256 or 128)
-  int splits;  // k splits (1: no partials)
+  int tm;        // token rows of the block tile (256 or 128)
+  int splits;    // uniform reduction splits (1: none)
+  int64_t full;  // tail schedule: tiles run whole
+  int tail_q;    // tail schedule: split tiles (0: uniform schedule)
+  int tail_s;    // tail schedule: splits per tail tile
 };
-GemmConfig gemm_config(int64_t M, int64_t N, int64_t Kred);
-int gemm_splits(int64_t M, int64_t N, int64_t Kred);
+GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred);
+int64_t gemm_blocks(const GemmConfig& c, int64_t M, int64_t Nout);
+size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout);
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                            const uint16_t* x, const uint16_t* xs, const uint16_t* B,
-                           uint16_t* y, float* part, int splits, int64_t M, int64_t N, int64_t K,
-                           int r, const Nf4Levels& L, hipStream_t s);
+                           uint16_t* y, float* part, int64_t M, int64_t N, int64_t K, int r,
+                           const Nf4Levels& L, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, uint16_t* out,
                                 hipStream_t s);
+// the reduction after a fused GEMM's main kernel, if its schedule has one
+hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M, int64_t Nout,
+                              uint16_t* out, hipStream_t s);
 
 // gemm_decode.hip -- forward for M <= 32: split-K partials
 // part[S][M][N + r] (columns N.. hold x . A^T), then
@@ -85,13 +97,11 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
                              float scale, float* part, int splits, uint16_t* y, int64_t M,
                              int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s);
 
-// gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]; splits > 1 as in the
-// forward GEMM (partials [splits][M][K])
-GemmConfig dx_gemm_config(int64_t M, int64_t K, int64_t N);
-int dx_gemm_splits(int64_t M, int64_t K, int64_t N);
+// gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]; scheduled by
+// gemm_config(M, K, N) (output M x K, reduction N)
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
-                          uint16_t* dx, float* part, int splits, int64_t M, int64_t N, int64_t K,
-                          int r, const Nf4Levels& L, hipStream_t s);
+                          uint16_t* dx, float* part, int64_t M, int64_t N, int64_t K, int r,
+                          const Nf4Levels& L, hipStream_t s);
 
 }  // namespace qlora

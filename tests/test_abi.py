@@ -57,9 +57,12 @@ def test_status_strings():
 
 def test_workspace_sizes():
     ws = q.workspace_bytes
-    # many output tiles, no adapter: one kernel, no scratch
-    assert ws(0, 4096, 22016, 8192, 0) == 0
+    # output tiles that fill whole rounds of the chip, no adapter: one
+    # kernel, no scratch (dX of 4096 x 8192: 16 x 32 = 512 tiles of 256 x 256)
     assert ws(1, 4096, 22016, 8192, 0) == 0
+    # 16 x 86 = 1376 forward tiles: 5 full rounds of 256, then 96 tail tiles
+    # split 2 ways into tile-local fp32 partials
+    assert ws(0, 4096, 22016, 8192, 0) == 2 * 96 * 256 * 256 * 4
     # few output tiles: fp32 split-K partials even without an adapter
     assert ws(0, 512, 4096, 4096, 0) >= 512 * 4096 * 4 * 2
     f = ws(0, 512, 4096, 4096, 16)

@@ -71,3 +71,11 @@ def test_decode_8192(cuda, M):
 
 def test_layer_65b_m4096(cuda):
     _check_layer(workloads.layer_65b())
+
+
+def test_split_tail_schedules_128_token_tiles(cuda):
+    """3200 x 2816 x 3072: the forward runs 256 whole 256x128 tiles plus 19
+    tail tiles split 8 ways, dX 256 whole tiles plus 44 tail tiles split 5
+    ways (the last sampled row, M - 1, lies in a tail tile of both)."""
+    _check_layer(workloads.layer(3200, 2816, 3072, 16, 32.0, seed=21, name="tail128",
+                                 outlier_frac=0.001))
