@@ -84,8 +84,9 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   L.decode = M <= qlora::kDecodeMaxM;
   if (M == 0) return L;
   if (L.decode) {
-    // split-K partials of x . W'^T and x . A^T: [S][M][N + r] fp32
-    L.dsplits = qlora::decode_splits(M, N, K);
+    // with an adapter: fp32 sums of x . W'^T and k-split partials of
+    // x . A^T, [S][M][N + r]; without one the decode path needs none
+    L.dsplits = qlora::decode_splits(M, N, K, r);
     L.part_off = 0;
     L.total = round_up((size_t)L.dsplits * M * (N + r) * sizeof(float), 256);
     return L;
@@ -278,9 +279,10 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
     const Nf4Levels L = levels_arg();
     const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
     if (ws.decode) {
-      return hip_status(qlora::launch_decode_fwd(w->codes, w->qscale, w->dq_step, x, A, B, r,
-                                                 scale, at<float>(workspace, ws.part_off),
-                                                 ws.dsplits, y, M, N, K, L, s));
+      return hip_status(qlora::launch_decode_fwd(
+          w->codes, w->qscale, w->dq_step, x, A, B, r, scale,
+          ws.total > 0 ? at<float>(workspace, ws.part_off) : nullptr, ws.dsplits, y, M, N, K, L,
+          s));
     }
     uint16_t* xs = nullptr;
     if (r > 0) {

@@ -9,34 +9,37 @@
 //
 //  * a 32x32x16 MFMA takes 32 weight rows (n) as its A operand and the
 //    (zero-padded) tokens as its 32 B columns;
-//  * lane (row l%32, half l/32) owns one whole 64-weight block per 128-wide
-//    k span, so it builds that block's 16-entry bf16 table once and decodes
-//    its 64 codes into the A operands of 8 consecutive MFMAs.  The reduction
-//    order over k is permuted consistently for A and B (MFMA j of a span
-//    sums k = base + 64 g + 8 j + e over g = 0, 1 and e = 0..7);
+//  * a block owns 32 weight rows over the whole reduction, so no partial
+//    sums leave the chip: the row's NF4 blocks are dealt to 16 slots (8
+//    waves x the two lane halves), lane (row l%32, half l/32) of wave w
+//    taking slot 2 w + l/32 of each chunk of 16 blocks.  The codes come in
+//    by DMA, two whole row pieces per instruction, into an LDS ring four
+//    chunks deep, so the weight is streamed in full cache lines.  For each block the lane builds the block's 16-entry bf16
+//    table once and decodes its 64 codes into the A operands of 8
+//    consecutive MFMAs; the reduction order over k is permuted consistently
+//    for A and B (MFMA j of a block pair sums k = 64 b + 8 j + e, e = 0..7,
+//    over the two lane halves' blocks b);
 //  * the table lives in LDS, entry c of lane l of wave w at byte
 //    4096 w + 256 c + 4 l, so a lookup is one v_perm (which places the
 //    code, tagged with the wave, next to the lane's byte offset) and one
 //    2-byte LDS read, and the 64 lanes of a read always hit 64 distinct
-//    banks.  That is about two thirds of the vector work of resolving codes
-//    with byte permutes in registers;
-//  * x is small and stays in L2: each lane reads its token's 16-byte
-//    operand pieces directly, two spans ahead;
-//  * a block is 8 waves on 32 rows; each wave takes a contiguous eighth of
-//    the block's k range and keeps the codes of the next 2 spans in flight
-//    while it decodes the current 2.
+//    banks -- about two thirds of the vector work of resolving codes with
+//    byte permutes in registers;
+//  * x is small and stays in L2: each token lane reads its 16-byte operand
+//    pieces directly, one chunk ahead;
+//  * the 8 waves' partial tiles are added in LDS in wave order.
 //
 // The adapter's down projection x . A^T rides along: rows of A (bf16, used
-// as they are) form extra 32-row tiles whose partial sums land in columns
-// N .. N+r-1 of the partial output.  Those tiles come first in the grid and
-// are split finer over k, so they finish early instead of trailing.
+// as they are) form extra 32-row tiles, split over k into short pieces
+// (their partial sums land in columns N .. N+r-1 of part[z]).  Those tiles
+// come last in the grid and fill in as the weight tiles finish.  With an adapter, the weight tiles write their fp32 sums to part[0]
+// and decode_reduce forms the fp32 adapter term (alpha/r) . (x . A^T) . B^T
+// and rounds y to bf16 once; without one, the weight tiles round and store
+// y themselves.
 //
-// Grid: 1-D over (A tiles x SA splits) then (weight tiles x SW splits),
-// ordered so that consecutive ranks share an XCD (workgroups are dealt to
-// the 8 XCDs round-robin): the blocks of neighbouring row tiles run behind
-// one L2.  Partial sums go to part[S][M][N + r] (S = max(SW, SA));
-// decode_reduce adds them in a fixed order, forms the fp32 adapter term
-// (alpha/r) . (x . A^T) . B^T and rounds y to bf16 once.
+// Grid: 1-D over the weight tiles, then (A tiles x SA splits), ordered so
+// that consecutive ranks share an XCD (workgroups are dealt to the 8 XCDs
+// round-robin).
 
 #include <type_traits>
 
@@ -48,9 +51,18 @@ namespace qlora {
 namespace {
 
 constexpr int WAVES = 8;    // waves per block
-constexpr int SPAN = 128;   // k per span (two 64-weight blocks per row)
-constexpr int BATCH = 2;    // spans whose codes are requested together
+constexpr int SLOTS = 2 * WAVES;  // NF4-block slots per weight row
+constexpr int SPAN = 128;   // k per span of the adapter tiles
 constexpr int kTabBytes = WAVES * 16 * 64 * 4;  // per-lane NF4 tables, 32 KiB
+constexpr int NSTAGE = 4;   // code chunks in the LDS ring
+constexpr int kStageU4 = 32 * 512 / 16;  // one chunk: 32 rows x 512 bytes
+constexpr int kLdsBytes = kTabBytes + NSTAGE * kStageU4 * 16;
+
+// s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS
+// operations of this wave are outstanding (expcnt left free).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
 
 struct DecodeParams {
   const uint8_t* codes;
@@ -61,19 +73,19 @@ struct DecodeParams {
   float* part;
   int64_t M, N, K;
   int r;
-  int sw, sa;          // k splits of the weight tiles and of the A tiles
-  int64_t a_blocks;    // A tiles x sa (they come first)
-  int64_t blocks;      // a_blocks + weight tiles x sw
+  uint16_t* y;         // bf16 output when r == 0 (no adapter term to add)
+  int sa;              // k splits of the A tiles
+  int64_t w_blocks;    // weight tiles (they come first)
+  int64_t blocks;      // w_blocks + A tiles x sa
   Nf4Levels L;
 };
 
-// codes of one span plus the raw scale byte and step: s' is formed only when
-// the span is decoded, so that issuing the loads never waits for them
-struct Span {
+// codes of one NF4 block plus the raw scale byte and step: s' is formed
+// only when the block is decoded, so that issuing the loads never waits
+struct Blk {
   u32x4_t c[2];
   uint32_t q;
   float st;
-  bool ok;  // false: past the range, decodes to zeros
 };
 
 }  // namespace
@@ -81,16 +93,14 @@ struct Span {
 __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p) {
   // the tables are the kernel's only LDS (at offset 0, so a lookup address
   // needs no base added); after the main loop the space holds the reduction
-  __shared__ __align__(16) uint8_t lds[kTabBytes];
+  __shared__ __align__(16) uint8_t lds[kLdsBytes];
 
   const int64_t id = blockIdx.x, per_xcd = (int64_t)gridDim.x / 8;
   const int64_t rank = (id % 8) * per_xcd + id / 8;  // grid padded to a multiple of 8
   if (rank >= p.blocks) return;
-  const bool a_tile = rank < p.a_blocks;
-  const int splits = a_tile ? p.sa : p.sw;
-  const int64_t lr_rank = a_tile ? rank : rank - p.a_blocks;
-  const int64_t tile = lr_rank / splits;
-  const int z = (int)(lr_rank % splits);
+  const bool a_tile = rank >= p.w_blocks;
+  const int64_t tile = a_tile ? (rank - p.w_blocks) / p.sa : rank;
+  const int z = a_tile ? (int)((rank - p.w_blocks) % p.sa) : 0;
 
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
@@ -98,13 +108,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
   const int64_t n0 = tile * 32;
   const int64_t nrows = a_tile ? p.r : N;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-
-  // this wave's spans: the block's share of k, cut in contiguous eighths
-  const int64_t spans_total = (K + SPAN - 1) / SPAN;
-  const int64_t bs0 = spans_total * z / splits, bs1 = spans_total * (z + 1) / splits;
-  const int64_t per_w = (bs1 - bs0 + WAVES - 1) / WAVES;
-  const int64_t s_begin = bs0 + wave * per_w < bs1 ? bs0 + wave * per_w : bs1;
-  const int64_t s_end = s_begin + per_w < bs1 ? s_begin + per_w : bs1;
   const int64_t n = n0 + lr;
   const bool row_ok = n < nrows;
   const bool tok_ok = lr < M;
@@ -114,44 +117,68 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 
-  // x operands.  Only the M token lanes load (the other lanes' columns of
-  // the product are never stored, whatever their registers hold); spans past
-  // the range read span 0, whose weights decode to zero.  The values are used
-  // as loaded, so nothing waits for them before the MFMA that needs them.
-  auto load_x = [&](int64_t sp, u32x4_t (&xb)[8]) {
-    const int64_t kb = sp * SPAN + 64 * lg;
-    const bool ok = sp < s_end && kb < K;
-    const uint16_t* xp = xrow + (ok ? kb : 0);
-    if (tok_ok) {
+  // x operands of the 64 k starting at kb (8 pieces of 16 bytes).  Lanes
+  // past the M tokens read token 0's row (their columns of the product are
+  // never stored): the loads are unconditional, so no branch makes the
+  // compiler's wait analysis assume they might be missing.
+  auto load_x = [&](int64_t kb, u32x4_t (&xb)[8]) {
+    const uint16_t* xp = xrow + kb;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) xb[j] = *reinterpret_cast<const u32x4_t*>(xp + 8 * j);
-    }
+    for (int j = 0; j < 8; ++j) xb[j] = *reinterpret_cast<const u32x4_t*>(xp + 8 * j);
   };
 
   if (!a_tile) {
-    // Loads are unconditional (a span out of range reads the row's first
-    // block and is decoded with a zero scale), so no branch separates them
-    // and they all stay in flight together.
-    const uint8_t* row_codes = p.codes + (((row_ok ? n : 0) * K) >> 1);
+    // The row's NF4 blocks go in chunks of 16 (1024 k); within a chunk lane
+    // (row l%32, half l/32) of wave w decodes block 2 w + l/32.  The codes
+    // reach LDS by DMA (buffer loads that write LDS directly) in a ring of
+    // NSTAGE chunks: each instruction moves 1 KiB, two whole 512-byte row
+    // pieces, so the weight stream is read in full cache lines (reading 16
+    // bytes per row per lane would touch 64 lines per instruction).  In a
+    // stage, row r's 16-byte piece c sits at r * 512 + 16 (c ^ (r % 16)), so
+    // the 16 rows one LDS read cycle serves hit 16 distinct bank groups.
+    // Scale bytes, steps and x pieces are per-lane loads into registers.
+    const int64_t nblk = K / 64;
+    const int64_t nch = (nblk + 15) / 16;
+    const int slot = 2 * wave + lg;
     const int64_t row_blk = ((row_ok ? n : 0) * K) >> 6;
-    auto load_span = [&](int64_t sp, Span& S) {
-      const int64_t kb = sp * SPAN + 64 * lg;
-      const bool ok = row_ok && sp < s_end && kb < K;
-      const int64_t kk = ok ? kb : 0;
-      const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(row_codes + (kk >> 1));
-      S.c[0] = cp[0];
-      S.c[1] = cp[1];
-      const int64_t b = row_blk + (kk >> 6);
-      S.q = p.qscale[b];
-      S.st = p.step[b >> 8];
-      S.ok = ok;
+    const __amdgpu_buffer_rsrc_t cres = make_rsrc(p.codes, (uint32_t)((N * K) >> 1));
+    uint32_t cvoff[2];  // instruction h fills rows 4 wave + 2 h + lane / 32
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 4 * wave + 2 * h + (lane >> 5);
+      const int c = (lane & 31) ^ (r & 15);
+      cvoff[h] = (uint32_t)((n0 + r) * (K >> 1) + 16 * c);
+    }
+    auto dma_codes = [&](u32x4_t* stage, int64_t ch) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            cres, (__attribute__((address_space(3))) void*)(stage + 64 * (2 * wave + h)), 16,
+            cvoff[h] + (uint32_t)(ch * 512), 0, 0, 0);
     };
+    struct Scale {
+      uint32_t q;
+      float st;
+    };
+    auto blk_of = [&](int64_t ch) { return 16 * ch + slot; };
+    auto load_scale = [&](int64_t ch, Scale& S) {
+      const int64_t b = blk_of(ch) < nblk ? blk_of(ch) : 0;
+      S.q = p.qscale[row_blk + b];
+      S.st = p.step[(row_blk + b) >> 8];
+    };
+    auto xk = [&](int64_t ch) { return (blk_of(ch) < nblk ? blk_of(ch) : 0) * 64; };
+
     uint16_t* tab_w = reinterpret_cast<uint16_t*>(lds) + wave * 2048 + lane * 2;
-    const uint32_t wtag = (uint32_t)wave * 0x10101010u;  // wave in bits 4..6 of each code byte
+    const uint32_t wtag = (uint32_t)wave * 0x10101010u;  // wave in bits 4..7 of each code byte
     const uint32_t lane4 = (uint32_t)lane * 4u;
-    auto decode_span = [&](const Span& S, const u32x4_t (&xb)[8]) {
+    const int rsw = lr & 15;
+    auto decode_chunk = [&](const u32x4_t* stage, int64_t ch, const Scale& S,
+                            const u32x4_t (&xb)[8]) {
+      const bool ok = row_ok && blk_of(ch) < nblk;
+      const u32x4_t c0 = stage[lr * 32 + ((2 * slot) ^ rsw)];
+      const u32x4_t c1 = stage[lr * 32 + ((2 * slot + 1) ^ rsw)];
       // this lane's block table: entry c = bf16_rne(fp32(L[c] * s'))
-      const float sc = S.ok ? nf4_block_scale(S.q, S.st) : 0.0f;
+      const float sc = ok ? nf4_block_scale(S.q, S.st) : 0.0f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const uint32_t pk = pack_bf16x2(p.L.v[2 * q] * sc, p.L.v[2 * q + 1] * sc);
@@ -160,7 +187,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t v = S.c[j >> 2][j & 3];
+        const uint32_t v = (j < 4 ? c0 : c1)[j & 3];
         const uint32_t ev = (v & 0x0F0F0F0Fu) | wtag;
         const uint32_t od = ((v >> 4) & 0x0F0F0F0Fu) | wtag;
         const uint32_t q4[2] = {perm(od, ev, 0x05010400u), perm(od, ev, 0x07030602u)};
@@ -178,50 +205,80 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       }
     };
 
-    // codes: batches of 2 spans in two register sets (batch b + 1 in flight
-    // while batch b decodes); x: two spans ahead in four register sets
-    // (span u of a batch of parity q uses set 2 q + u)
-    Span C0[BATCH], C1[BATCH];
-    u32x4_t X[2 * BATCH][8];
+    // Issue order per chunk iteration: DMA of chunk + 3, its scales, x of
+    // chunk + 1 (a virtual iteration -1 issues DMA 2 and x 0 in the
+    // prologue).  The DMA of chunk + 1 is then complete once at most 26
+    // loads are outstanding at the end of an iteration (fewer than the 34
+    // issued after it in steady state; exactly 26 after the first one).
+    u32x4_t* const ring = reinterpret_cast<u32x4_t*>(lds + kTabBytes);
+    Scale Sc[NSTAGE];
+    u32x4_t X[2][8];
 #pragma unroll
-    for (int u = 0; u < 2 * BATCH; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 8; ++j) X[u][j] = zero;
-    const int64_t nb = (s_end - s_begin + BATCH - 1) / BATCH;
-    auto load_batch = [&](int64_t b, Span (&C)[BATCH]) {
+    const int64_t lastc = nch - 1;
+    auto cl = [&](int64_t c) { return c < lastc ? c : lastc; };
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) load_span(s_begin + b * BATCH + u, C[u]);
-    };
-    auto run_batch = [&](int64_t b, const Span (&C)[BATCH], auto parity) {
-      constexpr int q = decltype(parity)::value;
-      const int64_t sp = s_begin + b * BATCH;
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        load_x(sp + u + 2, X[(2 * q + u + 2) % 4]);
-        if (sp + u < s_end) decode_span(C[u], X[2 * q + u]);
-      }
-    };
-    if (nb > 0) {
-      load_batch(0, C0);
-      load_x(s_begin, X[0]);
-      load_x(s_begin + 1, X[1]);
+    for (int c = 0; c < NSTAGE - 1; ++c) {
+      dma_codes(ring + c * kStageU4, cl(c));
+      load_scale(cl(c), Sc[c]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    for (int64_t b = 0; b < nb; b += 2) {
-      if (b + 1 < nb) load_batch(b + 1, C1);
-      run_batch(b, C0, std::integral_constant<int, 0>());
-      if (b + 1 < nb) {
-        if (b + 2 < nb) load_batch(b + 2, C0);
-        run_batch(b + 1, C1, std::integral_constant<int, 1>());
+    load_x(xk(0), X[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(18, 0));
+    __builtin_amdgcn_s_barrier();
+
+    auto iteration = [&](int64_t ch, auto phase, const u32x4_t* __restrict__ rd,
+                         u32x4_t* __restrict__ fill) {
+      constexpr int ph = decltype(phase)::value;
+      dma_codes(fill, cl(ch + 3));
+      load_scale(cl(ch + 3), Sc[(ph + 3) % NSTAGE]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(xk(cl(ch + 1)), X[(ph + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_chunk(rd, ch, Sc[ph], X[ph & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(26, 0));
+      __builtin_amdgcn_s_barrier();
+    };
+    u32x4_t* const R0 = ring;
+    u32x4_t* const R1 = ring + kStageU4;
+    u32x4_t* const R2 = ring + 2 * kStageU4;
+    u32x4_t* const R3 = ring + 3 * kStageU4;
+    int64_t ch = 0;
+    for (; ch + 4 <= nch; ch += 4) {
+      iteration(ch, std::integral_constant<int, 0>(), R0, R3);
+      iteration(ch + 1, std::integral_constant<int, 1>(), R1, R0);
+      iteration(ch + 2, std::integral_constant<int, 2>(), R2, R1);
+      iteration(ch + 3, std::integral_constant<int, 3>(), R3, R2);
+    }
+    if (ch < nch) {
+      iteration(ch, std::integral_constant<int, 0>(), R0, R3);
+      if (ch + 1 < nch) {
+        iteration(ch + 1, std::integral_constant<int, 1>(), R1, R0);
+        if (ch + 2 < nch) iteration(ch + 2, std::integral_constant<int, 2>(), R2, R1);
       }
     }
+    // the clamped prefetches past the end are still writing LDS
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   } else {
-    // rows of A: bf16 operands as stored
+    // rows of A: bf16 operands as stored; this split's spans, cut in
+    // contiguous pieces over the waves (k = span base + 64 lg + 8 j + e)
+    const int64_t spans_total = (K + SPAN - 1) / SPAN;
+    const int64_t bs0 = spans_total * z / p.sa, bs1 = spans_total * (z + 1) / p.sa;
+    const int64_t per_w = (bs1 - bs0 + WAVES - 1) / WAVES;
+    const int64_t s_begin = bs0 + wave * per_w < bs1 ? bs0 + wave * per_w : bs1;
+    const int64_t s_end = s_begin + per_w < bs1 ? s_begin + per_w : bs1;
     const uint16_t* arow = p.A + (row_ok ? n : 0) * K;
     for (int64_t sp = s_begin; sp < s_end; ++sp) {
       const int64_t kb = sp * SPAN + 64 * lg;
       const bool ok = row_ok && kb < K;
       u32x4_t xb[8], av[8];
-      load_x(sp, xb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xb[j] = zero;
+      load_x(kb < K ? kb : 0, xb);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         av[j] = ok ? *reinterpret_cast<const u32x4_t*>(arow + kb + 8 * j) : zero;
@@ -230,9 +287,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     }
   }
 
-  // ---- sum the 8 waves' tiles in LDS (wave order), write the partial ----
+  // ---- sum the waves' tiles in LDS (wave order), write the result ----
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);  // [8][32 rows][M], M <= 32
+  float* red = reinterpret_cast<float*>(lds);  // [WAVES][32 rows][M], M <= 32
   const int mcols = (int)M;
   // D[n][m]: lane holds token m = lr, rows n = 8(v/4) + 4 lg + v%4
   if (tok_ok) {
@@ -249,7 +306,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       float s = 0.0f;
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) s += red[(w * 32 + row) * mcols + m];
-      p.part[((int64_t)z * M + m) * ldp + col0 + row] = s;
+      if (p.y)  // no adapter: this is y
+        p.y[(int64_t)m * N + n0 + row] = __builtin_bit_cast(uint16_t, (__bf16)s);
+      else
+        p.part[((int64_t)z * M + m) * ldp + col0 + row] = s;
     }
   }
 }
@@ -323,40 +383,21 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
 
 namespace {
 
-// k splits of the weight tiles: the fewest that keep the chip's 256 CUs
-// (one 8-wave block each) evenly busy -- rounds of blocks times work per
-// block, plus a small cost per split -- with at least one span per wave.
-int weight_splits(int64_t N, int64_t K) {
-  const int64_t tiles = (N + 31) / 32;
-  const int64_t spans = (K + SPAN - 1) / SPAN;
-  int best = 1;
-  double best_cost = 1e30;
-  for (int s = 1; s <= 8; ++s) {
-    if (s > 1 && spans / s < WAVES) break;
-    const int64_t rounds = (tiles * s + 255) / 256;
-    const double cost = (double)rounds / s * (1.0 + 0.03 * s);
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = s;
-    }
-  }
-  return best;
-}
-
-// the A tiles are few and carry 4x the bytes per row: split them finer
+// k splits of the adapter's A tiles, which run after the weight tiles: short
+// pieces (about 512 k each, at most 16) that fill in as CUs free up
 int a_splits(int64_t K) {
-  const int64_t spans = (K + SPAN - 1) / SPAN;
-  int s = 8;
-  while (s > 1 && spans / s < WAVES) --s;
-  return s;
+  int64_t s = K / 512;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return (int)s;
 }
 
 }  // namespace
 
-int decode_splits(int64_t M, int64_t N, int64_t K) {
+int decode_splits(int64_t M, int64_t N, int64_t K, int r) {
   (void)M;
-  const int sw = weight_splits(N, K), sa = a_splits(K);
-  return sw > sa ? sw : sa;
+  (void)N;
+  return r > 0 ? a_splits(K) : 0;
 }
 
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const float* step,
@@ -374,18 +415,18 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
   p.N = N;
   p.K = K;
   p.r = r;
-  p.sw = weight_splits(N, K);
-  p.sa = a_splits(K);
-  if (p.sw > splits || p.sa > splits) return hipErrorInvalidValue;  // workspace sized for fewer
-  p.a_blocks = (int64_t)((r + 31) / 32) * p.sa;
-  p.blocks = p.a_blocks + ((N + 31) / 32) * p.sw;
+  p.sa = r > 0 ? a_splits(K) : 1;
+  if (r > 0 && (p.sa > splits || part == nullptr)) return hipErrorInvalidValue;
+  p.y = r > 0 ? nullptr : y;
+  p.w_blocks = (N + 31) / 32;
+  p.blocks = p.w_blocks + (r > 0 ? (int64_t)((r + 31) / 32) * p.sa : 0);
   p.L = L;
   const int64_t grid = (p.blocks + 7) / 8 * 8;
   hipLaunchKernelGGL(decode_main_kernel, dim3((unsigned)grid), dim3(WAVES * 64), 0, s, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || r == 0) return e;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s,
-                     part, p.sw, p.sa, B, r, scale, y, M, N);
+                     part, 1, p.sa, B, r, scale, y, M, N);
   return hipGetLastError();
 }
 

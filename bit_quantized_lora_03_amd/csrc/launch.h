@@ -87,11 +87,13 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, ui
 hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M, int64_t Nout,
                               uint16_t* out, hipStream_t s);
 
-// gemm_decode.hip -- forward for M <= 32: split-K partials
-// part[S][M][N + r] (columns N.. hold x . A^T), then
-// y = bf16(sum part + scale . xa . B^T)
+// gemm_decode.hip -- forward for M <= 32.  Without an adapter one kernel
+// writes y.  With one, the weight tiles write fp32 sums to part[0][M][N + r]
+// and the k-split A tiles x . A^T to part[z][m][N + j], then
+// y = bf16(part[0] + scale . (sum_z xa) . B^T); decode_splits is the number
+// of partial planes (0: none).
 constexpr int kDecodeMaxM = 32;
-int decode_splits(int64_t M, int64_t N, int64_t K);
+int decode_splits(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const float* step,
                              const uint16_t* x, const uint16_t* A, const uint16_t* B, int r,
                              float scale, float* part, int splits, uint16_t* y, int64_t M,

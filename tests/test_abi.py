@@ -72,6 +72,8 @@ def test_workspace_sizes():
     # few tokens: the decode path keeps k-split partials of x.W'^T and x.A^T
     d = ws(0, 16, 8192, 8192, 64)
     assert d >= 16 * (8192 + 64) * 4 and d % 256 == 0
+    # ... and without an adapter the decode kernel writes y itself
+    assert ws(0, 16, 8192, 8192, 0) == 0
     assert ws(0, 16, 100, 4096, 16) == 0          # N % 64
     assert ws(0, 16, 4096, 100, 16) == 0          # K % 64
     assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
