@@ -37,9 +37,7 @@
 // and rounds y to bf16 once; without one, the weight tiles round and store
 // y themselves.
 //
-// Grid: 1-D over the weight tiles, then (A tiles x SA splits), ordered so
-// that consecutive ranks share an XCD (workgroups are dealt to the 8 XCDs
-// round-robin).
+// Grid: 1-D over the weight tiles, then (A tiles x SA splits).
 
 #include <type_traits>
 
@@ -95,12 +93,23 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
   // needs no base added); after the main loop the space holds the reduction
   __shared__ __align__(16) uint8_t lds[kLdsBytes];
 
-  const int64_t id = blockIdx.x, per_xcd = (int64_t)gridDim.x / 8;
-  const int64_t rank = (id % 8) * per_xcd + id / 8;  // grid padded to a multiple of 8
-  if (rank >= p.blocks) return;
-  const bool a_tile = rank >= p.w_blocks;
-  const int64_t tile = a_tile ? (rank - p.w_blocks) / p.sa : rank;
-  const int z = a_tile ? (int)((rank - p.w_blocks) % p.sa) : 0;
+  // Weight tiles take the first ids, A tiles the last: workgroups are
+  // dispatched in id order, so the A tiles fill in as weight tiles finish
+  // instead of holding CUs the weight tiles need.  Among the weight tiles,
+  // ids are turned into ranks contiguous within an XCD (ids are dealt to
+  // the 8 XCDs round-robin), so neighbouring row tiles share an L2.
+  const int64_t id = blockIdx.x;
+  if (id >= p.blocks) return;
+  const bool a_tile = id >= p.w_blocks;
+  int64_t tile;
+  int z = 0;
+  if (a_tile) {
+    tile = (id - p.w_blocks) / p.sa;
+    z = (int)((id - p.w_blocks) % p.sa);
+  } else {
+    const int64_t xcd = id % 8, per = p.w_blocks / 8, extra = p.w_blocks % 8;
+    tile = xcd * per + (xcd < extra ? xcd : extra) + id / 8;
+  }
 
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
@@ -314,26 +323,17 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
   }
 }
 
-// sum over splits z = 0 .. splits-1 in order, eight loads issued at a time
-__device__ __forceinline__ float sum_splits(const float* __restrict__ part, int64_t stride,
-                                            int splits) {
-  float s = 0.0f;
-  for (int z0 = 0; z0 < splits; z0 += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = z0 + u < splits ? part[(int64_t)(z0 + u) * stride] : 0.0f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (z0 + u < splits) s += v[u];
-  }
-  return s;
-}
-
-// y[m][n] = bf16( sum_z part[z][m][n] + scale * sum_j xa[m][j] B[n][j] ) with
-// xa[m][j] = sum_z part[z][m][N + j]; fixed summation orders.  Block of 256
-// threads = 64 columns n x 4 token groups.
+// y[m][n] = bf16( part[0][m][n] + scale * sum_j xa[m][j] B[n][j] ) with
+// xa[m][j] = sum_z part[z][m][N + j] (z < sa), fixed summation orders.
+// Block of 256 threads = 32 columns n x 8 lanes; lane g of a column holds
+// B[n][8 g .. 8 g + 7] (the 8 lanes read the 128-byte row whole), forms its
+// share of the r-sum for every token, and the shares are added by a fixed
+// butterfly over the 8 lanes.  The partial sums were written by the
+// previous kernel and are read from beyond L2, so all of a pass's loads are
+// issued before any is used.
+constexpr int kMaxASplits = 16;
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part,
-                                                            int sw, int sa,
+                                                            int sa,
                                                             const uint16_t* __restrict__ B,
                                                             int r, float scale,
                                                             uint16_t* __restrict__ y, int64_t M,
@@ -341,20 +341,36 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
   __shared__ float xa[32 * 256];
   const int t = threadIdx.x;
   const int64_t ldp = N + r;
-  for (int e = t; e < M * r; e += 256) {
-    const int64_t m = e / r, j = e - m * r;
-    xa[e] = sum_splits(part + m * ldp + N + j, M * ldp, sa);
+  constexpr int EPT = 4;  // xa elements per thread per pass
+  const int total = (int)(M * r);
+  for (int e0 = t; e0 < total; e0 += 256 * EPT) {
+    float v[EPT][kMaxASplits];
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      const int e = e0 + 256 * u < total ? e0 + 256 * u : 0;
+      const int64_t m = e / r, j = e - m * r;
+      const float* src = part + m * ldp + N + j;
+#pragma unroll
+      for (int z = 0; z < kMaxASplits; ++z) v[u][z] = z < sa ? src[(int64_t)z * M * ldp] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < EPT; ++u) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int z = 0; z < kMaxASplits; ++z)
+        if (z < sa) acc += v[u][z];
+      if (e0 + 256 * u < total) xa[e0 + 256 * u] = acc;
+    }
   }
   __syncthreads();
-  const int64_t n = (int64_t)blockIdx.x * 64 + (t & 63);
-  const int mg = t >> 6;
-  if (n >= N) return;
-  constexpr int MPT = 8;  // tokens per thread (M <= 32, 4 groups)
-  float lsum[MPT];
+  const int g = t & 7;                               // lane within the column
+  const int64_t n = (int64_t)blockIdx.x * 32 + (t >> 3);
+  const bool n_ok = n < N;
+  float sh[kDecodeMaxM];                             // this lane's share, per token
 #pragma unroll
-  for (int i = 0; i < MPT; ++i) lsum[i] = 0.0f;
-  for (int jc = 0; jc < r; jc += 8) {
-    const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(B + n * r + jc);
+  for (int m = 0; m < kDecodeMaxM; ++m) sh[m] = 0.0f;
+  for (int jc = 8 * g; jc < r; jc += 64) {
+    const u32x4_t bv = n_ok ? *reinterpret_cast<const u32x4_t*>(B + n * r + jc) : u32x4_t{0, 0, 0, 0};
     float b[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -362,32 +378,41 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
       b[2 * e + 1] = bf16_bits_to_f32(bv[e] >> 16);
     }
 #pragma unroll
-    for (int i = 0; i < MPT; ++i) {
-      const int m = mg + 4 * i;
+    for (int m = 0; m < kDecodeMaxM; ++m) {
       if (m < M) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lsum[i] += xa[m * r + jc + e] * b[e];
+        for (int e = 0; e < 8; ++e) sh[m] += xa[m * r + jc + e] * b[e];
       }
     }
   }
+  // butterfly over the 8 lanes of the column (a fixed order)
 #pragma unroll
-  for (int i = 0; i < MPT; ++i) {
-    const int m = mg + 4 * i;
-    if (m < M) {
-      float acc = sum_splits(part + m * ldp + n, M * ldp, sw);
-      acc += scale * lsum[i];
-      y[m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+  for (int d = 1; d < 8; d <<= 1) {
+#pragma unroll
+    for (int m = 0; m < kDecodeMaxM; ++m)
+      if (m < M) sh[m] += __shfl_xor(sh[m], d, 8);
+  }
+  // lane g stores tokens g, g + 8, ...
+  if (n_ok) {
+#pragma unroll
+    for (int m0 = 0; m0 < kDecodeMaxM; m0 += 8) {
+      const int m = m0 + g;
+      if (m < M) {
+        const float acc = part[m * ldp + n] + scale * sh[m];
+        y[m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+      }
     }
   }
 }
 
 namespace {
 
-// k splits of the adapter's A tiles, which run after the weight tiles: short
-// pieces (about 512 k each, at most 16) that fill in as CUs free up
+// k splits of the adapter's A tiles, which run after the weight tiles:
+// pieces of about 2048 k (at most 16), few enough that the reduction reads
+// few partial planes
 int a_splits(int64_t K) {
-  int64_t s = K / 512;
-  if (s > 16) s = 16;
+  int64_t s = K / 2048;
+  if (s > kMaxASplits) s = kMaxASplits;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -421,12 +446,11 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
   p.w_blocks = (N + 31) / 32;
   p.blocks = p.w_blocks + (r > 0 ? (int64_t)((r + 31) / 32) * p.sa : 0);
   p.L = L;
-  const int64_t grid = (p.blocks + 7) / 8 * 8;
-  hipLaunchKernelGGL(decode_main_kernel, dim3((unsigned)grid), dim3(WAVES * 64), 0, s, p);
+  hipLaunchKernelGGL(decode_main_kernel, dim3((unsigned)p.blocks), dim3(WAVES * 64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || r == 0) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s,
-                     part, 1, p.sa, B, r, scale, y, M, N);
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((N + 31) / 32)), dim3(256), 0, s,
+                     part, p.sa, B, r, scale, y, M, N);
   return hipGetLastError();
 }
 
