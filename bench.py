@@ -269,8 +269,10 @@ def main():
             raise RuntimeError(f"{what}: {lib.qlora_status_string(rc).decode()}")
 
     def quantize():
-        check(lib.qlora_quantize_nf4(P(w_d), n, 64, P(codes), P(absmax), sp()), "quantize")
-        check(lib.qlora_double_quant(P(absmax), n // 64, 256, P(qs), P(st), sp()), "double_quant")
+        # quantise + double-quantise in one pass (the same bits as the two
+        # separate calls, which the parity tests check)
+        check(lib.qlora_quantize_nf4_dq(P(w_d), n, P(codes), P(absmax), P(qs), P(st), sp()),
+              "quantize_nf4_dq")
 
     quantize()
     torch.cuda.synchronize()

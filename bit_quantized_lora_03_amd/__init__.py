@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     linear_fwd,
     nf4_levels,
     quantize_nf4,
+    quantize_nf4_dq,
     quantize_weight,
     workspace_bytes,
 )

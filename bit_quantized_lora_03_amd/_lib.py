@@ -20,7 +20,8 @@ QLORA_OK = 0
 STATUS_NAMES = {0: "QLORA_OK", -1: "QLORA_EINVAL", -2: "QLORA_ESHAPE", -3: "QLORA_EALIGN",
                 -4: "QLORA_ENOTSUP", -5: "QLORA_EWORKSPACE", -6: "QLORA_EHIP"}
 
-EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_dequantize_nf4",
+EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
+           "qlora_dequantize_nf4",
            "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_workspace_bytes",
            "qlora_nf4_levels", "qlora_status_string")
 
@@ -56,6 +57,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "qlora_quantize_nf4": ([vp, i64, i32, vp, vp, vp], ctypes.c_int),
         "qlora_double_quant": ([vp, i64, i32, vp, vp, vp], ctypes.c_int),
+        "qlora_quantize_nf4_dq": ([vp, i64, vp, vp, vp, vp, vp], ctypes.c_int),
         "qlora_dequantize_nf4": ([wp, vp, vp], ctypes.c_int),
         "qlora_linear_fwd": ([wp, vp, i64, vp, vp, i32, f32, vp, vp, sz, vp], ctypes.c_int),
         "qlora_linear_bwd": ([wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, i32, vp, sz, vp],
@@ -148,11 +150,28 @@ def double_quant(absmax) -> Tuple[object, object]:
     return q, step
 
 
+def quantize_nf4_dq(w) -> Tuple[object, object, object, object]:
+    """fp32 device tensor -> (codes, absmax, qscale, dq_step) in one pass:
+    the outputs of quantize_nf4 followed by double_quant, bit for bit."""
+    torch = _torch()
+    assert w.dtype == torch.float32 and w.is_cuda and w.is_contiguous()
+    n = w.numel()
+    nb = (n + 63) // 64
+    codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(nb, dtype=torch.float32, device=w.device)
+    q = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    step = torch.empty((nb + 255) // 256, dtype=torch.float32, device=w.device)
+    check(lib().qlora_quantize_nf4_dq(_ptr(w), n, _ptr(codes), _ptr(absmax), _ptr(q),
+                                      _ptr(step), _stream_ptr()),
+          "qlora_quantize_nf4_dq")
+    return codes, absmax, q, step
+
+
 def quantize_weight(w) -> PackedWeight:
-    """fp32 [N, K] device weight -> PackedWeight (quantise, then double-quantise)."""
+    """fp32 [N, K] device weight -> PackedWeight (quantise and double-quantise
+    in one pass)."""
     N, K = w.shape
-    codes, absmax = quantize_nf4(w.contiguous().view(-1))
-    q, step = double_quant(absmax)
+    codes, _, q, step = quantize_nf4_dq(w.contiguous().view(-1))
     return PackedWeight(codes, q, step, N, K)
 
 

@@ -231,6 +231,30 @@ int qlora_double_quant(const float* absmax, int64_t n_blocks, int32_t blocksize2
   }
 }
 
+int qlora_quantize_nf4_dq(const float* w, int64_t n_elems, uint8_t* codes, float* absmax,
+                          uint8_t* qscale, float* dq_step, void* stream) {
+  try {
+    if (n_elems < 0) return QLORA_EINVAL;
+    if (n_elems == 0) return QLORA_OK;
+    if (!w || !codes || !absmax || !qscale || !dq_step) return QLORA_EINVAL;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(absmax) || !aligned16(qscale) ||
+        !aligned16(dq_step))
+      return QLORA_EALIGN;
+    const int64_t nb = (n_elems + 63) / 64;
+    const size_t nw = (size_t)n_elems * 4, nc = (size_t)(n_elems + 1) / 2, na = (size_t)nb * 4,
+                 nq = (size_t)nb, ns = (size_t)((nb + 255) / 256) * 4;
+    const void* p[5] = {w, codes, absmax, qscale, dq_step};
+    const size_t sz[5] = {nw, nc, na, nq, ns};
+    for (int i = 0; i < 5; ++i)
+      for (int j = i + 1; j < 5; ++j)
+        if (overlap(p[i], sz[i], p[j], sz[j])) return QLORA_EINVAL;
+    return hip_status(qlora::launch_quantize_dq(w, n_elems, codes, absmax, qscale, dq_step,
+                                                code_bins_arg(), as_stream(stream)));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
 int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream) {
   try {
     if (!w || !w->codes || !w->qscale || !w->dq_step || !out) return QLORA_EINVAL;

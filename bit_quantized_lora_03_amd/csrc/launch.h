@@ -15,6 +15,10 @@ hipError_t launch_quantize(const float* w, int64_t n, uint8_t* codes, float* abs
                            const Nf4CodeBins& bins, hipStream_t s);
 hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* qscale,
                                float* step, hipStream_t s);
+// both in one pass (one workgroup per group of 256 blocks)
+hipError_t launch_quantize_dq(const float* w, int64_t n, uint8_t* codes, float* absmax,
+                              uint8_t* qscale, float* step, const Nf4CodeBins& bins,
+                              hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
                           int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s);
 

@@ -96,6 +96,105 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Quantiser and double quantisation in one pass: a workgroup of 1024 lanes
+// owns one group of 256 blocks (16384 weights), each lane 16 consecutive
+// weights (four 16-byte loads), four lanes per block.  The block absmax is
+// a max over the 4 lanes, the lane's codes follow at once (they need only
+// the block's absmax), and the group's step -- a max over the workgroup --
+// comes last; every step uses exactly the arithmetic of
+// nf4_quantize_kernel and double_quant_kernel, so the outputs are the same
+// bits.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void nf4_quantize_dq_kernel(
+    const float* __restrict__ w, int64_t n, uint8_t* __restrict__ codes,
+    float* __restrict__ absmax, uint8_t* __restrict__ qscale, float* __restrict__ step_out,
+    Nf4CodeBins bins) {
+#pragma clang fp contract(off)
+  __shared__ uint2 tab[64];
+  __shared__ float wmax[16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (t < 64)
+    tab[t] = make_uint2(__float_as_uint(bins.thr[t]), bins.base[t]);
+
+  const int64_t g = blockIdx.x;
+  const int64_t nb = (n + 63) >> 6;
+  const int64_t e0 = g * 16384 + (int64_t)t * 16;  // this lane's 16 weights
+  const int64_t b = e0 >> 6;                       // its block
+  const bool full = e0 + 16 <= n;
+  float v[16];
+  if (full) {
+    const float4* p = reinterpret_cast<const float4*>(w + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = p[i];
+      v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (e0 + i < n) ? w[e0 + i] : 0.0f;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 4));
+  m = fmaxf(m, __shfl_xor(m, 2, 4));  // the block's absmax (0 past the end)
+  __syncthreads();                    // the code table is in LDS
+
+  // codes, as in nf4_quantize_kernel
+  uint32_t packed[2] = {0u, 0u};
+  const bool direct = m >= 0x1p-60f && m <= 0x1p60f;
+  const float y = direct ? __fdiv_rn(1.0f, m) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float u;
+    if (direct) {
+      const float q = v[i] * y;
+      const float res = __builtin_fmaf(-q, m, v[i]);  // exact
+      u = __builtin_fmaf(res, y, q);
+    } else {
+      u = __fdiv_rn(v[i], m);
+    }
+    const uint2 tt = tab[nf4_bin(u)];
+    const uint32_t c = tt.y + (u > __uint_as_float(tt.x) ? 1u : 0u);
+    packed[i >> 3] |= c << (4 * (i & 7));
+  }
+  if (!(m > 0.0f)) {  // zero block
+    packed[0] = packed[1] = 0x77777777u;
+  } else if (!full) {  // padding past n
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (e0 + i >= n)
+        packed[i >> 3] = (packed[i >> 3] & ~(15u << (4 * (i & 7)))) | (7u << (4 * (i & 7)));
+  }
+  if (full) {
+    const u32x2_t o = {packed[0], packed[1]};
+    *reinterpret_cast<u32x2_t*>(codes + (e0 >> 1)) = o;
+  } else if (e0 < n) {
+    const int64_t nbytes = (n + 1) >> 1;
+    for (int i = 0; i < 8; ++i)
+      if ((e0 >> 1) + i < nbytes) codes[(e0 >> 1) + i] = (uint8_t)(packed[i >> 2] >> (8 * (i & 3)));
+  }
+
+  // the group's max over its 256 block scales (blocks past the end count 0)
+  float gm = m;
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) gm = fmaxf(gm, __shfl_xor(gm, o, 64));
+  if (lane == 0) wmax[wave] = gm;
+  __syncthreads();
+  gm = wmax[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) gm = fmaxf(gm, wmax[i]);
+  const float st = __fdiv_rn(gm, 255.0f);
+  if ((t & 3) == 0 && b < nb) {
+    uint32_t q = 0;
+    if (st > 0.0f) q = (uint32_t)fminf(rintf(__fdiv_rn(m, st)), 255.0f);
+    qscale[b] = (uint8_t)q;
+    absmax[b] = m;
+  }
+  if (t == 0) step_out[g] = st;
+}
+
+// ---------------------------------------------------------------------------
 // Double quantisation: one wave per group of 256 scales, 4 scales per lane.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void double_quant_kernel(
@@ -169,6 +268,15 @@ hipError_t launch_quantize(const float* w, int64_t n, uint8_t* codes, float* abs
   const int64_t lanes = (n + 7) >> 3;
   const int grid = grid_for(lanes, 256, 256 * 32);
   hipLaunchKernelGGL(nf4_quantize_kernel, dim3(grid), dim3(256), 0, s, w, n, codes, absmax, bins);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dq(const float* w, int64_t n, uint8_t* codes, float* absmax,
+                              uint8_t* qscale, float* step, const Nf4CodeBins& bins,
+                              hipStream_t s) {
+  const int64_t groups = (n + 16383) / 16384;
+  hipLaunchKernelGGL(nf4_quantize_dq_kernel, dim3((unsigned)groups), dim3(1024), 0, s, w, n, codes,
+                     absmax, qscale, step, bins);
   return hipGetLastError();
 }
 

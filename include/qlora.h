@@ -105,6 +105,16 @@ int qlora_quantize_nf4(const float* w, int64_t n_elems, int32_t blocksize,
 int qlora_double_quant(const float* absmax, int64_t n_blocks, int32_t blocksize2,
                        uint8_t* qscale, float* dq_step, void* stream);
 
+/* Quantisation and double quantisation in one pass: the outputs of
+ * qlora_quantize_nf4 (blocksize 64) followed by qlora_double_quant
+ * (blocksize 256) on its absmax, bit for bit, from one read of w.
+ * [QLoRA / infivelines.com]: NF4 blocks of 64, scales quantised again in
+ * blocks of 256.  Arguments as in those two calls (absmax is still
+ * written); n_elems may be 0 (nothing is enqueued); the five buffers must
+ * not overlap (EINVAL) and must be 16-byte aligned (EALIGN).               */
+int qlora_quantize_nf4_dq(const float* w, int64_t n_elems, uint8_t* codes, float* absmax,
+                          uint8_t* qscale, float* dq_step, void* stream);
+
 /* Standalone dequantisation to bf16 (the same device function the GEMMs
  * use): out[i] = bf16_rne(fp32(L[code_i] * fp32(qscale[b] * dq_step[b/256]))).
  * [QLoRA / infivelines.com]: the base is dequantised to bf16.

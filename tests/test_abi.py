@@ -105,6 +105,20 @@ def test_double_quant_validation():
     assert L.qlora_double_quant(P0, 512, 256, P0 + 16, P2, None) == -1
 
 
+def test_quantize_dq_validation():
+    L = q.lib()
+    f = L.qlora_quantize_nf4_dq
+    # w [128] at P0; codes, absmax, qscale, step at disjoint aligned places
+    ok = (P0, 128, P1, P2, P3, P4)
+    assert f(P0, -1, P1, P2, P3, P4, None) == -1
+    assert f(P0, 0, None, None, None, None, None) == 0             # empty: no-op
+    assert f(None, 128, P1, P2, P3, P4, None) == -1
+    assert f(P0, 128, P1, P2, None, P4, None) == -1
+    assert f(P0, 128, P1, P2, P3 + 1, P4, None) == -3
+    assert f(P0, 128, P1, P2, P3, P2, None) == -1                 # step over absmax
+    assert f(P0, 128, P0 + 256, P2, P3, P4, None) == -1           # codes inside w
+
+
 def test_dequant_validation():
     L = q.lib()
     w = _weight()

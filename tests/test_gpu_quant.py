@@ -22,15 +22,27 @@ def _gpu_quant(w: np.ndarray):
     return host(codes), host(absmax), host(qs), host(step)
 
 
+def _gpu_quant_fused(w: np.ndarray):
+    import torch
+    wd = dev(np.ascontiguousarray(w, dtype=np.float32).reshape(-1))
+    codes, absmax, qs, step = q.quantize_nf4_dq(wd)
+    torch.cuda.synchronize()
+    return host(codes), host(absmax), host(qs), host(step)
+
+
 def _assert_bitexact(w: np.ndarray, label: str):
+    """Both paths -- the two separate calls and the one-pass call -- against
+    the oracle, bit for bit."""
     print(f"quantise {label} n={w.size}", flush=True)
-    codes, absmax, qs, step = _gpu_quant(w)
     oc, op, oa = oracle.quantize_nf4(w)
     oq, ost = oracle.double_quant(oa)
-    assert np.array_equal(codes, op), label + ": packed codes"
-    assert np.array_equal(absmax.view(np.uint32), oa.view(np.uint32)), label + ": absmax"
-    assert np.array_equal(qs, oq), label + ": qscale"
-    assert np.array_equal(step.view(np.uint32), ost.view(np.uint32)), label + ": step"
+    for path, run in (("separate", _gpu_quant), ("one-pass", _gpu_quant_fused)):
+        codes, absmax, qs, step = run(w)
+        tag = f"{label} ({path})"
+        assert np.array_equal(codes, op), tag + ": packed codes"
+        assert np.array_equal(absmax.view(np.uint32), oa.view(np.uint32)), tag + ": absmax"
+        assert np.array_equal(qs, oq), tag + ": qscale"
+        assert np.array_equal(step.view(np.uint32), ost.view(np.uint32)), tag + ": step"
 
 
 def _special_weight():
@@ -117,7 +129,7 @@ def test_quantize_65b_layer_sampled_groups(cuda):
     oracle from its own 16384 weights."""
     L = workloads.layer_65b()
     w = L.w
-    codes, absmax, qs, step = _gpu_quant(w)
+    codes, absmax, qs, step = _gpu_quant_fused(w)
     flat = w.reshape(-1)
     ng = flat.size // 16384
     rng = np.random.default_rng(5)
