@@ -167,40 +167,48 @@ def cpu_threads():
 
 def run_cpu_baseline(L, kind, budget_s):
     """Time the fp64 oracle on the host on this workload (test infrastructure,
-    used here only as the CPU reference)."""
+    used here only as the CPU reference).  One repetition is quantise +
+    double-quant + dequant of the whole weight and the layer on the batch
+    (or on a token sample scaled linearly when the batch alone would exceed
+    the budget); repetitions continue until about half the budget is spent,
+    and the median one is reported."""
     import oracle
-    t0 = time.perf_counter()
-    flops = 0.0
     w = L.w
     x = L.f32("x")
+    dy = L.f32("dy") if "bwd" in kind else None
     A = L.f32("A") if L.r else None
     B = L.f32("B") if L.r else None
-    _, packed, absmax = oracle.quantize_nf4(w)
-    q, step = oracle.double_quant(absmax)
-    t_q = time.perf_counter()
-    wd = oracle.bf16_bits_to_f64(oracle.dequant_nf4_bits(packed, q, step, w.size)).reshape(w.shape)
-    # the layer on a bounded token sample if the full batch would exceed the budget
     M = L.M
     rows = M
     est = (fwd_flops(M, L.N, L.K, L.r) + (bwd_flops(M, L.N, L.K, L.r) if "bwd" in kind else 0)) / 50e9
     if est > budget_s:
         rows = max(1, int(M * budget_s / est))
-    t1 = time.perf_counter()
-    oracle.lora_linear_fwd(x[:rows], wd, A, B, L.alpha)
-    flops += fwd_flops(rows, L.N, L.K, L.r)
-    if "bwd" in kind:
-        oracle.lora_linear_bwd(x[:rows], L.f32("dy")[:rows], wd, A, B, L.alpha)
-        flops += bwd_flops(rows, L.N, L.K, L.r)
-    t2 = time.perf_counter()
-    # scale to a full step: quantise/dequantise once, the layer for M tokens
-    layer_s = (t2 - t1) * (M / rows)
-    step_s = (t_q - t0) + (t1 - t_q) + layer_s
+    reps = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        _, packed, absmax = oracle.quantize_nf4(w)
+        q, step = oracle.double_quant(absmax)
+        t_q = time.perf_counter()
+        wd = oracle.bf16_bits_to_f64(oracle.dequant_nf4_bits(packed, q, step, w.size)).reshape(w.shape)
+        t1 = time.perf_counter()
+        oracle.lora_linear_fwd(x[:rows], wd, A, B, L.alpha)
+        if "bwd" in kind:
+            oracle.lora_linear_bwd(x[:rows], dy[:rows], wd, A, B, L.alpha)
+        t2 = time.perf_counter()
+        # scale to a full step: quantise/dequantise once, the layer for M tokens
+        layer_s = (t2 - t1) * (M / rows)
+        reps.append(((t_q - t0) + (t1 - t_q) + layer_s, t_q - t0, t1 - t_q, t2 - t1))
+        if time.perf_counter() - t_start > 0.5 * budget_s:
+            break
+    reps.sort()
+    step_s, tq, td, tl = reps[len(reps) // 2]
     full_flops = fwd_flops(M, L.N, L.K, L.r) + (bwd_flops(M, L.N, L.K, L.r) if "bwd" in kind else 0)
     threads, blas = cpu_threads()
-    sample = (f"quantise + double-quant + dequant of the full {L.N}x{L.K} weight; "
+    sample = (f"median of {len(reps)} repetitions ({time.perf_counter() - t_start:.1f} s): "
+              f"quantise + double-quant + dequant of the full {L.N}x{L.K} weight; "
               f"layer on {rows} of {M} tokens, scaled linearly to {M} "
-              f"(quant {t_q - t0:.2f}s, dequant {t1 - t_q:.2f}s, layer {t2 - t1:.2f}s; "
-              f"blas={blas})")
+              f"(quant {tq:.2f}s, dequant {td:.2f}s, layer {tl:.2f}s; blas={blas})")
     return {"value": full_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "sample": sample, "step_s": step_s}
 
