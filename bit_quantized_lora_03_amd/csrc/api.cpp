@@ -65,6 +65,16 @@ int check_weight(const qlora_nf4_weight* w) {
   return QLORA_OK;
 }
 
+// The kernels address every tensor with 32-bit byte offsets (buffer loads):
+// the packed codes and each activation tensor must stay within 2 GiB.
+constexpr int64_t kMaxTensorBytes = int64_t{1} << 31;
+int check_sizes(int64_t M, int64_t N, int64_t K) {
+  if (N / 2 > kMaxTensorBytes / K) return QLORA_ESHAPE;  // codes: N * K / 2 bytes
+  if (M > 0 && (N > kMaxTensorBytes / 2 / M || K > kMaxTensorBytes / 2 / M))
+    return QLORA_ESHAPE;                                  // x, dy, y, dx: M * (N or K) * 2
+  return QLORA_OK;
+}
+
 int check_rank(int32_t r) {
   if (r < 0) return QLORA_EINVAL;
   if (r > QLORA_MAX_RANK || r % 8) return QLORA_ESHAPE;
@@ -73,8 +83,7 @@ int check_rank(int32_t r) {
 
 // ---- workspace layout --------------------------------------------------
 struct FwdWs {
-  size_t p_off, xs_off, xst_off, part_off, total;
-  int psplits;   // k splits of the adapter down-projection (1: no partials)
+  size_t xs_off, xst_off, part_off, total;
   int dsplits;   // k splits of the decode path
   size_t gpart;  // fp32 partials of the fused GEMM's schedule (0: none)
   bool decode;   // few tokens: split-K decode path
@@ -93,12 +102,9 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   }
   size_t off = 0;
   if (r > 0) {
-    // fp32 k-split partials of x . A^T, then xs = [hi | lo] of s . x . A^T: [M][2r] bf16
-    int unused = 1;
-    qlora::lora_proj_plan(M, r, K, 0, L.psplits, unused);
-    L.p_off = 0;
-    L.xs_off = L.psplits > 1 ? round_up((size_t)L.psplits * M * r * sizeof(float), 256) : 0;
-    L.xst_off = round_up(L.xs_off + (size_t)M * 2 * r * sizeof(uint16_t), 256);
+    // xs = [hi | lo] of s . x . A^T: [M][2r] bf16, and its token-contiguous copy
+    L.xs_off = 0;
+    L.xst_off = round_up((size_t)M * 2 * r * sizeof(uint16_t), 256);
     off = round_up(L.xst_off + (size_t)pad32(M) * 2 * r * sizeof(uint16_t), 256);
   }
   L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, N, K), M, N);
@@ -111,37 +117,23 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t pa_off, pg_off, xs_off, gs_off, xst_off, gst_off, cb_off, ca_off, part_off, total;
-  int psplits_a, psplits_g;  // k splits of x . A^T and dy . B (1: no partials)
-  int tsplits;  // token splits of the dA / dB reductions (1: no partials)
-  size_t gpart; // fp32 partials of the dX GEMM's schedule (0: none)
+  size_t xs_off, gs_off, xst_off, gst_off, part_off, total;
+  size_t gpart;  // fp32 partials of the dX GEMM's schedule (0: none)
 };
 BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs L{};
   if (M == 0) return L;
   size_t off = 0;
   if (r > 0) {
-    // fp32 partials of x . A^T and dy . B; xs = [hi | lo] of s . x . A^T and
-    // gs = [hi | lo] of s . dy . B, [M][2r] bf16 each; fp32 token-split
-    // partials of dB [N][r] and dA [r][K]
-    qlora::lora_proj_plan(M, r, K, N, L.psplits_a, L.psplits_g);
-    L.pa_off = off;
-    if (L.psplits_a > 1) off = round_up(off + (size_t)L.psplits_a * M * r * sizeof(float), 256);
-    L.pg_off = off;
-    if (L.psplits_g > 1) off = round_up(off + (size_t)L.psplits_g * M * r * sizeof(float), 256);
+    // xs = [hi | lo] of s . x . A^T and gs = [hi | lo] of s . dy . B, [M][2r]
+    // bf16 each, and their token-contiguous copies [2r][Mp]
     const size_t pair = (size_t)M * 2 * r * sizeof(uint16_t),
                  pairT = (size_t)pad32(M) * 2 * r * sizeof(uint16_t);
-    L.xs_off = off;
+    L.xs_off = 0;
     L.gs_off = round_up(L.xs_off + pair, 256);
     L.xst_off = round_up(L.gs_off + pair, 256);
     L.gst_off = round_up(L.xst_off + pairT, 256);
     off = round_up(L.gst_off + pairT, 256);
-    L.tsplits = qlora::lora_grad_splits(M, N, K);
-    if (L.tsplits > 1) {
-      L.cb_off = off;
-      L.ca_off = round_up(off + (size_t)L.tsplits * N * r * sizeof(float), 256);
-      off = round_up(L.ca_off + (size_t)L.tsplits * r * K * sizeof(float), 256);
-    }
   }
   L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, K, N), M, K);
   if (L.gpart > 0) {
@@ -165,7 +157,9 @@ const char* qlora_status_string(int status) {
   switch (status) {
     case QLORA_OK: return "ok";
     case QLORA_EINVAL: return "invalid argument (null pointer, negative size or aliasing)";
-    case QLORA_ESHAPE: return "unsupported shape (N, K must be multiples of 64; r a multiple of 8 <= 256)";
+    case QLORA_ESHAPE:
+      return "unsupported shape (N, K must be multiples of 64; r a multiple of 8 <= 256; "
+             "codes and each activation tensor at most 2 GiB)";
     case QLORA_EALIGN: return "device pointer not 16-byte aligned";
     case QLORA_ENOTSUP: return "unsupported block size (64 / 256 only)";
     case QLORA_EWORKSPACE: return "workspace missing or too small";
@@ -186,7 +180,9 @@ int qlora_nf4_levels(float* levels, float* thresholds) {
 }
 
 size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r) {
-  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64 || check_rank(r) != QLORA_OK) return 0;
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64 || check_rank(r) != QLORA_OK ||
+      check_sizes(M, N, K) != QLORA_OK)
+    return 0;
   if (op == 0) return fwd_layout(M, N, K, r).total;
   if (op == 1) return bwd_layout(M, N, K, r).total;
   return 0;
@@ -283,6 +279,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
     if ((st = check_rank(r)) != QLORA_OK) return st;
     if (M < 0) return QLORA_EINVAL;
     const int64_t N = w->N, K = w->K;
+    if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
     if (M == 0) return QLORA_OK;
     if (!x || !y) return QLORA_EINVAL;
     if (r > 0 && (!A || !B)) return QLORA_EINVAL;
@@ -311,9 +308,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
     uint16_t* xs = nullptr;
     if (r > 0) {
       xs = at<uint16_t>(workspace, ws.xs_off);
-      float* P = ws.psplits > 1 ? at<float>(workspace, ws.p_off) : nullptr;
-      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), P, K, 0,
-                                  ws.psplits};
+      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), K, 0};
       if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s))) !=
           QLORA_OK)
         return st;
@@ -336,6 +331,7 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
     if ((st = check_rank(r)) != QLORA_OK) return st;
     if (M < 0) return QLORA_EINVAL;
     const int64_t N = w->N, K = w->K;
+    if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
     if (M == 0) {
       // a sum over no tokens: dA = dB = 0 (or unchanged when accumulating)
       if (r == 0) return QLORA_OK;
@@ -343,9 +339,8 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
       if (!aligned16(dA) || !aligned16(dB)) return QLORA_EALIGN;
       if (overlap(dA, (size_t)r * K * 4, dB, (size_t)N * r * 4)) return QLORA_EINVAL;
       // the gradient kernel with no tokens writes zeros (or adds nothing)
-      const qlora::LoraGradJob jb{nullptr, nullptr, dB, nullptr, N, 0},
-          ja{nullptr, nullptr, dA, nullptr, K, 1};
-      return hip_status(qlora::launch_lora_grad(jb, ja, 0, r, accumulate, 1, as_stream(stream)));
+      const qlora::LoraGradJob jb{nullptr, nullptr, dB, N, 0}, ja{nullptr, nullptr, dA, K, 1};
+      return hip_status(qlora::launch_lora_grad(jb, ja, 0, r, accumulate, as_stream(stream)));
     }
     if (!dy) return QLORA_EINVAL;
     if (r > 0 && (!A || !B || !x || !dA || !dB)) return QLORA_EINVAL;
@@ -383,19 +378,12 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
       // xs = split(s . x . A^T), gs = split(s . dy . B) in one launch
       uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
       uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
-      const qlora::LoraProjJob jx{x, A, xs, xsT,
-                                  ws.psplits_a > 1 ? at<float>(workspace, ws.pa_off) : nullptr,
-                                  K, 0, ws.psplits_a},
-          jg{dy, B, gs, gsT, ws.psplits_g > 1 ? at<float>(workspace, ws.pg_off) : nullptr, N, 1,
-             ws.psplits_g};
+      const qlora::LoraProjJob jx{x, A, xs, xsT, K, 0}, jg{dy, B, gs, gsT, N, 1};
       if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, s))) != QLORA_OK)
         return st;
       // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x
-      const bool tp = ws.tsplits > 1;
-      const qlora::LoraGradJob jb{dy, xsT, dB, tp ? at<float>(workspace, ws.cb_off) : nullptr, N, 0},
-          ja{x, gsT, dA, tp ? at<float>(workspace, ws.ca_off) : nullptr, K, 1};
-      if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, ws.tsplits, s))) !=
-          QLORA_OK)
+      const qlora::LoraGradJob jb{dy, xsT, dB, N, 0}, ja{x, gsT, dA, K, 1};
+      if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, s))) != QLORA_OK)
         return st;
     }
     if (dx) {

@@ -27,41 +27,30 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const flo
 // v = scale * sum_k X[m][k] * Y(j, k), with Y(j, k) = Y[j * Kred + k]
 // (kmajor == 0, A [r, Kred]) or Y[k * r + j] (kmajor == 1, B [Kred, r]);
 // also outT[j][m] = hi, outT[r + j][m] = lo with rows of Mp = M rounded up
-// to 32 (zero past M).  With splits > 1 the job's k range is split over
-// blocks writing fp32 partials P [splits][M][r], added in split order by a
-// second kernel.
-constexpr int kProjMaxSplits = 16;
+// to 32 (zero past M).  Each block reduces its whole range itself.
 struct LoraProjJob {
   const uint16_t* X;  // [M, Kred] bf16
   const uint16_t* Y;
   uint16_t* out;      // [M, 2r] bf16
   uint16_t* outT;     // [2r, Mp] bf16
-  float* P;           // [splits][M][r] fp32 (splits > 1)
   int64_t Kred;
   int kmajor;
-  int splits;
 };
-// splits of one job (K1 = 0) or of two jobs sharing a launch
-void lora_proj_plan(int64_t M, int r, int64_t K0, int64_t K1, int& s0, int& s1);
 // one job, or two in one launch (j1 non-null)
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                             float scale, hipStream_t s);
 // lora_grad: C (+)= sum_m G[m][g] * (ST[j][m] + ST[r + j][m]), C [ldg, r]
-// (transposed == 0) or [r, ldg] (transposed == 1); both jobs in one launch.
-// With splits > 1 the tokens are split over blocks writing fp32 partials
-// Cp [splits][C's layout], added to C in split order by a second kernel.
-constexpr int kGradMaxSplits = 16;
+// (transposed == 0) or [r, ldg] (transposed == 1); both jobs in one launch,
+// each block reducing over all tokens itself.
 struct LoraGradJob {
   const uint16_t* G;   // [M, ldg] bf16, ldg a multiple of 64
   const uint16_t* ST;  // [2r, Mp] bf16 (hi rows, then lo rows), zero past M
   float* C;
-  float* Cp;          // [splits][ldg * r] fp32 (splits > 1)
   int64_t ldg;
   int transposed;
 };
-int lora_grad_splits(int64_t M, int64_t ldg0, int64_t ldg1);
 hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
-                            int accumulate, int splits, hipStream_t s);
+                            int accumulate, hipStream_t s);
 
 // gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T.
 // Schedule of a fused GEMM with an Mout x Nout output (Nout in tiles of 256)

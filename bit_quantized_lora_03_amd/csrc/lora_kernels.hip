@@ -14,24 +14,68 @@
 //  * lora_grad: C (+)= G^T . (S_hi + S_lo) with the reduction over the
 //    tokens: dB [N, r] = dy^T . xs and dA [r, K] = gs^T . x.
 //
-// Both are latency-bound at the shapes of the layer (a few MB per call), so
-// the reduction is spread over many small blocks: the waves of a block take
-// interleaved shares of its range and are added in LDS in wave order; when
-// a range is split over blocks, each block writes an fp32 partial and a
-// finalize kernel adds the partials in split order.  Results are therefore
-// deterministic.  Each wave keeps its next share's global loads in flight
-// while it works on the current one, and two jobs share one launch.
+// Both stream one big operand (x or dy) once and are bound by memory at
+// training sizes and by latency at small ones.  Every block owns its
+// outputs' whole reduction, so no partials leave the chip and no second
+// kernel runs: the eight waves of a block take interleaved 32-wide steps of
+// the reduction, each wave issues the global loads of a whole batch of
+// steps before it uses them (so a block keeps many loads in flight), and
+// the waves' sums are added in LDS in wave order.  Results are therefore
+// deterministic.
+//
+// Where an MFMA operand needs 8 consecutive reduction indices of a matrix
+// stored the other way round (B [Kred, r] in lora_proj, G [M, ldg] in
+// lora_grad), the wave stores the loaded rows as they are into its own LDS
+// slab and reads the operand back with ds_read_b64_tr_b16, gfx950's LDS
+// transpose read: within each group of 16 lanes, lane i receives element
+// i mod 4 of the 8-byte pieces addressed by lanes i/4, 4 + i/4, 8 + i/4 and
+// 12 + i/4.  So if lane c of a group points at row R0 + c/4, columns
+// C0 + 4 (c mod 4) .. + 3 of the slab, lane i receives rows R0 .. R0 + 3 of
+// column C0 + i; two such reads (R0 and R0 + 4) give the 8 values.  A slab
+// is private to its wave and a wave's LDS accesses complete in order, so no
+// barrier is needed around it.
 
 #include "device_common.h"
 #include "launch.h"
 
 namespace qlora {
 
+namespace {
+
+constexpr int kWaves = 8;             // waves per block (both kernels)
+constexpr int kThreads = 64 * kWaves;
+
 __device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 __host__ __device__ __forceinline__ int64_t pad32(int64_t M) { return (M + 31) / 32 * 32; }
+
+// Loads go through buffer descriptors: 32-bit lane offsets instead of 64-bit
+// addresses, and a lane offset at or past the tensor's size reads zero
+// (rows past M, rank columns past r, steps past a wave's share).  The
+// scalar offset, which the bounds check does not see, carries only the
+// wave-uniform step position.
+constexpr uint32_t kOff = 0x80000000u;  // past every tensor (each is below 2 GiB)
+__device__ __forceinline__ u32x4_t ldb(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff,
+                                                                           (int)soff, 0));
+}
+
+// 8 bf16 of one slab column: rows row0 .. row0 + 7 (as two transpose reads,
+// rows row0 + 4h + c/4 addressed by lane c of the 16-lane group), column
+// col0 + lane % 16.  `stride` is the slab row length in bf16.
+__device__ __forceinline__ u32x4_t read_tr8(const uint16_t* slab, int stride, int row0, int col0,
+                                            int i) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const uint16_t* p = slab + (row0 + (i >> 2)) * stride + col0 + 4 * (i & 3);
+  const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+  const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * stride));
+  const u32x2_t h0 = __builtin_bit_cast(u32x2_t, r0), h1 = __builtin_bit_cast(u32x2_t, r1);
+  const u32x4_t v = {h0[0], h0[1], h1[0], h1[1]};
+  return v;
+}
 
 // Store the bf16 pair of v for (m, j) in both layouts (m < Mp; rows past M
 // only get zeros in the transposed copy).
@@ -49,454 +93,304 @@ __device__ __forceinline__ void put_split(const LoraProjJob& J, int64_t M, int r
   J.outT[(int64_t)(r + j) * Mp + m] = lo;
 }
 
-// ---------------------------------------------------------------------------
-// lora_proj: grid (sum over jobs of ceil(M/64) * ceil(r/(16 JT)) * splits),
-// 256 threads.  A block owns 64 tokens x 16 JT rank columns of one job and
-// the z-th share of that job's reduction (jobs split in proportion to their
-// reduction length, so their blocks carry equal work); wave w owns tokens
-// 16 w .. 16 w + 15 and runs the block's whole k share with 16x16x32 MFMA.
-// The token operand is one 16-byte load per lane (8 consecutive k of a
-// row), straight from global memory, and so is A's operand per 16-column
-// group (the four waves read the same A pieces, which stay in L1).  B
-// ([Kred, r]) has k as its slow index, so the block loads it as 16-byte row
-// pieces (8 rank columns of one k), turns them around once in a shared,
-// double-buffered LDS tile per batch of k steps, and every wave reads its
-// operands from there.  With one split the waves write the bf16 pairs
-// themselves; otherwise they write fp32 partials P[z][m][j] and
-// lora_proj_finalize adds the shares in order.
-// ---------------------------------------------------------------------------
-constexpr int kProjBatch = 4;  // k steps per register set
-constexpr int kProjTRow = 40;  // transposed B row: 32 k + 8 pad (bf16), 80 bytes
+}  // namespace
 
+// ---------------------------------------------------------------------------
+// lora_proj: grid = sum over jobs of (Mp / 16) * ceil(r / RC) blocks, 512
+// threads.  A block owns 16 tokens x RC = 16 JT rank columns of one job and
+// that job's whole reduction; wave w takes the 32-wide k steps w, w + 8, ...
+// with 16x16x32 MFMA (tokens as rows).  The token operand is one 16-byte
+// load per lane (8 consecutive k of a row); so is A's operand per 16-column
+// group.  B's rows (8 rank columns of one k per 16 bytes) go through the
+// wave's slab and come back transposed.
+// ---------------------------------------------------------------------------
 template <int JT>
-__global__ __launch_bounds__(256) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
-                                                        int64_t blocks0, int64_t M, int r,
-                                                        float scale) {
-  __shared__ __align__(16) uint16_t tb[2][kProjBatch][16 * JT * kProjTRow];
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
+__global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
+                                                             int64_t blocks0, int64_t M, int r,
+                                                             float scale) {
+  constexpr int RC = 16 * JT;            // rank columns of the block
+  constexpr int RS = RC + 8;             // slab row: RC bf16 + 16 bytes of pad
+  constexpr int SLAB = 32 * RS;          // bf16 per wave
+  constexpr int BS = JT == 1 ? 8 : 4;    // k steps per batch of loads
+  constexpr int REDS = RC + 4;           // fp32 row of the cross-wave sums
+  constexpr int SLAB_BYTES = kWaves * SLAB * 2, RED_BYTES = kWaves * 16 * REDS * 4;
+  __shared__ __align__(16) char lds[SLAB_BYTES > RED_BYTES ? SLAB_BYTES : RED_BYTES];
+
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const bool second = (int64_t)blockIdx.x >= blocks0;
   const LoraProjJob J = second ? j1 : j0;
-  const int splits = J.splits;
-
-  const int jblocks = (r + 16 * JT - 1) / (16 * JT);
-  const int64_t b0 = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
-  const int z = (int)(b0 % splits);
-  const int64_t bb = b0 / splits;
-  const int64_t mblk = (bb / jblocks) * 64;
-  const int64_t m0 = mblk + 16 * wave;
-  const int jc = (int)(bb % jblocks) * 16 * JT;
+  const int64_t b = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
+  const int jchunks = (r + RC - 1) / RC;
+  const int64_t m0 = 16 * (b / jchunks);
+  const int jc = (int)(b % jchunks) * RC;
   const int i = lane & 15, kg = lane >> 4;
   const int64_t m = m0 + i;
-  const bool mok = m < M;
   const int64_t Kred = J.Kred;
   const int64_t nsteps = Kred / 32;
-  const int64_t st0 = nsteps * z / splits, st1 = nsteps * (z + 1) / splits;
-  const int64_t ns = st1 - st0;
-  const int64_t nb = (ns + kProjBatch - 1) / kProjBatch;
-  const uint16_t* xrow = J.X + (mok ? m : 0) * Kred + 8 * kg;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const int64_t cnt = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(J.X, (uint32_t)(M * Kred * 2));
+  const __amdgpu_buffer_rsrc_t yres = make_rsrc(J.Y, (uint32_t)((int64_t)r * Kred * 2));
+  // rows m in [M, Mp) lie past x's end and read as zero
+  const uint32_t xoff = (uint32_t)((m * Kred + 8 * kg) * 2);
+  uint16_t* slab = reinterpret_cast<uint16_t*>(lds) + wave * SLAB;
+  const bool kmajor = J.kmajor != 0;
 
   f32x4_t acc[JT];
 #pragma unroll
   for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto load_x = [&](int64_t bi, u32x4_t (&xv)[kProjBatch]) {
+  // Y pieces of a step: A: column group jt's 16 bytes; B: piece p = lane +
+  // 64 q of the 32 x RC slab, row p / (2 JT), 8 columns at 8 (p mod 2 JT)
+  struct Batch {
+    u32x4_t x[BS];
+    u32x4_t y[BS][JT];
+  };
+  auto load = [&](int64_t u0, Batch& R) {
 #pragma unroll
-    for (int u = 0; u < kProjBatch; ++u) {
-      const int64_t s = bi * kProjBatch + u;
-      xv[u] = (mok && s < ns) ? *reinterpret_cast<const u32x4_t*>(xrow + 32 * (st0 + s)) : zero;
+    for (int bb = 0; bb < BS; ++bb) {
+      const int64_t u = u0 + bb;
+      const bool ok = u < cnt;
+      const uint32_t k0 = (uint32_t)(32 * (wave + kWaves * u));
+      R.x[bb] = ldb(xres, ok ? xoff : kOff, 2 * k0);
+#pragma unroll
+      for (int q = 0; q < JT; ++q) {
+        if (!kmajor) {
+          const int jj = jc + 16 * q + i;
+          R.y[bb][q] = ldb(yres, (ok && jj < r) ? (uint32_t)((jj * Kred + 8 * kg) * 2) : kOff,
+                           2 * k0);
+        } else {
+          const int p = lane + 64 * q, row = p / (2 * JT), col = jc + 8 * (p % (2 * JT));
+          R.y[bb][q] = ldb(yres, (ok && col < r) ? (uint32_t)((row * r + col) * 2) : kOff,
+                           2 * k0 * (uint32_t)r);
+        }
+      }
+    }
+  };
+  // steps past the wave's count carry zero operands and add nothing
+  auto compute = [&](const Batch& R) {
+#pragma unroll
+    for (int bb = 0; bb < BS; ++bb) {
+      if (!kmajor) {
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma16x16x32(R.x[bb], R.y[bb][jt], acc[jt]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < JT; ++q) {
+          const int p = lane + 64 * q, row = p / (2 * JT), cp = p % (2 * JT);
+          *reinterpret_cast<u32x4_t*>(slab + row * RS + 8 * cp) = R.y[bb][q];
+        }
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+          acc[jt] = mfma16x16x32(R.x[bb], read_tr8(slab, RS, 8 * kg, 16 * jt, i), acc[jt]);
+      }
     }
   };
 
-  if (!J.kmajor) {
-    // A [r, Kred]: row pieces are MFMA operands as they are
-    auto load_a = [&](int64_t bi, u32x4_t (&yv)[kProjBatch][JT]) {
-#pragma unroll
-      for (int u = 0; u < kProjBatch; ++u) {
-        const int64_t s = bi * kProjBatch + u;
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-          const int jj = jc + 16 * jt + i;
-          yv[u][jt] = (jj < r && s < ns)
-                          ? *reinterpret_cast<const u32x4_t*>(J.Y + (int64_t)jj * Kred +
-                                                              32 * (st0 + s) + 8 * kg)
-                          : zero;
-        }
-      }
-    };
-    auto mma = [&](const u32x4_t (&xv)[kProjBatch], const u32x4_t (&yv)[kProjBatch][JT]) {
-#pragma unroll
-      for (int u = 0; u < kProjBatch; ++u)
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma16x16x32(xv[u], yv[u][jt], acc[jt]);
-    };
-    u32x4_t X0[kProjBatch], X1[kProjBatch], Y0[kProjBatch][JT], Y1[kProjBatch][JT];
-    if (nb > 0) {
-      load_x(0, X0);
-      load_a(0, Y0);
-    }
-    for (int64_t bi = 0; bi < nb; bi += 2) {
-      if (bi + 1 < nb) {
-        load_x(bi + 1, X1);
-        load_a(bi + 1, Y1);
-      }
-      mma(X0, Y0);
-      if (bi + 1 < nb) {
-        if (bi + 2 < nb) {
-          load_x(bi + 2, X0);
-          load_a(bi + 2, Y0);
-        }
-        mma(X1, Y1);
-      }
-    }
-  } else {
-    // B [Kred, r]: thread t loads JT row pieces per batch, piece p = t + 256 q:
-    // step p / (64 JT), k row (p mod 64 JT) / (2 JT), columns 8 (p mod 2 JT)
-    auto load_b = [&](int64_t bi, u32x4_t (&br)[JT]) {
-#pragma unroll
-      for (int q = 0; q < JT; ++q) {
-        const int pc = t + 256 * q;
-        const int u = pc / (64 * JT), w = pc % (64 * JT);
-        const int kr = w / (2 * JT), cp = w % (2 * JT);
-        const int64_t s = bi * kProjBatch + u;
-        const int col = jc + 8 * cp;
-        br[q] = (col < r && s < ns)
-                    ? *reinterpret_cast<const u32x4_t*>(J.Y + (32 * (st0 + s) + kr) * r + col)
-                    : zero;
-      }
-    };
-    auto put_b = [&](int buf, const u32x4_t (&br)[JT]) {
-#pragma unroll
-      for (int q = 0; q < JT; ++q) {
-        const int pc = t + 256 * q;
-        const int u = pc / (64 * JT), w = pc % (64 * JT);
-        const int kr = w / (2 * JT), cp = w % (2 * JT);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          tb[buf][u][(8 * cp + e) * kProjTRow + kr] = (uint16_t)(br[q][e >> 1] >> (16 * (e & 1)));
-      }
-    };
-    auto mma = [&](int buf, const u32x4_t (&xv)[kProjBatch]) {
-#pragma unroll
-      for (int u = 0; u < kProjBatch; ++u)
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-          const u32x4_t b =
-              *reinterpret_cast<const u32x4_t*>(&tb[buf][u][(16 * jt + i) * kProjTRow + 8 * kg]);
-          acc[jt] = mfma16x16x32(xv[u], b, acc[jt]);
-        }
-    };
-    // Batch b's pieces go into buffer b & 1 after the barrier of batch b - 1,
-    // which every wave reaches only once it is done reading batch b - 2 (the
-    // same buffer); all waves run the same number of batches.
-    u32x4_t X0[kProjBatch], X1[kProjBatch], B0[JT], B1[JT];
-    if (nb > 0) {
-      load_x(0, X0);
-      load_b(0, B0);
-    }
-    for (int64_t bi = 0; bi < nb; bi += 2) {
-      if (bi + 1 < nb) {
-        load_x(bi + 1, X1);
-        load_b(bi + 1, B1);
-      }
-      put_b(0, B0);
-      __syncthreads();
-      mma(0, X0);
-      if (bi + 1 < nb) {
-        if (bi + 2 < nb) {
-          load_x(bi + 2, X0);
-          load_b(bi + 2, B0);
-        }
-        put_b(1, B1);
-        __syncthreads();
-        mma(1, X1);
-      }
+  Batch R0, R1;
+  if (cnt > 0) load(0, R0);
+  for (int64_t u0 = 0; u0 < cnt; u0 += 2 * BS) {
+    if (u0 + BS < cnt) load(u0 + BS, R1);
+    compute(R0);
+    if (u0 + BS < cnt) {
+      if (u0 + 2 * BS < cnt) load(u0 + 2 * BS, R0);
+      compute(R1);
     }
   }
 
-  // D[token][j]: lane holds column j = lane % 16, tokens 4 (lane / 16) + v
+  // D[token][j]: lane holds column j = 16 jt + lane % 16, tokens 4 (lane / 16) + v
+  __syncthreads();  // every slab is done; the sums reuse the LDS
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * kg + v) * REDS + 16 * jt + i] = acc[jt][v];
+  __syncthreads();
   const int64_t Mp = pad32(M);
+  for (int e = t; e < 16 * RC; e += kThreads) {
+    const int tok = e & 15, j = e >> 4;  // tokens fastest: outT rows are token-contiguous
+    float sum = red[tok * REDS + j];
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) {
-    const int jo = jc + 16 * jt + i;
-    if (jo >= r) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t mo = m0 + 4 * kg + v;
-      if (splits == 1) {
-        if (mo < Mp) put_split(J, M, r, mo, jo, scale * acc[jt][v]);
-      } else if (mo < M) {
-        J.P[((int64_t)z * M + mo) * r + jo] = acc[jt][v];
-      }
-    }
-  }
-}
-
-// bf16 pairs of scale * sum_z P[z] (z in order); grid-stride over both
-// jobs' Mp x r values (rows past M get zeros in the transposed copy).
-__global__ __launch_bounds__(256) void lora_proj_finalize_kernel(LoraProjJob j0, LoraProjJob j1,
-                                                                 int njobs, int64_t M, int r,
-                                                                 float scale) {
-  const int64_t per = pad32(M) * r, total = per * njobs;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const bool second = e >= per;
-    const LoraProjJob J = second ? j1 : j0;
-    const int splits = J.splits;
-    if (splits == 1) continue;  // the job's blocks wrote their results themselves
-    const int64_t ee = second ? e - per : e;
-    const int64_t m = ee / r;
-    const int j = (int)(ee - m * r);
-    float sum = 0.0f;
-    if (m < M) {
-      float v[16];
-#pragma unroll
-      for (int z = 0; z < 16; ++z) v[z] = z < splits ? J.P[((int64_t)z * M + m) * r + j] : 0.0f;
-      sum = v[0];
-#pragma unroll
-      for (int z = 1; z < 16; ++z)
-        if (z < splits) sum += v[z];
-    }
-    put_split(J, M, r, m, j, scale * sum);
+    for (int w = 1; w < kWaves; ++w) sum += red[(w * 16 + tok) * REDS + j];
+    const int64_t mo = m0 + tok;
+    const int jo = jc + j;
+    if (jo < r && mo < Mp) put_split(J, M, r, mo, jo, scale * sum);
   }
 }
 
 static int proj_jt(int r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
 
-// k splits of one or two jobs sharing a launch: about 512 blocks in all,
-// each job's splits in proportion to its reduction length (equal work per
-// block), at least 8 k steps per split.
-void lora_proj_plan(int64_t M, int r, int64_t K0, int64_t K1, int& s0, int& s1) {
-  const int jw = 16 * proj_jt(r);
-  const int64_t tiles = ((M + 63) / 64) * ((r + jw - 1) / jw);
-  const double total_k = (double)K0 + (double)K1;
-  auto pick = [&](int64_t Kred) {
-    if (Kred <= 0 || tiles == 0) return 1;
-    int64_t s = (int64_t)(512.0 * (double)Kred / (total_k * (double)tiles) + 0.5);
-    if (s > Kred / 256) s = Kred / 256;
-    if (s > kProjMaxSplits) s = kProjMaxSplits;
-    return s < 1 ? 1 : (int)s;
-  };
-  s0 = pick(K0);
-  s1 = pick(K1);
-}
-
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                             float scale, hipStream_t s) {
-  const int njobs = j1 ? 2 : 1;
   const int jt = proj_jt(r);
-  const int jw = 16 * jt;
-  // ceil(M/64) token blocks cover every row of the transposed copy (Mp =
-  // M rounded up to 32 <= the blocks' extent); rows past Mp are not written
-  const int64_t tiles = ((M + 63) / 64) * ((r + jw - 1) / jw);
+  const int rc = 16 * jt;
+  // Mp / 16 token blocks cover every row of the transposed copy
+  const int64_t blocks_per_job = (pad32(M) / 16) * ((r + rc - 1) / rc);
   const LoraProjJob jb = j1 ? *j1 : j0;
-  const int64_t blocks0 = tiles * j0.splits, blocks1 = j1 ? tiles * j1->splits : 0;
-  if (blocks0 + blocks1 == 0) return hipSuccess;
-  const dim3 grid((unsigned)(blocks0 + blocks1));
+  const int64_t blocks0 = blocks_per_job, total = blocks_per_job * (j1 ? 2 : 1);
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)total);
   if (jt == 1)
-    hipLaunchKernelGGL(lora_proj_kernel<1>, grid, dim3(256), 0, s, j0, jb, blocks0, M, r, scale);
+    hipLaunchKernelGGL(lora_proj_kernel<1>, grid, dim3(kThreads), 0, s, j0, jb, blocks0, M, r,
+                       scale);
   else if (jt == 2)
-    hipLaunchKernelGGL(lora_proj_kernel<2>, grid, dim3(256), 0, s, j0, jb, blocks0, M, r, scale);
+    hipLaunchKernelGGL(lora_proj_kernel<2>, grid, dim3(kThreads), 0, s, j0, jb, blocks0, M, r,
+                       scale);
   else
-    hipLaunchKernelGGL(lora_proj_kernel<4>, grid, dim3(256), 0, s, j0, jb, blocks0, M, r, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || (j0.splits == 1 && (!j1 || j1->splits == 1))) return e;
-  int64_t g = (pad32(M) * r * njobs + 255) / 256;
-  if (g > 2048) g = 2048;
-  hipLaunchKernelGGL(lora_proj_finalize_kernel, dim3((unsigned)g), dim3(256), 0, s, j0, jb,
-                     njobs, M, r, scale);
+    hipLaunchKernelGGL(lora_proj_kernel<4>, grid, dim3(kThreads), 0, s, j0, jb, blocks0, M, r,
+                       scale);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// lora_grad: grid ((ldg0 / 64 + ldg1 / 64) * splits), 256 threads.  A block
-// owns 64 columns g of the big operand G (dy for dB, x for dA), all r
-// columns of the small operand S (in chunks of 16 JT) and the z-th share of the
-// tokens.  Wave w takes the 32-token steps w, w + 4, ... of that share.  G
-// is token-major, so the wave stores each step's G rows transposed (tokens
-// contiguous) in its own LDS tile and reads 16-byte MFMA operands back; S
-// comes from the transposed copy ST [2r][Mp] as direct 16-byte loads.
-// 16x16x32 MFMA with G columns as rows and S columns as columns; hi and lo
-// are two MFMAs on the same G operand.  No barrier is needed inside the
-// loop: a wave's LDS accesses are executed in order and no other wave
-// touches its tile.  With one split the block writes C itself; otherwise it
-// writes the partial Cp[z] (C's layout) and lora_grad_finalize adds them in
-// order.
+// lora_grad: grid = (ldg0 + ldg1) / 64 blocks, 512 threads.  A block owns 64
+// columns g0 .. g0 + 63 of the big operand G (dy for dB, x for dA), all r
+// columns of the small operand S (in chunks of RC = 16 JT) and every token.
+// Wave w takes the 32-token steps w, w + 8, ...: it stores the step's G rows
+// (tokens x 64 columns, as loaded) in its slab and reads 16 x 32 MFMA
+// operands back transposed (G columns as rows, 8 consecutive tokens per
+// lane); S comes from the transposed copy ST [2r][Mp] as direct 16-byte
+// loads, hi and lo as two MFMAs on the same G operand.
 // ---------------------------------------------------------------------------
-constexpr int kGradRow = 40;               // LDS row: 32 tokens + 8 pad (bf16), 80 bytes
-constexpr int kGradTile = 64 * kGradRow;   // one wave's transposed G step
-constexpr int kGradRed = 68;               // fp32 row stride of the cross-wave reduction
-
-// JT: 16-column groups of S held per step (1, 2 or 4), so small ranks keep
-// few registers and more blocks fit on a CU.
 template <int JT>
-__global__ __launch_bounds__(256) void lora_grad_kernel(LoraGradJob j0, LoraGradJob j1,
-                                                        int64_t blocks0, int64_t M, int r,
-                                                        int accumulate, int splits) {
-  __shared__ __align__(16) float red[4 * 64 * kGradRed];  // 69632 B; the tiles alias its start
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, LoraGradJob j1,
+                                                             int64_t blocks0, int64_t M, int r,
+                                                             int accumulate) {
+  constexpr int RC = 16 * JT;
+  constexpr int GS = 64 + 8;                        // slab row: 64 bf16 + 16 bytes of pad
+  constexpr int SLAB = 32 * GS;                     // bf16 per wave
+  constexpr int BS = JT == 4 ? 1 : 2;                  // token steps per batch of loads
+  constexpr int REDS = RC + 4;
+  constexpr int SLAB_BYTES = kWaves * SLAB * 2, RED_BYTES = kWaves * 16 * REDS * 4;
+  __shared__ __align__(16) char lds[SLAB_BYTES > RED_BYTES ? SLAB_BYTES : RED_BYTES];
+
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const bool second = (int64_t)blockIdx.x >= blocks0;
   const LoraGradJob J = second ? j1 : j0;
   const int64_t ldg = J.ldg;
-  const int64_t bb = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
-  const int z = (int)(bb % splits);
-  const int64_t g0 = 64 * (bb / splits);
-  float* C = splits == 1 ? J.C : J.Cp + (int64_t)z * ldg * r;
-  const int acc_out = splits == 1 ? accumulate : 0;
-
-  uint16_t* tile = reinterpret_cast<uint16_t*>(red) + wave * kGradTile;
-  const int tk = lane & 31, ch = lane >> 5;  // token of a step, chunk parity
-  const int i = lane & 15, kg = lane >> 4;   // MFMA operand lane coordinates
+  const int64_t g0 = 64 * (second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x);
+  const int i = lane & 15, kg = lane >> 4;
   const int64_t Mp = pad32(M);
   const int64_t nst = Mp / 32;
-  const int64_t st0 = nst * z / splits, st1 = nst * (z + 1) / splits;
-  const int64_t ns = st1 - st0 > wave ? (st1 - st0 - wave + 3) / 4 : 0;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const int64_t cnt = nst > wave ? (nst - wave + kWaves - 1) / kWaves : 0;
+  uint16_t* slab = reinterpret_cast<uint16_t*>(lds) + wave * SLAB;
+  float* red = reinterpret_cast<float*>(lds);
+  const __amdgpu_buffer_rsrc_t gres = make_rsrc(J.G, (uint32_t)(M * ldg * 2));
+  const __amdgpu_buffer_rsrc_t sres = make_rsrc(J.ST, (uint32_t)(2 * r * Mp * 2));
+  const uint32_t sl_off = (uint32_t)(r * Mp * 2);  // lo rows follow the hi rows
 
-  for (int jc = 0; jc < r; jc += 16 * JT) {
-    const int R = r - jc < 16 * JT ? r - jc : 16 * JT;  // multiple of 8
-
-    // step s of this wave: tokens t0 + tk with t0 = 32 (st0 + wave + 4 s);
-    // G chunk c = ch + 2u (8 columns); S operands of the 16-column groups
-    auto load_step = [&](int64_t s, u32x4_t (&gv)[4], u32x4_t (&sh)[JT], u32x4_t (&sl)[JT]) {
-      const int64_t t0 = 32 * (st0 + wave + 4 * s);
-      const int64_t m = t0 + tk;
-      const bool ok = m < M;
-      const uint16_t* grow = J.G + (ok ? m : 0) * ldg + g0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        gv[u] = ok ? *reinterpret_cast<const u32x4_t*>(grow + 8 * (ch + 2 * u)) : zero;
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        if (16 * jt < R) {
-          const int col = jc + 16 * jt + i;
-          const bool cok = col < r;
-          const int64_t off = t0 + 8 * kg;
-          sh[jt] = cok ? *reinterpret_cast<const u32x4_t*>(J.ST + (int64_t)col * Mp + off) : zero;
-          sl[jt] = cok ? *reinterpret_cast<const u32x4_t*>(J.ST + (int64_t)(r + col) * Mp + off)
-                       : zero;
-        } else {
-          sh[jt] = zero;
-          sl[jt] = zero;
-        }
-      }
-    };
+  for (int jc = 0; jc < r; jc += RC) {
     f32x4_t acc[4][JT];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int b = 0; b < JT; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    auto mma_step = [&](const u32x4_t (&gv)[4], const u32x4_t (&sh)[JT], const u32x4_t (&sl)[JT]) {
+
+    // G piece p = lane + 64 q of a step: token p / 8, 8 columns at 8 (p mod 8)
+    uint32_t goff[4], soff[JT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int q = 0; q < 4; ++q) {
+      const int p = lane + 64 * q;
+      goff[q] = (uint32_t)((((p >> 3) * ldg) + g0 + 8 * (p & 7)) * 2);
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          tile[(8 * (ch + 2 * u) + e) * kGradRow + tk] = (uint16_t)(gv[u][e >> 1] >> (16 * (e & 1)));
+    for (int jt = 0; jt < JT; ++jt)
+      soff[jt] = (uint32_t)(((int64_t)(jc + 16 * jt + i) * Mp + 8 * kg) * 2);
+    struct Batch {
+      u32x4_t g[BS][4];
+      u32x4_t sh[BS][JT], sl[BS][JT];
+    };
+    auto load = [&](int64_t u0, Batch& R) {
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const u32x4_t a =
-            *reinterpret_cast<const u32x4_t*>(tile + (16 * gi + i) * kGradRow + 8 * kg);
+      for (int bb = 0; bb < BS; ++bb) {
+        const int64_t u = u0 + bb;
+        const bool ok = u < cnt;
+        const uint32_t t0 = (uint32_t)(32 * (wave + kWaves * u));
+        // the G row is part of the lane offset (rows past M read as zero)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          R.g[bb][q] = ldb(gres, ok ? goff[q] + t0 * (uint32_t)ldg * 2 : kOff, 0);
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
-          if (16 * jt < R) {
-            acc[gi][jt] = mfma16x16x32(a, sh[jt], acc[gi][jt]);
-            acc[gi][jt] = mfma16x16x32(a, sl[jt], acc[gi][jt]);
+          const bool cok = ok && jc + 16 * jt + i < r;
+          R.sh[bb][jt] = ldb(sres, cok ? soff[jt] : kOff, 2 * t0);
+          R.sl[bb][jt] = ldb(sres, cok ? soff[jt] + sl_off : kOff, 2 * t0);
+        }
+      }
+    };
+    auto compute = [&](const Batch& R) {
+#pragma unroll
+      for (int bb = 0; bb < BS; ++bb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int p = lane + 64 * q;
+          *reinterpret_cast<u32x4_t*>(slab + (p >> 3) * GS + 8 * (p & 7)) = R.g[bb][q];
+        }
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          const u32x4_t a = read_tr8(slab, GS, 8 * kg, 16 * gi, i);
+#pragma unroll
+          for (int jt = 0; jt < JT; ++jt) {
+            acc[gi][jt] = mfma16x16x32(a, R.sh[bb][jt], acc[gi][jt]);
+            acc[gi][jt] = mfma16x16x32(a, R.sl[bb][jt], acc[gi][jt]);
           }
         }
       }
     };
 
-    u32x4_t G0[4], H0[JT], L0[JT], G1[4], H1[JT], L1[JT];
-    if (ns > 0) load_step(0, G0, H0, L0);
-    for (int64_t s = 0; s < ns; s += 2) {
-      if (s + 1 < ns) load_step(s + 1, G1, H1, L1);
-      mma_step(G0, H0, L0);
-      if (s + 1 < ns) {
-        if (s + 2 < ns) load_step(s + 2, G0, H0, L0);
-        mma_step(G1, H1, L1);
+    Batch R0, R1;
+    if (cnt > 0) load(0, R0);
+    for (int64_t u0 = 0; u0 < cnt; u0 += 2 * BS) {
+      if (u0 + BS < cnt) load(u0 + BS, R1);
+      compute(R0);
+      if (u0 + BS < cnt) {
+        if (u0 + 2 * BS < cnt) load(u0 + 2 * BS, R0);
+        compute(R1);
       }
     }
 
-    __syncthreads();  // every wave is done with its tile; reuse LDS for the sums
-    // D[g][j]: lane holds column j = lane % 16, rows 4 (lane / 16) + v
+    // D[g][j]: lane holds column j = 16 jt + lane % 16, rows 4 (lane / 16) + v
+    // of G-column tile gi; one tile's wave sums at a time
+    const int R = r - jc < RC ? r - jc : RC;
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi)
+    for (int gi = 0; gi < 4; ++gi) {
+      __syncthreads();  // slabs (first tile) or the last tile's sums are done
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
-        if (16 * jt < R)
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            red[(wave * 64 + 16 * gi + 4 * kg + v) * kGradRed + 16 * jt + i] = acc[gi][jt][v];
-    __syncthreads();
-    for (int e = threadIdx.x; e < 64 * R; e += 256) {
-      // consecutive threads write consecutive addresses of C
-      const int gl = J.transposed ? (e & 63) : e / R;
-      const int j = J.transposed ? (e >> 6) : e % R;
-      const float sum = ((red[(0 * 64 + gl) * kGradRed + j] + red[(1 * 64 + gl) * kGradRed + j]) +
-                         red[(2 * 64 + gl) * kGradRed + j]) +
-                        red[(3 * 64 + gl) * kGradRed + j];
-      const int64_t g = g0 + gl;
-      const int jo = jc + j;
-      float* c = J.transposed ? C + (int64_t)jo * ldg + g : C + g * r + jo;
-      *c = acc_out ? *c + sum : sum;
+        for (int v = 0; v < 4; ++v)
+          red[(wave * 16 + 4 * kg + v) * REDS + 16 * jt + i] = acc[gi][jt][v];
+      __syncthreads();
+      for (int e = t; e < 16 * R; e += kThreads) {
+        // consecutive threads write consecutive addresses of C
+        const int gl = J.transposed ? (e & 15) : e / R;
+        const int j = J.transposed ? (e >> 4) : e % R;
+        float sum = red[gl * REDS + j];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) sum += red[(w * 16 + gl) * REDS + j];
+        const int64_t g = g0 + 16 * gi + gl;
+        const int jo = jc + j;
+        float* c = J.transposed ? J.C + (int64_t)jo * ldg + g : J.C + g * r + jo;
+        *c = accumulate ? *c + sum : sum;
+      }
     }
-    __syncthreads();  // before the next chunk overwrites the tiles
+    __syncthreads();  // before the next chunk's slabs overwrite the sums
   }
-}
-
-// C (+)= sum_z Cp[z] (z in order), grid-stride over both jobs' outputs
-__global__ __launch_bounds__(256) void lora_grad_finalize_kernel(LoraGradJob j0, LoraGradJob j1,
-                                                                 int r, int accumulate,
-                                                                 int splits) {
-  const int64_t n0 = j0.ldg * r, total = n0 + j1.ldg * r;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const bool second = e >= n0;
-    const float* Cp = second ? j1.Cp : j0.Cp;
-    float* C = second ? j1.C : j0.C;
-    const int64_t n = second ? total - n0 : n0;
-    const int64_t ee = second ? e - n0 : e;
-    float v[16];
-#pragma unroll
-    for (int z = 0; z < 16; ++z) v[z] = z < splits ? Cp[(int64_t)z * n + ee] : 0.0f;
-    float sum = v[0];
-#pragma unroll
-    for (int z = 1; z < 16; ++z)
-      if (z < splits) sum += v[z];
-    C[ee] = accumulate ? C[ee] + sum : sum;
-  }
-}
-
-int lora_grad_splits(int64_t M, int64_t ldg0, int64_t ldg1) {
-  const int64_t blocks = ldg0 / 64 + ldg1 / 64;
-  const int64_t nst = pad32(M) / 32;
-  int64_t s = blocks > 0 ? (512 + blocks - 1) / blocks : 1;
-  if (s > nst / 4) s = nst / 4;  // at least one 32-token step per wave
-  if (s > kGradMaxSplits) s = kGradMaxSplits;
-  return s < 1 ? 1 : (int)s;
 }
 
 hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
-                            int accumulate, int splits, hipStream_t s) {
+                            int accumulate, hipStream_t s) {
   const int64_t b0 = j0.ldg / 64, b1 = j1.ldg / 64;
   if (b0 + b1 == 0 || r == 0) return hipSuccess;
-  const dim3 grid((unsigned)((b0 + b1) * splits));
+  const dim3 grid((unsigned)(b0 + b1));
   if (r <= 16)
-    hipLaunchKernelGGL(lora_grad_kernel<1>, grid, dim3(256), 0, s, j0, j1, b0 * splits, M, r,
-                       accumulate, splits);
+    hipLaunchKernelGGL(lora_grad_kernel<1>, grid, dim3(kThreads), 0, s, j0, j1, b0, M, r,
+                       accumulate);
   else if (r <= 32)
-    hipLaunchKernelGGL(lora_grad_kernel<2>, grid, dim3(256), 0, s, j0, j1, b0 * splits, M, r,
-                       accumulate, splits);
+    hipLaunchKernelGGL(lora_grad_kernel<2>, grid, dim3(kThreads), 0, s, j0, j1, b0, M, r,
+                       accumulate);
   else
-    hipLaunchKernelGGL(lora_grad_kernel<4>, grid, dim3(256), 0, s, j0, j1, b0 * splits, M, r,
-                       accumulate, splits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
-  int64_t g = ((j0.ldg + j1.ldg) * r + 255) / 256;
-  if (g > 2048) g = 2048;
-  hipLaunchKernelGGL(lora_grad_finalize_kernel, dim3((unsigned)g), dim3(256), 0, s, j0, j1, r,
-                     accumulate, splits);
+    hipLaunchKernelGGL(lora_grad_kernel<4>, grid, dim3(kThreads), 0, s, j0, j1, b0, M, r,
+                       accumulate);
   return hipGetLastError();
 }
 

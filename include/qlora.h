@@ -54,7 +54,8 @@ extern "C" {
 /* ---- status codes -------------------------------------------------------- */
 #define QLORA_OK          0
 #define QLORA_EINVAL     (-1) /* null pointer, negative size, aliasing        */
-#define QLORA_ESHAPE     (-2) /* K or N not a multiple of 64, r > 256 or r%8  */
+#define QLORA_ESHAPE     (-2) /* K or N not a multiple of 64, r > 256 or r%8,
+                                  or a tensor above 2 GiB (see below)          */
 #define QLORA_EALIGN     (-3) /* a device pointer is not 16-byte aligned      */
 #define QLORA_ENOTSUP    (-4) /* blocksize != 64 or blocksize2 != 256         */
 #define QLORA_EWORKSPACE (-5) /* workspace NULL or smaller than required      */
@@ -127,7 +128,9 @@ int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream)
  *   x  [M, K] bf16        A [r, K] bf16        B [N, r] bf16
  *   y  [M, N] bf16 output: y = x.deq(W)^T + (alpha/r).(x.A^T).B^T,
  *      accumulated in fp32 and rounded once to bf16 (nearest-even).
- * M >= 1 is arbitrary; N and K must be multiples of 64 (ESHAPE); r is 0 or
+ * M >= 1 is arbitrary; N and K must be multiples of 64 (ESHAPE), the
+ * packed codes (N*K/2 bytes) and x and y (M*K*2, M*N*2 bytes) at most
+ * 2 GiB each (ESHAPE: the kernels use 32-bit byte offsets); r is 0 or
  * a multiple of 8 up to 256 (r = 0: base only, A and B may be NULL).
  * workspace: device scratch of at least
  * qlora_linear_workspace_bytes(0, M, N, K, r) bytes, 256-byte aligned.      */
@@ -145,6 +148,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
  *   dB [N, r] fp32 output:  dB = (alpha/r).dy^T.(x.A^T)
  *   accumulate != 0 adds the new dA/dB to the existing contents.
  * r = 0: only dx is produced (A, B, dA, dB may be NULL).
+ * Shapes and size limits as for the forward pass (ESHAPE).
  * workspace: at least qlora_linear_workspace_bytes(1, M, N, K, r) bytes.    */
 int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
                      int64_t M, const uint16_t* A, const uint16_t* B, int32_t r,

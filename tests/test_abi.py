@@ -143,6 +143,9 @@ def test_fwd_validation():
     assert call(w=_weight(256, 256, codes=P0 + 1)) == -3
     assert call(r=12) == -2
     assert call(r=264) == -2
+    assert call(M=(1 << 22) + 1) == -2                        # x above 2 GiB
+    assert call(w=_weight(65536, 131072)) == -2               # codes above 2 GiB
+    assert q.workspace_bytes(0, (1 << 22) + 1, 256, 256, 8) == 0
     assert call(r=-8) == -1
     assert call(M=-1) == -1
     assert call(x=None) == -1
@@ -171,6 +174,7 @@ def test_bwd_validation():
     assert call(dA=None) == -1
     assert call(x=None) == -1
     assert call(r=4) == -2
+    assert call(M=(1 << 22) + 1) == -2                        # dy, x above 2 GiB
     assert call(dB=P4 + 196608 + 4) == -3
     assert call(ws=None) == -5
     assert call(dx=P3) == -1                                  # dx aliases x
