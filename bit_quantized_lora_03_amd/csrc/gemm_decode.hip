@@ -12,9 +12,10 @@
 //  * a block owns 32 weight rows over the whole reduction, so no partial
 //    sums leave the chip: the row's NF4 blocks are dealt to 16 slots (8
 //    waves x the two lane halves), lane (row l%32, half l/32) of wave w
-//    taking slot 2 w + l/32 of each chunk of 16 blocks.  The codes come in
-//    by DMA, two whole row pieces per instruction, into an LDS ring four
-//    chunks deep, so the weight is streamed in full cache lines.  For each block the lane builds the block's 16-entry bf16
+//    taking slot 2 w + l/32 of each chunk of 16 blocks.  Each wave brings
+//    in exactly the codes it decodes by DMA, into an LDS ring of its own
+//    six chunks deep, so waves never wait for one another until the final
+//    sum.  For each block the lane builds the block's 16-entry bf16
 //    table once and decodes its 64 codes into the A operands of 8
 //    consecutive MFMAs; the reduction order over k is permuted consistently
 //    for A and B (MFMA j of a block pair sums k = 64 b + 8 j + e, e = 0..7,
@@ -26,7 +27,8 @@
 //    banks -- about two thirds of the vector work of resolving codes with
 //    byte permutes in registers;
 //  * x is small and stays in L2: each token lane reads its 16-byte operand
-//    pieces directly, one chunk ahead;
+//    pieces directly, two chunks ahead (lanes past the M tokens read
+//    nothing: their offsets lie beyond x, which returns zeros);
 //  * the 8 waves' partial tiles are added in LDS in wave order.
 //
 // The adapter's down projection x . A^T rides along: rows of A (bf16, used
@@ -52,9 +54,10 @@ constexpr int WAVES = 8;    // waves per block
 constexpr int SLOTS = 2 * WAVES;  // NF4-block slots per weight row
 constexpr int SPAN = 128;   // k per span of the adapter tiles
 constexpr int kTabBytes = WAVES * 16 * 64 * 4;  // per-lane NF4 tables, 32 KiB
-constexpr int NSTAGE = 4;   // code chunks in the LDS ring
-constexpr int kStageU4 = 32 * 512 / 16;  // one chunk: 32 rows x 512 bytes
-constexpr int kLdsBytes = kTabBytes + NSTAGE * kStageU4 * 16;
+constexpr int NSTAGE = 6;   // code chunks in the LDS ring
+constexpr int kStageU4 = 32 * 64 / 16;  // one wave's chunk: 32 rows x its 2 blocks (64 bytes)
+constexpr int kLdsBytes = kTabBytes + WAVES * NSTAGE * kStageU4 * 16;
+constexpr int kXBytes = 32768;  // x staged in LDS when it fits (see decode_x_in_lds)
 
 // s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS
 // operations of this wave are outstanding (expcnt left free).
@@ -88,10 +91,12 @@ struct Blk {
 
 }  // namespace
 
+// XL: x lives in LDS for the whole reduction (few tokens; decode_x_in_lds)
+template <bool XL>
 __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p) {
-  // the tables are the kernel's only LDS (at offset 0, so a lookup address
+  // the tables start the kernel's LDS (at offset 0, so a lookup address
   // needs no base added); after the main loop the space holds the reduction
-  __shared__ __align__(16) uint8_t lds[kLdsBytes];
+  __shared__ __align__(16) uint8_t lds[kLdsBytes + (XL ? kXBytes : 0)];
 
   // Weight tiles take the first ids, A tiles the last: workgroups are
   // dispatched in id order, so the A tiles fill in as weight tiles finish
@@ -121,6 +126,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
   const bool row_ok = n < nrows;
   const bool tok_ok = lr < M;
   const uint16_t* xrow = p.x + (tok_ok ? lr : 0) * K;
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(p.x, (uint32_t)(M * K * 2));
 
   f32x16_t acc;
 #pragma unroll
@@ -138,31 +144,33 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
 
   if (!a_tile) {
     // The row's NF4 blocks go in chunks of 16 (1024 k); within a chunk lane
-    // (row l%32, half l/32) of wave w decodes block 2 w + l/32.  The codes
-    // reach LDS by DMA (buffer loads that write LDS directly) in a ring of
-    // NSTAGE chunks: each instruction moves 1 KiB, two whole 512-byte row
-    // pieces, so the weight stream is read in full cache lines (reading 16
-    // bytes per row per lane would touch 64 lines per instruction).  In a
-    // stage, row r's 16-byte piece c sits at r * 512 + 16 (c ^ (r % 16)), so
-    // the 16 rows one LDS read cycle serves hit 16 distinct bank groups.
-    // Scale bytes, steps and x pieces are per-lane loads into registers.
+    // (row l%32, half l/32) of wave w decodes block 2 w + l/32.  Each wave
+    // brings in exactly the codes it decodes -- its two blocks of the 32
+    // rows, 64 bytes per row and chunk -- by DMA (buffer loads that write
+    // LDS directly) into a ring of its own, NSTAGE chunks deep, so no wave
+    // waits for another: the main loop has no barrier.  (Together the 8
+    // waves read each row's 512-byte chunk piece.)  In a stage, row r's
+    // 16-byte piece p (0, 1: block 2 w; 2, 3: block 2 w + 1) sits at
+    // r * 64 + 16 (p ^ ((r / 4) % 4)), so the 16 rows one LDS read cycle
+    // serves cover all 64 banks.  Scale bytes, steps and x pieces are
+    // per-lane loads into registers.
     const int64_t nblk = K / 64;
     const int64_t nch = (nblk + 15) / 16;
     const int slot = 2 * wave + lg;
     const int64_t row_blk = ((row_ok ? n : 0) * K) >> 6;
     const __amdgpu_buffer_rsrc_t cres = make_rsrc(p.codes, (uint32_t)((N * K) >> 1));
-    uint32_t cvoff[2];  // instruction h fills rows 4 wave + 2 h + lane / 32
+    uint32_t cvoff[2];  // instruction h fills physical pieces 64 h + lane
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int r = 4 * wave + 2 * h + (lane >> 5);
-      const int c = (lane & 31) ^ (r & 15);
-      cvoff[h] = (uint32_t)((n0 + r) * (K >> 1) + 16 * c);
+      const int pc = 64 * h + lane, r = pc >> 2;
+      const int lp = (pc & 3) ^ ((r >> 2) & 3);
+      cvoff[h] = (uint32_t)((n0 + r) * (K >> 1) + 64 * wave + 16 * lp);
     }
     auto dma_codes = [&](u32x4_t* stage, int64_t ch) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            cres, (__attribute__((address_space(3))) void*)(stage + 64 * (2 * wave + h)), 16,
+            cres, (__attribute__((address_space(3))) void*)(stage + 64 * h), 16,
             cvoff[h] + (uint32_t)(ch * 512), 0, 0, 0);
     };
     struct Scale {
@@ -175,17 +183,28 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       S.q = p.qscale[row_blk + b];
       S.st = p.step[(row_blk + b) >> 8];
     };
-    auto xk = [&](int64_t ch) { return (blk_of(ch) < nblk ? blk_of(ch) : 0) * 64; };
+    // x pieces of the lane's block of chunk ch: 8 x 16 bytes of token lr.
+    // Lanes past the M tokens (and blocks past the row's end) get a lane
+    // offset beyond x, so their loads return zero without touching memory;
+    // the loads themselves are unconditional, so no branch makes the
+    // compiler's wait analysis assume they might be missing.
+    const uint32_t xrow_off = (uint32_t)(lr * K * 2);
+    auto load_xc = [&](int64_t ch, u32x4_t (&xb)[8]) {
+      const uint32_t off = (tok_ok && blk_of(ch) < nblk)
+                               ? xrow_off + (uint32_t)(blk_of(ch) * 128)
+                               : 0x80000000u;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xb[j] = buffer_load16(xres, off + 16 * j);
+    };
 
     uint16_t* tab_w = reinterpret_cast<uint16_t*>(lds) + wave * 2048 + lane * 2;
     const uint32_t wtag = (uint32_t)wave * 0x10101010u;  // wave in bits 4..7 of each code byte
     const uint32_t lane4 = (uint32_t)lane * 4u;
-    const int rsw = lr & 15;
-    auto decode_chunk = [&](const u32x4_t* stage, int64_t ch, const Scale& S,
-                            const u32x4_t (&xb)[8]) {
+    const int rsw = (lr >> 2) & 3;
+    auto decode_chunk = [&](const u32x4_t* stage, int64_t ch, const Scale& S, auto&& xop) {
       const bool ok = row_ok && blk_of(ch) < nblk;
-      const u32x4_t c0 = stage[lr * 32 + ((2 * slot) ^ rsw)];
-      const u32x4_t c1 = stage[lr * 32 + ((2 * slot + 1) ^ rsw)];
+      const u32x4_t c0 = stage[lr * 4 + ((2 * lg) ^ rsw)];
+      const u32x4_t c1 = stage[lr * 4 + ((2 * lg + 1) ^ rsw)];
       // this lane's block table: entry c = bf16_rne(fp32(L[c] * s'))
       const float sc = ok ? nf4_block_scale(S.q, S.st) : 0.0f;
 #pragma unroll
@@ -210,65 +229,164 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
         u32x4_t a;
 #pragma unroll
         for (int q = 0; q < 4; ++q) a[q] = h[2 * q] | (h[2 * q + 1] << 16);
-        acc = mfma32x32x16(a, xb[j], acc);
+        acc = mfma32x32x16(a, xop(j), acc);
       }
     };
 
-    // Issue order per chunk iteration: DMA of chunk + 3, its scales, x of
-    // chunk + 1 (a virtual iteration -1 issues DMA 2 and x 0 in the
-    // prologue).  The DMA of chunk + 1 is then complete once at most 26
-    // loads are outstanding at the end of an iteration (fewer than the 34
-    // issued after it in steady state; exactly 26 after the first one).
-    u32x4_t* const ring = reinterpret_cast<u32x4_t*>(lds + kTabBytes);
+    // Issue order.  The prologue loads x (of chunks 0 and 1, or -- with x
+    // in LDS -- every piece of x the wave will read), then the DMA and
+    // scales of chunks 0 .. NSTAGE - 2; iteration ch loads x of chunk
+    // ch + 2 (not with x in LDS), then issues the DMA of chunk
+    // ch + NSTAGE - 1 and its scales, decodes chunk ch and at its end waits
+    // for chunk ch + 1's DMA.  Loads complete in order, so a wait for x of
+    // chunk ch (issued first in iteration ch - 2) also waits for the DMAs
+    // issued before it, up to chunk ch + 2's: x comes two iterations ahead
+    // and first in its iteration so that this never forces a DMA earlier
+    // than three iterations after its issue (x in LDS takes x out of the
+    // count altogether).  The end-of-iteration wait is "at most W
+    // outstanding", W being the number of operations issued after chunk
+    // ch + 1's DMA; with kOps operations per iteration that is
+    // 2 + kOps (NSTAGE - 2) in the steady state (it was issued in iteration
+    // ch + 2 - NSTAGE) and, with x in registers, 26 + 8 ch while the DMA
+    // came from the prologue.  Waits are immediates, so W is a template
+    // argument: the first group of iterations gets its own, later groups the
+    // steady one, and a short reduction (fewer chunks than one group) the
+    // smallest, which waits at least as long as needed.
+    constexpr int kOps = XL ? 4 : 12;  // vector-memory operations per iteration
+    constexpr int kWaitSteady = 2 + kOps * (NSTAGE - 2);
+    static_assert(kWaitSteady <= 63, "vmcnt holds at most 63");
+    u32x4_t* const ring =
+        reinterpret_cast<u32x4_t*>(lds + kTabBytes) + wave * NSTAGE * kStageU4;
     Scale Sc[NSTAGE];
-    u32x4_t X[2][8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) X[u][j] = zero;
+    u32x4_t X[XL ? 1 : 3][8];
     const int64_t lastc = nch - 1;
     auto cl = [&](int64_t c) { return c < lastc ? c : lastc; };
+
+    // x in LDS: rows of 2K + 16 bytes (the pad puts consecutive tokens 4
+    // banks apart), then one 128-byte zero area per wave, read by lanes
+    // past the M tokens and for blocks past the row's end.  Each wave
+    // stages exactly the pieces it reads -- its two blocks of every chunk,
+    // for every token -- so no other wave's writes are involved: piece
+    // i = lane + 64 q is byte 16 (i mod 16) of block 16 ch + 2 w + (i mod
+    // 16) / 8, chunk ch = (i / 16) mod nch, token (i / 16) / nch.
+    uint8_t* const xl = lds + kLdsBytes;
+    const int64_t xrb = 2 * K + 16;
+    constexpr int kXq = 4;  // pieces per lane (the x budget bounds M K / 64 by 256)
+    u32x4_t xv[XL ? kXq : 1];
+    uint32_t xdst[XL ? kXq : 1];
+    if constexpr (XL) {
+      // 32-bit index math, every offset computed before the select, so the
+      // selects stay selects (a branch around the loads would make the
+      // compiler wait for each load before the next)
+      const uint32_t nch32 = (uint32_t)nch, m32 = (uint32_t)M, nblk32 = (uint32_t)nblk;
+      const uint32_t xrow_bytes = (uint32_t)(2 * K), xrb32 = (uint32_t)xrb;
+#pragma unroll
+      for (int q = 0; q < kXq; ++q) {
+        const uint32_t i = (uint32_t)(lane + 64 * q);
+        const uint32_t pc = i & 15u, rest = i >> 4;
+        const uint32_t tk = rest / nch32, c = rest - tk * nch32;
+        const uint32_t b = 16u * c + 2u * (uint32_t)wave + (pc >> 3);
+        const uint32_t col = 128u * b + 16u * (pc & 7u);
+        const bool ok = tk < m32 && b < nblk32;
+        const uint32_t src = tk * xrow_bytes + col, dst = tk * xrb32 + col;
+        xv[q] = buffer_load16(xres, ok ? src : 0x80000000u);
+        xdst[q] = ok ? dst : 0xFFFFFFFFu;
+      }
+    } else {
+      load_xc(0, X[0]);
+      load_xc(cl(1), X[1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < NSTAGE - 1; ++c) {
       dma_codes(ring + c * kStageU4, cl(c));
       load_scale(cl(c), Sc[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    load_x(xk(0), X[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(18, 0));
-    __builtin_amdgcn_s_barrier();
+    if constexpr (XL) {
+      // the wave's own pieces and zero area; its later reads follow in order
+#pragma unroll
+      for (int q = 0; q < kXq; ++q)
+        if (xdst[q] != 0xFFFFFFFFu) *reinterpret_cast<u32x4_t*>(xl + xdst[q]) = xv[q];
+      if (lane < 8) *reinterpret_cast<u32x4_t*>(xl + M * xrb + 128 * wave + 16 * lane) = zero;
+    }
+    // chunk 0's DMA: followed by its scales and NSTAGE - 2 DMA + scale pairs
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 + 4 * (NSTAGE - 2), 0));
 
-    auto iteration = [&](int64_t ch, auto phase, const u32x4_t* __restrict__ rd,
+    // x operand j of chunk ch from LDS: token lr's 16 bytes at k = 64 b + 8 j
+    auto x_lds = [&](int64_t ch) {
+      const int64_t b = blk_of(ch);
+      const uint32_t xa = (tok_ok && b < nblk) ? (uint32_t)(lr * xrb + 128 * b)
+                                                : (uint32_t)(M * xrb + 128 * wave);
+      return [=](int j) -> u32x4_t {
+        return *reinterpret_cast<const u32x4_t*>(xl + xa + 16 * j);
+      };
+    };
+
+    // phase = ch mod NSTAGE: the stage read (rd), the stage filled (fill),
+    // the scale set and the x set (ch mod 3) are then compile-time choices
+    auto iteration = [&](int64_t ch, auto phase, auto wait, const u32x4_t* __restrict__ rd,
                          u32x4_t* __restrict__ fill) {
       constexpr int ph = decltype(phase)::value;
-      dma_codes(fill, cl(ch + 3));
-      load_scale(cl(ch + 3), Sc[(ph + 3) % NSTAGE]);
-      __builtin_amdgcn_sched_barrier(0);
-      load_x(xk(cl(ch + 1)), X[(ph + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      decode_chunk(rd, ch, Sc[ph], X[ph & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(26, 0));
-      __builtin_amdgcn_s_barrier();
-    };
-    u32x4_t* const R0 = ring;
-    u32x4_t* const R1 = ring + kStageU4;
-    u32x4_t* const R2 = ring + 2 * kStageU4;
-    u32x4_t* const R3 = ring + 3 * kStageU4;
-    int64_t ch = 0;
-    for (; ch + 4 <= nch; ch += 4) {
-      iteration(ch, std::integral_constant<int, 0>(), R0, R3);
-      iteration(ch + 1, std::integral_constant<int, 1>(), R1, R0);
-      iteration(ch + 2, std::integral_constant<int, 2>(), R2, R1);
-      iteration(ch + 3, std::integral_constant<int, 3>(), R3, R2);
-    }
-    if (ch < nch) {
-      iteration(ch, std::integral_constant<int, 0>(), R0, R3);
-      if (ch + 1 < nch) {
-        iteration(ch + 1, std::integral_constant<int, 1>(), R1, R0);
-        if (ch + 2 < nch) iteration(ch + 2, std::integral_constant<int, 2>(), R2, R1);
+      constexpr int W = decltype(wait)::value;
+      static_assert(NSTAGE % 3 == 0, "x sets rotate with the phase");
+      if constexpr (!XL) {
+        load_xc(cl(ch + 2), X[(ph + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      dma_codes(fill, cl(ch + NSTAGE - 1));
+      load_scale(cl(ch + NSTAGE - 1), Sc[(ph + NSTAGE - 1) % NSTAGE]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (XL)
+        decode_chunk(rd, ch, Sc[ph], x_lds(ch));
+      else
+        decode_chunk(rd, ch, Sc[ph], [&](int j) -> u32x4_t { return X[ph % 3][j]; });
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(W, 0));
+    };
+    static_assert(NSTAGE == 6, "the loop below is unrolled for six stages");
+    u32x4_t* const R[NSTAGE] = {ring, ring + kStageU4, ring + 2 * kStageU4,
+                                ring + 3 * kStageU4, ring + 4 * kStageU4, ring + 5 * kStageU4};
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    using P3 = std::integral_constant<int, 3>;
+    using P4 = std::integral_constant<int, 4>;
+    using P5 = std::integral_constant<int, 5>;
+    // with x in LDS every iteration's count is the steady one
+    using W0 = std::integral_constant<int, XL ? kWaitSteady : 26>;
+    using W1 = std::integral_constant<int, XL ? kWaitSteady : 34>;
+    using W2 = std::integral_constant<int, XL ? kWaitSteady : 42>;
+    using WS = std::integral_constant<int, kWaitSteady>;
+    static_assert(XL || 26 + 8 * (NSTAGE - 3) == kWaitSteady,
+                  "iteration NSTAGE - 3 reaches the steady state");
+    if (nch >= 6) {
+      iteration(0, P0(), W0(), R[0], R[5]);
+      iteration(1, P1(), W1(), R[1], R[0]);
+      iteration(2, P2(), W2(), R[2], R[1]);
+      iteration(3, P3(), WS(), R[3], R[2]);
+      iteration(4, P4(), WS(), R[4], R[3]);
+      iteration(5, P5(), WS(), R[5], R[4]);
+      int64_t ch = 6;
+      for (; ch + 6 <= nch; ch += 6) {
+        iteration(ch, P0(), WS(), R[0], R[5]);
+        iteration(ch + 1, P1(), WS(), R[1], R[0]);
+        iteration(ch + 2, P2(), WS(), R[2], R[1]);
+        iteration(ch + 3, P3(), WS(), R[3], R[2]);
+        iteration(ch + 4, P4(), WS(), R[4], R[3]);
+        iteration(ch + 5, P5(), WS(), R[5], R[4]);
+      }
+      if (ch < nch) iteration(ch, P0(), WS(), R[0], R[5]);
+      if (ch + 1 < nch) iteration(ch + 1, P1(), WS(), R[1], R[0]);
+      if (ch + 2 < nch) iteration(ch + 2, P2(), WS(), R[2], R[1]);
+      if (ch + 3 < nch) iteration(ch + 3, P3(), WS(), R[3], R[2]);
+      if (ch + 4 < nch) iteration(ch + 4, P4(), WS(), R[4], R[3]);
+    } else {
+      iteration(0, P0(), W0(), R[0], R[5]);
+      if (1 < nch) iteration(1, P1(), W0(), R[1], R[0]);
+      if (2 < nch) iteration(2, P2(), W0(), R[2], R[1]);
+      if (3 < nch) iteration(3, P3(), W0(), R[3], R[2]);
+      if (4 < nch) iteration(4, P4(), W0(), R[4], R[3]);
     }
     // the clamped prefetches past the end are still writing LDS
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -419,6 +537,14 @@ int a_splits(int64_t K) {
 
 }  // namespace
 
+// x fits in LDS: M rows of 2K + 16 bytes plus the waves' zero areas, and
+// each wave's share (M tokens x its 16 pieces of every chunk) is at most
+// 4 pieces per lane.
+bool decode_x_in_lds(int64_t M, int64_t K) {
+  const int64_t nch = (K / 64 + 15) / 16;
+  return M * (2 * K + 16) + WAVES * 128 <= kXBytes && M * nch * 16 <= 64 * 4;
+}
+
 int decode_splits(int64_t M, int64_t N, int64_t K, int r) {
   (void)M;
   (void)N;
@@ -446,7 +572,12 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
   p.w_blocks = (N + 31) / 32;
   p.blocks = p.w_blocks + (r > 0 ? (int64_t)((r + 31) / 32) * p.sa : 0);
   p.L = L;
-  hipLaunchKernelGGL(decode_main_kernel, dim3((unsigned)p.blocks), dim3(WAVES * 64), 0, s, p);
+  if (decode_x_in_lds(M, K))
+    hipLaunchKernelGGL(decode_main_kernel<true>, dim3((unsigned)p.blocks), dim3(WAVES * 64), 0, s,
+                       p);
+  else
+    hipLaunchKernelGGL(decode_main_kernel<false>, dim3((unsigned)p.blocks), dim3(WAVES * 64), 0, s,
+                       p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || r == 0) return e;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((N + 31) / 32)), dim3(256), 0, s,
