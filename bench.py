@@ -8,7 +8,10 @@ already resident in HBM: NF4-quantise the fp32 base weight, double-quantise
 its block scales, run the fused forward (dequant-in-GEMM + LoRA) and the
 backward (dX through the frozen base, dA, dB).  The step is captured once
 in a HIP graph and replayed; K replays are timed between device
-synchronisations.  Rank 0 prints one JSON line.
+synchronisations.  The decode-shaped workloads rotate 16 weight copies
+(so each call reads its weight from HBM) and run forward only; their 16
+steps are also captured back to back in one graph, like consecutive
+layers, which is what is replayed.  Rank 0 prints one JSON line.
 
 value = algorithmic fwd+bwd flops per step / step time, in TFLOP/s.  The
 `roofline` object is for the dominant kernel, timed alone with HIP events
@@ -325,12 +328,33 @@ def main():
                 step(j)
             graphs.append(g)
         torch.cuda.synchronize()
+    # with rotating weights, one graph also holds all rot steps back to back
+    # (like consecutive layers): a replay per step would leave the GPU idle
+    # between graph launches when a step is only tens of microseconds
+    group = None
+    if graphs and rot > 1:
+        group = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(group):
+            for j in range(rot):
+                step(j)
+        torch.cuda.synchronize()
 
     def run(i):
         if graphs:
             graphs[i % rot].replay()
         else:
             step(i)
+
+    def run_steps(n):
+        # n consecutive steps starting at slot 0
+        i = 0
+        if group is not None:
+            while n - i >= rot:
+                group.replay()
+                i += rot
+        while i < n:
+            run(i)
+            i += 1
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -339,15 +363,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        run(i)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(args.steps):
-        run(i)
+    run_steps(args.steps)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

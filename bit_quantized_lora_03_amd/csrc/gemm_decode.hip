@@ -443,82 +443,119 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
 
 // y[m][n] = bf16( part[0][m][n] + scale * sum_j xa[m][j] B[n][j] ) with
 // xa[m][j] = sum_z part[z][m][N + j] (z < sa), fixed summation orders.
-// Block of 256 threads = 32 columns n x 8 lanes; lane g of a column holds
-// B[n][8 g .. 8 g + 7] (the 8 lanes read the 128-byte row whole), forms its
-// share of the r-sum for every token, and the shares are added by a fixed
-// butterfly over the 8 lanes.  The partial sums were written by the
-// previous kernel and are read from beyond L2, so all of a pass's loads are
-// issued before any is used.
+// The r-sum is a small matrix product, so it runs on MFMA like the fused
+// GEMMs' adapter columns: xa is split into bf16 hi + lo (hi + lo equals the
+// fp32 value to 2^-17), tokens as the 32 A rows, and B's rows -- 16-byte
+// pieces along j, as stored -- as the B columns.  Block of 256 threads, 128
+// columns n (32 per wave); the block first forms xa's hi/lo rows in LDS
+// (every block does: xa is M x r), with all of a pass's loads issued before
+// any is used.  Each lane's B pieces and base sums are loaded at the start,
+// so their latency overlaps that phase.  Loads go through buffer
+// descriptors (out-of-range offsets read zero), so no branch separates them.
 constexpr int kMaxASplits = 16;
+constexpr int kRedCols = 128;                   // columns per block
+constexpr int kXsRow = 256 + 8;  // LDS row of xa's hi or lo (bf16): r <= 256 + 16 bytes of pad
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part,
                                                             int sa,
                                                             const uint16_t* __restrict__ B,
                                                             int r, float scale,
                                                             uint16_t* __restrict__ y, int64_t M,
                                                             int64_t N) {
-  __shared__ float xa[32 * 256];
+  __shared__ __align__(16) uint16_t xs[2][kDecodeMaxM][kXsRow];
   const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int64_t ldp = N + r;
-  constexpr int EPT = 4;  // xa elements per thread per pass
-  const int total = (int)(M * r);
+  const int64_t n = (int64_t)blockIdx.x * kRedCols + 32 * wave + lr;  // this lane's column
+  const bool n_ok = n < N;
+  const int ks = (r + 15) / 16;                   // 16-wide MFMA steps over j
+  constexpr uint32_t kOut = 0x80000000u;          // past both tensors
+  const __amdgpu_buffer_rsrc_t pres =
+      make_rsrc(part, (uint32_t)((int64_t)sa * M * ldp * 4));
+  const __amdgpu_buffer_rsrc_t bres = make_rsrc(B, (uint32_t)(N * r * 2));
+
+  // B operand of step s: B[n][16 s + 8 lg .. + 7]
+  constexpr int kMaxSteps = 256 / 16;  // r <= 256
+  u32x4_t bop[kMaxSteps];
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSteps; ++s2) {
+    const int j = 16 * s2 + 8 * lg;
+    bop[s2] = buffer_load16(bres, (n_ok && j < r) ? (uint32_t)((n * r + j) * 2) : kOut);
+  }
+  // base sums of the tokens this lane's accumulators hold:
+  // rows 8 (v / 4) + 4 lg + v % 4 of the 32 x 32 tile
+  float base[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t m = 8 * (v >> 2) + 4 * lg + (v & 3);
+    base[v] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(
+                   pres, (n_ok && m < M) ? (int)((m * ldp + n) * 4) : (int)kOut, 0, 0));
+  }
+
+  // xa's hi/lo rows for tokens < M (j < 16 ks; zero past r), 4 per thread per pass
+  constexpr int EPT = 4;
+  const int cols = 16 * ks;
+  const int total = (int)M * cols;
   for (int e0 = t; e0 < total; e0 += 256 * EPT) {
     float v[EPT][kMaxASplits];
 #pragma unroll
     for (int u = 0; u < EPT; ++u) {
-      const int e = e0 + 256 * u < total ? e0 + 256 * u : 0;
-      const int64_t m = e / r, j = e - m * r;
-      const float* src = part + m * ldp + N + j;
+      const int e = e0 + 256 * u;
+      const int m = e / cols, j = e - m * cols;
+      const uint32_t off = (uint32_t)(((int64_t)m * ldp + N + j) * 4);
 #pragma unroll
-      for (int z = 0; z < kMaxASplits; ++z) v[u][z] = z < sa ? src[(int64_t)z * M * ldp] : 0.0f;
+      for (int z = 0; z < kMaxASplits; ++z) {
+        const bool ok = e < total && j < r && z < sa;
+        v[u][z] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       pres, ok ? (int)(off + (uint32_t)((int64_t)z * M * ldp * 4)) : (int)kOut,
+                       0, 0));
+      }
     }
 #pragma unroll
     for (int u = 0; u < EPT; ++u) {
-      float acc = 0.0f;
+      const int e = e0 + 256 * u;
+      float acc = v[u][0];
 #pragma unroll
-      for (int z = 0; z < kMaxASplits; ++z)
+      for (int z = 1; z < kMaxASplits; ++z)
         if (z < sa) acc += v[u][z];
-      if (e0 + 256 * u < total) xa[e0 + 256 * u] = acc;
+      if (e < total) {
+        const int m = e / cols, j = e - m * cols;
+        const uint16_t hi = __builtin_bit_cast(uint16_t, (__bf16)acc);
+        const uint16_t lo = __builtin_bit_cast(uint16_t, (__bf16)(acc - bf16_bits_to_f32(hi)));
+        xs[0][m][j] = hi;
+        xs[1][m][j] = lo;
+      }
     }
+  }
+  // token rows past M are zero
+  for (int e = (int)M * cols + t; e < kDecodeMaxM * cols; e += 256) {
+    const int m = e / cols, j = e - m * cols;
+    xs[0][m][j] = 0;
+    xs[1][m][j] = 0;
   }
   __syncthreads();
-  const int g = t & 7;                               // lane within the column
-  const int64_t n = (int64_t)blockIdx.x * 32 + (t >> 3);
-  const bool n_ok = n < N;
-  float sh[kDecodeMaxM];                             // this lane's share, per token
+
+  // D[token][n] = sum_j xa[token][j] B[n][j]: A = xa rows (lane: token lr,
+  // j = 16 s + 8 lg ..), B = this lane's B pieces; hi, then lo, per step
+  f32x16_t acc;
 #pragma unroll
-  for (int m = 0; m < kDecodeMaxM; ++m) sh[m] = 0.0f;
-  for (int jc = 8 * g; jc < r; jc += 64) {
-    const u32x4_t bv = n_ok ? *reinterpret_cast<const u32x4_t*>(B + n * r + jc) : u32x4_t{0, 0, 0, 0};
-    float b[8];
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      b[2 * e] = bf16_bits_to_f32(bv[e] & 0xFFFFu);
-      b[2 * e + 1] = bf16_bits_to_f32(bv[e] >> 16);
-    }
-#pragma unroll
-    for (int m = 0; m < kDecodeMaxM; ++m) {
-      if (m < M) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sh[m] += xa[m * r + jc + e] * b[e];
-      }
+  for (int s2 = 0; s2 < kMaxSteps; ++s2) {
+    if (s2 < ks) {
+      const u32x4_t ahi = *reinterpret_cast<const u32x4_t*>(&xs[0][lr][16 * s2 + 8 * lg]);
+      const u32x4_t alo = *reinterpret_cast<const u32x4_t*>(&xs[1][lr][16 * s2 + 8 * lg]);
+      acc = mfma32x32x16(ahi, bop[s2], acc);
+      acc = mfma32x32x16(alo, bop[s2], acc);
     }
   }
-  // butterfly over the 8 lanes of the column (a fixed order)
-#pragma unroll
-  for (int d = 1; d < 8; d <<= 1) {
-#pragma unroll
-    for (int m = 0; m < kDecodeMaxM; ++m)
-      if (m < M) sh[m] += __shfl_xor(sh[m], d, 8);
-  }
-  // lane g stores tokens g, g + 8, ...
   if (n_ok) {
 #pragma unroll
-    for (int m0 = 0; m0 < kDecodeMaxM; m0 += 8) {
-      const int m = m0 + g;
-      if (m < M) {
-        const float acc = part[m * ldp + n] + scale * sh[m];
-        y[m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)acc);
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = 8 * (v >> 2) + 4 * lg + (v & 3);
+      if (m < M)
+        y[m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(base[v] + scale * acc[v]));
     }
   }
 }
@@ -580,8 +617,8 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
                        p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || r == 0) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((N + 31) / 32)), dim3(256), 0, s,
-                     part, p.sa, B, r, scale, y, M, N);
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((N + kRedCols - 1) / kRedCols)),
+                     dim3(256), 0, s, part, p.sa, B, r, scale, y, M, N);
   return hipGetLastError();
 }
 
