@@ -562,11 +562,11 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restr
 
 namespace {
 
-// k splits of the adapter's A tiles, which run after the weight tiles:
-// pieces of about 2048 k (at most 16), few enough that the reduction reads
-// few partial planes
+// k splits of the adapter's A tiles, which run after the weight tiles as
+// CUs free up: pieces of about 512 k (at most 16, the planes the reduction
+// reads), so each takes about one memory round trip
 int a_splits(int64_t K) {
-  int64_t s = K / 2048;
+  int64_t s = K / 512;
   if (s > kMaxASplits) s = kMaxASplits;
   if (s < 1) s = 1;
   return (int)s;
