@@ -417,7 +417,7 @@ def main():
         ach = kb / (k_fwd * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBPS, "traffic": None,
-                "kernel": "decode_main_kernel + decode_reduce_kernel (base only)",
+                "kernel": "decode_main_kernel (base only)",
                 "per_launch": kb, "duration_ms": k_fwd}
         key = "decode"
     else:

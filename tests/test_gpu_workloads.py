@@ -79,3 +79,20 @@ def test_split_tail_schedules_128_token_tiles(cuda):
     ways (the last sampled row, M - 1, lies in a tail tile of both)."""
     _check_layer(workloads.layer(3200, 2816, 3072, 16, 32.0, seed=21, name="tail128",
                                  outlier_frac=0.001))
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 256, 7872, 8),     # x staged in LDS; 123 NF4 blocks: last chunk ragged
+    (3, 256, 5248, 16),    # x would fit in LDS, but a wave's share exceeds 4 pieces per lane
+    (1, 320, 15808, 24),   # largest K with x in LDS at M = 1: 16 chunks (groups of 6 + 4)
+    (8, 192, 1088, 64),    # x in LDS, 17 blocks in 2 chunks, 6 row tiles
+    (32, 128, 2048, 0),    # most tokens the decode path takes, no adapter
+    (7, 128, 6208, 40),    # x in registers, 97 blocks: ragged chunk and ragged rank steps
+], ids=lambda s: "x".join(map(str, s)))
+def test_decode_path_edges(cuda, shape):
+    """Few-token forward (M <= 32): both ways of feeding x (staged in LDS when
+    M rows of x fit, else per-lane loads), ragged reductions, row tiles and
+    ranks, against the oracle on every token."""
+    M, N, K, r = shape
+    _check_layer(workloads.layer(M, N, K, r, 16.0, seed=31, name=f"decode_{M}x{N}x{K}x{r}"),
+                 with_bwd=False)
