@@ -62,6 +62,40 @@ __device__ __forceinline__ u32x4_t ldb(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
                                                                            (int)soff, 0));
 }
 
+// The job a block works on is picked by comparing blockIdx with a kernel
+// argument, which is the same for every lane, but the compiler cannot tell:
+// a buffer descriptor built from a value it takes to differ between lanes
+// gets a readfirstlane loop around every load.  Reading each field through
+// readfirstlane states that it is uniform.
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  return reinterpret_cast<T*>(uniform64(reinterpret_cast<uint64_t>(p)));
+}
+__device__ __forceinline__ LoraProjJob uniform_job(const LoraProjJob& j) {
+  LoraProjJob u;
+  u.X = uniform_ptr(j.X);
+  u.Y = uniform_ptr(j.Y);
+  u.out = uniform_ptr(j.out);
+  u.outT = uniform_ptr(j.outT);
+  u.Kred = (int64_t)uniform64((uint64_t)j.Kred);
+  u.kmajor = __builtin_amdgcn_readfirstlane(j.kmajor);
+  return u;
+}
+__device__ __forceinline__ LoraGradJob uniform_job(const LoraGradJob& j) {
+  LoraGradJob u;
+  u.G = uniform_ptr(j.G);
+  u.ST = uniform_ptr(j.ST);
+  u.C = uniform_ptr(j.C);
+  u.ldg = (int64_t)uniform64((uint64_t)j.ldg);
+  u.transposed = __builtin_amdgcn_readfirstlane(j.transposed);
+  return u;
+}
+
 // 8 bf16 of one slab column: rows row0 .. row0 + 7 (as two transpose reads,
 // rows row0 + 4h + c/4 addressed by lane c of the 16-lane group), column
 // col0 + lane % 16.  `stride` is the slab row length in bf16.
@@ -75,6 +109,13 @@ __device__ __forceinline__ u32x4_t read_tr8(const uint16_t* slab, int stride, in
   const u32x2_t h0 = __builtin_bit_cast(u32x2_t, r0), h1 = __builtin_bit_cast(u32x2_t, r1);
   const u32x4_t v = {h0[0], h0[1], h1[0], h1[1]};
   return v;
+}
+
+// Two packed bf16 as the dot-product operand.  The word is taken by value:
+// __builtin_bit_cast applied to a vector element (x[i]) reads the vector's
+// first word whatever the index, with this compiler.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) {
+  return __builtin_bit_cast(bf16x2_t, v);
 }
 
 // Store the bf16 pair of v for (m, j) in both layouts (m < Mp; rows past M
@@ -116,9 +157,11 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   constexpr int SLAB_BYTES = kWaves * SLAB * 2, RED_BYTES = kWaves * 16 * REDS * 4;
   __shared__ __align__(16) char lds[SLAB_BYTES > RED_BYTES ? SLAB_BYTES : RED_BYTES];
 
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int t = threadIdx.x, lane = t & 63;
+  // the wave index, stated uniform (scalar offsets are built from it)
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const bool second = (int64_t)blockIdx.x >= blocks0;
-  const LoraProjJob J = second ? j1 : j0;
+  const LoraProjJob J = uniform_job(second ? j1 : j0);
   const int64_t b = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
   const int jchunks = (r + RC - 1) / RC;
   const int64_t m0 = 16 * (b / jchunks);
@@ -145,25 +188,30 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
     u32x4_t x[BS];
     u32x4_t y[BS][JT];
   };
+  // Lane offsets of the Y pieces, fixed for the whole loop (kOff past r).
+  // Steps past the wave's count OR in kOff: a select the compiler keeps as
+  // one (a branch around the loads would make it wait for each load).
+  uint32_t yoff[JT];
+#pragma unroll
+  for (int q = 0; q < JT; ++q) {
+    if (!kmajor) {
+      const int jj = jc + 16 * q + i;
+      yoff[q] = jj < r ? (uint32_t)jj * (uint32_t)Kred * 2u + 16u * (uint32_t)kg : kOff;
+    } else {
+      const int p = lane + 64 * q, row = p / (2 * JT), col = jc + 8 * (p % (2 * JT));
+      yoff[q] = col < r ? (uint32_t)(row * r + col) * 2u : kOff;
+    }
+  }
   auto load = [&](int64_t u0, Batch& R) {
 #pragma unroll
     for (int bb = 0; bb < BS; ++bb) {
       const int64_t u = u0 + bb;
-      const bool ok = u < cnt;
+      const uint32_t past = u < cnt ? 0u : kOff;
       const uint32_t k0 = (uint32_t)(32 * (wave + kWaves * u));
-      R.x[bb] = ldb(xres, ok ? xoff : kOff, 2 * k0);
+      R.x[bb] = ldb(xres, xoff | past, 2 * k0);
 #pragma unroll
-      for (int q = 0; q < JT; ++q) {
-        if (!kmajor) {
-          const int jj = jc + 16 * q + i;
-          R.y[bb][q] = ldb(yres, (ok && jj < r) ? (uint32_t)((jj * Kred + 8 * kg) * 2) : kOff,
-                           2 * k0);
-        } else {
-          const int p = lane + 64 * q, row = p / (2 * JT), col = jc + 8 * (p % (2 * JT));
-          R.y[bb][q] = ldb(yres, (ok && col < r) ? (uint32_t)((row * r + col) * 2) : kOff,
-                           2 * k0 * (uint32_t)r);
-        }
-      }
+      for (int q = 0; q < JT; ++q)
+        R.y[bb][q] = ldb(yres, yoff[q] | past, kmajor ? 2 * k0 * (uint32_t)r : 2 * k0);
     }
   };
   // steps past the wave's count carry zero operands and add nothing
@@ -217,10 +265,141 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   }
 }
 
+// ---------------------------------------------------------------------------
+// lora_proj_small: the same product when M r is small (few tokens and a
+// small rank).  With 16 x 16 MFMA tiles such a job has only M / 16 blocks,
+// and each has to pull in a whole 16-row slice of x plus all of Y; here a
+// block owns 8 tokens x 8 rank columns (so M r / 64 blocks, each reading
+// 16 rows) and the whole reduction.  Its 256 threads take the 8-wide pieces
+// of the reduction t, t + 256, ... and accumulate with v_dot2_f32_bf16
+// (two bf16 products added into an fp32 sum, no conversions).  B's pieces
+// (8 rank columns of one k) are turned into (k, k + 1) pairs of one column
+// with one v_perm per pair.  The 256 threads' sums are added in LDS in a
+// fixed order, then by a fixed butterfly over 4 lanes.
+// ---------------------------------------------------------------------------
+constexpr int kSmallT = 8, kSmallR = 8;  // tokens, rank columns per block
+constexpr int kSmallRed = 65;            // LDS row of a thread's 64 sums (+1: no bank conflicts)
+
+__global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, LoraProjJob j1,
+                                                              int64_t blocks0, int64_t M, int r,
+                                                              float scale) {
+  __shared__ float red[256 * kSmallRed];
+  const int t = threadIdx.x;
+  const bool second = (int64_t)blockIdx.x >= blocks0;
+  const LoraProjJob J = uniform_job(second ? j1 : j0);
+  const int64_t b = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
+  const int rg = r / kSmallR;
+  const int64_t m0 = kSmallT * (b / rg);
+  const int jc = (int)(b % rg) * kSmallR;
+  const int64_t Kred = J.Kred;
+  const int64_t npc = Kred / 8;  // 8-wide pieces of the reduction
+  const int64_t cnt = npc > t ? (npc - t + 255) / 256 : 0;
+  const bool kmajor = J.kmajor != 0;
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(J.X, (uint32_t)(M * Kred * 2));
+  const __amdgpu_buffer_rsrc_t yres = make_rsrc(J.Y, (uint32_t)((int64_t)r * Kred * 2));
+  // rows past M lie past x's end and read as zero
+  uint32_t xoff[kSmallT];
+#pragma unroll
+  for (int i = 0; i < kSmallT; ++i) xoff[i] = (uint32_t)((m0 + i) * Kred * 2);
+
+  float acc[kSmallT][kSmallR];
+#pragma unroll
+  for (int i = 0; i < kSmallT; ++i)
+#pragma unroll
+    for (int j = 0; j < kSmallR; ++j) acc[i][j] = 0.0f;
+
+  // piece u of this thread: k = 8 (t + 256 u) .. + 7; x rows, then Y: A's
+  // rows jc .. jc + 7 (kmajor == 0) or B's rows k .. k + 7 (kmajor == 1)
+  struct Piece {
+    u32x4_t x[kSmallT];
+    u32x4_t y[kSmallR];
+  };
+  // Every offset here differs between lanes, so all of it is lane offset.
+  // Pieces past the thread's count OR in kOff: a select the compiler keeps
+  // as one (a branch around the loads would make it wait for each load).
+  uint32_t ybase[kSmallR];
+#pragma unroll
+  for (int q = 0; q < kSmallR; ++q)
+    ybase[q] = kmajor ? (uint32_t)(q * r + jc) * 2u : (uint32_t)(jc + q) * (uint32_t)Kred * 2u;
+  auto load = [&](int64_t u, Piece& P) {
+    const uint32_t past = u < cnt ? 0u : kOff;
+    const uint32_t pc = (uint32_t)(t + 256 * u);  // 8-wide piece index
+#pragma unroll
+    for (int i = 0; i < kSmallT; ++i) P.x[i] = ldb(xres, (xoff[i] + 16u * pc) | past, 0);
+#pragma unroll
+    for (int q = 0; q < kSmallR; ++q)
+      P.y[q] = ldb(yres, (ybase[q] + (kmajor ? 16u * (uint32_t)r * pc : 16u * pc)) | past, 0);
+  };
+
+  auto compute = [&](const Piece& P) {
+    u32x4_t yp[kSmallR];  // column q's (k, k + 1) pairs
+#pragma unroll
+    for (int q = 0; q < kSmallR; ++q) {
+      if (!kmajor) {
+        yp[q] = P.y[q];
+      } else {
+        // column q sits in dword q / 2 of each B row piece, half q % 2
+        const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+          yp[q][pp] = perm(P.y[2 * pp + 1][q >> 1], P.y[2 * pp][q >> 1], sel);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSmallT; ++i)
+#pragma unroll
+      for (int q = 0; q < kSmallR; ++q)
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+          acc[i][q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(P.x[i][pp]), as_bf16x2(yp[q][pp]),
+                                                      acc[i][q], false);
+  };
+  Piece P0, P1;
+  if (cnt > 0) load(0, P0);
+  for (int64_t u = 0; u < cnt; u += 2) {
+    if (u + 1 < cnt) load(u + 1, P1);
+    compute(P0);
+    if (u + 1 < cnt) {
+      if (u + 2 < cnt) load(u + 2, P0);
+      compute(P1);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < kSmallT; ++i)
+#pragma unroll
+    for (int q = 0; q < kSmallR; ++q) red[t * kSmallRed + i * kSmallR + q] = acc[i][q];
+  __syncthreads();
+  // output o = t / 4: its 256 sums, lane t % 4 taking every fourth
+  const int o = t >> 2, part = t & 3;
+  float sum = red[part * kSmallRed + o];
+  for (int tt = part + 4; tt < 256; tt += 4) sum += red[tt * kSmallRed + o];
+  sum += __shfl_xor(sum, 1, 4);
+  sum += __shfl_xor(sum, 2, 4);
+  const int64_t Mp = pad32(M);
+  const int64_t mo = m0 + o / kSmallR;
+  const int jo = jc + o % kSmallR;
+  if (part == 0 && mo < Mp && jo < r) put_split(J, M, r, mo, jo, scale * sum);
+}
+
+// small jobs (few tokens x a small rank) go to lora_proj_small: measured
+// faster at q_proj (M = 512, r = 16), slower at M = 2048, r = 16
+static bool proj_small(int64_t M, int r) { return M * r <= 16384; }
+
 static int proj_jt(int r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
 
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                             float scale, hipStream_t s) {
+  if (proj_small(M, r)) {
+    // Mp / 8 token groups cover every row of the transposed copy
+    const int64_t per_job = (pad32(M) / kSmallT) * (r / kSmallR);
+    const LoraProjJob jb = j1 ? *j1 : j0;
+    const int64_t total = per_job * (j1 ? 2 : 1);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(lora_proj_small_kernel, dim3((unsigned)total), dim3(256), 0, s, j0, jb,
+                       per_job, M, r, scale);
+    return hipGetLastError();
+  }
   const int jt = proj_jt(r);
   const int rc = 16 * jt;
   // Mp / 16 token blocks cover every row of the transposed copy
@@ -263,9 +442,11 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
   constexpr int SLAB_BYTES = kWaves * SLAB * 2, RED_BYTES = kWaves * 16 * REDS * 4;
   __shared__ __align__(16) char lds[SLAB_BYTES > RED_BYTES ? SLAB_BYTES : RED_BYTES];
 
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int t = threadIdx.x, lane = t & 63;
+  // the wave index, stated uniform (scalar offsets are built from it)
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const bool second = (int64_t)blockIdx.x >= blocks0;
-  const LoraGradJob J = second ? j1 : j0;
+  const LoraGradJob J = uniform_job(second ? j1 : j0);
   const int64_t ldg = J.ldg;
   const int64_t g0 = 64 * (second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x);
   const int i = lane & 15, kg = lane >> 4;

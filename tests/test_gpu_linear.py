@@ -28,7 +28,7 @@ SHAPES = [
     (5, 128, 192, 256, 8.0),
     (70, 448, 640, 0, 1.0),
     # the two adapter down-projections of the backward (over K and over N)
-    # get different k splits: N >> K and N << K
+    # with very different reduction lengths: N >> K and N << K
     (200, 4096, 512, 32, 64.0),
     (96, 256, 4096, 16, 32.0),
 ]
@@ -134,10 +134,20 @@ def test_one_hot_probes_are_bit_exact(cuda):
     assert np.array_equal(dx, wbits[ns, :])
 
 
-def test_zero_base_isolates_the_adapter_path(cuda):
-    """W = 0: y is the adapter term alone, tested at its own scale."""
-    L = _layer(129, 256, 512, 16, 32.0)
-    L.w_override = lambda: np.zeros((256, 512), dtype=np.float32)
+@pytest.mark.parametrize("shape", [
+    (129, 256, 512, 16, 32.0),    # few outputs: 8 x 8 tiles, bf16 dot products
+    (40, 192, 1024, 24, 48.0),    # ... three rank groups, ragged tokens
+    (33, 256, 2048, 128, 16.0),   # ... sixteen rank groups
+    (2304, 320, 448, 16, 32.0),   # more outputs: 16 x 16 MFMA tiles
+    (600, 128, 384, 64, 16.0),    # ... four 16-column groups per block
+], ids=[str(s) for s in [(129, 256, 512, 16), (40, 192, 1024, 24), (33, 256, 2048, 128),
+                         (2304, 320, 448, 16), (600, 128, 384, 64)]])
+def test_zero_base_isolates_the_adapter_path(cuda, shape):
+    """W = 0: y and dX are the adapter terms alone (x.A^T and dy.B through
+    both down-projection kernels), tested at their own scale, with dA, dB."""
+    M, N, K, r, alpha = shape
+    L = _layer(M, N, K, r, alpha)
+    L.w_override = lambda: np.zeros((N, K), dtype=np.float32)
     ol = OracleLayer(L.w)
     assert np.all(ol.w_deq == 0)
     check_close("y(W=0)", _run_fwd(L, ol), _ref_fwd(L, ol))
@@ -145,6 +155,8 @@ def test_zero_base_isolates_the_adapter_path(cuda):
     rdx, rdA, rdB = oracle.lora_linear_bwd(L.f32("x"), L.f32("dy"), ol.w_deq, L.f32("A"),
                                            L.f32("B"), L.alpha)
     check_close("dX(W=0)", dx, rdx)
+    check_close("dA(W=0)", dA, rdA)
+    check_close("dB(W=0)", dB, rdB)
 
 
 def test_deterministic(cuda):
