@@ -14,6 +14,9 @@ What it computes (numpy, fp64 unless a step fixes another precision):
   dequantisation to bf16.
 * ``lora_linear`` -- the layer y = x.W'^T + (alpha/r).(x.A^T).B^T and its
   gradients dX, dA, dB on the decoded weight W'.
+* ``merge`` -- the adapter merged into a base weight for export,
+  W_m = W_base + (alpha/r).B.A (fp32 and bf16 exports, re-quantisation, and
+  the errors of the three ways to export).
 
 Sources are cited by page title and section.  The pages state the format in
 words only; every reading taken where they are silent is written at the
@@ -43,3 +46,4 @@ from .nf4 import (  # noqa: F401
     storage_bits_per_weight,
 )
 from .lora_linear import lora_linear_fwd, lora_linear_bwd, lora_scale  # noqa: F401
+from .merge import merge_adapter, merged_bf16_bits, requantize, merge_errors  # noqa: F401

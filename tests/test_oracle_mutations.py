@@ -11,9 +11,11 @@ import pytest
 
 import oracle
 import oracle.lora_linear as ol
+import oracle.merge as om
 import oracle.nf4 as on
 from tests import test_oracle_levels as tl
 from tests import test_oracle_linear as tlin
+from tests import test_oracle_merge as tm
 from tests import test_oracle_quant as tq
 
 
@@ -93,7 +95,32 @@ def _fwd_wrong_sign(x, w, A, B, alpha):
     return _ORIG["fwd"](x, w, A, B, -alpha)
 
 
+def _merge_transposed(w_base, A, B, alpha):
+    d = _ORIG["merge"](np.zeros_like(np.asarray(w_base, dtype=np.float64)), A, B, alpha)
+    return np.asarray(w_base, dtype=np.float64) + d.T
+
+
+def _merge_scale_r_over_alpha(w_base, A, B, alpha):
+    r = 0 if A is None else np.asarray(A).shape[0]
+    return _ORIG["merge"](w_base, A, B, r * r / alpha if r else alpha)
+
+
+def _merged_bf16_from_f64(w_m):
+    # one rounding straight from fp64 (no fp32 step)
+    v = np.asarray(w_m, dtype=np.float64)
+    hi = v.astype(np.float32).view(np.uint32).astype(np.uint64) & 0xFFFF0000
+    lo_v = hi.astype(np.uint32).view(np.float32).astype(np.float64)
+    up = (hi + 0x10000).astype(np.uint32).view(np.float32).astype(np.float64)
+    lo_c, up_c = np.minimum(lo_v, up), np.maximum(lo_v, up)
+    pick_up = (np.abs(v - up_c) < np.abs(v - lo_c)) | (
+        (np.abs(v - up_c) == np.abs(v - lo_c)) & ((up_c.astype(np.float32).view(np.uint32)
+                                                   >> 16) % 2 == 0))
+    out = np.where(pick_up, up_c, lo_c).astype(np.float32)
+    return (out.view(np.uint32) >> 16).astype(np.uint16)
+
+
 _ORIG = {
+    "merge": om.merge_adapter,
     "thr": on.nf4_thresholds_f32,
     "dq": on.double_quant,
     "bwd": ol.lora_linear_bwd,
@@ -129,6 +156,12 @@ CASES = [
      tlin.test_zero_base_with_identity_adapters_is_scaled_copy),
     ("adapter term subtracted", [(oracle, "lora_linear_fwd", _fwd_wrong_sign)],
      lambda: tlin.test_forward_equals_triple_loop(3, 5, 7, 2, 4.0)),
+    ("merge adds (B.A)^T", [(oracle, "merge_adapter", _merge_transposed)],
+     lambda: tm.test_merge_equals_triple_loop(4, 4, 1, 1.0)),
+    ("merge scaled by r/alpha", [(oracle, "merge_adapter", _merge_scale_r_over_alpha)],
+     tm.test_one_entry_update_lands_at_row_of_B_column_of_A),
+    ("bf16 export rounded from fp64", [(oracle, "merged_bf16_bits", _merged_bf16_from_f64)],
+     tm.test_bf16_export_rounds_through_fp32_to_nearest_even),
 ]
 
 
