@@ -69,6 +69,14 @@ def quant_bytes(N, K):
     return 4 * n + n // 2 + 4 * nb + (4 * nb + nb + 4 * math.ceil(nb / 256))
 
 
+def merge_bytes(N, K, r, nf4):
+    """Algorithmic HBM bytes of one merge launch with both exports: the base
+    (packed NF4 with its scales, or fp32), A and B once, fp32 + bf16 out."""
+    n = N * K
+    base = packed_weight_bytes(N, K) if nf4 else 4 * n
+    return base + 2 * r * (N + K) + 6 * n
+
+
 def make_layer(name):
     from bit_quantized_lora_03_amd import workloads as wl
     if name == "linear256_m16_r8":
@@ -131,7 +139,7 @@ def _source_digest(key):
     """Hash of the kernel sources a recorded traffic figure was taken with."""
     import hashlib
     files = {"fwd": ["gemm_fwd.hip"], "dx": ["gemm_bwd.hip", "gemm_fwd.hip"],
-             "decode": ["gemm_decode.hip"]}[key] + ["device_common.h"]
+             "decode": ["gemm_decode.hip"], "merge": ["merge.hip"]}[key] + ["device_common.h"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "bit_quantized_lora_03_amd", "csrc", f), "rb") as fh:
@@ -421,17 +429,45 @@ def main():
                 "per_launch": kb, "duration_ms": k_fwd}
         key = "decode"
     else:
-        name, t_k, fl, sp = ("fwd_gemm_kernel", k_fwd, 2 * M * N * K, fsched)
+        name, t_k, fl, sched = ("fwd_gemm_kernel", k_fwd, 2 * M * N * K, fsched)
         key = "fwd"
         if "bwd" in kind and k_dx > k_fwd:
-            name, t_k, fl, sp = ("dx_gemm_kernel", k_dx, 2 * M * N * K, dsched)
+            name, t_k, fl, sched = ("dx_gemm_kernel", k_dx, 2 * M * N * K, dsched)
             key = "dx"
-        name += _schedule_label(sp)
+        name += _schedule_label(sched)
         ach = fl / (t_k * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "kernel": name + " (base only)",
                 "per_launch": fl, "duration_ms": t_k}
     roof["traffic"] = _recorded_traffic(args.workload, key)
+
+    # ---- adapter merge for export (not part of the step): W_m = W + s.B.A,
+    # fp32 and bf16 exports, from the NF4 base and from the fp32 original ----
+    merge = None
+    if r:
+        mf = torch.empty((N, K), dtype=torch.float32, device=dev)
+        mb = torch.empty((N, K), dtype=torch.int16, device=dev)
+        wt0 = weights[0][3]
+
+        def merge_call(nf4):
+            check(lib.qlora_merge_adapter(ctypes.byref(wt0) if nf4 else None,
+                                          None if nf4 else P(w_d), N, K, P(A_d), P(B_d), r,
+                                          alpha, P(mf), P(mb), sp()), "merge")
+
+        mreps = max(5, min(reps, 20))
+        t_nf4 = timed(lambda i: merge_call(True), mreps)
+        t_w0 = timed(lambda i: merge_call(False), mreps)
+        b_nf4 = merge_bytes(N, K, r, True)
+        b_w0 = merge_bytes(N, K, r, False)
+        ach = b_nf4 / (t_nf4 * 1e-3) / 1e9
+        merge = {"nf4_base_ms": round(t_nf4, 5), "w0_base_ms": round(t_w0, 5),
+                 "w0_base_GBps": round(b_w0 / (t_w0 * 1e-3) / 1e9, 1),
+                 "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+                              "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+                              "traffic": _recorded_traffic(args.workload, "merge"),
+                              "kernel": "merge_kernel (NF4 base, fp32 + bf16 out)",
+                              "per_launch": b_nf4, "duration_ms": round(t_nf4, 5)}}
+        del mf, mb
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -456,6 +492,7 @@ def main():
         "weight_GBps": round(wbytes / (ms_step * 1e-3) / 1e9, 2),
         "roofline": roof,
         "ops": {k: round(v, 5) for k, v in ops.items()},
+        "merge": merge,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "step_s"},
         "wall_s": round(wall, 4),
     }

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     lib,
     linear_bwd,
     linear_fwd,
+    merge_adapter,
     nf4_levels,
     quantize_nf4,
     quantize_nf4_dq,

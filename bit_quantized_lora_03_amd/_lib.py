@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "QLORA_OK", -1: "QLORA_EINVAL", -2: "QLORA_ESHAPE", -3: "QLOR
 EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
            "qlora_dequantize_nf4",
            "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_workspace_bytes",
-           "qlora_nf4_levels", "qlora_status_string")
+           "qlora_merge_adapter", "qlora_nf4_levels", "qlora_status_string")
 
 
 class QloraError(RuntimeError):
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         "qlora_linear_bwd": ([wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, i32, vp, sz, vp],
                              ctypes.c_int),
         "qlora_linear_workspace_bytes": ([i32, i64, i64, i64, i32], sz),
+        "qlora_merge_adapter": ([wp, vp, i64, i64, vp, vp, i32, f32, vp, vp, vp], ctypes.c_int),
         "qlora_nf4_levels": ([vp, vp], ctypes.c_int),
         "qlora_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
@@ -230,3 +231,31 @@ def linear_bwd(pw: PackedWeight, x, dy, A, B, alpha: float, need_dx: bool = True
                                  _ptr(ws), need if workspace is None else ws.numel(),
                                  _stream_ptr()), "qlora_linear_bwd")
     return dx, dA, dB
+
+
+def merge_adapter(base, A, B, alpha: float, out_f32: bool = True, out_bf16: bool = True,
+                  requantize: bool = False):
+    """W_m = W_base + (alpha/r).B.A for export.  ``base`` is a PackedWeight
+    (merge into the decoded 4-bit base) or an fp32 [N, K] device tensor (the
+    original weights).  Returns ``(fp32 [N, K] or None, bf16 bits [N, K]
+    (int16) or None, PackedWeight or None)``; the last is the fp32 merge
+    quantised again (``requantize=True``; needs the fp32 output)."""
+    torch = _torch()
+    if requantize and not out_f32:
+        raise ValueError("requantize needs the fp32 merge")
+    packed = isinstance(base, PackedWeight)
+    if packed:
+        N, K, device = base.N, base.K, base.codes.device
+    else:
+        N, K = base.shape
+        device = base.device
+    r = 0 if A is None else A.shape[0]
+    f = torch.empty((N, K), dtype=torch.float32, device=device) if out_f32 else None
+    b = torch.empty((N, K), dtype=torch.int16, device=device) if out_bf16 else None
+    s = base.struct() if packed else None
+    check(lib().qlora_merge_adapter(ctypes.byref(s) if packed else None,
+                                    None if packed else base.data_ptr(), N, K, _ptr(A),
+                                    _ptr(B), r, float(alpha), _ptr(f), _ptr(b),
+                                    _stream_ptr()), "qlora_merge_adapter")
+    q = quantize_weight(f) if requantize else None
+    return f, b, q

@@ -398,4 +398,47 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
   }
 }
 
+int qlora_merge_adapter(const qlora_nf4_weight* w, const float* w0, int64_t N, int64_t K,
+                        const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                        float* out_f32, uint16_t* out_bf16, void* stream) {
+  try {
+    if ((w == nullptr) == (w0 == nullptr)) return QLORA_EINVAL;
+    if (!out_f32 && !out_bf16) return QLORA_EINVAL;
+    int st = check_rank(r);
+    if (st != QLORA_OK) return st;
+    if (N <= 0 || K <= 0) return QLORA_EINVAL;
+    if (w) {
+      if ((st = check_weight(w)) != QLORA_OK) return st;
+      if (w->N != N || w->K != K) return QLORA_ESHAPE;
+    }
+    if (N % 64 || K % 64) return QLORA_ESHAPE;
+    // B is read through 32-bit buffer offsets; everything else is addressed
+    // with 64-bit pointers (N * K bounded only to keep the sizes below exact)
+    if (N * r * 2 >= kMaxTensorBytes || N > (int64_t{1} << 40) / K) return QLORA_ESHAPE;
+    if (r > 0 && (!A || !B)) return QLORA_EINVAL;
+    if ((w0 && !aligned16(w0)) || (out_f32 && !aligned16(out_f32)) ||
+        (out_bf16 && !aligned16(out_bf16)) || (r > 0 && (!aligned16(A) || !aligned16(B))))
+      return QLORA_EALIGN;
+    const size_t n = (size_t)N * (size_t)K;
+    const size_t nf = out_f32 ? n * 4 : 0, nb = out_bf16 ? n * 2 : 0;
+    const size_t na = r > 0 ? (size_t)r * K * 2 : 0, nB = r > 0 ? (size_t)N * r * 2 : 0;
+    const void* ins[5] = {w0, A, B, w ? w->codes : nullptr, w ? w->qscale : nullptr};
+    const size_t in_bytes[5] = {w0 ? n * 4 : 0, na, nB, w ? n / 2 : 0, w ? n / 64 : 0};
+    for (int i = 0; i < 5; ++i)
+      if (overlap(out_f32, nf, ins[i], in_bytes[i]) || overlap(out_bf16, nb, ins[i], in_bytes[i]))
+        return QLORA_EINVAL;
+    if (w && (overlap(out_f32, nf, w->dq_step, (n / 64 + 255) / 256 * 4) ||
+              overlap(out_bf16, nb, w->dq_step, (n / 64 + 255) / 256 * 4)))
+      return QLORA_EINVAL;
+    if (overlap(out_f32, nf, out_bf16, nb)) return QLORA_EINVAL;
+    const float scale = r > 0 ? alpha / (float)r : 0.0f;
+    return hip_status(qlora::launch_merge(w ? w->codes : nullptr, w ? w->qscale : nullptr,
+                                          w ? w->dq_step : nullptr, w0, A, B, r, scale,
+                                          out_f32, out_bf16, N, K, levels_arg(),
+                                          as_stream(stream)));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
 }  // extern "C"

@@ -99,4 +99,20 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
                           uint16_t* dx, float* part, int64_t M, int64_t N, int64_t K, int r,
                           const Nf4Levels& L, hipStream_t s);
 
+// merge.hip -- W_m = W_base + scale . B . A for export.  The base is the NF4
+// weight (codes non-null) or the fp32 original w0; out_f32 and/or out_bf16
+// [N, K]; N, K multiples of 64, N * r * 2 < 2^31.  One wave per 64-column
+// strip of K and `tiles_per_wave` 32-row tiles of N.
+constexpr int64_t kMergeTargetWaves = 4096;
+struct MergePlan {
+  int tiles_per_wave;
+  int64_t waves;
+  int64_t blocks;  // 4 waves each
+};
+MergePlan merge_plan(int64_t N, int64_t K);
+hipError_t launch_merge(const uint8_t* codes, const uint8_t* qscale, const float* step,
+                        const float* w0, const uint16_t* A, const uint16_t* B, int r,
+                        float scale, float* out_f32, uint16_t* out_bf16, int64_t N, int64_t K,
+                        const Nf4Levels& L, hipStream_t s);
+
 }  // namespace qlora

@@ -156,6 +156,34 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
                      int32_t accumulate, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/* Merge the adapter into a base weight for export:
+ *     W_m = W_base + (alpha/r) . B . A          ([N, K], row-major)
+ * [QLoRA -- the democratization event, deployment note]: a merged model is
+ * made by dequantising the base, merging the adapter, and possibly
+ * quantising again.  [QLoRA / infivelines.com, the recipe's last step]:
+ * merging into the 4-bit base and saving it loses precision twice; merge
+ * against the original weights.  [QLoRA, and fine-tuning a 7B model on a
+ * free GPU, "Merging a QLoRA adapter"]: merging into the full-precision
+ * base is the usual practice.
+ *   Base: exactly one of
+ *     w   the NF4 weight, decoded exactly as qlora_dequantize_nf4 does
+ *         (w->N == N and w->K == K), or
+ *     w0  [N, K] fp32 original weights (e.g. the quantiser's input).
+ *   A [r, K] bf16, B [N, r] bf16; r is 0 or a multiple of 8 up to 256
+ *     (r = 0: W_m = W_base, A and B may be NULL).
+ *   out_f32  [N, K] fp32:  fl32(W_base + s.U), one rounding, where U is the
+ *            fp32 sum of the exact products B[n][j] * A[j][k] and
+ *            s = fp32(alpha / r); may be NULL.
+ *   out_bf16 [N, K] bf16:  that fp32 value rounded to nearest even; may be
+ *            NULL.  At least one output must be given (EINVAL).
+ *   To quantise the merge again, pass out_f32 to qlora_quantize_nf4_dq.
+ * N and K must be multiples of 64 and N * r * 2 < 2^31 (ESHAPE).  Device
+ * pointers, 16-byte aligned (EALIGN); outputs must not overlap each other
+ * or the inputs (EINVAL).  No workspace.                                   */
+int qlora_merge_adapter(const qlora_nf4_weight* w, const float* w0, int64_t N, int64_t K,
+                        const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                        float* out_f32, uint16_t* out_bf16, void* stream);
+
 /* Workspace bytes for op 0 (forward) or 1 (backward) at the given shape;
  * 0 for an invalid shape.  Host-only; never touches the GPU.               */
 size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,

@@ -180,3 +180,34 @@ def test_bwd_validation():
     assert call(dx=P3) == -1                                  # dx aliases x
     assert call(dA=P4 + 65536) == -1                          # dA overlaps dx
     assert call(dB=P4 + (1 << 19)) == -1                      # dB inside workspace
+
+
+def test_merge_validation():
+    L = q.lib()
+    w = _weight(256, 256)
+    P5 = 64 << 20  # outputs far from every input
+    base = dict(w=w, w0=None, N=256, K=256, A=P4, B=P4 + 8192, r=8, f=P5, b=P5 + (1 << 20))
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.qlora_merge_adapter(ctypes.byref(a["w"]) if a["w"] is not None else None,
+                                     a["w0"], a["N"], a["K"], a["A"], a["B"], a["r"], 16.0,
+                                     a["f"], a["b"], None)
+    assert call(w=None) == -1                                 # no base
+    assert call(w0=P3) == -1                                  # two bases
+    assert call(f=None, b=None) == -1                         # no output
+    assert call(r=12) == -2
+    assert call(r=-8) == -1
+    assert call(A=None) == -1
+    assert call(N=320) == -2                                  # N differs from w's
+    assert call(w=None, w0=P3, N=250) == -2
+    assert call(w=None, w0=P3, K=250) == -2
+    assert call(w=None, w0=P3, N=(1 << 22), r=256) == -2      # B above 2 GiB
+    assert call(w=None, w0=P3 + 4) == -3
+    assert call(f=P5 + 8) == -3
+    assert call(b=P5 + (1 << 20) + 2) == -3
+    assert call(B=P4 + 8) == -3
+    assert call(b=P5 + 4096) == -1                            # bf16 out overlaps fp32 out
+    assert call(f=P0) == -1                                   # fp32 out over the codes
+    assert call(w=None, w0=P3, f=P3 + 4096) == -1             # fp32 out over w0
+    assert call(b=P4) == -1                                   # bf16 out over A
