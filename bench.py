@@ -69,6 +69,11 @@ def quant_bytes(N, K):
     return 4 * n + n // 2 + 4 * nb + (4 * nb + nb + 4 * math.ceil(nb / 256))
 
 
+def _wbits(w):
+    from bit_quantized_lora_03_amd import workloads
+    return workloads.to_bf16_bits(w)
+
+
 def merge_bytes(N, K, r, nf4):
     """Algorithmic HBM bytes of one merge launch with both exports: the base
     (packed NF4 with its scales, or fp32), A and B once, fp32 + bf16 out."""
@@ -441,6 +446,43 @@ def main():
                 "per_launch": fl, "duration_ms": t_k}
     roof["traffic"] = _recorded_traffic(args.workload, key)
 
+    # ---- the same layer on an unquantised bf16 weight (same kernels, no
+    # dequantisation): the pages compare QLoRA training with LoRA on a 16-bit
+    # base.  Training quantises once, so the ratio is over fwd + bwd only.
+    # The same-shape torch bf16 GEMM (hipBLASLt) is context, not a target.
+    unq = None
+    if kind != "fwd":
+        Wq = to_dev(_wbits(L.w))
+
+        need16 = max(q.workspace_bytes(2, M, N, K, r), q.workspace_bytes(3, M, N, K, r), 256)
+        ws16 = torch.empty(need16, dtype=torch.uint8, device=dev)
+
+        def fwd16():
+            check(lib.qlora_linear_bf16_fwd(P(Wq), N, K, P(x_d), M, P(A_d), P(B_d), r, alpha,
+                                            P(y), P(ws16), ws16.numel(), sp()), "bf16 fwd")
+
+        def bwd16():
+            check(lib.qlora_linear_bf16_bwd(P(Wq), N, K, P(x_d), P(dy_d), M, P(A_d), P(B_d), r,
+                                            alpha, P(dx), P(dA), P(dB), 0, P(ws16), ws16.numel(),
+                                            sp()), "bf16 bwd")
+        t_f16 = timed(lambda i: fwd16(), reps)
+        t_b16 = timed(lambda i: bwd16(), reps)
+        t_f4 = timed(lambda i: fwd(0), reps)
+        t_b4 = timed(lambda i: bwd(), reps)
+        xb, Wt = x_d.view(torch.bfloat16), Wq.view(torch.bfloat16)
+        dyb = dy_d.view(torch.bfloat16)
+        t_lt_f = timed(lambda i: torch.matmul(xb, Wt.t()), reps)
+        t_lt_d = timed(lambda i: torch.matmul(dyb, Wt), reps)
+        unq = {"nf4_fwd_ms": round(t_f4, 5), "nf4_bwd_ms": round(t_b4, 5),
+               "bf16_fwd_ms": round(t_f16, 5), "bf16_bwd_ms": round(t_b16, 5),
+               "ratio_fwd_bwd": round((t_f4 + t_b4) / (t_f16 + t_b16), 4),
+               "torch_bf16_gemm_fwd_ms": round(t_lt_f, 5),
+               "torch_bf16_gemm_dx_ms": round(t_lt_d, 5),
+               # base-only fused NF4 GEMM calls against the library's bf16 GEMM
+               "nf4_fwd_gemm_over_torch": round(k_fwd / t_lt_f, 4),
+               "nf4_dx_gemm_over_torch": round(k_dx / t_lt_d, 4)}
+        del Wq, ws16
+
     # ---- adapter merge for export (not part of the step): W_m = W + s.B.A,
     # fp32 and bf16 exports, from the NF4 base and from the fp32 original ----
     merge = None
@@ -492,6 +534,7 @@ def main():
         "weight_GBps": round(wbytes / (ms_step * 1e-3) / 1e9, 2),
         "roofline": roof,
         "ops": {k: round(v, 5) for k, v in ops.items()},
+        "vs_unquantised": unq,
         "merge": merge,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "step_s"},
         "wall_s": round(wall, 4),

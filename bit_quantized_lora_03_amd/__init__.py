@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     dequantize,
     double_quant,
     lib,
+    linear_bf16_bwd,
+    linear_bf16_fwd,
     linear_bwd,
     linear_fwd,
     merge_adapter,

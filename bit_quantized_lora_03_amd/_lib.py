@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "QLORA_OK", -1: "QLORA_EINVAL", -2: "QLORA_ESHAPE", -3: "QLOR
 EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
            "qlora_dequantize_nf4",
            "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_workspace_bytes",
+           "qlora_linear_bf16_fwd", "qlora_linear_bf16_bwd",
            "qlora_merge_adapter", "qlora_nf4_levels", "qlora_status_string")
 
 
@@ -64,6 +65,10 @@ def lib() -> ctypes.CDLL:
                              ctypes.c_int),
         "qlora_linear_workspace_bytes": ([i32, i64, i64, i64, i32], sz),
         "qlora_merge_adapter": ([wp, vp, i64, i64, vp, vp, i32, f32, vp, vp, vp], ctypes.c_int),
+        "qlora_linear_bf16_fwd": ([vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, sz, vp],
+                                  ctypes.c_int),
+        "qlora_linear_bf16_bwd": ([vp, i64, i64, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, i32,
+                                   vp, sz, vp], ctypes.c_int),
         "qlora_nf4_levels": ([vp, vp], ctypes.c_int),
         "qlora_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
@@ -230,6 +235,46 @@ def linear_bwd(pw: PackedWeight, x, dy, A, B, alpha: float, need_dx: bool = True
                                  float(alpha), _ptr(dx), _ptr(dA), _ptr(dB), int(accumulate),
                                  _ptr(ws), need if workspace is None else ws.numel(),
                                  _stream_ptr()), "qlora_linear_bwd")
+    return dx, dA, dB
+
+
+def linear_bf16_fwd(W, x, A, B, alpha: float, y=None, workspace=None):
+    """The same layer on an unquantised bf16 weight W [N, K] (bf16 or int16
+    bit patterns): y = x.W^T + (alpha/r).(x.A^T).B^T."""
+    torch = _torch()
+    N, K = W.shape
+    M = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    ws, need = _ws(2, M, N, K, r, x.device, workspace)
+    check(lib().qlora_linear_bf16_fwd(_ptr(W), N, K, _ptr(x), M, _ptr(A), _ptr(B), r,
+                                      float(alpha), _ptr(y), _ptr(ws),
+                                      need if workspace is None else ws.numel(), _stream_ptr()),
+          "qlora_linear_bf16_fwd")
+    return y
+
+
+def linear_bf16_bwd(W, x, dy, A, B, alpha: float, need_dx: bool = True, dA=None, dB=None,
+                    accumulate: bool = False, workspace=None):
+    """Backward of :func:`linear_bf16_fwd`: (dx or None, dA fp32 or None,
+    dB fp32 or None)."""
+    torch = _torch()
+    N, K = W.shape
+    M = dy.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dx = torch.empty((M, K), dtype=dy.dtype, device=dy.device) if need_dx else None
+    if r > 0:
+        if dA is None:
+            dA = torch.empty((r, K), dtype=torch.float32, device=dy.device)
+        if dB is None:
+            dB = torch.empty((N, r), dtype=torch.float32, device=dy.device)
+    ws, need = _ws(3, M, N, K, r, dy.device, workspace)
+    check(lib().qlora_linear_bf16_bwd(_ptr(W), N, K, _ptr(x), _ptr(dy), M, _ptr(A), _ptr(B), r,
+                                      float(alpha), _ptr(dx), _ptr(dA), _ptr(dB),
+                                      int(accumulate), _ptr(ws),
+                                      need if workspace is None else ws.numel(), _stream_ptr()),
+          "qlora_linear_bf16_bwd")
     return dx, dA, dB
 
 

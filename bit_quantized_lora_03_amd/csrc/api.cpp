@@ -65,6 +65,15 @@ int check_weight(const qlora_nf4_weight* w) {
   return QLORA_OK;
 }
 
+// Validate a bf16 weight [N, K] of the unquantised layer.
+int check_bf16_weight(const uint16_t* W, int64_t N, int64_t K) {
+  if (!W) return QLORA_EINVAL;
+  if (N <= 0 || K <= 0) return QLORA_EINVAL;
+  if (N % 64 || K % 64) return QLORA_ESHAPE;
+  if (!aligned16(W)) return QLORA_EALIGN;
+  return QLORA_OK;
+}
+
 // The kernels address every tensor with 32-bit byte offsets (buffer loads):
 // the packed codes and each activation tensor must stay within 2 GiB.
 constexpr int64_t kMaxTensorBytes = int64_t{1} << 31;
@@ -88,9 +97,10 @@ struct FwdWs {
   size_t gpart;  // fp32 partials of the fused GEMM's schedule (0: none)
   bool decode;   // few tokens: split-K decode path
 };
-FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+// nf4: the few-token decode path exists for the NF4 weight only
+FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool nf4 = true) {
   FwdWs L{};
-  L.decode = M <= qlora::kDecodeMaxM;
+  L.decode = nf4 && M <= qlora::kDecodeMaxM;
   if (M == 0) return L;
   if (L.decode) {
     // with an adapter: fp32 sums of x . W'^T and k-split partials of
@@ -149,6 +159,144 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
+// The base weight of a linear call: the NF4 weight, or a bf16 one (the
+// unquantised comparison layer).
+struct Wref {
+  const uint8_t* codes;
+  const uint8_t* qscale;
+  const float* step;
+  const uint16_t* wbf;
+  int64_t N, K;
+  bool nf4() const { return wbf == nullptr; }
+  const void* data() const { return nf4() ? static_cast<const void*>(codes) : wbf; }
+  size_t bytes() const { return nf4() ? (size_t)N * K / 2 : (size_t)N * K * 2; }
+};
+
+int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
+             int32_t r, float alpha, uint16_t* y, void* workspace, size_t ws_bytes,
+             void* stream) {
+  try {
+    int st = QLORA_OK;
+    if ((st = check_rank(r)) != QLORA_OK) return st;
+    if (M < 0) return QLORA_EINVAL;
+    const int64_t N = w->N, K = w->K;
+    if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
+    if (M == 0) return QLORA_OK;
+    if (!x || !y) return QLORA_EINVAL;
+    if (r > 0 && (!A || !B)) return QLORA_EINVAL;
+    if (!aligned16(x) || !aligned16(y) || (r > 0 && (!aligned16(A) || !aligned16(B))))
+      return QLORA_EALIGN;
+    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4());
+    if (ws.total > 0) {
+      if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
+    }
+    const size_t ny = (size_t)M * N * 2;
+    if (overlap(y, ny, x, (size_t)M * K * 2) || overlap(y, ny, w->data(), w->bytes()) ||
+        (r > 0 && (overlap(y, ny, A, (size_t)r * K * 2) || overlap(y, ny, B, (size_t)N * r * 2))) ||
+        (ws.total > 0 && overlap(y, ny, workspace, ws.total)))
+      return QLORA_EINVAL;
+
+    hipStream_t s = as_stream(stream);
+    const Nf4Levels L = levels_arg();
+    const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+    if (ws.decode) {
+      return hip_status(qlora::launch_decode_fwd(
+          w->codes, w->qscale, w->step, x, A, B, r, scale,
+          ws.total > 0 ? at<float>(workspace, ws.part_off) : nullptr, ws.dsplits, y, M, N, K, L,
+          s));
+    }
+    uint16_t* xs = nullptr;
+    if (r > 0) {
+      xs = at<uint16_t>(workspace, ws.xs_off);
+      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), K, 0};
+      if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s))) !=
+          QLORA_OK)
+        return st;
+    }
+    float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
+    return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->step, w->wbf, x, xs, B, y,
+                                             part, M, N, K, r, L, s));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
+int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, const uint16_t* A,
+             const uint16_t* B, int32_t r, float alpha, uint16_t* dx, float* dA, float* dB,
+             int32_t accumulate, void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    int st = QLORA_OK;
+    if ((st = check_rank(r)) != QLORA_OK) return st;
+    if (M < 0) return QLORA_EINVAL;
+    const int64_t N = w->N, K = w->K;
+    if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
+    if (M == 0) {
+      // a sum over no tokens: dA = dB = 0 (or unchanged when accumulating)
+      if (r == 0) return QLORA_OK;
+      if (!dA || !dB) return QLORA_EINVAL;
+      if (!aligned16(dA) || !aligned16(dB)) return QLORA_EALIGN;
+      if (overlap(dA, (size_t)r * K * 4, dB, (size_t)N * r * 4)) return QLORA_EINVAL;
+      // the gradient kernel with no tokens writes zeros (or adds nothing)
+      const qlora::LoraGradJob jb{nullptr, nullptr, dB, N, 0}, ja{nullptr, nullptr, dA, K, 1};
+      return hip_status(qlora::launch_lora_grad(jb, ja, 0, r, accumulate, as_stream(stream)));
+    }
+    if (!dy) return QLORA_EINVAL;
+    if (r > 0 && (!A || !B || !x || !dA || !dB)) return QLORA_EINVAL;
+    if (!aligned16(dy) || (dx && !aligned16(dx)) ||
+        (r > 0 && (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
+                   !aligned16(dB))))
+      return QLORA_EALIGN;
+    const BwdWs ws = bwd_layout(M, N, K, r);
+    if (ws.total > 0) {
+      if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
+    }
+    // outputs must not overlap inputs, the workspace or each other
+    const size_t nxb = (size_t)M * K * 2, nyb = (size_t)M * N * 2, nab = (size_t)r * K * 4,
+                 nbb = (size_t)N * r * 4;
+    const void* ins[] = {x, dy, A, B, w->data(), workspace};
+    const size_t in_sz[] = {nxb, nyb, (size_t)r * K * 2, (size_t)N * r * 2, w->bytes(),
+                            ws.total};
+    void* outs[] = {dx, r > 0 ? dA : nullptr, r > 0 ? dB : nullptr};
+    const size_t out_sz[] = {nxb, nab, nbb};
+    for (int o = 0; o < 3; ++o) {
+      for (int i = 0; i < 6; ++i)
+        if (overlap(outs[o], out_sz[o], ins[i], in_sz[i])) return QLORA_EINVAL;
+      for (int o2 = o + 1; o2 < 3; ++o2)
+        if (overlap(outs[o], out_sz[o], outs[o2], out_sz[o2])) return QLORA_EINVAL;
+    }
+    hipStream_t s = as_stream(stream);
+
+    const Nf4Levels L = levels_arg();
+    uint16_t* gs = nullptr;
+    if (r > 0) {
+      uint16_t* xs = at<uint16_t>(workspace, ws.xs_off);
+      gs = at<uint16_t>(workspace, ws.gs_off);
+      const float scale = alpha / static_cast<float>(r);
+      // xs = split(s . x . A^T), gs = split(s . dy . B) in one launch
+      uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
+      uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
+      const qlora::LoraProjJob jx{x, A, xs, xsT, K, 0}, jg{dy, B, gs, gsT, N, 1};
+      if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, s))) != QLORA_OK)
+        return st;
+      // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x
+      const qlora::LoraGradJob jb{dy, xsT, dB, N, 0}, ja{x, gsT, dA, K, 1};
+      if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, s))) != QLORA_OK)
+        return st;
+    }
+    if (dx) {
+      float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
+      if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->step, w->wbf, dy, gs,
+                                                 A, dx, part, M, N, K, r, L, s))) != QLORA_OK)
+        return st;
+    }
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,7 +332,8 @@ size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
       check_sizes(M, N, K) != QLORA_OK)
     return 0;
   if (op == 0) return fwd_layout(M, N, K, r).total;
-  if (op == 1) return bwd_layout(M, N, K, r).total;
+  if (op == 1 || op == 3) return bwd_layout(M, N, K, r).total;
+  if (op == 2) return fwd_layout(M, N, K, r, false).total;
   return 0;
 }
 
@@ -273,129 +422,41 @@ int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream)
 int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, const uint16_t* A,
                      const uint16_t* B, int32_t r, float alpha, uint16_t* y, void* workspace,
                      size_t ws_bytes, void* stream) {
-  try {
-    int st = check_weight(w);
-    if (st != QLORA_OK) return st;
-    if ((st = check_rank(r)) != QLORA_OK) return st;
-    if (M < 0) return QLORA_EINVAL;
-    const int64_t N = w->N, K = w->K;
-    if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
-    if (M == 0) return QLORA_OK;
-    if (!x || !y) return QLORA_EINVAL;
-    if (r > 0 && (!A || !B)) return QLORA_EINVAL;
-    if (!aligned16(x) || !aligned16(y) || (r > 0 && (!aligned16(A) || !aligned16(B))))
-      return QLORA_EALIGN;
-    const FwdWs ws = fwd_layout(M, N, K, r);
-    if (ws.total > 0) {
-      if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
-      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
-    }
-    const size_t ny = (size_t)M * N * 2;
-    if (overlap(y, ny, x, (size_t)M * K * 2) || overlap(y, ny, w->codes, (size_t)N * K / 2) ||
-        (r > 0 && (overlap(y, ny, A, (size_t)r * K * 2) || overlap(y, ny, B, (size_t)N * r * 2))) ||
-        (ws.total > 0 && overlap(y, ny, workspace, ws.total)))
-      return QLORA_EINVAL;
-
-    hipStream_t s = as_stream(stream);
-    const Nf4Levels L = levels_arg();
-    const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-    if (ws.decode) {
-      return hip_status(qlora::launch_decode_fwd(
-          w->codes, w->qscale, w->dq_step, x, A, B, r, scale,
-          ws.total > 0 ? at<float>(workspace, ws.part_off) : nullptr, ws.dsplits, y, M, N, K, L,
-          s));
-    }
-    uint16_t* xs = nullptr;
-    if (r > 0) {
-      xs = at<uint16_t>(workspace, ws.xs_off);
-      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), K, 0};
-      if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s))) !=
-          QLORA_OK)
-        return st;
-    }
-    float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
-    return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->dq_step, x, xs, B, y, part,
-                                             M, N, K, r, L, s));
-  } catch (...) {
-    return QLORA_EHIP;
-  }
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  return fwd_impl(&wr, x, M, A, B, r, alpha, y, workspace, ws_bytes, stream);
 }
 
 int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t M,
                      const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* dx,
                      float* dA, float* dB, int32_t accumulate, void* workspace, size_t ws_bytes,
                      void* stream) {
-  try {
-    int st = check_weight(w);
-    if (st != QLORA_OK) return st;
-    if ((st = check_rank(r)) != QLORA_OK) return st;
-    if (M < 0) return QLORA_EINVAL;
-    const int64_t N = w->N, K = w->K;
-    if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
-    if (M == 0) {
-      // a sum over no tokens: dA = dB = 0 (or unchanged when accumulating)
-      if (r == 0) return QLORA_OK;
-      if (!dA || !dB) return QLORA_EINVAL;
-      if (!aligned16(dA) || !aligned16(dB)) return QLORA_EALIGN;
-      if (overlap(dA, (size_t)r * K * 4, dB, (size_t)N * r * 4)) return QLORA_EINVAL;
-      // the gradient kernel with no tokens writes zeros (or adds nothing)
-      const qlora::LoraGradJob jb{nullptr, nullptr, dB, N, 0}, ja{nullptr, nullptr, dA, K, 1};
-      return hip_status(qlora::launch_lora_grad(jb, ja, 0, r, accumulate, as_stream(stream)));
-    }
-    if (!dy) return QLORA_EINVAL;
-    if (r > 0 && (!A || !B || !x || !dA || !dB)) return QLORA_EINVAL;
-    if (!aligned16(dy) || (dx && !aligned16(dx)) ||
-        (r > 0 && (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
-                   !aligned16(dB))))
-      return QLORA_EALIGN;
-    const BwdWs ws = bwd_layout(M, N, K, r);
-    if (ws.total > 0) {
-      if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
-      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
-    }
-    // outputs must not overlap inputs, the workspace or each other
-    const size_t nxb = (size_t)M * K * 2, nyb = (size_t)M * N * 2, nab = (size_t)r * K * 4,
-                 nbb = (size_t)N * r * 4;
-    const void* ins[] = {x, dy, A, B, w->codes, workspace};
-    const size_t in_sz[] = {nxb, nyb, (size_t)r * K * 2, (size_t)N * r * 2, (size_t)N * K / 2,
-                            ws.total};
-    void* outs[] = {dx, r > 0 ? dA : nullptr, r > 0 ? dB : nullptr};
-    const size_t out_sz[] = {nxb, nab, nbb};
-    for (int o = 0; o < 3; ++o) {
-      for (int i = 0; i < 6; ++i)
-        if (overlap(outs[o], out_sz[o], ins[i], in_sz[i])) return QLORA_EINVAL;
-      for (int o2 = o + 1; o2 < 3; ++o2)
-        if (overlap(outs[o], out_sz[o], outs[o2], out_sz[o2])) return QLORA_EINVAL;
-    }
-    hipStream_t s = as_stream(stream);
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, dx, dA, dB, accumulate, workspace, ws_bytes,
+                  stream);
+}
 
-    const Nf4Levels L = levels_arg();
-    uint16_t* gs = nullptr;
-    if (r > 0) {
-      uint16_t* xs = at<uint16_t>(workspace, ws.xs_off);
-      gs = at<uint16_t>(workspace, ws.gs_off);
-      const float scale = alpha / static_cast<float>(r);
-      // xs = split(s . x . A^T), gs = split(s . dy . B) in one launch
-      uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
-      uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
-      const qlora::LoraProjJob jx{x, A, xs, xsT, K, 0}, jg{dy, B, gs, gsT, N, 1};
-      if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, s))) != QLORA_OK)
-        return st;
-      // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x
-      const qlora::LoraGradJob jb{dy, xsT, dB, N, 0}, ja{x, gsT, dA, K, 1};
-      if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, s))) != QLORA_OK)
-        return st;
-    }
-    if (dx) {
-      float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
-      if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->dq_step, dy, gs, A, dx,
-                                                 part, M, N, K, r, L, s))) != QLORA_OK)
-        return st;
-    }
-    return QLORA_OK;
-  } catch (...) {
-    return QLORA_EHIP;
-  }
+int qlora_linear_bf16_fwd(const uint16_t* W, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                          const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                          uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+  const int st = check_bf16_weight(W, N, K);
+  if (st != QLORA_OK) return st;
+  const Wref wr{nullptr, nullptr, nullptr, W, N, K};
+  return fwd_impl(&wr, x, M, A, B, r, alpha, y, workspace, ws_bytes, stream);
+}
+
+int qlora_linear_bf16_bwd(const uint16_t* W, int64_t N, int64_t K, const uint16_t* x,
+                          const uint16_t* dy, int64_t M, const uint16_t* A, const uint16_t* B,
+                          int32_t r, float alpha, uint16_t* dx, float* dA, float* dB,
+                          int32_t accumulate, void* workspace, size_t ws_bytes, void* stream) {
+  const int st = check_bf16_weight(W, N, K);
+  if (st != QLORA_OK) return st;
+  const Wref wr{nullptr, nullptr, nullptr, W, N, K};
+  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, dx, dA, dB, accumulate, workspace, ws_bytes,
+                  stream);
 }
 
 int qlora_merge_adapter(const qlora_nf4_weight* w, const float* w0, int64_t N, int64_t K,

@@ -47,9 +47,10 @@ constexpr int WROW = 560;
 constexpr int WSTAGE = RT * WROW;  // bytes per W stage
 
 struct DxParams {
-  const uint8_t* codes;
+  const uint8_t* codes;   // NF4 weight (WF = kWeightNf4)
   const uint8_t* qscale;
   const float* step;
+  const uint16_t* wbf;    // bf16 weight [N, K] (WF = kWeightBf16)
   const uint16_t* dy;
   const uint16_t* gs;
   const uint16_t* A;
@@ -79,9 +80,14 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 // MS: 32-wide token subtiles per wave; MS = 4 is the 256 (k) x 256 (m)
 // tile, MS = 2 the 256 x 128 tile for small-M shapes (twice the output tiles,
 // so half the reduction splits and half their fp32 partials).
-template <int MS>
+//
+// WF: the weight's format.  kWeightBf16 (the unquantised comparison layer)
+// loads each thread's 64 bf16 of the slab row instead of decoding a block;
+// the values reach the slab at the same points of the schedule.
+template <int MS, int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
+  constexpr bool NF4 = WF == kWeightNf4;
   constexpr int TM = 64 * MS;   // token rows of the block tile
   constexpr int XR = TM / 32;   // dy rows staged per thread
   // one LDS array: two W^T stages, then two dy stages (the epilogue reuses
@@ -130,18 +136,28 @@ void dx_gemm_kernel(DxParams p) {
   // The scale byte and its step stay raw until the tile is decoded (an
   // iteration later): forming s' here would make the wave wait for this
   // prefetch -- and, since loads return in order, for every load before it.
-  struct Codes {
+  struct CodesNf4 {
     u32x4_t c0, c1;
     uint32_t q;
     float st;
   };
+  struct WordsBf16 {
+    u32x4_t w[8];  // chunk c: the 8 values at k = kcol + 8c .. + 7
+  };
+  using Codes = std::conditional_t<NF4, CodesNf4, WordsBf16>;
   auto load_codes = [&](int64_t st, Codes& c) {
     const int64_t idx = (st * RT + wr) * K + kcol;  // first element of the block
-    const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
-    c.c0 = cp[0];
-    c.c1 = cp[1];
-    c.q = p.qscale[idx >> 6];
-    c.st = p.step[idx >> 14];
+    if constexpr (NF4) {
+      const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
+      c.c0 = cp[0];
+      c.c1 = cp[1];
+      c.q = p.qscale[idx >> 6];
+      c.st = p.step[idx >> 14];
+    } else {
+      const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(p.wbf + idx);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c.w[i] = wp[i];
+    }
   };
   auto load_dy = [&](int64_t st, u32x4_t (&yr)[XR]) {
     const uint32_t o = yoff + (uint32_t)(st * RT * 2);
@@ -199,11 +215,14 @@ void dx_gemm_kernel(DxParams p) {
     load_codes(st0, C[0]);
     load_dy(st0, Y[0]);
     store_dy(0, Y[0]);
-    {
+    if constexpr (NF4) {
       const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(C[0].q, C[0].st));
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         store8(0, c, nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) store8(0, c, C[0].w[c]);
     }
     load_dy(cl(st0 + 1), Y[1]);
     load_codes(cl(st0 + 1), C[1]);
@@ -253,7 +272,14 @@ void dx_gemm_kernel(DxParams p) {
         o23 = perm(hi, lo, 0x07030602u);
       };
       auto unit = [&](int u) {
-        if (u < 4) {
+        if constexpr (!NF4) {
+          // no table or decode: a chunk's store sits where its decode ends
+          if (u >= 8 && u < 56) {
+            if ((u - 8) % 6 == 5) store8(nxt, (u - 8) / 6, cn.w[(u - 8) / 6]);
+          } else if (u >= 56 && u < 56 + XR) {
+            dyt[nxt][rk((t >> 3) + 32 * (u - 56), t & 7)] = Y[nxt][u - 56];
+          }
+        } else if (u < 4) {
           if (u == 0) sc = nf4_block_scale(cn.q, cn.st);
           pk[2 * u] = pack_bf16x2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
           pk[2 * u + 1] = pack_bf16x2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
@@ -345,9 +371,9 @@ void dx_gemm_kernel(DxParams p) {
 }
 
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
-                          uint16_t* dx, float* part, int64_t M, int64_t N, int64_t K, int r,
-                          const Nf4Levels& L, hipStream_t s) {
+                          const uint16_t* wbf, const uint16_t* dy, const uint16_t* gs,
+                          const uint16_t* A, uint16_t* dx, float* part, int64_t M, int64_t N,
+                          int64_t K, int r, const Nf4Levels& L, hipStream_t s) {
   // output M x K, reduction N: the forward GEMM's schedule with the roles
   // of N and K exchanged
   const GemmConfig cfg = gemm_config(M, K, N);
@@ -356,6 +382,7 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.codes = codes;
   p.qscale = qscale;
   p.step = step;
+  p.wbf = wbf;
   p.dy = dy;
   p.gs = gs;
   p.A = A;
@@ -371,10 +398,22 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.tail_s = cfg.tail_s;
   p.L = L;
   const int64_t blocks = gemm_blocks(cfg, M, K);
-  if (cfg.tm == 256)
-    hipLaunchKernelGGL(dx_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(dx_gemm_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const bool nf4 = wbf == nullptr;
+  if (cfg.tm == 256) {
+    if (nf4)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4>), dim3((unsigned)blocks), dim3(256), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16>), dim3((unsigned)blocks), dim3(256), 0,
+                         s, p);
+  } else {
+    if (nf4)
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4>), dim3((unsigned)blocks), dim3(256), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16>), dim3((unsigned)blocks), dim3(256), 0,
+                         s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_reduce(cfg, part, M, K, dx, s);

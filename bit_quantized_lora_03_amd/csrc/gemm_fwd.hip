@@ -52,9 +52,10 @@ constexpr int ROW_CHUNKS = KT / 8;  // 16-byte chunks per tile row
 constexpr int NSTAGE = 4;           // activation ring depth
 
 struct FwdParams {
-  const uint8_t* codes;
+  const uint8_t* codes;   // NF4 weight (WF = kWeightNf4)
   const uint8_t* qscale;
   const float* step;
+  const uint16_t* wbf;    // bf16 weight [N, K] (WF = kWeightBf16)
   const uint16_t* x;
   const uint16_t* xs;
   const uint16_t* B;
@@ -101,9 +102,19 @@ __device__ __forceinline__ void swap_halves(u32x4_t& a, u32x4_t& b, int v) {
 // JT = 8 amortises each decoded weight over 256 tokens; JT = 4 doubles the
 // number of output tiles for small-M shapes and so halves the k splits
 // (and their fp32 partials) needed to fill the chip.
-template <int JT>
+// WF: the weight's format.  kWeightNf4 decodes each thread's block as
+// described above; kWeightBf16 (the unquantised comparison layer) loads the
+// 64 bf16 of the same row tile instead and skips the table and decode, so
+// the two share every other part of the kernel.
+template <int JT, int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(FwdParams p) {
+  constexpr bool NF4 = WF == kWeightNf4;
+  // weight ring depth (tiles loaded ahead) and vector loads per weight tile:
+  // a bf16 tile is 8 x 16 bytes per thread, so the 256-token tile (whose
+  // accumulators leave the fewest registers) keeps two tiles, not four
+  constexpr int WD = NF4 ? 4 : (JT == 8 ? 2 : 4);
+  constexpr int LC = NF4 ? 4 : 8;
   constexpr int TM = 32 * JT;             // token rows of the block tile
   constexpr int XR = TM / 32;             // x chunks staged per thread per tile
   constexpr int XST = TM * ROW_CHUNKS;    // u32x4 per ring stage
@@ -143,7 +154,8 @@ void fwd_gemm_kernel(FwdParams p) {
 
   // this thread decodes weight row n0 + t (clamped)
   const int64_t wrow = clamp_row(n0 + t, N);
-  const uint8_t* wcodes = p.codes + ((wrow * K) >> 1);
+  const uint8_t* wcodes = NF4 ? p.codes + ((wrow * K) >> 1) : nullptr;
+  const uint16_t* wvals = NF4 ? nullptr : p.wbf + wrow * K;
   const int64_t wblk0 = (wrow * K) >> 6;
 
   // The x tile reaches LDS by DMA (buffer loads that write LDS directly):
@@ -172,18 +184,28 @@ void fwd_gemm_kernel(FwdParams p) {
   // The scale byte and its step stay raw until the tile is decoded:
   // forming s' at load time would make the wave wait for this prefetch --
   // and, since loads return in order, for every load before it.
-  struct Codes {
+  struct CodesNf4 {
     u32x4_t c0, c1;
     uint32_t q;
     float st;
   };
+  struct WordsBf16 {
+    u32x4_t w[8];  // chunk c: the 8 values at k = 8c .. 8c + 7 of the tile
+  };
+  using Codes = std::conditional_t<NF4, CodesNf4, WordsBf16>;
   auto load_codes = [&](int64_t kt, Codes& c) {
-    const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(wcodes + kt * (KT / 2));
-    c.c0 = cp[0];
-    c.c1 = cp[1];
-    const int64_t b = wblk0 + kt;
-    c.q = p.qscale[b];
-    c.st = p.step[b >> 8];
+    if constexpr (NF4) {
+      const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(wcodes + kt * (KT / 2));
+      c.c0 = cp[0];
+      c.c1 = cp[1];
+      const int64_t b = wblk0 + kt;
+      c.q = p.qscale[b];
+      c.st = p.step[b >> 8];
+    } else {
+      const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(wvals + kt * KT);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c.w[i] = wp[i];
+    }
   };
   auto store_x = [&](int stage, int q, const u32x4_t& v) {
     Xs(stage, (t >> 3) + 32 * q, t & 7) = v;
@@ -203,7 +225,7 @@ void fwd_gemm_kernel(FwdParams p) {
     // are clamped into the split, so loads are unconditional.
     const int64_t last = kt1 - 1;
     auto cl = [&](int64_t v) { return v < last ? v : last; };
-    Codes C[NSTAGE];
+    Codes C[WD];
     u32x4_t Ap[2][2];    // A operands of a step: [step parity][i]
     u32x4_t op[2][JT];   // B operands, by step parity
 
@@ -245,7 +267,8 @@ void fwd_gemm_kernel(FwdParams p) {
     };
     // table unit u (0..7) of a block: four products-and-packs, four perms
     auto table_unit = [&](const Codes& c, int u) {
-      if (u < 4) {
+      if constexpr (!NF4) return;
+      else if (u < 4) {
         if (u == 0) sc = nf4_block_scale(c.q, c.st);
         pk[2 * u] = pack_bf16x2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
         pk[2 * u + 1] = pack_bf16x2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
@@ -259,10 +282,16 @@ void fwd_gemm_kernel(FwdParams p) {
     // 4 + pr (5 units each, about 5 vector ops per unit), then the
     // lane-half exchange (2 units) that makes them step pr's A operands
     auto pair_unit = [&](const Codes& c, int pr, int w, u32x4_t (&dst)[2]) {
+      if constexpr (!NF4) {
+        if (w == 0) {
+          dlo = c.w[pr];
+          dhi = c.w[4 + pr];
+        }
+      }
       if (w < 5) {
-        decode_part(c.c0[pr], w, dlo);
+        if constexpr (NF4) decode_part(c.c0[pr], w, dlo);
       } else if (w < 10) {
-        decode_part(c.c1[pr], w - 5, dhi);
+        if constexpr (NF4) decode_part(c.c1[pr], w - 5, dhi);
       } else {
         const int v = 2 * (w - 10);
         swap_halves(dlo, dhi, v);
@@ -278,25 +307,27 @@ void fwd_gemm_kernel(FwdParams p) {
     // and first pair of tile kt0; then wait for x tiles kt0 and kt0+1.  The
     // issue order (kept by scheduling fences) ends like an iteration's: x
     // tile kt0+2, then the codes of kt0+3, which the waits below count on.
+    // (With a weight ring of depth WD the middle loads are tiles
+    // kt0+1 .. kt0+WD-2 and the last one tile kt0+WD-1.)
     load_codes(kt0, C[0]);
 #pragma unroll
     for (int q = 0; q < XR; ++q) dma_x(&lds[0], kt0, q);
 #pragma unroll
     for (int q = 0; q < XR; ++q) dma_x(&lds[XST], cl(kt0 + 1), q);
     __builtin_amdgcn_sched_barrier(0);
-    load_codes(cl(kt0 + 1), C[1]);
-    load_codes(cl(kt0 + 2), C[2]);
+#pragma unroll
+    for (int d = 1; d + 1 < WD; ++d) load_codes(cl(kt0 + d), C[d]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < XR; ++q) dma_x(&lds[2 * XST], cl(kt0 + 2), q);
     __builtin_amdgcn_sched_barrier(0);
-    load_codes(cl(kt0 + 3), C[3]);
+    load_codes(cl(kt0 + WD - 1), C[WD - 1]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 8; ++u) table_unit(C[0], u);
 #pragma unroll
     for (int w = 0; w < 12; ++w) pair_unit(C[0], 0, w, Ap[0]);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(12 + XR, 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((WD - 1) * LC + XR, 0));
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int j = 0; j < JT; ++j) op[0][j] = read_b(0, 0, j);
@@ -336,11 +367,11 @@ void fwd_gemm_kernel(FwdParams p) {
 #pragma unroll
           for (int u = s * NU / SPK; u < (s + 1) * NU / SPK; ++u) {
             if (kk < 3)
-              pair_unit(C[ph], kk + 1, u, Ap[(kk + 1) & 1]);
+              pair_unit(C[ph % WD], kk + 1, u, Ap[(kk + 1) & 1]);
             else if (u < 8)
-              table_unit(C[(ph + 1) % NSTAGE], u);
+              table_unit(C[(ph + 1) % WD], u);
             else
-              pair_unit(C[(ph + 1) % NSTAGE], 0, u - 8, Ap[0]);
+              pair_unit(C[(ph + 1) % WD], 0, u - 8, Ap[0]);
           }
           const int slot = SPK * kk + s;
           if (slot % 8 == 7) dma_x(fill, cl(kt + 3), slot / 8);  // x chunk of tile kt+3
@@ -352,9 +383,9 @@ void fwd_gemm_kernel(FwdParams p) {
       // DMA'd during the last iteration) does not also wait for them, nor
       // for the codes issued at the end of the last iteration: x tile kt+2
       // is complete once at most those 4 + XR + 4 loads are outstanding
-      load_codes(cl(kt + 4), C[ph]);
+      load_codes(cl(kt + WD), C[ph % WD]);
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(XR + 8, 0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(XR + 2 * LC, 0));
       __builtin_amdgcn_s_barrier();
     };
     u32x4_t* const S0 = &lds[0];
@@ -575,15 +606,16 @@ hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M,
 }
 
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                           const uint16_t* x, const uint16_t* xs, const uint16_t* B,
-                           uint16_t* y, float* part, int64_t M, int64_t N, int64_t K, int r,
-                           const Nf4Levels& L, hipStream_t s) {
+                           const uint16_t* wbf, const uint16_t* x, const uint16_t* xs,
+                           const uint16_t* B, uint16_t* y, float* part, int64_t M, int64_t N,
+                           int64_t K, int r, const Nf4Levels& L, hipStream_t s) {
   const GemmConfig cfg = gemm_config(M, N, K);
   if (gemm_partial_bytes(cfg, M, N) > 0 && part == nullptr) return hipErrorInvalidValue;
   FwdParams p;
   p.codes = codes;
   p.qscale = qscale;
   p.step = step;
+  p.wbf = wbf;
   p.x = x;
   p.xs = xs;
   p.B = B;
@@ -599,10 +631,22 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.tail_s = cfg.tail_s;
   p.L = L;
   const int64_t blocks = gemm_blocks(cfg, M, N);
-  if (cfg.tm == 256)
-    hipLaunchKernelGGL(fwd_gemm_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(fwd_gemm_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const bool nf4 = wbf == nullptr;
+  if (cfg.tm == 256) {
+    if (nf4)
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4>), dim3((unsigned)blocks), dim3(256), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightBf16>), dim3((unsigned)blocks), dim3(256),
+                         0, s, p);
+  } else {
+    if (nf4)
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4>), dim3((unsigned)blocks), dim3(256), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightBf16>), dim3((unsigned)blocks), dim3(256),
+                         0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_reduce(cfg, part, M, N, y, s);

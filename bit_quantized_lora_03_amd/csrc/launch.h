@@ -70,10 +70,13 @@ struct GemmConfig {
 GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred);
 int64_t gemm_blocks(const GemmConfig& c, int64_t M, int64_t Nout);
 size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout);
+// The weight is the NF4 one (codes, qscale, step) when wbf is null, else the
+// bf16 weight wbf [N, K] (the unquantised layer, same kernel skeleton).
+constexpr int kWeightNf4 = 0, kWeightBf16 = 1;
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                           const uint16_t* x, const uint16_t* xs, const uint16_t* B,
-                           uint16_t* y, float* part, int64_t M, int64_t N, int64_t K, int r,
-                           const Nf4Levels& L, hipStream_t s);
+                           const uint16_t* wbf, const uint16_t* x, const uint16_t* xs,
+                           const uint16_t* B, uint16_t* y, float* part, int64_t M, int64_t N,
+                           int64_t K, int r, const Nf4Levels& L, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, uint16_t* out,
                                 hipStream_t s);
 // the reduction after a fused GEMM's main kernel, if its schedule has one
@@ -95,9 +98,9 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
 // gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]; scheduled by
 // gemm_config(M, K, N) (output M x K, reduction N)
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const uint16_t* dy, const uint16_t* gs, const uint16_t* A,
-                          uint16_t* dx, float* part, int64_t M, int64_t N, int64_t K, int r,
-                          const Nf4Levels& L, hipStream_t s);
+                          const uint16_t* wbf, const uint16_t* dy, const uint16_t* gs,
+                          const uint16_t* A, uint16_t* dx, float* part, int64_t M, int64_t N,
+                          int64_t K, int r, const Nf4Levels& L, hipStream_t s);
 
 // merge.hip -- W_m = W_base + scale . B . A for export.  The base is the NF4
 // weight (codes non-null) or the fp32 original w0; out_f32 and/or out_bf16

@@ -184,8 +184,31 @@ int qlora_merge_adapter(const qlora_nf4_weight* w, const float* w0, int64_t N, i
                         const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                         float* out_f32, uint16_t* out_bf16, void* stream);
 
-/* Workspace bytes for op 0 (forward) or 1 (backward) at the given shape;
- * 0 for an invalid shape.  Host-only; never touches the GPU.               */
+/* The same layer with an unquantised bf16 base weight W [N, K] (row-major,
+ * out x in), through the same kernels with the dequantisation left out:
+ * the "LoRA on a 16-bit base" that QLoRA is compared with.
+ * [QLoRA / infivelines.com]: because the base is dequantised on every
+ * pass, training takes about a third longer than LoRA on an unquantised
+ * base; [QLoRA, and fine-tuning a 7B model on a free GPU, "What it costs
+ * in quality"]: where the bf16 model fits, bf16 training is the faster.
+ *   y  = x.W^T + (alpha/r).(x.A^T).B^T                     (forward)
+ *   dx = dy.W + (alpha/r).(dy.B).A,  dA, dB as in qlora_linear_bwd
+ * Arguments, shapes (N, K multiples of 64), rounding, accumulation, errors
+ * and size limits are those of qlora_linear_fwd / qlora_linear_bwd with
+ * W in place of the packed weight (W 16-byte aligned, EALIGN).  Every M
+ * runs the tiled GEMMs (there is no few-token path for this weight).
+ * workspace: qlora_linear_workspace_bytes(2 (forward) or 3 (backward), ...). */
+int qlora_linear_bf16_fwd(const uint16_t* W, int64_t N, int64_t K, const uint16_t* x, int64_t M,
+                          const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                          uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+int qlora_linear_bf16_bwd(const uint16_t* W, int64_t N, int64_t K, const uint16_t* x,
+                          const uint16_t* dy, int64_t M, const uint16_t* A, const uint16_t* B,
+                          int32_t r, float alpha, uint16_t* dx, float* dA, float* dB,
+                          int32_t accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for op 0 (forward) or 1 (backward) of the NF4 layer, or
+ * op 2 (forward) or 3 (backward) of the bf16-weight layer, at the given
+ * shape; 0 for an invalid shape.  Host-only; never touches the GPU.        */
 size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
                                     int32_t r);
 

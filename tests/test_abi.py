@@ -78,7 +78,12 @@ def test_workspace_sizes():
     assert ws(0, 16, 4096, 100, 16) == 0          # K % 64
     assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
     assert ws(0, 16, 4096, 4096, 264) == 0        # r > 256
-    assert ws(2, 16, 4096, 4096, 16) == 0         # bad op
+    assert ws(4, 16, 4096, 4096, 16) == 0         # bad op
+    # bf16-weight layer: no few-token path, so the tiled GEMMs' workspace
+    # at every M; its backward is laid out as the NF4 backward
+    assert ws(2, 512, 4096, 4096, 16) == ws(0, 512, 4096, 4096, 16)
+    assert ws(2, 16, 8192, 8192, 0) > 0           # split-K partials, no decode kernel
+    assert ws(3, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
 
 
 def _weight(N=128, K=128, codes=P0, qs=P1, st=P2):
@@ -211,3 +216,40 @@ def test_merge_validation():
     assert call(f=P0) == -1                                   # fp32 out over the codes
     assert call(w=None, w0=P3, f=P3 + 4096) == -1             # fp32 out over w0
     assert call(b=P4) == -1                                   # bf16 out over A
+
+
+def test_bf16_layer_validation():
+    L = q.lib()
+    need = q.workspace_bytes(2, 16, 256, 256, 8)
+    base = dict(W=P0, N=256, K=256, x=P3, M=16, A=P4, B=P4 + 8192, r=8, y=P4 + 65536,
+                ws=P4 + (1 << 19), wsb=need)
+
+    def fwd(**kw):
+        a = dict(base, **kw)
+        return L.qlora_linear_bf16_fwd(a["W"], a["N"], a["K"], a["x"], a["M"], a["A"], a["B"],
+                                       a["r"], 16.0, a["y"], a["ws"], a["wsb"], None)
+    assert fwd(W=None) == -1
+    assert fwd(N=250) == -2
+    assert fwd(K=100) == -2
+    assert fwd(W=P0 + 2) == -3
+    assert fwd(r=12) == -2
+    assert fwd(x=None) == -1
+    assert fwd(ws=None) == -5
+    assert fwd(y=P0) == -1                                    # y over W
+    assert fwd(M=(1 << 22) + 1) == -2                         # x above 2 GiB
+    assert fwd(M=0) == 0
+    needb = q.workspace_bytes(3, 16, 256, 256, 8)
+
+    def bwd(**kw):
+        a = dict(base, dy=P3 + 16384, dx=P4 + 65536, dA=P4 + 131072, dB=P4 + 196608,
+                 wsb=needb)
+        a.update(kw)
+        return L.qlora_linear_bf16_bwd(a["W"], a["N"], a["K"], a["x"], a["dy"], a["M"], a["A"],
+                                       a["B"], a["r"], 16.0, a["dx"], a["dA"], a["dB"], 0,
+                                       a["ws"], a["wsb"], None)
+    assert bwd(W=None) == -1
+    assert bwd(dy=None) == -1
+    assert bwd(dA=None) == -1
+    assert bwd(N=320 + 1) == -2
+    assert bwd(dx=P0) == -1                                   # dx over W
+    assert bwd(dB=P4 + 196608 + 4) == -3
