@@ -64,6 +64,18 @@ def weight_f32(seed: int, index: int, n: int, k: int, sigma: float,
     return w
 
 
+def keep_mask(seed: int, index: int, M: int, K: int, p: float) -> np.ndarray:
+    """A LoRA-dropout keep mask [M, K] (uint8 0/1): each element kept with
+    probability 1 - p, from its own seeded stream."""
+    return (_rng(seed, index).random((M, K)) >= p).astype(np.uint8)
+
+
+def pack_keep(keep: np.ndarray) -> np.ndarray:
+    """[M, K] 0/1 -> the library's packed layout [M, K/8]: bit (k mod 8) of
+    byte (m, k / 8) is keep[m, k]."""
+    return np.packbits(np.ascontiguousarray(keep, dtype=np.uint8), axis=1, bitorder="little")
+
+
 @dataclass
 class Layer:
     """One linear layer's inputs.  Arrays are drawn lazily on first access."""

@@ -13,7 +13,8 @@ What it computes (numpy, fp64 unless a step fixes another precision):
   double quantisation of the block scales (groups of 256) and the bit-exact
   dequantisation to bf16.
 * ``lora_linear`` -- the layer y = x.W'^T + (alpha/r).(x.A^T).B^T and its
-  gradients dX, dA, dB on the decoded weight W'.
+  gradients dX, dA, dB on the decoded weight W', optionally with LoRA
+  dropout on the adapter's input (the keep-mask is an input).
 * ``merge`` -- the adapter merged into a base weight for export,
   W_m = W_base + (alpha/r).B.A (fp32 and bf16 exports, re-quantisation, and
   the errors of the three ways to export).
@@ -45,5 +46,5 @@ from .nf4 import (  # noqa: F401
     dequant_nf4_bits,
     storage_bits_per_weight,
 )
-from .lora_linear import lora_linear_fwd, lora_linear_bwd, lora_scale  # noqa: F401
+from .lora_linear import lora_linear_fwd, lora_linear_bwd, lora_scale, dropped_input  # noqa: F401
 from .merge import merge_adapter, merged_bf16_bits, requantize, merge_errors  # noqa: F401

@@ -16,6 +16,7 @@ import oracle.nf4 as on
 from tests import test_oracle_levels as tl
 from tests import test_oracle_linear as tlin
 from tests import test_oracle_merge as tm
+from tests import test_oracle_dropout as tdo
 from tests import test_oracle_quant as tq
 
 
@@ -119,6 +120,29 @@ def _merged_bf16_from_f64(w_m):
     return (out.view(np.uint32) >> 16).astype(np.uint16)
 
 
+def _drop_without_rescale(x, keep, p):
+    x64 = np.asarray(x, dtype=np.float64)
+    return x64 if keep is None else x64 * np.asarray(keep, dtype=np.float64)
+
+
+def _bwd_dx_adapter_unmasked(x, dy, w, A, B, alpha, keep=None, p=0.0):
+    dX, dA, dB = _ORIG["bwd"](x, dy, w, A, B, alpha, keep=keep, p=p)
+    if keep is None or A is None:
+        return dX, dA, dB
+    s = ol.lora_scale(alpha, np.asarray(A).shape[0])
+    gA = s * ((np.asarray(dy, dtype=np.float64) @ np.asarray(B, dtype=np.float64))
+              @ np.asarray(A, dtype=np.float64))
+    base = np.asarray(dy, dtype=np.float64) @ np.asarray(w, dtype=np.float64)
+    return base + gA / (1.0 - p), dA, dB
+
+
+def _fwd_mask_on_base_too(x, w, A, B, alpha, keep=None, p=0.0):
+    if keep is None:
+        return _ORIG["fwd"](x, w, A, B, alpha)
+    xd = np.asarray(x, dtype=np.float64) * np.asarray(keep, dtype=np.float64)
+    return _ORIG["fwd"](xd, w, A, B, alpha, keep=keep, p=p)
+
+
 _ORIG = {
     "merge": om.merge_adapter,
     "thr": on.nf4_thresholds_f32,
@@ -162,6 +186,13 @@ CASES = [
      tm.test_one_entry_update_lands_at_row_of_B_column_of_A),
     ("bf16 export rounded from fp64", [(oracle, "merged_bf16_bits", _merged_bf16_from_f64)],
      tm.test_bf16_export_rounds_through_fp32_to_nearest_even),
+    ("dropout without 1/(1-p)", [(ol, "dropped_input", _drop_without_rescale)],
+     lambda: tdo.test_forward_equals_triple_loop(3, 5, 7, 2, 4.0, 0.25)),
+    ("dropout mask missing on dX's adapter term",
+     [(oracle, "lora_linear_bwd", _bwd_dx_adapter_unmasked)],
+     lambda: tdo.test_adjoint_identity_for_x(60)),
+    ("dropout applied to the base term too", [(oracle, "lora_linear_fwd", _fwd_mask_on_base_too)],
+     tdo.test_nothing_kept_leaves_the_base_alone),
 ]
 
 
