@@ -449,6 +449,33 @@ def main():
                "torch_bf16_gemm_dx_ms": round(t_lt_d, 5)}
         del Wq, ws16
 
+    # ---- the same fwd + bwd with LoRA dropout (p = 0.05, as the pages
+    # configure) on the adapter's input; the keep mask is a resident input ----
+    drop = None
+    if kind != "fwd" and r:
+        from bit_quantized_lora_03_amd import workloads as _wl
+        p_drop = 0.05
+        keep_d = to_dev(_wl.pack_keep(_wl.keep_mask(L.seed, 60, M, K, p_drop)))
+        need_d = max(q.workspace_bytes(4, M, N, K, r), q.workspace_bytes(5, M, N, K, r), 256)
+        ws_d = torch.empty(need_d, dtype=torch.uint8, device=dev)
+        wt_d = weights[0][3]
+
+        def fwd_d():
+            check(lib.qlora_linear_fwd_dropout(ctypes.byref(wt_d), P(x_d), M, P(A_d), P(B_d), r,
+                                               alpha, P(keep_d), p_drop, P(y), P(ws_d),
+                                               ws_d.numel(), sp()), "fwd dropout")
+
+        def bwd_d():
+            check(lib.qlora_linear_bwd_dropout(ctypes.byref(wt_d), P(x_d), P(dy_d), M, P(A_d),
+                                               P(B_d), r, alpha, P(keep_d), p_drop, P(dx), P(dA),
+                                               P(dB), 0, P(ws_d), ws_d.numel(), sp()),
+                  "bwd dropout")
+        t_fd = timed(lambda i: fwd_d(), reps)
+        t_bd = timed(lambda i: bwd_d(), reps)
+        drop = {"p": p_drop, "fwd_ms": round(t_fd, 5), "bwd_ms": round(t_bd, 5),
+                "over_no_dropout": round((t_fd + t_bd) / (ops["fwd_ms"] + ops["bwd_ms"]), 4)}
+        del keep_d, ws_d
+
     # ---- adapter merge for export (not part of the step): W_m = W + s.B.A,
     # fp32 and bf16 exports, from the NF4 base and from the fp32 original ----
     merge = None
@@ -538,6 +565,7 @@ def main():
         "roofline": roof,
         "ops": {k: round(v, 5) for k, v in ops.items()},
         "vs_unquantised": unq,
+        "dropout": drop,
         "merge": merge,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "step_s"},
         "wall_s": round(wall, 4),

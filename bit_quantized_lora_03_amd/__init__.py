@@ -21,7 +21,9 @@ from ._lib import (  # noqa: F401
     linear_bf16_bwd,
     linear_bf16_fwd,
     linear_bwd,
+    linear_bwd_dropout,
     linear_fwd,
+    linear_fwd_dropout,
     merge_adapter,
     nf4_levels,
     quantize_nf4,

@@ -172,21 +172,26 @@ struct Wref {
   size_t bytes() const { return nf4() ? (size_t)N * K / 2 : (size_t)N * K * 2; }
 };
 
+// keep (or null) and p: LoRA dropout on the adapter's input
 int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
-             int32_t r, float alpha, uint16_t* y, void* workspace, size_t ws_bytes,
-             void* stream) {
+             int32_t r, float alpha, const uint8_t* keep, float p, uint16_t* y,
+             void* workspace, size_t ws_bytes, void* stream) {
   try {
     int st = QLORA_OK;
     if ((st = check_rank(r)) != QLORA_OK) return st;
+    if (keep && !(p >= 0.0f && p < 1.0f)) return QLORA_EINVAL;
+    if (r == 0) keep = nullptr;
     if (M < 0) return QLORA_EINVAL;
     const int64_t N = w->N, K = w->K;
     if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
     if (M == 0) return QLORA_OK;
     if (!x || !y) return QLORA_EINVAL;
     if (r > 0 && (!A || !B)) return QLORA_EINVAL;
-    if (!aligned16(x) || !aligned16(y) || (r > 0 && (!aligned16(A) || !aligned16(B))))
+    if (!aligned16(x) || !aligned16(y) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
+        (keep && !aligned16(keep)))
       return QLORA_EALIGN;
-    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4());
+    // the few-token decode kernel has no dropout: the tiled path then runs
+    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep);
     if (ws.total > 0) {
       if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
       if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
@@ -194,12 +199,15 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
     const size_t ny = (size_t)M * N * 2;
     if (overlap(y, ny, x, (size_t)M * K * 2) || overlap(y, ny, w->data(), w->bytes()) ||
         (r > 0 && (overlap(y, ny, A, (size_t)r * K * 2) || overlap(y, ny, B, (size_t)N * r * 2))) ||
-        (ws.total > 0 && overlap(y, ny, workspace, ws.total)))
+        (ws.total > 0 && overlap(y, ny, workspace, ws.total)) ||
+        (keep && overlap(y, ny, keep, (size_t)M * K / 8)))
       return QLORA_EINVAL;
 
     hipStream_t s = as_stream(stream);
     const Nf4Levels L = levels_arg();
-    const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+    // inverted dropout: the kept values are scaled by 1 / (1 - p), folded into s
+    const float scale =
+        r > 0 ? alpha / static_cast<float>(r) / (keep ? 1.0f - p : 1.0f) : 0.0f;
     if (ws.decode) {
       return hip_status(qlora::launch_decode_fwd(
           w->codes, w->qscale, w->step, x, A, B, r, scale,
@@ -209,7 +217,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
     uint16_t* xs = nullptr;
     if (r > 0) {
       xs = at<uint16_t>(workspace, ws.xs_off);
-      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), K, 0};
+      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), K, 0, keep};
       if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s))) !=
           QLORA_OK)
         return st;
@@ -223,11 +231,14 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
 }
 
 int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, const uint16_t* A,
-             const uint16_t* B, int32_t r, float alpha, uint16_t* dx, float* dA, float* dB,
-             int32_t accumulate, void* workspace, size_t ws_bytes, void* stream) {
+             const uint16_t* B, int32_t r, float alpha, const uint8_t* keep, float p,
+             uint16_t* dx, float* dA, float* dB, int32_t accumulate, void* workspace,
+             size_t ws_bytes, void* stream) {
   try {
     int st = QLORA_OK;
     if ((st = check_rank(r)) != QLORA_OK) return st;
+    if (keep && !(p >= 0.0f && p < 1.0f)) return QLORA_EINVAL;
+    if (r == 0) keep = nullptr;
     if (M < 0) return QLORA_EINVAL;
     const int64_t N = w->N, K = w->K;
     if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
@@ -245,7 +256,8 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
     if (r > 0 && (!A || !B || !x || !dA || !dB)) return QLORA_EINVAL;
     if (!aligned16(dy) || (dx && !aligned16(dx)) ||
         (r > 0 && (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
-                   !aligned16(dB))))
+                   !aligned16(dB))) ||
+        (keep && !aligned16(keep)))
       return QLORA_EALIGN;
     const BwdWs ws = bwd_layout(M, N, K, r);
     if (ws.total > 0) {
@@ -255,13 +267,13 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
     // outputs must not overlap inputs, the workspace or each other
     const size_t nxb = (size_t)M * K * 2, nyb = (size_t)M * N * 2, nab = (size_t)r * K * 4,
                  nbb = (size_t)N * r * 4;
-    const void* ins[] = {x, dy, A, B, w->data(), workspace};
+    const void* ins[] = {x, dy, A, B, w->data(), workspace, keep};
     const size_t in_sz[] = {nxb, nyb, (size_t)r * K * 2, (size_t)N * r * 2, w->bytes(),
-                            ws.total};
+                            ws.total, keep ? (size_t)M * K / 8 : 0};
     void* outs[] = {dx, r > 0 ? dA : nullptr, r > 0 ? dB : nullptr};
     const size_t out_sz[] = {nxb, nab, nbb};
     for (int o = 0; o < 3; ++o) {
-      for (int i = 0; i < 6; ++i)
+      for (int i = 0; i < 7; ++i)
         if (overlap(outs[o], out_sz[o], ins[i], in_sz[i])) return QLORA_EINVAL;
       for (int o2 = o + 1; o2 < 3; ++o2)
         if (overlap(outs[o], out_sz[o], outs[o2], out_sz[o2])) return QLORA_EINVAL;
@@ -273,21 +285,23 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
     if (r > 0) {
       uint16_t* xs = at<uint16_t>(workspace, ws.xs_off);
       gs = at<uint16_t>(workspace, ws.gs_off);
-      const float scale = alpha / static_cast<float>(r);
-      // xs = split(s . x . A^T), gs = split(s . dy . B) in one launch
+      // with dropout, s / (1 - p): dB, dA and dX's adapter term all carry it
+      const float scale = alpha / static_cast<float>(r) / (keep ? 1.0f - p : 1.0f);
+      // xs = split(s . x~ . A^T), gs = split(s . dy . B) in one launch (x~:
+      // x with the dropped values zeroed)
       uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
       uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
-      const qlora::LoraProjJob jx{x, A, xs, xsT, K, 0}, jg{dy, B, gs, gsT, N, 1};
+      const qlora::LoraProjJob jx{x, A, xs, xsT, K, 0, keep}, jg{dy, B, gs, gsT, N, 1, nullptr};
       if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, s))) != QLORA_OK)
         return st;
-      // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x
-      const qlora::LoraGradJob jb{dy, xsT, dB, N, 0}, ja{x, gsT, dA, K, 1};
+      // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x~
+      const qlora::LoraGradJob jb{dy, xsT, dB, N, 0, nullptr}, ja{x, gsT, dA, K, 1, keep};
       if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, s))) != QLORA_OK)
         return st;
     }
     if (dx) {
       float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
-      if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->step, w->wbf, dy, gs,
+      if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->step, w->wbf, keep, dy, gs,
                                                  A, dx, part, M, N, K, r, L, s))) != QLORA_OK)
         return st;
     }
@@ -333,7 +347,8 @@ size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
     return 0;
   if (op == 0) return fwd_layout(M, N, K, r).total;
   if (op == 1 || op == 3) return bwd_layout(M, N, K, r).total;
-  if (op == 2) return fwd_layout(M, N, K, r, false).total;
+  if (op == 2 || op == 4) return fwd_layout(M, N, K, r, false).total;
+  if (op == 5) return bwd_layout(M, N, K, r).total;
   return 0;
 }
 
@@ -425,7 +440,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
   const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
-  return fwd_impl(&wr, x, M, A, B, r, alpha, y, workspace, ws_bytes, stream);
+  return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, 0.0f, y, workspace, ws_bytes, stream);
 }
 
 int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t M,
@@ -435,8 +450,8 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
   const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
-  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, dx, dA, dB, accumulate, workspace, ws_bytes,
-                  stream);
+  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, nullptr, 0.0f, dx, dA, dB, accumulate,
+                  workspace, ws_bytes, stream);
 }
 
 int qlora_linear_bf16_fwd(const uint16_t* W, int64_t N, int64_t K, const uint16_t* x, int64_t M,
@@ -445,7 +460,7 @@ int qlora_linear_bf16_fwd(const uint16_t* W, int64_t N, int64_t K, const uint16_
   const int st = check_bf16_weight(W, N, K);
   if (st != QLORA_OK) return st;
   const Wref wr{nullptr, nullptr, nullptr, W, N, K};
-  return fwd_impl(&wr, x, M, A, B, r, alpha, y, workspace, ws_bytes, stream);
+  return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, 0.0f, y, workspace, ws_bytes, stream);
 }
 
 int qlora_linear_bf16_bwd(const uint16_t* W, int64_t N, int64_t K, const uint16_t* x,
@@ -455,8 +470,32 @@ int qlora_linear_bf16_bwd(const uint16_t* W, int64_t N, int64_t K, const uint16_
   const int st = check_bf16_weight(W, N, K);
   if (st != QLORA_OK) return st;
   const Wref wr{nullptr, nullptr, nullptr, W, N, K};
-  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, dx, dA, dB, accumulate, workspace, ws_bytes,
-                  stream);
+  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, nullptr, 0.0f, dx, dA, dB, accumulate,
+                  workspace, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                             const uint8_t* keep, float p, uint16_t* y, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  if (!keep) return QLORA_EINVAL;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  return fwd_impl(&wr, x, M, A, B, r, alpha, keep, p, y, workspace, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int32_t r,
+                             float alpha, const uint8_t* keep, float p, uint16_t* dx, float* dA,
+                             float* dB, int32_t accumulate, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  if (!keep) return QLORA_EINVAL;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, keep, p, dx, dA, dB, accumulate, workspace,
+                  ws_bytes, stream);
 }
 
 int qlora_merge_adapter(const qlora_nf4_weight* w, const float* w0, int64_t N, int64_t K,

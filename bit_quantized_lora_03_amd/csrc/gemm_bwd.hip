@@ -51,6 +51,7 @@ struct DxParams {
   const uint8_t* qscale;
   const float* step;
   const uint16_t* wbf;    // bf16 weight [N, K] (WF = kWeightBf16)
+  const uint8_t* keep;    // LoRA dropout keep bits [M, K / 8] (DROP)
   const uint16_t* dy;
   const uint16_t* gs;
   const uint16_t* A;
@@ -84,7 +85,12 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 // WF: the weight's format.  kWeightBf16 (the unquantised comparison layer)
 // loads each thread's 64 bf16 of the slab row instead of decoding a block;
 // the values reach the slab at the same points of the schedule.
-template <int MS, int WF>
+//
+// DROP (LoRA dropout): the adapter term of dX is masked elementwise by the
+// keep bits, the base term is not.  Both share the accumulators, so the
+// adapter rows run first, the accumulators are masked, and the base
+// reduction adds onto them: the sum is still rounded once.
+template <int MS, int WF, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
   constexpr bool NF4 = WF == kWeightNf4;
@@ -202,6 +208,64 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
       for (int j = 0; j < MS; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
   };
+
+  // --- adapter rows: gs [M, 2r] against [A ; A] (last split only) ---
+  const int r = p.r;
+  auto adapter_rows = [&]() {
+    const int ext_tiles = (2 * r + RT - 1) / RT;
+    const int64_t m = clamp_row(m0 + (t % TM), M);
+    for (int e = 0; e < ext_tiles; ++e) {
+      // W^T side: reduction row c = e*64 + wr is A's row (c mod r), zero past 2r
+      const int c = e * RT + wr;
+      const bool row_ok = c < 2 * r;
+      const int arow = c < r ? c : c - r;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        store8(0, q, row_ok ? *reinterpret_cast<const u32x4_t*>(p.A + (int64_t)arow * K + kcol + 8 * q)
+                              : zero);
+      // dy side: rows m, columns c of gs
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int col = e * RT + 8 * q;
+        if (t < TM)
+          dyt[0][rk(t, q)] =
+              col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.gs + m * 2 * r + col) : zero;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) mfma_step(0, kk);
+      __syncthreads();
+    }
+  };
+
+  // Dropout mask on the accumulators: lane (lr, lg) of acc[i][j] holds
+  // token m0 + 32 MS wm + 32 j + lr and, in register v, column
+  // k0 + 128 wk + 32 i + 8 (v / 4) + 4 lg + v % 4 -- 16 bits of the
+  // 32-bit keep word of that token row at column k0 + 128 wk + 32 i.
+  // Rows past M read zero (not stored); columns past K are not stored.
+  auto mask_acc = [&]() {
+    const __amdgpu_buffer_rsrc_t kres = make_rsrc(p.keep, (uint32_t)(M * K / 8));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < MS; ++j) {
+        const int64_t m = m0 + 32 * MS * wm + 32 * j + lr;
+        const int64_t kw = k0 + 128 * wk + 32 * i;
+        const uint32_t word = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            kres, (int)(uint32_t)(m * (K / 8) + kw / 8), 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int bit = 8 * (v >> 2) + 4 * lg + (v & 3);
+          acc[i][j][v] = ((word >> bit) & 1u) ? acc[i][j][v] : 0.0f;
+        }
+      }
+  };
+  if constexpr (DROP) {
+    if (z == nz - 1) {
+      adapter_rows();
+      mask_acc();
+    }
+  }
 
   if (st0 < st1) {
     // Register sets indexed by slab parity (relative to st0), loaded at the
@@ -329,33 +393,8 @@ void dx_gemm_kernel(DxParams p) {
     }
   }
 
-  // --- adapter rows: gs [M, 2r] against [A ; A] (last split only) ---
-  const int r = p.r;
-  if (z == nz - 1) {
-    const int ext_tiles = (2 * r + RT - 1) / RT;
-    const int64_t m = clamp_row(m0 + (t % TM), M);
-    for (int e = 0; e < ext_tiles; ++e) {
-      // W^T side: reduction row c = e*64 + wr is A's row (c mod r), zero past 2r
-      const int c = e * RT + wr;
-      const bool row_ok = c < 2 * r;
-      const int arow = c < r ? c : c - r;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        store8(0, q, row_ok ? *reinterpret_cast<const u32x4_t*>(p.A + (int64_t)arow * K + kcol + 8 * q)
-                              : zero);
-      // dy side: rows m, columns c of gs
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int col = e * RT + 8 * q;
-        if (t < TM)
-          dyt[0][rk(t, q)] =
-              col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.gs + m * 2 * r + col) : zero;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) mfma_step(0, kk);
-      __syncthreads();
-    }
+  if constexpr (!DROP) {
+    if (z == nz - 1) adapter_rows();
   }
 
   // --- epilogue: D[k][m] -> dx[m][k] (or the split's fp32 partial) ---
@@ -371,9 +410,10 @@ void dx_gemm_kernel(DxParams p) {
 }
 
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const uint16_t* wbf, const uint16_t* dy, const uint16_t* gs,
-                          const uint16_t* A, uint16_t* dx, float* part, int64_t M, int64_t N,
-                          int64_t K, int r, const Nf4Levels& L, hipStream_t s) {
+                          const uint16_t* wbf, const uint8_t* keep, const uint16_t* dy,
+                          const uint16_t* gs, const uint16_t* A, uint16_t* dx, float* part,
+                          int64_t M, int64_t N, int64_t K, int r, const Nf4Levels& L,
+                          hipStream_t s) {
   // output M x K, reduction N: the forward GEMM's schedule with the roles
   // of N and K exchanged
   const GemmConfig cfg = gemm_config(M, K, N);
@@ -383,6 +423,7 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.qscale = qscale;
   p.step = step;
   p.wbf = wbf;
+  p.keep = keep;
   p.dy = dy;
   p.gs = gs;
   p.A = A;
@@ -398,21 +439,27 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.tail_s = cfg.tail_s;
   p.L = L;
   const int64_t blocks = gemm_blocks(cfg, M, K);
-  const bool nf4 = wbf == nullptr;
+  const bool nf4 = wbf == nullptr, drop = keep != nullptr && r > 0;
+  const dim3 grid((unsigned)blocks);
+  // MS = 4 (256-token tile) or 2; weight format; dropout mask or not
   if (cfg.tm == 256) {
-    if (nf4)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4>), dim3((unsigned)blocks), dim3(256), 0,
-                         s, p);
+    if (nf4 && !drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false>), grid, dim3(256), 0, s, p);
+    else if (nf4)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, true>), grid, dim3(256), 0, s, p);
+    else if (!drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, false>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16>), dim3((unsigned)blocks), dim3(256), 0,
-                         s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, true>), grid, dim3(256), 0, s, p);
   } else {
-    if (nf4)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4>), dim3((unsigned)blocks), dim3(256), 0,
-                         s, p);
+    if (nf4 && !drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false>), grid, dim3(256), 0, s, p);
+    else if (nf4)
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, true>), grid, dim3(256), 0, s, p);
+    else if (!drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, false>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16>), dim3((unsigned)blocks), dim3(256), 0,
-                         s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, true>), grid, dim3(256), 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

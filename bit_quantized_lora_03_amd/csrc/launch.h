@@ -35,6 +35,9 @@ struct LoraProjJob {
   uint16_t* outT;     // [2r, Mp] bf16
   int64_t Kred;
   int kmajor;
+  // LoRA dropout on X (or null): [M, Kred / 8] bytes, bit k mod 8 of byte
+  // (m, k / 8) set where X[m][k] is kept; dropped values count as zero
+  const uint8_t* keep = nullptr;
 };
 // one job, or two in one launch (j1 non-null)
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
@@ -48,6 +51,7 @@ struct LoraGradJob {
   float* C;
   int64_t ldg;
   int transposed;
+  const uint8_t* keep = nullptr;  // dropout mask on G, as in LoraProjJob (or null)
 };
 hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
                             int accumulate, hipStream_t s);
@@ -97,10 +101,12 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
 
 // gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]; scheduled by
 // gemm_config(M, K, N) (output M x K, reduction N)
+// keep (or null): LoRA dropout bits [M, K / 8] masking the adapter term.
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const uint16_t* wbf, const uint16_t* dy, const uint16_t* gs,
-                          const uint16_t* A, uint16_t* dx, float* part, int64_t M, int64_t N,
-                          int64_t K, int r, const Nf4Levels& L, hipStream_t s);
+                          const uint16_t* wbf, const uint8_t* keep, const uint16_t* dy,
+                          const uint16_t* gs, const uint16_t* A, uint16_t* dx, float* part,
+                          int64_t M, int64_t N, int64_t K, int r, const Nf4Levels& L,
+                          hipStream_t s);
 
 // merge.hip -- W_m = W_base + scale . B . A for export.  The base is the NF4
 // weight (codes non-null) or the fp32 original w0; out_f32 and/or out_bf16

@@ -62,6 +62,38 @@ __device__ __forceinline__ u32x4_t ldb(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
                                                                            (int)soff, 0));
 }
 
+// One byte through a buffer descriptor (zero past its end).
+__device__ __forceinline__ uint32_t ldb8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
+// LoRA dropout: the 8 bf16 of a 16-byte chunk (consecutive k, value i in
+// halfword i) keep their bits where bit i of the chunk's keep byte is set
+// and become +0 where it is clear.
+__device__ __forceinline__ u32x4_t keep8(const u32x4_t v, uint32_t kb) {
+  u32x4_t o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t b = kb >> (2 * d);
+    o[d] = v[d] & (((b & 1u) ? 0x0000FFFFu : 0u) | ((b & 2u) ? 0xFFFF0000u : 0u));
+  }
+  return o;
+}
+
+// The keep-mask of a job, [rows, cols / 8] bytes, through a descriptor;
+// `all` is ORed into every loaded byte (0xFF: the job has no mask, so
+// every bit reads as kept).
+struct KeepBits {
+  __amdgpu_buffer_rsrc_t res;
+  uint32_t all;
+};
+__device__ __forceinline__ KeepBits keep_bits(const uint8_t* keep, int64_t bytes) {
+  KeepBits k;
+  k.res = make_rsrc(keep, keep ? (uint32_t)bytes : 0u);
+  k.all = keep ? 0u : 0xFFu;
+  return k;
+}
+
 // The job a block works on is picked by comparing blockIdx with a kernel
 // argument, which is the same for every lane, but the compiler cannot tell:
 // a buffer descriptor built from a value it takes to differ between lanes
@@ -84,6 +116,7 @@ __device__ __forceinline__ LoraProjJob uniform_job(const LoraProjJob& j) {
   u.outT = uniform_ptr(j.outT);
   u.Kred = (int64_t)uniform64((uint64_t)j.Kred);
   u.kmajor = __builtin_amdgcn_readfirstlane(j.kmajor);
+  u.keep = uniform_ptr(j.keep);
   return u;
 }
 __device__ __forceinline__ LoraGradJob uniform_job(const LoraGradJob& j) {
@@ -93,6 +126,7 @@ __device__ __forceinline__ LoraGradJob uniform_job(const LoraGradJob& j) {
   u.C = uniform_ptr(j.C);
   u.ldg = (int64_t)uniform64((uint64_t)j.ldg);
   u.transposed = __builtin_amdgcn_readfirstlane(j.transposed);
+  u.keep = uniform_ptr(j.keep);
   return u;
 }
 
@@ -145,7 +179,8 @@ __device__ __forceinline__ void put_split(const LoraProjJob& J, int64_t M, int r
 // group.  B's rows (8 rank columns of one k per 16 bytes) go through the
 // wave's slab and come back transposed.
 // ---------------------------------------------------------------------------
-template <int JT>
+// DROP: the jobs may carry a keep-mask on X (LoRA dropout; see keep8).
+template <int JT, bool DROP>
 __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
                                                              int64_t blocks0, int64_t M, int r,
                                                              float scale) {
@@ -177,6 +212,9 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   const uint32_t xoff = (uint32_t)((m * Kred + 8 * kg) * 2);
   uint16_t* slab = reinterpret_cast<uint16_t*>(lds) + wave * SLAB;
   const bool kmajor = J.kmajor != 0;
+  // keep byte of the lane's x chunk: (m Kred + k0 + 8 kg) / 8
+  const KeepBits kp = keep_bits(J.keep, M * Kred / 8);
+  const uint32_t koff = (uint32_t)(m * (Kred / 8) + kg);
 
   f32x4_t acc[JT];
 #pragma unroll
@@ -187,6 +225,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   struct Batch {
     u32x4_t x[BS];
     u32x4_t y[BS][JT];
+    uint32_t kb[BS];
   };
   // Lane offsets of the Y pieces, fixed for the whole loop (kOff past r).
   // Steps past the wave's count OR in kOff: a select the compiler keeps as
@@ -209,6 +248,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
       const uint32_t past = u < cnt ? 0u : kOff;
       const uint32_t k0 = (uint32_t)(32 * (wave + kWaves * u));
       R.x[bb] = ldb(xres, xoff | past, 2 * k0);
+      if constexpr (DROP) R.kb[bb] = ldb8(kp.res, koff | past, k0 / 8) | kp.all;
 #pragma unroll
       for (int q = 0; q < JT; ++q)
         R.y[bb][q] = ldb(yres, yoff[q] | past, kmajor ? 2 * k0 * (uint32_t)r : 2 * k0);
@@ -218,9 +258,10 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   auto compute = [&](const Batch& R) {
 #pragma unroll
     for (int bb = 0; bb < BS; ++bb) {
+      const u32x4_t xv = DROP ? keep8(R.x[bb], R.kb[bb]) : R.x[bb];
       if (!kmajor) {
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma16x16x32(R.x[bb], R.y[bb][jt], acc[jt]);
+        for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma16x16x32(xv, R.y[bb][jt], acc[jt]);
       } else {
 #pragma unroll
         for (int q = 0; q < JT; ++q) {
@@ -229,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
         }
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
-          acc[jt] = mfma16x16x32(R.x[bb], read_tr8(slab, RS, 8 * kg, 16 * jt, i), acc[jt]);
+          acc[jt] = mfma16x16x32(xv, read_tr8(slab, RS, 8 * kg, 16 * jt, i), acc[jt]);
       }
     }
   };
@@ -280,6 +321,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
 constexpr int kSmallT = 8, kSmallR = 8;  // tokens, rank columns per block
 constexpr int kSmallRed = 65;            // LDS row of a thread's 64 sums (+1: no bank conflicts)
 
+template <bool DROP>
 __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, LoraProjJob j1,
                                                               int64_t blocks0, int64_t M, int r,
                                                               float scale) {
@@ -298,9 +340,13 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(J.X, (uint32_t)(M * Kred * 2));
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(J.Y, (uint32_t)((int64_t)r * Kred * 2));
   // rows past M lie past x's end and read as zero
-  uint32_t xoff[kSmallT];
+  uint32_t xoff[kSmallT], koff[kSmallT];
 #pragma unroll
-  for (int i = 0; i < kSmallT; ++i) xoff[i] = (uint32_t)((m0 + i) * Kred * 2);
+  for (int i = 0; i < kSmallT; ++i) {
+    xoff[i] = (uint32_t)((m0 + i) * Kred * 2);
+    koff[i] = (uint32_t)((m0 + i) * (Kred / 8));  // keep byte of piece pc: koff + pc
+  }
+  const KeepBits kp = keep_bits(J.keep, M * Kred / 8);
 
   float acc[kSmallT][kSmallR];
 #pragma unroll
@@ -313,6 +359,7 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
   struct Piece {
     u32x4_t x[kSmallT];
     u32x4_t y[kSmallR];
+    uint32_t kb[kSmallT];
   };
   // Every offset here differs between lanes, so all of it is lane offset.
   // Pieces past the thread's count OR in kOff: a select the compiler keeps
@@ -325,7 +372,10 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
     const uint32_t past = u < cnt ? 0u : kOff;
     const uint32_t pc = (uint32_t)(t + 256 * u);  // 8-wide piece index
 #pragma unroll
-    for (int i = 0; i < kSmallT; ++i) P.x[i] = ldb(xres, (xoff[i] + 16u * pc) | past, 0);
+    for (int i = 0; i < kSmallT; ++i) {
+      P.x[i] = ldb(xres, (xoff[i] + 16u * pc) | past, 0);
+      if constexpr (DROP) P.kb[i] = ldb8(kp.res, (koff[i] + pc) | past, 0) | kp.all;
+    }
 #pragma unroll
     for (int q = 0; q < kSmallR; ++q)
       P.y[q] = ldb(yres, (ybase[q] + (kmajor ? 16u * (uint32_t)r * pc : 16u * pc)) | past, 0);
@@ -346,13 +396,15 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
       }
     }
 #pragma unroll
-    for (int i = 0; i < kSmallT; ++i)
+    for (int i = 0; i < kSmallT; ++i) {
+      const u32x4_t xv = DROP ? keep8(P.x[i], P.kb[i]) : P.x[i];
 #pragma unroll
       for (int q = 0; q < kSmallR; ++q)
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp)
-          acc[i][q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(P.x[i][pp]), as_bf16x2(yp[q][pp]),
+          acc[i][q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[pp]), as_bf16x2(yp[q][pp]),
                                                       acc[i][q], false);
+    }
   };
   Piece P0, P1;
   if (cnt > 0) load(0, P0);
@@ -388,16 +440,17 @@ static bool proj_small(int64_t M, int r) { return M * r <= 16384; }
 
 static int proj_jt(int r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
 
-hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
-                            float scale, hipStream_t s) {
+template <bool DROP>
+static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
+                              float scale, hipStream_t s) {
   if (proj_small(M, r)) {
     // Mp / 8 token groups cover every row of the transposed copy
     const int64_t per_job = (pad32(M) / kSmallT) * (r / kSmallR);
     const LoraProjJob jb = j1 ? *j1 : j0;
     const int64_t total = per_job * (j1 ? 2 : 1);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL(lora_proj_small_kernel, dim3((unsigned)total), dim3(256), 0, s, j0, jb,
-                       per_job, M, r, scale);
+    hipLaunchKernelGGL((lora_proj_small_kernel<DROP>), dim3((unsigned)total), dim3(256), 0, s,
+                       j0, jb, per_job, M, r, scale);
     return hipGetLastError();
   }
   const int jt = proj_jt(r);
@@ -409,15 +462,21 @@ hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)total);
   if (jt == 1)
-    hipLaunchKernelGGL(lora_proj_kernel<1>, grid, dim3(kThreads), 0, s, j0, jb, blocks0, M, r,
-                       scale);
+    hipLaunchKernelGGL((lora_proj_kernel<1, DROP>), grid, dim3(kThreads), 0, s, j0, jb, blocks0,
+                       M, r, scale);
   else if (jt == 2)
-    hipLaunchKernelGGL(lora_proj_kernel<2>, grid, dim3(kThreads), 0, s, j0, jb, blocks0, M, r,
-                       scale);
+    hipLaunchKernelGGL((lora_proj_kernel<2, DROP>), grid, dim3(kThreads), 0, s, j0, jb, blocks0,
+                       M, r, scale);
   else
-    hipLaunchKernelGGL(lora_proj_kernel<4>, grid, dim3(kThreads), 0, s, j0, jb, blocks0, M, r,
-                       scale);
+    hipLaunchKernelGGL((lora_proj_kernel<4, DROP>), grid, dim3(kThreads), 0, s, j0, jb, blocks0,
+                       M, r, scale);
   return hipGetLastError();
+}
+
+hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
+                            float scale, hipStream_t s) {
+  if (j0.keep || (j1 && j1->keep)) return launch_proj<true>(j0, j1, M, r, scale, s);
+  return launch_proj<false>(j0, j1, M, r, scale, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -430,14 +489,17 @@ hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_
 // lane); S comes from the transposed copy ST [2r][Mp] as direct 16-byte
 // loads, hi and lo as two MFMAs on the same G operand.
 // ---------------------------------------------------------------------------
-template <int JT>
+// DROP: the jobs may carry a keep-mask on G (LoRA dropout; see keep8).
+template <int JT, bool DROP>
 __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, LoraGradJob j1,
                                                              int64_t blocks0, int64_t M, int r,
                                                              int accumulate) {
   constexpr int RC = 16 * JT;
   constexpr int GS = 64 + 8;                        // slab row: 64 bf16 + 16 bytes of pad
   constexpr int SLAB = 32 * GS;                     // bf16 per wave
-  constexpr int BS = JT == 4 ? 1 : 2;                  // token steps per batch of loads
+  // token steps per batch of loads (one with a keep-mask: its bytes would
+  // otherwise push the r <= 32 variant past its registers)
+  constexpr int BS = (JT == 4 || DROP) ? 1 : 2;
   constexpr int REDS = RC + 4;
   constexpr int SLAB_BYTES = kWaves * SLAB * 2, RED_BYTES = kWaves * 16 * REDS * 4;
   __shared__ __align__(16) char lds[SLAB_BYTES > RED_BYTES ? SLAB_BYTES : RED_BYTES];
@@ -458,6 +520,7 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
   const __amdgpu_buffer_rsrc_t gres = make_rsrc(J.G, (uint32_t)(M * ldg * 2));
   const __amdgpu_buffer_rsrc_t sres = make_rsrc(J.ST, (uint32_t)(2 * r * Mp * 2));
   const uint32_t sl_off = (uint32_t)(r * Mp * 2);  // lo rows follow the hi rows
+  const KeepBits kp = keep_bits(J.keep, M * ldg / 8);
 
   for (int jc = 0; jc < r; jc += RC) {
     f32x4_t acc[4][JT];
@@ -467,11 +530,12 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
       for (int b = 0; b < JT; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // G piece p = lane + 64 q of a step: token p / 8, 8 columns at 8 (p mod 8)
-    uint32_t goff[4], soff[JT];
+    uint32_t goff[4], kgoff[4], soff[JT];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = lane + 64 * q;
       goff[q] = (uint32_t)((((p >> 3) * ldg) + g0 + 8 * (p & 7)) * 2);
+      kgoff[q] = (uint32_t)((p >> 3) * (ldg / 8) + g0 / 8 + (p & 7));  // the piece's keep byte
     }
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
@@ -479,6 +543,7 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
     struct Batch {
       u32x4_t g[BS][4];
       u32x4_t sh[BS][JT], sl[BS][JT];
+      uint32_t kb[BS][4];
     };
     auto load = [&](int64_t u0, Batch& R) {
 #pragma unroll
@@ -488,8 +553,11 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
         const uint32_t t0 = (uint32_t)(32 * (wave + kWaves * u));
         // the G row is part of the lane offset (rows past M read as zero)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q) {
           R.g[bb][q] = ldb(gres, ok ? goff[q] + t0 * (uint32_t)ldg * 2 : kOff, 0);
+          if constexpr (DROP)
+            R.kb[bb][q] = ldb8(kp.res, ok ? kgoff[q] + t0 * (uint32_t)(ldg / 8) : kOff, 0) | kp.all;
+        }
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
           const bool cok = ok && jc + 16 * jt + i < r;
@@ -504,7 +572,8 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int p = lane + 64 * q;
-          *reinterpret_cast<u32x4_t*>(slab + (p >> 3) * GS + 8 * (p & 7)) = R.g[bb][q];
+          *reinterpret_cast<u32x4_t*>(slab + (p >> 3) * GS + 8 * (p & 7)) =
+              DROP ? keep8(R.g[bb][q], R.kb[bb][q]) : R.g[bb][q];
         }
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
@@ -558,21 +627,28 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
   }
 }
 
-hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
-                            int accumulate, hipStream_t s) {
+template <bool DROP>
+static hipError_t launch_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
+                              int accumulate, hipStream_t s) {
   const int64_t b0 = j0.ldg / 64, b1 = j1.ldg / 64;
   if (b0 + b1 == 0 || r == 0) return hipSuccess;
   const dim3 grid((unsigned)(b0 + b1));
   if (r <= 16)
-    hipLaunchKernelGGL(lora_grad_kernel<1>, grid, dim3(kThreads), 0, s, j0, j1, b0, M, r,
-                       accumulate);
+    hipLaunchKernelGGL((lora_grad_kernel<1, DROP>), grid, dim3(kThreads), 0, s, j0, j1, b0, M,
+                       r, accumulate);
   else if (r <= 32)
-    hipLaunchKernelGGL(lora_grad_kernel<2>, grid, dim3(kThreads), 0, s, j0, j1, b0, M, r,
-                       accumulate);
+    hipLaunchKernelGGL((lora_grad_kernel<2, DROP>), grid, dim3(kThreads), 0, s, j0, j1, b0, M,
+                       r, accumulate);
   else
-    hipLaunchKernelGGL(lora_grad_kernel<4>, grid, dim3(kThreads), 0, s, j0, j1, b0, M, r,
-                       accumulate);
+    hipLaunchKernelGGL((lora_grad_kernel<4, DROP>), grid, dim3(kThreads), 0, s, j0, j1, b0, M,
+                       r, accumulate);
   return hipGetLastError();
+}
+
+hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
+                            int accumulate, hipStream_t s) {
+  if (j0.keep || j1.keep) return launch_grad<true>(j0, j1, M, r, accumulate, s);
+  return launch_grad<false>(j0, j1, M, r, accumulate, s);
 }
 
 }  // namespace qlora

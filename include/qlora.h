@@ -184,6 +184,36 @@ int qlora_merge_adapter(const qlora_nf4_weight* w, const float* w0, int64_t N, i
                         const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                         float* out_f32, uint16_t* out_bf16, void* stream);
 
+/* Forward and backward with LoRA dropout on the adapter's input.
+ * [QLoRA -- Module 12.4, "Hugging Face + BitsAndBytes"]: the adapter config
+ * sets lora_dropout (0.05 there).  The pages give no formula; the standard
+ * LoRA dropout is taken: the adapter sees x~ = x * keep / (1 - p), the base
+ * term sees x, so
+ *   y  = x.deq(W)^T + (alpha/r).(x~.A^T).B^T
+ *   dx = dy.deq(W) + (alpha/r).((dy.B).A) * keep / (1 - p)
+ *   dA = (alpha/r).(dy.B)^T.x~          dB = (alpha/r).dy^T.(x~.A^T)
+ * The random draws are an input:
+ *   keep [M, K/8] bytes (device, 16-byte aligned): bit (k mod 8) of byte
+ *        (m, k/8) is 1 where x[m][k] is kept; the same mask must be passed
+ *        to the backward of the same step.
+ *   p    dropout probability, 0 <= p < 1 (EINVAL otherwise); 1/(1 - p) is
+ *        folded into the fp32 scale alpha/r.
+ * Other arguments, rounding (y and dx still rounded once), errors and size
+ * limits as qlora_linear_fwd / qlora_linear_bwd; keep must not overlap an
+ * output (EINVAL).  The forward always runs the tiled GEMMs (no few-token
+ * path); its workspace is qlora_linear_workspace_bytes(4, ...), the
+ * backward's qlora_linear_workspace_bytes(5, ...).  With r = 0 there is no
+ * adapter and keep is ignored.                                             */
+int qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                             const uint8_t* keep, float p, uint16_t* y, void* workspace,
+                             size_t ws_bytes, void* stream);
+int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int32_t r,
+                             float alpha, const uint8_t* keep, float p, uint16_t* dx, float* dA,
+                             float* dB, int32_t accumulate, void* workspace, size_t ws_bytes,
+                             void* stream);
+
 /* The same layer with an unquantised bf16 base weight W [N, K] (row-major,
  * out x in), through the same kernels with the dequantisation left out:
  * the "LoRA on a 16-bit base" that QLoRA is compared with.
@@ -206,8 +236,9 @@ int qlora_linear_bf16_bwd(const uint16_t* W, int64_t N, int64_t K, const uint16_
                           int32_t r, float alpha, uint16_t* dx, float* dA, float* dB,
                           int32_t accumulate, void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for op 0 (forward) or 1 (backward) of the NF4 layer, or
- * op 2 (forward) or 3 (backward) of the bf16-weight layer, at the given
+/* Workspace bytes for op 0 (forward) or 1 (backward) of the NF4 layer,
+ * op 2 (forward) or 3 (backward) of the bf16-weight layer, or op 4
+ * (forward) or 5 (backward) of the NF4 layer with dropout, at the given
  * shape; 0 for an invalid shape.  Host-only; never touches the GPU.        */
 size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
                                     int32_t r);

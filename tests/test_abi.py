@@ -78,7 +78,10 @@ def test_workspace_sizes():
     assert ws(0, 16, 4096, 100, 16) == 0          # K % 64
     assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
     assert ws(0, 16, 4096, 4096, 264) == 0        # r > 256
-    assert ws(4, 16, 4096, 4096, 16) == 0         # bad op
+    assert ws(6, 16, 4096, 4096, 16) == 0         # bad op
+    # dropout: the forward never takes the few-token path
+    assert ws(4, 16, 8192, 8192, 64) == ws(2, 16, 8192, 8192, 64)
+    assert ws(5, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
     # bf16-weight layer: no few-token path, so the tiled GEMMs' workspace
     # at every M; its backward is laid out as the NF4 backward
     assert ws(2, 512, 4096, 4096, 16) == ws(0, 512, 4096, 4096, 16)
@@ -253,3 +256,37 @@ def test_bf16_layer_validation():
     assert bwd(N=320 + 1) == -2
     assert bwd(dx=P0) == -1                                   # dx over W
     assert bwd(dB=P4 + 196608 + 4) == -3
+
+
+def test_dropout_validation():
+    L = q.lib()
+    w = _weight(256, 256)
+    need = q.workspace_bytes(4, 16, 256, 256, 8)
+    base = dict(x=P3, M=16, A=P4, B=P4 + 8192, r=8, keep=P4 + (1 << 18), p=0.05, y=P4 + 65536,
+                ws=P4 + (1 << 19), wsb=need)
+
+    def fwd(**kw):
+        a = dict(base, **kw)
+        return L.qlora_linear_fwd_dropout(ctypes.byref(w), a["x"], a["M"], a["A"], a["B"], a["r"],
+                                          16.0, a["keep"], a["p"], a["y"], a["ws"], a["wsb"], None)
+    assert fwd(keep=None) == -1
+    assert fwd(p=1.0) == -1
+    assert fwd(p=-0.1) == -1
+    assert fwd(p=float("nan")) == -1
+    assert fwd(keep=P4 + (1 << 18) + 4) == -3
+    assert fwd(y=P4 + (1 << 18)) == -1                        # y over the mask
+    assert fwd(r=12) == -2
+    assert fwd(M=0) == 0
+    needb = q.workspace_bytes(5, 16, 256, 256, 8)
+
+    def bwd(**kw):
+        a = dict(base, dy=P3 + 16384, dx=P4 + 65536, dA=P4 + 131072, dB=P4 + 196608,
+                 wsb=needb)
+        a.update(kw)
+        return L.qlora_linear_bwd_dropout(ctypes.byref(w), a["x"], a["dy"], a["M"], a["A"],
+                                          a["B"], a["r"], 16.0, a["keep"], a["p"], a["dx"],
+                                          a["dA"], a["dB"], 0, a["ws"], a["wsb"], None)
+    assert bwd(keep=None) == -1
+    assert bwd(p=1.5) == -1
+    assert bwd(dx=P4 + (1 << 18)) == -1                       # dx over the mask
+    assert bwd(keep=P4 + 3) == -3
