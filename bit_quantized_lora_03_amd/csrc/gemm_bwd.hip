@@ -251,11 +251,13 @@ void dx_gemm_kernel(DxParams p) {
       for (int j = 0; j < MS; ++j) {
         const int64_t m = m0 + 32 * MS * wm + 32 * j + lr;
         const int64_t kw = k0 + 128 * wk + 32 * i;
+        // the lane half's bits first, so every bit index below is a constant
         const uint32_t word = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-            kres, (int)(uint32_t)(m * (K / 8) + kw / 8), 0, 0);
+                                  kres, (int)(uint32_t)(m * (K / 8) + kw / 8), 0, 0) >>
+                              (4 * lg);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int bit = 8 * (v >> 2) + 4 * lg + (v & 3);
+          const int bit = 8 * (v >> 2) + (v & 3);
           acc[i][j][v] = ((word >> bit) & 1u) ? acc[i][j][v] : 0.0f;
         }
       }
