@@ -11,7 +11,7 @@ What it computes (numpy, fp64 unless a step fixes another precision):
 * ``nf4``   -- the 16 NF4 levels and their decision thresholds, the blockwise
   absmax quantiser (blocks of 64, two 4-bit codes per byte), the 8-bit
   double quantisation of the block scales (groups of 256) and the bit-exact
-  dequantisation to bf16.
+  dequantisation to bf16 (and, for the fp16 compute-type variant, to fp16).
 * ``lora_linear`` -- the layer y = x.W'^T + (alpha/r).(x.A^T).B^T and its
   gradients dX, dA, dB on the decoded weight W', optionally with LoRA
   dropout on the adapter's input (the keep-mask is an input).
@@ -44,6 +44,9 @@ from .nf4 import (  # noqa: F401
     double_quant,
     dequant_scales,
     dequant_nf4_bits,
+    dequant_nf4_f16_bits,
+    f16_rne_bits,
+    f16_bits_to_f64,
     storage_bits_per_weight,
 )
 from .lora_linear import lora_linear_fwd, lora_linear_bwd, lora_scale, dropped_input  # noqa: F401

@@ -124,6 +124,20 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def f16_rne_bits(values_f32: np.ndarray) -> np.ndarray:
+    """Round fp32 values to IEEE binary16 (round to nearest even, with
+    subnormals and overflow to infinity) and return the bits -- numpy's
+    float32 -> float16 conversion, which is that IEEE operation."""
+    v = np.ascontiguousarray(values_f32, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        return v.astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen binary16 bit patterns to fp64 exactly."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
 # --------------------------------------------------------------------------
 # Level-1 quantiser: blockwise absmax, NF4 codes, nibble packing
 # --------------------------------------------------------------------------
@@ -244,6 +258,25 @@ def dequant_nf4_bits(packed: np.ndarray, q: np.ndarray, step: np.ndarray,
     prod = (levels[codes] * scale[block_of_elem].astype(np.float64)
             ).astype(np.float32)
     return bf16_rne_bits(prod)
+
+
+def dequant_nf4_f16_bits(packed: np.ndarray, q: np.ndarray, step: np.ndarray,
+                         n: int, blocksize: int = BLOCK,
+                         blocksize2: int = GROUP) -> np.ndarray:
+    """Dequantise to fp16 bit patterns, bit-exactly: the fp16 compute-type
+    variant.  "QLoRA: Fine-Tuning a 7B Model on a 16GB GPU" (digipro.cn),
+    the flags paragraph: compute_dtype float16 dequantises to fp16 for the
+    matrix multiplies.  Reading: as the bf16 dequantisation, with the one
+    fp32 product rounded to binary16 (nearest even) instead:
+    w' = fp16_rne(fp32(L32[code] * s')).
+    """
+    codes = unpack_codes(packed, n)
+    scale = dequant_scales(q, step, blocksize2)
+    block_of_elem = np.arange(n) // blocksize
+    levels = nf4_levels_f32().astype(np.float64)
+    prod = (levels[codes] * scale[block_of_elem].astype(np.float64)
+            ).astype(np.float32)
+    return f16_rne_bits(prod)
 
 
 def storage_bits_per_weight(n: int, double_quantised: bool = True,

@@ -17,6 +17,7 @@ from tests import test_oracle_levels as tl
 from tests import test_oracle_linear as tlin
 from tests import test_oracle_merge as tm
 from tests import test_oracle_dropout as tdo
+from tests import test_oracle_f16 as tf16
 from tests import test_oracle_quant as tq
 
 
@@ -143,6 +144,14 @@ def _fwd_mask_on_base_too(x, w, A, B, alpha, keep=None, p=0.0):
     return _ORIG["fwd"](xd, w, A, B, alpha, keep=keep, p=p)
 
 
+def _f16_truncating(values_f32):
+    # round toward zero: go through float64 -> float16 after clearing the
+    # bits below fp16's precision (a plausible cheap conversion)
+    v = np.ascontiguousarray(values_f32, dtype=np.float32).view(np.uint32) & 0xFFFFE000
+    with np.errstate(over="ignore"):
+        return v.view(np.float32).astype(np.float16).view(np.uint16)
+
+
 _ORIG = {
     "merge": om.merge_adapter,
     "thr": on.nf4_thresholds_f32,
@@ -191,6 +200,9 @@ CASES = [
     ("dropout mask missing on dX's adapter term",
      [(oracle, "lora_linear_bwd", _bwd_dx_adapter_unmasked)],
      lambda: tdo.test_adjoint_identity_for_x(60)),
+    ("fp16 conversion truncating", [(on, "f16_rne_bits", _f16_truncating),
+                                    (oracle, "f16_rne_bits", _f16_truncating)],
+     tf16.test_f16_rounding_hand_values),
     ("dropout applied to the base term too", [(oracle, "lora_linear_fwd", _fwd_mask_on_base_too)],
      tdo.test_nothing_kept_leaves_the_base_alone),
 ]
