@@ -481,6 +481,37 @@ def main():
                 "over_no_dropout": round((t_fd + t_bd) / (t_f + t_b), 4)}
         del keep_d, ws_d
 
+    # ---- the fp16 compute-type variant of the same fwd + bwd (same packed
+    # weight; x, A, B, dy in fp16), each timed right after the bf16 call ----
+    f16 = None
+    if kind != "fwd":
+        def h16(t):
+            return t.view(torch.bfloat16).float().half().view(torch.int16)
+        x16, dy16 = h16(x_d), h16(dy_d)
+        A16 = h16(A_d) if r else None
+        B16 = h16(B_d) if r else None
+        need16 = max(q.workspace_bytes(6, M, N, K, r), q.workspace_bytes(7, M, N, K, r), 256)
+        ws_h = torch.empty(need16, dtype=torch.uint8, device=dev)
+        wt_h = weights[0][3]
+
+        def fwd_h():
+            check(lib.qlora_linear_fwd_f16(ctypes.byref(wt_h), P(x16), M, P(A16), P(B16), r,
+                                           alpha, P(y), P(ws_h), ws_h.numel(), sp()), "fwd f16")
+
+        def bwd_h():
+            check(lib.qlora_linear_bwd_f16(ctypes.byref(wt_h), P(x16), P(dy16), M, P(A16),
+                                           P(B16), r, alpha, P(dx), P(dA) if r else None,
+                                           P(dB) if r else None, 0, P(ws_h), ws_h.numel(),
+                                           sp()), "bwd f16")
+        t_f = timed(lambda i: fwd(0), reps)
+        t_fh = timed(lambda i: fwd_h(), reps)
+        t_b = timed(lambda i: bwd(), reps)
+        t_bh = timed(lambda i: bwd_h(), reps)
+        f16 = {"fwd_ms": round(t_fh, 5), "bwd_ms": round(t_bh, 5),
+               "bf16_fwd_ms": round(t_f, 5), "bf16_bwd_ms": round(t_b, 5),
+               "over_bf16": round((t_fh + t_bh) / (t_f + t_b), 4)}
+        del x16, dy16, A16, B16, ws_h
+
     # ---- adapter merge for export (not part of the step): W_m = W + s.B.A,
     # fp32 and bf16 exports, from the NF4 base and from the fp32 original ----
     merge = None
@@ -571,6 +602,7 @@ def main():
         "ops": {k: round(v, 5) for k, v in ops.items()},
         "vs_unquantised": unq,
         "dropout": drop,
+        "fp16": f16,
         "merge": merge,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "step_s"},
         "wall_s": round(wall, 4),

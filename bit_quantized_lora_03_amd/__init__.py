@@ -16,14 +16,17 @@ from ._lib import (  # noqa: F401
     PackedWeight,
     QloraError,
     dequantize,
+    dequantize_f16,
     double_quant,
     lib,
     linear_bf16_bwd,
     linear_bf16_fwd,
     linear_bwd,
     linear_bwd_dropout,
+    linear_bwd_f16,
     linear_fwd,
     linear_fwd_dropout,
+    linear_fwd_f16,
     merge_adapter,
     nf4_levels,
     quantize_nf4,

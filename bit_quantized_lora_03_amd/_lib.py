@@ -24,6 +24,7 @@ EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
            "qlora_dequantize_nf4",
            "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_workspace_bytes",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
+           "qlora_dequantize_nf4_f16", "qlora_linear_fwd_f16", "qlora_linear_bwd_f16",
            "qlora_linear_bf16_fwd", "qlora_linear_bf16_bwd",
            "qlora_merge_adapter", "qlora_nf4_levels", "qlora_status_string")
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
                              ctypes.c_int),
         "qlora_linear_workspace_bytes": ([i32, i64, i64, i64, i32], sz),
         "qlora_merge_adapter": ([wp, vp, i64, i64, vp, vp, i32, f32, vp, vp, vp], ctypes.c_int),
+        "qlora_dequantize_nf4_f16": ([wp, vp, vp], ctypes.c_int),
+        "qlora_linear_fwd_f16": ([wp, vp, i64, vp, vp, i32, f32, vp, vp, sz, vp], ctypes.c_int),
+        "qlora_linear_bwd_f16": ([wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, i32, vp, sz, vp],
+                                 ctypes.c_int),
         "qlora_linear_fwd_dropout": ([wp, vp, i64, vp, vp, i32, f32, vp, f32, vp, vp, sz, vp],
                                      ctypes.c_int),
         "qlora_linear_bwd_dropout": ([wp, vp, vp, i64, vp, vp, i32, f32, vp, f32, vp, vp, vp, i32,
@@ -240,6 +245,54 @@ def linear_bwd(pw: PackedWeight, x, dy, A, B, alpha: float, need_dx: bool = True
                                  float(alpha), _ptr(dx), _ptr(dA), _ptr(dB), int(accumulate),
                                  _ptr(ws), need if workspace is None else ws.numel(),
                                  _stream_ptr()), "qlora_linear_bwd")
+    return dx, dA, dB
+
+
+def dequantize_f16(pw: PackedWeight):
+    """PackedWeight -> fp16 bit patterns as an int16 device tensor [N, K]."""
+    torch = _torch()
+    out = torch.empty((pw.N, pw.K), dtype=torch.int16, device=pw.codes.device)
+    s = pw.struct()
+    check(lib().qlora_dequantize_nf4_f16(ctypes.byref(s), _ptr(out), _stream_ptr()),
+          "qlora_dequantize_nf4_f16")
+    return out
+
+
+def linear_fwd_f16(pw: PackedWeight, x, A, B, alpha: float, y=None, workspace=None):
+    """The fp16 compute-type forward: x, A, B (fp16 or int16 bit patterns)
+    and y in fp16."""
+    torch = _torch()
+    M = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if y is None:
+        y = torch.empty((M, pw.N), dtype=x.dtype, device=x.device)
+    ws, need = _ws(6, M, pw.N, pw.K, r, x.device, workspace)
+    s = pw.struct()
+    check(lib().qlora_linear_fwd_f16(ctypes.byref(s), _ptr(x), M, _ptr(A), _ptr(B), r,
+                                     float(alpha), _ptr(y), _ptr(ws),
+                                     need if workspace is None else ws.numel(), _stream_ptr()),
+          "qlora_linear_fwd_f16")
+    return y
+
+
+def linear_bwd_f16(pw: PackedWeight, x, dy, A, B, alpha: float, need_dx: bool = True, dA=None,
+                   dB=None, accumulate: bool = False, workspace=None):
+    """The fp16 compute-type backward: (dx fp16 or None, dA fp32, dB fp32)."""
+    torch = _torch()
+    M = dy.shape[0]
+    r = 0 if A is None else A.shape[0]
+    dx = torch.empty((M, pw.K), dtype=dy.dtype, device=dy.device) if need_dx else None
+    if r > 0:
+        if dA is None:
+            dA = torch.empty((r, pw.K), dtype=torch.float32, device=dy.device)
+        if dB is None:
+            dB = torch.empty((pw.N, r), dtype=torch.float32, device=dy.device)
+    ws, need = _ws(7, M, pw.N, pw.K, r, dy.device, workspace)
+    s = pw.struct()
+    check(lib().qlora_linear_bwd_f16(ctypes.byref(s), _ptr(x), _ptr(dy), M, _ptr(A), _ptr(B), r,
+                                     float(alpha), _ptr(dx), _ptr(dA), _ptr(dB), int(accumulate),
+                                     _ptr(ws), need if workspace is None else ws.numel(),
+                                     _stream_ptr()), "qlora_linear_bwd_f16")
     return dx, dA, dB
 
 

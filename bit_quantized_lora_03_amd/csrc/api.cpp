@@ -173,9 +173,10 @@ struct Wref {
 };
 
 // keep (or null) and p: LoRA dropout on the adapter's input
+// f16: the fp16 compute type (x, A, B, y in fp16), NF4 weight, no dropout
 int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
              int32_t r, float alpha, const uint8_t* keep, float p, uint16_t* y,
-             void* workspace, size_t ws_bytes, void* stream) {
+             void* workspace, size_t ws_bytes, void* stream, bool f16 = false) {
   try {
     int st = QLORA_OK;
     if ((st = check_rank(r)) != QLORA_OK) return st;
@@ -191,7 +192,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
         (keep && !aligned16(keep)))
       return QLORA_EALIGN;
     // the few-token decode kernel has no dropout: the tiled path then runs
-    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep);
+    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep && !f16);
     if (ws.total > 0) {
       if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
       if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
@@ -218,13 +219,13 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
     if (r > 0) {
       xs = at<uint16_t>(workspace, ws.xs_off);
       const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), K, 0, keep};
-      if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s))) !=
+      if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s, f16))) !=
           QLORA_OK)
         return st;
     }
     float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
     return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->step, w->wbf, x, xs, B, y,
-                                             part, M, N, K, r, L, s));
+                                             part, M, N, K, r, L, s, f16));
   } catch (...) {
     return QLORA_EHIP;
   }
@@ -233,7 +234,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
 int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, const uint16_t* A,
              const uint16_t* B, int32_t r, float alpha, const uint8_t* keep, float p,
              uint16_t* dx, float* dA, float* dB, int32_t accumulate, void* workspace,
-             size_t ws_bytes, void* stream) {
+             size_t ws_bytes, void* stream, bool f16 = false) {
   try {
     int st = QLORA_OK;
     if ((st = check_rank(r)) != QLORA_OK) return st;
@@ -250,7 +251,8 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
       if (overlap(dA, (size_t)r * K * 4, dB, (size_t)N * r * 4)) return QLORA_EINVAL;
       // the gradient kernel with no tokens writes zeros (or adds nothing)
       const qlora::LoraGradJob jb{nullptr, nullptr, dB, N, 0}, ja{nullptr, nullptr, dA, K, 1};
-      return hip_status(qlora::launch_lora_grad(jb, ja, 0, r, accumulate, as_stream(stream)));
+      return hip_status(
+          qlora::launch_lora_grad(jb, ja, 0, r, accumulate, as_stream(stream), f16));
     }
     if (!dy) return QLORA_EINVAL;
     if (r > 0 && (!A || !B || !x || !dA || !dB)) return QLORA_EINVAL;
@@ -292,17 +294,18 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
       uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
       uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
       const qlora::LoraProjJob jx{x, A, xs, xsT, K, 0, keep}, jg{dy, B, gs, gsT, N, 1, nullptr};
-      if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, s))) != QLORA_OK)
+      if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, s, f16))) != QLORA_OK)
         return st;
       // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x~
       const qlora::LoraGradJob jb{dy, xsT, dB, N, 0, nullptr}, ja{x, gsT, dA, K, 1, keep};
-      if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, s))) != QLORA_OK)
+      if ((st = hip_status(qlora::launch_lora_grad(jb, ja, M, r, accumulate, s, f16))) !=
+          QLORA_OK)
         return st;
     }
     if (dx) {
       float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
       if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->step, w->wbf, keep, dy, gs,
-                                                 A, dx, part, M, N, K, r, L, s))) != QLORA_OK)
+                                                 A, dx, part, M, N, K, r, L, s, f16))) != QLORA_OK)
         return st;
     }
     return QLORA_OK;
@@ -347,8 +350,8 @@ size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
     return 0;
   if (op == 0) return fwd_layout(M, N, K, r).total;
   if (op == 1 || op == 3) return bwd_layout(M, N, K, r).total;
-  if (op == 2 || op == 4) return fwd_layout(M, N, K, r, false).total;
-  if (op == 5) return bwd_layout(M, N, K, r).total;
+  if (op == 2 || op == 4 || op == 6) return fwd_layout(M, N, K, r, false).total;
+  if (op == 5 || op == 7) return bwd_layout(M, N, K, r).total;
   return 0;
 }
 
@@ -415,7 +418,7 @@ int qlora_quantize_nf4_dq(const float* w, int64_t n_elems, uint8_t* codes, float
   }
 }
 
-int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream) {
+static int dequantize_impl(const qlora_nf4_weight* w, uint16_t* out, void* stream, bool f16) {
   try {
     if (!w || !w->codes || !w->qscale || !w->dq_step || !out) return QLORA_EINVAL;
     if (w->N <= 0 || w->K <= 0) return QLORA_EINVAL;
@@ -428,10 +431,39 @@ int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream)
     if (overlap(out, no, w->codes, (size_t)n / 2) || overlap(out, no, w->qscale, (size_t)n / 64))
       return QLORA_EINVAL;
     return hip_status(qlora::launch_dequant(w->codes, w->qscale, w->dq_step, n / 64, out,
-                                            levels_arg(), as_stream(stream)));
+                                            levels_arg(), as_stream(stream), f16));
   } catch (...) {
     return QLORA_EHIP;
   }
+}
+
+int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream) {
+  return dequantize_impl(w, out, stream, false);
+}
+
+int qlora_dequantize_nf4_f16(const qlora_nf4_weight* w, uint16_t* out, void* stream) {
+  return dequantize_impl(w, out, stream, true);
+}
+
+int qlora_linear_fwd_f16(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
+                         const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                         uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, 0.0f, y, workspace, ws_bytes, stream,
+                  true);
+}
+
+int qlora_linear_bwd_f16(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
+                         int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                         uint16_t* dx, float* dA, float* dB, int32_t accumulate, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, nullptr, 0.0f, dx, dA, dB, accumulate,
+                  workspace, ws_bytes, stream, true);
 }
 
 int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, const uint16_t* A,

@@ -10,10 +10,16 @@ namespace qlora {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Compute-type traits (bf16 or fp16), defined with the MFMA wrappers below.
+struct Bf16T;
+struct F16T;
 
 // The 16 fp32 NF4 levels, passed to kernels by value (lands in SGPRs).
 struct Nf4Levels {
@@ -71,14 +77,16 @@ struct Nf4Lut {
   uint32_t hi[4];
 };
 
+template <class DT = Bf16T>
 __device__ __forceinline__ Nf4Lut nf4_make_lut(const Nf4Levels& L, float scale) {
   uint32_t p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    // one fp32 product per level, then round-to-nearest-even to bf16
+    // one fp32 product per level, then round-to-nearest-even to the
+    // compute type
     const float a = L.v[2 * i] * scale;
     const float b = L.v[2 * i + 1] * scale;
-    p[i] = pack_bf16x2(a, b);
+    p[i] = DT::pack2(a, b);
   }
   Nf4Lut t;
 #pragma unroll
@@ -210,12 +218,13 @@ __device__ __forceinline__ BlockWork block_work(int64_t id, int64_t total, int64
 // 32-column slice goes through the wave's own LDS area (32 x (32 NI + 4)
 // fp32; the 4-float pad puts consecutive columns 4 banks apart) and comes
 // back row-contiguous: 8 NI lanes then store one column's 32 NI rows.
-// `part` selects fp32 partials, otherwise values are rounded to bf16.
+// `part` selects fp32 partials, otherwise values are rounded to the
+// compute type DT.
 template <int NI>
 constexpr int epi_stride() { return 32 * NI + 4; }
 template <int NI>
 constexpr int epi_floats() { return 32 * epi_stride<NI>(); }  // per wave
-template <int NI, int NJ>
+template <int NI, int NJ, class DT = Bf16T>
 __device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[NI][NJ], float* scratch,
                                                int64_t row0, int64_t col0, int64_t nrows,
                                                int64_t ncols, bool part, float* outf,
@@ -247,8 +256,8 @@ __device__ __forceinline__ void store_acc_tile(const f32x16_t (&acc)[NI][NJ], fl
           *reinterpret_cast<f32x4_t*>(outf + m * ld + row) = v;
         } else {
           u32x2_t o;
-          o[0] = pack_bf16x2(v[0], v[1]);
-          o[1] = pack_bf16x2(v[2], v[3]);
+          o[0] = DT::pack2(v[0], v[1]);
+          o[1] = DT::pack2(v[2], v[3]);
           *reinterpret_cast<u32x2_t*>(outh + m * ld + row) = o;
         }
       }
@@ -263,5 +272,53 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
 __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
+
+// The 16-bit compute type of a kernel: bf16 (the layer's) or fp16 (its
+// fp16 compute-type variant).  Operands travel as raw 16-bit patterns;
+// these are the only places the format matters: fp32 -> 16-bit conversion
+// (round to nearest even), the MFMAs and the two-term dot product.
+// (By-value helpers: a bit_cast of one element of a register vector to a
+// 2-vector read element 0 whatever the index.)
+struct Bf16T {
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+  static __device__ __forceinline__ uint16_t cvt(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+  }
+  static __device__ __forceinline__ float tof(uint16_t h) { return bf16_bits_to_f32(h); }
+  static __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return mfma32x32x16(a, b, c);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return mfma16x16x32(a, b, c);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+  }
+};
+struct F16T {
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const f16x2_t v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ uint16_t cvt(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
+  static __device__ __forceinline__ float tof(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+  }
+  static __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
+                                  __builtin_bit_cast(f16x2_t, b), c, false);
+  }
+};
 
 }  // namespace qlora

@@ -90,7 +90,9 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 // keep bits, the base term is not.  Both share the accumulators, so the
 // adapter rows run first, the accumulators are masked, and the base
 // reduction adds onto them: the sum is still rounded once.
-template <int MS, int WF, bool DROP>
+//
+// DT: the 16-bit compute type (Bf16T, or F16T for the fp16 variant).
+template <int MS, int WF, bool DROP, class DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
   constexpr bool NF4 = WF == kWeightNf4;
@@ -206,7 +208,7 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < MS; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < MS; ++j) acc[i][j] = DT::mfma32(a[i], b[j], acc[i][j]);
   };
 
   // --- adapter rows: gs [M, 2r] against [A ; A] (last split only) ---
@@ -282,7 +284,7 @@ void dx_gemm_kernel(DxParams p) {
     load_dy(st0, Y[0]);
     store_dy(0, Y[0]);
     if constexpr (NF4) {
-      const Nf4Lut lut = nf4_make_lut(p.L, nf4_block_scale(C[0].q, C[0].st));
+      const Nf4Lut lut = nf4_make_lut<DT>(p.L, nf4_block_scale(C[0].q, C[0].st));
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         store8(0, c, nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]));
@@ -347,8 +349,8 @@ void dx_gemm_kernel(DxParams p) {
           }
         } else if (u < 4) {
           if (u == 0) sc = nf4_block_scale(cn.q, cn.st);
-          pk[2 * u] = pack_bf16x2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
-          pk[2 * u + 1] = pack_bf16x2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
+          pk[2 * u] = DT::pack2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
+          pk[2 * u + 1] = DT::pack2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
         } else if (u < 8) {
           const int j = u - 4;
           lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
@@ -379,7 +381,7 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
         for (int s2 = 0; s2 < SPK; ++s2) {
           const int i = s2 / MS, j = s2 % MS;
-          acc[i][j] = mfma32x32x16(op[kk & 1][0][i], op[kk & 1][1][j], acc[i][j]);
+          acc[i][j] = DT::mfma32(op[kk & 1][0][i], op[kk & 1][1][j], acc[i][j]);
           if (kk < 3 && s2 >= SPK - NRD) read_op(kk + 1, (kk + 1) & 1, s2 - (SPK - NRD));
           constexpr int UPS = 16 / SPK;  // units per slot: 64 units over 4 SPK slots
 #pragma unroll
@@ -403,11 +405,11 @@ void dx_gemm_kernel(DxParams p) {
   __syncthreads();  // the LDS stages are free from here on
   float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<4>();
   if (bw.tail >= 0)  // tile-local [TM][256] partial
-    store_acc_tile<4, MS>(acc, scratch, 128 * wk, 32 * MS * wm, K - k0, M - m0, true,
+    store_acc_tile<4, MS, DT>(acc, scratch, 128 * wk, 32 * MS * wm, K - k0, M - m0, true,
                           p.part + ((int64_t)z * p.tail_q + bw.tail) * TM * TILE, nullptr,
                           TILE, lane);
   else
-    store_acc_tile<4, MS>(acc, scratch, k0 + 128 * wk, m0 + 32 * MS * wm, K, M, nz > 1,
+    store_acc_tile<4, MS, DT>(acc, scratch, k0 + 128 * wk, m0 + 32 * MS * wm, K, M, nz > 1,
                           nz > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
 }
 
@@ -415,7 +417,7 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
                           const uint16_t* wbf, const uint8_t* keep, const uint16_t* dy,
                           const uint16_t* gs, const uint16_t* A, uint16_t* dx, float* part,
                           int64_t M, int64_t N, int64_t K, int r, const Nf4Levels& L,
-                          hipStream_t s) {
+                          hipStream_t s, bool f16) {
   // output M x K, reduction N: the forward GEMM's schedule with the roles
   // of N and K exchanged
   const GemmConfig cfg = gemm_config(M, K, N);
@@ -443,29 +445,36 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   const int64_t blocks = gemm_blocks(cfg, M, K);
   const bool nf4 = wbf == nullptr, drop = keep != nullptr && r > 0;
   const dim3 grid((unsigned)blocks);
-  // MS = 4 (256-token tile) or 2; weight format; dropout mask or not
+  // token tile; weight format; dropout mask or not; compute type (fp16
+  // with the NF4 weight and no mask only)
   if (cfg.tm == 256) {
-    if (nf4 && !drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false>), grid, dim3(256), 0, s, p);
+    if (f16)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, F16T>), grid, dim3(256), 0, s, p);
+    else if (nf4 && !drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, Bf16T>), grid, dim3(256), 0, s, p);
     else if (nf4)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, true, Bf16T>), grid, dim3(256), 0, s, p);
     else if (!drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, false>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, false, Bf16T>), grid, dim3(256), 0, s,
+                         p);
     else
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, true, Bf16T>), grid, dim3(256), 0, s, p);
   } else {
-    if (nf4 && !drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false>), grid, dim3(256), 0, s, p);
+    if (f16)
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, F16T>), grid, dim3(256), 0, s, p);
+    else if (nf4 && !drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, Bf16T>), grid, dim3(256), 0, s, p);
     else if (nf4)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, true, Bf16T>), grid, dim3(256), 0, s, p);
     else if (!drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, false>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, false, Bf16T>), grid, dim3(256), 0, s,
+                         p);
     else
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, true>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, true, Bf16T>), grid, dim3(256), 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_gemm_reduce(cfg, part, M, K, dx, s);
+  return launch_gemm_reduce(cfg, part, M, K, dx, s, f16);
 }
 
 }  // namespace qlora

@@ -106,7 +106,8 @@ __device__ __forceinline__ void swap_halves(u32x4_t& a, u32x4_t& b, int v) {
 // described above; kWeightBf16 (the unquantised comparison layer) loads the
 // 64 bf16 of the same row tile instead and skips the table and decode, so
 // the two share every other part of the kernel.
-template <int JT, int WF>
+// DT: the 16-bit compute type (Bf16T, or F16T for the fp16 variant).
+template <int JT, int WF, class DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(FwdParams p) {
   constexpr bool NF4 = WF == kWeightNf4;
@@ -270,8 +271,8 @@ void fwd_gemm_kernel(FwdParams p) {
       if constexpr (!NF4) return;
       else if (u < 4) {
         if (u == 0) sc = nf4_block_scale(c.q, c.st);
-        pk[2 * u] = pack_bf16x2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
-        pk[2 * u + 1] = pack_bf16x2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
+        pk[2 * u] = DT::pack2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
+        pk[2 * u + 1] = DT::pack2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
       } else {
         const int j = u - 4;
         lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
@@ -355,7 +356,7 @@ void fwd_gemm_kernel(FwdParams p) {
 #pragma unroll
         for (int s = 0; s < SPK; ++s) {
           const int j = s >> 1, i = s & 1;
-          acc[i][j] = mfma32x32x16(Ap[kk & 1][i], op[kk & 1][j], acc[i][j]);
+          acc[i][j] = DT::mfma32(Ap[kk & 1][i], op[kk & 1][j], acc[i][j]);
           if (i == 1) {
             // operand j of the next step: this tile's, or the next tile's
             // first (its stage was completed before the last barrier)
@@ -444,7 +445,7 @@ void fwd_gemm_kernel(FwdParams p) {
         for (int j = 0; j < JT; ++j) {
           const u32x4_t b = read_b(0, kk, j);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) acc[i][j] = mfma32x32x16(a[i][kk], b, acc[i][j]);
+          for (int i = 0; i < 2; ++i) acc[i][j] = DT::mfma32(a[i][kk], b, acc[i][j]);
         }
     }
   }
@@ -453,15 +454,16 @@ void fwd_gemm_kernel(FwdParams p) {
   __syncthreads();  // the LDS ring is free from here on
   float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<2>();
   if (bw.tail >= 0)  // tile-local [TM][256] partial
-    store_acc_tile<2, JT>(acc, scratch, 64 * wave, 0, N - n0, M - m0, true,
+    store_acc_tile<2, JT, DT>(acc, scratch, 64 * wave, 0, N - n0, M - m0, true,
                           p.part + ((int64_t)z * p.tail_q + bw.tail) * TM * TILE_N, nullptr,
                           TILE_N, lane);
   else
-    store_acc_tile<2, JT>(acc, scratch, n0 + 64 * wave, m0, N, M, nz > 1,
+    store_acc_tile<2, JT, DT>(acc, scratch, n0 + 64 * wave, m0, N, M, nz > 1,
                           nz > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
 }
 
-// out[i] = bf16(sum_z part[z][i]), i over M*N (4 per thread), fixed order.
+// out[i] = DT(sum_z part[z][i]), i over M*N (4 per thread), fixed order.
+template <class DT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int splits, int64_t count,
                                                             uint16_t* __restrict__ out) {
@@ -476,25 +478,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
       s[3] += v[3];
     }
     u32x2_t o;
-    o[0] = pack_bf16x2(s[0], s[1]);
-    o[1] = pack_bf16x2(s[2], s[3]);
+    o[0] = DT::pack2(s[0], s[1]);
+    o[1] = DT::pack2(s[2], s[3]);
     *reinterpret_cast<u32x2_t*>(out + i) = o;
   }
 }
 
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, uint16_t* out,
-                                hipStream_t s) {
+                                hipStream_t s, bool f16) {
   int64_t g = (count / 4 + 255) / 256;
   if (g > 8192) g = 8192;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)g), dim3(256), 0, s, part, splits,
-                     count, out);
+  if (f16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<F16T>, dim3((unsigned)g), dim3(256), 0, s, part,
+                       splits, count, out);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<Bf16T>, dim3((unsigned)g), dim3(256), 0, s, part,
+                       splits, count, out);
   return hipGetLastError();
 }
 
-// Tail partials -> bf16 output: out[m0 + mi][n0 + ni] = bf16(sum_z
+// Tail partials -> 16-bit output: out[m0 + mi][n0 + ni] = DT(sum_z
 // tpart[z][q][mi][ni]) for the tail tiles q, fixed split order; 4 elements
 // per thread.
+template <class DT>
 __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ tpart,
                                                           int tm, int64_t full, int tail_q,
                                                           int tail_s, int64_t M, int64_t Nout,
@@ -520,8 +527,8 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restric
       sum[3] += v[3];
     }
     u32x2_t o;
-    o[0] = pack_bf16x2(sum[0], sum[1]);
-    o[1] = pack_bf16x2(sum[2], sum[3]);
+    o[0] = DT::pack2(sum[0], sum[1]);
+    o[1] = DT::pack2(sum[2], sum[3]);
     *reinterpret_cast<u32x2_t*>(out + m * Nout + n) = o;
   }
 }
@@ -592,23 +599,27 @@ size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout) {
 }
 
 hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M, int64_t Nout,
-                              uint16_t* out, hipStream_t s) {
+                              uint16_t* out, hipStream_t s, bool f16) {
   if (c.tail_q > 0) {
     const int64_t count = (int64_t)c.tail_q * c.tm * TILE_N / 4;
     int64_t g = (count + 255) / 256;
     if (g > 8192) g = 8192;
-    hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)g), dim3(256), 0, s, part, c.tm,
-                       c.full, c.tail_q, c.tail_s, M, Nout, out);
+    if (f16)
+      hipLaunchKernelGGL(tail_reduce_kernel<F16T>, dim3((unsigned)g), dim3(256), 0, s, part,
+                         c.tm, c.full, c.tail_q, c.tail_s, M, Nout, out);
+    else
+      hipLaunchKernelGGL(tail_reduce_kernel<Bf16T>, dim3((unsigned)g), dim3(256), 0, s, part,
+                         c.tm, c.full, c.tail_q, c.tail_s, M, Nout, out);
     return hipGetLastError();
   }
-  if (c.splits > 1) return launch_splitk_reduce(part, c.splits, M * Nout, out, s);
+  if (c.splits > 1) return launch_splitk_reduce(part, c.splits, M * Nout, out, s, f16);
   return hipSuccess;
 }
 
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                            const uint16_t* wbf, const uint16_t* x, const uint16_t* xs,
                            const uint16_t* B, uint16_t* y, float* part, int64_t M, int64_t N,
-                           int64_t K, int r, const Nf4Levels& L, hipStream_t s) {
+                           int64_t K, int r, const Nf4Levels& L, hipStream_t s, bool f16) {
   const GemmConfig cfg = gemm_config(M, N, K);
   if (gemm_partial_bytes(cfg, M, N) > 0 && part == nullptr) return hipErrorInvalidValue;
   FwdParams p;
@@ -632,24 +643,26 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.L = L;
   const int64_t blocks = gemm_blocks(cfg, M, N);
   const bool nf4 = wbf == nullptr;
+  const dim3 grid((unsigned)blocks);
+  // token tile; weight format; compute type (fp16 with the NF4 weight only)
   if (cfg.tm == 256) {
-    if (nf4)
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4>), dim3((unsigned)blocks), dim3(256), 0,
-                         s, p);
+    if (f16)
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, F16T>), grid, dim3(256), 0, s, p);
+    else if (nf4)
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, Bf16T>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightBf16>), dim3((unsigned)blocks), dim3(256),
-                         0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightBf16, Bf16T>), grid, dim3(256), 0, s, p);
   } else {
-    if (nf4)
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4>), dim3((unsigned)blocks), dim3(256), 0,
-                         s, p);
+    if (f16)
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, F16T>), grid, dim3(256), 0, s, p);
+    else if (nf4)
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, Bf16T>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightBf16>), dim3((unsigned)blocks), dim3(256),
-                         0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightBf16, Bf16T>), grid, dim3(256), 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_gemm_reduce(cfg, part, M, N, y, s);
+  return launch_gemm_reduce(cfg, part, M, N, y, s, f16);
 }
 
 }  // namespace qlora

@@ -19,8 +19,10 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* qscale,
 hipError_t launch_quantize_dq(const float* w, int64_t n, uint8_t* codes, float* absmax,
                               uint8_t* qscale, float* step, const Nf4CodeBins& bins,
                               hipStream_t s);
+// out: bf16, or fp16 (f16) -- the same decode rounded to the compute type
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s);
+                          int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s,
+                          bool f16 = false);
 
 // lora_kernels.hip -- rank-r kernels of the adapter path
 // lora_proj: out[m][j] = hi, out[m][r + j] = lo, the bf16 pair of
@@ -40,8 +42,10 @@ struct LoraProjJob {
   const uint8_t* keep = nullptr;
 };
 // one job, or two in one launch (j1 non-null)
+// f16: the fp16 compute type (operands and the hi/lo pairs in fp16; no
+// keep-mask), else bf16.
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
-                            float scale, hipStream_t s);
+                            float scale, hipStream_t s, bool f16 = false);
 // lora_grad: C (+)= sum_m G[m][g] * (ST[j][m] + ST[r + j][m]), C [ldg, r]
 // (transposed == 0) or [r, ldg] (transposed == 1); both jobs in one launch,
 // each block reducing over all tokens itself.
@@ -54,7 +58,7 @@ struct LoraGradJob {
   const uint8_t* keep = nullptr;  // dropout mask on G, as in LoraProjJob (or null)
 };
 hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
-                            int accumulate, hipStream_t s);
+                            int accumulate, hipStream_t s, bool f16 = false);
 
 // gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T.
 // Schedule of a fused GEMM with an Mout x Nout output (Nout in tiles of 256)
@@ -76,16 +80,19 @@ int64_t gemm_blocks(const GemmConfig& c, int64_t M, int64_t Nout);
 size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout);
 // The weight is the NF4 one (codes, qscale, step) when wbf is null, else the
 // bf16 weight wbf [N, K] (the unquantised layer, same kernel skeleton).
+// f16: the fp16 compute type (x, xs, B, y in fp16; the NF4 weight decoded
+// to fp16); only with the NF4 weight.
 constexpr int kWeightNf4 = 0, kWeightBf16 = 1;
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
                            const uint16_t* wbf, const uint16_t* x, const uint16_t* xs,
                            const uint16_t* B, uint16_t* y, float* part, int64_t M, int64_t N,
-                           int64_t K, int r, const Nf4Levels& L, hipStream_t s);
+                           int64_t K, int r, const Nf4Levels& L, hipStream_t s,
+                           bool f16 = false);
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, uint16_t* out,
-                                hipStream_t s);
+                                hipStream_t s, bool f16 = false);
 // the reduction after a fused GEMM's main kernel, if its schedule has one
 hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M, int64_t Nout,
-                              uint16_t* out, hipStream_t s);
+                              uint16_t* out, hipStream_t s, bool f16 = false);
 
 // gemm_decode.hip -- forward for M <= 32.  Without an adapter one kernel
 // writes y.  With one, the weight tiles write fp32 sums to part[0][M][N + r]
@@ -106,7 +113,7 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
                           const uint16_t* wbf, const uint8_t* keep, const uint16_t* dy,
                           const uint16_t* gs, const uint16_t* A, uint16_t* dx, float* part,
                           int64_t M, int64_t N, int64_t K, int r, const Nf4Levels& L,
-                          hipStream_t s);
+                          hipStream_t s, bool f16 = false);
 
 // merge.hip -- W_m = W_base + scale . B . A for export.  The base is the NF4
 // weight (codes non-null) or the fp32 original w0; out_f32 and/or out_bf16

@@ -45,10 +45,6 @@ namespace {
 constexpr int kWaves = 8;             // waves per block (both kernels)
 constexpr int kThreads = 64 * kWaves;
 
-__device__ __forceinline__ uint16_t bf16_rne_bits(float v) {
-  return __builtin_bit_cast(uint16_t, (__bf16)v);
-}
-
 __host__ __device__ __forceinline__ int64_t pad32(int64_t M) { return (M + 31) / 32 * 32; }
 
 // Loads go through buffer descriptors: 32-bit lane offsets instead of 64-bit
@@ -145,22 +141,16 @@ __device__ __forceinline__ u32x4_t read_tr8(const uint16_t* slab, int stride, in
   return v;
 }
 
-// Two packed bf16 as the dot-product operand.  The word is taken by value:
-// __builtin_bit_cast applied to a vector element (x[i]) reads the vector's
-// first word whatever the index, with this compiler.
-__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) {
-  return __builtin_bit_cast(bf16x2_t, v);
-}
-
-// Store the bf16 pair of v for (m, j) in both layouts (m < Mp; rows past M
-// only get zeros in the transposed copy).
+// Store the 16-bit pair (compute type DT) of v for (m, j) in both layouts
+// (m < Mp; rows past M only get zeros in the transposed copy).
+template <class DT>
 __device__ __forceinline__ void put_split(const LoraProjJob& J, int64_t M, int r, int64_t m,
                                           int j, float v) {
   const int64_t Mp = pad32(M);
   uint16_t hi = 0, lo = 0;
   if (m < M) {
-    hi = bf16_rne_bits(v);
-    lo = bf16_rne_bits(v - bf16_bits_to_f32(hi));  // v - hi is exact
+    hi = DT::cvt(v);
+    lo = DT::cvt(v - DT::tof(hi));  // v - hi is exact
     J.out[m * 2 * r + j] = hi;
     J.out[m * 2 * r + r + j] = lo;
   }
@@ -180,7 +170,7 @@ __device__ __forceinline__ void put_split(const LoraProjJob& J, int64_t M, int r
 // wave's slab and come back transposed.
 // ---------------------------------------------------------------------------
 // DROP: the jobs may carry a keep-mask on X (LoRA dropout; see keep8).
-template <int JT, bool DROP>
+template <int JT, bool DROP, class DT>
 __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
                                                              int64_t blocks0, int64_t M, int r,
                                                              float scale) {
@@ -261,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
       const u32x4_t xv = DROP ? keep8(R.x[bb], R.kb[bb]) : R.x[bb];
       if (!kmajor) {
 #pragma unroll
-        for (int jt = 0; jt < JT; ++jt) acc[jt] = mfma16x16x32(xv, R.y[bb][jt], acc[jt]);
+        for (int jt = 0; jt < JT; ++jt) acc[jt] = DT::mfma16(xv, R.y[bb][jt], acc[jt]);
       } else {
 #pragma unroll
         for (int q = 0; q < JT; ++q) {
@@ -270,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
         }
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
-          acc[jt] = mfma16x16x32(xv, read_tr8(slab, RS, 8 * kg, 16 * jt, i), acc[jt]);
+          acc[jt] = DT::mfma16(xv, read_tr8(slab, RS, 8 * kg, 16 * jt, i), acc[jt]);
       }
     }
   };
@@ -302,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
     for (int w = 1; w < kWaves; ++w) sum += red[(w * 16 + tok) * REDS + j];
     const int64_t mo = m0 + tok;
     const int jo = jc + j;
-    if (jo < r && mo < Mp) put_split(J, M, r, mo, jo, scale * sum);
+    if (jo < r && mo < Mp) put_split<DT>(J, M, r, mo, jo, scale * sum);
   }
 }
 
@@ -321,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
 constexpr int kSmallT = 8, kSmallR = 8;  // tokens, rank columns per block
 constexpr int kSmallRed = 65;            // LDS row of a thread's 64 sums (+1: no bank conflicts)
 
-template <bool DROP>
+template <bool DROP, class DT>
 __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, LoraProjJob j1,
                                                               int64_t blocks0, int64_t M, int r,
                                                               float scale) {
@@ -402,8 +392,7 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
       for (int q = 0; q < kSmallR; ++q)
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp)
-          acc[i][q] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[pp]), as_bf16x2(yp[q][pp]),
-                                                      acc[i][q], false);
+          acc[i][q] = DT::dot2(xv[pp], yp[q][pp], acc[i][q]);
     }
   };
   Piece P0, P1;
@@ -431,7 +420,7 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
   const int64_t Mp = pad32(M);
   const int64_t mo = m0 + o / kSmallR;
   const int jo = jc + o % kSmallR;
-  if (part == 0 && mo < Mp && jo < r) put_split(J, M, r, mo, jo, scale * sum);
+  if (part == 0 && mo < Mp && jo < r) put_split<DT>(J, M, r, mo, jo, scale * sum);
 }
 
 // small jobs (few tokens x a small rank) go to lora_proj_small: measured
@@ -440,7 +429,7 @@ static bool proj_small(int64_t M, int r) { return M * r <= 16384; }
 
 static int proj_jt(int r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
 
-template <bool DROP>
+template <bool DROP, class DT>
 static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                               float scale, hipStream_t s) {
   if (proj_small(M, r)) {
@@ -449,8 +438,8 @@ static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int6
     const LoraProjJob jb = j1 ? *j1 : j0;
     const int64_t total = per_job * (j1 ? 2 : 1);
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((lora_proj_small_kernel<DROP>), dim3((unsigned)total), dim3(256), 0, s,
-                       j0, jb, per_job, M, r, scale);
+    hipLaunchKernelGGL((lora_proj_small_kernel<DROP, DT>), dim3((unsigned)total), dim3(256), 0,
+                       s, j0, jb, per_job, M, r, scale);
     return hipGetLastError();
   }
   const int jt = proj_jt(r);
@@ -462,21 +451,22 @@ static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int6
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)total);
   if (jt == 1)
-    hipLaunchKernelGGL((lora_proj_kernel<1, DROP>), grid, dim3(kThreads), 0, s, j0, jb, blocks0,
-                       M, r, scale);
+    hipLaunchKernelGGL((lora_proj_kernel<1, DROP, DT>), grid, dim3(kThreads), 0, s, j0, jb,
+                       blocks0, M, r, scale);
   else if (jt == 2)
-    hipLaunchKernelGGL((lora_proj_kernel<2, DROP>), grid, dim3(kThreads), 0, s, j0, jb, blocks0,
-                       M, r, scale);
+    hipLaunchKernelGGL((lora_proj_kernel<2, DROP, DT>), grid, dim3(kThreads), 0, s, j0, jb,
+                       blocks0, M, r, scale);
   else
-    hipLaunchKernelGGL((lora_proj_kernel<4, DROP>), grid, dim3(kThreads), 0, s, j0, jb, blocks0,
-                       M, r, scale);
+    hipLaunchKernelGGL((lora_proj_kernel<4, DROP, DT>), grid, dim3(kThreads), 0, s, j0, jb,
+                       blocks0, M, r, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
-                            float scale, hipStream_t s) {
-  if (j0.keep || (j1 && j1->keep)) return launch_proj<true>(j0, j1, M, r, scale, s);
-  return launch_proj<false>(j0, j1, M, r, scale, s);
+                            float scale, hipStream_t s, bool f16) {
+  if (f16) return launch_proj<false, F16T>(j0, j1, M, r, scale, s);  // no dropout in fp16
+  if (j0.keep || (j1 && j1->keep)) return launch_proj<true, Bf16T>(j0, j1, M, r, scale, s);
+  return launch_proj<false, Bf16T>(j0, j1, M, r, scale, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -490,7 +480,7 @@ hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_
 // loads, hi and lo as two MFMAs on the same G operand.
 // ---------------------------------------------------------------------------
 // DROP: the jobs may carry a keep-mask on G (LoRA dropout; see keep8).
-template <int JT, bool DROP>
+template <int JT, bool DROP, class DT>
 __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, LoraGradJob j1,
                                                              int64_t blocks0, int64_t M, int r,
                                                              int accumulate) {
@@ -580,8 +570,8 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
           const u32x4_t a = read_tr8(slab, GS, 8 * kg, 16 * gi, i);
 #pragma unroll
           for (int jt = 0; jt < JT; ++jt) {
-            acc[gi][jt] = mfma16x16x32(a, R.sh[bb][jt], acc[gi][jt]);
-            acc[gi][jt] = mfma16x16x32(a, R.sl[bb][jt], acc[gi][jt]);
+            acc[gi][jt] = DT::mfma16(a, R.sh[bb][jt], acc[gi][jt]);
+            acc[gi][jt] = DT::mfma16(a, R.sl[bb][jt], acc[gi][jt]);
           }
         }
       }
@@ -627,28 +617,29 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
   }
 }
 
-template <bool DROP>
+template <bool DROP, class DT>
 static hipError_t launch_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
                               int accumulate, hipStream_t s) {
   const int64_t b0 = j0.ldg / 64, b1 = j1.ldg / 64;
   if (b0 + b1 == 0 || r == 0) return hipSuccess;
   const dim3 grid((unsigned)(b0 + b1));
   if (r <= 16)
-    hipLaunchKernelGGL((lora_grad_kernel<1, DROP>), grid, dim3(kThreads), 0, s, j0, j1, b0, M,
-                       r, accumulate);
+    hipLaunchKernelGGL((lora_grad_kernel<1, DROP, DT>), grid, dim3(kThreads), 0, s, j0, j1,
+                       b0, M, r, accumulate);
   else if (r <= 32)
-    hipLaunchKernelGGL((lora_grad_kernel<2, DROP>), grid, dim3(kThreads), 0, s, j0, j1, b0, M,
-                       r, accumulate);
+    hipLaunchKernelGGL((lora_grad_kernel<2, DROP, DT>), grid, dim3(kThreads), 0, s, j0, j1,
+                       b0, M, r, accumulate);
   else
-    hipLaunchKernelGGL((lora_grad_kernel<4, DROP>), grid, dim3(kThreads), 0, s, j0, j1, b0, M,
-                       r, accumulate);
+    hipLaunchKernelGGL((lora_grad_kernel<4, DROP, DT>), grid, dim3(kThreads), 0, s, j0, j1,
+                       b0, M, r, accumulate);
   return hipGetLastError();
 }
 
 hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
-                            int accumulate, hipStream_t s) {
-  if (j0.keep || j1.keep) return launch_grad<true>(j0, j1, M, r, accumulate, s);
-  return launch_grad<false>(j0, j1, M, r, accumulate, s);
+                            int accumulate, hipStream_t s, bool f16) {
+  if (f16) return launch_grad<false, F16T>(j0, j1, M, r, accumulate, s);  // no dropout in fp16
+  if (j0.keep || j1.keep) return launch_grad<true, Bf16T>(j0, j1, M, r, accumulate, s);
+  return launch_grad<false, Bf16T>(j0, j1, M, r, accumulate, s);
 }
 
 }  // namespace qlora

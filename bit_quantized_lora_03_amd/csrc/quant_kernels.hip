@@ -239,6 +239,8 @@ __global__ __launch_bounds__(256) void double_quant_kernel(
 // Standalone dequantiser: one lane per 64-weight block (the decode routine
 // the GEMMs run on their tiles), 32 code bytes in, 128 bf16 bytes out.
 // ---------------------------------------------------------------------------
+// DT: the 16-bit output type (Bf16T, or F16T for the fp16 compute type).
+template <class DT>
 __global__ __launch_bounds__(256) void nf4_dequant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ qscale,
     const float* __restrict__ step, int64_t nb, uint16_t* __restrict__ out,
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
     const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(codes + (b << 5));
     const u32x4_t c0 = cp[0], c1 = cp[1];
-    const Nf4Lut lut = nf4_make_lut(L, nf4_block_scale(qscale[b], step[b >> 8]));
+    const Nf4Lut lut = nf4_make_lut<DT>(L, nf4_block_scale(qscale[b], step[b >> 8]));
     u32x4_t* op = reinterpret_cast<u32x4_t*>(out + (b << 6));
 #pragma unroll
     for (int i = 0; i < 4; ++i) op[i] = nf4_decode8(lut, c0[i]);
@@ -289,10 +291,15 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* qscale,
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s) {
+                          int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s,
+                          bool f16) {
   const int grid = grid_for(nb, 256, 256 * 16);
-  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid), dim3(256), 0, s, codes, qscale, step, nb,
-                     out, L);
+  if (f16)
+    hipLaunchKernelGGL(nf4_dequant_kernel<F16T>, dim3(grid), dim3(256), 0, s, codes, qscale, step,
+                       nb, out, L);
+  else
+    hipLaunchKernelGGL(nf4_dequant_kernel<Bf16T>, dim3(grid), dim3(256), 0, s, codes, qscale,
+                       step, nb, out, L);
   return hipGetLastError();
 }
 

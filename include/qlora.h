@@ -184,6 +184,27 @@ int qlora_merge_adapter(const qlora_nf4_weight* w, const float* w0, int64_t N, i
                         const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                         float* out_f32, uint16_t* out_bf16, void* stream);
 
+/* The fp16 compute-type variant.  [QLoRA: Fine-Tuning a 7B Model on a 16GB
+ * GPU, the flags paragraph]: compute_dtype float16 dequantises to fp16 for
+ * the matrix multiplies.  The same layer and the same packed weight, with
+ * every 16-bit tensor in IEEE binary16 instead of bf16:
+ *   qlora_dequantize_nf4_f16: out[i] = fp16_rne(fp32(L[code_i] * s'_b))
+ *   qlora_linear_fwd_f16 / qlora_linear_bwd_f16: x, A, B, y, dy, dx are
+ *     fp16 (uint16_t patterns); dA, dB fp32; fp32 accumulation, y and dx
+ *     rounded once to fp16 (nearest even).  Values beyond fp16's range
+ *     overflow to infinity (not checked).
+ * Arguments, errors and size limits as the bf16 calls; every M runs the
+ * tiled GEMMs (no few-token path); workspace
+ * qlora_linear_workspace_bytes(6 (forward) or 7 (backward), ...).         */
+int qlora_dequantize_nf4_f16(const qlora_nf4_weight* w, uint16_t* out, void* stream);
+int qlora_linear_fwd_f16(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
+                         const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                         uint16_t* y, void* workspace, size_t ws_bytes, void* stream);
+int qlora_linear_bwd_f16(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
+                         int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                         uint16_t* dx, float* dA, float* dB, int32_t accumulate, void* workspace,
+                         size_t ws_bytes, void* stream);
+
 /* Forward and backward with LoRA dropout on the adapter's input.
  * [QLoRA -- Module 12.4, "Hugging Face + BitsAndBytes"]: the adapter config
  * sets lora_dropout (0.05 there).  The pages give no formula; the standard
@@ -237,9 +258,10 @@ int qlora_linear_bf16_bwd(const uint16_t* W, int64_t N, int64_t K, const uint16_
                           int32_t accumulate, void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes for op 0 (forward) or 1 (backward) of the NF4 layer,
- * op 2 (forward) or 3 (backward) of the bf16-weight layer, or op 4
- * (forward) or 5 (backward) of the NF4 layer with dropout, at the given
- * shape; 0 for an invalid shape.  Host-only; never touches the GPU.        */
+ * op 2 (forward) or 3 (backward) of the bf16-weight layer, op 4 (forward)
+ * or 5 (backward) of the NF4 layer with dropout, or op 6 (forward) or 7
+ * (backward) of the fp16 compute type, at the given shape; 0 for an
+ * invalid shape.  Host-only; never touches the GPU.                        */
 size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
                                     int32_t r);
 

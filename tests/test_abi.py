@@ -78,7 +78,10 @@ def test_workspace_sizes():
     assert ws(0, 16, 4096, 100, 16) == 0          # K % 64
     assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
     assert ws(0, 16, 4096, 4096, 264) == 0        # r > 256
-    assert ws(6, 16, 4096, 4096, 16) == 0         # bad op
+    assert ws(8, 16, 4096, 4096, 16) == 0         # bad op
+    # fp16 compute type: the tiled path at every M, same layouts
+    assert ws(6, 16, 8192, 8192, 64) == ws(2, 16, 8192, 8192, 64)
+    assert ws(7, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
     # dropout: the forward never takes the few-token path
     assert ws(4, 16, 8192, 8192, 64) == ws(2, 16, 8192, 8192, 64)
     assert ws(5, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
@@ -290,3 +293,25 @@ def test_dropout_validation():
     assert bwd(p=1.5) == -1
     assert bwd(dx=P4 + (1 << 18)) == -1                       # dx over the mask
     assert bwd(keep=P4 + 3) == -3
+
+
+def test_f16_validation():
+    L = q.lib()
+    w = _weight(256, 256)
+    need = q.workspace_bytes(6, 16, 256, 256, 8)
+    assert L.qlora_dequantize_nf4_f16(ctypes.byref(w), None, None) == -1
+    assert L.qlora_dequantize_nf4_f16(ctypes.byref(w), P3 + 2, None) == -3
+    call = lambda **kw: L.qlora_linear_fwd_f16(
+        ctypes.byref(kw.get("w", w)), kw.get("x", P3), kw.get("M", 16), kw.get("A", P4),
+        kw.get("B", P4 + 8192), kw.get("r", 8), 16.0, kw.get("y", P4 + 65536),
+        kw.get("ws", P4 + (1 << 19)), kw.get("wsb", need), None)
+    assert call(w=_weight(250, 256)) == -2
+    assert call(r=12) == -2
+    assert call(x=None) == -1
+    assert call(y=P3) == -1
+    assert call(wsb=need - 1) == -5
+    assert call(M=0) == 0
+    needb = q.workspace_bytes(7, 16, 256, 256, 8)
+    assert L.qlora_linear_bwd_f16(ctypes.byref(w), P3, None, 16, P4, P4 + 8192, 8, 16.0,
+                                  P4 + 65536, P4 + 131072, P4 + 196608, 0, P4 + (1 << 19), needb,
+                                  None) == -1                     # no dy
