@@ -97,18 +97,21 @@ def make_layer(name):
     raise SystemExit(f"unknown workload {name}")
 
 
-def _gemm_schedule(M, Nout, Kred):
+def _gemm_schedule(M, Nout, Kred, narrow=False):
     """Mirror of the library's schedule for a fused GEMM with an M x Nout
     output and a reduction of Kred (for naming the launches in the roofline
-    line only): (token tile, uniform splits, tail tiles, tail splits)."""
+    line only): (token tile, uniform splits, tail tiles, tail splits, n
+    tile).  narrow: the forward on the NF4 weight, which may take the
+    256-token x 128-n tile (split schedule only)."""
     slots = 256
     nkt = Kred // 64
-    n_t = (Nout + 255) // 256
-    best, best_t = (256, 1, 0, 1), float("inf")
-    for tm in (256, 128):
-        tiles = ((M + tm - 1) // tm) * n_t
-        rate = 1.1e15 if tm == 256 else 0.8e15
-        t_tile = 2.0 * tm * 256 * Kred / (rate / slots)
+    best, best_t = (256, 1, 0, 1, 256), float("inf")
+    shapes = [(256, 256, 1.1e15), (128, 256, 0.8e15)] + ([(256, 128, 1.0e15)] if narrow else [])
+    for tm, tn, rate in shapes:
+        tiles = ((M + tm - 1) // tm) * ((Nout + tn - 1) // tn)
+        t_tile = 2.0 * tm * tn * Kred / (rate / slots)
+        if tn != 256 and tiles >= 192:
+            continue
         if tiles < 192:
             s = max(1, min(256 // tiles, nkt // 4, 16))
             blocks = tiles * s
@@ -116,28 +119,29 @@ def _gemm_schedule(M, Nout, Kred):
             est = 2.0 * M * Nout * Kred / (rate * fill)
             if s > 1:
                 est += 2.0 * s * M * Nout * 4 / 5.0e12
-            cfg = (tm, s, 0, 1)
+            cfg = (tm, s, 0, 1, tn)
         else:
             rounds, q = divmod(tiles, slots)
             ts = min(slots // q if q else 1, nkt // 4, 8)
             if q and ts >= 2:
-                est = (rounds + 1.0 / ts) * t_tile + 2.0 * ts * q * tm * 256 * 4 / 5.0e12
-                cfg = (tm, 1, q, ts)
+                est = (rounds + 1.0 / ts) * t_tile + 2.0 * ts * q * tm * tn * 4 / 5.0e12
+                cfg = (tm, 1, q, ts, tn)
             else:
                 est = (rounds + (1 if q else 0)) * t_tile
-                cfg = (tm, 1, 0, 1)
+                cfg = (tm, 1, 0, 1, tn)
         if est < best_t:
             best, best_t = cfg, est
     return best
 
 
 def _schedule_label(cfg):
-    tm, s, q, ts = cfg
+    tm, s, q, ts, tn = cfg
+    tile = f" [{tm} tokens x {tn} n tile]"
     if q:
-        return f" + tail_reduce_kernel ({q} tail tiles split {ts})"
+        return tile + f" + tail_reduce_kernel ({q} tail tiles split {ts})"
     if s > 1:
-        return f" + splitk_reduce_kernel (k split {s})"
-    return ""
+        return tile + f" + splitk_reduce_kernel (k split {s})"
+    return tile
 
 
 def _source_digest(key):
@@ -553,7 +557,7 @@ def main():
 
     # the unit the roofline line is about: one base-only fused-GEMM call (the
     # GEMM kernel, plus its split-K reduce kernel when the output is small)
-    fsched = _gemm_schedule(M, N, K)
+    fsched = _gemm_schedule(M, N, K, narrow=True)
     dsched = _gemm_schedule(M, K, N)
     if M <= 32:
         # decode: HBM-bound; algorithmic bytes of the base-only launch

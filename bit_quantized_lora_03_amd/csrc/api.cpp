@@ -97,10 +97,13 @@ struct FwdWs {
   size_t gpart;  // fp32 partials of the fused GEMM's schedule (0: none)
   bool decode;   // few tokens: split-K decode path
 };
-// nf4: the few-token decode path exists for the NF4 weight only
-FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool nf4 = true) {
+// decode: the few-token decode path may run (NF4 weight, bf16, no dropout);
+// nf4w: the weight is the NF4 one (the fused GEMM may then take its narrow
+// tile, which sizes the partials differently)
+FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool decode = true,
+                 bool nf4w = true) {
   FwdWs L{};
-  L.decode = nf4 && M <= qlora::kDecodeMaxM;
+  L.decode = decode && M <= qlora::kDecodeMaxM;
   if (M == 0) return L;
   if (L.decode) {
     // with an adapter: fp32 sums of x . W'^T and k-split partials of
@@ -117,7 +120,7 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool nf4 = true) {
     L.xst_off = round_up((size_t)M * 2 * r * sizeof(uint16_t), 256);
     off = round_up(L.xst_off + (size_t)pad32(M) * 2 * r * sizeof(uint16_t), 256);
   }
-  L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, N, K), M, N);
+  L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, N, K, nf4w), M, N);
   if (L.gpart > 0) {
     L.part_off = off;
     off = round_up(off + L.gpart, 256);
@@ -192,7 +195,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
         (keep && !aligned16(keep)))
       return QLORA_EALIGN;
     // the few-token decode kernel has no dropout: the tiled path then runs
-    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep && !f16);
+    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep && !f16, w->nf4());
     if (ws.total > 0) {
       if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
       if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
@@ -350,7 +353,8 @@ size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
     return 0;
   if (op == 0) return fwd_layout(M, N, K, r).total;
   if (op == 1 || op == 3) return bwd_layout(M, N, K, r).total;
-  if (op == 2 || op == 4 || op == 6) return fwd_layout(M, N, K, r, false).total;
+  if (op == 2) return fwd_layout(M, N, K, r, false, false).total;
+  if (op == 4 || op == 6) return fwd_layout(M, N, K, r, false, true).total;
   if (op == 5 || op == 7) return bwd_layout(M, N, K, r).total;
   return 0;
 }

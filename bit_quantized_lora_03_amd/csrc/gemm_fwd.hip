@@ -107,28 +107,40 @@ __device__ __forceinline__ void swap_halves(u32x4_t& a, u32x4_t& b, int v) {
 // 64 bf16 of the same row tile instead and skips the table and decode, so
 // the two share every other part of the kernel.
 // DT: the 16-bit compute type (Bf16T, or F16T for the fp16 variant).
-template <int JT, int WF, class DT>
+//
+// RW: weight rows per wave.  64 (the block tile is 256 n x TM): each lane
+// decodes a whole row and the lane halves swap chunks, as described above.
+// 32 (the block tile is 128 n x TM, NF4 only): lanes l and l + 32 share
+// row l % 32 and each decodes just the four chunks its own MFMA operand
+// takes (chunks 4 (l / 32) + kk), so a lane decodes half as many weights
+// per MFMA and nothing is swapped -- the tile for small M, where a 256 x
+// 128 tile would give each decoded weight only 4 token tiles.
+template <int JT, int WF, class DT, int RW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(FwdParams p) {
   constexpr bool NF4 = WF == kWeightNf4;
+  constexpr bool HALF = RW == 32;
+  static_assert(RW == 64 || (HALF && NF4), "half rows per lane need the NF4 weight");
+  constexpr int NI = RW / 32;   // 32-row MFMA tiles per wave
+  constexpr int TN = 4 * RW;    // n extent of the block tile
   // weight ring depth (tiles loaded ahead) and vector loads per weight tile:
   // a bf16 tile is 8 x 16 bytes per thread, so the 256-token tile (whose
   // accumulators leave the fewest registers) keeps two tiles, not four
   constexpr int WD = NF4 ? 4 : (JT == 8 ? 2 : 4);
-  constexpr int LC = NF4 ? 4 : 8;
+  constexpr int LC = NF4 ? (HALF ? 3 : 4) : 8;
   constexpr int TM = 32 * JT;             // token rows of the block tile
   constexpr int XR = TM / 32;             // x chunks staged per thread per tile
   constexpr int XST = TM * ROW_CHUNKS;    // u32x4 per ring stage
-  constexpr int EPI = 4 * epi_floats<2>() / 4;  // epilogue scratch, u32x4
+  constexpr int EPI = 4 * epi_floats<NI>() / 4;  // epilogue scratch, u32x4
   constexpr int LDS_U4 = NSTAGE * XST > EPI ? NSTAGE * XST : EPI;
   __shared__ u32x4_t lds[LDS_U4];
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int64_t m_tiles = (M + TM - 1) / TM, n_tiles = (N + TILE_N - 1) / TILE_N;
+  const int64_t m_tiles = (M + TM - 1) / TM, n_tiles = (N + TN - 1) / TN;
   const BlockWork bw = block_work(blockIdx.x, (int64_t)gridDim.x, m_tiles, n_tiles, p.splits,
                                   p.full, p.tail_q, p.tail_s);
-  const int64_t n0 = bw.n * TILE_N;
+  const int64_t n0 = bw.n * TN;
   const int64_t m0 = bw.m * TM;
   const int z = bw.z, nz = bw.nz;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
@@ -145,17 +157,18 @@ void fwd_gemm_kernel(FwdParams p) {
   const int64_t nkt = K / KT;
   const int64_t kt0 = nkt * z / nz, kt1 = nkt * (z + 1) / nz;
 
-  f32x16_t acc[2][JT];
+  f32x16_t acc[NI][JT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < JT; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // this thread decodes weight row n0 + t (clamped)
-  const int64_t wrow = clamp_row(n0 + t, N);
-  const uint8_t* wcodes = NF4 ? p.codes + ((wrow * K) >> 1) : nullptr;
+  // this thread decodes weight row n0 + t (clamped), or with half rows the
+  // half lg of row n0 + 32 wave + lr
+  const int64_t wrow = clamp_row(HALF ? n0 + 32 * wave + lr : n0 + t, N);
+  const uint8_t* wcodes = NF4 ? p.codes + ((wrow * K) >> 1) + (HALF ? 16 * lg : 0) : nullptr;
   const uint16_t* wvals = NF4 ? nullptr : p.wbf + wrow * K;
   const int64_t wblk0 = (wrow * K) >> 6;
 
@@ -190,12 +203,23 @@ void fwd_gemm_kernel(FwdParams p) {
     uint32_t q;
     float st;
   };
+  struct CodesHalf {
+    u32x4_t c;  // word i: the codes of chunk 4 lg + i of the tile
+    uint32_t q;
+    float st;
+  };
   struct WordsBf16 {
     u32x4_t w[8];  // chunk c: the 8 values at k = 8c .. 8c + 7 of the tile
   };
-  using Codes = std::conditional_t<NF4, CodesNf4, WordsBf16>;
+  using Codes =
+      std::conditional_t<NF4, std::conditional_t<HALF, CodesHalf, CodesNf4>, WordsBf16>;
   auto load_codes = [&](int64_t kt, Codes& c) {
-    if constexpr (NF4) {
+    if constexpr (HALF) {
+      c.c = *reinterpret_cast<const u32x4_t*>(wcodes + kt * (KT / 2));
+      const int64_t b = wblk0 + kt;
+      c.q = p.qscale[b];
+      c.st = p.step[b >> 8];
+    } else if constexpr (NF4) {
       const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(wcodes + kt * (KT / 2));
       c.c0 = cp[0];
       c.c1 = cp[1];
@@ -227,7 +251,7 @@ void fwd_gemm_kernel(FwdParams p) {
     const int64_t last = kt1 - 1;
     auto cl = [&](int64_t v) { return v < last ? v : last; };
     Codes C[WD];
-    u32x4_t Ap[2][2];    // A operands of a step: [step parity][i]
+    u32x4_t Ap[2][NI];   // A operands of a step: [step parity][i]
     u32x4_t op[2][JT];   // B operands, by step parity
 
     // Decode state.  The weights are decoded just in time: during step kk
@@ -282,27 +306,34 @@ void fwd_gemm_kernel(FwdParams p) {
     // pair unit w (0..11) of chunk pair pr: the decode of code words pr and
     // 4 + pr (5 units each, about 5 vector ops per unit), then the
     // lane-half exchange (2 units) that makes them step pr's A operands
-    auto pair_unit = [&](const Codes& c, int pr, int w, u32x4_t (&dst)[2]) {
-      if constexpr (!NF4) {
-        if (w == 0) {
-          dlo = c.w[pr];
-          dhi = c.w[4 + pr];
-        }
-      }
-      if (w < 5) {
-        if constexpr (NF4) decode_part(c.c0[pr], w, dlo);
-      } else if (w < 10) {
-        if constexpr (NF4) decode_part(c.c1[pr], w - 5, dhi);
+    auto pair_unit = [&](const Codes& c, int pr, int w, u32x4_t (&dst)[NI]) {
+      if constexpr (HALF) {
+        // word pr of the lane's own codes is its operand for step pr
+        if (w < 5) decode_part(c.c[pr], w, dlo);
+        if (w == 4) dst[0] = dlo;
       } else {
-        const int v = 2 * (w - 10);
-        swap_halves(dlo, dhi, v);
-        swap_halves(dlo, dhi, v + 1);
-        if (w == 11) {
-          dst[0] = dlo;
-          dst[1] = dhi;
+        if constexpr (!NF4) {
+          if (w == 0) {
+            dlo = c.w[pr];
+            dhi = c.w[4 + pr];
+          }
+        }
+        if (w < 5) {
+          if constexpr (NF4) decode_part(c.c0[pr], w, dlo);
+        } else if (w < 10) {
+          if constexpr (NF4) decode_part(c.c1[pr], w - 5, dhi);
+        } else {
+          const int v = 2 * (w - 10);
+          swap_halves(dlo, dhi, v);
+          swap_halves(dlo, dhi, v + 1);
+          if (w == 11) {
+            dst[0] = dlo;
+            dst[NI - 1] = dhi;
+          }
         }
       }
     };
+    constexpr int NUP = HALF ? 5 : 12;  // units of one pair (one word with half rows)
 
     // Prologue: codes of tiles kt0..kt0+3, x tiles kt0..kt0+2, the table
     // and first pair of tile kt0; then wait for x tiles kt0 and kt0+1.  The
@@ -327,7 +358,7 @@ void fwd_gemm_kernel(FwdParams p) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) table_unit(C[0], u);
 #pragma unroll
-    for (int w = 0; w < 12; ++w) pair_unit(C[0], 0, w, Ap[0]);
+    for (int w = 0; w < NUP; ++w) pair_unit(C[0], 0, w, Ap[0]);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm((WD - 1) * LC + XR, 0));
     __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -344,20 +375,21 @@ void fwd_gemm_kernel(FwdParams p) {
     auto iteration = [&](int64_t kt, auto phase, u32x4_t* __restrict__ rd0,
                          u32x4_t* __restrict__ rd1, u32x4_t* __restrict__ fill) {
       constexpr int ph = decltype(phase)::value;
-      constexpr int SPK = 2 * JT;  // MFMAs (slots) per k step
+      constexpr int SPK = NI * JT;  // MFMAs (slots) per k step
+      constexpr int DP = 4 * SPK / XR;  // slots between the x DMAs (XR per tile)
       auto rb = [&](u32x4_t* st, int kk, int j) -> u32x4_t {
         return st[rk(32 * j + lr, 4 * lg + kk)];
       };
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        // steps 0..2 decode pair kk+1 of this tile (12 units); step 3
-        // builds the next tile's table and decodes its pair 0 (20 units)
-        const int NU = kk < 3 ? 12 : 20;
+        // steps 0..2 decode pair kk+1 of this tile (NUP units); step 3
+        // builds the next tile's table and decodes its pair 0 (8 + NUP)
+        const int NU = kk < 3 ? NUP : 8 + NUP;
 #pragma unroll
         for (int s = 0; s < SPK; ++s) {
-          const int j = s >> 1, i = s & 1;
+          const int j = s / NI, i = s % NI;
           acc[i][j] = DT::mfma32(Ap[kk & 1][i], op[kk & 1][j], acc[i][j]);
-          if (i == 1) {
+          if (i == NI - 1) {
             // operand j of the next step: this tile's, or the next tile's
             // first (its stage was completed before the last barrier)
             if (kk < 3)
@@ -375,7 +407,7 @@ void fwd_gemm_kernel(FwdParams p) {
               pair_unit(C[(ph + 1) % WD], 0, u - 8, Ap[0]);
           }
           const int slot = SPK * kk + s;
-          if (slot % 8 == 7) dma_x(fill, cl(kt + 3), slot / 8);  // x chunk of tile kt+3
+          if (slot % DP == DP - 1) dma_x(fill, cl(kt + 3), slot / DP);  // x chunk of tile kt+3
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -383,7 +415,7 @@ void fwd_gemm_kernel(FwdParams p) {
       // after this iteration's DMA so that the wait below (for the x tile
       // DMA'd during the last iteration) does not also wait for them, nor
       // for the codes issued at the end of the last iteration: x tile kt+2
-      // is complete once at most those 4 + XR + 4 loads are outstanding
+      // is complete once at most those LC + XR + LC loads are outstanding
       load_codes(cl(kt + WD), C[ph % WD]);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(XR + 2 * LC, 0));
@@ -428,12 +460,12 @@ void fwd_gemm_kernel(FwdParams p) {
             col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.xs + m * 2 * r + col) : zero;
         store_x(0, q, v);
       }
-      u32x4_t a[2][4];
+      u32x4_t a[NI][4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const int64_t row = clamp_row(n0 + 64 * wave + 32 * i + lr, N);
+          const int64_t row = clamp_row(n0 + RW * wave + 32 * i + lr, N);
           const int col = e * KT + 8 * (4 * lg + kk);
           const int jj = col < r ? col : col - r;
           a[i][kk] = col < 2 * r ? *reinterpret_cast<const u32x4_t*>(p.B + row * r + jj) : zero;
@@ -445,21 +477,21 @@ void fwd_gemm_kernel(FwdParams p) {
         for (int j = 0; j < JT; ++j) {
           const u32x4_t b = read_b(0, kk, j);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) acc[i][j] = DT::mfma32(a[i][kk], b, acc[i][j]);
+          for (int i = 0; i < NI; ++i) acc[i][j] = DT::mfma32(a[i][kk], b, acc[i][j]);
         }
     }
   }
 
   // --- epilogue: D[n][m] -> y[m][n], or the split's fp32 partial ---
   __syncthreads();  // the LDS ring is free from here on
-  float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<2>();
-  if (bw.tail >= 0)  // tile-local [TM][256] partial
-    store_acc_tile<2, JT, DT>(acc, scratch, 64 * wave, 0, N - n0, M - m0, true,
-                          p.part + ((int64_t)z * p.tail_q + bw.tail) * TM * TILE_N, nullptr,
-                          TILE_N, lane);
+  float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<NI>();
+  if (bw.tail >= 0)  // tile-local [TM][TN] partial
+    store_acc_tile<NI, JT, DT>(acc, scratch, RW * wave, 0, N - n0, M - m0, true,
+                               p.part + ((int64_t)z * p.tail_q + bw.tail) * TM * TN, nullptr,
+                               TN, lane);
   else
-    store_acc_tile<2, JT, DT>(acc, scratch, n0 + 64 * wave, m0, N, M, nz > 1,
-                          nz > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
+    store_acc_tile<NI, JT, DT>(acc, scratch, n0 + RW * wave, m0, N, M, nz > 1,
+                               nz > 1 ? p.part + (int64_t)z * M * N : nullptr, p.y, N, lane);
 }
 
 // out[i] = DT(sum_z part[z][i]), i over M*N (4 per thread), fixed order.
@@ -542,19 +574,27 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restric
 // whole, except that a last round filled less than half is split: its
 // tail_q tiles are split 256 / tail_q ways (at most 8, at least 4 k tiles
 // each), so it takes a fraction of a round.  The rates are the measured
-// sustained throughputs of the two tiles.
-GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred) {
+// sustained throughputs of the tiles.  With `narrow` (the forward GEMM on
+// the NF4 weight) a third tile, 256 tokens x 128 n with half rows per lane,
+// is considered for the split schedule.
+GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred, bool narrow) {
   constexpr int kSlots = 256;  // concurrent blocks: one per CU
   const int64_t nkt = Kred / KT;
-  const int64_t n_t = (Nout + TILE_N - 1) / TILE_N;
-  GemmConfig best{256, 1, 0, 0, 1};
+  GemmConfig best{256, 1, 0, 0, 1, TILE_N};
   double best_t = 1e300;
-  for (int tm : {256, 128}) {
-    const int64_t tiles = ((M + tm - 1) / tm) * n_t;
-    const double rate = tm == 256 ? 1.1e15 : 0.8e15;  // flop/s, whole chip
-    const double t_tile = 2.0 * tm * TILE_N * (double)Kred / (rate / kSlots);
-    GemmConfig c{tm, 1, 0, 0, 1};
+  struct Shape {
+    int tm, tn;
+    double rate;  // flop/s, whole chip
+  };
+  const Shape shapes[3] = {{256, TILE_N, 1.1e15}, {128, TILE_N, 0.8e15}, {256, 128, 1.0e15}};
+  for (int si = 0; si < (narrow ? 3 : 2); ++si) {
+    const int tm = shapes[si].tm, tn = shapes[si].tn;
+    const double rate = shapes[si].rate;
+    const int64_t tiles = ((M + tm - 1) / tm) * ((Nout + tn - 1) / tn);
+    const double t_tile = 2.0 * tm * tn * (double)Kred / (rate / kSlots);
+    GemmConfig c{tm, 1, 0, 0, 1, tn};
     double est;
+    if (tn != TILE_N && tiles >= 192) continue;  // the narrow tile: split schedule only
     if (tiles < 192) {
       int64_t sp = 256 / tiles;
       if (sp > nkt / 4) sp = nkt / 4;
@@ -574,7 +614,7 @@ GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred) {
         c.full = tiles - q;
         c.tail_q = (int)q;
         c.tail_s = (int)ts;
-        est = (rounds + 1.0 / ts) * t_tile + 2.0 * ts * q * tm * TILE_N * 4 / 5.0e12;
+        est = (rounds + 1.0 / ts) * t_tile + 2.0 * ts * q * tm * tn * 4 / 5.0e12;
       } else {
         est = (rounds + (q > 0 ? 1 : 0)) * t_tile;
       }
@@ -589,7 +629,7 @@ GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred) {
 
 int64_t gemm_blocks(const GemmConfig& c, int64_t M, int64_t Nout) {
   if (c.tail_q > 0) return c.full + (int64_t)c.tail_q * c.tail_s;
-  return ((Nout + TILE_N - 1) / TILE_N) * ((M + c.tm - 1) / c.tm) * c.splits;
+  return ((Nout + c.tn - 1) / c.tn) * ((M + c.tm - 1) / c.tm) * c.splits;
 }
 
 size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout) {
@@ -620,7 +660,8 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
                            const uint16_t* wbf, const uint16_t* x, const uint16_t* xs,
                            const uint16_t* B, uint16_t* y, float* part, int64_t M, int64_t N,
                            int64_t K, int r, const Nf4Levels& L, hipStream_t s, bool f16) {
-  const GemmConfig cfg = gemm_config(M, N, K);
+  const bool nf4 = wbf == nullptr;
+  const GemmConfig cfg = gemm_config(M, N, K, nf4);
   if (gemm_partial_bytes(cfg, M, N) > 0 && part == nullptr) return hipErrorInvalidValue;
   FwdParams p;
   p.codes = codes;
@@ -642,23 +683,28 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.tail_s = cfg.tail_s;
   p.L = L;
   const int64_t blocks = gemm_blocks(cfg, M, N);
-  const bool nf4 = wbf == nullptr;
   const dim3 grid((unsigned)blocks);
-  // token tile; weight format; compute type (fp16 with the NF4 weight only)
-  if (cfg.tm == 256) {
+  // block tile (tokens x n); weight format; compute type (fp16 and the
+  // narrow tile with the NF4 weight only)
+  if (cfg.tn != TILE_N) {
     if (f16)
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, F16T>), grid, dim3(256), 0, s, p);
-    else if (nf4)
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, F16T, 32>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightBf16, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, Bf16T, 32>), grid, dim3(256), 0, s, p);
+  } else if (cfg.tm == 256) {
+    if (f16)
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, F16T, 64>), grid, dim3(256), 0, s, p);
+    else if (nf4)
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, Bf16T, 64>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightBf16, Bf16T, 64>), grid, dim3(256), 0, s, p);
   } else {
     if (f16)
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, F16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, F16T, 64>), grid, dim3(256), 0, s, p);
     else if (nf4)
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, Bf16T, 64>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightBf16, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightBf16, Bf16T, 64>), grid, dim3(256), 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -61,7 +61,7 @@ hipError_t launch_lora_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_
                             int accumulate, hipStream_t s, bool f16 = false);
 
 // gemm_fwd.hip -- y = x . deq(W)^T + xs . [B | B]^T.
-// Schedule of a fused GEMM with an Mout x Nout output (Nout in tiles of 256)
+// Schedule of a fused GEMM with an Mout x Nout output (Nout in tiles of tn)
 // and a reduction of Kred (in tiles of 64): either every tile's reduction is
 // split `splits` ways (fp32 partials part[splits][M][Nout], reduced by
 // splitk_reduce), or -- when the tiles fill at least one round of the chip
@@ -74,8 +74,11 @@ struct GemmConfig {
   int64_t full;  // tail schedule: tiles run whole
   int tail_q;    // tail schedule: split tiles (0: uniform schedule)
   int tail_s;    // tail schedule: splits per tail tile
+  int tn;        // Nout extent of the block tile: 256, or 128 (the forward's
+                 // narrow tile, uniform schedule only)
 };
-GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred);
+// narrow: the 128-wide tile may be chosen (the forward on the NF4 weight)
+GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred, bool narrow = false);
 int64_t gemm_blocks(const GemmConfig& c, int64_t M, int64_t Nout);
 size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout);
 // The weight is the NF4 one (codes, qscale, step) when wbf is null, else the

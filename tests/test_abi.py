@@ -79,17 +79,22 @@ def test_workspace_sizes():
     assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
     assert ws(0, 16, 4096, 4096, 264) == 0        # r > 256
     assert ws(8, 16, 4096, 4096, 16) == 0         # bad op
-    # fp16 compute type: the tiled path at every M, same layouts
-    assert ws(6, 16, 8192, 8192, 64) == ws(2, 16, 8192, 8192, 64)
+    # fp16 compute type and dropout: the tiled forward at every M (never the
+    # few-token path), both on the NF4 weight, so laid out alike
+    assert ws(6, 16, 8192, 8192, 64) == ws(4, 16, 8192, 8192, 64)
+    assert ws(6, 512, 4096, 4096, 16) == ws(0, 512, 4096, 4096, 16)
     assert ws(7, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
-    # dropout: the forward never takes the few-token path
-    assert ws(4, 16, 8192, 8192, 64) == ws(2, 16, 8192, 8192, 64)
     assert ws(5, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
     # bf16-weight layer: no few-token path, so the tiled GEMMs' workspace
     # at every M; its backward is laid out as the NF4 backward
     assert ws(2, 512, 4096, 4096, 16) == ws(0, 512, 4096, 4096, 16)
     assert ws(2, 16, 8192, 8192, 0) > 0           # split-K partials, no decode kernel
     assert ws(3, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
+    # ... and no narrow (128-wide) tile: at 16 tokens the NF4 forward's 64
+    # narrow tiles split 4 ways, the bf16 weight's 32 wide tiles 8 ways
+    part = lambda s: s * 16 * 8192 * 4
+    assert ws(4, 16, 8192, 8192, 64) >= part(4) and ws(4, 16, 8192, 8192, 64) < part(8)
+    assert ws(2, 16, 8192, 8192, 64) >= part(8)
 
 
 def _weight(N=128, K=128, codes=P0, qs=P1, st=P2):
