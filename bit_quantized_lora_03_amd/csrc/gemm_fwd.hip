@@ -15,23 +15,24 @@
 //
 // Block tile 256 (n) x TM (m) x 64 (k), TM = 256 or 128; 4 waves, wave w
 // owning weight rows 64 w .. 64 w + 63 against all TM tokens (2 x TM/32
-// MFMA 32x32x16 tiles, fp32 accumulate, one wave per SIMD).  Thread t
-// decodes row 64 w + t of its wave into eight 8-value chunks.  MFMA step kk
-// of a k tile takes, in lanes 0..31, k chunk kk and, in lanes 32..63, chunk
-// 4 + kk (the reduction order inside a tile is free, as long as both
-// operands use the same one), so lane l needs chunk kk of row l % 32 and
-// lane l + 32 chunk 4 + kk of it: one v_permlane32_swap per register pair
-// exchanges the halves decoded by the other 32 lanes.
+// MFMA 32x32x16 tiles, fp32 accumulate, one wave per SIMD); small-M split
+// schedules may use a narrow 128 (n) x 256 (m) tile instead (RW below).
+// Thread t decodes row 64 w + t of its wave into eight 8-value chunks.
+// MFMA step kk of a k tile takes, in lanes 0..31, k chunk kk and, in
+// lanes 32..63, chunk 4 + kk (the reduction order inside a tile is free, as
+// long as both operands use the same one), so lane l needs chunk kk of row
+// l % 32 and lane l + 32 chunk 4 + kk of it: one v_permlane32_swap per
+// register pair exchanges the halves decoded by the other 32 lanes.
 //
-// Pipeline: the activation tile goes through a 3-stage LDS ring, each chunk
-// loaded into a register one k tile before it is written, so one barrier
-// per k tile covers both hazards and the B operands of the next tile's
-// first step can be read before that barrier.  While the MFMAs of tile t
-// run, the same waves decode tile t+1's codes (loaded one tile earlier) in
-// small, fixed pieces placed between the MFMAs, so the matrix cores and the
-// vector ALUs work at the same time.  Out-of-range rows are clamped to the
-// last valid row instead of branched around, so the loop body is a single
-// basic block; their results are never stored.
+// Pipeline: the activation tile goes through a 4-stage LDS ring, filled by
+// DMA three k tiles ahead, so one barrier per k tile covers both hazards
+// and the B operands of the next tile's first step can be read before that
+// barrier.  While the MFMAs of tile t run, the same waves decode tile t+1's
+// codes (loaded four tiles ahead) in small, fixed pieces placed between the
+// MFMAs, so the matrix cores and the vector ALUs work at the same time.
+// Out-of-range rows are clamped to the last valid row instead of branched
+// around, so the loop body is a single basic block; their results are
+// never stored.
 //
 // When the output has too few tiles to fill the chip, the k range is split
 // over blocks that write fp32 partials; splitk_reduce adds them in a fixed
@@ -113,8 +114,8 @@ __device__ __forceinline__ void swap_halves(u32x4_t& a, u32x4_t& b, int v) {
 // 32 (the block tile is 128 n x TM, NF4 only): lanes l and l + 32 share
 // row l % 32 and each decodes just the four chunks its own MFMA operand
 // takes (chunks 4 (l / 32) + kk), so a lane decodes half as many weights
-// per MFMA and nothing is swapped -- the tile for small M, where a 256 x
-// 128 tile would give each decoded weight only 4 token tiles.
+// per MFMA and nothing is swapped -- the tile for small M, where the
+// 256 n x 128 token tile would give each decoded weight only 4 token tiles.
 template <int JT, int WF, class DT, int RW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(FwdParams p) {
