@@ -395,15 +395,20 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
           acc[i][q] = DT::dot2(xv[pp], yp[q][pp], acc[i][q]);
     }
   };
+  // Loads are unconditional (a piece past the count reads zeros, which add
+  // nothing): a branch around them would leave the compiler, at the join,
+  // waiting for the newer piece as well before computing the older one.
+  // The fences keep each piece's loads ahead of the compute before them
+  // (the scheduler otherwise sinks them below it).
   Piece P0, P1;
-  if (cnt > 0) load(0, P0);
+  load(0, P0);
   for (int64_t u = 0; u < cnt; u += 2) {
-    if (u + 1 < cnt) load(u + 1, P1);
+    load(u + 1, P1);
+    __builtin_amdgcn_sched_barrier(0);
     compute(P0);
-    if (u + 1 < cnt) {
-      if (u + 2 < cnt) load(u + 2, P0);
-      compute(P1);
-    }
+    load(u + 2, P0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(P1);
   }
 
 #pragma unroll
@@ -411,10 +416,14 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
 #pragma unroll
     for (int q = 0; q < kSmallR; ++q) red[t * kSmallRed + i * kSmallR + q] = acc[i][q];
   __syncthreads();
-  // output o = t / 4: its 256 sums, lane t % 4 taking every fourth
+  // output o = t / 4: its 256 sums, lane t % 4 taking every fourth.  The
+  // trip count is a constant so the loop unrolls and its LDS reads are
+  // issued together (a lane-dependent bound left one read and one wait per
+  // step).
   const int o = t >> 2, part = t & 3;
   float sum = red[part * kSmallRed + o];
-  for (int tt = part + 4; tt < 256; tt += 4) sum += red[tt * kSmallRed + o];
+#pragma unroll
+  for (int i = 1; i < 64; ++i) sum += red[(part + 4 * i) * kSmallRed + o];
   sum += __shfl_xor(sum, 1, 4);
   sum += __shfl_xor(sum, 2, 4);
   const int64_t Mp = pad32(M);
