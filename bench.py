@@ -101,8 +101,8 @@ def _gemm_schedule(M, Nout, Kred, narrow=False):
     """Mirror of the library's schedule for a fused GEMM with an M x Nout
     output and a reduction of Kred (for naming the launches in the roofline
     line only): (token tile, uniform splits, tail tiles, tail splits, n
-    tile).  narrow: the forward on the NF4 weight, which may take the
-    256-token x 128-n tile (split schedule only)."""
+    tile).  narrow: a GEMM on the NF4 weight, which may take the 256-token
+    x 128 tile (split schedule only)."""
     slots = 256
     nkt = Kred // 64
     best, best_t = (256, 1, 0, 1, 256), float("inf")
@@ -558,7 +558,7 @@ def main():
     # the unit the roofline line is about: one base-only fused-GEMM call (the
     # GEMM kernel, plus its split-K reduce kernel when the output is small)
     fsched = _gemm_schedule(M, N, K, narrow=True)
-    dsched = _gemm_schedule(M, K, N)
+    dsched = _gemm_schedule(M, K, N, narrow=True)
     if M <= 32:
         # decode: HBM-bound; algorithmic bytes of the base-only launch
         kb = packed_weight_bytes(N, K) + 2 * M * K + 2 * M * N

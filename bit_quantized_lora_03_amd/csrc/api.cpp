@@ -133,7 +133,9 @@ struct BwdWs {
   size_t xs_off, gs_off, xst_off, gst_off, part_off, total;
   size_t gpart;  // fp32 partials of the dX GEMM's schedule (0: none)
 };
-BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+// nf4w: the weight is the NF4 one (the dX GEMM may then take its narrow
+// tile, which sizes the partials differently)
+BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool nf4w = true) {
   BwdWs L{};
   if (M == 0) return L;
   size_t off = 0;
@@ -148,7 +150,7 @@ BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
     L.gst_off = round_up(L.xst_off + pairT, 256);
     off = round_up(L.gst_off + pairT, 256);
   }
-  L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, K, N), M, K);
+  L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, K, N, nf4w), M, K);
   if (L.gpart > 0) {
     L.part_off = off;
     off = round_up(off + L.gpart, 256);
@@ -264,7 +266,7 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
                    !aligned16(dB))) ||
         (keep && !aligned16(keep)))
       return QLORA_EALIGN;
-    const BwdWs ws = bwd_layout(M, N, K, r);
+    const BwdWs ws = bwd_layout(M, N, K, r, w->nf4());
     if (ws.total > 0) {
       if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
       if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
@@ -352,7 +354,8 @@ size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
       check_sizes(M, N, K) != QLORA_OK)
     return 0;
   if (op == 0) return fwd_layout(M, N, K, r).total;
-  if (op == 1 || op == 3) return bwd_layout(M, N, K, r).total;
+  if (op == 1) return bwd_layout(M, N, K, r).total;
+  if (op == 3) return bwd_layout(M, N, K, r, false).total;
   if (op == 2) return fwd_layout(M, N, K, r, false, false).total;
   if (op == 4 || op == 6) return fwd_layout(M, N, K, r, false, true).total;
   if (op == 5 || op == 7) return bwd_layout(M, N, K, r).total;

@@ -21,7 +21,8 @@
 // split of s . dy . B, gs . [A ; A] is run as 2r extra reduction rows.
 //
 // Block tile 256 (k) x 256 (m), 64 reduction rows per stage; 4 waves in a
-// 2 x 2 grid of 128 x 128; two LDS stages of (W slab, dy tile).  As in the
+// 2 x 2 grid of 128 x 128; two LDS stages of (W slab, dy tile).  (Small-M
+// shapes use 256 x 128, or the narrow 128 x 256 tile described at KW.)  As in the
 // forward pass, the next slab is decoded while the current one multiplies,
 // codes are fetched two slabs ahead, out-of-range rows are clamped rather
 // than branched around, and small outputs split the reduction over blocks
@@ -44,7 +45,6 @@ constexpr int ROW_CHUNKS = RT / 8;
 // cycle start 12 banks apart (all 64 banks once), and the 4 rows one
 // transpose read touches (8 banks each) are disjoint.
 constexpr int WROW = 560;
-constexpr int WSTAGE = RT * WROW;  // bytes per W stage
 
 struct DxParams {
   const uint8_t* codes;   // NF4 weight (WF = kWeightNf4)
@@ -92,15 +92,28 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 // reduction adds onto them: the sum is still rounded once.
 //
 // DT: the 16-bit compute type (Bf16T, or F16T for the fp16 variant).
-template <int MS, int WF, bool DROP, class DT>
+//
+// KW: k extent of the block tile.  256 as above; 128 (NF4 only, with MS = 4:
+// a 128 (k) x 256 (m) tile for small-M split schedules) gives each thread
+// half an NF4 block -- the 32 values of its slab row at k quarter
+// kq -- so a thread decodes half as many weights per MFMA; each wave then
+// owns 64 (k) x 128 (m).  The slab rows shrink to 256 bytes + 48 of pad,
+// 76 dwords = 12 mod 64 banks, the same bank pattern as the wide slab.
+template <int MS, int WF, bool DROP, class DT, int KW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
   constexpr bool NF4 = WF == kWeightNf4;
+  constexpr bool HALF = KW == 128;
+  static_assert(KW == TILE || (HALF && NF4), "half blocks per thread need the NF4 weight");
+  constexpr int NI = KW / 64;         // 32-column (k) MFMA tiles per wave
+  constexpr int NCH = KW / 32;        // 8-value chunks each thread decodes
+  constexpr int WR = HALF ? 304 : WROW;  // W slab row stride, bytes
+  constexpr int WST = RT * WR;           // bytes per W stage
   constexpr int TM = 64 * MS;   // token rows of the block tile
   constexpr int XR = TM / 32;   // dy rows staged per thread
   // one LDS array: two W^T stages, then two dy stages (the epilogue reuses
   // it from the start)
-  constexpr int WT_U4 = 2 * WSTAGE / 16;
+  constexpr int WT_U4 = 2 * WST / 16;
   __shared__ u32x4_t lds[WT_U4 + 2 * TM * ROW_CHUNKS];
   char* const wbase = reinterpret_cast<char*>(&lds[0]);
   u32x4_t(*dyt)[TM * ROW_CHUNKS] = reinterpret_cast<u32x4_t(*)[TM * ROW_CHUNKS]>(&lds[WT_U4]);
@@ -108,16 +121,16 @@ void dx_gemm_kernel(DxParams p) {
   const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int wk = wave & 1, wm = wave >> 1;
   const int64_t M = p.M, N = p.N, K = p.K;
-  const int64_t m_tiles = (M + TM - 1) / TM, k_tiles = (K + TILE - 1) / TILE;
+  const int64_t m_tiles = (M + TM - 1) / TM, k_tiles = (K + KW - 1) / KW;
   const BlockWork bw = block_work(blockIdx.x, (int64_t)gridDim.x, m_tiles, k_tiles, p.splits,
                                   p.full, p.tail_q, p.tail_s);
-  const int64_t k0 = bw.n * TILE;
+  const int64_t k0 = bw.n * KW;
   const int64_t m0 = bw.m * TM;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
-  f32x16_t acc[4][MS];
+  f32x16_t acc[NI][MS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < MS; ++j)
 #pragma unroll
@@ -129,12 +142,13 @@ void dx_gemm_kernel(DxParams p) {
 
   // this thread decodes reduction row 16 wave + lane % 16 of the slab, k
   // quarter lane / 16 (so the 16 lanes of one LDS store cycle write 16
-  // rows); a quarter past K is clamped to the last block (never stored)
+  // rows); a quarter past K is clamped to the last in-range quarter (never
+  // stored)
   const int wr = 16 * wave + (lane & 15);
   const int kq = lane >> 4;
-  const int64_t kcol_raw = k0 + 64 * kq;
+  const int64_t kcol_raw = k0 + (KW / 4) * kq;
   const bool kcol_ok = kcol_raw < K;
-  const int64_t kcol = kcol_ok ? kcol_raw : K - 64;
+  const int64_t kcol = kcol_ok ? kcol_raw : K - KW / 4;
   // dy rows m0 + (t >> 3) + 32 j through a buffer descriptor: rows past M
   // read as zero
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.dy, (uint32_t)(M * N * 2));
@@ -149,13 +163,33 @@ void dx_gemm_kernel(DxParams p) {
     uint32_t q;
     float st;
   };
+  struct CodesHalf {
+    u32x4_t c0;  // the codes of the thread's 32 values
+    uint32_t q;
+    float st;
+  };
   struct WordsBf16 {
     u32x4_t w[8];  // chunk c: the 8 values at k = kcol + 8c .. + 7
   };
-  using Codes = std::conditional_t<NF4, CodesNf4, WordsBf16>;
+  using Codes =
+      std::conditional_t<NF4, std::conditional_t<HALF, CodesHalf, CodesNf4>, WordsBf16>;
+  // code word of chunk ch (8 values) of the thread's codes
+  auto word = [](const Codes& c, int ch) -> uint32_t {
+    if constexpr (HALF)
+      return c.c0[ch & 3];
+    else if constexpr (NF4)
+      return (ch < 4 ? c.c0 : c.c1)[ch & 3];
+    else
+      return 0u;
+  };
   auto load_codes = [&](int64_t st, Codes& c) {
-    const int64_t idx = (st * RT + wr) * K + kcol;  // first element of the block
-    if constexpr (NF4) {
+    // first element of the thread's values (a whole block, or half of one)
+    const int64_t idx = (st * RT + wr) * K + kcol;
+    if constexpr (HALF) {
+      c.c0 = *reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
+      c.q = p.qscale[idx >> 6];
+      c.st = p.step[idx >> 14];
+    } else if constexpr (NF4) {
       const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
       c.c0 = cp[0];
       c.c1 = cp[1];
@@ -176,37 +210,38 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
     for (int j = 0; j < XR; ++j) dyt[stage][rk((t >> 3) + 32 * j, t & 7)] = yr[j];
   };
-  // store 8 consecutive-k bf16 values (chunk c of this thread's 64) of
+  // store 8 consecutive-k 16-bit values (chunk c of this thread's NCH) of
   // reduction row `wr` into the W slab
   auto store8 = [&](int stage, int c, const u32x4_t v) {
-    *reinterpret_cast<u32x4_t*>(wbase + stage * WSTAGE + wr * WROW + (64 * kq + 8 * c) * 2) = v;
+    *reinterpret_cast<u32x4_t*>(wbase + stage * WST + wr * WR + ((KW / 4) * kq + 8 * c) * 2) = v;
   };
   // A operand of MFMA step kk, k sub-tile i: lane l holds column
-  // 128 wk + 32 i + l % 32 at reduction rows 16 kk + 8 (l / 32) + 0..7, from
+  // (KW / 2) wk + 32 i + l % 32 at reduction rows 16 kk + 8 (l / 32) + 0..7, from
   // two transpose reads (rows +0..3 and +4..7).  As provider, lane j of
   // 16-lane group g points at row 8 (g / 2) + j / 4 (+ 4 for the second
   // read), column 16 (g % 2) + 4 (j % 4).
   const int tg = lane >> 4, tj = lane & 15;
-  const int a_off = (8 * (tg >> 1) + (tj >> 2)) * WROW + (128 * wk + 16 * (tg & 1) + 4 * (tj & 3)) * 2;
+  const int a_off =
+      (8 * (tg >> 1) + (tj >> 2)) * WR + ((KW / 2) * wk + 16 * (tg & 1) + 4 * (tj & 3)) * 2;
   auto read_a = [&](int stage, int kk, int i) -> u32x4_t {
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s lds_v4s;
-    const int o = stage * WSTAGE + a_off + 16 * kk * WROW + 64 * i;
+    const int o = stage * WST + a_off + 16 * kk * WR + 64 * i;
     const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o));
-    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o + 4 * WROW));
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o + 4 * WR));
     const u32x2_t h0 = __builtin_bit_cast(u32x2_t, r0), h1 = __builtin_bit_cast(u32x2_t, r1);
     const u32x4_t v = {h0[0], h0[1], h1[0], h1[1]};
     return v;
   };
   auto mfma_step = [&](int stage, int kk) {
     const int ch = 2 * kk + lg;
-    u32x4_t a[4], b[MS];
+    u32x4_t a[NI], b[MS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = read_a(stage, kk, i);
+    for (int i = 0; i < NI; ++i) a[i] = read_a(stage, kk, i);
 #pragma unroll
     for (int j = 0; j < MS; ++j) b[j] = dyt[stage][rk(32 * MS * wm + 32 * j + lr, ch)];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < MS; ++j) acc[i][j] = DT::mfma32(a[i], b[j], acc[i][j]);
   };
@@ -222,7 +257,7 @@ void dx_gemm_kernel(DxParams p) {
       const bool row_ok = c < 2 * r;
       const int arow = c < r ? c : c - r;
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int q = 0; q < NCH; ++q)
         store8(0, q, row_ok ? *reinterpret_cast<const u32x4_t*>(p.A + (int64_t)arow * K + kcol + 8 * q)
                               : zero);
       // dy side: rows m, columns c of gs
@@ -242,17 +277,17 @@ void dx_gemm_kernel(DxParams p) {
 
   // Dropout mask on the accumulators: lane (lr, lg) of acc[i][j] holds
   // token m0 + 32 MS wm + 32 j + lr and, in register v, column
-  // k0 + 128 wk + 32 i + 8 (v / 4) + 4 lg + v % 4 -- 16 bits of the
-  // 32-bit keep word of that token row at column k0 + 128 wk + 32 i.
+  // k0 + (KW / 2) wk + 32 i + 8 (v / 4) + 4 lg + v % 4 -- 16 bits of the
+  // 32-bit keep word of that token row at column k0 + (KW / 2) wk + 32 i.
   // Rows past M read zero (not stored); columns past K are not stored.
   auto mask_acc = [&]() {
     const __amdgpu_buffer_rsrc_t kres = make_rsrc(p.keep, (uint32_t)(M * K / 8));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < MS; ++j) {
         const int64_t m = m0 + 32 * MS * wm + 32 * j + lr;
-        const int64_t kw = k0 + 128 * wk + 32 * i;
+        const int64_t kw = k0 + (KW / 2) * wk + 32 * i;
         // the lane half's bits first, so every bit index below is a constant
         const uint32_t word = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
                                   kres, (int)(uint32_t)(m * (K / 8) + kw / 8), 0, 0) >>
@@ -286,37 +321,39 @@ void dx_gemm_kernel(DxParams p) {
     if constexpr (NF4) {
       const Nf4Lut lut = nf4_make_lut<DT>(p.L, nf4_block_scale(C[0].q, C[0].st));
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        store8(0, c, nf4_decode8(lut, (c < 4 ? C[0].c0 : C[0].c1)[c & 3]));
+      for (int c = 0; c < NCH; ++c) store8(0, c, nf4_decode8(lut, word(C[0], c)));
     } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) store8(0, c, C[0].w[c]);
+      for (int c = 0; c < NCH; ++c) store8(0, c, C[0].w[c]);
     }
     load_dy(cl(st0 + 1), Y[1]);
     load_codes(cl(st0 + 1), C[1]);
     __syncthreads();
 
-    // Hand-scheduled iteration, as in the forward pass: each of the 64
-    // MFMAs of the slab is followed by one unit of other work and a
-    // scheduling fence -- the table of slab st+1's block (units 0..7), the
-    // decode of its 8 code words (6 units each, about 5 vector ops per
-    // unit; the last one stores the 8 values into the W slab), the LDS writes of
-    // its dy rows (units 56..63) -- and the operand reads of step kk+1 ride
-    // in slots 8..15 of step kk, so the vector work fits in the MFMAs' shadow.
+    // Hand-scheduled iteration, as in the forward pass: each of the MFMAs
+    // of the slab is followed by a fixed share of the 64 units of other
+    // work and a scheduling fence -- the table of slab st+1's block (units
+    // 0..7), the decode of its NCH code words (6 units each, about 5 vector
+    // ops per unit; the last one stores the 8 values into the W slab), the
+    // LDS writes of its dy rows (the XR units after those) -- and the
+    // operand reads of step kk+1 ride in the last slots of step kk, so the
+    // vector work fits in the MFMAs' shadow.
     auto iteration = [&](int64_t st, auto parity) {
       constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
       load_dy(cl(st + 2), Y[cur]);
       load_codes(cl(st + 2), C[cur]);
       const Codes& cn = C[nxt];
-      constexpr int SPK = 4 * MS;  // MFMAs (slots) per k step
-      constexpr int NRD = 4 + MS;  // operand reads per k step
-      u32x4_t op[2][2][4];         // [buffer][a|b][i]
+      constexpr int SPK = NI * MS;  // MFMAs (slots) per k step
+      constexpr int NRD = NI + MS;  // operand reads per k step
+      constexpr int DEC = 8 + 6 * NCH;  // units before the dy rows
+      static_assert(SPK >= NRD && DEC + XR <= 64, "unit schedule");
+      u32x4_t op[2][2][4];          // [buffer][a|b][i]
       auto read_op = [&](int kk, int buf, int q) {
         const int ch = 2 * kk + lg;
-        if (q < 4)
+        if (q < NI)
           op[buf][0][q] = read_a(cur, kk, q);
         else
-          op[buf][1][q - 4] = dyt[cur][rk(32 * MS * wm + 32 * (q - 4) + lr, ch)];
+          op[buf][1][q - NI] = dyt[cur][rk(32 * MS * wm + 32 * (q - NI) + lr, ch)];
       };
 #pragma unroll
       for (int q = 0; q < NRD; ++q) read_op(0, 0, q);
@@ -342,10 +379,10 @@ void dx_gemm_kernel(DxParams p) {
       auto unit = [&](int u) {
         if constexpr (!NF4) {
           // no table or decode: a chunk's store sits where its decode ends
-          if (u >= 8 && u < 56) {
+          if (u >= 8 && u < DEC) {
             if ((u - 8) % 6 == 5) store8(nxt, (u - 8) / 6, cn.w[(u - 8) / 6]);
-          } else if (u >= 56 && u < 56 + XR) {
-            dyt[nxt][rk((t >> 3) + 32 * (u - 56), t & 7)] = Y[nxt][u - 56];
+          } else if (u >= DEC && u < DEC + XR) {
+            dyt[nxt][rk((t >> 3) + 32 * (u - DEC), t & 7)] = Y[nxt][u - DEC];
           }
         } else if (u < 4) {
           if (u == 0) sc = nf4_block_scale(cn.q, cn.st);
@@ -355,9 +392,9 @@ void dx_gemm_kernel(DxParams p) {
           const int j = u - 4;
           lut.lo[j] = perm(pk[2 * j + 1], pk[2 * j], 0x06040200u);
           lut.hi[j] = perm(pk[2 * j + 1], pk[2 * j], 0x07050301u);
-        } else if (u < 56) {
+        } else if (u < DEC) {
           const int c = (u - 8) / 6, w = (u - 8) % 6;
-          const uint32_t v = (c < 4 ? cn.c0 : cn.c1)[c & 3];
+          const uint32_t v = word(cn, c);
           switch (w) {
             case 0: {
               const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
@@ -371,9 +408,9 @@ void dx_gemm_kernel(DxParams p) {
             case 4: { uint32_t o2, o3; lookup_b(dn1, o2, o3); dv[2] = o2; dv[3] = o3; break; }
             default: store8(nxt, c, dv); break;
           }
-        } else if (u < 56 + XR) {
+        } else if (u < DEC + XR) {
           // slab st+1's dy rows into the other stage
-          dyt[nxt][rk((t >> 3) + 32 * (u - 56), t & 7)] = Y[nxt][u - 56];
+          dyt[nxt][rk((t >> 3) + 32 * (u - DEC), t & 7)] = Y[nxt][u - DEC];
         }
       };
 #pragma unroll
@@ -403,14 +440,15 @@ void dx_gemm_kernel(DxParams p) {
 
   // --- epilogue: D[k][m] -> dx[m][k] (or the split's fp32 partial) ---
   __syncthreads();  // the LDS stages are free from here on
-  float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<4>();
-  if (bw.tail >= 0)  // tile-local [TM][256] partial
-    store_acc_tile<4, MS, DT>(acc, scratch, 128 * wk, 32 * MS * wm, K - k0, M - m0, true,
-                          p.part + ((int64_t)z * p.tail_q + bw.tail) * TM * TILE, nullptr,
-                          TILE, lane);
+  float* scratch = reinterpret_cast<float*>(&lds[0]) + wave * epi_floats<NI>();
+  if (bw.tail >= 0)  // tile-local [TM][KW] partial
+    store_acc_tile<NI, MS, DT>(acc, scratch, (KW / 2) * wk, 32 * MS * wm, K - k0, M - m0, true,
+                               p.part + ((int64_t)z * p.tail_q + bw.tail) * TM * KW, nullptr,
+                               KW, lane);
   else
-    store_acc_tile<4, MS, DT>(acc, scratch, k0 + 128 * wk, m0 + 32 * MS * wm, K, M, nz > 1,
-                          nz > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K, lane);
+    store_acc_tile<NI, MS, DT>(acc, scratch, k0 + (KW / 2) * wk, m0 + 32 * MS * wm, K, M,
+                               nz > 1, nz > 1 ? p.part + (int64_t)z * M * K : nullptr, p.dx, K,
+                               lane);
 }
 
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
@@ -420,7 +458,8 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
                           hipStream_t s, bool f16) {
   // output M x K, reduction N: the forward GEMM's schedule with the roles
   // of N and K exchanged
-  const GemmConfig cfg = gemm_config(M, K, N);
+  const bool nf4 = wbf == nullptr, drop = keep != nullptr && r > 0;
+  const GemmConfig cfg = gemm_config(M, K, N, nf4);
   if (gemm_partial_bytes(cfg, M, K) > 0 && part == nullptr) return hipErrorInvalidValue;
   DxParams p;
   p.codes = codes;
@@ -443,34 +482,52 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.tail_s = cfg.tail_s;
   p.L = L;
   const int64_t blocks = gemm_blocks(cfg, M, K);
-  const bool nf4 = wbf == nullptr, drop = keep != nullptr && r > 0;
   const dim3 grid((unsigned)blocks);
-  // token tile; weight format; dropout mask or not; compute type (fp16
-  // with the NF4 weight and no mask only)
-  if (cfg.tm == 256) {
+  // block tile (k x tokens); weight format; dropout mask or not; compute
+  // type (fp16 with the NF4 weight and no mask only; the narrow tile with
+  // the NF4 weight only)
+  if (cfg.tn != TILE) {
     if (f16)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, F16T>), grid, dim3(256), 0, s, p);
-    else if (nf4 && !drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, Bf16T>), grid, dim3(256), 0, s, p);
-    else if (nf4)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, true, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, F16T, 128>), grid, dim3(256), 0,
+                         s, p);
     else if (!drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, false, Bf16T>), grid, dim3(256), 0, s,
-                         p);
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, Bf16T, 128>), grid, dim3(256), 0,
+                         s, p);
     else
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, true, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, true, Bf16T, 128>), grid, dim3(256), 0,
+                         s, p);
+  } else if (cfg.tm == 256) {
+    if (f16)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, F16T, 256>), grid, dim3(256), 0,
+                         s, p);
+    else if (nf4 && !drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, Bf16T, 256>), grid, dim3(256), 0,
+                         s, p);
+    else if (nf4)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, true, Bf16T, 256>), grid, dim3(256), 0,
+                         s, p);
+    else if (!drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, false, Bf16T, 256>), grid, dim3(256), 0,
+                         s, p);
+    else
+      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, true, Bf16T, 256>), grid, dim3(256), 0,
+                         s, p);
   } else {
     if (f16)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, F16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, F16T, 256>), grid, dim3(256), 0,
+                         s, p);
     else if (nf4 && !drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, Bf16T, 256>), grid, dim3(256), 0,
+                         s, p);
     else if (nf4)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, true, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, true, Bf16T, 256>), grid, dim3(256), 0,
+                         s, p);
     else if (!drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, false, Bf16T>), grid, dim3(256), 0, s,
-                         p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, false, Bf16T, 256>), grid, dim3(256), 0,
+                         s, p);
     else
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, true, Bf16T>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, true, Bf16T, 256>), grid, dim3(256), 0,
+                         s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
