@@ -136,7 +136,7 @@ def _gemm_schedule(M, Nout, Kred, narrow=False):
 
 def _schedule_label(cfg):
     tm, s, q, ts, tn = cfg
-    tile = f" [{tm} tokens x {tn} n tile]"
+    tile = f" [{tm} tokens x {tn} output columns tile]"
     if q:
         return tile + f" + tail_reduce_kernel ({q} tail tiles split {ts})"
     if s > 1:
