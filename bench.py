@@ -100,28 +100,31 @@ def make_layer(name):
 def _gemm_schedule(M, Nout, Kred, narrow=False):
     """Mirror of the library's schedule for a fused GEMM with an M x Nout
     output and a reduction of Kred (for naming the launches in the roofline
-    line only): (token tile, uniform splits, tail tiles, tail splits, n
-    tile).  narrow: a GEMM on the NF4 weight, which may take the 256-token
-    x 128 tile (split schedule only)."""
+    line only): (token tile, uniform splits, tail tiles, tail splits, output
+    column tile).  narrow: a GEMM on the NF4 weight, which may also take the
+    128 x 128 tile (split schedule, or whole tiles filling whole rounds)."""
     slots = 256
     nkt = Kred // 64
     best, best_t = (256, 1, 0, 1, 256), float("inf")
-    shapes = [(256, 256, 1.1e15), (128, 256, 0.8e15)] + ([(256, 128, 1.0e15)] if narrow else [])
+    shapes = [(256, 256, 1.1e15), (128, 256, 0.8e15)]
+    if narrow:
+        shapes += [(128, 128, 0.85e15)]
     for tm, tn, rate in shapes:
-        tiles = ((M + tm - 1) // tm) * ((Nout + tn - 1) // tn)
+        m_t = (M + tm - 1) // tm
+        tiles = m_t * ((Nout + tn - 1) // tn)
         t_tile = 2.0 * tm * tn * Kred / (rate / slots)
-        if tn != 256 and tiles >= 192:
-            continue
         if tiles < 192:
             s = max(1, min(256 // tiles, nkt // 4, 16))
             blocks = tiles * s
             fill = 1.0 if blocks >= slots else blocks / slots
-            est = 2.0 * M * Nout * Kred / (rate * fill)
+            est = 2.0 * (m_t * tm) * Nout * Kred / (rate * fill)
             if s > 1:
                 est += 2.0 * s * M * Nout * 4 / 5.0e12
             cfg = (tm, s, 0, 1, tn)
         else:
             rounds, q = divmod(tiles, slots)
+            if tn != 256 and q != 0:
+                continue
             ts = min(slots // q if q else 1, nkt // 4, 8)
             if q and ts >= 2:
                 est = (rounds + 1.0 / ts) * t_tile + 2.0 * ts * q * tm * tn * 4 / 5.0e12

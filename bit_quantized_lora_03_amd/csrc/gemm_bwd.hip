@@ -22,7 +22,7 @@
 //
 // Block tile 256 (k) x 256 (m), 64 reduction rows per stage; 4 waves in a
 // 2 x 2 grid of 128 x 128; two LDS stages of (W slab, dy tile).  (Small-M
-// shapes use 256 x 128, or the narrow 128 x 256 tile described at KW.)  As in the
+// shapes use 256 x 128, or the narrow 128 x 128 tile described at KW.)  As in the
 // forward pass, the next slab is decoded while the current one multiplies,
 // codes are fetched two slabs ahead, out-of-range rows are clamped rather
 // than branched around, and small outputs split the reduction over blocks
@@ -93,12 +93,12 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 //
 // DT: the 16-bit compute type (Bf16T, or F16T for the fp16 variant).
 //
-// KW: k extent of the block tile.  256 as above; 128 (NF4 only, with MS = 4:
-// a 128 (k) x 256 (m) tile for small-M split schedules) gives each thread
-// half an NF4 block -- the 32 values of its slab row at k quarter
-// kq -- so a thread decodes half as many weights per MFMA; each wave then
-// owns 64 (k) x 128 (m).  The slab rows shrink to 256 bytes + 48 of pad,
-// 76 dwords = 12 mod 64 banks, the same bank pattern as the wide slab.
+// KW: k extent of the block tile.  256 as above; 128 (NF4 only, used with
+// MS = 2: a 128 (k) x 128 (m) tile for small-M shapes) gives each thread
+// half an NF4 block -- the 32 values of its slab row at k quarter kq -- so
+// a thread decodes half as many weights per MFMA; each wave then owns
+// 64 (k) x 64 (m).  The slab rows shrink to 256 bytes + 48 of pad, 76
+// dwords = 12 mod 64 banks, the same bank pattern as the wide slab.
 template <int MS, int WF, bool DROP, class DT, int KW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
@@ -488,13 +488,13 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   // the NF4 weight only)
   if (cfg.tn != TILE) {
     if (f16)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, F16T, 128>), grid, dim3(256), 0,
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, F16T, 128>), grid, dim3(256), 0,
                          s, p);
     else if (!drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, Bf16T, 128>), grid, dim3(256), 0,
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, Bf16T, 128>), grid, dim3(256), 0,
                          s, p);
     else
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, true, Bf16T, 128>), grid, dim3(256), 0,
+      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, true, Bf16T, 128>), grid, dim3(256), 0,
                          s, p);
   } else if (cfg.tm == 256) {
     if (f16)

@@ -15,8 +15,8 @@
 //
 // Block tile 256 (n) x TM (m) x 64 (k), TM = 256 or 128; 4 waves, wave w
 // owning weight rows 64 w .. 64 w + 63 against all TM tokens (2 x TM/32
-// MFMA 32x32x16 tiles, fp32 accumulate, one wave per SIMD); small-M split
-// schedules may use a narrow 128 (n) x 256 (m) tile instead (RW below).
+// MFMA 32x32x16 tiles, fp32 accumulate, one wave per SIMD); small-M
+// shapes may use a narrow 128 (n) x 128 (m) tile instead (RW below).
 // Thread t decodes row 64 w + t of its wave into eight 8-value chunks.
 // MFMA step kk of a k tile takes, in lanes 0..31, k chunk kk and, in
 // lanes 32..63, chunk 4 + kk (the reduction order inside a tile is free, as
@@ -111,11 +111,12 @@ __device__ __forceinline__ void swap_halves(u32x4_t& a, u32x4_t& b, int v) {
 //
 // RW: weight rows per wave.  64 (the block tile is 256 n x TM): each lane
 // decodes a whole row and the lane halves swap chunks, as described above.
-// 32 (the block tile is 128 n x TM, NF4 only): lanes l and l + 32 share
-// row l % 32 and each decodes just the four chunks its own MFMA operand
-// takes (chunks 4 (l / 32) + kk), so a lane decodes half as many weights
-// per MFMA and nothing is swapped -- the tile for small M, where the
-// 256 n x 128 token tile would give each decoded weight only 4 token tiles.
+// 32 (the block tile is 128 n x TM, NF4 only; used with TM = 128): lanes l
+// and l + 32 share row l % 32 and each decodes just the four chunks its own
+// MFMA operand takes (chunks 4 (l / 32) + kk), so a lane decodes half as
+// many weights per MFMA and nothing is swapped.  The 128 x 128 tile thus
+// has the decode-to-MFMA ratio of the 256 x 256 one while giving small-M
+// shapes four times the output tiles (fewer k splits, fewer partials).
 template <int JT, int WF, class DT, int RW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(FwdParams p) {
@@ -567,17 +568,19 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restric
 }
 
 // Schedule of a fused GEMM: output Mout x Nout, reduction Kred (both GEMMs
-// tile the reduction by 64 and the non-token output dimension by 256).  For
-// each token tile (256 or 128 rows) the estimate is
+// tile the reduction by 64 and the non-token output dimension by 256, or
+// by 128 with the narrow tiles).  For
+// each block tile the estimate is
 //   rounds * (time of one tile on one CU) + fp32 partial traffic,
 // where a round is 256 concurrent blocks (one per CU).  Few tiles: split
-// every tile's reduction until ~256 blocks run.  Otherwise the tiles run
-// whole, except that a last round filled less than half is split: its
-// tail_q tiles are split 256 / tail_q ways (at most 8, at least 4 k tiles
-// each), so it takes a fraction of a round.  The rates are the measured
-// sustained throughputs of the tiles.  With `narrow` (the forward GEMM on
-// the NF4 weight) a third tile, 256 tokens x 128 n with half rows per lane,
-// is considered for the split schedule.
+// every tile's reduction until ~256 blocks run (flops counted on the token
+// rows the tiles cover, padding included).  Otherwise the tiles run whole,
+// except that a last round filled less than half is split: its tail_q
+// tiles are split 256 / tail_q ways (at most 8, at least 4 k tiles each),
+// so it takes a fraction of a round.  The rates are the measured sustained
+// throughputs of the tiles.  With `narrow` (a GEMM on the NF4 weight) a
+// 128 x 128 tile is considered too, for the split schedule or for whole
+// tiles that fill whole rounds (never the split tail).
 GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred, bool narrow) {
   constexpr int kSlots = 256;  // concurrent blocks: one per CU
   const int64_t nkt = Kred / KT;
@@ -587,15 +590,15 @@ GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred, bool narrow) {
     int tm, tn;
     double rate;  // flop/s, whole chip
   };
-  const Shape shapes[3] = {{256, TILE_N, 1.1e15}, {128, TILE_N, 0.8e15}, {256, 128, 1.0e15}};
+  const Shape shapes[3] = {{256, TILE_N, 1.1e15}, {128, TILE_N, 0.8e15}, {128, 128, 0.85e15}};
   for (int si = 0; si < (narrow ? 3 : 2); ++si) {
     const int tm = shapes[si].tm, tn = shapes[si].tn;
     const double rate = shapes[si].rate;
-    const int64_t tiles = ((M + tm - 1) / tm) * ((Nout + tn - 1) / tn);
+    const int64_t m_t = (M + tm - 1) / tm;
+    const int64_t tiles = m_t * ((Nout + tn - 1) / tn);
     const double t_tile = 2.0 * tm * tn * (double)Kred / (rate / kSlots);
     GemmConfig c{tm, 1, 0, 0, 1, tn};
     double est;
-    if (tn != TILE_N && tiles >= 192) continue;  // the narrow tile: split schedule only
     if (tiles < 192) {
       int64_t sp = 256 / tiles;
       if (sp > nkt / 4) sp = nkt / 4;
@@ -604,10 +607,11 @@ GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred, bool narrow) {
       c.splits = (int)sp;
       const double blocks = (double)tiles * sp;
       const double fill = blocks >= kSlots ? 1.0 : blocks / kSlots;
-      est = 2.0 * M * Nout * (double)Kred / (rate * fill);
+      est = 2.0 * (m_t * tm) * Nout * (double)Kred / (rate * fill);
       if (sp > 1) est += 2.0 * sp * (double)M * Nout * 4 / 5.0e12;
     } else {
       const int64_t rounds = tiles / kSlots, q = tiles % kSlots;
+      if (tn != TILE_N && q != 0) continue;
       int64_t ts = q > 0 ? kSlots / q : 1;
       if (ts > nkt / 4) ts = nkt / 4;
       if (ts > 8) ts = 8;
@@ -689,9 +693,9 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   // narrow tile with the NF4 weight only)
   if (cfg.tn != TILE_N) {
     if (f16)
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, F16T, 32>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, F16T, 32>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, Bf16T, 32>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, Bf16T, 32>), grid, dim3(256), 0, s, p);
   } else if (cfg.tm == 256) {
     if (f16)
       hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, F16T, 64>), grid, dim3(256), 0, s, p);

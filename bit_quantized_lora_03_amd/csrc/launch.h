@@ -74,10 +74,10 @@ struct GemmConfig {
   int64_t full;  // tail schedule: tiles run whole
   int tail_q;    // tail schedule: split tiles (0: uniform schedule)
   int tail_s;    // tail schedule: splits per tail tile
-  int tn;        // Nout extent of the block tile: 256, or 128 (the forward's
-                 // narrow tile, uniform schedule only)
+  int tn;        // Nout extent of the block tile: 256, or 128 (the narrow
+                 // 128 x 128 tile; never with the tail schedule)
 };
-// narrow: the 128-wide tile may be chosen (the forward on the NF4 weight)
+// narrow: the 128 x 128 tile may be chosen (a GEMM on the NF4 weight)
 GemmConfig gemm_config(int64_t M, int64_t Nout, int64_t Kred, bool narrow = false);
 int64_t gemm_blocks(const GemmConfig& c, int64_t M, int64_t Nout);
 size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout);

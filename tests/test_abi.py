@@ -86,12 +86,16 @@ def test_workspace_sizes():
     assert ws(7, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
     assert ws(5, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
     # bf16-weight layer: no few-token path, so the tiled GEMMs' workspace
-    # at every M; its backward is laid out as the NF4 backward
-    assert ws(2, 512, 4096, 4096, 16) == ws(0, 512, 4096, 4096, 16)
+    # at every M
     assert ws(2, 16, 8192, 8192, 0) > 0           # split-K partials, no decode kernel
-    assert ws(3, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
-    # ... and no narrow (128-wide) tile: at 16 tokens the NF4 forward's 64
-    # narrow tiles split 4 ways, the bf16 weight's 32 wide tiles 8 ways
+    # ... and no narrow 128 x 128 tile: at q_proj its 64 tiles of 128 tokens
+    # x 256 split 4 ways, the NF4 layer's 128 narrow tiles 2 ways (both GEMMs)
+    P = 512 * 4096 * 4
+    for op_b, op_n in ((2, 0), (3, 1)):
+        assert ws(op_b, 512, 4096, 4096, 16) >= 4 * P
+        assert 2 * P <= ws(op_n, 512, 4096, 4096, 16) < 3 * P
+    # at 16 tokens the NF4 forward's 64 narrow tiles split 4 ways, the bf16
+    # weight's 32 tiles of 256 x 256 8 ways
     part = lambda s: s * 16 * 8192 * 4
     assert ws(4, 16, 8192, 8192, 64) >= part(4) and ws(4, 16, 8192, 8192, 64) < part(8)
     assert ws(2, 16, 8192, 8192, 64) >= part(8)
