@@ -74,10 +74,20 @@ def test_layer_65b_m4096(cuda):
 
 
 def test_split_tail_schedules_128_token_tiles(cuda):
-    """3200 x 2816 x 3072: the forward runs 256 whole 256x128 tiles plus 19
-    tail tiles split 8 ways, dX 256 whole tiles plus 44 tail tiles split 5
-    ways (the last sampled row, M - 1, lies in a tail tile of both)."""
+    """3200 x 2816 x 3072: the forward runs 256 whole tiles of 128 tokens x
+    256 plus 19 tail tiles split 8 ways, dX 256 whole tiles plus 44 tail
+    tiles split 5 ways (the last sampled row, M - 1, lies in a tail tile of
+    both)."""
     _check_layer(workloads.layer(3200, 2816, 3072, 16, 32.0, seed=21, name="tail128",
+                                 outlier_frac=0.001))
+
+
+@pytest.mark.parametrize("M", [1024, 64])
+def test_narrow_tile_schedules(cuda, M):
+    """4096 x 4096 with the narrow 128 x 128 tile in both GEMMs: at M = 1024
+    as 256 whole tiles (one round, no split, no reduce kernel), at M = 64 as
+    32 tiles split 8 ways (64 of each tile's 128 token rows are padding)."""
+    _check_layer(workloads.layer(M, 4096, 4096, 16, 32.0, seed=41, name=f"narrow_m{M}",
                                  outlier_frac=0.001))
 
 
