@@ -300,18 +300,19 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
 // lora_proj_small: the same product when M r is small (few tokens and a
 // small rank).  With 16 x 16 MFMA tiles such a job has only M / 16 blocks,
 // and each has to pull in a whole 16-row slice of x plus all of Y; here a
-// block owns 8 tokens x 8 rank columns (so M r / 64 blocks, each reading
-// 16 rows) and the whole reduction.  Its 256 threads take the 8-wide pieces
+// block owns TT tokens x 8 rank columns (so M r / (8 TT) blocks, each
+// reading TT + 8 rows) and the whole reduction: TT = 8, or 4 when 8-token
+// blocks would leave CUs without one.  Its 256 threads take the 8-wide pieces
 // of the reduction t, t + 256, ... and accumulate with v_dot2_f32_bf16
 // (two bf16 products added into an fp32 sum, no conversions).  B's pieces
 // (8 rank columns of one k) are turned into (k, k + 1) pairs of one column
 // with one v_perm per pair.  The 256 threads' sums are added in LDS in a
-// fixed order, then by a fixed butterfly over 4 lanes.
+// fixed order, then by a fixed butterfly over 256 / (8 TT) lanes.
 // ---------------------------------------------------------------------------
-constexpr int kSmallT = 8, kSmallR = 8;  // tokens, rank columns per block
-constexpr int kSmallRed = 65;            // LDS row of a thread's 64 sums (+1: no bank conflicts)
+constexpr int kSmallR = 8;     // rank columns per block
+constexpr int kSmallRed = 65;  // LDS row of a thread's (up to) 64 sums (+1: no bank conflicts)
 
-template <bool DROP, class DT>
+template <bool DROP, class DT, int TT>
 __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, LoraProjJob j1,
                                                               int64_t blocks0, int64_t M, int r,
                                                               float scale) {
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
   const LoraProjJob J = uniform_job(second ? j1 : j0);
   const int64_t b = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
   const int rg = r / kSmallR;
-  const int64_t m0 = kSmallT * (b / rg);
+  const int64_t m0 = TT * (b / rg);
   const int jc = (int)(b % rg) * kSmallR;
   const int64_t Kred = J.Kred;
   const int64_t npc = Kred / 8;  // 8-wide pieces of the reduction
@@ -330,26 +331,26 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(J.X, (uint32_t)(M * Kred * 2));
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(J.Y, (uint32_t)((int64_t)r * Kred * 2));
   // rows past M lie past x's end and read as zero
-  uint32_t xoff[kSmallT], koff[kSmallT];
+  uint32_t xoff[TT], koff[TT];
 #pragma unroll
-  for (int i = 0; i < kSmallT; ++i) {
+  for (int i = 0; i < TT; ++i) {
     xoff[i] = (uint32_t)((m0 + i) * Kred * 2);
     koff[i] = (uint32_t)((m0 + i) * (Kred / 8));  // keep byte of piece pc: koff + pc
   }
   const KeepBits kp = keep_bits(J.keep, M * Kred / 8);
 
-  float acc[kSmallT][kSmallR];
+  float acc[TT][kSmallR];
 #pragma unroll
-  for (int i = 0; i < kSmallT; ++i)
+  for (int i = 0; i < TT; ++i)
 #pragma unroll
     for (int j = 0; j < kSmallR; ++j) acc[i][j] = 0.0f;
 
   // piece u of this thread: k = 8 (t + 256 u) .. + 7; x rows, then Y: A's
   // rows jc .. jc + 7 (kmajor == 0) or B's rows k .. k + 7 (kmajor == 1)
   struct Piece {
-    u32x4_t x[kSmallT];
+    u32x4_t x[TT];
     u32x4_t y[kSmallR];
-    uint32_t kb[kSmallT];
+    uint32_t kb[TT];
   };
   // Every offset here differs between lanes, so all of it is lane offset.
   // Pieces past the thread's count OR in kOff: a select the compiler keeps
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
     const uint32_t past = u < cnt ? 0u : kOff;
     const uint32_t pc = (uint32_t)(t + 256 * u);  // 8-wide piece index
 #pragma unroll
-    for (int i = 0; i < kSmallT; ++i) {
+    for (int i = 0; i < TT; ++i) {
       P.x[i] = ldb(xres, (xoff[i] + 16u * pc) | past, 0);
       if constexpr (DROP) P.kb[i] = ldb8(kp.res, (koff[i] + pc) | past, 0) | kp.all;
     }
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
       }
     }
 #pragma unroll
-    for (int i = 0; i < kSmallT; ++i) {
+    for (int i = 0; i < TT; ++i) {
       const u32x4_t xv = DROP ? keep8(P.x[i], P.kb[i]) : P.x[i];
 #pragma unroll
       for (int q = 0; q < kSmallR; ++q)
@@ -412,20 +413,21 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
   }
 
 #pragma unroll
-  for (int i = 0; i < kSmallT; ++i)
+  for (int i = 0; i < TT; ++i)
 #pragma unroll
     for (int q = 0; q < kSmallR; ++q) red[t * kSmallRed + i * kSmallR + q] = acc[i][q];
   __syncthreads();
-  // output o = t / 4: its 256 sums, lane t % 4 taking every fourth.  The
-  // trip count is a constant so the loop unrolls and its LDS reads are
-  // issued together (a lane-dependent bound left one read and one wait per
-  // step).
-  const int o = t >> 2, part = t & 3;
+  // output o = t / LPO (TT x 8 outputs): its 256 sums, lane t % LPO taking
+  // every LPO-th, then a butterfly over those LPO lanes.  The trip count is
+  // a constant so the loop unrolls and its LDS reads are issued together (a
+  // lane-dependent bound left one read and one wait per step).
+  constexpr int LPO = 256 / (TT * kSmallR);
+  const int o = t / LPO, part = t % LPO;
   float sum = red[part * kSmallRed + o];
 #pragma unroll
-  for (int i = 1; i < 64; ++i) sum += red[(part + 4 * i) * kSmallRed + o];
-  sum += __shfl_xor(sum, 1, 4);
-  sum += __shfl_xor(sum, 2, 4);
+  for (int i = 1; i < 256 / LPO; ++i) sum += red[(part + LPO * i) * kSmallRed + o];
+#pragma unroll
+  for (int w = 1; w < LPO; w <<= 1) sum += __shfl_xor(sum, w, LPO);
   const int64_t Mp = pad32(M);
   const int64_t mo = m0 + o / kSmallR;
   const int jo = jc + o % kSmallR;
@@ -442,13 +444,20 @@ template <bool DROP, class DT>
 static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                               float scale, hipStream_t s) {
   if (proj_small(M, r)) {
-    // Mp / 8 token groups cover every row of the transposed copy
-    const int64_t per_job = (pad32(M) / kSmallT) * (r / kSmallR);
+    // Mp / TT token groups cover every row of the transposed copy; 4-token
+    // blocks when 8-token ones would not give every CU a block
+    const int jobs = j1 ? 2 : 1;
+    const bool t4 = (pad32(M) / 8) * (r / kSmallR) * jobs < 256;
+    const int64_t per_job = (pad32(M) / (t4 ? 4 : 8)) * (r / kSmallR);
     const LoraProjJob jb = j1 ? *j1 : j0;
-    const int64_t total = per_job * (j1 ? 2 : 1);
+    const int64_t total = per_job * jobs;
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((lora_proj_small_kernel<DROP, DT>), dim3((unsigned)total), dim3(256), 0,
-                       s, j0, jb, per_job, M, r, scale);
+    if (t4)
+      hipLaunchKernelGGL((lora_proj_small_kernel<DROP, DT, 4>), dim3((unsigned)total), dim3(256),
+                         0, s, j0, jb, per_job, M, r, scale);
+    else
+      hipLaunchKernelGGL((lora_proj_small_kernel<DROP, DT, 8>), dim3((unsigned)total), dim3(256),
+                         0, s, j0, jb, per_job, M, r, scale);
     return hipGetLastError();
   }
   const int jt = proj_jt(r);
