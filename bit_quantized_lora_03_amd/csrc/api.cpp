@@ -90,6 +90,17 @@ int check_rank(int32_t r) {
   return QLORA_OK;
 }
 
+// The adapter kernels address A [r, K] and B [N, r] (bf16), the hi/lo
+// products [M][2r] and their token-contiguous copies [2r][pad32(M)] (bf16)
+// with 32-bit buffer offsets as well: each must stay below 2 GiB.
+int check_adapter_sizes(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (r == 0) return QLORA_OK;
+  if (int64_t{2} * r * K >= kMaxTensorBytes || int64_t{2} * r * N >= kMaxTensorBytes ||
+      int64_t{4} * r * pad32(M) >= kMaxTensorBytes)
+    return QLORA_ESHAPE;
+  return QLORA_OK;
+}
+
 // ---- workspace layout --------------------------------------------------
 struct FwdWs {
   size_t xs_off, xst_off, part_off, total;
@@ -105,6 +116,13 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool decode = true,
   FwdWs L{};
   L.decode = decode && M <= qlora::kDecodeMaxM;
   if (M == 0) return L;
+  if (L.decode && r > 0) {
+    // the decode path's partial planes [S][M][N + r] fp32 are addressed with
+    // 32-bit buffer offsets; shapes whose planes would pass 2 GiB take the
+    // tiled path instead
+    const int64_t S = qlora::decode_splits(M, N, K, r);
+    if (S * M * (N + r) * int64_t{4} >= kMaxTensorBytes) L.decode = false;
+  }
   if (L.decode) {
     // with an adapter: fp32 sums of x . W'^T and k-split partials of
     // x . A^T, [S][M][N + r]; without one the decode path needs none
@@ -190,6 +208,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
     if (M < 0) return QLORA_EINVAL;
     const int64_t N = w->N, K = w->K;
     if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
+    if ((st = check_adapter_sizes(M, N, K, r)) != QLORA_OK) return st;
     if (M == 0) return QLORA_OK;
     if (!x || !y) return QLORA_EINVAL;
     if (r > 0 && (!A || !B)) return QLORA_EINVAL;
@@ -248,6 +267,7 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
     if (M < 0) return QLORA_EINVAL;
     const int64_t N = w->N, K = w->K;
     if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
+    if ((st = check_adapter_sizes(M, N, K, r)) != QLORA_OK) return st;
     if (M == 0) {
       // a sum over no tokens: dA = dB = 0 (or unchanged when accumulating)
       if (r == 0) return QLORA_OK;
@@ -329,7 +349,7 @@ const char* qlora_status_string(int status) {
     case QLORA_EINVAL: return "invalid argument (null pointer, negative size or aliasing)";
     case QLORA_ESHAPE:
       return "unsupported shape (N, K must be multiples of 64; r a multiple of 8 <= 256; "
-             "codes and each activation tensor at most 2 GiB)";
+             "codes, each activation tensor, A, B and the adapter products below 2 GiB)";
     case QLORA_EALIGN: return "device pointer not 16-byte aligned";
     case QLORA_ENOTSUP: return "unsupported block size (64 / 256 only)";
     case QLORA_EWORKSPACE: return "workspace missing or too small";
@@ -351,7 +371,7 @@ int qlora_nf4_levels(float* levels, float* thresholds) {
 
 size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r) {
   if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64 || check_rank(r) != QLORA_OK ||
-      check_sizes(M, N, K) != QLORA_OK)
+      check_sizes(M, N, K) != QLORA_OK || check_adapter_sizes(M, N, K, r) != QLORA_OK)
     return 0;
   if (op == 0) return fwd_layout(M, N, K, r).total;
   if (op == 1) return bwd_layout(M, N, K, r).total;

@@ -55,7 +55,7 @@ extern "C" {
 #define QLORA_OK          0
 #define QLORA_EINVAL     (-1) /* null pointer, negative size, aliasing        */
 #define QLORA_ESHAPE     (-2) /* K or N not a multiple of 64, r > 256 or r%8,
-                                  or a tensor above 2 GiB (see below)          */
+                                  or a tensor at or above 2 GiB (see below)    */
 #define QLORA_EALIGN     (-3) /* a device pointer is not 16-byte aligned      */
 #define QLORA_ENOTSUP    (-4) /* blocksize != 64 or blocksize2 != 256         */
 #define QLORA_EWORKSPACE (-5) /* workspace NULL or smaller than required      */
@@ -130,8 +130,10 @@ int qlora_dequantize_nf4(const qlora_nf4_weight* w, uint16_t* out, void* stream)
  *      accumulated in fp32 and rounded once to bf16 (nearest-even).
  * M >= 1 is arbitrary; N and K must be multiples of 64 (ESHAPE), the
  * packed codes (N*K/2 bytes) and x and y (M*K*2, M*N*2 bytes) at most
- * 2 GiB each (ESHAPE: the kernels use 32-bit byte offsets); r is 0 or
- * a multiple of 8 up to 256 (r = 0: base only, A and B may be NULL).
+ * 2 GiB each, and A, B and the adapter products (2*r*K, 2*N*r and
+ * 4*r*(M rounded up to 32) bytes) below 2 GiB (ESHAPE: the kernels use
+ * 32-bit byte offsets); r is 0 or a multiple of 8 up to 256 (r = 0: base
+ * only, A and B may be NULL).
  * workspace: device scratch of at least
  * qlora_linear_workspace_bytes(0, M, N, K, r) bytes, 256-byte aligned.      */
 int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,

@@ -324,3 +324,43 @@ def test_f16_validation():
     assert L.qlora_linear_bwd_f16(ctypes.byref(w), P3, None, 16, P4, P4 + 8192, 8, 16.0,
                                   P4 + 65536, P4 + 131072, P4 + 196608, 0, P4 + (1 << 19), needb,
                                   None) == -1                     # no dy
+
+
+def test_adapter_buffers_above_2gib_are_rejected():
+    """The adapter kernels address A [r, K], B [N, r] and the hi/lo products
+    [M][2r] (and their token-contiguous copies [2r][pad32(M)]) with 32-bit
+    buffer offsets: a shape that puts any of them at 2 GiB or more is
+    rejected before any HIP call, in the forward, the backward and the
+    workspace query."""
+    L = q.lib()
+    big_k = _weight(256, 1 << 22)       # A: 2 * 256 * 2^22 = 2 GiB
+    big_n = _weight(1 << 22, 64)        # B: 2 * 2^22 * 256 = 2 GiB
+    small = _weight(64, 64)
+
+    def fwd(w, M, r):
+        return L.qlora_linear_fwd(ctypes.byref(w), P3, M, P4, P4 + 8192, r, 16.0, 64 << 30,
+                                  None, 0, None)
+
+    def bwd(w, M, r):
+        return L.qlora_linear_bwd(ctypes.byref(w), P3, P3 + 16384, M, P4, P4 + 8192, r, 16.0,
+                                  64 << 30, 65 << 30, 66 << 30, 0, None, 0, None)
+    for w, M in ((big_k, 16), (big_n, 16), (small, 1 << 21)):   # last: 4 * 256 * 2^21
+        assert fwd(w, M, 256) == -2
+        assert bwd(w, M, 256) == -2
+        assert q.workspace_bytes(0, M, w.N, w.K, 256) == 0
+        assert q.workspace_bytes(1, M, w.N, w.K, 256) == 0
+    # one rank step below each limit passes validation up to the workspace
+    assert fwd(_weight(256, 1 << 22), 16, 248) == -5
+    # the backward with no tokens still checks the adapter sizes
+    assert bwd(big_n, 0, 256) == -2
+
+
+def test_decode_partials_above_2gib_take_the_tiled_path():
+    """The few-token path keeps fp32 partial planes [S][M][N + r] that its
+    kernels address with 32-bit offsets; where they would reach 2 GiB the
+    forward takes the tiled GEMM (the dropout forward's layout) instead."""
+    ws = q.workspace_bytes
+    N = 1 << 24                          # 32 * 2^24 * 4 = 2 GiB of partials
+    assert ws(0, 32, N, 64, 8) == ws(4, 32, N, 64, 8)
+    # a small shape still takes the decode path (its own, smaller layout)
+    assert ws(0, 32, 4096, 4096, 8) != ws(4, 32, 4096, 4096, 8)
