@@ -38,7 +38,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
-DEFAULT_WORKLOAD = "q_proj4096_m512_r16"
+DEFAULT_WORKLOAD = "up65b_m4096_r64"
 
 
 def packed_weight_bytes(N, K):
@@ -188,24 +188,45 @@ def cpu_threads():
     return len(os.sched_getaffinity(0)), "?"
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def run_cpu_baseline(L, kind, budget_s):
-    """Time the fp64 oracle on the host on this workload (test infrastructure,
-    used here only as the CPU reference).  One repetition is quantise +
-    double-quant + dequant of the whole weight and the layer on the batch
-    (or on a token sample scaled linearly when the batch alone would exceed
-    the budget); repetitions continue until about half the budget is spent,
-    and the median one is reported."""
+    """Time the fp64 oracle on the host on a bounded sample of this workload
+    (test infrastructure, used here only as the CPU reference).
+
+    The sample is a smaller layer of the same workload: the first n_s of the
+    N output rows of W (quantise + double-quant + dequant) and the layer on
+    the first m_s of the M tokens against those rows (forward and, for a
+    training step, backward).  Every part of the step is linear in the rows
+    and tokens it covers, so the time is scaled by N / n_s (encoding) and
+    (M / m_s) * (N / n_s) (layer).  Repetitions continue until about half
+    the budget is spent; the median is reported."""
     import oracle
-    w = L.w
-    x = L.f32("x")
-    dy = L.f32("dy") if "bwd" in kind else None
-    A = L.f32("A") if L.r else None
-    B = L.f32("B") if L.r else None
-    M = L.M
-    rows = M
-    est = (fwd_flops(M, L.N, L.K, L.r) + (bwd_flops(M, L.N, L.K, L.r) if "bwd" in kind else 0)) / 50e9
-    if est > budget_s:
-        rows = max(1, int(M * budget_s / est))
+    N, K, M, r = L.N, L.K, L.M, L.r
+    # about budget/2 of encoding and budget/2 of layer per repetition, at
+    # ~30 M weights/s (encoding) and ~50 GFLOP/s (fp64 BLAS) on this kind of host
+    n_s = N
+    while n_s > 64 and n_s * K > 15e6 * budget_s / 2:
+        n_s //= 2
+    n_s = max(64, n_s - n_s % 64)
+    layer_fl = lambda m: (fwd_flops(m, n_s, K, r) + (bwd_flops(m, n_s, K, r) if "bwd" in kind else 0))
+    m_s = M
+    while m_s > 1 and layer_fl(m_s) / 50e9 > budget_s / 4:
+        m_s = max(1, m_s // 2)
+    w = np.ascontiguousarray(L.w[:n_s])
+    x = L.f32("x")[:m_s]
+    dy = L.f32("dy")[:m_s, :n_s] if "bwd" in kind else None
+    A = L.f32("A") if r else None
+    B = L.f32("B")[:n_s] if r else None
     reps = []
     t_start = time.perf_counter()
     while True:
@@ -215,25 +236,195 @@ def run_cpu_baseline(L, kind, budget_s):
         t_q = time.perf_counter()
         wd = oracle.bf16_bits_to_f64(oracle.dequant_nf4_bits(packed, q, step, w.size)).reshape(w.shape)
         t1 = time.perf_counter()
-        oracle.lora_linear_fwd(x[:rows], wd, A, B, L.alpha)
+        oracle.lora_linear_fwd(x, wd, A, B, L.alpha)
         if "bwd" in kind:
-            oracle.lora_linear_bwd(x[:rows], dy[:rows], wd, A, B, L.alpha)
+            oracle.lora_linear_bwd(x, dy, wd, A, B, L.alpha)
         t2 = time.perf_counter()
-        # scale to a full step: quantise/dequantise once, the layer for M tokens
-        layer_s = (t2 - t1) * (M / rows)
-        reps.append(((t_q - t0) + (t1 - t_q) + layer_s, t_q - t0, t1 - t_q, t2 - t1))
+        enc_scale = N / n_s
+        layer_scale = (M / m_s) * (N / n_s)
+        reps.append(((t1 - t0) * enc_scale + (t2 - t1) * layer_scale, t_q - t0, t1 - t_q, t2 - t1))
         if time.perf_counter() - t_start > 0.5 * budget_s:
             break
     reps.sort()
     step_s, tq, td, tl = reps[len(reps) // 2]
-    full_flops = fwd_flops(M, L.N, L.K, L.r) + (bwd_flops(M, L.N, L.K, L.r) if "bwd" in kind else 0)
+    full_flops = fwd_flops(M, N, K, r) + (bwd_flops(M, N, K, r) if "bwd" in kind else 0)
     threads, blas = cpu_threads()
-    sample = (f"median of {len(reps)} repetitions ({time.perf_counter() - t_start:.1f} s): "
-              f"quantise + double-quant + dequant of the full {L.N}x{L.K} weight; "
-              f"layer on {rows} of {M} tokens, scaled linearly to {M} "
-              f"(quant {tq:.2f}s, dequant {td:.2f}s, layer {tl:.2f}s; blas={blas})")
+    sample = (f"median of {len(reps)} repetitions ({time.perf_counter() - t_start:.1f} s) on "
+              f"{cpu_model()}: quantise + double-quant + dequant of {n_s} of the {N} rows "
+              f"of the {N}x{K} weight (single-threaded numpy; {tq:.2f}s + {td:.2f}s), "
+              f"layer {'fwd + bwd' if 'bwd' in kind else 'fwd'} on {m_s} of {M} tokens "
+              f"against those rows (fp64 {blas} BLAS on {threads} threads; {tl:.2f}s); "
+              f"scaled linearly to the full step")
     return {"value": full_flops / step_s / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": sample, "step_s": step_s}
+            "kind": "oracle", "sample": sample, "cpu": cpu_model(), "step_s": step_s}
+
+
+def _to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda:0")
+
+
+def _timed(fn, reps):
+    """Average ms of fn(i) over reps back-to-back calls, HIP events on the
+    current stream (the one the library launches on)."""
+    import torch
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _capture(fn):
+    """fn() captured in a HIP graph (after two eager runs on a side stream)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def measure_gates(lib, to_dev, check, timed, steps):
+    """The gated workloads, timed in the same run as the headline:
+
+    * MFMA gate -- the 7B MLP layers (gate, up: 4096 -> 11008; down:
+      11008 -> 4096) at 2048 tokens: the base-only fused forward call and the
+      base-only dX call (each the GEMM kernel, plus its reduce kernel where
+      the schedule splits), 2MNK / time against 2.5 PFLOP/s; the calls with
+      the rank-16 adapter as context.
+    * HBM gate -- the decode-like 8192 x 8192 layer at 1, 4 and 16 tokens
+      with the rank-64 adapter, rotating 16 weight copies (554 MB, more than
+      the 256 MB on-package cache), 16 calls captured per graph: algorithmic
+      bytes (packed weight, x, A, B, y) / time against 8 TB/s, and the same
+      for the base-only call.
+    """
+    import torch
+    from bit_quantized_lora_03_amd import workloads as wl, _lib
+    P = lambda t: None if t is None else t.data_ptr()
+    sp = lambda: torch.cuda.current_stream().cuda_stream
+    dev = torch.device("cuda:0")
+    res = {}
+    greps = max(10, min(steps, 30))
+
+    def quantize(w):
+        Nw, Kw = w.shape
+        n = Nw * Kw
+        wd = to_dev(w)
+        c = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        a = torch.empty(n // 64, dtype=torch.float32, device=dev)
+        qq = torch.empty(n // 64, dtype=torch.uint8, device=dev)
+        st = torch.empty((n // 64 + 255) // 256, dtype=torch.float32, device=dev)
+        check(lib.qlora_quantize_nf4_dq(P(wd), n, P(c), P(a), P(qq), P(st), sp()), "quantize")
+        torch.cuda.synchronize()
+        del wd, a
+        return c, qq, st
+
+    for Lg in wl.mlp_7b():
+        Mg, Ng, Kg, rg, al = Lg.M, Lg.N, Lg.K, Lg.r, Lg.alpha
+        c, qq, st = quantize(Lg.w)
+        wt = _lib.Nf4Weight(P(c), P(qq), P(st), Ng, Kg)
+        xg, dyg = to_dev(Lg.x_bits), to_dev(Lg.dy_bits)
+        Ag, Bg = to_dev(Lg.A_bits), to_dev(Lg.B_bits)
+        yg = torch.empty((Mg, Ng), dtype=torch.int16, device=dev)
+        dxg = torch.empty((Mg, Kg), dtype=torch.int16, device=dev)
+        dAg = torch.empty((rg, Kg), dtype=torch.float32, device=dev)
+        dBg = torch.empty((Ng, rg), dtype=torch.float32, device=dev)
+        need = max(int(lib.qlora_linear_workspace_bytes(0, Mg, Ng, Kg, rg)),
+                   int(lib.qlora_linear_workspace_bytes(1, Mg, Ng, Kg, rg)), 256)
+        wsg = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def f(rr):
+            check(lib.qlora_linear_fwd(ctypes.byref(wt), P(xg), Mg, P(Ag) if rr else None,
+                                       P(Bg) if rr else None, rr, al, P(yg), P(wsg), wsg.numel(),
+                                       sp()), "gate fwd")
+
+        def b(rr):
+            check(lib.qlora_linear_bwd(ctypes.byref(wt), P(xg), P(dyg), Mg, P(Ag) if rr else None,
+                                       P(Bg) if rr else None, rr, al, P(dxg),
+                                       P(dAg) if rr else None, P(dBg) if rr else None, 0, P(wsg),
+                                       wsg.numel(), sp()), "gate bwd")
+        t_f = timed(lambda i: f(rg), greps)
+        t_b = timed(lambda i: b(rg), greps)
+        t_f0 = timed(lambda i: f(0), greps)
+        t_d0 = timed(lambda i: b(0), greps)
+        fl = 2.0 * Mg * Ng * Kg
+        res[Lg.name] = {
+            "M": Mg, "N": Ng, "K": Kg, "r": rg,
+            "fwd_gemm_ms": round(t_f0, 5),
+            "fwd_gemm_TFLOPs": round(fl / (t_f0 * 1e-3) / 1e12, 1),
+            "fwd_gemm_frac": round(fl / (t_f0 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "dx_gemm_ms": round(t_d0, 5),
+            "dx_gemm_TFLOPs": round(fl / (t_d0 * 1e-3) / 1e12, 1),
+            "dx_gemm_frac": round(fl / (t_d0 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "fwd_call_ms": round(t_f, 5), "bwd_call_ms": round(t_b, 5),
+            "fwd_bwd_TFLOPs": round((fwd_flops(Mg, Ng, Kg, rg) + bwd_flops(Mg, Ng, Kg, rg))
+                                    / ((t_f + t_b) * 1e-3) / 1e12, 1),
+            "gate_frac": 0.6,
+        }
+        del c, qq, st, xg, dyg, Ag, Bg, yg, dxg, dAg, dBg, wsg
+        torch.cuda.empty_cache()
+
+    rot = wl.DECODE_ROTATION
+    L0 = wl.decode_8192(1, 0)
+    Nd, Kd, rd, ad = L0.N, L0.K, L0.r, L0.alpha
+    c0, q0, s0 = quantize(L0.w)
+    copies = [(c0, q0, s0)] + [(c0.clone(), q0.clone(), s0.clone()) for _ in range(rot - 1)]
+    wts = [_lib.Nf4Weight(P(c), P(qq), P(st), Nd, Kd) for c, qq, st in copies]
+    Ad, Bd = to_dev(L0.A_bits), to_dev(L0.B_bits)
+    for Md in (1, 4, 16):
+        Ld = wl.decode_8192(Md)
+        xd = to_dev(Ld.x_bits)
+        yd = torch.empty((Md, Nd), dtype=torch.int16, device=dev)
+        need = max(int(lib.qlora_linear_workspace_bytes(0, Md, Nd, Kd, rd)), 256)
+        wsd = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def call(j, rr):
+            check(lib.qlora_linear_fwd(ctypes.byref(wts[j]), P(xd), Md, P(Ad) if rr else None,
+                                       P(Bd) if rr else None, rr, ad, P(yd), P(wsd), wsd.numel(),
+                                       sp()), "decode fwd")
+
+        def rotation(rr):
+            for j in range(rot):
+                call(j, rr)
+        times = {}
+        for rr in (rd, 0):
+            g = _capture(lambda: rotation(rr))
+            replays = 125                                   # 2000 calls
+            times[rr] = timed(lambda i: g.replay(), replays) / rot
+            del g
+        tb = packed_weight_bytes(Nd, Kd) + 2 * Md * Kd + 2 * Md * Nd
+        tt = fwd_bytes(Md, Nd, Kd, rd)
+        res[f"decode8192_m{Md}"] = {
+            "M": Md, "N": Nd, "K": Kd, "r": rd, "weight_rotation": rot,
+            "call_ms": round(times[rd], 5),
+            "total_GBps": round(tt / (times[rd] * 1e-3) / 1e9, 1),
+            "frac": round(tt / (times[rd] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "base_only_ms": round(times[0], 5),
+            "base_only_GBps": round(tb / (times[0] * 1e-3) / 1e9, 1),
+            "base_only_frac": round(tb / (times[0] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "gate_frac": 0.7,
+        }
+        del xd, yd, wsd
+    del copies, wts, c0, q0, s0, Ad, Bd
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -248,6 +439,10 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager calls, no graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--no-gates", action="store_true",
+                    help="skip the gate measurements of the 7B MLP and decode workloads")
+    ap.add_argument("--gates-only", action="store_true",
+                    help="time only the gate workloads (for profiling them on their own)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -261,6 +456,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.gates_only:
+        lib = q.lib()
+
+        def check0(rc, what):
+            if rc != 0:
+                raise RuntimeError(f"{what}: {lib.qlora_status_string(rc).decode()}")
+        print(json.dumps({"gates": measure_gates(lib, _to_dev, check0, _timed, args.steps)}))
+        return
     L, kind = make_layer(args.workload)
     M, N, K, r, alpha = L.M, L.N, L.K, L.r, L.alpha
     lib = q.lib()
@@ -584,6 +787,10 @@ def main():
                 "per_launch": fl, "duration_ms": t_k}
     roof["traffic"] = _recorded_traffic(args.workload, key)
 
+    gates = None
+    if not args.no_gates and args.workload == DEFAULT_WORKLOAD:
+        gates = measure_gates(lib, to_dev, check, timed, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(L, kind, args.cpu_budget)
@@ -611,6 +818,7 @@ def main():
         "dropout": drop,
         "fp16": f16,
         "merge": merge,
+        "gates": gates,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "step_s"},
         "wall_s": round(wall, 4),
     }

@@ -228,12 +228,16 @@ def linear_fwd(pw: PackedWeight, x, A, B, alpha: float, y=None, workspace=None):
 
 
 def linear_bwd(pw: PackedWeight, x, dy, A, B, alpha: float, need_dx: bool = True,
-               dA=None, dB=None, accumulate: bool = False, workspace=None):
-    """Returns (dx or None, dA fp32 [r, K] or None, dB fp32 [N, r] or None)."""
+               dA=None, dB=None, accumulate: bool = False, workspace=None, dx=None):
+    """Returns (dx or None, dA fp32 [r, K] or None, dB fp32 [N, r] or None);
+    dx, dA, dB may be passed in as output tensors."""
     torch = _torch()
     M = dy.shape[0]
     r = 0 if A is None else A.shape[0]
-    dx = torch.empty((M, pw.K), dtype=dy.dtype, device=dy.device) if need_dx else None
+    if need_dx and dx is None:
+        dx = torch.empty((M, pw.K), dtype=dy.dtype, device=dy.device)
+    if not need_dx:
+        dx = None
     if r > 0:
         if dA is None:
             dA = torch.empty((r, pw.K), dtype=torch.float32, device=dy.device)

@@ -104,3 +104,66 @@ def layer_inputs(L: workloads.Layer):
         d["A"] = dev(L.A_bits)
         d["B"] = dev(L.B_bits)
     return d
+
+
+# ---------------------------------------------------------------------------
+# guard-byte canaries around device outputs
+# ---------------------------------------------------------------------------
+
+GUARD_BYTES = 4096          # keeps the output 4096-byte aligned
+GUARD_PATTERN = 0xA5        # the guard regions
+FILL_PATTERN = 0xFF         # the output itself: NaN in bf16/fp16/fp32
+
+
+class Guarded:
+    """A device output tensor with GUARD_BYTES of a known pattern on each
+    side, and its own bytes preset to 0xFF (NaN for every float type, so an
+    element the kernel never writes fails the finiteness check).
+
+    ``.t`` is the output view (exactly ``shape`` x ``dtype``, no padding);
+    :meth:`check` asserts both guard regions are unchanged, i.e. no kernel
+    wrote past either end of the tensor."""
+
+    def __init__(self, shape, dtype, init=None):
+        import torch
+        shape = tuple(int(s) for s in shape)
+        esize = torch.empty((), dtype=dtype).element_size()
+        self.nbytes = int(np.prod(shape, dtype=np.int64)) * esize
+        self.buf = torch.full((GUARD_BYTES + self.nbytes + GUARD_BYTES,), GUARD_PATTERN,
+                              dtype=torch.uint8, device="cuda")
+        inner = self.buf[GUARD_BYTES:GUARD_BYTES + self.nbytes]
+        inner.fill_(FILL_PATTERN)
+        self.t = inner.view(dtype).view(shape)
+        if init is not None:
+            self.t.copy_(init)
+
+    def check(self, name: str) -> None:
+        import torch
+        torch.cuda.synchronize()
+        head = self.buf[:GUARD_BYTES].cpu().numpy()
+        tail = self.buf[GUARD_BYTES + self.nbytes:].cpu().numpy()
+        bad_h = int(np.count_nonzero(head != GUARD_PATTERN))
+        bad_t = int(np.count_nonzero(tail != GUARD_PATTERN))
+        assert bad_h == 0 and bad_t == 0, (
+            f"{name}: {bad_h} guard bytes before and {bad_t} after the tensor were written")
+
+
+def stratified_rows(M: int, tile: int = 256, extra: int = 16, seed: int = 0) -> np.ndarray:
+    """Token rows for sampled full-size parity: at least one row in every
+    ``tile``-token tile, every residue mod 32 (the MFMA row layout), the
+    first and the last 33 rows, and ``extra`` random rows."""
+    if M <= 96:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    rows = set(range(0, 1)) | set(range(M - 33, M))
+    ntiles = (M + tile - 1) // tile
+    for t in range(ntiles):
+        lo, hi = t * tile, min(M, (t + 1) * tile)
+        rows.add(int(rng.integers(lo, hi)))
+    for res in range(32):
+        cands = np.arange(res, M, 32)
+        rows.add(int(cands[rng.integers(0, cands.size)]))
+    rows.update(int(v) for v in rng.choice(M, min(extra, M), replace=False))
+    out = np.array(sorted(rows))
+    assert out.min() >= 0 and out.max() < M
+    return out
