@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     linear_fwd,
     linear_fwd_dropout,
     linear_fwd_f16,
+    linear_fwd_noalloc,
     merge_adapter,
     nf4_levels,
     quantize_nf4,

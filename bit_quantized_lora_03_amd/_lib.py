@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 
 QLORA_OK = 0
 STATUS_NAMES = {0: "QLORA_OK", -1: "QLORA_EINVAL", -2: "QLORA_ESHAPE", -3: "QLORA_EALIGN",
-                -4: "QLORA_ENOTSUP", -5: "QLORA_EWORKSPACE", -6: "QLORA_EHIP"}
+                -4: "QLORA_ENOTSUP", -5: "QLORA_EWORKSPACE", -6: "QLORA_EHIP",
+                -7: "QLORA_ESCRATCH"}
 
 EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
            "qlora_dequantize_nf4",
@@ -26,7 +27,8 @@ EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
            "qlora_dequantize_nf4_f16", "qlora_linear_fwd_f16", "qlora_linear_bwd_f16",
            "qlora_linear_bf16_fwd", "qlora_linear_bf16_bwd",
-           "qlora_merge_adapter", "qlora_nf4_levels", "qlora_status_string")
+           "qlora_merge_adapter", "qlora_linear_fwd_noalloc", "qlora_nf4_levels",
+           "qlora_status_string")
 
 
 class QloraError(RuntimeError):
@@ -79,6 +81,7 @@ def lib() -> ctypes.CDLL:
                                   ctypes.c_int),
         "qlora_linear_bf16_bwd": ([vp, i64, i64, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, i32,
                                    vp, sz, vp], ctypes.c_int),
+        "qlora_linear_fwd_noalloc": ([wp, vp, i64, vp, vp, i32, f32, vp, vp], ctypes.c_int),
         "qlora_nf4_levels": ([vp, vp], ctypes.c_int),
         "qlora_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
@@ -224,6 +227,22 @@ def linear_fwd(pw: PackedWeight, x, A, B, alpha: float, y=None, workspace=None):
     check(lib().qlora_linear_fwd(ctypes.byref(s), _ptr(x), M, _ptr(A), _ptr(B), r, float(alpha),
                                  _ptr(y), _ptr(ws), need if workspace is None else ws.numel(),
                                  _stream_ptr()), "qlora_linear_fwd")
+    return y
+
+
+def linear_fwd_noalloc(pw: PackedWeight, x, A, B, alpha: float, y=None):
+    """The forward of :func:`linear_fwd` through qlora_linear_fwd_noalloc: no
+    workspace argument (the library's static scratch buffer serves); the
+    call allocates nothing when ``y`` is given."""
+    torch = _torch()
+    M = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if y is None:
+        y = torch.empty((M, pw.N), dtype=x.dtype, device=x.device)
+    s = pw.struct()
+    check(lib().qlora_linear_fwd_noalloc(ctypes.byref(s), _ptr(x), M, _ptr(A), _ptr(B), r,
+                                         float(alpha), _ptr(y), _stream_ptr()),
+          "qlora_linear_fwd_noalloc")
     return y
 
 

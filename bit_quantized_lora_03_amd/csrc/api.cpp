@@ -197,9 +197,12 @@ struct Wref {
 
 // keep (or null) and p: LoRA dropout on the adapter's input
 // f16: the fp16 compute type (x, A, B, y in fp16), NF4 weight, no dropout
+// src (or null): the workspace comes from src(need) once every argument has
+// been validated, instead of from workspace / ws_bytes
 int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
              int32_t r, float alpha, const uint8_t* keep, float p, uint16_t* y,
-             void* workspace, size_t ws_bytes, void* stream, bool f16 = false) {
+             void* workspace, size_t ws_bytes, void* stream, bool f16 = false,
+             qlora::WorkspaceSource src = nullptr) {
   try {
     int st = QLORA_OK;
     if ((st = check_rank(r)) != QLORA_OK) return st;
@@ -217,16 +220,21 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
       return QLORA_EALIGN;
     // the few-token decode kernel has no dropout: the tiled path then runs
     const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep && !f16, w->nf4());
-    if (ws.total > 0) {
-      if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
-      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
-    }
     const size_t ny = (size_t)M * N * 2;
     if (overlap(y, ny, x, (size_t)M * K * 2) || overlap(y, ny, w->data(), w->bytes()) ||
         (r > 0 && (overlap(y, ny, A, (size_t)r * K * 2) || overlap(y, ny, B, (size_t)N * r * 2))) ||
-        (ws.total > 0 && overlap(y, ny, workspace, ws.total)) ||
         (keep && overlap(y, ny, keep, (size_t)M * K / 8)))
       return QLORA_EINVAL;
+    if (src && ws.total > 0) {
+      workspace = src(ws.total, &st);
+      if (!workspace) return st;
+      ws_bytes = ws.total;
+    }
+    if (ws.total > 0) {
+      if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
+      if (overlap(y, ny, workspace, ws.total)) return QLORA_EINVAL;
+    }
 
     hipStream_t s = as_stream(stream);
     const Nf4Levels L = levels_arg();
@@ -341,6 +349,19 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
 
 }  // namespace
 
+namespace qlora {
+
+int linear_fwd_sourced(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                       const uint16_t* B, int32_t r, float alpha, uint16_t* y,
+                       WorkspaceSource src, void* stream) {
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, 0.0f, y, nullptr, 0, stream, false, src);
+}
+
+}  // namespace qlora
+
 extern "C" {
 
 const char* qlora_status_string(int status) {
@@ -354,6 +375,9 @@ const char* qlora_status_string(int status) {
     case QLORA_ENOTSUP: return "unsupported block size (64 / 256 only)";
     case QLORA_EWORKSPACE: return "workspace missing or too small";
     case QLORA_EHIP: return "HIP launch or runtime error";
+    case QLORA_ESCRATCH:
+      return "the call needs more scratch than the library's static buffer holds "
+             "(QLORA_NOALLOC_SCRATCH_BYTES); use the call with a caller workspace";
     default: return "unknown status";
   }
 }

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libqlora.so")
 
 SOURCES = ["api.cpp", "nf4_table.cpp", "quant_kernels.hip", "lora_kernels.hip",
-           "gemm_fwd.hip", "gemm_bwd.hip", "gemm_decode.hip", "merge.hip"]
+           "gemm_fwd.hip", "gemm_bwd.hip", "gemm_decode.hip", "merge.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 HIP_FLAGS = [

@@ -8,7 +8,16 @@
 
 #include "device_common.h"
 
+struct qlora_nf4_weight;
+
 namespace qlora {
+
+// api.cpp -- the forward pass whose workspace comes from src(need, &status)
+// once every argument has been validated (null with *status set on failure)
+using WorkspaceSource = void* (*)(size_t need, int* status);
+int linear_fwd_sourced(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                       const uint16_t* B, int32_t r, float alpha, uint16_t* y,
+                       WorkspaceSource src, void* stream);
 
 // quant_kernels.hip
 hipError_t launch_quantize(const float* w, int64_t n, uint8_t* codes, float* absmax,

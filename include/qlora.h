@@ -60,6 +60,8 @@ extern "C" {
 #define QLORA_ENOTSUP    (-4) /* blocksize != 64 or blocksize2 != 256         */
 #define QLORA_EWORKSPACE (-5) /* workspace NULL or smaller than required      */
 #define QLORA_EHIP       (-6) /* a HIP launch or runtime call failed          */
+#define QLORA_ESCRATCH   (-7) /* the allocation-free call needs more than
+                                  QLORA_NOALLOC_SCRATCH_BYTES of scratch       */
 
 #define QLORA_BLOCK   64   /* weights per absmax block                       */
 #define QLORA_GROUP   256  /* block scales per double-quantisation group      */
@@ -258,6 +260,33 @@ int qlora_linear_bf16_bwd(const uint16_t* W, int64_t N, int64_t K, const uint16_
                           const uint16_t* dy, int64_t M, const uint16_t* A, const uint16_t* B,
                           int32_t r, float alpha, uint16_t* dx, float* dA, float* dB,
                           int32_t accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/* The forward pass of qlora_linear_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation, kernels and
+ * bits, with the workspace taken from a static device buffer that the
+ * library holds instead of a caller argument.
+ *   - The buffer is QLORA_NOALLOC_SCRATCH_BYTES (96 MiB) per GPU, allocated
+ *     when the library's code is loaded on that GPU and held until the
+ *     process ends.  A call whose workspace need,
+ *     qlora_linear_workspace_bytes(0, M, N, K, r), exceeds it returns
+ *     QLORA_ESCRATCH before any HIP call (every workload of this library
+ *     fits: the largest, 2048 tokens through an 11008 -> 4096 layer, needs
+ *     64.25 MiB).
+ *   - The call allocates nothing (no hipMalloc, no hipFree).  On the first
+ *     call on a GPU it looks up that GPU's copy of the buffer (a
+ *     hipGetSymbolAddress with the current device, which must be the
+ *     stream's device) and keeps the address.
+ *   - Every call on one GPU shares that GPU's buffer: calls that may
+ *     overlap in time on one GPU (different streams, or several host
+ *     threads) race and give wrong results; serialise them (one stream) or
+ *     use qlora_linear_fwd with separate workspaces.  The buffer keeps the
+ *     last call's contents; no kernel reads what an earlier call left.
+ * Arguments, shapes, rounding and other errors as qlora_linear_fwd.        */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                             uint16_t* y, void* stream);
 
 /* Workspace bytes for op 0 (forward) or 1 (backward) of the NF4 layer,
  * op 2 (forward) or 3 (backward) of the bf16-weight layer, op 4 (forward)

@@ -50,7 +50,7 @@ def test_library_table_equals_oracle_bitwise():
 
 def test_status_strings():
     L = q.lib()
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert len(L.qlora_status_string(code)) >= 2
     assert L.qlora_status_string(-99) == b"unknown status"
 
@@ -364,3 +364,30 @@ def test_decode_partials_above_2gib_take_the_tiled_path():
     assert ws(0, 32, N, 64, 8) == ws(4, 32, N, 64, 8)
     # a small shape still takes the decode path (its own, smaller layout)
     assert ws(0, 32, 4096, 4096, 8) != ws(4, 32, 4096, 4096, 8)
+
+
+def test_noalloc_forward_validation():
+    """qlora_linear_fwd_noalloc validates like qlora_linear_fwd, and rejects a
+    call whose workspace need exceeds the static scratch buffer with
+    QLORA_ESCRATCH -- all before any HIP call (no GPU here)."""
+    L = q.lib()
+    cap = 96 << 20
+    w = _weight(4096, 4096)
+
+    def call(**kw):
+        a = dict(w=w, x=P3, M=16384, A=P4, B=P4 + (4 << 20), r=256, y=64 << 30)
+        a.update(kw)
+        return L.qlora_linear_fwd_noalloc(ctypes.byref(a["w"]), a["x"], a["M"], a["A"], a["B"],
+                                          a["r"], 16.0, a["y"], None)
+    # 65536 tokens at rank 256: the hi/lo adapter products alone are 128 MiB
+    assert q.workspace_bytes(0, 65536, 4096, 4096, 256) > cap
+    assert call(M=65536) == -7
+    assert b"static" in L.qlora_status_string(-7)
+    # the other errors of the forward, in the same order
+    assert L.qlora_linear_fwd_noalloc(None, P3, 16, P4, P4, 8, 16.0, P1, None) == -1
+    assert call(w=_weight(250, 256)) == -2
+    assert call(r=12) == -2
+    assert call(x=None) == -1
+    assert call(x=P3 + 2) == -3
+    assert call(y=P3) == -1                                   # y aliases x
+    assert call(M=0) == 0                                     # empty: no-op
