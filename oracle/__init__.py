@@ -15,6 +15,9 @@ What it computes (numpy, fp64 unless a step fixes another precision):
 * ``lora_linear`` -- the layer y = x.W'^T + (alpha/r).(x.A^T).B^T and its
   gradients dX, dA, dB on the decoded weight W', optionally with LoRA
   dropout on the adapter's input (the keep-mask is an input).
+* ``philox`` -- Philox4x32-10 and the LoRA-dropout keep mask the library
+  draws from it in-kernel (counter = mask byte and stream offset, key =
+  seed; 16-bit draws against a threshold).
 * ``merge`` -- the adapter merged into a base weight for export,
   W_m = W_base + (alpha/r).B.A (fp32 and bf16 exports, re-quantisation, and
   the errors of the three ways to export).
@@ -51,3 +54,10 @@ from .nf4 import (  # noqa: F401
 )
 from .lora_linear import lora_linear_fwd, lora_linear_bwd, lora_scale, dropped_input  # noqa: F401
 from .merge import merge_adapter, merged_bf16_bits, requantize, merge_errors  # noqa: F401
+from .philox import (  # noqa: F401
+    philox4x32_10,
+    dropout_threshold,
+    realised_dropout,
+    dropout_uniforms,
+    dropout_keep_philox,
+)
