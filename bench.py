@@ -680,16 +680,35 @@ def main():
                                                P(B_d), r, alpha, P(keep_d), p_drop, P(dx), P(dA),
                                                P(dB), 0, P(ws_d), ws_d.numel(), sp()),
                   "bwd dropout")
+        # the keep bits drawn in the kernels (Philox4x32-10 from a seed and
+        # an offset, no mask tensor)
+        need_r = max(q.workspace_bytes(8, M, N, K, r), q.workspace_bytes(9, M, N, K, r), 256)
+        ws_r = torch.empty(need_r, dtype=torch.uint8, device=dev)
+
+        def fwd_r():
+            check(lib.qlora_linear_fwd_dropout_rng(ctypes.byref(wt_d), P(x_d), M, P(A_d), P(B_d),
+                                                   r, alpha, p_drop, 1234, 5, P(y), P(ws_r),
+                                                   ws_r.numel(), sp()), "fwd dropout rng")
+
+        def bwd_r():
+            check(lib.qlora_linear_bwd_dropout_rng(ctypes.byref(wt_d), P(x_d), P(dy_d), M,
+                                                   P(A_d), P(B_d), r, alpha, p_drop, 1234, 5,
+                                                   P(dx), P(dA), P(dB), 0, P(ws_r),
+                                                   ws_r.numel(), sp()), "bwd dropout rng")
         # each dropout call timed right after the same call without dropout
         # (the chip's clock drifts over a long run)
         t_f = timed(lambda i: fwd(0), reps)
         t_fd = timed(lambda i: fwd_d(), reps)
+        t_fr = timed(lambda i: fwd_r(), reps)
         t_b = timed(lambda i: bwd(), reps)
         t_bd = timed(lambda i: bwd_d(), reps)
+        t_br = timed(lambda i: bwd_r(), reps)
         drop = {"p": p_drop, "fwd_ms": round(t_fd, 5), "bwd_ms": round(t_bd, 5),
                 "fwd_ms_without": round(t_f, 5), "bwd_ms_without": round(t_b, 5),
-                "over_no_dropout": round((t_fd + t_bd) / (t_f + t_b), 4)}
-        del keep_d, ws_d
+                "over_no_dropout": round((t_fd + t_bd) / (t_f + t_b), 4),
+                "drawn_fwd_ms": round(t_fr, 5), "drawn_bwd_ms": round(t_br, 5),
+                "drawn_over_no_dropout": round((t_fr + t_br) / (t_f + t_b), 4)}
+        del keep_d, ws_d, ws_r
 
     # ---- the fp16 compute-type variant of the same fwd + bwd (same packed
     # weight; x, A, B, dy in fp16), each timed right after the bf16 call ----

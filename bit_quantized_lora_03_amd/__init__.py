@@ -18,14 +18,17 @@ from ._lib import (  # noqa: F401
     dequantize,
     dequantize_f16,
     double_quant,
+    dropout_keep_mask,
     lib,
     linear_bf16_bwd,
     linear_bf16_fwd,
     linear_bwd,
     linear_bwd_dropout,
+    linear_bwd_dropout_rng,
     linear_bwd_f16,
     linear_fwd,
     linear_fwd_dropout,
+    linear_fwd_dropout_rng,
     linear_fwd_f16,
     linear_fwd_noalloc,
     merge_adapter,

@@ -27,6 +27,8 @@ EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
            "qlora_dequantize_nf4_f16", "qlora_linear_fwd_f16", "qlora_linear_bwd_f16",
            "qlora_linear_bf16_fwd", "qlora_linear_bf16_bwd",
+           "qlora_dropout_keep_mask", "qlora_linear_fwd_dropout_rng",
+           "qlora_linear_bwd_dropout_rng",
            "qlora_merge_adapter", "qlora_linear_fwd_noalloc", "qlora_nf4_levels",
            "qlora_status_string")
 
@@ -56,8 +58,8 @@ def lib() -> ctypes.CDLL:
         raise ImportError(f"{LIB_PATH} is missing; build it with "
                           "`python -m bit_quantized_lora_03_amd.csrc.build`")
     L = ctypes.CDLL(LIB_PATH)
-    vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                             ctypes.c_float, ctypes.c_size_t)
+    vp, i64, i32, f32, sz, u64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64)
     wp = ctypes.POINTER(Nf4Weight)
     sig = {
         "qlora_quantize_nf4": ([vp, i64, i32, vp, vp, vp], ctypes.c_int),
@@ -82,6 +84,11 @@ def lib() -> ctypes.CDLL:
         "qlora_linear_bf16_bwd": ([vp, i64, i64, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, i32,
                                    vp, sz, vp], ctypes.c_int),
         "qlora_linear_fwd_noalloc": ([wp, vp, i64, vp, vp, i32, f32, vp, vp], ctypes.c_int),
+        "qlora_dropout_keep_mask": ([i64, i64, f32, u64, u64, vp, vp], ctypes.c_int),
+        "qlora_linear_fwd_dropout_rng": ([wp, vp, i64, vp, vp, i32, f32, f32, u64, u64, vp, vp,
+                                          sz, vp], ctypes.c_int),
+        "qlora_linear_bwd_dropout_rng": ([wp, vp, vp, i64, vp, vp, i32, f32, f32, u64, u64, vp,
+                                          vp, vp, i32, vp, sz, vp], ctypes.c_int),
         "qlora_nf4_levels": ([vp, vp], ctypes.c_int),
         "qlora_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
@@ -357,6 +364,64 @@ def linear_bwd_dropout(pw: PackedWeight, x, dy, A, B, alpha: float, keep, p: flo
                                          _ptr(dA), _ptr(dB), int(accumulate), _ptr(ws),
                                          need if workspace is None else ws.numel(),
                                          _stream_ptr()), "qlora_linear_bwd_dropout")
+    return dx, dA, dB
+
+
+def dropout_keep_mask(M: int, K: int, p: float, seed: int, offset: int, device=None, keep=None):
+    """The packed keep mask [M, K/8] (uint8) that the library's drawn LoRA
+    dropout uses for (p, seed, offset)."""
+    torch = _torch()
+    if keep is None:
+        keep = torch.empty((M, K // 8), dtype=torch.uint8, device=device or "cuda")
+    check(lib().qlora_dropout_keep_mask(M, K, float(p), int(seed), int(offset), _ptr(keep),
+                                        _stream_ptr()), "qlora_dropout_keep_mask")
+    return keep
+
+
+def linear_fwd_dropout_rng(pw: PackedWeight, x, A, B, alpha: float, p: float, seed: int,
+                           offset: int, y=None, workspace=None):
+    """The forward with LoRA dropout drawn by the library (Philox4x32-10 from
+    (seed, offset); no mask argument)."""
+    torch = _torch()
+    M = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if y is None:
+        y = torch.empty((M, pw.N), dtype=x.dtype, device=x.device)
+    ws, need = _ws(8, M, pw.N, pw.K, r, x.device, workspace)
+    s = pw.struct()
+    check(lib().qlora_linear_fwd_dropout_rng(ctypes.byref(s), _ptr(x), M, _ptr(A), _ptr(B), r,
+                                             float(alpha), float(p), int(seed), int(offset),
+                                             _ptr(y), _ptr(ws),
+                                             need if workspace is None else ws.numel(),
+                                             _stream_ptr()), "qlora_linear_fwd_dropout_rng")
+    return y
+
+
+def linear_bwd_dropout_rng(pw: PackedWeight, x, dy, A, B, alpha: float, p: float, seed: int,
+                           offset: int, need_dx: bool = True, dA=None, dB=None,
+                           accumulate: bool = False, workspace=None, dx=None):
+    """Backward of :func:`linear_fwd_dropout_rng` with the same (p, seed,
+    offset): the library draws the same keep bits again."""
+    torch = _torch()
+    M = dy.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if need_dx and dx is None:
+        dx = torch.empty((M, pw.K), dtype=dy.dtype, device=dy.device)
+    if not need_dx:
+        dx = None
+    if r > 0:
+        if dA is None:
+            dA = torch.empty((r, pw.K), dtype=torch.float32, device=dy.device)
+        if dB is None:
+            dB = torch.empty((pw.N, r), dtype=torch.float32, device=dy.device)
+    ws, need = _ws(9, M, pw.N, pw.K, r, dy.device, workspace)
+    s = pw.struct()
+    check(lib().qlora_linear_bwd_dropout_rng(ctypes.byref(s), _ptr(x), _ptr(dy), M, _ptr(A),
+                                             _ptr(B), r, float(alpha), float(p), int(seed),
+                                             int(offset), _ptr(dx), _ptr(dA), _ptr(dB),
+                                             int(accumulate), _ptr(ws),
+                                             need if workspace is None else ws.numel(),
+                                             _stream_ptr()), "qlora_linear_bwd_dropout_rng")
     return dx, dA, dB
 
 

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <stdexcept>
@@ -50,6 +51,20 @@ qlora::Nf4CodeBins code_bins_arg() {
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// LoRA dropout drawn in the kernels: the Philox key and stream offset, and
+// the threshold t = nearest integer to 65536 p (ties to even; the product
+// is exact), so the realised dropout probability is t / 65536.
+qlora::PhiloxDrop philox_drop(float p, uint64_t seed, uint64_t offset) {
+  qlora::PhiloxDrop d;
+  d.k0 = (uint32_t)seed;
+  d.k1 = (uint32_t)(seed >> 32);
+  d.o0 = (uint32_t)offset;
+  d.o1 = (uint32_t)(offset >> 32);
+  d.t = (uint32_t)std::nearbyint((double)p * 65536.0);
+  return d;
+}
+float realised_p(const qlora::PhiloxDrop& d) { return (float)((double)d.t / 65536.0); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_EHIP; }
 
@@ -148,12 +163,14 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool decode = true,
 }
 
 struct BwdWs {
-  size_t xs_off, gs_off, xst_off, gst_off, part_off, total;
+  size_t xs_off, gs_off, xst_off, gst_off, part_off, mask_off, total;
   size_t gpart;  // fp32 partials of the dX GEMM's schedule (0: none)
 };
 // nf4w: the weight is the NF4 one (the dX GEMM may then take its narrow
-// tile, which sizes the partials differently)
-BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool nf4w = true) {
+// tile, which sizes the partials differently); mask: room for the keep mask
+// [M, K / 8] of a dropout drawn in the kernels
+BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool nf4w = true,
+                 bool mask = false) {
   BwdWs L{};
   if (M == 0) return L;
   size_t off = 0;
@@ -172,6 +189,10 @@ BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool nf4w = true) {
   if (L.gpart > 0) {
     L.part_off = off;
     off = round_up(off + L.gpart, 256);
+  }
+  if (mask && r > 0) {
+    L.mask_off = off;
+    off = round_up(off + (size_t)M * (size_t)(K / 8), 256);
   }
   L.total = off;
   return L;
@@ -199,15 +220,19 @@ struct Wref {
 // f16: the fp16 compute type (x, A, B, y in fp16), NF4 weight, no dropout
 // src (or null): the workspace comes from src(need) once every argument has
 // been validated, instead of from workspace / ws_bytes
+// drop (or null): LoRA dropout drawn in the kernels (keep is then null)
 int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, const uint16_t* B,
              int32_t r, float alpha, const uint8_t* keep, float p, uint16_t* y,
              void* workspace, size_t ws_bytes, void* stream, bool f16 = false,
-             qlora::WorkspaceSource src = nullptr) {
+             qlora::WorkspaceSource src = nullptr, const qlora::PhiloxDrop* drop = nullptr) {
   try {
     int st = QLORA_OK;
     if ((st = check_rank(r)) != QLORA_OK) return st;
-    if (keep && !(p >= 0.0f && p < 1.0f)) return QLORA_EINVAL;
-    if (r == 0) keep = nullptr;
+    if ((keep || drop) && !(p >= 0.0f && p < 1.0f)) return QLORA_EINVAL;
+    if (r == 0) {
+      keep = nullptr;
+      drop = nullptr;
+    }
     if (M < 0) return QLORA_EINVAL;
     const int64_t N = w->N, K = w->K;
     if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
@@ -219,7 +244,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
         (keep && !aligned16(keep)))
       return QLORA_EALIGN;
     // the few-token decode kernel has no dropout: the tiled path then runs
-    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep && !f16, w->nf4());
+    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep && !drop && !f16, w->nf4());
     const size_t ny = (size_t)M * N * 2;
     if (overlap(y, ny, x, (size_t)M * K * 2) || overlap(y, ny, w->data(), w->bytes()) ||
         (r > 0 && (overlap(y, ny, A, (size_t)r * K * 2) || overlap(y, ny, B, (size_t)N * r * 2))) ||
@@ -238,9 +263,11 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
 
     hipStream_t s = as_stream(stream);
     const Nf4Levels L = levels_arg();
-    // inverted dropout: the kept values are scaled by 1 / (1 - p), folded into s
+    // inverted dropout: the kept values are scaled by 1 / (1 - p), folded
+    // into s (a drawn dropout realises p as t / 65536)
+    const float pd = drop ? realised_p(*drop) : p;
     const float scale =
-        r > 0 ? alpha / static_cast<float>(r) / (keep ? 1.0f - p : 1.0f) : 0.0f;
+        r > 0 ? alpha / static_cast<float>(r) / (keep || drop ? 1.0f - pd : 1.0f) : 0.0f;
     if (ws.decode) {
       return hip_status(qlora::launch_decode_fwd(
           w->codes, w->qscale, w->step, x, A, B, r, scale,
@@ -250,7 +277,11 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
     uint16_t* xs = nullptr;
     if (r > 0) {
       xs = at<uint16_t>(workspace, ws.xs_off);
-      const qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), K, 0, keep};
+      qlora::LoraProjJob jx{x, A, xs, at<uint16_t>(workspace, ws.xst_off), K, 0, keep};
+      if (drop) {
+        jx.rng = 1;
+        jx.drop = *drop;
+      }
       if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s, f16))) !=
           QLORA_OK)
         return st;
@@ -263,15 +294,22 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
   }
 }
 
+// drop (or null): LoRA dropout drawn in the kernels (keep is then null): the
+// down-projection draws the keep bits and stores them in the workspace, where
+// the gradient and dX kernels read them as a passed-in mask
 int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, const uint16_t* A,
              const uint16_t* B, int32_t r, float alpha, const uint8_t* keep, float p,
              uint16_t* dx, float* dA, float* dB, int32_t accumulate, void* workspace,
-             size_t ws_bytes, void* stream, bool f16 = false) {
+             size_t ws_bytes, void* stream, bool f16 = false,
+             const qlora::PhiloxDrop* drop = nullptr) {
   try {
     int st = QLORA_OK;
     if ((st = check_rank(r)) != QLORA_OK) return st;
-    if (keep && !(p >= 0.0f && p < 1.0f)) return QLORA_EINVAL;
-    if (r == 0) keep = nullptr;
+    if ((keep || drop) && !(p >= 0.0f && p < 1.0f)) return QLORA_EINVAL;
+    if (r == 0) {
+      keep = nullptr;
+      drop = nullptr;
+    }
     if (M < 0) return QLORA_EINVAL;
     const int64_t N = w->N, K = w->K;
     if ((st = check_sizes(M, N, K)) != QLORA_OK) return st;
@@ -294,7 +332,7 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
                    !aligned16(dB))) ||
         (keep && !aligned16(keep)))
       return QLORA_EALIGN;
-    const BwdWs ws = bwd_layout(M, N, K, r, w->nf4());
+    const BwdWs ws = bwd_layout(M, N, K, r, w->nf4(), drop != nullptr);
     if (ws.total > 0) {
       if (!workspace || ws_bytes < ws.total) return QLORA_EWORKSPACE;
       if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return QLORA_EALIGN;
@@ -321,12 +359,22 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
       uint16_t* xs = at<uint16_t>(workspace, ws.xs_off);
       gs = at<uint16_t>(workspace, ws.gs_off);
       // with dropout, s / (1 - p): dB, dA and dX's adapter term all carry it
-      const float scale = alpha / static_cast<float>(r) / (keep ? 1.0f - p : 1.0f);
+      // (a drawn dropout realises p as t / 65536)
+      const float pd = drop ? realised_p(*drop) : p;
+      const float scale =
+          alpha / static_cast<float>(r) / (keep || drop ? 1.0f - pd : 1.0f);
       // xs = split(s . x~ . A^T), gs = split(s . dy . B) in one launch (x~:
       // x with the dropped values zeroed)
       uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
       uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
-      const qlora::LoraProjJob jx{x, A, xs, xsT, K, 0, keep}, jg{dy, B, gs, gsT, N, 1, nullptr};
+      qlora::LoraProjJob jx{x, A, xs, xsT, K, 0, keep}, jg{dy, B, gs, gsT, N, 1, nullptr};
+      if (drop) {
+        // drawn here once; dA and dX read the stored bytes
+        jx.rng = 1;
+        jx.drop = *drop;
+        jx.keep_out = at<uint8_t>(workspace, ws.mask_off);
+        keep = jx.keep_out;
+      }
       if ((st = hip_status(qlora::launch_lora_proj(jx, &jg, M, r, scale, s, f16))) != QLORA_OK)
         return st;
       // dB [N, r] = dy^T . (xs_hi + xs_lo);  dA [r, K] = (gs_hi + gs_lo)^T . x~
@@ -403,7 +451,53 @@ size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
   if (op == 2) return fwd_layout(M, N, K, r, false, false).total;
   if (op == 4 || op == 6) return fwd_layout(M, N, K, r, false, true).total;
   if (op == 5 || op == 7) return bwd_layout(M, N, K, r).total;
+  if (op == 8) return fwd_layout(M, N, K, r, false, true).total;
+  if (op == 9) return bwd_layout(M, N, K, r, true, true).total;
   return 0;
+}
+
+int qlora_dropout_keep_mask(int64_t M, int64_t K, float p, uint64_t seed, uint64_t offset,
+                            uint8_t* keep, void* stream) {
+  try {
+    if (M < 0 || K <= 0) return QLORA_EINVAL;
+    if (!(p >= 0.0f && p < 1.0f)) return QLORA_EINVAL;
+    if (K % 8) return QLORA_ESHAPE;
+    // the activation the mask belongs to is at most 2 GiB of bf16
+    if (M > 0 && K > kMaxTensorBytes / 2 / M) return QLORA_ESHAPE;
+    if (M == 0) return QLORA_OK;
+    if (!keep) return QLORA_EINVAL;
+    if (!aligned16(keep)) return QLORA_EALIGN;
+    return hip_status(
+        qlora::launch_dropout_mask(philox_drop(p, seed, offset), M, K, keep, as_stream(stream)));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
+int qlora_linear_fwd_dropout_rng(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
+                                 const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                                 float p, uint64_t seed, uint64_t offset, uint16_t* y,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const qlora::PhiloxDrop d = philox_drop(p, seed, offset);
+  return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, p, y, workspace, ws_bytes, stream, false,
+                  nullptr, &d);
+}
+
+int qlora_linear_bwd_dropout_rng(const qlora_nf4_weight* w, const uint16_t* x,
+                                 const uint16_t* dy, int64_t M, const uint16_t* A,
+                                 const uint16_t* B, int32_t r, float alpha, float p,
+                                 uint64_t seed, uint64_t offset, uint16_t* dx, float* dA,
+                                 float* dB, int32_t accumulate, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  const int st = check_weight(w);
+  if (st != QLORA_OK) return st;
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const qlora::PhiloxDrop d = philox_drop(p, seed, offset);
+  return bwd_impl(&wr, x, dy, M, A, B, r, alpha, nullptr, p, dx, dA, dB, accumulate, workspace,
+                  ws_bytes, stream, false, &d);
 }
 
 int qlora_quantize_nf4(const float* w, int64_t n_elems, int32_t blocksize, uint8_t* codes,

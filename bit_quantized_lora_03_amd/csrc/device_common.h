@@ -128,6 +128,53 @@ __device__ __forceinline__ float nf4_block_scale(uint32_t q, float step) {
   return static_cast<float>(q) * step;
 }
 
+// ---------------------------------------------------------------------------
+// Counter-based draws for LoRA dropout: Philox4x32 with ten rounds (Salmon,
+// Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
+// SC 2011).  A round forms the 64-bit products M0 * X0 and M1 * X2 and maps
+// (X0, X1, X2, X3) to (hi1 ^ X1 ^ K0, lo1, hi0 ^ X3 ^ K1, lo0); the key
+// advances by the Weyl constants between rounds.
+//
+// The keep bits of one 8-element chunk of an activation come from one call:
+// counter (chunk index, 0, offset lo, offset hi) -- the chunk index is the
+// byte of the packed [M, K/8] mask, below 2^32 for every tensor the library
+// accepts -- and key (seed lo, seed hi).  Element j takes the 16-bit half
+// j % 2 (low first) of word j / 2 and is kept iff it is >= t.
+// ---------------------------------------------------------------------------
+struct PhiloxDrop {
+  uint32_t k0, k1;    // key: the seed
+  uint32_t o0, o1;    // counter words 2, 3: the stream offset
+  uint32_t t;         // threshold: nearest integer to 65536 p
+};
+
+__device__ __forceinline__ u32x4_t philox4x32_10(u32x4_t x, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x[2];
+    x = u32x4_t{(uint32_t)(p1 >> 32) ^ x[1] ^ k0, (uint32_t)p1,
+                (uint32_t)(p0 >> 32) ^ x[3] ^ k1, (uint32_t)p0};
+  }
+  return x;
+}
+
+// The keep byte of mask byte `chunk` (bit j set where element 8 chunk + j
+// of the flattened [M, K] activation is kept).
+__device__ __forceinline__ uint32_t philox_keep_byte(const PhiloxDrop& d, uint32_t chunk) {
+  const u32x4_t w = philox4x32_10(u32x4_t{chunk, 0u, d.o0, d.o1}, d.k0, d.k1);
+  uint32_t kb = 0;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    kb |= ((w[h] & 0xFFFFu) >= d.t ? 1u : 0u) << (2 * h);
+    kb |= ((w[h] >> 16) >= d.t ? 1u : 0u) << (2 * h + 1);
+  }
+  return kb;
+}
+
 // Raw buffer access (gfx9 descriptor: untyped dwords, DATA_FORMAT 32).
 // Loads at byte offsets at or past `bytes` return zero, which the GEMMs use
 // for rows beyond the tensor instead of branching.

@@ -49,10 +49,19 @@ struct LoraProjJob {
   // LoRA dropout on X (or null): [M, Kred / 8] bytes, bit k mod 8 of byte
   // (m, k / 8) set where X[m][k] is kept; dropped values count as zero
   const uint8_t* keep = nullptr;
+  // LoRA dropout drawn in the kernel instead (rng != 0): the keep byte of
+  // chunk (m, k / 8) is philox_keep_byte(drop, m Kred / 8 + k / 8); where
+  // keep_out is given, the drawn bytes are also stored there ([M, Kred / 8])
+  int rng = 0;
+  PhiloxDrop drop{};
+  uint8_t* keep_out = nullptr;
 };
 // one job, or two in one launch (j1 non-null)
 // f16: the fp16 compute type (operands and the hi/lo pairs in fp16; no
 // keep-mask), else bf16.
+// the packed keep mask [M, K / 8] that `drop` draws (philox_keep_byte)
+hipError_t launch_dropout_mask(const PhiloxDrop& drop, int64_t M, int64_t K, uint8_t* keep,
+                               hipStream_t s);
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                             float scale, hipStream_t s, bool f16 = false);
 // lora_grad: C (+)= sum_m G[m][g] * (ST[j][m] + ST[r + j][m]), C [ldg, r]

@@ -113,6 +113,13 @@ __device__ __forceinline__ LoraProjJob uniform_job(const LoraProjJob& j) {
   u.Kred = (int64_t)uniform64((uint64_t)j.Kred);
   u.kmajor = __builtin_amdgcn_readfirstlane(j.kmajor);
   u.keep = uniform_ptr(j.keep);
+  u.rng = __builtin_amdgcn_readfirstlane(j.rng);
+  u.drop.k0 = __builtin_amdgcn_readfirstlane(j.drop.k0);
+  u.drop.k1 = __builtin_amdgcn_readfirstlane(j.drop.k1);
+  u.drop.o0 = __builtin_amdgcn_readfirstlane(j.drop.o0);
+  u.drop.o1 = __builtin_amdgcn_readfirstlane(j.drop.o1);
+  u.drop.t = __builtin_amdgcn_readfirstlane(j.drop.t);
+  u.keep_out = uniform_ptr(j.keep_out);
   return u;
 }
 __device__ __forceinline__ LoraGradJob uniform_job(const LoraGradJob& j) {
@@ -169,8 +176,10 @@ __device__ __forceinline__ void put_split(const LoraProjJob& J, int64_t M, int r
 // group.  B's rows (8 rank columns of one k per 16 bytes) go through the
 // wave's slab and come back transposed.
 // ---------------------------------------------------------------------------
-// DROP: the jobs may carry a keep-mask on X (LoRA dropout; see keep8).
-template <int JT, bool DROP, class DT>
+// DROP: LoRA dropout on X (see keep8): 0 none, 1 the jobs may carry a
+// keep-mask, 2 a job may draw its keep bits (rng) -- the blocks of the first
+// rank chunk then also store them to keep_out.
+template <int JT, int DROP, class DT>
 __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
                                                              int64_t blocks0, int64_t M, int r,
                                                              float scale) {
@@ -238,17 +247,30 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
       const uint32_t past = u < cnt ? 0u : kOff;
       const uint32_t k0 = (uint32_t)(32 * (wave + kWaves * u));
       R.x[bb] = ldb(xres, xoff | past, 2 * k0);
-      if constexpr (DROP) R.kb[bb] = ldb8(kp.res, koff | past, k0 / 8) | kp.all;
+      if constexpr (DROP == 1) R.kb[bb] = ldb8(kp.res, koff | past, k0 / 8) | kp.all;
 #pragma unroll
       for (int q = 0; q < JT; ++q)
         R.y[bb][q] = ldb(yres, yoff[q] | past, kmajor ? 2 * k0 * (uint32_t)r : 2 * k0);
     }
   };
+  // drawn keep bytes: the first rank chunk's blocks store those of real
+  // tokens and steps
+  const bool store_keep = DROP == 2 && J.keep_out != nullptr && jc == 0 && m < M;
   // steps past the wave's count carry zero operands and add nothing
-  auto compute = [&](const Batch& R) {
+  auto compute = [&](const Batch& R, int64_t u0) {
 #pragma unroll
     for (int bb = 0; bb < BS; ++bb) {
-      const u32x4_t xv = DROP ? keep8(R.x[bb], R.kb[bb]) : R.x[bb];
+      uint32_t kb = 0xFFu;
+      if constexpr (DROP == 1) kb = R.kb[bb];
+      if constexpr (DROP == 2) {
+        if (J.rng) {
+          const int64_t u = u0 + bb;
+          const uint32_t chunk = koff + (uint32_t)(4 * (wave + kWaves * u));
+          kb = philox_keep_byte(J.drop, chunk);
+          if (store_keep && u < cnt) J.keep_out[chunk] = (uint8_t)kb;
+        }
+      }
+      const u32x4_t xv = DROP ? keep8(R.x[bb], kb) : R.x[bb];
       if (!kmajor) {
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) acc[jt] = DT::mfma16(xv, R.y[bb][jt], acc[jt]);
@@ -269,10 +291,10 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   if (cnt > 0) load(0, R0);
   for (int64_t u0 = 0; u0 < cnt; u0 += 2 * BS) {
     if (u0 + BS < cnt) load(u0 + BS, R1);
-    compute(R0);
+    compute(R0, u0);
     if (u0 + BS < cnt) {
       if (u0 + 2 * BS < cnt) load(u0 + 2 * BS, R0);
-      compute(R1);
+      compute(R1, u0 + BS);
     }
   }
 
@@ -312,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
 constexpr int kSmallR = 8;     // rank columns per block
 constexpr int kSmallRed = 65;  // LDS row of a thread's (up to) 64 sums (+1: no bank conflicts)
 
-template <bool DROP, class DT, int TT>
+template <int DROP, class DT, int TT>
 __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, LoraProjJob j1,
                                                               int64_t blocks0, int64_t M, int r,
                                                               float scale) {
@@ -365,14 +387,17 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
       P.x[i] = ldb(xres, (xoff[i] + 16u * pc) | past, 0);
-      if constexpr (DROP) P.kb[i] = ldb8(kp.res, (koff[i] + pc) | past, 0) | kp.all;
+      if constexpr (DROP == 1) P.kb[i] = ldb8(kp.res, (koff[i] + pc) | past, 0) | kp.all;
     }
 #pragma unroll
     for (int q = 0; q < kSmallR; ++q)
       P.y[q] = ldb(yres, (ybase[q] + (kmajor ? 16u * (uint32_t)r * pc : 16u * pc)) | past, 0);
   };
 
-  auto compute = [&](const Piece& P) {
+  // drawn keep bytes: the first rank group's blocks store those of real
+  // tokens and pieces
+  const bool store_keep = DROP == 2 && J.keep_out != nullptr && jc == 0;
+  auto compute = [&](const Piece& P, int64_t u) {
     u32x4_t yp[kSmallR];  // column q's (k, k + 1) pairs
 #pragma unroll
     for (int q = 0; q < kSmallR; ++q) {
@@ -388,7 +413,16 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
     }
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-      const u32x4_t xv = DROP ? keep8(P.x[i], P.kb[i]) : P.x[i];
+      uint32_t kb = 0xFFu;
+      if constexpr (DROP == 1) kb = P.kb[i];
+      if constexpr (DROP == 2) {
+        if (J.rng) {
+          const uint32_t chunk = koff[i] + (uint32_t)(t + 256 * u);
+          kb = philox_keep_byte(J.drop, chunk);
+          if (store_keep && u < cnt && m0 + i < M) J.keep_out[chunk] = (uint8_t)kb;
+        }
+      }
+      const u32x4_t xv = DROP ? keep8(P.x[i], kb) : P.x[i];
 #pragma unroll
       for (int q = 0; q < kSmallR; ++q)
 #pragma unroll
@@ -406,10 +440,10 @@ __global__ __launch_bounds__(256) void lora_proj_small_kernel(LoraProjJob j0, Lo
   for (int64_t u = 0; u < cnt; u += 2) {
     load(u + 1, P1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(P0);
+    compute(P0, u);
     load(u + 2, P0);
     __builtin_amdgcn_sched_barrier(0);
-    compute(P1);
+    compute(P1, u + 1);
   }
 
 #pragma unroll
@@ -440,7 +474,7 @@ static bool proj_small(int64_t M, int r) { return M * r <= 16384; }
 
 static int proj_jt(int r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
 
-template <bool DROP, class DT>
+template <int DROP, class DT>
 static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                               float scale, hipStream_t s) {
   if (proj_small(M, r)) {
@@ -482,9 +516,26 @@ static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int6
 
 hipError_t launch_lora_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                             float scale, hipStream_t s, bool f16) {
-  if (f16) return launch_proj<false, F16T>(j0, j1, M, r, scale, s);  // no dropout in fp16
-  if (j0.keep || (j1 && j1->keep)) return launch_proj<true, Bf16T>(j0, j1, M, r, scale, s);
-  return launch_proj<false, Bf16T>(j0, j1, M, r, scale, s);
+  if (f16) return launch_proj<0, F16T>(j0, j1, M, r, scale, s);  // no dropout in fp16
+  if (j0.rng || (j1 && j1->rng)) return launch_proj<2, Bf16T>(j0, j1, M, r, scale, s);
+  if (j0.keep || (j1 && j1->keep)) return launch_proj<1, Bf16T>(j0, j1, M, r, scale, s);
+  return launch_proj<0, Bf16T>(j0, j1, M, r, scale, s);
+}
+
+// The packed keep mask [M, K / 8] of a drawn dropout: one byte per thread.
+__global__ __launch_bounds__(256) void dropout_mask_kernel(PhiloxDrop drop, int64_t nbytes,
+                                                           uint8_t* keep) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b < nbytes) keep[b] = (uint8_t)philox_keep_byte(drop, (uint32_t)b);
+}
+
+hipError_t launch_dropout_mask(const PhiloxDrop& drop, int64_t M, int64_t K, uint8_t* keep,
+                               hipStream_t s) {
+  const int64_t nbytes = M * (K / 8);
+  if (nbytes == 0) return hipSuccess;
+  hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)((nbytes + 255) / 256)), dim3(256), 0,
+                     s, drop, nbytes, keep);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

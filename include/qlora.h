@@ -239,6 +239,46 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, const
                              float* dB, int32_t accumulate, void* workspace, size_t ws_bytes,
                              void* stream);
 
+/* LoRA dropout with the keep bits drawn by the library, from a
+ * counter-based generator, instead of passed in.  [QLoRA -- Module 12.4,
+ * "Hugging Face + BitsAndBytes"] sets lora_dropout (0.05); the generator
+ * is Philox4x32 with ten rounds (Salmon, Moraes, Dror and Shaw, "Parallel
+ * Random Numbers: As Easy as 1, 2, 3", SC 2011).
+ *   The keep bits of elements 8c .. 8c+7 of the flattened [M, K] x (mask
+ *   byte c = m*(K/8) + k/8) come from one Philox call with counter
+ *   (c, 0, offset lo, offset hi) and key (seed lo, seed hi): element 8c+j
+ *   takes the 16-bit half j%2 (low first) of output word j/2, u, and is
+ *   kept iff u >= t, t = nearest integer to 65536*p (ties to even).  The
+ *   realised dropout probability is t/65536 (0.05 -> 0.0500031), and the
+ *   inverted scaling uses it: the adapter sees x~ = x*keep/(1 - t/65536).
+ *   The same (seed, offset) in the forward and the backward of a step
+ *   draws the same bits (the backward draws them again; nothing is stored
+ *   between the calls); use a new offset (or seed) for every step and
+ *   layer.  0 <= p < 1 (EINVAL otherwise).
+ *   qlora_dropout_keep_mask writes the bits the layer draws, in the
+ *     packed layout of qlora_linear_fwd_dropout's keep argument ([M, K/8]
+ *     bytes, 16-byte aligned; K a multiple of 8 and M*K*2 at most 2 GiB,
+ *     ESHAPE), so qlora_linear_fwd_dropout with that mask and p =
+ *     t/65536 computes the same layer.
+ *   qlora_linear_fwd_dropout_rng / qlora_linear_bwd_dropout_rng: the
+ *     layer of qlora_linear_fwd_dropout / qlora_linear_bwd_dropout with
+ *     the drawn bits; other arguments, rounding, errors and size limits
+ *     alike; the forward always runs the tiled GEMMs; workspace
+ *     qlora_linear_workspace_bytes(8 (forward) or 9 (backward), ...); the
+ *     backward keeps the drawn mask in its workspace.                     */
+int qlora_dropout_keep_mask(int64_t M, int64_t K, float p, uint64_t seed, uint64_t offset,
+                            uint8_t* keep, void* stream);
+int qlora_linear_fwd_dropout_rng(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
+                                 const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                                 float p, uint64_t seed, uint64_t offset, uint16_t* y,
+                                 void* workspace, size_t ws_bytes, void* stream);
+int qlora_linear_bwd_dropout_rng(const qlora_nf4_weight* w, const uint16_t* x,
+                                 const uint16_t* dy, int64_t M, const uint16_t* A,
+                                 const uint16_t* B, int32_t r, float alpha, float p,
+                                 uint64_t seed, uint64_t offset, uint16_t* dx, float* dA,
+                                 float* dB, int32_t accumulate, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
 /* The same layer with an unquantised bf16 base weight W [N, K] (row-major,
  * out x in), through the same kernels with the dequantisation left out:
  * the "LoRA on a 16-bit base" that QLoRA is compared with.
@@ -290,9 +330,10 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const uint16_t* x, int64
 
 /* Workspace bytes for op 0 (forward) or 1 (backward) of the NF4 layer,
  * op 2 (forward) or 3 (backward) of the bf16-weight layer, op 4 (forward)
- * or 5 (backward) of the NF4 layer with dropout, or op 6 (forward) or 7
- * (backward) of the fp16 compute type, at the given shape; 0 for an
- * invalid shape.  Host-only; never touches the GPU.                        */
+ * or 5 (backward) of the NF4 layer with dropout, op 6 (forward) or 7
+ * (backward) of the fp16 compute type, or op 8 (forward) or 9 (backward)
+ * of the NF4 layer with dropout drawn by the library, at the given shape;
+ * 0 for an invalid shape.  Host-only; never touches the GPU.               */
 size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
                                     int32_t r);
 

@@ -78,7 +78,7 @@ def test_workspace_sizes():
     assert ws(0, 16, 4096, 100, 16) == 0          # K % 64
     assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
     assert ws(0, 16, 4096, 4096, 264) == 0        # r > 256
-    assert ws(8, 16, 4096, 4096, 16) == 0         # bad op
+    assert ws(10, 16, 4096, 4096, 16) == 0        # bad op
     # fp16 compute type and dropout: the tiled forward at every M (never the
     # few-token path), both on the NF4 weight, so laid out alike
     assert ws(6, 16, 8192, 8192, 64) == ws(4, 16, 8192, 8192, 64)
@@ -391,3 +391,37 @@ def test_noalloc_forward_validation():
     assert call(x=P3 + 2) == -3
     assert call(y=P3) == -1                                   # y aliases x
     assert call(M=0) == 0                                     # empty: no-op
+
+
+def test_drawn_dropout_validation():
+    L = q.lib()
+    w = _weight(256, 256)
+    f = L.qlora_dropout_keep_mask
+    assert f(16, 256, 0.05, 1, 2, None, None) == -1               # no output
+    assert f(16, 256, 1.0, 1, 2, P3, None) == -1                  # p = 1
+    assert f(16, 256, float("nan"), 1, 2, P3, None) == -1
+    assert f(-1, 256, 0.05, 1, 2, P3, None) == -1
+    assert f(16, 252, 0.05, 1, 2, P3, None) == -2                 # K % 8
+    assert f(16, 256, 0.05, 1, 2, P3 + 4, None) == -3
+    assert f(0, 256, 0.05, 1, 2, None, None) == 0                 # empty: no-op
+    assert f(1 << 20, 1 << 11, 0.05, 1, 2, P3, None) == -2        # x above 2 GiB
+    need = q.workspace_bytes(8, 16, 256, 256, 8)
+    assert need == q.workspace_bytes(4, 16, 256, 256, 8)
+    fwd = lambda **kw: L.qlora_linear_fwd_dropout_rng(
+        ctypes.byref(w), kw.get("x", P3), kw.get("M", 16), P4, P4 + 8192, kw.get("r", 8), 16.0,
+        kw.get("p", 0.05), 7, 9, kw.get("y", P4 + 65536), P4 + (1 << 19), kw.get("wsb", need),
+        None)
+    assert fwd(p=1.0) == -1
+    assert fwd(p=-0.5) == -1
+    assert fwd(r=12) == -2
+    assert fwd(wsb=need - 1) == -5
+    assert fwd(y=P3) == -1
+    assert fwd(M=0) == 0
+    # the backward keeps the drawn mask [M, K/8] in its workspace
+    nb = q.workspace_bytes(9, 16, 256, 256, 8)
+    assert nb >= q.workspace_bytes(5, 16, 256, 256, 8) + 16 * 256 // 8
+    bwd = lambda **kw: L.qlora_linear_bwd_dropout_rng(
+        ctypes.byref(w), P3, P3 + 16384, 16, P4, P4 + 8192, 8, 16.0, kw.get("p", 0.05), 7, 9,
+        P4 + 65536, P4 + 131072, P4 + 196608, 0, P4 + (1 << 19), kw.get("wsb", nb), None)
+    assert bwd(p=1.5) == -1
+    assert bwd(wsb=nb - 1) == -5
