@@ -213,29 +213,49 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
         tab_w[(2 * q) * 128] = (uint16_t)pk;
         tab_w[(2 * q + 1) * 128] = (uint16_t)(pk >> 16);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      // the 8 table reads of step j (weights 8 j .. 8 j + 7 of the block)
+      auto lookup = [&](int j, uint32_t (&h)[8]) {
         const uint32_t v = (j < 4 ? c0 : c1)[j & 3];
+        // byte i of ev holds code 2i, of od code 2i + 1, each tagged with
+        // 16 * wave; the address perm takes the byte straight from them
         const uint32_t ev = (v & 0x0F0F0F0Fu) | wtag;
         const uint32_t od = ((v >> 4) & 0x0F0F0F0Fu) | wtag;
-        const uint32_t q4[2] = {perm(od, ev, 0x05010400u), perm(od, ev, 0x07030602u)};
-        uint32_t h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           // byte 0: the lane's offset, byte 1: code + 16 wave -> LDS address
-          const uint32_t addr = perm(q4[e >> 2], lane4, 0x0C0C0000u | ((4u + (e & 3)) << 8));
+          const uint32_t addr =
+              perm((e & 1) ? od : ev, lane4, 0x0C0C0000u | ((4u + (e >> 1)) << 8));
           h[e] = *reinterpret_cast<const uint16_t*>(lds + addr);
         }
+      };
+      // Software-pipelined: step j + 1's reads are issued before step j's
+      // values are packed, so each step's LDS latency runs behind the
+      // previous step's packing and MFMA instead of stalling the wave.
+      // (x operands read from LDS are issued with their step's lookups, so
+      // waiting for a step's operands never waits for the next step's reads)
+      uint32_t h[2][8];
+      u32x4_t xv[2];
+      lookup(0, h[0]);
+      xv[0] = xop(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j + 1 < 8) {
+          lookup(j + 1, h[(j + 1) & 1]);
+          xv[(j + 1) & 1] = xop(j + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         u32x4_t a;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = h[2 * q] | (h[2 * q + 1] << 16);
-        acc = mfma32x32x16(a, xop(j), acc);
+        for (int q = 0; q < 4; ++q) a[q] = h[j & 1][2 * q] | (h[j & 1][2 * q + 1] << 16);
+        acc = mfma32x32x16(a, xv[j & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    // Issue order.  The prologue loads x (of chunks 0 and 1, or -- with x
-    // in LDS -- every piece of x the wave will read), then the DMA and
-    // scales of chunks 0 .. NSTAGE - 2; iteration ch loads x of chunk
+    // Issue order.  The prologue issues, in rounds c = 0 .. NSTAGE - 2,
+    // chunk c's DMA and scales, followed in round 0 by x of chunk 0 (or --
+    // with x in LDS -- every piece of x the wave will read) and in round 1
+    // by x of chunk 1; iteration ch loads x of chunk
     // ch + 2 (not with x in LDS), then issues the DMA of chunk
     // ch + NSTAGE - 1 and its scales, decodes chunk ch and at its end waits
     // for chunk ch + 1's DMA.  Loads complete in order, so a wait for x of
@@ -247,8 +267,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // outstanding", W being the number of operations issued after chunk
     // ch + 1's DMA; with kOps operations per iteration that is
     // 2 + kOps (NSTAGE - 2) in the steady state (it was issued in iteration
-    // ch + 2 - NSTAGE) and, with x in registers, 26 + 8 ch while the DMA
-    // came from the prologue.  Waits are immediates, so W is a template
+    // ch + 2 - NSTAGE) and, with x in registers, 34, 34 and 42 in the first
+    // three iterations (x of chunk 1 follows chunk 1's DMA in the
+    // prologue).  Waits are immediates, so W is a template
     // argument: the first group of iterations gets its own, later groups the
     // steady one, and a short reduction (fewer chunks than one group) the
     // smallest, which waits at least as long as needed.
@@ -274,33 +295,42 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     constexpr int kXq = 4;  // pieces per lane (the x budget bounds M K / 64 by 256)
     u32x4_t xv[XL ? kXq : 1];
     uint32_t xdst[XL ? kXq : 1];
-    if constexpr (XL) {
-      // 32-bit index math, every offset computed before the select, so the
-      // selects stay selects (a branch around the loads would make the
-      // compiler wait for each load before the next)
-      const uint32_t nch32 = (uint32_t)nch, m32 = (uint32_t)M, nblk32 = (uint32_t)nblk;
-      const uint32_t xrow_bytes = (uint32_t)(2 * K), xrb32 = (uint32_t)xrb;
-#pragma unroll
-      for (int q = 0; q < kXq; ++q) {
-        const uint32_t i = (uint32_t)(lane + 64 * q);
-        const uint32_t pc = i & 15u, rest = i >> 4;
-        const uint32_t tk = rest / nch32, c = rest - tk * nch32;
-        const uint32_t b = 16u * c + 2u * (uint32_t)wave + (pc >> 3);
-        const uint32_t col = 128u * b + 16u * (pc & 7u);
-        const bool ok = tk < m32 && b < nblk32;
-        const uint32_t src = tk * xrow_bytes + col, dst = tk * xrb32 + col;
-        xv[q] = buffer_load16(xres, ok ? src : 0x80000000u);
-        xdst[q] = ok ? dst : 0xFFFFFFFFu;
-      }
-    } else {
-      load_xc(0, X[0]);
-      load_xc(cl(1), X[1]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    // The prologue's loads go out in rounds, one chunk per wave per round
+    // with a barrier (issue order only: no memory is waited for) between
+    // rounds, so every wave's chunk 0 reaches the memory pipeline before
+    // any wave's chunk 1: issued wave by wave instead, the last waves'
+    // first chunk queued behind the first waves' whole prefetch and landed
+    // several microseconds later.  Round c: chunk c's DMA and scales, then
+    // x (chunks 0 and 1 in registers, or every staged piece in round 0).
 #pragma unroll
     for (int c = 0; c < NSTAGE - 1; ++c) {
       dma_codes(ring + c * kStageU4, cl(c));
       load_scale(cl(c), Sc[c]);
+      if constexpr (XL) {
+        if (c == 0) {
+          // 32-bit index math, every offset computed before the select, so
+          // the selects stay selects (a branch around the loads would make
+          // the compiler wait for each load before the next)
+          const uint32_t nch32 = (uint32_t)nch, m32 = (uint32_t)M, nblk32 = (uint32_t)nblk;
+          const uint32_t xrow_bytes = (uint32_t)(2 * K), xrb32 = (uint32_t)xrb;
+#pragma unroll
+          for (int q = 0; q < kXq; ++q) {
+            const uint32_t i = (uint32_t)(lane + 64 * q);
+            const uint32_t pc = i & 15u, rest = i >> 4;
+            const uint32_t tk = rest / nch32, cc = rest - tk * nch32;
+            const uint32_t b = 16u * cc + 2u * (uint32_t)wave + (pc >> 3);
+            const uint32_t col = 128u * b + 16u * (pc & 7u);
+            const bool ok = tk < m32 && b < nblk32;
+            const uint32_t src = tk * xrow_bytes + col, dst = tk * xrb32 + col;
+            xv[q] = buffer_load16(xres, ok ? src : 0x80000000u);
+            xdst[q] = ok ? dst : 0xFFFFFFFFu;
+          }
+        }
+      } else {
+        if (c < 2) load_xc(cl(c), X[c]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (XL) {
@@ -310,8 +340,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
         if (xdst[q] != 0xFFFFFFFFu) *reinterpret_cast<u32x4_t*>(xl + xdst[q]) = xv[q];
       if (lane < 8) *reinterpret_cast<u32x4_t*>(xl + M * xrb + 128 * wave + 16 * lane) = zero;
     }
-    // chunk 0's DMA: followed by its scales and NSTAGE - 2 DMA + scale pairs
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 + 4 * (NSTAGE - 2), 0));
+    // chunk 0's DMA: followed by its scales, the x loads (XL: kXq, else two
+    // chunks of 8) and NSTAGE - 2 DMA + scale pairs
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 + (XL ? kXq : 16) + 4 * (NSTAGE - 2), 0));
 
     // x operand j of chunk ch from LDS: token lr's 16 bytes at k = 64 b + 8 j
     auto x_lds = [&](int64_t ch) {
@@ -353,8 +384,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     using P3 = std::integral_constant<int, 3>;
     using P4 = std::integral_constant<int, 4>;
     using P5 = std::integral_constant<int, 5>;
-    // with x in LDS every iteration's count is the steady one
-    using W0 = std::integral_constant<int, XL ? kWaitSteady : 26>;
+    // with x in LDS every iteration's count is the steady one; with x in
+    // registers, chunk 1's x follows chunk 1's DMA in the prologue, so the
+    // first wait also counts it
+    using W0 = std::integral_constant<int, XL ? kWaitSteady : 34>;
     using W1 = std::integral_constant<int, XL ? kWaitSteady : 34>;
     using W2 = std::integral_constant<int, XL ? kWaitSteady : 42>;
     using WS = std::integral_constant<int, kWaitSteady>;
