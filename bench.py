@@ -443,6 +443,9 @@ def main():
                     help="skip the gate measurements of the 7B MLP and decode workloads")
     ap.add_argument("--gates-only", action="store_true",
                     help="time only the gate workloads (for profiling them on their own)")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="after the timed steps, run only the base-only fused-GEMM calls "
+                         "(for profiling the roofline kernels)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -618,11 +621,15 @@ def main():
 
     reps = max(10, args.steps)
     ops = {}
-    if "quant" in kind:
+    if args.roofline_only:
+        args.no_gates = True
+        args.no_cpu_baseline = True
+    if "quant" in kind and not args.roofline_only:
         ops["quantize_ms"] = timed(lambda i: quantize(), reps)
-    ops["fwd_ms"] = timed(lambda i: fwd(i % rot), reps)
-    if "bwd" in kind:
-        ops["bwd_ms"] = timed(lambda i: bwd(), reps)
+    if not args.roofline_only:
+        ops["fwd_ms"] = timed(lambda i: fwd(i % rot), reps)
+        if "bwd" in kind:
+            ops["bwd_ms"] = timed(lambda i: bwd(), reps)
     # (These run before the base-only roofline calls below, which stay the
     # last dispatches of their kernels for the profiles.)
     # ---- the same layer on an unquantised bf16 weight (same kernels, no
@@ -630,7 +637,7 @@ def main():
     # base.  Training quantises once, so the ratio is over fwd + bwd only.
     # The same-shape torch bf16 GEMM (hipBLASLt) is context, not a target.
     unq = None
-    if kind != "fwd":
+    if kind != "fwd" and not args.roofline_only:
         Wq = to_dev(_wbits(L.w))
 
         need16 = max(q.workspace_bytes(2, M, N, K, r), q.workspace_bytes(3, M, N, K, r), 256)
@@ -662,7 +669,7 @@ def main():
     # ---- the same fwd + bwd with LoRA dropout (p = 0.05, as the pages
     # configure) on the adapter's input; the keep mask is a resident input ----
     drop = None
-    if kind != "fwd" and r:
+    if kind != "fwd" and r and not args.roofline_only:
         from bit_quantized_lora_03_amd import workloads as _wl
         p_drop = 0.05
         keep_d = to_dev(_wl.pack_keep(_wl.keep_mask(L.seed, 60, M, K, p_drop)))
@@ -713,7 +720,7 @@ def main():
     # ---- the fp16 compute-type variant of the same fwd + bwd (same packed
     # weight; x, A, B, dy in fp16), each timed right after the bf16 call ----
     f16 = None
-    if kind != "fwd":
+    if kind != "fwd" and not args.roofline_only:
         def h16(t):
             return t.view(torch.bfloat16).float().half().view(torch.int16)
         x16, dy16 = h16(x_d), h16(dy_d)
@@ -744,7 +751,7 @@ def main():
     # ---- adapter merge for export (not part of the step): W_m = W + s.B.A,
     # fp32 and bf16 exports, from the NF4 base and from the fp32 original ----
     merge = None
-    if r:
+    if r and not args.roofline_only:
         mf = torch.empty((N, K), dtype=torch.float32, device=dev)
         mb = torch.empty((N, K), dtype=torch.int16, device=dev)
         wt0 = weights[0][3]

@@ -118,7 +118,7 @@ int check_adapter_sizes(int64_t M, int64_t N, int64_t K, int32_t r) {
 
 // ---- workspace layout --------------------------------------------------
 struct FwdWs {
-  size_t xs_off, xst_off, part_off, total;
+  size_t xs_off, xst_off, part_off, ppart_off, total;
   int dsplits;   // k splits of the decode path
   size_t gpart;  // fp32 partials of the fused GEMM's schedule (0: none)
   bool decode;   // few tokens: split-K decode path
@@ -152,6 +152,12 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool decode = true,
     L.xs_off = 0;
     L.xst_off = round_up((size_t)M * 2 * r * sizeof(uint16_t), 256);
     off = round_up(L.xst_off + (size_t)pad32(M) * 2 * r * sizeof(uint16_t), 256);
+    // fp32 partials of a split down-projection
+    const size_t pp = qlora::lora_proj_partial_bytes(qlora::lora_proj_plan(M, r, K, 0), 0, M, r);
+    if (pp > 0) {
+      L.ppart_off = off;
+      off = round_up(off + pp, 256);
+    }
   }
   L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, N, K, nf4w), M, N);
   if (L.gpart > 0) {
@@ -163,7 +169,7 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool decode = true,
 }
 
 struct BwdWs {
-  size_t xs_off, gs_off, xst_off, gst_off, part_off, mask_off, total;
+  size_t xs_off, gs_off, xst_off, gst_off, part_off, mask_off, ppx_off, ppg_off, total;
   size_t gpart;  // fp32 partials of the dX GEMM's schedule (0: none)
 };
 // nf4w: the weight is the NF4 one (the dX GEMM may then take its narrow
@@ -184,6 +190,18 @@ BwdWs bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool nf4w = true,
     L.xst_off = round_up(L.gs_off + pair, 256);
     L.gst_off = round_up(L.xst_off + pairT, 256);
     off = round_up(L.gst_off + pairT, 256);
+    // fp32 partials of the split down-projections (x . A^T, dy . B)
+    const qlora::ProjPlan pp = qlora::lora_proj_plan(M, r, K, N);
+    const size_t px = qlora::lora_proj_partial_bytes(pp, 0, M, r);
+    const size_t pg = qlora::lora_proj_partial_bytes(pp, 1, M, r);
+    if (px > 0) {
+      L.ppx_off = off;
+      off = round_up(off + px, 256);
+    }
+    if (pg > 0) {
+      L.ppg_off = off;
+      off = round_up(off + pg, 256);
+    }
   }
   L.gpart = qlora::gemm_partial_bytes(qlora::gemm_config(M, K, N, nf4w), M, K);
   if (L.gpart > 0) {
@@ -282,6 +300,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
         jx.rng = 1;
         jx.drop = *drop;
       }
+      if (ws.ppart_off) jx.part = at<float>(workspace, ws.ppart_off);
       if ((st = hip_status(qlora::launch_lora_proj(jx, nullptr, M, r, scale, s, f16))) !=
           QLORA_OK)
         return st;
@@ -368,6 +387,8 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
       uint16_t* xsT = at<uint16_t>(workspace, ws.xst_off);
       uint16_t* gsT = at<uint16_t>(workspace, ws.gst_off);
       qlora::LoraProjJob jx{x, A, xs, xsT, K, 0, keep}, jg{dy, B, gs, gsT, N, 1, nullptr};
+      if (ws.ppx_off) jx.part = at<float>(workspace, ws.ppx_off);
+      if (ws.ppg_off) jg.part = at<float>(workspace, ws.ppg_off);
       if (drop) {
         // drawn here once; dA and dX read the stored bytes
         jx.rng = 1;

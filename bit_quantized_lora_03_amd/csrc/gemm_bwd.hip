@@ -40,11 +40,16 @@ namespace {
 constexpr int TILE = 256;
 constexpr int RT = 64;  // reduction rows per stage
 constexpr int ROW_CHUNKS = RT / 8;
-// W slab row stride in LDS, bytes: 512 of data plus 48 of pad.  140 dwords
-// = 12 mod 64 banks, so the 16 rows one store instruction writes per LDS
-// cycle start 12 banks apart (all 64 banks once), and the 4 rows one
-// transpose read touches (8 banks each) are disjoint.
-constexpr int WROW = 560;
+// W slab row stride in LDS, bytes: 512 of data plus 64 of pad (144 dwords,
+// 16 mod 64 banks), with the 16-byte pieces of row r XOR-swizzled by
+// (r / 4) mod 4 within each 64-byte window (slab_swz).  A 16-byte store
+// serves 16 lanes (16 rows at one column) per LDS cycle and a transpose
+// read 32 lanes (4 rows x 64 contiguous bytes); with this layout both touch
+// each of the 64 banks once.  (A plain 12-mod-64 stride, conflict-free for
+// the stores, made the four rows of a transpose read overlap by 4 banks:
+// about half the dX kernel's LDS cycles were bank conflicts.)
+constexpr int WROW = 576;
+__device__ __forceinline__ int slab_swz(int row) { return ((row >> 2) & 3) << 4; }
 
 struct DxParams {
   const uint8_t* codes;   // NF4 weight (WF = kWeightNf4)
@@ -97,8 +102,8 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 // MS = 2: a 128 (k) x 128 (m) tile for small-M shapes) gives each thread
 // half an NF4 block -- the 32 values of its slab row at k quarter kq -- so
 // a thread decodes half as many weights per MFMA; each wave then owns
-// 64 (k) x 64 (m).  The slab rows shrink to 256 bytes + 48 of pad, 76
-// dwords = 12 mod 64 banks, the same bank pattern as the wide slab.
+// 64 (k) x 64 (m).  The slab rows shrink to 256 bytes + 64 of pad, 80
+// dwords = 16 mod 64 banks, swizzled like the wide slab.
 template <int MS, int WF, bool DROP, class DT, int KW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
@@ -107,7 +112,7 @@ void dx_gemm_kernel(DxParams p) {
   static_assert(KW == TILE || (HALF && NF4), "half blocks per thread need the NF4 weight");
   constexpr int NI = KW / 64;         // 32-column (k) MFMA tiles per wave
   constexpr int NCH = KW / 32;        // 8-value chunks each thread decodes
-  constexpr int WR = HALF ? 304 : WROW;  // W slab row stride, bytes
+  constexpr int WR = HALF ? 320 : WROW;  // W slab row stride, bytes
   constexpr int WST = RT * WR;           // bytes per W stage
   constexpr int TM = 64 * MS;   // token rows of the block tile
   constexpr int XR = TM / 32;   // dy rows staged per thread
@@ -213,22 +218,27 @@ void dx_gemm_kernel(DxParams p) {
   // store 8 consecutive-k 16-bit values (chunk c of this thread's NCH) of
   // reduction row `wr` into the W slab
   auto store8 = [&](int stage, int c, const u32x4_t v) {
-    *reinterpret_cast<u32x4_t*>(wbase + stage * WST + wr * WR + ((KW / 4) * kq + 8 * c) * 2) = v;
+    *reinterpret_cast<u32x4_t*>(wbase + stage * WST + wr * WR +
+                                ((((KW / 4) * kq + 8 * c) * 2) ^ slab_swz(wr))) = v;
   };
   // A operand of MFMA step kk, k sub-tile i: lane l holds column
   // (KW / 2) wk + 32 i + l % 32 at reduction rows 16 kk + 8 (l / 32) + 0..7, from
   // two transpose reads (rows +0..3 and +4..7).  As provider, lane j of
   // 16-lane group g points at row 8 (g / 2) + j / 4 (+ 4 for the second
   // read), column 16 (g % 2) + 4 (j % 4).
+  // (The swizzle term of a row does not change with kk, as 16 kk is a
+  // multiple of 4 rows, nor with i, which moves by whole 64-byte windows.)
   const int tg = lane >> 4, tj = lane & 15;
-  const int a_off =
-      (8 * (tg >> 1) + (tj >> 2)) * WR + ((KW / 2) * wk + 16 * (tg & 1) + 4 * (tj & 3)) * 2;
+  const int a_row = 8 * (tg >> 1) + (tj >> 2);
+  const int a_col = ((KW / 2) * wk + 16 * (tg & 1) + 4 * (tj & 3)) * 2;
+  const int a_off0 = a_row * WR + (a_col ^ slab_swz(a_row));
+  const int a_off1 = (a_row + 4) * WR + (a_col ^ slab_swz(a_row + 4));
   auto read_a = [&](int stage, int kk, int i) -> u32x4_t {
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s lds_v4s;
-    const int o = stage * WST + a_off + 16 * kk * WR + 64 * i;
-    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o));
-    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o + 4 * WR));
+    const int o = stage * WST + 16 * kk * WR + 64 * i;
+    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o + a_off0));
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o + a_off1));
     const u32x2_t h0 = __builtin_bit_cast(u32x2_t, r0), h1 = __builtin_bit_cast(u32x2_t, r1);
     const u32x4_t v = {h0[0], h0[1], h1[0], h1[1]};
     return v;

@@ -55,7 +55,23 @@ struct LoraProjJob {
   int rng = 0;
   PhiloxDrop drop{};
   uint8_t* keep_out = nullptr;
+  // reduction split (lora_proj_plan): S > 1 blocks per (token, rank)
+  // tile each sum a share of Kred into fp32 partials part [S][r][Mp], which
+  // a finalize pass adds in split order
+  int S = 1;
+  float* part = nullptr;
 };
+// How lora_proj runs one or two jobs (reduction lengths kred0, kred1; 0 =
+// no second job): the small kernel, or the MFMA kernel with TT 16-token
+// tiles per block and S[j] reduction splits for job j.
+struct ProjPlan {
+  bool small;
+  int tt;
+  int s[2];
+};
+ProjPlan lora_proj_plan(int64_t M, int r, int64_t kred0, int64_t kred1);
+// fp32 partials a job of the plan needs (0 when it is not split)
+size_t lora_proj_partial_bytes(const ProjPlan& p, int job, int64_t M, int r);
 // one job, or two in one launch (j1 non-null)
 // f16: the fp16 compute type (operands and the hi/lo pairs in fp16; no
 // keep-mask), else bf16.

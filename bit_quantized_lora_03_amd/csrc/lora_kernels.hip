@@ -120,6 +120,8 @@ __device__ __forceinline__ LoraProjJob uniform_job(const LoraProjJob& j) {
   u.drop.o1 = __builtin_amdgcn_readfirstlane(j.drop.o1);
   u.drop.t = __builtin_amdgcn_readfirstlane(j.drop.t);
   u.keep_out = uniform_ptr(j.keep_out);
+  u.S = __builtin_amdgcn_readfirstlane(j.S);
+  u.part = uniform_ptr(j.part);
   return u;
 }
 __device__ __forceinline__ LoraGradJob uniform_job(const LoraGradJob& j) {
@@ -168,25 +170,34 @@ __device__ __forceinline__ void put_split(const LoraProjJob& J, int64_t M, int r
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// lora_proj: grid = sum over jobs of (Mp / 16) * ceil(r / RC) blocks, 512
-// threads.  A block owns 16 tokens x RC = 16 JT rank columns of one job and
-// that job's whole reduction; wave w takes the 32-wide k steps w, w + 8, ...
-// with 16x16x32 MFMA (tokens as rows).  The token operand is one 16-byte
-// load per lane (8 consecutive k of a row); so is A's operand per 16-column
-// group.  B's rows (8 rank columns of one k per 16 bytes) go through the
-// wave's slab and come back transposed.
+// lora_proj: grid = sum over jobs of ceil(Mp / (16 TT)) * ceil(r / RC) * S
+// blocks, 512 threads.  A block owns 16 TT tokens x RC = 16 JT rank columns
+// of one job and a contiguous 1/S share of that job's 32-wide reduction
+// steps; wave w takes the block's steps w, w + 8, ... with 16x16x32 MFMA
+// (tokens as rows).  The token operand is one 16-byte load per lane and
+// token tile (8 consecutive k of a row); A's operand is one per 16-column
+// group, shared by the TT token tiles, so a block reads A (or B) once for
+// 16 TT tokens -- at training sizes the small operand, re-read by every
+// token block, is what the kernel's L2 traffic is made of.  B's rows (8
+// rank columns of one k per 16 bytes) go through the wave's slab and come
+// back transposed, once per step for all TT tiles.  The waves' sums are
+// added in LDS in wave order, one token tile at a time; with S = 1 the
+// block stores the hi/lo pairs itself, otherwise fp32 partials that
+// lora_proj_finalize adds in split order.
 // ---------------------------------------------------------------------------
 // DROP: LoRA dropout on X (see keep8): 0 none, 1 the jobs may carry a
 // keep-mask, 2 a job may draw its keep bits (rng) -- the blocks of the first
 // rank chunk then also store them to keep_out.
-template <int JT, int DROP, class DT>
+template <int JT, int TT, int DROP, class DT>
 __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, LoraProjJob j1,
                                                              int64_t blocks0, int64_t M, int r,
                                                              float scale) {
   constexpr int RC = 16 * JT;            // rank columns of the block
   constexpr int RS = RC + 8;             // slab row: RC bf16 + 16 bytes of pad
   constexpr int SLAB = 32 * RS;          // bf16 per wave
-  constexpr int BS = JT == 1 ? 8 : 4;    // k steps per batch of loads
+  // k steps per batch of loads (a batch holds TT + JT operands per step;
+  // sized so that no variant spills)
+  constexpr int BS = TT >= 4 ? 1 : (TT == 2 ? 2 : (JT == 1 ? 8 : (JT == 2 ? 4 : 2)));
   constexpr int REDS = RC + 4;           // fp32 row of the cross-wave sums
   constexpr int SLAB_BYTES = kWaves * SLAB * 2, RED_BYTES = kWaves * 16 * REDS * 4;
   __shared__ __align__(16) char lds[SLAB_BYTES > RED_BYTES ? SLAB_BYTES : RED_BYTES];
@@ -198,33 +209,42 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   const LoraProjJob J = uniform_job(second ? j1 : j0);
   const int64_t b = second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x;
   const int jchunks = (r + RC - 1) / RC;
-  const int64_t m0 = 16 * (b / jchunks);
-  const int jc = (int)(b % jchunks) * RC;
+  const int S = J.S;
+  const int z = (int)(b % S);
+  const int64_t rest = b / S;
+  const int64_t m0 = 16 * TT * (rest / jchunks);
+  const int jc = (int)(rest % jchunks) * RC;
   const int i = lane & 15, kg = lane >> 4;
-  const int64_t m = m0 + i;
   const int64_t Kred = J.Kred;
   const int64_t nsteps = Kred / 32;
-  const int64_t cnt = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+  const int64_t s0 = nsteps * z / S, s1 = nsteps * (z + 1) / S;
+  const int64_t cnt = s1 - s0 > wave ? (s1 - s0 - wave + kWaves - 1) / kWaves : 0;
   const __amdgpu_buffer_rsrc_t xres = make_rsrc(J.X, (uint32_t)(M * Kred * 2));
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(J.Y, (uint32_t)((int64_t)r * Kred * 2));
-  // rows m in [M, Mp) lie past x's end and read as zero
-  const uint32_t xoff = (uint32_t)((m * Kred + 8 * kg) * 2);
+  // rows m in [M, Mp) (and past Mp) lie past x's end and read as zero
+  uint32_t xoff[TT], koff[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int64_t m = m0 + 16 * tt + i;
+    xoff[tt] = (uint32_t)((m * Kred + 8 * kg) * 2);
+    koff[tt] = (uint32_t)(m * (Kred / 8) + kg);  // keep byte of the lane's x chunk: + k0 / 8
+  }
   uint16_t* slab = reinterpret_cast<uint16_t*>(lds) + wave * SLAB;
   const bool kmajor = J.kmajor != 0;
-  // keep byte of the lane's x chunk: (m Kred + k0 + 8 kg) / 8
   const KeepBits kp = keep_bits(J.keep, M * Kred / 8);
-  const uint32_t koff = (uint32_t)(m * (Kred / 8) + kg);
 
-  f32x4_t acc[JT];
+  f32x4_t acc[TT][JT];
 #pragma unroll
-  for (int jt = 0; jt < JT; ++jt) acc[jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt) acc[tt][jt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   // Y pieces of a step: A: column group jt's 16 bytes; B: piece p = lane +
   // 64 q of the 32 x RC slab, row p / (2 JT), 8 columns at 8 (p mod 2 JT)
   struct Batch {
-    u32x4_t x[BS];
+    u32x4_t x[BS][TT];
     u32x4_t y[BS][JT];
-    uint32_t kb[BS];
+    uint32_t kb[BS][TT];
   };
   // Lane offsets of the Y pieces, fixed for the whole loop (kOff past r).
   // Steps past the wave's count OR in kOff: a select the compiler keeps as
@@ -240,14 +260,18 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
       yoff[q] = col < r ? (uint32_t)(row * r + col) * 2u : kOff;
     }
   }
+  auto k_of = [&](int64_t u) { return (uint32_t)(32 * (s0 + wave + kWaves * u)); };
   auto load = [&](int64_t u0, Batch& R) {
 #pragma unroll
     for (int bb = 0; bb < BS; ++bb) {
       const int64_t u = u0 + bb;
       const uint32_t past = u < cnt ? 0u : kOff;
-      const uint32_t k0 = (uint32_t)(32 * (wave + kWaves * u));
-      R.x[bb] = ldb(xres, xoff | past, 2 * k0);
-      if constexpr (DROP == 1) R.kb[bb] = ldb8(kp.res, koff | past, k0 / 8) | kp.all;
+      const uint32_t k0 = k_of(u);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        R.x[bb][tt] = ldb(xres, xoff[tt] | past, 2 * k0);
+        if constexpr (DROP == 1) R.kb[bb][tt] = ldb8(kp.res, koff[tt] | past, k0 / 8) | kp.all;
+      }
 #pragma unroll
       for (int q = 0; q < JT; ++q)
         R.y[bb][q] = ldb(yres, yoff[q] | past, kmajor ? 2 * k0 * (uint32_t)r : 2 * k0);
@@ -255,34 +279,47 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   };
   // drawn keep bytes: the first rank chunk's blocks store those of real
   // tokens and steps
-  const bool store_keep = DROP == 2 && J.keep_out != nullptr && jc == 0 && m < M;
+  const bool store_keep = DROP == 2 && J.keep_out != nullptr && jc == 0;
   // steps past the wave's count carry zero operands and add nothing
   auto compute = [&](const Batch& R, int64_t u0) {
 #pragma unroll
     for (int bb = 0; bb < BS; ++bb) {
-      uint32_t kb = 0xFFu;
-      if constexpr (DROP == 1) kb = R.kb[bb];
-      if constexpr (DROP == 2) {
-        if (J.rng) {
-          const int64_t u = u0 + bb;
-          const uint32_t chunk = koff + (uint32_t)(4 * (wave + kWaves * u));
-          kb = philox_keep_byte(J.drop, chunk);
-          if (store_keep && u < cnt) J.keep_out[chunk] = (uint8_t)kb;
-        }
-      }
-      const u32x4_t xv = DROP ? keep8(R.x[bb], kb) : R.x[bb];
-      if (!kmajor) {
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) acc[jt] = DT::mfma16(xv, R.y[bb][jt], acc[jt]);
-      } else {
+      const int64_t u = u0 + bb;
+      if (kmajor) {
 #pragma unroll
         for (int q = 0; q < JT; ++q) {
           const int p = lane + 64 * q, row = p / (2 * JT), cp = p % (2 * JT);
           *reinterpret_cast<u32x4_t*>(slab + row * RS + 8 * cp) = R.y[bb][q];
         }
+      }
+      // B's operands from the slab: read each once for the TT tiles (with
+      // one tile, one at a time next to its MFMA, which keeps fewer live)
+      u32x4_t yv[JT];
+      if constexpr (TT > 1) {
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
-          acc[jt] = DT::mfma16(xv, read_tr8(slab, RS, 8 * kg, 16 * jt, i), acc[jt]);
+          yv[jt] = kmajor ? read_tr8(slab, RS, 8 * kg, 16 * jt, i) : R.y[bb][jt];
+      }
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        uint32_t kb = 0xFFu;
+        if constexpr (DROP == 1) kb = R.kb[bb][tt];
+        if constexpr (DROP == 2) {
+          if (J.rng) {
+            const uint32_t chunk = koff[tt] + k_of(u) / 8;
+            kb = philox_keep_byte(J.drop, chunk);
+            if (store_keep && u < cnt && m0 + 16 * tt + i < M) J.keep_out[chunk] = (uint8_t)kb;
+          }
+        }
+        const u32x4_t xv = DROP ? keep8(R.x[bb][tt], kb) : R.x[bb][tt];
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          if constexpr (TT > 1)
+            acc[tt][jt] = DT::mfma16(xv, yv[jt], acc[tt][jt]);
+          else
+            acc[tt][jt] = DT::mfma16(
+                xv, kmajor ? read_tr8(slab, RS, 8 * kg, 16 * jt, i) : R.y[bb][jt], acc[tt][jt]);
+        }
       }
     }
   };
@@ -299,23 +336,51 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   }
 
   // D[token][j]: lane holds column j = 16 jt + lane % 16, tokens 4 (lane / 16) + v
-  __syncthreads();  // every slab is done; the sums reuse the LDS
   float* red = reinterpret_cast<float*>(lds);
-#pragma unroll
-  for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[(wave * 16 + 4 * kg + v) * REDS + 16 * jt + i] = acc[jt][v];
-  __syncthreads();
   const int64_t Mp = pad32(M);
-  for (int e = t; e < 16 * RC; e += kThreads) {
-    const int tok = e & 15, j = e >> 4;  // tokens fastest: outT rows are token-contiguous
-    float sum = red[tok * REDS + j];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += red[(w * 16 + tok) * REDS + j];
-    const int64_t mo = m0 + tok;
-    const int jo = jc + j;
-    if (jo < r && mo < Mp) put_split<DT>(J, M, r, mo, jo, scale * sum);
+  for (int tt = 0; tt < TT; ++tt) {
+    __syncthreads();  // every slab (first tile) or the last tile's sums are done
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[(wave * 16 + 4 * kg + v) * REDS + 16 * jt + i] = acc[tt][jt][v];
+    __syncthreads();
+    for (int e = t; e < 16 * RC; e += kThreads) {
+      const int tok = e & 15, j = e >> 4;  // tokens fastest: outT rows are token-contiguous
+      float sum = red[tok * REDS + j];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) sum += red[(w * 16 + tok) * REDS + j];
+      const int64_t mo = m0 + 16 * tt + tok;
+      const int jo = jc + j;
+      if (jo < r && mo < Mp) {
+        if (S == 1)
+          put_split<DT>(J, M, r, mo, jo, scale * sum);
+        else
+          J.part[((int64_t)z * r + jo) * Mp + mo] = sum;
+      }
+    }
   }
+}
+
+// The split jobs' hi/lo pairs: element e of a job is (j, m) = (e / Mp,
+// e % Mp); its S partials are added in split order and scaled once.
+template <class DT>
+__global__ __launch_bounds__(256) void lora_proj_finalize_kernel(LoraProjJob j0, LoraProjJob j1,
+                                                                 int64_t n0, int64_t M, int r,
+                                                                 float scale) {
+  const int64_t Mp = pad32(M);
+  int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool second = e >= n0;
+  const LoraProjJob& J = second ? j1 : j0;
+  if (second) e -= n0;
+  if (e >= Mp * r) return;
+  const int j = (int)(e / Mp);
+  const int64_t m = e % Mp;
+  float sum = 0.0f;
+  for (int zz = 0; zz < J.S; ++zz) sum += J.part[((int64_t)zz * r + j) * Mp + m];
+  put_split<DT>(J, M, r, m, j, scale * sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -474,10 +539,77 @@ static bool proj_small(int64_t M, int r) { return M * r <= 16384; }
 
 static int proj_jt(int r) { return r <= 16 ? 1 : (r <= 32 ? 2 : 4); }
 
+// Token tiles per block: the largest (up to 8, or 4 for ranks above 32)
+// that leaves at least 16 token blocks.  Splits: about 256 blocks in all, dealt to the jobs in
+// proportion to their reduction lengths, each split at least two steps per
+// wave and at most 16 splits.
+ProjPlan lora_proj_plan(int64_t M, int r, int64_t kred0, int64_t kred1) {
+  ProjPlan p{};
+  p.s[0] = p.s[1] = 1;
+  p.tt = 1;
+  if (r == 0 || M == 0) return p;
+  if (proj_small(M, r)) {
+    p.small = true;
+    return p;
+  }
+  const int64_t Mp = pad32(M);
+  const int rc = 16 * proj_jt(r);
+  const int64_t jch = (r + rc - 1) / rc;
+  // (at most 4 with rank tiles of 64 columns: 8 would not fit the registers)
+  int tt = proj_jt(r) == 4 ? 4 : 8;
+  while (tt > 1 && Mp / (16 * tt) < 16) tt /= 2;
+  p.tt = tt;
+  const int64_t base = (Mp + 16 * tt - 1) / (16 * tt) * jch;  // blocks per job, unsplit
+  const int64_t ktot = kred0 + kred1;
+  for (int j = 0; j < 2; ++j) {
+    const int64_t kr = j ? kred1 : kred0;
+    if (kr <= 0) continue;
+    int64_t sj = (256 * kr + ktot * base / 2) / (ktot * base);
+    const int64_t smax = kr / (32 * kWaves * 2);
+    if (sj > smax) sj = smax;
+    if (sj > 16) sj = 16;
+    if (sj < 1) sj = 1;
+    p.s[j] = (int)sj;
+  }
+  return p;
+}
+
+size_t lora_proj_partial_bytes(const ProjPlan& p, int job, int64_t M, int r) {
+  if (p.small || p.s[job] <= 1) return 0;
+  return (size_t)p.s[job] * (size_t)r * (size_t)pad32(M) * sizeof(float);
+}
+
+template <int JT, int TT, int DROP, class DT>
+static void launch_proj_tiled(dim3 grid, hipStream_t s, const LoraProjJob& j0,
+                              const LoraProjJob& jb, int64_t blocks0, int64_t M, int r,
+                              float scale) {
+  hipLaunchKernelGGL((lora_proj_kernel<JT, TT, DROP, DT>), grid, dim3(kThreads), 0, s, j0, jb,
+                     blocks0, M, r, scale);
+}
+
+template <int JT, int DROP, class DT>
+static void launch_proj_tt(int tt, dim3 grid, hipStream_t s, const LoraProjJob& j0,
+                           const LoraProjJob& jb, int64_t blocks0, int64_t M, int r,
+                           float scale) {
+  if constexpr (JT < 4) {
+    if (tt >= 8) {
+      launch_proj_tiled<JT, 8, DROP, DT>(grid, s, j0, jb, blocks0, M, r, scale);
+      return;
+    }
+  }
+  if (tt >= 4)
+    launch_proj_tiled<JT, 4, DROP, DT>(grid, s, j0, jb, blocks0, M, r, scale);
+  else if (tt == 2)
+    launch_proj_tiled<JT, 2, DROP, DT>(grid, s, j0, jb, blocks0, M, r, scale);
+  else
+    launch_proj_tiled<JT, 1, DROP, DT>(grid, s, j0, jb, blocks0, M, r, scale);
+}
+
 template <int DROP, class DT>
 static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int64_t M, int r,
                               float scale, hipStream_t s) {
-  if (proj_small(M, r)) {
+  const ProjPlan plan = lora_proj_plan(M, r, j0.Kred, j1 ? j1->Kred : 0);
+  if (plan.small) {
     // Mp / TT token groups cover every row of the transposed copy; 4-token
     // blocks when 8-token ones would not give every CU a block
     const int jobs = j1 ? 2 : 1;
@@ -496,21 +628,31 @@ static hipError_t launch_proj(const LoraProjJob& j0, const LoraProjJob* j1, int6
   }
   const int jt = proj_jt(r);
   const int rc = 16 * jt;
-  // Mp / 16 token blocks cover every row of the transposed copy
-  const int64_t blocks_per_job = (pad32(M) / 16) * ((r + rc - 1) / rc);
-  const LoraProjJob jb = j1 ? *j1 : j0;
-  const int64_t blocks0 = blocks_per_job, total = blocks_per_job * (j1 ? 2 : 1);
+  LoraProjJob a = j0, b = j1 ? *j1 : j0;
+  a.S = plan.s[0];
+  b.S = j1 ? plan.s[1] : plan.s[0];
+  if ((a.S > 1 && !a.part) || (j1 && b.S > 1 && !b.part)) return hipErrorInvalidValue;
+  // ceil(Mp / (16 TT)) token blocks cover every row of the transposed copy
+  const int64_t tiles = (pad32(M) + 16 * plan.tt - 1) / (16 * plan.tt) * ((r + rc - 1) / rc);
+  const int64_t blocks0 = tiles * a.S, total = blocks0 + (j1 ? tiles * b.S : 0);
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)total);
   if (jt == 1)
-    hipLaunchKernelGGL((lora_proj_kernel<1, DROP, DT>), grid, dim3(kThreads), 0, s, j0, jb,
-                       blocks0, M, r, scale);
+    launch_proj_tt<1, DROP, DT>(plan.tt, grid, s, a, b, blocks0, M, r, scale);
   else if (jt == 2)
-    hipLaunchKernelGGL((lora_proj_kernel<2, DROP, DT>), grid, dim3(kThreads), 0, s, j0, jb,
-                       blocks0, M, r, scale);
+    launch_proj_tt<2, DROP, DT>(plan.tt, grid, s, a, b, blocks0, M, r, scale);
   else
-    hipLaunchKernelGGL((lora_proj_kernel<4, DROP, DT>), grid, dim3(kThreads), 0, s, j0, jb,
-                       blocks0, M, r, scale);
+    launch_proj_tt<4, DROP, DT>(plan.tt, grid, s, a, b, blocks0, M, r, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n0 = a.S > 1 ? pad32(M) * r : 0;
+  const int64_t n1 = (j1 && b.S > 1) ? pad32(M) * r : 0;
+  if (n0 + n1 == 0) return hipSuccess;
+  // a job that is not split already stored its pairs: give the finalize
+  // only the split ones (an unsplit first job is replaced by the second)
+  const LoraProjJob& f0 = n0 ? a : b;
+  hipLaunchKernelGGL((lora_proj_finalize_kernel<DT>), dim3((unsigned)((n0 + n1 + 255) / 256)),
+                     dim3(256), 0, s, f0, b, n0 ? n0 : n1, M, r, scale);
   return hipGetLastError();
 }
 

@@ -312,7 +312,7 @@ int qlora_linear_bf16_bwd(const uint16_t* W, int64_t N, int64_t K, const uint16_
  *     qlora_linear_workspace_bytes(0, M, N, K, r), exceeds it returns
  *     QLORA_ESCRATCH before any HIP call (every workload of this library
  *     fits: the largest, 2048 tokens through an 11008 -> 4096 layer, needs
- *     64.25 MiB).
+ *     66.25 MiB).
  *   - The call allocates nothing (no hipMalloc, no hipFree).  On the first
  *     call on a GPU it looks up that GPU's copy of the buffer (a
  *     hipGetSymbolAddress with the current device, which must be the

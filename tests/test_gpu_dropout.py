@@ -34,6 +34,8 @@ SHAPES = [
     (600, 256, 512, 256, 8.0, 0.05),
     (1024, 1024, 768, 16, 32.0, 0.05),
     (200, 4096, 512, 32, 64.0, 0.05),
+    (1000, 4096, 1024, 64, 16.0, 0.05),  # split down-projections, 4 token tiles
+    (2100, 8192, 256, 32, 64.0, 0.1),    # dy.B split, 8 token tiles
 ]
 
 

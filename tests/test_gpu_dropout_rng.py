@@ -54,6 +54,8 @@ SHAPES = [
     (600, 256, 512, 128, 8.0, 0.05),     # MFMA kernel, two rank chunks of 64
     (33, 192, 1024, 256, 32.0, 0.3),     # small kernel, 32 rank groups
     (1024, 1024, 768, 16, 32.0, 0.05),
+    (1000, 4096, 1024, 64, 16.0, 0.05),  # split down-projections, 4 token tiles
+    (2304, 320, 4096, 16, 32.0, 0.05),   # 8 token tiles, x.A^T split 8 ways
 ]
 
 

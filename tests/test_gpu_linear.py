@@ -2,7 +2,9 @@
 oracle, through the C ABI.  The GEMMs are fed the oracle's packed weight,
 so their parity does not depend on the GPU quantiser (tested separately).
 
-Bar: max|T_gpu - T_oracle| <= 2e-2 * rms(T_oracle) for y, dX, dA, dB.
+Bar: max|T_gpu - T_oracle| <= 2e-2 * rms(T_oracle) for y, dX, dA, dB (for
+the bf16 outputs y and dX, or their own rounding floor where one large
+element puts that above 2e-2).
 Exact cases: one-hot probes read back the decoded weight bit for bit.
 """
 
@@ -12,7 +14,8 @@ import pytest
 import oracle
 import bit_quantized_lora_03_amd as q
 from bit_quantized_lora_03_amd import workloads
-from tests.gpu_util import Guarded, OracleLayer, bf16_values, check_close, dev, host
+from tests.gpu_util import (Guarded, OracleLayer, bf16_values, check_close, check_close_bf16, dev,
+                            host)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +34,12 @@ SHAPES = [
     # with very different reduction lengths: N >> K and N << K
     (200, 4096, 512, 32, 64.0),
     (96, 256, 4096, 16, 32.0),
+    # the down-projection's token tiles and reduction splits: 8 tiles with
+    # x.A^T split (dy.B not), 4 tiles with both split, 8 tiles with only
+    # dy.B split (ragged token blocks in each)
+    (2304, 320, 4096, 16, 32.0),
+    (1000, 4096, 1024, 64, 16.0),
+    (2100, 8192, 256, 32, 64.0),
 ]
 
 
@@ -93,7 +102,7 @@ def test_forward_parity(cuda, shape):
     print(f"fwd {shape}", flush=True)
     L = _layer(*shape)
     ol = OracleLayer(L.w)
-    check_close("y", _run_fwd(L, ol), _ref_fwd(L, ol))
+    check_close_bf16("y", _run_fwd(L, ol), _ref_fwd(L, ol))
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
@@ -106,7 +115,7 @@ def test_backward_parity(cuda, shape):
     rdx, rdA, rdB = oracle.lora_linear_bwd(L.f32("x"), L.f32("dy"), ol.w_deq,
                                            L.f32("A") if r else None,
                                            L.f32("B") if r else None, alpha)
-    check_close("dX", dx, rdx)
+    check_close_bf16("dX", dx, rdx)
     if r:
         check_close("dA", dA, rdA)
         check_close("dB", dB, rdB)
@@ -155,8 +164,12 @@ def test_one_hot_probes_are_bit_exact(cuda):
     (33, 256, 2048, 128, 16.0),   # ... sixteen rank groups
     (2304, 320, 448, 16, 32.0),   # more outputs: 16 x 16 MFMA tiles
     (600, 128, 384, 64, 16.0),    # ... four 16-column groups per block
+    (2304, 320, 4096, 16, 32.0),  # 8 token tiles, x.A^T split 8 ways
+    (1000, 4096, 1024, 64, 16.0), # 4 token tiles, both reductions split
+    (2100, 8192, 256, 32, 64.0),  # 8 token tiles, dy.B split
 ], ids=[str(s) for s in [(129, 256, 512, 16), (40, 192, 1024, 24), (33, 256, 2048, 128),
-                         (2304, 320, 448, 16), (600, 128, 384, 64)]])
+                         (2304, 320, 448, 16), (600, 128, 384, 64), (2304, 320, 4096, 16),
+                         (1000, 4096, 1024, 64), (2100, 8192, 256, 32)]])
 def test_zero_base_isolates_the_adapter_path(cuda, shape):
     """W = 0: y and dX are the adapter terms alone (x.A^T and dy.B through
     both down-projection kernels), tested at their own scale, with dA, dB."""
@@ -203,8 +216,9 @@ def test_empty_token_batch(cuda):
     assert np.all(host(dA) == 0) and np.all(host(dB) == 0)
 
 
-@pytest.mark.parametrize("shape", [(300, 320, 448, 16, 32.0), (8, 256, 512, 64, 16.0)],
-                         ids=["main", "decode"])
+@pytest.mark.parametrize("shape", [(300, 320, 448, 16, 32.0), (8, 256, 512, 64, 16.0),
+                                   (1000, 4096, 1024, 64, 16.0)],
+                         ids=["main", "decode", "split-down-projection"])
 def test_graph_replay_matches_eager(cuda, shape):
     """The whole fwd + bwd captured in one HIP graph: every replay (with
     eager work and synchronisations between replays) equals the eager run

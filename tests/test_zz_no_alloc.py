@@ -19,10 +19,10 @@ SEQUENCES = {
     # tiled GEMM with 2-way split partials and the adapter products, then the
     # few-token path with its adapter partial planes
     "q_proj_then_decode": [(512, 4096, 4096, 16, 32.0), (16, 2048, 2048, 64, 16.0)],
-    # the 65B-class layer (tail-split partials, 50 MiB of scratch), then a
-    # ragged small layer on the tiled path
+    # the 65B-class layer (tail-split and down-projection partials, 54 MiB
+    # of scratch), then a ragged small layer on the tiled path
     "up65b_then_ragged": [(4096, 22016, 8192, 64, 16.0), (300, 320, 448, 16, 32.0)],
-    # the largest workload need (64.25 MiB), then a base-only ragged call
+    # the largest workload need (66.25 MiB), then a base-only ragged call
     "mlp_down_then_base_only": [(2048, 4096, 11008, 16, 32.0), (70, 448, 640, 0, 1.0)],
 }
 
