@@ -324,15 +324,19 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
     }
   };
 
+  // Loads are unconditional (steps past the count read zeros, which add
+  // nothing): a branch around them would make the compiler, at the join,
+  // wait for the newer batch too before computing the older one.  The
+  // fences keep each batch's loads ahead of the compute before them.
   Batch R0, R1;
-  if (cnt > 0) load(0, R0);
+  load(0, R0);
   for (int64_t u0 = 0; u0 < cnt; u0 += 2 * BS) {
-    if (u0 + BS < cnt) load(u0 + BS, R1);
+    load(u0 + BS, R1);
+    __builtin_amdgcn_sched_barrier(0);
     compute(R0, u0);
-    if (u0 + BS < cnt) {
-      if (u0 + 2 * BS < cnt) load(u0 + 2 * BS, R0);
-      compute(R1, u0 + BS);
-    }
+    load(u0 + 2 * BS, R0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(R1, u0 + BS);
   }
 
   // D[token][j]: lane holds column j = 16 jt + lane % 16, tokens 4 (lane / 16) + v
@@ -788,15 +792,16 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
       }
     };
 
+    // unconditional loads, as in lora_proj (zeros past the count)
     Batch R0, R1;
-    if (cnt > 0) load(0, R0);
+    load(0, R0);
     for (int64_t u0 = 0; u0 < cnt; u0 += 2 * BS) {
-      if (u0 + BS < cnt) load(u0 + BS, R1);
+      load(u0 + BS, R1);
+      __builtin_amdgcn_sched_barrier(0);
       compute(R0);
-      if (u0 + BS < cnt) {
-        if (u0 + 2 * BS < cnt) load(u0 + 2 * BS, R0);
-        compute(R1);
-      }
+      load(u0 + 2 * BS, R0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(R1);
     }
 
     // D[g][j]: lane holds column j = 16 jt + lane % 16, rows 4 (lane / 16) + v
