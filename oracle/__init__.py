@@ -18,6 +18,9 @@ What it computes (numpy, fp64 unless a step fixes another precision):
 * ``philox`` -- Philox4x32-10 and the LoRA-dropout keep mask the library
   draws from it in-kernel (counter = mask byte and stream offset, key =
   seed; 16-bit draws against a threshold).
+* ``dq_centred`` -- the paper-style variant of the scale encoding: block
+  scales centred on their tensor mean and coded as symmetric signed 8-bit
+  values per group of 256 (s' = fp32(fp32(q * step) + mean)).
 * ``merge`` -- the adapter merged into a base weight for export,
   W_m = W_base + (alpha/r).B.A (fp32 and bf16 exports, re-quantisation, and
   the errors of the three ways to export).
@@ -53,6 +56,13 @@ from .nf4 import (  # noqa: F401
     storage_bits_per_weight,
 )
 from .lora_linear import lora_linear_fwd, lora_linear_bwd, lora_scale, dropped_input  # noqa: F401
+from .dq_centred import (  # noqa: F401
+    centred_mean,
+    double_quant_centred,
+    dequant_scales_centred,
+    dequant_nf4_centred_bits,
+    dequant_nf4_centred_f16_bits,
+)
 from .merge import merge_adapter, merged_bf16_bits, requantize, merge_errors  # noqa: F401
 from .philox import (  # noqa: F401
     philox4x32_10,
