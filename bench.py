@@ -748,6 +748,52 @@ def main():
                "over_bf16": round((t_fh + t_bh) / (t_f + t_b), 4)}
         del x16, dy16, A16, B16, ws_h
 
+    # ---- the mean-centred scale format of the same weight (its own
+    # quantisation of w; the same kernels with that format's block-scale
+    # decode), fwd + bwd each timed right after the unsigned-format call ----
+    centred = None
+    if kind != "fwd" and not args.roofline_only:
+        nb = n // 64
+        c_c = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        a_c = torch.empty(nb, dtype=torch.float32, device=dev)
+        q_c = torch.empty(nb, dtype=torch.uint8, device=dev)
+        s_c = torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev)
+        m_c = torch.empty(1, dtype=torch.float32, device=dev)
+        ws_c = torch.empty(max(int(lib.qlora_dq_centred_workspace_bytes(nb)), 256),
+                           dtype=torch.uint8, device=dev)
+
+        def quantize_c():
+            check(lib.qlora_quantize_nf4_dq_centred(P(w_d), n, P(c_c), P(a_c), P(q_c), P(s_c),
+                                                    P(m_c), P(ws_c), ws_c.numel(), sp()),
+                  "quantize centred")
+        quantize_c()
+        wt_c = _lib.Nf4Weight(c_c.data_ptr(), q_c.data_ptr(), s_c.data_ptr(), N, K,
+                              m_c.data_ptr())
+
+        def fwd_c():
+            check(lib.qlora_linear_fwd(ctypes.byref(wt_c), P(x_d), M, P(A_d) if r else None,
+                                       P(B_d) if r else None, r, alpha, P(y), P(ws), ws.numel(),
+                                       sp()), "fwd centred")
+
+        def bwd_c():
+            check(lib.qlora_linear_bwd(ctypes.byref(wt_c), P(x_d), P(dy_d), M,
+                                       P(A_d) if r else None, P(B_d) if r else None, r, alpha,
+                                       P(dx), P(dA) if r else None, P(dB) if r else None, 0,
+                                       P(ws), ws.numel(), sp()), "bwd centred")
+        t_q = timed(lambda i: quantize(), reps) if "quant" in kind else None
+        t_qc = timed(lambda i: quantize_c(), reps)
+        t_f = timed(lambda i: fwd(0), reps)
+        t_fc = timed(lambda i: fwd_c(), reps)
+        t_b = timed(lambda i: bwd(), reps)
+        t_bc = timed(lambda i: bwd_c(), reps)
+        centred = {"quantize_ms": round(t_qc, 5), "fwd_ms": round(t_fc, 5),
+                   "bwd_ms": round(t_bc, 5), "unsigned_fwd_ms": round(t_f, 5),
+                   "unsigned_bwd_ms": round(t_b, 5),
+                   "fwd_bwd_over_unsigned": round((t_fc + t_bc) / (t_f + t_b), 4)}
+        if t_q is not None:
+            centred["unsigned_quantize_ms"] = round(t_q, 5)
+        del c_c, a_c, q_c, s_c, m_c, ws_c
+
     # ---- adapter merge for export (not part of the step): W_m = W + s.B.A,
     # fp32 and bf16 exports, from the NF4 base and from the fp32 original ----
     merge = None
@@ -843,6 +889,7 @@ def main():
         "vs_unquantised": unq,
         "dropout": drop,
         "fp16": f16,
+        "centred_scales": centred,
         "merge": merge,
         "gates": gates,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "step_s"},

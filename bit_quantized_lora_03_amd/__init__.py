@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     dequantize,
     dequantize_f16,
     double_quant,
+    double_quant_centred,
     dropout_keep_mask,
     lib,
     linear_bf16_bwd,
@@ -35,6 +36,8 @@ from ._lib import (  # noqa: F401
     nf4_levels,
     quantize_nf4,
     quantize_nf4_dq,
+    quantize_nf4_dq_centred,
     quantize_weight,
+    quantize_weight_centred,
     workspace_bytes,
 )

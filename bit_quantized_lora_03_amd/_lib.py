@@ -22,6 +22,8 @@ STATUS_NAMES = {0: "QLORA_OK", -1: "QLORA_EINVAL", -2: "QLORA_ESHAPE", -3: "QLOR
                 -7: "QLORA_ESCRATCH"}
 
 EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
+           "qlora_dq_centred_workspace_bytes", "qlora_double_quant_centred",
+           "qlora_quantize_nf4_dq_centred",
            "qlora_dequantize_nf4",
            "qlora_linear_fwd", "qlora_linear_bwd", "qlora_linear_workspace_bytes",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dropout",
@@ -41,9 +43,11 @@ class QloraError(RuntimeError):
 
 
 class Nf4Weight(ctypes.Structure):
-    """``qlora_nf4_weight``: device pointers to codes, qscale, dq_step; N, K."""
+    """``qlora_nf4_weight``: device pointers to codes, qscale, dq_step; N, K;
+    dq_mean (null for the unsigned scale format)."""
     _fields_ = [("codes", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
-                ("dq_step", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+                ("dq_step", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("dq_mean", ctypes.c_void_p)]
 
 
 _lib = None
@@ -65,6 +69,10 @@ def lib() -> ctypes.CDLL:
         "qlora_quantize_nf4": ([vp, i64, i32, vp, vp, vp], ctypes.c_int),
         "qlora_double_quant": ([vp, i64, i32, vp, vp, vp], ctypes.c_int),
         "qlora_quantize_nf4_dq": ([vp, i64, vp, vp, vp, vp, vp], ctypes.c_int),
+        "qlora_dq_centred_workspace_bytes": ([i64], sz),
+        "qlora_double_quant_centred": ([vp, i64, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "qlora_quantize_nf4_dq_centred": ([vp, i64, vp, vp, vp, vp, vp, vp, sz, vp],
+                                          ctypes.c_int),
         "qlora_dequantize_nf4": ([wp, vp, vp], ctypes.c_int),
         "qlora_linear_fwd": ([wp, vp, i64, vp, vp, i32, f32, vp, vp, sz, vp], ctypes.c_int),
         "qlora_linear_bwd": ([wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, i32, vp, sz, vp],
@@ -141,15 +149,17 @@ def _ptr(t) -> Optional[int]:
 
 
 class PackedWeight:
-    """A frozen NF4 base weight living in device memory."""
+    """A frozen NF4 base weight living in device memory; ``dq_mean`` (an fp32
+    device tensor of one element) marks the mean-centred scale format."""
 
-    def __init__(self, codes, qscale, dq_step, N: int, K: int):
+    def __init__(self, codes, qscale, dq_step, N: int, K: int, dq_mean=None):
         self.codes, self.qscale, self.dq_step = codes, qscale, dq_step
+        self.dq_mean = dq_mean
         self.N, self.K = int(N), int(K)
 
     def struct(self) -> Nf4Weight:
         return Nf4Weight(self.codes.data_ptr(), self.qscale.data_ptr(),
-                         self.dq_step.data_ptr(), self.N, self.K)
+                         self.dq_step.data_ptr(), self.N, self.K, _ptr(self.dq_mean))
 
 
 def quantize_nf4(w) -> Tuple[object, object]:
@@ -191,6 +201,55 @@ def quantize_nf4_dq(w) -> Tuple[object, object, object, object]:
                                       _ptr(step), _stream_ptr()),
           "qlora_quantize_nf4_dq")
     return codes, absmax, q, step
+
+
+def _dqc_workspace(nb, device):
+    torch = _torch()
+    need = int(lib().qlora_dq_centred_workspace_bytes(nb))
+    return torch.empty(max(need, 256), dtype=torch.uint8, device=device), need
+
+
+def double_quant_centred(absmax) -> Tuple[object, object, object]:
+    """fp32 block scales -> (qscale uint8 [nb] two's-complement codes,
+    dq_step fp32 [ceil(nb/256)], dq_mean fp32 [1]): the mean-centred format."""
+    torch = _torch()
+    assert absmax.dtype == torch.float32 and absmax.is_cuda and absmax.is_contiguous()
+    nb = absmax.numel()
+    q = torch.empty(nb, dtype=torch.uint8, device=absmax.device)
+    step = torch.empty((nb + 255) // 256, dtype=torch.float32, device=absmax.device)
+    mean = torch.empty(1, dtype=torch.float32, device=absmax.device)
+    ws, need = _dqc_workspace(nb, absmax.device)
+    check(lib().qlora_double_quant_centred(_ptr(absmax), nb, _ptr(q), _ptr(step), _ptr(mean),
+                                           _ptr(ws), ws.numel(), _stream_ptr()),
+          "qlora_double_quant_centred")
+    return q, step, mean
+
+
+def quantize_nf4_dq_centred(w) -> Tuple[object, object, object, object, object]:
+    """fp32 device tensor -> (codes, absmax, qscale, dq_step, dq_mean): the
+    quantiser followed by the mean-centred double quantisation."""
+    torch = _torch()
+    assert w.dtype == torch.float32 and w.is_cuda and w.is_contiguous()
+    n = w.numel()
+    nb = (n + 63) // 64
+    codes = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(nb, dtype=torch.float32, device=w.device)
+    q = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    step = torch.empty((nb + 255) // 256, dtype=torch.float32, device=w.device)
+    mean = torch.empty(1, dtype=torch.float32, device=w.device)
+    ws, need = _dqc_workspace(nb, w.device)
+    check(lib().qlora_quantize_nf4_dq_centred(_ptr(w), n, _ptr(codes), _ptr(absmax), _ptr(q),
+                                              _ptr(step), _ptr(mean), _ptr(ws), ws.numel(),
+                                              _stream_ptr()),
+          "qlora_quantize_nf4_dq_centred")
+    return codes, absmax, q, step, mean
+
+
+def quantize_weight_centred(w) -> PackedWeight:
+    """fp32 [N, K] device weight -> PackedWeight in the mean-centred format."""
+    N, K = w.shape
+    codes, _, q, step, mean = quantize_nf4_dq_centred(w.contiguous().view(-1))
+    return PackedWeight(codes, q, step, N, K, dq_mean=mean)
 
 
 def quantize_weight(w) -> PackedWeight:

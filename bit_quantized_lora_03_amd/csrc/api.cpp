@@ -77,6 +77,7 @@ int check_weight(const qlora_nf4_weight* w) {
   if (w->N <= 0 || w->K <= 0) return QLORA_EINVAL;
   if (w->N % 64 || w->K % 64) return QLORA_ESHAPE;
   if (!aligned16(w->codes) || !aligned16(w->qscale) || !aligned16(w->dq_step)) return QLORA_EALIGN;
+  if (w->dq_mean && (reinterpret_cast<uintptr_t>(w->dq_mean) & 3)) return QLORA_EALIGN;
   return QLORA_OK;
 }
 
@@ -229,6 +230,7 @@ struct Wref {
   const float* step;
   const uint16_t* wbf;
   int64_t N, K;
+  const float* mean = nullptr;  // mean-centred scale format (or null)
   bool nf4() const { return wbf == nullptr; }
   const void* data() const { return nf4() ? static_cast<const void*>(codes) : wbf; }
   size_t bytes() const { return nf4() ? (size_t)N * K / 2 : (size_t)N * K * 2; }
@@ -288,7 +290,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
         r > 0 ? alpha / static_cast<float>(r) / (keep || drop ? 1.0f - pd : 1.0f) : 0.0f;
     if (ws.decode) {
       return hip_status(qlora::launch_decode_fwd(
-          w->codes, w->qscale, w->step, x, A, B, r, scale,
+          w->codes, w->qscale, w->step, w->mean, x, A, B, r, scale,
           ws.total > 0 ? at<float>(workspace, ws.part_off) : nullptr, ws.dsplits, y, M, N, K, L,
           s));
     }
@@ -306,7 +308,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
         return st;
     }
     float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
-    return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->step, w->wbf, x, xs, B, y,
+    return hip_status(qlora::launch_fwd_gemm(w->codes, w->qscale, w->step, w->mean, w->wbf, x, xs, B, y,
                                              part, M, N, K, r, L, s, f16));
   } catch (...) {
     return QLORA_EHIP;
@@ -406,7 +408,7 @@ int bwd_impl(const Wref* w, const uint16_t* x, const uint16_t* dy, int64_t M, co
     }
     if (dx) {
       float* part = ws.gpart > 0 ? at<float>(workspace, ws.part_off) : nullptr;
-      if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->step, w->wbf, keep, dy, gs,
+      if ((st = hip_status(qlora::launch_dx_gemm(w->codes, w->qscale, w->step, w->mean, w->wbf, keep, dy, gs,
                                                  A, dx, part, M, N, K, r, L, s, f16))) != QLORA_OK)
         return st;
     }
@@ -425,7 +427,7 @@ int linear_fwd_sourced(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, 
                        WorkspaceSource src, void* stream) {
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, 0.0f, y, nullptr, 0, stream, false, src);
 }
 
@@ -501,7 +503,7 @@ int qlora_linear_fwd_dropout_rng(const qlora_nf4_weight* w, const uint16_t* x, i
                                  void* workspace, size_t ws_bytes, void* stream) {
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   const qlora::PhiloxDrop d = philox_drop(p, seed, offset);
   return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, p, y, workspace, ws_bytes, stream, false,
                   nullptr, &d);
@@ -515,7 +517,7 @@ int qlora_linear_bwd_dropout_rng(const qlora_nf4_weight* w, const uint16_t* x,
                                  void* stream) {
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   const qlora::PhiloxDrop d = philox_drop(p, seed, offset);
   return bwd_impl(&wr, x, dy, M, A, B, r, alpha, nullptr, p, dx, dA, dB, accumulate, workspace,
                   ws_bytes, stream, false, &d);
@@ -584,6 +586,75 @@ int qlora_quantize_nf4_dq(const float* w, int64_t n_elems, uint8_t* codes, float
   }
 }
 
+size_t qlora_dq_centred_workspace_bytes(int64_t n_blocks) {
+  return n_blocks > 0 ? qlora::dq_centred_workspace_bytes(n_blocks) : 0;
+}
+
+// the checks shared by the two mean-centred entry points (absmax and the
+// outputs of the scale encoding)
+static int check_dq_centred(const float* absmax, int64_t nb, const uint8_t* qscale,
+                            const float* dq_step, const float* dq_mean, void* workspace,
+                            size_t ws_bytes) {
+  if (!absmax || !qscale || !dq_step || !dq_mean || !workspace) return QLORA_EINVAL;
+  if (!aligned16(absmax) || !aligned16(qscale) || !aligned16(dq_step) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(dq_mean) & 3))
+    return QLORA_EALIGN;
+  if (ws_bytes < qlora::dq_centred_workspace_bytes(nb)) return QLORA_EWORKSPACE;
+  const size_t ns = (size_t)((nb + 255) / 256) * 4, nw = qlora::dq_centred_workspace_bytes(nb);
+  const void* p[5] = {absmax, qscale, dq_step, dq_mean, workspace};
+  const size_t sz[5] = {(size_t)nb * 4, (size_t)nb, ns, 4, nw};
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(p[i], sz[i], p[j], sz[j])) return QLORA_EINVAL;
+  return QLORA_OK;
+}
+
+int qlora_double_quant_centred(const float* absmax, int64_t n_blocks, uint8_t* qscale,
+                               float* dq_step, float* dq_mean, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  try {
+    if (n_blocks < 0) return QLORA_EINVAL;
+    if (n_blocks == 0) return QLORA_OK;
+    const int st = check_dq_centred(absmax, n_blocks, qscale, dq_step, dq_mean, workspace,
+                                    ws_bytes);
+    if (st != QLORA_OK) return st;
+    return hip_status(qlora::launch_double_quant_centred(absmax, n_blocks, qscale, dq_step,
+                                                         dq_mean, workspace, as_stream(stream)));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
+int qlora_quantize_nf4_dq_centred(const float* w, int64_t n_elems, uint8_t* codes, float* absmax,
+                                  uint8_t* qscale, float* dq_step, float* dq_mean,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  try {
+    if (n_elems < 0) return QLORA_EINVAL;
+    if (n_elems == 0) return QLORA_OK;
+    if (!w || !codes) return QLORA_EINVAL;
+    if (!aligned16(w) || !aligned16(codes)) return QLORA_EALIGN;
+    const int64_t nb = (n_elems + 63) / 64;
+    int st = check_dq_centred(absmax, nb, qscale, dq_step, dq_mean, workspace, ws_bytes);
+    if (st != QLORA_OK) return st;
+    const size_t nw = (size_t)n_elems * 4, nc = (size_t)(n_elems + 1) / 2;
+    const void* outs[6] = {codes, absmax, qscale, dq_step, dq_mean, workspace};
+    const size_t osz[6] = {nc, (size_t)nb * 4, (size_t)nb, (size_t)((nb + 255) / 256) * 4, 4,
+                           qlora::dq_centred_workspace_bytes(nb)};
+    for (int i = 0; i < 6; ++i) {
+      if (overlap(w, nw, outs[i], osz[i])) return QLORA_EINVAL;
+      if (i > 0 && overlap(codes, nc, outs[i], osz[i])) return QLORA_EINVAL;
+    }
+    hipStream_t s = as_stream(stream);
+    if ((st = hip_status(qlora::launch_quantize(w, n_elems, codes, absmax, code_bins_arg(), s))) !=
+        QLORA_OK)
+      return st;
+    return hip_status(
+        qlora::launch_double_quant_centred(absmax, nb, qscale, dq_step, dq_mean, workspace, s));
+  } catch (...) {
+    return QLORA_EHIP;
+  }
+}
+
 static int dequantize_impl(const qlora_nf4_weight* w, uint16_t* out, void* stream, bool f16) {
   try {
     if (!w || !w->codes || !w->qscale || !w->dq_step || !out) return QLORA_EINVAL;
@@ -596,8 +667,9 @@ static int dequantize_impl(const qlora_nf4_weight* w, uint16_t* out, void* strea
     const size_t no = (size_t)n * 2;
     if (overlap(out, no, w->codes, (size_t)n / 2) || overlap(out, no, w->qscale, (size_t)n / 64))
       return QLORA_EINVAL;
-    return hip_status(qlora::launch_dequant(w->codes, w->qscale, w->dq_step, n / 64, out,
-                                            levels_arg(), as_stream(stream), f16));
+    if (w->dq_mean && (reinterpret_cast<uintptr_t>(w->dq_mean) & 3)) return QLORA_EALIGN;
+    return hip_status(qlora::launch_dequant(w->codes, w->qscale, w->dq_step, w->dq_mean, n / 64,
+                                            out, levels_arg(), as_stream(stream), f16));
   } catch (...) {
     return QLORA_EHIP;
   }
@@ -616,7 +688,7 @@ int qlora_linear_fwd_f16(const qlora_nf4_weight* w, const uint16_t* x, int64_t M
                          uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, 0.0f, y, workspace, ws_bytes, stream,
                   true);
 }
@@ -627,7 +699,7 @@ int qlora_linear_bwd_f16(const qlora_nf4_weight* w, const uint16_t* x, const uin
                          size_t ws_bytes, void* stream) {
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   return bwd_impl(&wr, x, dy, M, A, B, r, alpha, nullptr, 0.0f, dx, dA, dB, accumulate,
                   workspace, ws_bytes, stream, true);
 }
@@ -637,7 +709,7 @@ int qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t M, co
                      size_t ws_bytes, void* stream) {
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   return fwd_impl(&wr, x, M, A, B, r, alpha, nullptr, 0.0f, y, workspace, ws_bytes, stream);
 }
 
@@ -647,7 +719,7 @@ int qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_
                      void* stream) {
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   return bwd_impl(&wr, x, dy, M, A, B, r, alpha, nullptr, 0.0f, dx, dA, dB, accumulate,
                   workspace, ws_bytes, stream);
 }
@@ -679,7 +751,7 @@ int qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, int64
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
   if (!keep) return QLORA_EINVAL;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   return fwd_impl(&wr, x, M, A, B, r, alpha, keep, p, y, workspace, ws_bytes, stream);
 }
 
@@ -691,7 +763,7 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, const
   const int st = check_weight(w);
   if (st != QLORA_OK) return st;
   if (!keep) return QLORA_EINVAL;
-  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K};
+  const Wref wr{w->codes, w->qscale, w->dq_step, nullptr, w->N, w->K, w->dq_mean};
   return bwd_impl(&wr, x, dy, M, A, B, r, alpha, keep, p, dx, dA, dB, accumulate, workspace,
                   ws_bytes, stream);
 }
@@ -731,7 +803,8 @@ int qlora_merge_adapter(const qlora_nf4_weight* w, const float* w0, int64_t N, i
     if (overlap(out_f32, nf, out_bf16, nb)) return QLORA_EINVAL;
     const float scale = r > 0 ? alpha / (float)r : 0.0f;
     return hip_status(qlora::launch_merge(w ? w->codes : nullptr, w ? w->qscale : nullptr,
-                                          w ? w->dq_step : nullptr, w0, A, B, r, scale,
+                                          w ? w->dq_step : nullptr,
+                                          w ? w->dq_mean : nullptr, w0, A, B, r, scale,
                                           out_f32, out_bf16, N, K, levels_arg(),
                                           as_stream(stream)));
   } catch (...) {

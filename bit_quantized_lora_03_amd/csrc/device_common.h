@@ -122,10 +122,36 @@ __device__ __forceinline__ u32x4_t nf4_decode8(const Nf4Lut& t, uint32_t v) {
   return out;
 }
 
-// Decoded block scale s' = fp32(q * step): q (0..255) converts exactly and
-// the single fp32 product is rounded once.
+// The block-scale format of a weight.  Unsigned (the default): the byte q
+// is 0..255 and s' = fp32(q * step).  Mean-centred (the paper-style
+// variant): the byte is a two's-complement code and s' =
+// fp32(fp32(q * step) + mean).  One formula serves both: the signed value
+// is (q ^ sx) - sx with sx = 0x80 (centred) or 0 (unsigned), and the
+// unsigned format adds mu = +0, which leaves its non-negative product
+// unchanged.
+struct ScaleFmt {
+  uint32_t sx;
+  float mu;
+};
+__device__ __forceinline__ ScaleFmt scale_fmt(const float* dq_mean) {
+  ScaleFmt f;
+  f.sx = dq_mean ? 0x80u : 0u;
+  f.mu = dq_mean ? *dq_mean : 0.0f;
+  return f;
+}
+
+// Decoded block scale of the unsigned format: s' = fp32(q * step) (q
+// converts exactly; one rounding).
 __device__ __forceinline__ float nf4_block_scale(uint32_t q, float step) {
   return static_cast<float>(q) * step;
+}
+
+// Decoded block scale of either format: the code converts exactly, and the
+// product and the sum are each rounded once (never fused).
+__device__ __forceinline__ float nf4_block_scale(uint32_t q, float step, ScaleFmt f) {
+#pragma clang fp contract(off)
+  const float prod = static_cast<float>((int)(q ^ f.sx) - (int)f.sx) * step;
+  return prod + f.mu;
 }
 
 // ---------------------------------------------------------------------------

@@ -52,9 +52,10 @@ constexpr int WROW = 576;
 __device__ __forceinline__ int slab_swz(int row) { return ((row >> 2) & 3) << 4; }
 
 struct DxParams {
-  const uint8_t* codes;   // NF4 weight (WF = kWeightNf4)
+  const uint8_t* codes;   // NF4 weight (WF = kWeightNf4 or kWeightNf4Centred)
   const uint8_t* qscale;
   const float* step;
+  const float* dq_mean;   // the mean-centred scale format's mean (or null)
   const uint16_t* wbf;    // bf16 weight [N, K] (WF = kWeightBf16)
   const uint8_t* keep;    // LoRA dropout keep bits [M, K / 8] (DROP)
   const uint16_t* dy;
@@ -87,7 +88,8 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 // tile, MS = 2 the 256 x 128 tile for small-M shapes (twice the output tiles,
 // so half the reduction splits and half their fp32 partials).
 //
-// WF: the weight's format.  kWeightBf16 (the unquantised comparison layer)
+// WF: the weight's format.  kWeightNf4Centred decodes as kWeightNf4 with
+// the mean-centred format's block scale.  kWeightBf16 (the unquantised comparison layer)
 // loads each thread's 64 bf16 of the slab row instead of decoding a block;
 // the values reach the slab at the same points of the schedule.
 //
@@ -107,7 +109,8 @@ __device__ __forceinline__ int rk(int row, int chunk) {
 template <int MS, int WF, bool DROP, class DT, int KW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dx_gemm_kernel(DxParams p) {
-  constexpr bool NF4 = WF == kWeightNf4;
+  constexpr bool NF4 = WF != kWeightBf16;  // an NF4 weight (either scale format)
+  constexpr bool CTR = WF == kWeightNf4Centred;
   constexpr bool HALF = KW == 128;
   static_assert(KW == TILE || (HALF && NF4), "half blocks per thread need the NF4 weight");
   constexpr int NI = KW / 64;         // 32-column (k) MFMA tiles per wave
@@ -132,6 +135,7 @@ void dx_gemm_kernel(DxParams p) {
   const int64_t k0 = bw.n * KW;
   const int64_t m0 = bw.m * TM;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const ScaleFmt fmt = scale_fmt(CTR ? p.dq_mean : nullptr);
 
   f32x16_t acc[NI][MS];
 #pragma unroll
@@ -329,7 +333,7 @@ void dx_gemm_kernel(DxParams p) {
     load_dy(st0, Y[0]);
     store_dy(0, Y[0]);
     if constexpr (NF4) {
-      const Nf4Lut lut = nf4_make_lut<DT>(p.L, nf4_block_scale(C[0].q, C[0].st));
+      const Nf4Lut lut = nf4_make_lut<DT>(p.L, (CTR ? nf4_block_scale(C[0].q, C[0].st, fmt) : nf4_block_scale(C[0].q, C[0].st)));
 #pragma unroll
       for (int c = 0; c < NCH; ++c) store8(0, c, nf4_decode8(lut, word(C[0], c)));
     } else {
@@ -395,7 +399,7 @@ void dx_gemm_kernel(DxParams p) {
             dyt[nxt][rk((t >> 3) + 32 * (u - DEC), t & 7)] = Y[nxt][u - DEC];
           }
         } else if (u < 4) {
-          if (u == 0) sc = nf4_block_scale(cn.q, cn.st);
+          if (u == 0) sc = CTR ? nf4_block_scale(cn.q, cn.st, fmt) : nf4_block_scale(cn.q, cn.st);
           pk[2 * u] = DT::pack2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
           pk[2 * u + 1] = DT::pack2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
         } else if (u < 8) {
@@ -461,8 +465,40 @@ void dx_gemm_kernel(DxParams p) {
                                lane);
 }
 
+// block tile (k x tokens), dropout mask or not, compute type for a weight
+// format: fp16 with the NF4 weight and no mask only, the narrow tile with
+// the NF4 weight only
+template <int WF>
+static void launch_dx_kernel(const GemmConfig& cfg, bool f16, bool drop, dim3 grid,
+                             hipStream_t s, const DxParams& p) {
+  constexpr bool Q = WF != kWeightBf16;
+  auto go = [&](auto ms, auto kw) {
+    constexpr int MS = decltype(ms)::value, KW = decltype(kw)::value;
+    if constexpr (Q) {
+      if (f16) {
+        hipLaunchKernelGGL((dx_gemm_kernel<MS, WF, false, F16T, KW>), grid, dim3(256), 0, s, p);
+        return;
+      }
+    }
+    if (drop)
+      hipLaunchKernelGGL((dx_gemm_kernel<MS, WF, true, Bf16T, KW>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((dx_gemm_kernel<MS, WF, false, Bf16T, KW>), grid, dim3(256), 0, s, p);
+  };
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
+  if (cfg.tn != TILE) {
+    if constexpr (Q) go(I2(), std::integral_constant<int, 128>());
+  } else if (cfg.tm == 256) {
+    go(I4(), std::integral_constant<int, TILE>());
+  } else {
+    go(I2(), std::integral_constant<int, TILE>());
+  }
+}
+
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const uint16_t* wbf, const uint8_t* keep, const uint16_t* dy,
+                          const float* dq_mean, const uint16_t* wbf, const uint8_t* keep,
+                          const uint16_t* dy,
                           const uint16_t* gs, const uint16_t* A, uint16_t* dx, float* part,
                           int64_t M, int64_t N, int64_t K, int r, const Nf4Levels& L,
                           hipStream_t s, bool f16) {
@@ -475,6 +511,7 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.codes = codes;
   p.qscale = qscale;
   p.step = step;
+  p.dq_mean = dq_mean;
   p.wbf = wbf;
   p.keep = keep;
   p.dy = dy;
@@ -493,52 +530,12 @@ hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const flo
   p.L = L;
   const int64_t blocks = gemm_blocks(cfg, M, K);
   const dim3 grid((unsigned)blocks);
-  // block tile (k x tokens); weight format; dropout mask or not; compute
-  // type (fp16 with the NF4 weight and no mask only; the narrow tile with
-  // the NF4 weight only)
-  if (cfg.tn != TILE) {
-    if (f16)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, F16T, 128>), grid, dim3(256), 0,
-                         s, p);
-    else if (!drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, Bf16T, 128>), grid, dim3(256), 0,
-                         s, p);
-    else
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, true, Bf16T, 128>), grid, dim3(256), 0,
-                         s, p);
-  } else if (cfg.tm == 256) {
-    if (f16)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, F16T, 256>), grid, dim3(256), 0,
-                         s, p);
-    else if (nf4 && !drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, false, Bf16T, 256>), grid, dim3(256), 0,
-                         s, p);
-    else if (nf4)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightNf4, true, Bf16T, 256>), grid, dim3(256), 0,
-                         s, p);
-    else if (!drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, false, Bf16T, 256>), grid, dim3(256), 0,
-                         s, p);
-    else
-      hipLaunchKernelGGL((dx_gemm_kernel<4, kWeightBf16, true, Bf16T, 256>), grid, dim3(256), 0,
-                         s, p);
-  } else {
-    if (f16)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, F16T, 256>), grid, dim3(256), 0,
-                         s, p);
-    else if (nf4 && !drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, false, Bf16T, 256>), grid, dim3(256), 0,
-                         s, p);
-    else if (nf4)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightNf4, true, Bf16T, 256>), grid, dim3(256), 0,
-                         s, p);
-    else if (!drop)
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, false, Bf16T, 256>), grid, dim3(256), 0,
-                         s, p);
-    else
-      hipLaunchKernelGGL((dx_gemm_kernel<2, kWeightBf16, true, Bf16T, 256>), grid, dim3(256), 0,
-                         s, p);
-  }
+  if (!nf4)
+    launch_dx_kernel<kWeightBf16>(cfg, false, drop, grid, s, p);
+  else if (dq_mean)
+    launch_dx_kernel<kWeightNf4Centred>(cfg, f16, drop, grid, s, p);
+  else
+    launch_dx_kernel<kWeightNf4>(cfg, f16, drop, grid, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_reduce(cfg, part, M, K, dx, s, f16);

@@ -69,6 +69,7 @@ struct DecodeParams {
   const uint8_t* codes;
   const uint8_t* qscale;
   const float* step;
+  const float* dq_mean;  // the mean-centred scale format's mean (or null)
   const uint16_t* x;
   const uint16_t* A;
   float* part;
@@ -92,7 +93,8 @@ struct Blk {
 }  // namespace
 
 // XL: x lives in LDS for the whole reduction (few tokens; decode_x_in_lds)
-template <bool XL>
+// CTR: the weight has the mean-centred scale format
+template <bool XL, bool CTR>
 __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p) {
   // the tables start the kernel's LDS (at offset 0, so a lookup address
   // needs no base added); after the main loop the space holds the reduction
@@ -122,6 +124,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
   const int64_t n0 = tile * 32;
   const int64_t nrows = a_tile ? p.r : N;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const ScaleFmt fmt = scale_fmt(CTR ? p.dq_mean : nullptr);
   const int64_t n = n0 + lr;
   const bool row_ok = n < nrows;
   const bool tok_ok = lr < M;
@@ -206,7 +209,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       const u32x4_t c0 = stage[lr * 4 + ((2 * lg) ^ rsw)];
       const u32x4_t c1 = stage[lr * 4 + ((2 * lg + 1) ^ rsw)];
       // this lane's block table: entry c = bf16_rne(fp32(L[c] * s'))
-      const float sc = ok ? nf4_block_scale(S.q, S.st) : 0.0f;
+      const float sc =
+          ok ? (CTR ? nf4_block_scale(S.q, S.st, fmt) : nf4_block_scale(S.q, S.st)) : 0.0f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const uint32_t pk = pack_bf16x2(p.L.v[2 * q] * sc, p.L.v[2 * q + 1] * sc);
@@ -622,13 +626,15 @@ int decode_splits(int64_t M, int64_t N, int64_t K, int r) {
 }
 
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                             const uint16_t* x, const uint16_t* A, const uint16_t* B, int r,
+                             const float* dq_mean, const uint16_t* x, const uint16_t* A,
+                             const uint16_t* B, int r,
                              float scale, float* part, int splits, uint16_t* y, int64_t M,
                              int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s) {
   DecodeParams p;
   p.codes = codes;
   p.qscale = qscale;
   p.step = step;
+  p.dq_mean = dq_mean;
   p.x = x;
   p.A = A;
   p.part = part;
@@ -642,12 +648,19 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
   p.w_blocks = (N + 31) / 32;
   p.blocks = p.w_blocks + (r > 0 ? (int64_t)((r + 31) / 32) * p.sa : 0);
   p.L = L;
-  if (decode_x_in_lds(M, K))
-    hipLaunchKernelGGL(decode_main_kernel<true>, dim3((unsigned)p.blocks), dim3(WAVES * 64), 0, s,
-                       p);
-  else
-    hipLaunchKernelGGL(decode_main_kernel<false>, dim3((unsigned)p.blocks), dim3(WAVES * 64), 0, s,
-                       p);
+  const dim3 grid((unsigned)p.blocks), block(WAVES * 64);
+  const bool xl = decode_x_in_lds(M, K);
+  if (dq_mean) {
+    if (xl)
+      hipLaunchKernelGGL((decode_main_kernel<true, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_main_kernel<false, true>), grid, block, 0, s, p);
+  } else {
+    if (xl)
+      hipLaunchKernelGGL((decode_main_kernel<true, false>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_main_kernel<false, false>), grid, block, 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || r == 0) return e;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((N + kRedCols - 1) / kRedCols)),

@@ -53,9 +53,10 @@ constexpr int ROW_CHUNKS = KT / 8;  // 16-byte chunks per tile row
 constexpr int NSTAGE = 4;           // activation ring depth
 
 struct FwdParams {
-  const uint8_t* codes;   // NF4 weight (WF = kWeightNf4)
+  const uint8_t* codes;   // NF4 weight (WF = kWeightNf4 or kWeightNf4Centred)
   const uint8_t* qscale;
   const float* step;
+  const float* dq_mean;   // the mean-centred scale format's mean (or null)
   const uint16_t* wbf;    // bf16 weight [N, K] (WF = kWeightBf16)
   const uint16_t* x;
   const uint16_t* xs;
@@ -104,7 +105,8 @@ __device__ __forceinline__ void swap_halves(u32x4_t& a, u32x4_t& b, int v) {
 // number of output tiles for small-M shapes and so halves the k splits
 // (and their fp32 partials) needed to fill the chip.
 // WF: the weight's format.  kWeightNf4 decodes each thread's block as
-// described above; kWeightBf16 (the unquantised comparison layer) loads the
+// described above (kWeightNf4Centred likewise, with the mean-centred
+// format's block scale); kWeightBf16 (the unquantised comparison layer) loads the
 // 64 bf16 of the same row tile instead and skips the table and decode, so
 // the two share every other part of the kernel.
 // DT: the 16-bit compute type (Bf16T, or F16T for the fp16 variant).
@@ -120,7 +122,8 @@ __device__ __forceinline__ void swap_halves(u32x4_t& a, u32x4_t& b, int v) {
 template <int JT, int WF, class DT, int RW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(FwdParams p) {
-  constexpr bool NF4 = WF == kWeightNf4;
+  constexpr bool NF4 = WF != kWeightBf16;  // an NF4 weight (either scale format)
+  constexpr bool CTR = WF == kWeightNf4Centred;
   constexpr bool HALF = RW == 32;
   static_assert(RW == 64 || (HALF && NF4), "half rows per lane need the NF4 weight");
   constexpr int NI = RW / 32;   // 32-row MFMA tiles per wave
@@ -155,6 +158,7 @@ void fwd_gemm_kernel(FwdParams p) {
     return Xs(stage, 32 * j + lr, 4 * lg + kk);
   };
 
+  const ScaleFmt fmt = scale_fmt(CTR ? p.dq_mean : nullptr);
   // k tiles of this split
   const int64_t nkt = K / KT;
   const int64_t kt0 = nkt * z / nz, kt1 = nkt * (z + 1) / nz;
@@ -296,7 +300,7 @@ void fwd_gemm_kernel(FwdParams p) {
     auto table_unit = [&](const Codes& c, int u) {
       if constexpr (!NF4) return;
       else if (u < 4) {
-        if (u == 0) sc = nf4_block_scale(c.q, c.st);
+        if (u == 0) sc = CTR ? nf4_block_scale(c.q, c.st, fmt) : nf4_block_scale(c.q, c.st);
         pk[2 * u] = DT::pack2(p.L.v[4 * u] * sc, p.L.v[4 * u + 1] * sc);
         pk[2 * u + 1] = DT::pack2(p.L.v[4 * u + 2] * sc, p.L.v[4 * u + 3] * sc);
       } else {
@@ -661,9 +665,42 @@ hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M,
   return hipSuccess;
 }
 
+// block tile (tokens x n) and compute type for a weight format: fp16 and
+// the narrow tile with the NF4 weight only
+template <int WF>
+static void launch_fwd_kernel(const GemmConfig& cfg, bool f16, dim3 grid, hipStream_t s,
+                              const FwdParams& p) {
+  constexpr bool Q = WF != kWeightBf16;
+  if (cfg.tn != TILE_N) {
+    if constexpr (Q) {
+      if (f16)
+        hipLaunchKernelGGL((fwd_gemm_kernel<4, WF, F16T, 32>), grid, dim3(256), 0, s, p);
+      else
+        hipLaunchKernelGGL((fwd_gemm_kernel<4, WF, Bf16T, 32>), grid, dim3(256), 0, s, p);
+    }
+  } else if (cfg.tm == 256) {
+    if constexpr (Q) {
+      if (f16) {
+        hipLaunchKernelGGL((fwd_gemm_kernel<8, WF, F16T, 64>), grid, dim3(256), 0, s, p);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((fwd_gemm_kernel<8, WF, Bf16T, 64>), grid, dim3(256), 0, s, p);
+  } else {
+    if constexpr (Q) {
+      if (f16) {
+        hipLaunchKernelGGL((fwd_gemm_kernel<4, WF, F16T, 64>), grid, dim3(256), 0, s, p);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((fwd_gemm_kernel<4, WF, Bf16T, 64>), grid, dim3(256), 0, s, p);
+  }
+}
+
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                           const uint16_t* wbf, const uint16_t* x, const uint16_t* xs,
-                           const uint16_t* B, uint16_t* y, float* part, int64_t M, int64_t N,
+                           const float* dq_mean, const uint16_t* wbf, const uint16_t* x,
+                           const uint16_t* xs, const uint16_t* B, uint16_t* y, float* part,
+                           int64_t M, int64_t N,
                            int64_t K, int r, const Nf4Levels& L, hipStream_t s, bool f16) {
   const bool nf4 = wbf == nullptr;
   const GemmConfig cfg = gemm_config(M, N, K, nf4);
@@ -672,6 +709,7 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.codes = codes;
   p.qscale = qscale;
   p.step = step;
+  p.dq_mean = dq_mean;
   p.wbf = wbf;
   p.x = x;
   p.xs = xs;
@@ -689,28 +727,12 @@ hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const fl
   p.L = L;
   const int64_t blocks = gemm_blocks(cfg, M, N);
   const dim3 grid((unsigned)blocks);
-  // block tile (tokens x n); weight format; compute type (fp16 and the
-  // narrow tile with the NF4 weight only)
-  if (cfg.tn != TILE_N) {
-    if (f16)
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, F16T, 32>), grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, Bf16T, 32>), grid, dim3(256), 0, s, p);
-  } else if (cfg.tm == 256) {
-    if (f16)
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, F16T, 64>), grid, dim3(256), 0, s, p);
-    else if (nf4)
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightNf4, Bf16T, 64>), grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((fwd_gemm_kernel<8, kWeightBf16, Bf16T, 64>), grid, dim3(256), 0, s, p);
-  } else {
-    if (f16)
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, F16T, 64>), grid, dim3(256), 0, s, p);
-    else if (nf4)
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightNf4, Bf16T, 64>), grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((fwd_gemm_kernel<4, kWeightBf16, Bf16T, 64>), grid, dim3(256), 0, s, p);
-  }
+  if (!nf4)
+    launch_fwd_kernel<kWeightBf16>(cfg, false, grid, s, p);
+  else if (dq_mean)
+    launch_fwd_kernel<kWeightNf4Centred>(cfg, f16, grid, s, p);
+  else
+    launch_fwd_kernel<kWeightNf4>(cfg, f16, grid, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_gemm_reduce(cfg, part, M, N, y, s, f16);

@@ -28,10 +28,16 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* qscale,
 hipError_t launch_quantize_dq(const float* w, int64_t n, uint8_t* codes, float* absmax,
                               uint8_t* qscale, float* step, const Nf4CodeBins& bins,
                               hipStream_t s);
+// the mean-centred scale format: mean [1], step [groups], qscale (signed
+// codes) from the block scales; workspace of dq_centred_workspace_bytes
+size_t dq_centred_workspace_bytes(int64_t nb);
+hipError_t launch_double_quant_centred(const float* absmax, int64_t nb, uint8_t* qscale,
+                                       float* step, float* mean, void* workspace,
+                                       hipStream_t s);
 // out: bf16, or fp16 (f16) -- the same decode rounded to the compute type
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s,
-                          bool f16 = false);
+                          const float* dq_mean, int64_t nb, uint16_t* out, const Nf4Levels& L,
+                          hipStream_t s, bool f16 = false);
 
 // lora_kernels.hip -- rank-r kernels of the adapter path
 // lora_proj: out[m][j] = hi, out[m][r + j] = lo, the bf16 pair of
@@ -119,10 +125,13 @@ size_t gemm_partial_bytes(const GemmConfig& c, int64_t M, int64_t Nout);
 // bf16 weight wbf [N, K] (the unquantised layer, same kernel skeleton).
 // f16: the fp16 compute type (x, xs, B, y in fp16; the NF4 weight decoded
 // to fp16); only with the NF4 weight.
-constexpr int kWeightNf4 = 0, kWeightBf16 = 1;
+// kWeightNf4Centred: the NF4 weight with the mean-centred scale format
+// (dq_mean non-null); the same kernels, with that format's scale decode.
+constexpr int kWeightNf4 = 0, kWeightBf16 = 1, kWeightNf4Centred = 2;
 hipError_t launch_fwd_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                           const uint16_t* wbf, const uint16_t* x, const uint16_t* xs,
-                           const uint16_t* B, uint16_t* y, float* part, int64_t M, int64_t N,
+                           const float* dq_mean, const uint16_t* wbf, const uint16_t* x,
+                           const uint16_t* xs, const uint16_t* B, uint16_t* y, float* part,
+                           int64_t M, int64_t N,
                            int64_t K, int r, const Nf4Levels& L, hipStream_t s,
                            bool f16 = false);
 hipError_t launch_splitk_reduce(const float* part, int splits, int64_t count, uint16_t* out,
@@ -139,7 +148,8 @@ hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M,
 constexpr int kDecodeMaxM = 32;
 int decode_splits(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                             const uint16_t* x, const uint16_t* A, const uint16_t* B, int r,
+                             const float* dq_mean, const uint16_t* x, const uint16_t* A,
+                             const uint16_t* B, int r,
                              float scale, float* part, int splits, uint16_t* y, int64_t M,
                              int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s);
 
@@ -147,7 +157,8 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
 // gemm_config(M, K, N) (output M x K, reduction N)
 // keep (or null): LoRA dropout bits [M, K / 8] masking the adapter term.
 hipError_t launch_dx_gemm(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          const uint16_t* wbf, const uint8_t* keep, const uint16_t* dy,
+                          const float* dq_mean, const uint16_t* wbf, const uint8_t* keep,
+                          const uint16_t* dy,
                           const uint16_t* gs, const uint16_t* A, uint16_t* dx, float* part,
                           int64_t M, int64_t N, int64_t K, int r, const Nf4Levels& L,
                           hipStream_t s, bool f16 = false);
@@ -164,7 +175,8 @@ struct MergePlan {
 };
 MergePlan merge_plan(int64_t N, int64_t K);
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                        const float* w0, const uint16_t* A, const uint16_t* B, int r,
+                        const float* dq_mean, const float* w0, const uint16_t* A,
+                        const uint16_t* B, int r,
                         float scale, float* out_f32, uint16_t* out_bf16, int64_t N, int64_t K,
                         const Nf4Levels& L, hipStream_t s);
 

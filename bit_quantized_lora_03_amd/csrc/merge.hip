@@ -41,6 +41,7 @@ struct MergeArgs {
   const uint8_t* codes;   // NF4 base (or null)
   const uint8_t* qscale;
   const float* step;
+  const float* dq_mean;   // the mean-centred scale format's mean (or null)
   const float* w0;        // fp32 original base (or null)
   const uint16_t* A;      // [r, K] bf16
   const uint16_t* B;      // [N, r] bf16 (never null: any readable pointer when r = 0)
@@ -115,7 +116,7 @@ __device__ __forceinline__ void merge_tile(const MergeArgs& a, const Nf4Levels& 
                                            int64_t k0, int lane) {
   const int c = lane & 31, h = lane >> 5;
   Nf4Lut lut;
-  if constexpr (NF4) lut = nf4_make_lut(L, nf4_block_scale(in.q, in.st));
+  if constexpr (NF4) lut = nf4_make_lut(L, nf4_block_scale(in.q, in.st, scale_fmt(a.dq_mean)));
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     // zero-padded reduction steps (j >= r) multiply zeros: no guard needed
@@ -247,7 +248,8 @@ MergePlan merge_plan(int64_t N, int64_t K) {
 }
 
 hipError_t launch_merge(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                        const float* w0, const uint16_t* A, const uint16_t* B, int r,
+                        const float* dq_mean, const float* w0, const uint16_t* A,
+                        const uint16_t* B, int r,
                         float scale, float* out_f32, uint16_t* out_bf16, int64_t N, int64_t K,
                         const Nf4Levels& L, hipStream_t s) {
   const MergePlan p = merge_plan(N, K);
@@ -255,6 +257,7 @@ hipError_t launch_merge(const uint8_t* codes, const uint8_t* qscale, const float
   a.codes = codes;
   a.qscale = qscale;
   a.step = step;
+  a.dq_mean = dq_mean;
   a.w0 = w0;
   a.A = A;
   a.B = r > 0 ? B : reinterpret_cast<const uint16_t*>(codes ? (const void*)codes : (const void*)w0);

@@ -235,6 +235,123 @@ __global__ __launch_bounds__(256) void double_quant_kernel(
   }
 }
 
+static int grid_for(int64_t work_items, int per_block, int cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (int)g;
+}
+
+// ---------------------------------------------------------------------------
+// Mean-centred double quantisation (the paper-style scale format).  The mean
+// of all block scales is an fp64 sum in a fixed order -- each group's
+// scales in index order, the group sums in kDqcChunks contiguous chunks,
+// the chunk sums in chunk order -- so that it is reproducible bit for bit;
+// then each group codes d = fp32(s - mean) on the symmetric grid
+// step = fp32(max |d| / 127), q = clamp(rint(fp32(d / step)), -127, 127).
+// ---------------------------------------------------------------------------
+constexpr int kDqcChunks = 1024;
+
+// one lane per group: its scales summed in index order (fp64)
+__global__ __launch_bounds__(256) void dqc_group_sum_kernel(const float* __restrict__ absmax,
+                                                            int64_t nb,
+                                                            double* __restrict__ gsum) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t groups = (nb + 255) >> 8;
+  if (g >= groups) return;
+  const int64_t b0 = g << 8, b1 = b0 + 256 < nb ? b0 + 256 : nb;
+  double acc = 0.0;
+  int64_t b = b0;
+  for (; b + 4 <= b1; b += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(absmax + b);
+    acc += (double)v.x;
+    acc += (double)v.y;
+    acc += (double)v.z;
+    acc += (double)v.w;
+  }
+  for (; b < b1; ++b) acc += (double)absmax[b];
+  gsum[g] = acc;
+}
+
+// one workgroup: lane c sums chunk c of the group sums, lane 0 the chunks
+__global__ __launch_bounds__(kDqcChunks) void dqc_mean_kernel(const double* __restrict__ gsum,
+                                                              int64_t groups, int64_t nb,
+                                                              float* __restrict__ mean) {
+  __shared__ double chunk[kDqcChunks];
+  const int c = threadIdx.x;
+  const int64_t per = (groups + kDqcChunks - 1) / kDqcChunks;
+  const int64_t g0 = c * per, g1 = g0 + per < groups ? g0 + per : groups;
+  double acc = 0.0;
+  for (int64_t g = g0; g < g1; ++g) acc += gsum[g];
+  chunk[c] = acc;
+  __syncthreads();
+  if (c == 0) {
+    double total = 0.0;
+    for (int i = 0; i < kDqcChunks; ++i) total += chunk[i];
+    *mean = (float)(total / (double)nb);
+  }
+}
+
+// one wave per group, 4 scales per lane (the layout of double_quant_kernel)
+__global__ __launch_bounds__(256) void dqc_code_kernel(const float* __restrict__ absmax,
+                                                       int64_t nb,
+                                                       const float* __restrict__ mean,
+                                                       uint8_t* __restrict__ qscale,
+                                                       float* __restrict__ step_out) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int64_t groups = (nb + 255) >> 8;
+  const int64_t wave0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t wstride = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const float mu = *mean;
+  for (int64_t gidx = wave0; gidx < groups; gidx += wstride) {
+    const int64_t b0 = (gidx << 8) + 4 * lane;
+    float d[4];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d[i] = b0 + i < nb ? absmax[b0 + i] - mu : 0.0f;  // blocks past the end count 0
+      m = fmaxf(m, fabsf(d[i]));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float st = __fdiv_rn(m, 127.0f);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int q = 0;
+      if (st > 0.0f) q = (int)fminf(fmaxf(rintf(__fdiv_rn(d[i], st)), -127.0f), 127.0f);
+      packed |= ((uint32_t)q & 0xFFu) << (8 * i);
+    }
+    if (b0 + 4 <= nb) {
+      *reinterpret_cast<uint32_t*>(qscale + b0) = packed;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (b0 + i < nb) qscale[b0 + i] = (uint8_t)(packed >> (8 * i));
+    }
+    if (lane == 0) step_out[gidx] = st;
+  }
+}
+
+size_t dq_centred_workspace_bytes(int64_t nb) {
+  const int64_t groups = (nb + 255) >> 8;
+  return (size_t)((groups * 8 + 255) / 256 * 256);
+}
+
+hipError_t launch_double_quant_centred(const float* absmax, int64_t nb, uint8_t* qscale,
+                                       float* step, float* mean, void* workspace,
+                                       hipStream_t s) {
+  const int64_t groups = (nb + 255) >> 8;
+  double* gsum = static_cast<double*>(workspace);
+  hipLaunchKernelGGL(dqc_group_sum_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                     s, absmax, nb, gsum);
+  hipLaunchKernelGGL(dqc_mean_kernel, dim3(1), dim3(kDqcChunks), 0, s, gsum, groups, nb, mean);
+  const int grid = grid_for(groups, 4, 256 * 16);
+  hipLaunchKernelGGL(dqc_code_kernel, dim3(grid), dim3(256), 0, s, absmax, nb, mean, qscale,
+                     step);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Standalone dequantiser: one lane per 64-weight block (the decode routine
 // the GEMMs run on their tiles), 32 code bytes in, 128 bf16 bytes out.
@@ -243,26 +360,20 @@ __global__ __launch_bounds__(256) void double_quant_kernel(
 template <class DT>
 __global__ __launch_bounds__(256) void nf4_dequant_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ qscale,
-    const float* __restrict__ step, int64_t nb, uint16_t* __restrict__ out,
-    Nf4Levels L) {
+    const float* __restrict__ step, const float* __restrict__ dq_mean, int64_t nb,
+    uint16_t* __restrict__ out, Nf4Levels L) {
+  const ScaleFmt fmt = scale_fmt(dq_mean);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
     const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(codes + (b << 5));
     const u32x4_t c0 = cp[0], c1 = cp[1];
-    const Nf4Lut lut = nf4_make_lut<DT>(L, nf4_block_scale(qscale[b], step[b >> 8]));
+    const Nf4Lut lut = nf4_make_lut<DT>(L, nf4_block_scale(qscale[b], step[b >> 8], fmt));
     u32x4_t* op = reinterpret_cast<u32x4_t*>(out + (b << 6));
 #pragma unroll
     for (int i = 0; i < 4; ++i) op[i] = nf4_decode8(lut, c0[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) op[4 + i] = nf4_decode8(lut, c1[i]);
   }
-}
-
-static int grid_for(int64_t work_items, int per_block, int cap) {
-  int64_t g = (work_items + per_block - 1) / per_block;
-  if (g < 1) g = 1;
-  if (g > cap) g = cap;
-  return (int)g;
 }
 
 hipError_t launch_quantize(const float* w, int64_t n, uint8_t* codes, float* absmax,
@@ -291,15 +402,15 @@ hipError_t launch_double_quant(const float* absmax, int64_t nb, uint8_t* qscale,
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* qscale, const float* step,
-                          int64_t nb, uint16_t* out, const Nf4Levels& L, hipStream_t s,
-                          bool f16) {
+                          const float* dq_mean, int64_t nb, uint16_t* out, const Nf4Levels& L,
+                          hipStream_t s, bool f16) {
   const int grid = grid_for(nb, 256, 256 * 16);
   if (f16)
     hipLaunchKernelGGL(nf4_dequant_kernel<F16T>, dim3(grid), dim3(256), 0, s, codes, qscale, step,
-                       nb, out, L);
+                       dq_mean, nb, out, L);
   else
     hipLaunchKernelGGL(nf4_dequant_kernel<Bf16T>, dim3(grid), dim3(256), 0, s, codes, qscale,
-                       step, nb, out, L);
+                       step, dq_mean, nb, out, L);
   return hipGetLastError();
 }
 

@@ -72,14 +72,22 @@ extern "C" {
  *   codes   [N*K/2]           byte j = code(2j) | code(2j+1) << 4
  *   qscale  [N*K/64]          8-bit double-quantised block absmax
  *   dq_step [ceil(N*K/16384)] fp32 step of each group of 256 block scales
+ *   dq_mean NULL for the unsigned scale format; otherwise [1] fp32, the
+ *           tensor mean of the mean-centred format (qlora_double_quant_centred;
+ *           4-byte aligned, EALIGN).
  * Block b covers flattened elements [64b, 64b+64) and decodes with scale
- * s'_b = fp32(qscale[b] * dq_step[b/256]).                                  */
+ *   unsigned:     s'_b = fp32(qscale[b] * dq_step[b/256])
+ *   mean-centred: s'_b = fp32(fp32(int8(qscale[b]) * dq_step[b/256]) + dq_mean[0])
+ * (int8: the byte read as two's complement; the product and the sum are
+ * rounded separately).  Every call that takes a qlora_nf4_weight decodes
+ * either format.                                                           */
 typedef struct qlora_nf4_weight {
   const uint8_t* codes;
   const uint8_t* qscale;
   const float*   dq_step;
   int64_t        N;
   int64_t        K;
+  const float*   dq_mean;
 } qlora_nf4_weight;
 
 /* Blockwise NF4 quantisation.  [QLoRA / infivelines.com]: 16 levels at
@@ -118,8 +126,41 @@ int qlora_double_quant(const float* absmax, int64_t n_blocks, int32_t blocksize2
 int qlora_quantize_nf4_dq(const float* w, int64_t n_elems, uint8_t* codes, float* absmax,
                           uint8_t* qscale, float* dq_step, void* stream);
 
+/* Mean-centred double quantisation: the paper-style variant of the scale
+ * format.  [QLoRA -- the democratization event, the recipe]: double
+ * quantization as in the QLoRA paper the recipe cites, which centres the
+ * block scales on their mean so that a symmetric 8-bit code can be used;
+ * [QLoRA / infivelines.com]: groups of 256 scales.  The pages fix neither
+ * this format nor the reduction order, so both are this library's reading:
+ *   dq_mean [1] fp32: mu = fp32(T / n_blocks), T an fp64 sum -- each
+ *           group's scales in index order, the group sums in 1024
+ *           contiguous chunks of ceil(groups/1024) groups (in order), the
+ *           chunk sums in chunk order (the same bits on every run);
+ *   dq_step [ceil(n_blocks/256)] fp32: step = fp32(A / 127) with
+ *           A = max |fp32(absmax - mu)| over the group's blocks;
+ *   qscale  [n_blocks] two's-complement codes
+ *           q = clamp(rint(fp32(fp32(absmax - mu) / step)), -127, 127);
+ *           a group with A = 0 stores step 0 and q = 0.
+ * Decoding (every call on a qlora_nf4_weight with dq_mean set):
+ * s' = fp32(fp32(q * step) + mu).  Divisions are IEEE correctly rounded,
+ * rint rounds half to even.  workspace (16-byte aligned) must hold
+ * qlora_dq_centred_workspace_bytes(n_blocks) bytes (EWORKSPACE), no two
+ * buffers may overlap (EINVAL); n_blocks may be 0 (nothing is enqueued).
+ * Storage is that of the unsigned format plus the 4-byte mean.             */
+size_t qlora_dq_centred_workspace_bytes(int64_t n_blocks);
+int qlora_double_quant_centred(const float* absmax, int64_t n_blocks, uint8_t* qscale,
+                               float* dq_step, float* dq_mean, void* workspace, size_t ws_bytes,
+                               void* stream);
+/* qlora_quantize_nf4 (blocksize 64) followed by qlora_double_quant_centred
+ * on its absmax (written), with the workspace of
+ * qlora_dq_centred_workspace_bytes(ceil(n_elems/64)).                       */
+int qlora_quantize_nf4_dq_centred(const float* w, int64_t n_elems, uint8_t* codes, float* absmax,
+                                  uint8_t* qscale, float* dq_step, float* dq_mean,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
 /* Standalone dequantisation to bf16 (the same device function the GEMMs
- * use): out[i] = bf16_rne(fp32(L[code_i] * fp32(qscale[b] * dq_step[b/256]))).
+ * use): out[i] = bf16_rne(fp32(L[code_i] * s'_b)), s'_b the block's decoded
+ * scale in the weight's format (above).
  * [QLoRA / infivelines.com]: the base is dequantised to bf16.
  *   out  [N*K] bf16 (uint16_t patterns), row-major [N, K].
  * Requires N*K to be a multiple of 64.                                      */

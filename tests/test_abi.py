@@ -139,6 +139,48 @@ def test_quantize_dq_validation():
     assert f(P0, 128, P0 + 256, P2, P3, P4, None) == -1           # codes inside w
 
 
+P5 = 6 << 20
+P6 = 7 << 20
+
+
+def test_centred_double_quant_validation():
+    L = q.lib()
+    nb = 1000
+    need = L.qlora_dq_centred_workspace_bytes(nb)
+    assert need == 256                          # 4 groups x 8 bytes, rounded up to 256
+    assert L.qlora_dq_centred_workspace_bytes(0) == 0
+    assert L.qlora_dq_centred_workspace_bytes(256 * 5000) == 40192
+    f = L.qlora_double_quant_centred
+    # absmax at P0; qscale, step, mean, workspace at disjoint aligned places
+    assert f(P0, -1, P1, P2, P3, P4, need, None) == -1
+    assert f(P0, 0, None, None, None, None, 0, None) == 0          # empty: no-op
+    assert f(P0, nb, P1, P2, None, P4, need, None) == -1           # no mean
+    assert f(P0, nb, P1, P2, P3, None, need, None) == -1           # no workspace
+    assert f(P0, nb, P1, P2, P3 + 2, P4, need, None) == -3         # mean not 4-aligned
+    assert f(P0, nb, P1, P2, P3, P4 + 8, need, None) == -3         # workspace not 16-aligned
+    assert f(P0, nb, P1, P2, P3, P4, need - 1, None) == -5         # workspace too small
+    assert f(P0, nb, P1, P2, P0 + 64, P4, need, None) == -1        # mean inside absmax
+    assert f(P0, nb, P1, P2, P3, P1, need, None) == -1             # workspace over qscale
+    g = L.qlora_quantize_nf4_dq_centred
+    n = 64 * nb
+    assert g(P0, -1, P1, P2, P3, P4, P5, P6, need, None) == -1
+    assert g(P0, 0, None, None, None, None, None, None, 0, None) == 0
+    assert g(None, n, P1, P2, P3, P4, P5, P6, need, None) == -1
+    assert g(P0, n, P1 + 4, P2, P3, P4, P5, P6, need, None) == -3   # codes not aligned
+    assert g(P0, n, P1, P2, P3, P4, P5, P6, need - 8, None) == -5
+    assert g(P0, n, P0 + 1024, P2, P3, P4, P5, P6, need, None) == -1  # codes inside w
+    assert g(P0, n, P1, P2, P3, P4, P1 + 16, P6, need, None) == -1  # mean inside codes
+
+
+def test_centred_weight_mean_alignment():
+    L = q.lib()
+    w = _weight()
+    w.dq_mean = P3 + 2
+    assert L.qlora_dequantize_nf4(ctypes.byref(w), P4, None) == -3
+    assert L.qlora_linear_fwd(ctypes.byref(w), P4, 16, None, None, 0, 1.0, P0 + (64 << 20),
+                              None, 0, None) == -3
+
+
 def test_dequant_validation():
     L = q.lib()
     w = _weight()

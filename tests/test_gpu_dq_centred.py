@@ -1,0 +1,226 @@
+"""GPU parity of the mean-centred scale format, through the C ABI.
+
+* Quantiser: the codes and block scales (as the unsigned path) and the
+  centred qscale, step and mean bit-exact against the oracle -- ragged
+  lengths, one and several groups, a partial last group, more groups than
+  the mean's summation has chunks, constant and zero scales, the 65B-class
+  weight in full; both entry points (two calls and one pass).
+* Dequantisation of a centred weight bit-exact (bf16 and fp16).
+* Layer parity on a centred weight (the oracle's packed weight, so the GEMMs
+  are checked apart from the quantiser): one-hot probes read the decoded
+  weight back bit for bit through the tiled forward and dX GEMMs and the
+  few-token path; forward and backward (tiled and few-token shapes, with
+  LoRA dropout) within 2e-2 rms of the fp64 oracle (the bf16 rounding floor
+  where larger); the merge within its derived bound.
+Outputs sit between guard bytes.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import bit_quantized_lora_03_amd as q
+from bit_quantized_lora_03_amd import workloads
+from tests.gpu_util import Guarded, bf16_values, check_close, check_close_bf16, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _weight(n, seed, kind="normal"):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    if kind == "outliers":
+        w[rng.integers(0, n, max(1, n // 1000))] *= 10
+    elif kind == "constant":       # every block the same absmax
+        w = np.tile(np.linspace(-0.5, 0.5, 64, dtype=np.float32), (n + 63) // 64)[:n]
+    elif kind == "zeros":
+        w[:] = 0
+    return w
+
+
+def _oracle_encoding(w):
+    codes, packed, absmax = oracle.quantize_nf4(w)
+    qs, step, mu = oracle.double_quant_centred(absmax)
+    return packed, absmax, qs, step, mu
+
+
+def _check_quantiser(w, label):
+    import torch
+    n = w.size
+    print(f"quantise {label} n={n}", flush=True)
+    packed, absmax, qs, step, mu = _oracle_encoding(w)
+    wd = dev(w)
+    # one pass
+    c1, a1, q1, s1, m1 = q.quantize_nf4_dq_centred(wd)
+    # two calls
+    c2, a2 = q.quantize_nf4(wd)
+    q2, s2, m2 = q.double_quant_centred(a2)
+    torch.cuda.synchronize()
+    for tag, (c, a, qq, st, m) in (("one pass", (c1, a1, q1, s1, m1)),
+                                   ("two calls", (c2, a2, q2, s2, m2))):
+        assert np.array_equal(host(c), packed), f"{label} {tag}: codes"
+        assert np.array_equal(host(a).view(np.uint32), absmax.view(np.uint32)), f"{label} {tag}"
+        got_mu = host(m)[0]
+        assert got_mu.view(np.uint32) == np.float32(mu).view(np.uint32), \
+            f"{label} {tag}: mean {got_mu!r} != {mu!r}"
+        assert np.array_equal(host(st).view(np.uint32), step.view(np.uint32)), f"{label} {tag}"
+        gq = host(qq)
+        assert np.array_equal(gq, qs), \
+            f"{label} {tag}: {np.count_nonzero(gq != qs)} of {qs.size} codes differ"
+
+
+@pytest.mark.parametrize("n,kind", [
+    (64 * 37 + 5, "normal"),            # one partial group, a partial block
+    (64 * 256 * 3 + 64 * 17, "outliers"),
+    (64 * 256 * 2, "constant"),
+    (64 * 300, "zeros"),
+    (64 * 256 * 1100 + 64 * 9, "normal"),   # 1101 groups: two per summation chunk
+])
+def test_quantiser_bitexact(cuda, n, kind):
+    _check_quantiser(_weight(n, seed=n % 97, kind=kind), f"{kind}")
+
+
+def test_quantiser_bitexact_65b_weight(cuda):
+    """The 65B-class layer's 22016 x 8192 weight in full: the block scales
+    come from the oracle chunk by chunk (whole blocks), the centred encoding
+    from the oracle on all of them."""
+    import torch
+    L = workloads.layer_65b()
+    w = L.w.reshape(-1)
+    n = w.size
+    chunk = 64 * 256 * 512
+    absmax = np.concatenate([oracle.quantize_nf4(w[lo:lo + chunk])[2]
+                             for lo in range(0, n, chunk)])
+    qs, step, mu = oracle.double_quant_centred(absmax)
+    c, a, qq, st, m = q.quantize_nf4_dq_centred(dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a).view(np.uint32), absmax.view(np.uint32))
+    assert host(m)[0].view(np.uint32) == np.float32(mu).view(np.uint32)
+    assert np.array_equal(host(st).view(np.uint32), step.view(np.uint32))
+    assert np.array_equal(host(qq), qs)
+
+
+class CentredLayer:
+    """The oracle's NF4 encoding with centred scales, and its decoded W'."""
+
+    def __init__(self, w2d):
+        self.N, self.K = w2d.shape
+        self.packed, self.absmax, self.q, self.step, self.mu = _oracle_encoding(w2d.reshape(-1))
+        self.bits = oracle.dequant_nf4_centred_bits(self.packed, self.q, self.step, self.mu,
+                                                    self.N * self.K).reshape(self.N, self.K)
+        self.w_deq = oracle.bf16_bits_to_f64(self.bits)
+
+    def to_device(self):
+        import torch
+        return q.PackedWeight(dev(self.packed), dev(self.q), dev(self.step), self.N, self.K,
+                              dq_mean=torch.tensor([self.mu], dtype=torch.float32,
+                                                   device="cuda"))
+
+
+@pytest.mark.parametrize("N,K", [(320, 448), (2048, 1024)])
+def test_dequant_bitexact(cuda, N, K):
+    import torch
+    L = workloads.layer(1, N, K, 0, 1.0, seed=31, outlier_frac=0.001)
+    cl = CentredLayer(L.w)
+    pw = cl.to_device()
+    out = Guarded((N, K), torch.int16)
+    s = pw.struct()
+    import ctypes
+    q._lib.check(q.lib().qlora_dequantize_nf4(ctypes.byref(s), out.t.data_ptr(),
+                                              torch.cuda.current_stream().cuda_stream),
+                 "dequantize")
+    f16 = q.dequantize_f16(pw)
+    torch.cuda.synchronize()
+    out.check("dequant")
+    assert np.array_equal(host(out.t), cl.bits)
+    want16 = oracle.dequant_nf4_centred_f16_bits(cl.packed, cl.q, cl.step, cl.mu, N * K)
+    assert np.array_equal(host(f16).reshape(-1), want16)
+
+
+@pytest.mark.parametrize("M", [150, 8], ids=["tiled", "few-token"])
+def test_one_hot_probes_are_bit_exact(cuda, M):
+    """Base only, x = e_k rows: y[m, :] = W'[:, k_m] bit for bit; dy = e_n:
+    dX[m, :] = W'[n_m, :] (the tiled dX GEMM)."""
+    import torch
+    N, K = 320, 448
+    L = workloads.layer(1, N, K, 0, 1.0, seed=13, outlier_frac=0.001)
+    cl = CentredLayer(L.w)
+    pw = cl.to_device()
+    ks = (np.arange(M) * 3) % K
+    x = np.zeros((M, K), dtype=np.uint16)
+    x[np.arange(M), ks] = 0x3F80
+    y = host(q.linear_fwd(pw, dev(x), None, None, 1.0))
+    ns = (np.arange(M) * 2) % N
+    dy = np.zeros((M, N), dtype=np.uint16)
+    dy[np.arange(M), ns] = 0x3F80
+    dx, _, _ = q.linear_bwd(pw, None, dev(dy), None, None, 1.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(y, cl.bits[:, ks].T)
+    assert np.array_equal(host(dx), cl.bits[ns, :])
+
+
+# (M, N, K, r, alpha): tiled forward and dX, the few-token forward, a split
+# tail (more tiles than a round)
+SHAPES = [(300, 320, 448, 16, 32.0), (16, 512, 1024, 64, 16.0), (1, 256, 512, 8, 16.0),
+          (2100, 2304, 512, 32, 64.0)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])
+def test_layer_parity(cuda, shape):
+    import torch
+    M, N, K, r, alpha = shape
+    print(f"centred layer {shape}", flush=True)
+    L = workloads.layer(M, N, K, r, alpha, seed=17, outlier_frac=0.001)
+    cl = CentredLayer(L.w)
+    pw = cl.to_device()
+    x, dy, A, B = dev(L.x_bits), dev(L.dy_bits), dev(L.A_bits), dev(L.B_bits)
+    y = Guarded((M, N), torch.int16)
+    q.linear_fwd(pw, x, A, B, alpha, y=y.t)
+    gx = Guarded((M, K), torch.int16)
+    dx, dA, dB = q.linear_bwd(pw, x, dy, A, B, alpha, dx=gx.t)
+    torch.cuda.synchronize()
+    y.check("y")
+    gx.check("dX")
+    ry = oracle.lora_linear_fwd(L.f32("x"), cl.w_deq, L.f32("A"), L.f32("B"), alpha)
+    rdx, rdA, rdB = oracle.lora_linear_bwd(L.f32("x"), L.f32("dy"), cl.w_deq, L.f32("A"),
+                                           L.f32("B"), alpha)
+    check_close_bf16("y", bf16_values(host(y.t)), ry)
+    check_close_bf16("dX", bf16_values(host(gx.t)), rdx)
+    check_close("dA", host(dA), rdA)
+    check_close("dB", host(dB), rdB)
+
+
+def test_layer_parity_with_dropout(cuda):
+    import torch
+    M, N, K, r, alpha, p = 513, 384, 256, 64, 16.0, 0.1
+    L = workloads.layer(M, N, K, r, alpha, seed=19, outlier_frac=0.001)
+    cl = CentredLayer(L.w)
+    pw = cl.to_device()
+    x, dy, A, B = dev(L.x_bits), dev(L.dy_bits), dev(L.A_bits), dev(L.B_bits)
+    seed, offset = 77, 5
+    y = q.linear_fwd_dropout_rng(pw, x, A, B, alpha, p, seed, offset)
+    dx, dA, dB = q.linear_bwd_dropout_rng(pw, x, dy, A, B, alpha, p, seed, offset)
+    torch.cuda.synchronize()
+    keep = oracle.dropout_keep_philox(M, K, p, seed, offset)
+    pr = oracle.realised_dropout(p)
+    ry = oracle.lora_linear_fwd(L.f32("x"), cl.w_deq, L.f32("A"), L.f32("B"), alpha,
+                                keep=keep, p=pr)
+    rdx, rdA, rdB = oracle.lora_linear_bwd(L.f32("x"), L.f32("dy"), cl.w_deq, L.f32("A"),
+                                           L.f32("B"), alpha, keep=keep, p=pr)
+    check_close_bf16("y", bf16_values(host(y)), ry)
+    check_close_bf16("dX", bf16_values(host(dx)), rdx)
+    check_close("dA", host(dA), rdA)
+    check_close("dB", host(dB), rdB)
+
+
+def test_merge_on_a_centred_weight(cuda):
+    import torch
+    from tests.test_gpu_merge import check_merge
+    N, K, r, alpha = 320, 448, 24, 48.0
+    L = workloads.layer(1, N, K, r, alpha, seed=5, outlier_frac=0.001)
+    cl = CentredLayer(L.w)
+    pw = cl.to_device()
+    f32, b16, _ = q.merge_adapter(pw, dev(L.A_bits), dev(L.B_bits), alpha)
+    torch.cuda.synchronize()
+    w_m = oracle.merge_adapter(cl.w_deq, L.f32("A"), L.f32("B"), alpha)
+    check_merge("centred", L, w_m, host(f32), host(b16))
