@@ -167,8 +167,11 @@ def _recorded_traffic(workload, key):
     if not os.path.exists(path):
         return None
     for line in open(path):
-        if line.startswith("TRAFFIC "):
-            rec = json.loads(line[len("TRAFFIC "):])
+        if line.startswith("TRAFFIC {"):
+            try:
+                rec = json.loads(line[len("TRAFFIC "):])
+            except ValueError:
+                continue
             if rec.get("workload") == workload and rec.get("key") == key:
                 if rec.get("src") != _source_digest(key):
                     return None
