@@ -224,3 +224,31 @@ def test_merge_on_a_centred_weight(cuda):
     torch.cuda.synchronize()
     w_m = oracle.merge_adapter(cl.w_deq, L.f32("A"), L.f32("B"), alpha)
     check_merge("centred", L, w_m, host(f32), host(b16))
+
+
+@pytest.mark.parametrize("shape", [(300, 320, 448, 16, 32.0), (1024, 1024, 768, 16, 32.0)],
+                         ids=["ragged", "whole tiles"])
+def test_fp16_layer_parity(cuda, shape):
+    """The fp16 compute type on a centred weight: w' = fp16_rne(fp32(L[c] s'))
+    with the centred s', every 16-bit tensor in binary16."""
+    import torch
+    M, N, K, r, alpha = shape
+    L = workloads.layer(M, N, K, r, alpha, seed=29, outlier_frac=0.001)
+    cl = CentredLayer(L.w)
+    wb = oracle.dequant_nf4_centred_f16_bits(cl.packed, cl.q, cl.step, cl.mu, N * K)
+    wd = oracle.f16_bits_to_f64(wb).reshape(N, K)
+    t = {}
+    for k in ("x", "dy", "A", "B"):
+        bits = oracle.f16_rne_bits(L.f32(k).astype(np.float32))
+        t[k] = (bits, oracle.f16_bits_to_f64(bits))
+    pw = cl.to_device()
+    y = q.linear_fwd_f16(pw, dev(t["x"][0]), dev(t["A"][0]), dev(t["B"][0]), alpha)
+    dx, dA, dB = q.linear_bwd_f16(pw, dev(t["x"][0]), dev(t["dy"][0]), dev(t["A"][0]),
+                                  dev(t["B"][0]), alpha)
+    torch.cuda.synchronize()
+    ry = oracle.lora_linear_fwd(t["x"][1], wd, t["A"][1], t["B"][1], alpha)
+    rdx, rdA, rdB = oracle.lora_linear_bwd(t["x"][1], t["dy"][1], wd, t["A"][1], t["B"][1], alpha)
+    check_close("y", oracle.f16_bits_to_f64(host(y)), ry)
+    check_close("dX", oracle.f16_bits_to_f64(host(dx)), rdx)
+    check_close("dA", host(dA), rdA)
+    check_close("dB", host(dB), rdB)

@@ -24,14 +24,18 @@ SEQUENCES = {
     "up65b_then_ragged": [(4096, 22016, 8192, 64, 16.0), (300, 320, 448, 16, 32.0)],
     # the largest workload need (66.25 MiB), then a base-only ragged call
     "mlp_down_then_base_only": [(2048, 4096, 11008, 16, 32.0), (70, 448, 640, 0, 1.0)],
+    # weights in the mean-centred scale format: the tiled path, then the
+    # few-token path
+    "centred_tiled_then_decode": [(512, 4096, 4096, 16, 32.0), (8, 1024, 2048, 32, 64.0)],
 }
+CENTRED = {"centred_tiled_then_decode"}
 
 
-def _setup(shape, seed):
+def _setup(shape, seed, centred=False):
     import torch
     M, N, K, r, alpha = shape
     L = workloads.layer(M, N, K, r, alpha, seed=seed, outlier_frac=0.001)
-    pw = q.quantize_weight(dev(L.w))
+    pw = (q.quantize_weight_centred if centred else q.quantize_weight)(dev(L.w))
     x = dev(L.x_bits)
     A = dev(L.A_bits) if r else None
     B = dev(L.B_bits) if r else None
@@ -42,7 +46,7 @@ def _setup(shape, seed):
 @pytest.mark.parametrize("name", list(SEQUENCES))
 def test_noalloc_forward_equals_workspace_forward(cuda, name):
     import torch
-    calls = [_setup(shape, 70 + i) for i, shape in enumerate(SEQUENCES[name])]
+    calls = [_setup(shape, 70 + i, name in CENTRED) for i, shape in enumerate(SEQUENCES[name])]
     # the references first: they also load every kernel the calls use (the
     # runtime reserves memory for a kernel's code on its first launch)
     refs = [host(q.linear_fwd(pw, x, A, B, L.alpha)) for L, pw, x, A, B, _ in calls]
