@@ -136,6 +136,11 @@ void dx_gemm_kernel(DxParams p) {
   const int64_t m0 = bw.m * TM;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   const ScaleFmt fmt = scale_fmt(CTR ? p.dq_mean : nullptr);
+  // the merge selector's byte indices 0..3 in a register: the selector is
+  // then one v_and_or_b32 (a form that cannot carry two literal constants)
+  // instead of an and and an or
+  uint32_t kidx;
+  asm volatile("v_mov_b32 %0, 0x03020100" : "=v"(kidx));
 
   f32x16_t acc[NI][MS];
 #pragma unroll
@@ -379,14 +384,14 @@ void dx_gemm_kernel(DxParams p) {
       u32x4_t dv = zero;
       auto lookup_a = [&](uint32_t n) {  // low-byte planes of 4 codes
         nh = n & 0x07070707u;
-        pick = ((n >> 1) & 0x04040404u) | 0x03020100u;
-        la = perm(lut.lo[1], lut.lo[0], n);
+        pick = ((n >> 1) & 0x04040404u) | kidx;
+        la = perm(lut.lo[1], lut.lo[0], nh);
         lb = perm(lut.lo[3], lut.lo[2], nh);
       };
       auto lookup_b = [&](uint32_t n, uint32_t& o01, uint32_t& o23) {  // high bytes, merge
         const uint32_t lo = perm(lb, la, pick);
         const uint32_t hi =
-            perm(perm(lut.hi[3], lut.hi[2], nh), perm(lut.hi[1], lut.hi[0], n), pick);
+            perm(perm(lut.hi[3], lut.hi[2], nh), perm(lut.hi[1], lut.hi[0], nh), pick);
         o01 = perm(hi, lo, 0x05010400u);
         o23 = perm(hi, lo, 0x07030602u);
       };
@@ -411,9 +416,12 @@ void dx_gemm_kernel(DxParams p) {
           const uint32_t v = word(cn, c);
           switch (w) {
             case 0: {
-              const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
-              dn0 = perm(od, ev, 0x05010400u);  // codes 0..3 of the word, one per byte
-              dn1 = perm(od, ev, 0x07030602u);  // codes 4..7
+              // codes 0..3 (dn0) and 4..7 (dn1) of the word, one per byte in
+              // the low nibble; the high nibbles carry the neighbouring code,
+              // which no lookup reads (they use bits 0..2, the merge bit 3)
+              const uint32_t od = v >> 4;
+              dn0 = perm(od, v, 0x05010400u);
+              dn1 = perm(od, v, 0x07030602u);
               break;
             }
             case 1: lookup_a(dn0); break;
