@@ -126,7 +126,8 @@ void dx_gemm_kernel(DxParams p) {
   char* const wbase = reinterpret_cast<char*>(&lds[0]);
   u32x4_t(*dyt)[TM * ROW_CHUNKS] = reinterpret_cast<u32x4_t(*)[TM * ROW_CHUNKS]>(&lds[WT_U4]);
   const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: scalar addressing
+  const int lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int wk = wave & 1, wm = wave >> 1;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m_tiles = (M + TM - 1) / TM, k_tiles = (K + KW - 1) / KW;

@@ -140,7 +140,8 @@ void fwd_gemm_kernel(FwdParams p) {
   constexpr int LDS_U4 = NSTAGE * XST > EPI ? NSTAGE * XST : EPI;
   __shared__ u32x4_t lds[LDS_U4];
   const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: scalar addressing
+  const int lane = t & 63, lr = lane & 31, lg = lane >> 5;
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t m_tiles = (M + TM - 1) / TM, n_tiles = (N + TN - 1) / TN;
   const BlockWork bw = block_work(blockIdx.x, (int64_t)gridDim.x, m_tiles, n_tiles, p.splits,
