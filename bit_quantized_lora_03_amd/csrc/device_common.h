@@ -211,6 +211,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// The same with a wave-uniform part of the offset in the scalar operand
+// (soff must be uniform).  The range check covers the lane offset only, so
+// soff may not carry a term that is meant to push a lane out of range.
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buffer_load1(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
 
 // Block-to-tile mapping for a 1-D grid of `total` blocks.  Consecutive
 // workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2),

@@ -167,8 +167,18 @@ void dx_gemm_kernel(DxParams p) {
   // dy rows m0 + (t >> 3) + 32 j through a buffer descriptor: rows past M
   // read as zero
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.dy, (uint32_t)(M * N * 2));
-  const uint32_t yoff = (uint32_t)(((m0 + (t >> 3)) * N + 8 * (t & 7)) * 2);
-  const uint32_t yrow_step = (uint32_t)(32 * N * 2);
+  // lane offsets of the thread's XR dy rows (fixed), the slab's column in
+  // the scalar offset
+  uint32_t yvoff[XR];
+#pragma unroll
+  for (int j = 0; j < XR; ++j)
+    yvoff[j] = (uint32_t)(((m0 + (t >> 3) + 32 * j) * N + 8 * (t & 7)) * 2);
+  // NF4 codes and scale bytes likewise: the lane's element offset within a
+  // slab is fixed, the slab's first element is uniform
+  const __amdgpu_buffer_rsrc_t cres = make_rsrc(p.codes, (uint32_t)((N * K) >> 1));
+  const __amdgpu_buffer_rsrc_t qres = make_rsrc(p.qscale, (uint32_t)((N * K) >> 6));
+  const int64_t lidx = (int64_t)wr * K + kcol;
+  const uint32_t cvoff = (uint32_t)(lidx >> 1), qvoff = (uint32_t)(lidx >> 6);
 
   // The scale byte and its step stay raw until the tile is decoded (an
   // iteration later): forming s' here would make the wave wait for this
@@ -198,28 +208,24 @@ void dx_gemm_kernel(DxParams p) {
       return 0u;
   };
   auto load_codes = [&](int64_t st, Codes& c) {
-    // first element of the thread's values (a whole block, or half of one)
-    const int64_t idx = (st * RT + wr) * K + kcol;
-    if constexpr (HALF) {
-      c.c0 = *reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
-      c.q = p.qscale[idx >> 6];
-      c.st = p.step[idx >> 14];
-    } else if constexpr (NF4) {
-      const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(p.codes + (idx >> 1));
-      c.c0 = cp[0];
-      c.c1 = cp[1];
-      c.q = p.qscale[idx >> 6];
-      c.st = p.step[idx >> 14];
+    // first element of the thread's values (a whole block, or half of one):
+    // slab base sb (a multiple of 64 K) + the lane's lidx
+    const int64_t sb = st * RT * K;
+    if constexpr (NF4) {
+      c.c0 = buffer_load16(cres, cvoff, (uint32_t)(sb >> 1));
+      if constexpr (!HALF) c.c1 = buffer_load16(cres, cvoff + 16u, (uint32_t)(sb >> 1));
+      c.q = buffer_load1(qres, qvoff, (uint32_t)(sb >> 6));
+      c.st = p.step[(sb + lidx) >> 14];
     } else {
+      const int64_t idx = sb + lidx;
       const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(p.wbf + idx);
 #pragma unroll
       for (int i = 0; i < 8; ++i) c.w[i] = wp[i];
     }
   };
   auto load_dy = [&](int64_t st, u32x4_t (&yr)[XR]) {
-    const uint32_t o = yoff + (uint32_t)(st * RT * 2);
 #pragma unroll
-    for (int j = 0; j < XR; ++j) yr[j] = buffer_load16(yres, o + j * yrow_step);
+    for (int j = 0; j < XR; ++j) yr[j] = buffer_load16(yres, yvoff[j], (uint32_t)(st * RT * 2));
   };
   auto store_dy = [&](int stage, const u32x4_t (&yr)[XR]) {
 #pragma unroll

@@ -175,9 +175,14 @@ void fwd_gemm_kernel(FwdParams p) {
   // this thread decodes weight row n0 + t (clamped), or with half rows the
   // half lg of row n0 + 32 wave + lr
   const int64_t wrow = clamp_row(HALF ? n0 + 32 * wave + lr : n0 + t, N);
-  const uint8_t* wcodes = NF4 ? p.codes + ((wrow * K) >> 1) + (HALF ? 16 * lg : 0) : nullptr;
   const uint16_t* wvals = NF4 ? nullptr : p.wbf + wrow * K;
   const int64_t wblk0 = (wrow * K) >> 6;
+  // codes and scale bytes through buffer descriptors: the row's offset is
+  // the lane's (fixed), the k tile's the uniform scalar offset
+  const __amdgpu_buffer_rsrc_t cres = make_rsrc(p.codes, (uint32_t)((N * K) >> 1));
+  const __amdgpu_buffer_rsrc_t qres = make_rsrc(p.qscale, (uint32_t)((N * K) >> 6));
+  const uint32_t cvoff = (uint32_t)((wrow * K) >> 1) + (HALF ? 16u * (uint32_t)lg : 0u);
+  const uint32_t qvoff = (uint32_t)wblk0;
 
   // The x tile reaches LDS by DMA (buffer loads that write LDS directly):
   // instruction q of wave w fills the 1 KiB region R = XR w + q of a stage,
@@ -222,17 +227,14 @@ void fwd_gemm_kernel(FwdParams p) {
       std::conditional_t<NF4, std::conditional_t<HALF, CodesHalf, CodesNf4>, WordsBf16>;
   auto load_codes = [&](int64_t kt, Codes& c) {
     if constexpr (HALF) {
-      c.c = *reinterpret_cast<const u32x4_t*>(wcodes + kt * (KT / 2));
-      const int64_t b = wblk0 + kt;
-      c.q = p.qscale[b];
-      c.st = p.step[b >> 8];
+      c.c = buffer_load16(cres, cvoff, (uint32_t)(kt * (KT / 2)));
+      c.q = buffer_load1(qres, qvoff, (uint32_t)kt);
+      c.st = p.step[(wblk0 + kt) >> 8];
     } else if constexpr (NF4) {
-      const u32x4_t* cp = reinterpret_cast<const u32x4_t*>(wcodes + kt * (KT / 2));
-      c.c0 = cp[0];
-      c.c1 = cp[1];
-      const int64_t b = wblk0 + kt;
-      c.q = p.qscale[b];
-      c.st = p.step[b >> 8];
+      c.c0 = buffer_load16(cres, cvoff, (uint32_t)(kt * (KT / 2)));
+      c.c1 = buffer_load16(cres, cvoff + 16u, (uint32_t)(kt * (KT / 2)));
+      c.q = buffer_load1(qres, qvoff, (uint32_t)kt);
+      c.st = p.step[(wblk0 + kt) >> 8];
     } else {
       const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(wvals + kt * KT);
 #pragma unroll

@@ -135,19 +135,22 @@ def test_backward_accumulate_and_skip_dx(cuda):
     check_close("dB - dB0", dB.astype(np.float64) - dB0, rdB)
 
 
-def test_one_hot_probes_are_bit_exact(cuda):
+@pytest.mark.parametrize("N,K,step", [(320, 448, 3), (4096, 4096, 517)],
+                         ids=["tiled", "few-token"])
+def test_one_hot_probes_are_bit_exact(cuda, N, K, step):
     """Base only, x = one-hot rows e_k: y[m, :] = W'[:, k_m] bit for bit (one
-    exact bf16 product per output).  dy = e_n: dX[m, :] = W'[n_m, :]."""
+    exact bf16 product per output; at 4096 x 4096 with 8 rows, the few-token
+    path over four chunks with x in registers).  dy = e_n: dX[m, :] =
+    W'[n_m, :]."""
     import torch
-    N, K = 320, 448
     L = _layer(1, N, K, 0, 1.0)
     ol = OracleLayer(L.w)
     pw = ol.to_device()
-    ks = np.arange(0, K, 3)
+    ks = np.arange(0, K, step)
     x = np.zeros((ks.size, K), dtype=np.uint16)
     x[np.arange(ks.size), ks] = 0x3F80                     # bf16 1.0
     y = host(q.linear_fwd(pw, dev(x), None, None, 1.0))
-    ns = np.arange(0, N, 2)
+    ns = np.arange(0, N, 2 if N < 1024 else 263)
     dy = np.zeros((ns.size, N), dtype=np.uint16)
     dy[np.arange(ns.size), ns] = 0x3F80
     dx, _, _ = q.linear_bwd(pw, None, dev(dy), None, None, 1.0)
@@ -217,8 +220,9 @@ def test_empty_token_batch(cuda):
 
 
 @pytest.mark.parametrize("shape", [(300, 320, 448, 16, 32.0), (8, 256, 512, 64, 16.0),
-                                   (1000, 4096, 1024, 64, 16.0)],
-                         ids=["main", "decode", "split-down-projection"])
+                                   (8, 4096, 4096, 16, 16.0), (1000, 4096, 1024, 64, 16.0)],
+                         ids=["main", "decode-x-in-lds", "decode-x-in-registers",
+                              "split-down-projection"])
 def test_graph_replay_matches_eager(cuda, shape):
     """The whole fwd + bwd captured in one HIP graph: every replay (with
     eager work and synchronisations between replays) equals the eager run
