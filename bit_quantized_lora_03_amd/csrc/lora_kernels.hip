@@ -685,28 +685,38 @@ hipError_t launch_dropout_mask(const PhiloxDrop& drop, int64_t M, int64_t K, uin
 }
 
 // ---------------------------------------------------------------------------
-// lora_grad: grid = (ldg0 + ldg1) / 64 blocks, 512 threads.  A block owns 64
-// columns g0 .. g0 + 63 of the big operand G (dy for dB, x for dA), all r
-// columns of the small operand S (in chunks of RC = 16 JT) and every token.
-// Wave w takes the 32-token steps w, w + 8, ...: it stores the step's G rows
-// (tokens x 64 columns, as loaded) in its slab and reads 16 x 32 MFMA
-// operands back transposed (G columns as rows, 8 consecutive tokens per
-// lane); S comes from the transposed copy ST [2r][Mp] as direct 16-byte
-// loads, hi and lo as two MFMAs on the same G operand.
+// lora_grad: grid = (ldg0 + ldg1) / CT blocks, 512 threads.  A block owns CT
+// = 64 CW columns g0 .. g0 + CT - 1 of the big operand G (dy for dB, x for
+// dA), all r columns of the small operand S (in chunks of RC = 16 JT) and
+// every token.  Wave w takes the 32-token steps w, w + 8, ...: it stores the
+// step's G rows (tokens x CT columns, as loaded) in its slab and reads
+// 16 x 32 MFMA operands back transposed (G columns as rows, 8 consecutive
+// tokens per lane); S comes from the transposed copy ST [2r][Mp] as direct
+// 16-byte loads, hi and lo as two MFMAs on the same G operand.  A load of G
+// covers 8 / CW token rows x 128 CW contiguous bytes: with CW = 2 the runs
+// of 256 bytes per row stream from HBM markedly faster than runs of 128
+// (taken when the jobs' columns fill most CUs with the wider tiles).
 // ---------------------------------------------------------------------------
 // DROP: the jobs may carry a keep-mask on G (LoRA dropout; see keep8).
-template <int JT, bool DROP, class DT>
-__global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, LoraGradJob j1,
+template <int JT, bool DROP, class DT, int CW>
+__global__ __launch_bounds__(64 * (CW == 1 ? kWaves : 4)) void lora_grad_kernel(LoraGradJob j0, LoraGradJob j1,
                                                              int64_t blocks0, int64_t M, int r,
                                                              int accumulate) {
   constexpr int RC = 16 * JT;
-  constexpr int GS = 64 + 8;                        // slab row: 64 bf16 + 16 bytes of pad
+  constexpr int CT = 64 * CW;                       // G columns of the block
+  // waves per block: 8, or 4 with the wide tile (one per SIMD: its
+  // accumulators and two steps of loads need the whole register file)
+  constexpr int NW = CW == 1 ? kWaves : 4;
+  constexpr int NQ = 4 * CW;                        // G loads per step (and 16-column tiles)
+  // slab row: CT bf16 + pad; row strides of 36 dwords mod 64 banks keep the
+  // transposed reads conflict-free
+  constexpr int GS = CW == 1 ? 64 + 8 : CT + 72;
   constexpr int SLAB = 32 * GS;                     // bf16 per wave
   // token steps per batch of loads (one with a keep-mask: its bytes would
   // otherwise push the r <= 32 variant past its registers)
   constexpr int BS = (JT == 4 || DROP) ? 1 : 2;
   constexpr int REDS = RC + 4;
-  constexpr int SLAB_BYTES = kWaves * SLAB * 2, RED_BYTES = kWaves * 16 * REDS * 4;
+  constexpr int SLAB_BYTES = NW * SLAB * 2, RED_BYTES = NW * 16 * REDS * 4;
   __shared__ __align__(16) char lds[SLAB_BYTES > RED_BYTES ? SLAB_BYTES : RED_BYTES];
 
   const int t = threadIdx.x, lane = t & 63;
@@ -715,11 +725,11 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
   const bool second = (int64_t)blockIdx.x >= blocks0;
   const LoraGradJob J = uniform_job(second ? j1 : j0);
   const int64_t ldg = J.ldg;
-  const int64_t g0 = 64 * (second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x);
+  const int64_t g0 = CT * (second ? (int64_t)blockIdx.x - blocks0 : (int64_t)blockIdx.x);
   const int i = lane & 15, kg = lane >> 4;
   const int64_t Mp = pad32(M);
   const int64_t nst = Mp / 32;
-  const int64_t cnt = nst > wave ? (nst - wave + kWaves - 1) / kWaves : 0;
+  const int64_t cnt = nst > wave ? (nst - wave + NW - 1) / NW : 0;
   uint16_t* slab = reinterpret_cast<uint16_t*>(lds) + wave * SLAB;
   float* red = reinterpret_cast<float*>(lds);
   const __amdgpu_buffer_rsrc_t gres = make_rsrc(J.G, (uint32_t)(M * ldg * 2));
@@ -728,37 +738,38 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
   const KeepBits kp = keep_bits(J.keep, M * ldg / 8);
 
   for (int jc = 0; jc < r; jc += RC) {
-    f32x4_t acc[4][JT];
+    f32x4_t acc[NQ][JT];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < NQ; ++a)
 #pragma unroll
       for (int b = 0; b < JT; ++b) acc[a][b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // G piece p = lane + 64 q of a step: token p / 8, 8 columns at 8 (p mod 8)
-    uint32_t goff[4], kgoff[4], soff[JT];
+    // G piece p = lane + 64 q of a step: token p / (8 CW), 8 columns at
+    // 8 (p mod 8 CW)
+    uint32_t goff[NQ], kgoff[NQ], soff[JT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int p = lane + 64 * q;
-      goff[q] = (uint32_t)((((p >> 3) * ldg) + g0 + 8 * (p & 7)) * 2);
-      kgoff[q] = (uint32_t)((p >> 3) * (ldg / 8) + g0 / 8 + (p & 7));  // the piece's keep byte
+    for (int q = 0; q < NQ; ++q) {
+      const int p = lane + 64 * q, tk = p / (8 * CW), pc = p % (8 * CW);
+      goff[q] = (uint32_t)(((tk * ldg) + g0 + 8 * pc) * 2);
+      kgoff[q] = (uint32_t)(tk * (ldg / 8) + g0 / 8 + pc);  // the piece's keep byte
     }
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt)
       soff[jt] = (uint32_t)(((int64_t)(jc + 16 * jt + i) * Mp + 8 * kg) * 2);
     struct Batch {
-      u32x4_t g[BS][4];
+      u32x4_t g[BS][NQ];
       u32x4_t sh[BS][JT], sl[BS][JT];
-      uint32_t kb[BS][4];
+      uint32_t kb[BS][NQ];
     };
     auto load = [&](int64_t u0, Batch& R) {
 #pragma unroll
       for (int bb = 0; bb < BS; ++bb) {
         const int64_t u = u0 + bb;
         const bool ok = u < cnt;
-        const uint32_t t0 = (uint32_t)(32 * (wave + kWaves * u));
+        const uint32_t t0 = (uint32_t)(32 * (wave + NW * u));
         // the G row is part of the lane offset (rows past M read as zero)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < NQ; ++q) {
           R.g[bb][q] = ldb(gres, ok ? goff[q] + t0 * (uint32_t)ldg * 2 : kOff, 0);
           if constexpr (DROP)
             R.kb[bb][q] = ldb8(kp.res, ok ? kgoff[q] + t0 * (uint32_t)(ldg / 8) : kOff, 0) | kp.all;
@@ -775,13 +786,13 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
 #pragma unroll
       for (int bb = 0; bb < BS; ++bb) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < NQ; ++q) {
           const int p = lane + 64 * q;
-          *reinterpret_cast<u32x4_t*>(slab + (p >> 3) * GS + 8 * (p & 7)) =
+          *reinterpret_cast<u32x4_t*>(slab + (p / (8 * CW)) * GS + 8 * (p % (8 * CW))) =
               DROP ? keep8(R.g[bb][q], R.kb[bb][q]) : R.g[bb][q];
         }
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
+        for (int gi = 0; gi < NQ; ++gi) {
           const u32x4_t a = read_tr8(slab, GS, 8 * kg, 16 * gi, i);
 #pragma unroll
           for (int jt = 0; jt < JT; ++jt) {
@@ -808,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
     // of G-column tile gi; one tile's wave sums at a time
     const int R = r - jc < RC ? r - jc : RC;
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
+    for (int gi = 0; gi < NQ; ++gi) {
       __syncthreads();  // slabs (first tile) or the last tile's sums are done
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt)
@@ -816,13 +827,13 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
         for (int v = 0; v < 4; ++v)
           red[(wave * 16 + 4 * kg + v) * REDS + 16 * jt + i] = acc[gi][jt][v];
       __syncthreads();
-      for (int e = t; e < 16 * R; e += kThreads) {
+      for (int e = t; e < 16 * R; e += 64 * NW) {
         // consecutive threads write consecutive addresses of C
         const int gl = J.transposed ? (e & 15) : e / R;
         const int j = J.transposed ? (e >> 4) : e % R;
         float sum = red[gl * REDS + j];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) sum += red[(w * 16 + gl) * REDS + j];
+        for (int w = 1; w < NW; ++w) sum += red[(w * 16 + gl) * REDS + j];
         const int64_t g = g0 + 16 * gi + gl;
         const int jo = jc + j;
         float* c = J.transposed ? J.C + (int64_t)jo * ldg + g : J.C + g * r + jo;
@@ -833,21 +844,36 @@ __global__ __launch_bounds__(kThreads) void lora_grad_kernel(LoraGradJob j0, Lor
   }
 }
 
+template <bool DROP, class DT, int CW>
+static void launch_grad_cw(dim3 grid, hipStream_t s, const LoraGradJob& j0,
+                           const LoraGradJob& j1, int64_t b0, int64_t M, int r,
+                           int accumulate) {
+  const int threads = 64 * (CW == 1 ? kWaves : 4);
+  if (r <= 16)
+    hipLaunchKernelGGL((lora_grad_kernel<1, DROP, DT, CW>), grid, dim3(threads), 0, s, j0, j1,
+                       b0, M, r, accumulate);
+  else if (r <= 32)
+    hipLaunchKernelGGL((lora_grad_kernel<2, DROP, DT, CW>), grid, dim3(threads), 0, s, j0, j1,
+                       b0, M, r, accumulate);
+  else
+    hipLaunchKernelGGL((lora_grad_kernel<4, DROP, DT, CW>), grid, dim3(threads), 0, s, j0, j1,
+                       b0, M, r, accumulate);
+}
+
+// 128-column tiles when both jobs' columns divide into them and they still
+// give at least 224 blocks (most CUs one); 64-column ones otherwise
 template <bool DROP, class DT>
 static hipError_t launch_grad(const LoraGradJob& j0, const LoraGradJob& j1, int64_t M, int r,
                               int accumulate, hipStream_t s) {
-  const int64_t b0 = j0.ldg / 64, b1 = j1.ldg / 64;
-  if (b0 + b1 == 0 || r == 0) return hipSuccess;
+  if (r == 0 || j0.ldg + j1.ldg == 0) return hipSuccess;
+  const bool wide = j0.ldg % 128 == 0 && j1.ldg % 128 == 0 && (j0.ldg + j1.ldg) / 128 >= 224;
+  const int ct = wide ? 128 : 64;
+  const int64_t b0 = j0.ldg / ct, b1 = j1.ldg / ct;
   const dim3 grid((unsigned)(b0 + b1));
-  if (r <= 16)
-    hipLaunchKernelGGL((lora_grad_kernel<1, DROP, DT>), grid, dim3(kThreads), 0, s, j0, j1,
-                       b0, M, r, accumulate);
-  else if (r <= 32)
-    hipLaunchKernelGGL((lora_grad_kernel<2, DROP, DT>), grid, dim3(kThreads), 0, s, j0, j1,
-                       b0, M, r, accumulate);
+  if (wide)
+    launch_grad_cw<DROP, DT, 2>(grid, s, j0, j1, b0, M, r, accumulate);
   else
-    hipLaunchKernelGGL((lora_grad_kernel<4, DROP, DT>), grid, dim3(kThreads), 0, s, j0, j1,
-                       b0, M, r, accumulate);
+    launch_grad_cw<DROP, DT, 1>(grid, s, j0, j1, b0, M, r, accumulate);
   return hipGetLastError();
 }
 

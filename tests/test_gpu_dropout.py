@@ -36,6 +36,7 @@ SHAPES = [
     (200, 4096, 512, 32, 64.0, 0.05),
     (1000, 4096, 1024, 64, 16.0, 0.05),  # split down-projections, 4 token tiles
     (2100, 8192, 256, 32, 64.0, 0.1),    # dy.B split, 8 token tiles
+    (100, 28672, 128, 64, 16.0, 0.1),    # the gradient kernel's 128-column tiles
 ]
 
 

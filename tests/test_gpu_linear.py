@@ -121,6 +121,29 @@ def test_backward_parity(cuda, shape):
         check_close("dB", dB, rdB)
 
 
+@pytest.mark.parametrize("shape", [(100, 28672, 128, 16, 32.0), (100, 28672, 128, 32, 64.0),
+                                   (70, 27648, 1024, 64, 16.0)],
+                         ids=["r16", "r32", "r64-two-jobs"])
+def test_wide_gradient_tiles(cuda, shape):
+    """Enough G columns for the gradient kernel's 128-column tiles (four
+    waves, 256-byte runs per token row): 224 blocks, the dA job's first
+    block after the dB job's last, ragged tokens; dX, dA and dB against the
+    oracle, the accumulate mode on the last shape."""
+    M, N, K, r, alpha = shape
+    L = _layer(M, N, K, r, alpha)
+    ol = OracleLayer(L.w)
+    rng = np.random.default_rng(3)
+    acc = r == 64
+    dA0 = rng.standard_normal((r, K)).astype(np.float32) if acc else None
+    dB0 = rng.standard_normal((N, r)).astype(np.float32) if acc else None
+    dx, dA, dB = _run_bwd(L, ol, accumulate=acc, dA0=dA0, dB0=dB0)
+    rdx, rdA, rdB = oracle.lora_linear_bwd(L.f32("x"), L.f32("dy"), ol.w_deq, L.f32("A"),
+                                           L.f32("B"), L.alpha)
+    check_close_bf16("dX", dx, rdx)
+    check_close("dA", dA.astype(np.float64) - (dA0 if acc else 0), rdA)
+    check_close("dB", dB.astype(np.float64) - (dB0 if acc else 0), rdB)
+
+
 def test_backward_accumulate_and_skip_dx(cuda):
     L = _layer(100, 256, 320, 16, 32.0)
     ol = OracleLayer(L.w)
