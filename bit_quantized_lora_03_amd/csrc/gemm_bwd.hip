@@ -82,6 +82,12 @@ __device__ __forceinline__ int rk(int row, int chunk) {
   return row * ROW_CHUNKS + (chunk ^ ((row >> 1) & 7));
 }
 
+// s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS
+// operations of this wave are outstanding (expcnt left free).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+
 }  // namespace
 
 // MS: 32-wide token subtiles per wave; MS = 4 is the 256 (k) x 256 (m)
@@ -167,12 +173,24 @@ void dx_gemm_kernel(DxParams p) {
   // dy rows m0 + (t >> 3) + 32 j through a buffer descriptor: rows past M
   // read as zero
   const __amdgpu_buffer_rsrc_t yres = make_rsrc(p.dy, (uint32_t)(M * N * 2));
-  // lane offsets of the thread's XR dy rows (fixed), the slab's column in
-  // the scalar offset
-  uint32_t yvoff[XR];
+  // The dy tile reaches LDS by DMA (buffer loads that write LDS directly):
+  // instruction q of wave w fills tile rows 8 (XR w + q) .. + 7 of a stage,
+  // lane i its 16 bytes at 16 i -- row 8 (XR w + q) + i / 8 at physical
+  // chunk i % 8, which holds logical chunk (i % 8) ^ ((row / 2) % 8), the
+  // swizzled layout of rk -- so each lane fetches that chunk.  The row is
+  // in the lane offset (rows past M lie beyond the descriptor and read as
+  // zero), the slab's column in the scalar offset.
+  // (a fixed-size array: a lambda capturing one whose size depends on the
+  // template arguments, used as a buffer-load operand, fails to substitute
+  // in the host pass, which then silently drops the kernel's host stub)
+  static_assert(XR <= 8, "dy DMA offsets");
+  uint32_t yvoff[8];
 #pragma unroll
-  for (int j = 0; j < XR; ++j)
-    yvoff[j] = (uint32_t)(((m0 + (t >> 3) + 32 * j) * N + 8 * (t & 7)) * 2);
+  for (int q = 0; q < XR; ++q) {
+    const int row = 8 * (XR * wave + q) + (lane >> 3);
+    const int lc = (lane & 7) ^ ((row >> 1) & 7);
+    yvoff[q] = (uint32_t)(((m0 + row) * N + 8 * lc) * 2);
+  }
   // NF4 codes and scale bytes likewise: the lane's element offset within a
   // slab is fixed, the slab's first element is uniform
   const __amdgpu_buffer_rsrc_t cres = make_rsrc(p.codes, (uint32_t)((N * K) >> 1));
@@ -223,20 +241,27 @@ void dx_gemm_kernel(DxParams p) {
       for (int i = 0; i < 8; ++i) c.w[i] = wp[i];
     }
   };
-  auto load_dy = [&](int64_t st, u32x4_t (&yr)[XR]) {
+  auto dma_dy = [&](u32x4_t* stage, int64_t st) {
 #pragma unroll
-    for (int j = 0; j < XR; ++j) yr[j] = buffer_load16(yres, yvoff[j], (uint32_t)(st * RT * 2));
+    for (int q = 0; q < XR; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          yres, (__attribute__((address_space(3))) void*)(stage + 8 * (XR * wave + q) * ROW_CHUNKS),
+          16, yvoff[q], (uint32_t)(st * RT * 2), 0, 0);
   };
-  auto store_dy = [&](int stage, const u32x4_t (&yr)[XR]) {
-#pragma unroll
-    for (int j = 0; j < XR; ++j) dyt[stage][rk((t >> 3) + 32 * j, t & 7)] = yr[j];
-  };
+  // vector-memory operations of one load_codes (the DMA waits below count
+  // only the codes issued after a dy DMA)
+  constexpr int kCodeOps = NF4 ? (HALF ? 3 : 4) : 8;
   // store 8 consecutive-k 16-bit values (chunk c of this thread's NCH) of
   // reduction row `wr` into the W slab
-  auto store8 = [&](int stage, int c, const u32x4_t v) {
-    *reinterpret_cast<u32x4_t*>(wbase + stage * WST + wr * WR +
+  // (stage given as its base: the main loop passes restrict-qualified
+  // stage pointers, which tell the compiler the dy DMA's destination is
+  // disjoint from everything an iteration reads, so it places no wait for
+  // the DMA before those reads)
+  auto store8p = [&](char* stage_base, int c, const u32x4_t v) {
+    *reinterpret_cast<u32x4_t*>(stage_base + wr * WR +
                                 ((((KW / 4) * kq + 8 * c) * 2) ^ slab_swz(wr))) = v;
   };
+  auto store8 = [&](int stage, int c, const u32x4_t v) { store8p(wbase + stage * WST, c, v); };
   // A operand of MFMA step kk, k sub-tile i: lane l holds column
   // (KW / 2) wk + 32 i + l % 32 at reduction rows 16 kk + 8 (l / 32) + 0..7, from
   // two transpose reads (rows +0..3 and +4..7).  As provider, lane j of
@@ -249,16 +274,17 @@ void dx_gemm_kernel(DxParams p) {
   const int a_col = ((KW / 2) * wk + 16 * (tg & 1) + 4 * (tj & 3)) * 2;
   const int a_off0 = a_row * WR + (a_col ^ slab_swz(a_row));
   const int a_off1 = (a_row + 4) * WR + (a_col ^ slab_swz(a_row + 4));
-  auto read_a = [&](int stage, int kk, int i) -> u32x4_t {
+  auto read_ap = [&](const char* stage_base, int kk, int i) -> u32x4_t {
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s lds_v4s;
-    const int o = stage * WST + 16 * kk * WR + 64 * i;
-    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o + a_off0));
-    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wbase + o + a_off1));
+    const int o = 16 * kk * WR + 64 * i;
+    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(stage_base + o + a_off0));
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(stage_base + o + a_off1));
     const u32x2_t h0 = __builtin_bit_cast(u32x2_t, r0), h1 = __builtin_bit_cast(u32x2_t, r1);
     const u32x4_t v = {h0[0], h0[1], h1[0], h1[1]};
     return v;
   };
+  auto read_a = [&](int stage, int kk, int i) { return read_ap(wbase + stage * WST, kk, i); };
   auto mfma_step = [&](int stage, int kk) {
     const int ch = 2 * kk + lg;
     u32x4_t a[NI], b[MS];
@@ -340,10 +366,9 @@ void dx_gemm_kernel(DxParams p) {
     const int64_t last = st1 - 1;
     auto cl = [&](int64_t v) { return v < last ? v : last; };
     Codes C[2];
-    u32x4_t Y[2][XR];
+    dma_dy(dyt[0], st0);
+    __builtin_amdgcn_sched_barrier(0);
     load_codes(st0, C[0]);
-    load_dy(st0, Y[0]);
-    store_dy(0, Y[0]);
     if constexpr (NF4) {
       const Nf4Lut lut = nf4_make_lut<DT>(p.L, (CTR ? nf4_block_scale(C[0].q, C[0].st, fmt) : nf4_block_scale(C[0].q, C[0].st)));
 #pragma unroll
@@ -352,34 +377,41 @@ void dx_gemm_kernel(DxParams p) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) store8(0, c, C[0].w[c]);
     }
-    load_dy(cl(st0 + 1), Y[1]);
     load_codes(cl(st0 + 1), C[1]);
+    // slab st0's dy DMA (older than these codes) has landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kCodeOps, 0));
     __syncthreads();
 
     // Hand-scheduled iteration, as in the forward pass: each of the MFMAs
     // of the slab is followed by a fixed share of the 64 units of other
     // work and a scheduling fence -- the table of slab st+1's block (units
-    // 0..7), the decode of its NCH code words (6 units each, about 5 vector
-    // ops per unit; the last one stores the 8 values into the W slab), the
-    // LDS writes of its dy rows (the XR units after those) -- and the
-    // operand reads of step kk+1 ride in the last slots of step kk, so the
-    // vector work fits in the MFMAs' shadow.
-    auto iteration = [&](int64_t st, auto parity) {
+    // 0..7) and the decode of its NCH code words (6 units each, about 5
+    // vector ops per unit; the last one stores the 8 values into the W
+    // slab) -- and the operand reads of step kk+1 ride in the last slots of
+    // step kk, so the vector work fits in the MFMAs' shadow.  Slab st+1's
+    // dy tile is DMA'd into the other stage at the top (that stage was last
+    // read in the previous iteration, before its closing barrier) and
+    // waited for before this iteration's closing barrier; the codes go two
+    // slabs ahead into registers.
+    auto iteration = [&](int64_t st, auto parity, const u32x4_t* __restrict__ y_rd,
+                         u32x4_t* __restrict__ y_fill, const char* __restrict__ w_rd,
+                         char* __restrict__ w_fill) {
       constexpr int cur = decltype(parity)::value, nxt = cur ^ 1;
-      load_dy(cl(st + 2), Y[cur]);
+      dma_dy(y_fill, cl(st + 1));
+      __builtin_amdgcn_sched_barrier(0);
       load_codes(cl(st + 2), C[cur]);
       const Codes& cn = C[nxt];
       constexpr int SPK = NI * MS;  // MFMAs (slots) per k step
       constexpr int NRD = NI + MS;  // operand reads per k step
-      constexpr int DEC = 8 + 6 * NCH;  // units before the dy rows
-      static_assert(SPK >= NRD && DEC + XR <= 64, "unit schedule");
+      constexpr int DEC = 8 + 6 * NCH;  // table and decode units
+      static_assert(SPK >= NRD && DEC <= 64, "unit schedule");
       u32x4_t op[2][2][4];          // [buffer][a|b][i]
       auto read_op = [&](int kk, int buf, int q) {
         const int ch = 2 * kk + lg;
         if (q < NI)
-          op[buf][0][q] = read_a(cur, kk, q);
+          op[buf][0][q] = read_ap(w_rd, kk, q);
         else
-          op[buf][1][q - NI] = dyt[cur][rk(32 * MS * wm + 32 * (q - NI) + lr, ch)];
+          op[buf][1][q - NI] = y_rd[rk(32 * MS * wm + 32 * (q - NI) + lr, ch)];
       };
 #pragma unroll
       for (int q = 0; q < NRD; ++q) read_op(0, 0, q);
@@ -406,9 +438,7 @@ void dx_gemm_kernel(DxParams p) {
         if constexpr (!NF4) {
           // no table or decode: a chunk's store sits where its decode ends
           if (u >= 8 && u < DEC) {
-            if ((u - 8) % 6 == 5) store8(nxt, (u - 8) / 6, cn.w[(u - 8) / 6]);
-          } else if (u >= DEC && u < DEC + XR) {
-            dyt[nxt][rk((t >> 3) + 32 * (u - DEC), t & 7)] = Y[nxt][u - DEC];
+            if ((u - 8) % 6 == 5) store8p(w_fill, (u - 8) / 6, cn.w[(u - 8) / 6]);
           }
         } else if (u < 4) {
           if (u == 0) sc = CTR ? nf4_block_scale(cn.q, cn.st, fmt) : nf4_block_scale(cn.q, cn.st);
@@ -435,11 +465,8 @@ void dx_gemm_kernel(DxParams p) {
             case 2: { uint32_t o0, o1; lookup_b(dn0, o0, o1); dv[0] = o0; dv[1] = o1; break; }
             case 3: lookup_a(dn1); break;
             case 4: { uint32_t o2, o3; lookup_b(dn1, o2, o3); dv[2] = o2; dv[3] = o3; break; }
-            default: store8(nxt, c, dv); break;
+            default: store8p(w_fill, c, dv); break;
           }
-        } else if (u < DEC + XR) {
-          // slab st+1's dy rows into the other stage
-          dyt[nxt][rk((t >> 3) + 32 * (u - DEC), t & 7)] = Y[nxt][u - DEC];
         }
       };
 #pragma unroll
@@ -455,11 +482,18 @@ void dx_gemm_kernel(DxParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // slab st+1's dy DMA has landed (only this iteration's codes, issued
+      // after it, may still be in flight)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(kCodeOps, 0));
       __syncthreads();
     };
+    u32x4_t* const Y0 = dyt[0];
+    u32x4_t* const Y1 = dyt[1];
+    char* const W0 = wbase;
+    char* const W1 = wbase + WST;
     for (int64_t st = st0; st < st1; st += 2) {
-      iteration(st, std::integral_constant<int, 0>());
-      if (st + 1 < st1) iteration(st + 1, std::integral_constant<int, 1>());
+      iteration(st, std::integral_constant<int, 0>(), Y0, Y1, W0, W1);
+      if (st + 1 < st1) iteration(st + 1, std::integral_constant<int, 1>(), Y1, Y0, W1, W0);
     }
   }
 
