@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void lora_proj_kernel(LoraProjJob j0, Lor
   constexpr int SLAB = 32 * RS;          // bf16 per wave
   // k steps per batch of loads (a batch holds TT + JT operands per step;
   // sized so that no variant spills)
-  constexpr int BS = TT >= 4 ? 1 : (TT == 2 ? 2 : (JT == 1 ? 8 : (JT == 2 ? 4 : 2)));
+  constexpr int BS = TT >= 4 ? (TT == 4 && DROP == 0 ? 2 : 1) : (TT == 2 ? 2 : (JT == 1 ? 8 : (JT == 2 ? 4 : 2)));
   constexpr int REDS = RC + 4;           // fp32 row of the cross-wave sums
   constexpr int SLAB_BYTES = kWaves * SLAB * 2, RED_BYTES = kWaves * 16 * REDS * 4;
   __shared__ __align__(16) char lds[SLAB_BYTES > RED_BYTES ? SLAB_BYTES : RED_BYTES];
