@@ -14,7 +14,8 @@
 //    waves x the two lane halves), lane (row l%32, half l/32) of wave w
 //    taking slot 2 w + l/32 of each chunk of 16 blocks.  Each wave brings
 //    in exactly the codes it decodes by DMA, into an LDS ring of its own
-//    six chunks deep, so waves never wait for one another until the final
+//    (six chunks deep, three when x is staged in LDS, with the DMA three or
+//    two chunks ahead), so waves never wait for one another until the final
 //    sum.  For each block the lane builds the block's 16-entry bf16
 //    table once and decodes its 64 codes into the A operands of 8
 //    consecutive MFMAs; the reduction order over k is permuted consistently
@@ -54,10 +55,15 @@ constexpr int WAVES = 8;    // waves per block
 constexpr int SLOTS = 2 * WAVES;  // NF4-block slots per weight row
 constexpr int SPAN = 128;   // k per span of the adapter tiles
 constexpr int kTabBytes = WAVES * 16 * 64 * 4;  // per-lane NF4 tables, 32 KiB
-constexpr int NSTAGE = 6;   // code chunks in the LDS ring
+// Code chunks in each wave's LDS ring, and chunks whose DMA is in flight
+// ahead of the decode, with x in registers and with x in LDS.
+constexpr int NSTAGE = 6, kAheadReg = 3;
+constexpr int NSTAGE_XL = 3, kAheadXl = 2;
 constexpr int kStageU4 = 32 * 64 / 16;  // one wave's chunk: 32 rows x its 2 blocks (64 bytes)
-constexpr int kLdsBytes = kTabBytes + WAVES * NSTAGE * kStageU4 * 16;
-constexpr int kXBytes = 32768;  // x staged in LDS when it fits (see decode_x_in_lds)
+constexpr int ring_bytes(int nst) { return WAVES * nst * kStageU4 * 16; }
+// x staged in LDS when it fits (see decode_x_in_lds): the rest of the 160 KiB
+constexpr int kXBytes = 160 * 1024 - kTabBytes - ring_bytes(NSTAGE_XL);
+constexpr int kXq = 8;  // x pieces each lane stages (bounds M K / 64 by 64 kXq)
 
 // s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS
 // operations of this wave are outstanding (expcnt left free).
@@ -98,6 +104,10 @@ template <bool XL, bool CTR>
 __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p) {
   // the tables start the kernel's LDS (at offset 0, so a lookup address
   // needs no base added); after the main loop the space holds the reduction
+  constexpr int NST = XL ? NSTAGE_XL : NSTAGE;
+  constexpr int kAhead = XL ? kAheadXl : kAheadReg;
+  static_assert(kAhead >= 2 && kAhead < NST, "prefetch distance within the ring");
+  constexpr int kLdsBytes = kTabBytes + ring_bytes(NST);
   __shared__ __align__(16) uint8_t lds[kLdsBytes + (XL ? kXBytes : 0)];
 
   // Weight tiles take the first ids, A tiles the last: workgroups are
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // (row l%32, half l/32) of wave w decodes block 2 w + l/32.  Each wave
     // brings in exactly the codes it decodes -- its two blocks of the 32
     // rows, 64 bytes per row and chunk -- by DMA (buffer loads that write
-    // LDS directly) into a ring of its own, NSTAGE chunks deep, so no wave
+    // LDS directly) into a ring of its own, NST chunks deep, so no wave
     // waits for another: the main loop has no barrier.  (Together the 8
     // waves read each row's 512-byte chunk piece.)  In a stage, row r's
     // 16-byte piece p (0, 1: block 2 w; 2, 3: block 2 w + 1) sits at
@@ -256,12 +266,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       }
     };
 
-    // Issue order.  The prologue issues, in rounds c = 0 .. NSTAGE - 2,
+    // Issue order.  The prologue issues, in rounds c = 0 .. kAhead - 1,
     // chunk c's DMA and scales, followed in round 0 by x of chunk 0 (or --
     // with x in LDS -- every piece of x the wave will read) and in round 1
     // by x of chunk 1; iteration ch loads x of chunk
     // ch + 2 (not with x in LDS), then issues the DMA of chunk
-    // ch + NSTAGE - 1 and its scales, decodes chunk ch and at its end waits
+    // ch + kAhead and its scales, decodes chunk ch and at its end waits
     // for chunk ch + 1's DMA.  Loads complete in order, so a wait for x of
     // chunk ch (issued first in iteration ch - 2) also waits for the DMAs
     // issued before it, up to chunk ch + 2's: x comes two iterations ahead
@@ -270,19 +280,29 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // count altogether).  The end-of-iteration wait is "at most W
     // outstanding", W being the number of operations issued after chunk
     // ch + 1's DMA; with kOps operations per iteration that is
-    // 2 + kOps (NSTAGE - 2) in the steady state (it was issued in iteration
-    // ch + 2 - NSTAGE) and, with x in registers, 34, 34 and 42 in the first
-    // three iterations (x of chunk 1 follows chunk 1's DMA in the
-    // prologue).  Waits are immediates, so W is a template
+    // 2 + kOps (kAhead - 1) in the steady state (it was issued in iteration
+    // ch + 1 - kAhead), and while chunk ch + 1 still comes from the
+    // prologue, its scales, the prologue rounds after it (with x of chunk 1
+    // after chunk 1's DMA when x is in registers) and iterations 0 .. ch
+    // (wait_for below).  Waits are immediates, so W is a template
     // argument: the first group of iterations gets its own, later groups the
     // steady one, and a short reduction (fewer chunks than one group) the
-    // smallest, which waits at least as long as needed.
+    // smallest, which waits at least as long as needed.  The prefetch
+    // distance is shorter than the ring: issued all at once, a deep
+    // prologue holds every wave at the issue of its last loads (the CU's
+    // request queue is full) for about as long as the chip takes to deliver
+    // them, while chunk 0 is already there to decode.
     constexpr int kOps = XL ? 4 : 12;  // vector-memory operations per iteration
-    constexpr int kWaitSteady = 2 + kOps * (NSTAGE - 2);
+    constexpr int kWaitSteady = 2 + kOps * (kAhead - 1);
     static_assert(kWaitSteady <= 63, "vmcnt holds at most 63");
+    // operations issued after chunk c + 1's DMA by the end of iteration c
+    constexpr auto wait_for = [](int c) {
+      if (c + 1 >= kAhead) return kWaitSteady;
+      return 2 + (!XL && c == 0 ? 8 : 0) + 4 * (kAhead - 2 - c) + kOps * (c + 1);
+    };
     u32x4_t* const ring =
-        reinterpret_cast<u32x4_t*>(lds + kTabBytes) + wave * NSTAGE * kStageU4;
-    Scale Sc[NSTAGE];
+        reinterpret_cast<u32x4_t*>(lds + kTabBytes) + wave * NST * kStageU4;
+    Scale Sc[NST];
     u32x4_t X[XL ? 1 : 3][8];
     const int64_t lastc = nch - 1;
     auto cl = [&](int64_t c) { return c < lastc ? c : lastc; };
@@ -296,7 +316,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // 16) / 8, chunk ch = (i / 16) mod nch, token (i / 16) / nch.
     uint8_t* const xl = lds + kLdsBytes;
     const int64_t xrb = 2 * K + 16;
-    constexpr int kXq = 4;  // pieces per lane (the x budget bounds M K / 64 by 256)
     u32x4_t xv[XL ? kXq : 1];
     uint32_t xdst[XL ? kXq : 1];
     // The prologue's loads go out in rounds, one chunk per wave per round
@@ -307,7 +326,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // several microseconds later.  Round c: chunk c's DMA and scales, then
     // x (chunks 0 and 1 in registers, or every staged piece in round 0).
 #pragma unroll
-    for (int c = 0; c < NSTAGE - 1; ++c) {
+    for (int c = 0; c < kAhead; ++c) {
       dma_codes(ring + c * kStageU4, cl(c));
       load_scale(cl(c), Sc[c]);
       if constexpr (XL) {
@@ -345,8 +364,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       if (lane < 8) *reinterpret_cast<u32x4_t*>(xl + M * xrb + 128 * wave + 16 * lane) = zero;
     }
     // chunk 0's DMA: followed by its scales, the x loads (XL: kXq, else two
-    // chunks of 8) and NSTAGE - 2 DMA + scale pairs
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 + (XL ? kXq : 16) + 4 * (NSTAGE - 2), 0));
+    // chunks of 8) and kAhead - 1 DMA + scale pairs
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 + (XL ? kXq : 16) + 4 * (kAhead - 1), 0));
 
     // x operand j of chunk ch from LDS: token lr's 16 bytes at k = 64 b + 8 j
     auto x_lds = [&](int64_t ch) {
@@ -358,19 +377,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       };
     };
 
-    // phase = ch mod NSTAGE: the stage read (rd), the stage filled (fill),
+    // phase = ch mod NST: the stage read (rd), the stage filled (fill),
     // the scale set and the x set (ch mod 3) are then compile-time choices
     auto iteration = [&](int64_t ch, auto phase, auto wait, const u32x4_t* __restrict__ rd,
                          u32x4_t* __restrict__ fill) {
       constexpr int ph = decltype(phase)::value;
       constexpr int W = decltype(wait)::value;
-      static_assert(NSTAGE % 3 == 0, "x sets rotate with the phase");
+      static_assert(XL || NST % 3 == 0, "x sets rotate with the phase");
       if constexpr (!XL) {
         load_xc(cl(ch + 2), X[(ph + 2) % 3]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      dma_codes(fill, cl(ch + NSTAGE - 1));
-      load_scale(cl(ch + NSTAGE - 1), Sc[(ph + NSTAGE - 1) % NSTAGE]);
+      dma_codes(fill, cl(ch + kAhead));
+      load_scale(cl(ch + kAhead), Sc[(ph + kAhead) % NST]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (XL)
         decode_chunk(rd, ch, Sc[ph], x_lds(ch));
@@ -379,51 +398,53 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(W, 0));
     };
-    static_assert(NSTAGE == 6, "the loop below is unrolled for six stages");
-    u32x4_t* const R[NSTAGE] = {ring, ring + kStageU4, ring + 2 * kStageU4,
-                                ring + 3 * kStageU4, ring + 4 * kStageU4, ring + 5 * kStageU4};
+    static_assert(6 % NST == 0, "the loop below is unrolled by six iterations");
+    u32x4_t* const R[6] = {ring, ring + kStageU4, ring + 2 * kStageU4,
+                           ring + 3 * kStageU4, ring + 4 * kStageU4, ring + 5 * kStageU4};
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
     using P3 = std::integral_constant<int, 3>;
     using P4 = std::integral_constant<int, 4>;
     using P5 = std::integral_constant<int, 5>;
-    // with x in LDS every iteration's count is the steady one; with x in
-    // registers, chunk 1's x follows chunk 1's DMA in the prologue, so the
-    // first wait also counts it
-    using W0 = std::integral_constant<int, XL ? kWaitSteady : 34>;
-    using W1 = std::integral_constant<int, XL ? kWaitSteady : 34>;
-    using W2 = std::integral_constant<int, XL ? kWaitSteady : 42>;
+    // iteration ch (phase ch mod 6 here) reads stage ch mod NST and fills
+    // stage ch + kAhead (mod NST), the one it read kAhead - NST iterations ago
+    auto step = [&](int64_t ch, auto phase6, auto wait) {
+      constexpr int ph = decltype(phase6)::value % NST;
+      iteration(ch, std::integral_constant<int, ph>(), wait, R[ph], R[(ph + kAhead) % NST]);
+    };
     using WS = std::integral_constant<int, kWaitSteady>;
-    static_assert(XL || 26 + 8 * (NSTAGE - 3) == kWaitSteady,
-                  "iteration NSTAGE - 3 reaches the steady state");
+    constexpr auto lo = [](int a, int b) { return a < b ? a : b; };
+    constexpr int kWaitMin =
+        lo(lo(lo(wait_for(0), wait_for(1)), lo(wait_for(2), wait_for(3))), lo(wait_for(4), kWaitSteady));
+    using WM = std::integral_constant<int, kWaitMin>;
     if (nch >= 6) {
-      iteration(0, P0(), W0(), R[0], R[5]);
-      iteration(1, P1(), W1(), R[1], R[0]);
-      iteration(2, P2(), W2(), R[2], R[1]);
-      iteration(3, P3(), WS(), R[3], R[2]);
-      iteration(4, P4(), WS(), R[4], R[3]);
-      iteration(5, P5(), WS(), R[5], R[4]);
+      step(0, P0(), std::integral_constant<int, wait_for(0)>());
+      step(1, P1(), std::integral_constant<int, wait_for(1)>());
+      step(2, P2(), std::integral_constant<int, wait_for(2)>());
+      step(3, P3(), std::integral_constant<int, wait_for(3)>());
+      step(4, P4(), std::integral_constant<int, wait_for(4)>());
+      step(5, P5(), WS());
       int64_t ch = 6;
       for (; ch + 6 <= nch; ch += 6) {
-        iteration(ch, P0(), WS(), R[0], R[5]);
-        iteration(ch + 1, P1(), WS(), R[1], R[0]);
-        iteration(ch + 2, P2(), WS(), R[2], R[1]);
-        iteration(ch + 3, P3(), WS(), R[3], R[2]);
-        iteration(ch + 4, P4(), WS(), R[4], R[3]);
-        iteration(ch + 5, P5(), WS(), R[5], R[4]);
+        step(ch, P0(), WS());
+        step(ch + 1, P1(), WS());
+        step(ch + 2, P2(), WS());
+        step(ch + 3, P3(), WS());
+        step(ch + 4, P4(), WS());
+        step(ch + 5, P5(), WS());
       }
-      if (ch < nch) iteration(ch, P0(), WS(), R[0], R[5]);
-      if (ch + 1 < nch) iteration(ch + 1, P1(), WS(), R[1], R[0]);
-      if (ch + 2 < nch) iteration(ch + 2, P2(), WS(), R[2], R[1]);
-      if (ch + 3 < nch) iteration(ch + 3, P3(), WS(), R[3], R[2]);
-      if (ch + 4 < nch) iteration(ch + 4, P4(), WS(), R[4], R[3]);
+      if (ch < nch) step(ch, P0(), WS());
+      if (ch + 1 < nch) step(ch + 1, P1(), WS());
+      if (ch + 2 < nch) step(ch + 2, P2(), WS());
+      if (ch + 3 < nch) step(ch + 3, P3(), WS());
+      if (ch + 4 < nch) step(ch + 4, P4(), WS());
     } else {
-      iteration(0, P0(), W0(), R[0], R[5]);
-      if (1 < nch) iteration(1, P1(), W0(), R[1], R[0]);
-      if (2 < nch) iteration(2, P2(), W0(), R[2], R[1]);
-      if (3 < nch) iteration(3, P3(), W0(), R[3], R[2]);
-      if (4 < nch) iteration(4, P4(), W0(), R[4], R[3]);
+      step(0, P0(), WM());
+      if (1 < nch) step(1, P1(), WM());
+      if (2 < nch) step(2, P2(), WM());
+      if (3 < nch) step(3, P3(), WM());
+      if (4 < nch) step(4, P4(), WM());
     }
     // the clamped prefetches past the end are still writing LDS
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
@@ -616,7 +637,7 @@ int a_splits(int64_t K) {
 // 4 pieces per lane.
 bool decode_x_in_lds(int64_t M, int64_t K) {
   const int64_t nch = (K / 64 + 15) / 16;
-  return M * (2 * K + 16) + WAVES * 128 <= kXBytes && M * nch * 16 <= 64 * 4;
+  return M * (2 * K + 16) + WAVES * 128 <= kXBytes && M * nch * 16 <= 64 * kXq;
 }
 
 int decode_splits(int64_t M, int64_t N, int64_t K, int r) {
