@@ -27,9 +27,14 @@
 //    2-byte LDS read, and the 64 lanes of a read always hit 64 distinct
 //    banks -- about two thirds of the vector work of resolving codes with
 //    byte permutes in registers;
-//  * x is small and stays in L2: each token lane reads its 16-byte operand
-//    pieces directly, two chunks ahead (lanes past the M tokens read
-//    nothing: their offsets lie beyond x, which returns zeros);
+//  * x is small and stays in L2.  When M rows of it fit in LDS each wave
+//    stages, once, the pieces it will read; for up to 16 tokens each chunk's
+//    pieces reach a two-stage ring of each wave by DMA, one chunk ahead
+//    (four 1 KiB instructions per chunk instead of eight half-empty 16-byte
+//    loads per lane, which the memory pipeline accepts at half the rate);
+//    otherwise each token lane reads its 16-byte operand pieces directly,
+//    two chunks ahead (lanes past the M tokens read nothing: their offsets
+//    lie beyond x, which returns zeros);
 //  * the 8 waves' partial tiles are added in LDS in wave order.
 //
 // The adapter's down projection x . A^T rides along: rows of A (bf16, used
@@ -64,6 +69,11 @@ constexpr int ring_bytes(int nst) { return WAVES * nst * kStageU4 * 16; }
 // x staged in LDS when it fits (see decode_x_in_lds): the rest of the 160 KiB
 constexpr int kXBytes = 160 * 1024 - kTabBytes - ring_bytes(NSTAGE_XL);
 constexpr int kXq = 8;  // x pieces each lane stages (bounds M K / 64 by 64 kXq)
+// x by DMA per chunk (few tokens, x too large to stage whole): each wave's
+// ring of two chunk stages, 16 tokens x its 2 blocks (256 bytes) each
+constexpr int kXdTok = 16;
+constexpr int kXdStage = kXdTok * 256;
+constexpr int kXdBytes = WAVES * 2 * kXdStage;
 
 // s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS
 // operations of this wave are outstanding (expcnt left free).
@@ -98,17 +108,21 @@ struct Blk {
 
 }  // namespace
 
-// XL: x lives in LDS for the whole reduction (few tokens; decode_x_in_lds)
+// XM: where x comes from.  1 (XL): x lives in LDS for the whole reduction
+// (few tokens; decode_x_in_lds); 2 (XD): each chunk's x reaches a two-stage
+// LDS ring of each wave by DMA, one chunk ahead (M <= kXdTok); 0: each
+// token lane loads its x pieces into registers, two chunks ahead.
 // CTR: the weight has the mean-centred scale format
-template <bool XL, bool CTR>
+template <int XM, bool CTR>
 __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p) {
+  constexpr bool XL = XM == 1, XD = XM == 2;
   // the tables start the kernel's LDS (at offset 0, so a lookup address
   // needs no base added); after the main loop the space holds the reduction
-  constexpr int NST = XL ? NSTAGE_XL : NSTAGE;
-  constexpr int kAhead = XL ? kAheadXl : kAheadReg;
+  constexpr int NST = XL || XD ? NSTAGE_XL : NSTAGE;
+  constexpr int kAhead = XL || XD ? kAheadXl : kAheadReg;
   static_assert(kAhead >= 2 && kAhead < NST, "prefetch distance within the ring");
   constexpr int kLdsBytes = kTabBytes + ring_bytes(NST);
-  __shared__ __align__(16) uint8_t lds[kLdsBytes + (XL ? kXBytes : 0)];
+  __shared__ __align__(16) uint8_t lds[kLdsBytes + (XL ? kXBytes : XD ? kXdBytes : 0)];
 
   // Weight tiles take the first ids, A tiles the last: workgroups are
   // dispatched in id order, so the A tiles fill in as weight tiles finish
@@ -292,18 +306,21 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // prologue holds every wave at the issue of its last loads (the CU's
     // request queue is full) for about as long as the chip takes to deliver
     // them, while chunk 0 is already there to decode.
-    constexpr int kOps = XL ? 4 : 12;  // vector-memory operations per iteration
-    constexpr int kWaitSteady = 2 + kOps * (kAhead - 1);
+    constexpr int kOps = XL ? 4 : XD ? 8 : 12;  // vector-memory operations per iteration
+    // (XD: iteration ch issues x of chunk ch + 1 first, so the wait at its
+    // end is for that x DMA -- and with it every earlier load -- leaving
+    // only the iteration's code DMA and scales outstanding)
+    constexpr int kWaitSteady = XD ? 4 : 2 + kOps * (kAhead - 1);
     static_assert(kWaitSteady <= 63, "vmcnt holds at most 63");
     // operations issued after chunk c + 1's DMA by the end of iteration c
     constexpr auto wait_for = [](int c) {
-      if (c + 1 >= kAhead) return kWaitSteady;
+      if (XD || c + 1 >= kAhead) return kWaitSteady;
       return 2 + (!XL && c == 0 ? 8 : 0) + 4 * (kAhead - 2 - c) + kOps * (c + 1);
     };
     u32x4_t* const ring =
         reinterpret_cast<u32x4_t*>(lds + kTabBytes) + wave * NST * kStageU4;
     Scale Sc[NST];
-    u32x4_t X[XL ? 1 : 3][8];
+    u32x4_t X[XL || XD ? 1 : 3][8];
     const int64_t lastc = nch - 1;
     auto cl = [&](int64_t c) { return c < lastc ? c : lastc; };
 
@@ -316,6 +333,42 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // 16) / 8, chunk ch = (i / 16) mod nch, token (i / 16) / nch.
     uint8_t* const xl = lds + kLdsBytes;
     const int64_t xrb = 2 * K + 16;
+    // XD: stage s of wave w at xl + kXdStage (2 w + s); token t's 256 bytes
+    // (its 2 blocks of the chunk) at 256 t, logical 16-byte piece lp (block
+    // lp / 8, piece lp % 8) at physical piece lp ^ t, so the 16 tokens one
+    // 128-bit read cycle serves hit 16 distinct bank groups.  DMA
+    // instruction q fills tokens 4 q .. 4 q + 3 (lane i: token 4 q + i / 16,
+    // physical piece i % 16); tokens past M and blocks past the row's end
+    // read zeros through an offset beyond x.
+    uint8_t* const xdr = xl + (XD ? kXdStage * 2 * wave : 0);
+    uint32_t xdoff[4];
+    int xdblk[4];
+    bool xdtok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int tk = 4 * q + (lane >> 4), lp = (lane & 15) ^ tk;
+      xdblk[q] = 2 * wave + (lp >> 3);
+      xdtok[q] = tk < M;
+      xdoff[q] = (uint32_t)(tk * K * 2 + 128 * xdblk[q] + 16 * (lp & 7));
+    }
+    auto dma_x = [&](uint8_t* stage, int64_t ch) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = xdtok[q] && 16 * ch + xdblk[q] < nblk;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xres, (__attribute__((address_space(3))) void*)(stage + 1024 * q), 16,
+            ok ? xdoff[q] + (uint32_t)(ch * 2048) : 0x80000000u, 0, 0, 0);
+      }
+    };
+    // x operand j of a chunk in XD stage st: token lr % 16 (lanes of tokens
+    // past 16 read a copy; their columns are never stored), block lg
+    auto x_ring = [&](const uint8_t* st) {
+      const int tk = lr & 15;
+      const uint8_t* base = st + 256 * tk;
+      return [=](int j) -> u32x4_t {
+        return *reinterpret_cast<const u32x4_t*>(base + 16 * ((8 * lg + j) ^ tk));
+      };
+    };
     u32x4_t xv[XL ? kXq : 1];
     uint32_t xdst[XL ? kXq : 1];
     // The prologue's loads go out in rounds, one chunk per wave per round
@@ -325,11 +378,16 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // first chunk queued behind the first waves' whole prefetch and landed
     // several microseconds later.  Round c: chunk c's DMA and scales, then
     // x (chunks 0 and 1 in registers, or every staged piece in round 0).
+    if constexpr (XD) {
+      dma_x(xdr, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int c = 0; c < kAhead; ++c) {
       dma_codes(ring + c * kStageU4, cl(c));
       load_scale(cl(c), Sc[c]);
-      if constexpr (XL) {
+      if constexpr (XD) {
+      } else if constexpr (XL) {
         if (c == 0) {
           // 32-bit index math, every offset computed before the select, so
           // the selects stay selects (a branch around the loads would make
@@ -363,9 +421,11 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
         if (xdst[q] != 0xFFFFFFFFu) *reinterpret_cast<u32x4_t*>(xl + xdst[q]) = xv[q];
       if (lane < 8) *reinterpret_cast<u32x4_t*>(xl + M * xrb + 128 * wave + 16 * lane) = zero;
     }
-    // chunk 0's DMA: followed by its scales, the x loads (XL: kXq, else two
-    // chunks of 8) and kAhead - 1 DMA + scale pairs
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 + (XL ? kXq : 16) + 4 * (kAhead - 1), 0));
+    // chunk 0's DMA: followed by its scales, the x loads (XL: kXq, XD: none
+    // -- x of chunk 0 went first -- else two chunks of 8) and kAhead - 1
+    // DMA + scale pairs
+    __builtin_amdgcn_s_waitcnt(
+        waitcnt_imm(2 + (XL ? kXq : XD ? 0 : 16) + 4 * (kAhead - 1), 0));
 
     // x operand j of chunk ch from LDS: token lr's 16 bytes at k = 64 b + 8 j
     auto x_lds = [&](int64_t ch) {
@@ -380,18 +440,24 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     // phase = ch mod NST: the stage read (rd), the stage filled (fill),
     // the scale set and the x set (ch mod 3) are then compile-time choices
     auto iteration = [&](int64_t ch, auto phase, auto wait, const u32x4_t* __restrict__ rd,
-                         u32x4_t* __restrict__ fill) {
+                         u32x4_t* __restrict__ fill, const uint8_t* __restrict__ xrd,
+                         uint8_t* __restrict__ xfill) {
       constexpr int ph = decltype(phase)::value;
       constexpr int W = decltype(wait)::value;
-      static_assert(XL || NST % 3 == 0, "x sets rotate with the phase");
-      if constexpr (!XL) {
+      static_assert(XL || XD || NST % 3 == 0, "x sets rotate with the phase");
+      if constexpr (XD) {
+        dma_x(xfill, cl(ch + 1));
+        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (!XL) {
         load_xc(cl(ch + 2), X[(ph + 2) % 3]);
         __builtin_amdgcn_sched_barrier(0);
       }
       dma_codes(fill, cl(ch + kAhead));
       load_scale(cl(ch + kAhead), Sc[(ph + kAhead) % NST]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (XL)
+      if constexpr (XD)
+        decode_chunk(rd, ch, Sc[ph], x_ring(xrd));
+      else if constexpr (XL)
         decode_chunk(rd, ch, Sc[ph], x_lds(ch));
       else
         decode_chunk(rd, ch, Sc[ph], [&](int j) -> u32x4_t { return X[ph % 3][j]; });
@@ -409,9 +475,12 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
     using P5 = std::integral_constant<int, 5>;
     // iteration ch (phase ch mod 6 here) reads stage ch mod NST and fills
     // stage ch + kAhead (mod NST), the one it read kAhead - NST iterations ago
+    // (XD: x stage ch mod 2 is read, the other filled)
     auto step = [&](int64_t ch, auto phase6, auto wait) {
       constexpr int ph = decltype(phase6)::value % NST;
-      iteration(ch, std::integral_constant<int, ph>(), wait, R[ph], R[(ph + kAhead) % NST]);
+      constexpr int xs = decltype(phase6)::value % 2;
+      iteration(ch, std::integral_constant<int, ph>(), wait, R[ph], R[(ph + kAhead) % NST],
+                xdr + kXdStage * xs, xdr + kXdStage * (1 - xs));
     };
     using WS = std::integral_constant<int, kWaitSteady>;
     constexpr auto lo = [](int a, int b) { return a < b ? a : b; };
@@ -670,17 +739,21 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
   p.blocks = p.w_blocks + (r > 0 ? (int64_t)((r + 31) / 32) * p.sa : 0);
   p.L = L;
   const dim3 grid((unsigned)p.blocks), block(WAVES * 64);
-  const bool xl = decode_x_in_lds(M, K);
+  const int xm = decode_x_in_lds(M, K) ? 1 : (M <= kXdTok ? 2 : 0);
   if (dq_mean) {
-    if (xl)
-      hipLaunchKernelGGL((decode_main_kernel<true, true>), grid, block, 0, s, p);
+    if (xm == 1)
+      hipLaunchKernelGGL((decode_main_kernel<1, true>), grid, block, 0, s, p);
+    else if (xm == 2)
+      hipLaunchKernelGGL((decode_main_kernel<2, true>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((decode_main_kernel<false, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((decode_main_kernel<0, true>), grid, block, 0, s, p);
   } else {
-    if (xl)
-      hipLaunchKernelGGL((decode_main_kernel<true, false>), grid, block, 0, s, p);
+    if (xm == 1)
+      hipLaunchKernelGGL((decode_main_kernel<1, false>), grid, block, 0, s, p);
+    else if (xm == 2)
+      hipLaunchKernelGGL((decode_main_kernel<2, false>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((decode_main_kernel<false, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((decode_main_kernel<0, false>), grid, block, 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || r == 0) return e;

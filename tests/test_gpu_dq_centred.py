@@ -159,10 +159,10 @@ def test_one_hot_probes_are_bit_exact(cuda, M):
     assert np.array_equal(host(dx), cl.bits[ns, :])
 
 
-# (M, N, K, r, alpha): tiled forward and dX, the few-token forward, a split
-# tail (more tiles than a round)
+# (M, N, K, r, alpha): tiled forward and dX, the few-token forward (x staged
+# in LDS, and the per-chunk x ring), a split tail (more tiles than a round)
 SHAPES = [(300, 320, 448, 16, 32.0), (16, 512, 1024, 64, 16.0), (1, 256, 512, 8, 16.0),
-          (2100, 2304, 512, 32, 64.0)]
+          (12, 256, 8192, 16, 32.0), (2100, 2304, 512, 32, 64.0)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[str(s) for s in SHAPES])

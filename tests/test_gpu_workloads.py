@@ -101,16 +101,20 @@ def test_narrow_tile_schedules(cuda, M):
 
 @pytest.mark.parametrize("shape", [
     (2, 256, 7872, 8),     # x staged in LDS; 123 NF4 blocks: last chunk ragged
-    (3, 256, 5248, 16),    # x would fit in LDS, but a wave's share exceeds 4 pieces per lane
-    (1, 320, 15808, 24),   # largest K with x in LDS at M = 1: 16 chunks (groups of 6 + 4)
-    (8, 192, 1088, 64),    # x in LDS, 17 blocks in 2 chunks, 6 row tiles
-    (32, 128, 2048, 0),    # most tokens the decode path takes, no adapter
-    (7, 128, 6208, 40),    # x in registers, 97 blocks: ragged chunk and ragged rank steps
+    (3, 256, 5248, 16),    # x staged in LDS, 3 tokens x 6 chunks of pieces per wave
+    (1, 320, 15808, 24),   # largest K with x staged at M = 1: 16 chunks (groups of 6 + 4)
+    (8, 192, 1088, 64),    # x staged in LDS, 17 blocks in 2 chunks, 6 row tiles
+    (32, 128, 2048, 0),    # most tokens the decode path takes (x in registers), no adapter
+    (20, 256, 4096, 16),   # x in registers (more tokens than the x ring holds)
+    (7, 128, 6208, 40),    # x ring by DMA, 97 blocks: ragged chunk and ragged rank steps
+    (13, 384, 8256, 24),   # x ring, 129 blocks (a one-block last chunk), tokens 13..15 zero
+    (16, 256, 4160, 8),    # x ring full (16 tokens), 65 blocks
 ], ids=lambda s: "x".join(map(str, s)))
 def test_decode_path_edges(cuda, shape):
-    """Few-token forward (M <= 32): both ways of feeding x (staged in LDS when
-    M rows of x fit, else per-lane loads), ragged reductions, row tiles and
-    ranks, against the oracle on every token."""
+    """Few-token forward (M <= 32): the three ways of feeding x (staged in
+    LDS when M rows of x fit, a per-chunk DMA ring for up to 16 tokens, else
+    per-lane loads), ragged reductions, row tiles and ranks, against the
+    oracle on every token."""
     M, N, K, r = shape
     _check_layer(workloads.layer(M, N, K, r, 16.0, seed=31, name=f"decode_{M}x{N}x{K}x{r}"),
                  with_bwd=False)
