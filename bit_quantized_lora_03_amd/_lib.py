@@ -32,7 +32,7 @@ EXPORTS = ("qlora_quantize_nf4", "qlora_double_quant", "qlora_quantize_nf4_dq",
            "qlora_dropout_keep_mask", "qlora_linear_fwd_dropout_rng",
            "qlora_linear_bwd_dropout_rng",
            "qlora_merge_adapter", "qlora_linear_fwd_noalloc", "qlora_nf4_levels",
-           "qlora_status_string")
+           "qlora_nf4_thresholds", "qlora_status_string")
 
 
 class QloraError(RuntimeError):
@@ -97,7 +97,8 @@ def lib() -> ctypes.CDLL:
                                           sz, vp], ctypes.c_int),
         "qlora_linear_bwd_dropout_rng": ([wp, vp, vp, i64, vp, vp, i32, f32, f32, u64, u64, vp,
                                           vp, vp, i32, vp, sz, vp], ctypes.c_int),
-        "qlora_nf4_levels": ([vp, vp], ctypes.c_int),
+        "qlora_nf4_levels": ([vp], ctypes.c_int),
+        "qlora_nf4_thresholds": ([vp], ctypes.c_int),
         "qlora_status_string": ([ctypes.c_int], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -122,7 +123,8 @@ def nf4_levels():
     import numpy as np
     lv = np.zeros(16, dtype=np.float32)
     th = np.zeros(15, dtype=np.float32)
-    check(lib().qlora_nf4_levels(lv.ctypes.data, th.ctypes.data), "qlora_nf4_levels")
+    check(lib().qlora_nf4_levels(lv.ctypes.data), "qlora_nf4_levels")
+    check(lib().qlora_nf4_thresholds(th.ctypes.data), "qlora_nf4_thresholds")
     return lv, th
 
 

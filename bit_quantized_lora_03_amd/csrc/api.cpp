@@ -453,11 +453,22 @@ const char* qlora_status_string(int status) {
   }
 }
 
-int qlora_nf4_levels(float* levels, float* thresholds) {
+int qlora_nf4_levels(float out[16]) {
+  if (!out) return QLORA_EINVAL;
   try {
     const qlora::Nf4Table& t = qlora::nf4_table();
-    if (levels) std::memcpy(levels, t.level, sizeof(t.level));
-    if (thresholds) std::memcpy(thresholds, t.threshold, sizeof(t.threshold));
+    std::memcpy(out, t.level, sizeof(t.level));
+    return QLORA_OK;
+  } catch (...) {
+    return QLORA_EINVAL;
+  }
+}
+
+int qlora_nf4_thresholds(float out[15]) {
+  if (!out) return QLORA_EINVAL;
+  try {
+    const qlora::Nf4Table& t = qlora::nf4_table();
+    std::memcpy(out, t.threshold, sizeof(t.threshold));
     return QLORA_OK;
   } catch (...) {
     return QLORA_EINVAL;

@@ -378,11 +378,19 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const uint16_t* x, int64
 size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
                                     int32_t r);
 
-/* The library's own fp32 NF4 table (16 levels, ascending) and its 15 fp32
- * decision thresholds (level midpoints rounded towards -infinity), built on
- * the host from the library's own normal quantile function.  `levels` and
- * `thresholds` are HOST pointers; either may be NULL.  Never touches the GPU. */
-int qlora_nf4_levels(float* levels, float* thresholds);
+/* The library's own fp32 NF4 table: the 16 levels, ascending, built on the
+ * host from the library's own normal quantile function ("QLoRA"
+ * (infivelines.com): 16 levels at equal-probability quantiles of a normal,
+ * normalised to [-1, 1]).  `out` is a HOST pointer to 16 floats.  Returns
+ * QLORA_EINVAL for a NULL `out`.  Never touches the GPU.                    */
+int qlora_nf4_levels(float out[16]);
+
+/* The quantiser's 15 fp32 decision thresholds between consecutive levels of
+ * that table: threshold i is the midpoint of levels i and i + 1 rounded
+ * towards -infinity, and code(u) = #{i : u > threshold[i]} is the nearest
+ * level with ties to the lower one.  `out` is a HOST pointer to 15 floats.  Returns
+ * QLORA_EINVAL for a NULL `out`.  Never touches the GPU.                    */
+int qlora_nf4_thresholds(float out[15]);
 
 /* Static string for a status code (host only).                             */
 const char* qlora_status_string(int status);

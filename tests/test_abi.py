@@ -48,6 +48,12 @@ def test_library_table_equals_oracle_bitwise():
     assert np.array_equal(th.view(np.uint32), oracle.nf4_thresholds_f32().view(np.uint32))
 
 
+def test_table_calls_reject_null():
+    L = q.lib()
+    assert L.qlora_nf4_levels(None) == -1  # QLORA_EINVAL
+    assert L.qlora_nf4_thresholds(None) == -1  # QLORA_EINVAL
+
+
 def test_status_strings():
     L = q.lib()
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
