@@ -132,19 +132,13 @@ FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool decode = true,
   FwdWs L{};
   L.decode = decode && M <= qlora::kDecodeMaxM;
   if (M == 0) return L;
-  if (L.decode && r > 0) {
-    // the decode path's partial planes [S][M][N + r] fp32 are addressed with
-    // 32-bit buffer offsets; shapes whose planes would pass 2 GiB take the
-    // tiled path instead
-    const int64_t S = qlora::decode_splits(M, N, K, r);
-    if (S * M * (N + r) * int64_t{4} >= kMaxTensorBytes) L.decode = false;
-  }
   if (L.decode) {
-    // with an adapter: fp32 sums of x . W'^T and k-split partials of
-    // x . A^T, [S][M][N + r]; without one the decode path needs none
+    // with an adapter: the k-split partials of x . A^T, [S][M][r] fp32 (at
+    // most 16 x 32 x 256 floats, far inside the 32-bit offsets the kernel
+    // uses); without one the decode path needs none
     L.dsplits = qlora::decode_splits(M, N, K, r);
     L.part_off = 0;
-    L.total = round_up((size_t)L.dsplits * M * (N + r) * sizeof(float), 256);
+    L.total = round_up((size_t)L.dsplits * M * r * sizeof(float), 256);
     return L;
   }
   size_t off = 0;

@@ -37,15 +37,16 @@
 //    lie beyond x, which returns zeros);
 //  * the 8 waves' partial tiles are added in LDS in wave order.
 //
-// The adapter's down projection x . A^T rides along: rows of A (bf16, used
-// as they are) form extra 32-row tiles, split over k into short pieces
-// (their partial sums land in columns N .. N+r-1 of part[z]).  Those tiles
-// come last in the grid and fill in as the weight tiles finish.  With an adapter, the weight tiles write their fp32 sums to part[0]
-// and decode_reduce forms the fp32 adapter term (alpha/r) . (x . A^T) . B^T
-// and rounds y to bf16 once; without one, the weight tiles round and store
-// y themselves.
+// The adapter's down projection x . A^T runs first, as a launch of the same
+// kernel with only A tiles: rows of A (bf16, used as they are) form 32-row
+// tiles, split over k into short pieces whose fp32 partial sums land in
+// part[z][m][j].  The weight tiles then add the adapter term in their
+// epilogue: xa = sum_z part[z] (split order), (alpha/r) . xa . B^T for the
+// tile's 32 rows in fp32, and y is rounded to bf16 once.  Without an
+// adapter only the weight launch runs.
 //
-// Grid: 1-D over the weight tiles, then (A tiles x SA splits).
+// Grid: 1-D over the weight tiles (or, in the first launch, over the A
+// tiles x SA splits).
 
 #include <type_traits>
 
@@ -74,6 +75,8 @@ constexpr int kXq = 8;  // x pieces each lane stages (bounds M K / 64 by 64 kXq)
 constexpr int kXdTok = 16;
 constexpr int kXdStage = kXdTok * 256;
 constexpr int kXdBytes = WAVES * 2 * kXdStage;
+// at most this many k splits of the A tiles (partial planes of x . A^T)
+constexpr int kMaxASplits = 16;
 
 // s_waitcnt immediate: wait until at most `vm` vector-memory and `lgkm` LDS
 // operations of this wave are outstanding (expcnt left free).
@@ -88,10 +91,12 @@ struct DecodeParams {
   const float* dq_mean;  // the mean-centred scale format's mean (or null)
   const uint16_t* x;
   const uint16_t* A;
-  float* part;
+  const uint16_t* B;
+  float* part;         // x . A^T partials [sa][M][r] fp32 (the A tiles' output)
   int64_t M, N, K;
   int r;
-  uint16_t* y;         // bf16 output when r == 0 (no adapter term to add)
+  float scale;         // alpha / r
+  uint16_t* y;         // bf16 output of the weight tiles
   int sa;              // k splits of the A tiles
   int64_t w_blocks;    // weight tiles (they come first)
   int64_t blocks;      // w_blocks + A tiles x sa
@@ -124,11 +129,10 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
   constexpr int kLdsBytes = kTabBytes + ring_bytes(NST);
   __shared__ __align__(16) uint8_t lds[kLdsBytes + (XL ? kXBytes : XD ? kXdBytes : 0)];
 
-  // Weight tiles take the first ids, A tiles the last: workgroups are
-  // dispatched in id order, so the A tiles fill in as weight tiles finish
-  // instead of holding CUs the weight tiles need.  Among the weight tiles,
-  // ids are turned into ranks contiguous within an XCD (ids are dealt to
-  // the 8 XCDs round-robin), so neighbouring row tiles share an L2.
+  // Weight tiles take the first ids, A tiles the rest (a launch holds one
+  // kind or the other).  Among the weight tiles, ids are turned into ranks
+  // contiguous within an XCD (ids are dealt to the 8 XCDs round-robin), so
+  // neighbouring row tiles share an L2.
   const int64_t id = blockIdx.x;
   if (id >= p.blocks) return;
   const bool a_tile = id >= p.w_blocks;
@@ -552,146 +556,104 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
       red[(wave * 32 + 8 * (v >> 2) + 4 * lg + (v & 3)) * mcols + lr] = acc[v];
   }
   __syncthreads();
-  const int64_t col0 = a_tile ? N + n0 : n0;
-  const int64_t ldp = N + p.r;
-  for (int e = t; e < 32 * mcols; e += WAVES * 64) {
-    const int m = e >> 5, row = e & 31;  // consecutive threads: consecutive columns
-    if (n0 + row < nrows) {
-      float s = 0.0f;
+  // (token m, row) pairs of the tile: consecutive threads, consecutive rows
+  constexpr int kPairs = 32 * kDecodeMaxM / (WAVES * 64);
+  float sum[kPairs];
 #pragma unroll
-      for (int w = 0; w < WAVES; ++w) s += red[(w * 32 + row) * mcols + m];
-      if (p.y)  // no adapter: this is y
-        p.y[(int64_t)m * N + n0 + row] = __builtin_bit_cast(uint16_t, (__bf16)s);
-      else
-        p.part[((int64_t)z * M + m) * ldp + col0 + row] = s;
+  for (int i = 0; i < kPairs; ++i) {
+    const int e = t + WAVES * 64 * i, m = e >> 5, row = e & 31;
+    sum[i] = 0.0f;
+    if (e < 32 * mcols) {
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) sum[i] += red[(w * 32 + row) * mcols + m];
     }
   }
-}
-
-// y[m][n] = bf16( part[0][m][n] + scale * sum_j xa[m][j] B[n][j] ) with
-// xa[m][j] = sum_z part[z][m][N + j] (z < sa), fixed summation orders.
-// The r-sum is a small matrix product, so it runs on MFMA like the fused
-// GEMMs' adapter columns: xa is split into bf16 hi + lo (hi + lo equals the
-// fp32 value to 2^-17), tokens as the 32 A rows, and B's rows -- 16-byte
-// pieces along j, as stored -- as the B columns.  Block of 256 threads, 128
-// columns n (32 per wave); the block first forms xa's hi/lo rows in LDS
-// (every block does: xa is M x r), with all of a pass's loads issued before
-// any is used.  Each lane's B pieces and base sums are loaded at the start,
-// so their latency overlaps that phase.  Loads go through buffer
-// descriptors (out-of-range offsets read zero), so no branch separates them.
-constexpr int kMaxASplits = 16;
-constexpr int kRedCols = 128;                   // columns per block
-constexpr int kXsRow = 256 + 8;  // LDS row of xa's hi or lo (bf16): r <= 256 + 16 bytes of pad
-__global__ __launch_bounds__(256) void decode_reduce_kernel(const float* __restrict__ part,
-                                                            int sa,
-                                                            const uint16_t* __restrict__ B,
-                                                            int r, float scale,
-                                                            uint16_t* __restrict__ y, int64_t M,
-                                                            int64_t N) {
-  __shared__ __align__(16) uint16_t xs[2][kDecodeMaxM][kXsRow];
-  const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63, lr = lane & 31, lg = lane >> 5;
-  const int64_t ldp = N + r;
-  const int64_t n = (int64_t)blockIdx.x * kRedCols + 32 * wave + lr;  // this lane's column
-  const bool n_ok = n < N;
-  const int ks = (r + 15) / 16;                   // 16-wide MFMA steps over j
-  constexpr uint32_t kOut = 0x80000000u;          // past both tensors
-  const __amdgpu_buffer_rsrc_t pres =
-      make_rsrc(part, (uint32_t)((int64_t)sa * M * ldp * 4));
-  const __amdgpu_buffer_rsrc_t bres = make_rsrc(B, (uint32_t)(N * r * 2));
-
-  // B operand of step s: B[n][16 s + 8 lg .. + 7]
-  constexpr int kMaxSteps = 256 / 16;  // r <= 256
-  u32x4_t bop[kMaxSteps];
+  if (a_tile) {  // this split's partial of x . A^T, rows n0 .. n0 + 31 of A
 #pragma unroll
-  for (int s2 = 0; s2 < kMaxSteps; ++s2) {
-    const int j = 16 * s2 + 8 * lg;
-    bop[s2] = buffer_load16(bres, (n_ok && j < r) ? (uint32_t)((n * r + j) * 2) : kOut);
+    for (int i = 0; i < kPairs; ++i) {
+      const int e = t + WAVES * 64 * i, m = e >> 5, row = e & 31;
+      if (e < 32 * mcols && n0 + row < nrows)
+        p.part[((int64_t)z * M + m) * p.r + n0 + row] = sum[i];
+    }
+    return;
   }
-  // base sums of the tokens this lane's accumulators hold:
-  // rows 8 (v / 4) + 4 lg + v % 4 of the 32 x 32 tile
-  float base[16];
+  const int r = p.r;
+  if (r == 0) {  // no adapter: the sums are y
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t m = 8 * (v >> 2) + 4 * lg + (v & 3);
-    base[v] = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(
-                   pres, (n_ok && m < M) ? (int)((m * ldp + n) * 4) : (int)kOut, 0, 0));
+    for (int i = 0; i < kPairs; ++i) {
+      const int e = t + WAVES * 64 * i, m = e >> 5, row = e & 31;
+      if (e < 32 * mcols && n0 + row < N)
+        p.y[(int64_t)m * N + n0 + row] = __builtin_bit_cast(uint16_t, (__bf16)sum[i]);
+    }
+    return;
   }
-
-  // xa's hi/lo rows for tokens < M (j < 16 ks; zero past r), 4 per thread per pass
-  constexpr int EPT = 4;
-  const int cols = 16 * ks;
-  const int total = (int)M * cols;
-  for (int e0 = t; e0 < total; e0 += 256 * EPT) {
+  // The adapter term: y = bf16(sum + scale . sum_j xa[m][j] B[n][j]), with
+  // xa[m][j] = sum_z part[z][m][j] added in split order (the A tiles ran
+  // before this launch).  xa [M][r] fp32 and the tile's 32 rows of B (bf16,
+  // rows padded by 4 bytes against bank conflicts) replace the wave sums in
+  // LDS; the r-sum runs in fp32 on the vector units (32 M r multiply-adds
+  // per block).  Loads go through buffer descriptors, so splits past sa
+  // and rows past N read zero and need no branch.
+  __syncthreads();  // every thread has read its wave sums
+  static_assert(kDecodeMaxM * 256 * 4 <= 32 * 1024, "xa [M][r] fits below B's rows");
+  static_assert(32 * 1024 + 32 * (256 + 2) * 2 <= kTabBytes + ring_bytes(NSTAGE_XL),
+                "B's rows fit in the smallest variant's LDS");
+  float* xs = red;
+  uint16_t* bs = reinterpret_cast<uint16_t*>(lds + 32 * 1024);
+  const int brow = r + 2;
+  const int64_t nxa = M * r;
+  const __amdgpu_buffer_rsrc_t pres = make_rsrc(p.part, (uint32_t)(p.sa * nxa * 4));
+  const __amdgpu_buffer_rsrc_t bres = make_rsrc(p.B, (uint32_t)(N * r * 2));
+  constexpr int EPT = 2;
+  for (int64_t e0 = t; e0 < nxa; e0 += WAVES * 64 * EPT) {
     float v[EPT][kMaxASplits];
 #pragma unroll
-    for (int u = 0; u < EPT; ++u) {
-      const int e = e0 + 256 * u;
-      const int m = e / cols, j = e - m * cols;
-      const uint32_t off = (uint32_t)(((int64_t)m * ldp + N + j) * 4);
+    for (int u = 0; u < EPT; ++u)
 #pragma unroll
-      for (int z = 0; z < kMaxASplits; ++z) {
-        const bool ok = e < total && j < r && z < sa;
-        v[u][z] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(
-                       pres, ok ? (int)(off + (uint32_t)((int64_t)z * M * ldp * 4)) : (int)kOut,
-                       0, 0));
+      for (int zz = 0; zz < kMaxASplits; ++zz) {
+        const int64_t e = e0 + WAVES * 64 * u;
+        const uint32_t off = e < nxa ? (uint32_t)((zz * nxa + e) * 4) : 0x80000000u;
+        v[u][zz] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(pres, off, 0, 0));
       }
-    }
 #pragma unroll
     for (int u = 0; u < EPT; ++u) {
-      const int e = e0 + 256 * u;
-      float acc = v[u][0];
+      const int64_t e = e0 + WAVES * 64 * u;
+      float a = v[u][0];
 #pragma unroll
-      for (int z = 1; z < kMaxASplits; ++z)
-        if (z < sa) acc += v[u][z];
-      if (e < total) {
-        const int m = e / cols, j = e - m * cols;
-        const uint16_t hi = __builtin_bit_cast(uint16_t, (__bf16)acc);
-        const uint16_t lo = __builtin_bit_cast(uint16_t, (__bf16)(acc - bf16_bits_to_f32(hi)));
-        xs[0][m][j] = hi;
-        xs[1][m][j] = lo;
-      }
+      for (int zz = 1; zz < kMaxASplits; ++zz) a += v[u][zz];
+      if (e < nxa) xs[e] = a;
     }
   }
-  // token rows past M are zero
-  for (int e = (int)M * cols + t; e < kDecodeMaxM * cols; e += 256) {
-    const int m = e / cols, j = e - m * cols;
-    xs[0][m][j] = 0;
-    xs[1][m][j] = 0;
+  for (int e = t; e < 16 * r; e += WAVES * 64) {  // 32 rows x r bf16 as 2-element words
+    const int row = e / (r / 2), jj = 2 * (e - row * (r / 2));
+    const uint32_t off = (uint32_t)(((n0 + row) * r + jj) * 2);
+    const uint32_t w2 = __builtin_amdgcn_raw_buffer_load_b32(bres, off, 0, 0);
+    *reinterpret_cast<uint32_t*>(bs + row * brow + jj) = w2;
   }
   __syncthreads();
-
-  // D[token][n] = sum_j xa[token][j] B[n][j]: A = xa rows (lane: token lr,
-  // j = 16 s + 8 lg ..), B = this lane's B pieces; hi, then lo, per step
-  f32x16_t acc;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-#pragma unroll
-  for (int s2 = 0; s2 < kMaxSteps; ++s2) {
-    if (s2 < ks) {
-      const u32x4_t ahi = *reinterpret_cast<const u32x4_t*>(&xs[0][lr][16 * s2 + 8 * lg]);
-      const u32x4_t alo = *reinterpret_cast<const u32x4_t*>(&xs[1][lr][16 * s2 + 8 * lg]);
-      acc = mfma32x32x16(ahi, bop[s2], acc);
-      acc = mfma32x32x16(alo, bop[s2], acc);
-    }
-  }
-  if (n_ok) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t m = 8 * (v >> 2) + 4 * lg + (v & 3);
-      if (m < M)
-        y[m * N + n] = __builtin_bit_cast(uint16_t, (__bf16)(base[v] + scale * acc[v]));
+  for (int i = 0; i < kPairs; ++i) {
+    const int e = t + WAVES * 64 * i, m = e >> 5, row = e & 31;
+    if (e < 32 * mcols && n0 + row < N) {
+      const float* xm = xs + m * r;
+      const uint16_t* bn = bs + row * brow;
+      float a = 0.0f;
+      for (int j = 0; j < r; j += 2) {
+        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(bn + j);
+        a = fmaf(xm[j], bf16_bits_to_f32(w2 & 0xFFFFu), a);
+        a = fmaf(xm[j + 1], bf16_bits_to_f32(w2 >> 16), a);
+      }
+      p.y[(int64_t)m * N + n0 + row] =
+          __builtin_bit_cast(uint16_t, (__bf16)(sum[i] + p.scale * a));
     }
   }
 }
 
 namespace {
 
-// k splits of the adapter's A tiles, which run after the weight tiles as
-// CUs free up: pieces of about 512 k (at most 16, the planes the reduction
-// reads), so each takes about one memory round trip
+// k splits of the adapter's A tiles, which run in a launch of their own
+// before the weight tiles: pieces of about 512 k (at most 16, the planes the
+// weight tiles' epilogue adds), so each takes about one memory round trip
 int a_splits(int64_t K) {
   int64_t s = K / 512;
   if (s > kMaxASplits) s = kMaxASplits;
@@ -727,18 +689,31 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
   p.dq_mean = dq_mean;
   p.x = x;
   p.A = A;
+  p.B = B;
   p.part = part;
   p.M = M;
   p.N = N;
   p.K = K;
   p.r = r;
+  p.scale = scale;
+  p.y = y;
   p.sa = r > 0 ? a_splits(K) : 1;
   if (r > 0 && (p.sa > splits || part == nullptr)) return hipErrorInvalidValue;
-  p.y = r > 0 ? nullptr : y;
-  p.w_blocks = (N + 31) / 32;
-  p.blocks = p.w_blocks + (r > 0 ? (int64_t)((r + 31) / 32) * p.sa : 0);
   p.L = L;
-  const dim3 grid((unsigned)p.blocks), block(WAVES * 64);
+  const dim3 block(WAVES * 64);
+  if (r > 0) {
+    // the A tiles alone: x . A^T partials for the weight tiles' epilogue
+    DecodeParams pa = p;
+    pa.w_blocks = 0;
+    pa.blocks = (int64_t)((r + 31) / 32) * p.sa;
+    hipLaunchKernelGGL((decode_main_kernel<0, false>), dim3((unsigned)pa.blocks), block, 0, s,
+                       pa);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  p.w_blocks = (N + 31) / 32;
+  p.blocks = p.w_blocks;
+  const dim3 grid((unsigned)p.blocks);
   const int xm = decode_x_in_lds(M, K) ? 1 : (M <= kXdTok ? 2 : 0);
   if (dq_mean) {
     if (xm == 1)
@@ -755,10 +730,6 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
     else
       hipLaunchKernelGGL((decode_main_kernel<0, false>), grid, block, 0, s, p);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || r == 0) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((N + kRedCols - 1) / kRedCols)),
-                     dim3(256), 0, s, part, p.sa, B, r, scale, y, M, N);
   return hipGetLastError();
 }
 

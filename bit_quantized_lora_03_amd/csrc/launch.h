@@ -141,10 +141,10 @@ hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M,
                               uint16_t* out, hipStream_t s, bool f16 = false);
 
 // gemm_decode.hip -- forward for M <= 32.  Without an adapter one kernel
-// writes y.  With one, the weight tiles write fp32 sums to part[0][M][N + r]
-// and the k-split A tiles x . A^T to part[z][m][N + j], then
-// y = bf16(part[0] + scale . (sum_z xa) . B^T); decode_splits is the number
-// of partial planes (0: none).
+// writes y.  With one, a first launch of k-split A tiles writes the
+// partials of x . A^T to part[z][m][j] ([S][M][r] fp32), then the weight
+// tiles write y = bf16(x . W'^T + scale . (sum_z part[z]) . B^T);
+// decode_splits is the number of partial planes S (0: none).
 constexpr int kDecodeMaxM = 32;
 int decode_splits(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const float* step,

@@ -75,9 +75,10 @@ def test_workspace_sizes():
     b = ws(1, 512, 4096, 4096, 16)
     assert f > 0 and b > 0 and f % 256 == 0 and b % 256 == 0
     assert f >= 512 * 32 * 2 + ws(0, 512, 4096, 4096, 0)   # + the hi/lo split of x.A^T
-    # few tokens: the decode path keeps k-split partials of x.W'^T and x.A^T
+    # few tokens: the decode path keeps only the k-split partials of x.A^T,
+    # [16 splits][M][r] fp32 at K = 8192
     d = ws(0, 16, 8192, 8192, 64)
-    assert d >= 16 * (8192 + 64) * 4 and d % 256 == 0
+    assert d == 16 * 16 * 64 * 4
     # ... and without an adapter the decode kernel writes y itself
     assert ws(0, 16, 8192, 8192, 0) == 0
     assert ws(0, 16, 100, 4096, 16) == 0          # N % 64
@@ -403,16 +404,17 @@ def test_adapter_buffers_above_2gib_are_rejected():
     assert bwd(big_n, 0, 256) == -2
 
 
-def test_decode_partials_above_2gib_take_the_tiled_path():
-    """The few-token path keeps fp32 partial planes [S][M][N + r] that its
-    kernels address with 32-bit offsets; where they would reach 2 GiB the
-    forward takes the tiled GEMM (the dropout forward's layout) instead."""
+def test_decode_partials_stay_small_at_any_output_width():
+    """The few-token path's workspace holds only the k-split partials of
+    x . A^T, [S][M][r] fp32 (S <= 16), whatever N is: even an output of 2^24
+    columns keeps the decode path and its small layout, not the tiled GEMM's
+    (the dropout forward's layout)."""
     ws = q.workspace_bytes
-    N = 1 << 24                          # 32 * 2^24 * 4 = 2 GiB of partials
-    assert ws(0, 32, N, 64, 8) == ws(4, 32, N, 64, 8)
-    # a small shape still takes the decode path (its own, smaller layout)
-    assert ws(0, 32, 4096, 4096, 8) != ws(4, 32, 4096, 4096, 8)
-
+    N = 1 << 24
+    assert ws(0, 32, N, 64, 8) == 1 * 32 * 8 * 4      # K = 64: one split
+    assert ws(0, 32, N, 64, 8) != ws(4, 32, N, 64, 8)
+    assert ws(0, 32, 4096, 4096, 8) == 8 * 32 * 8 * 4  # K = 4096: 8 splits of 512
+    assert ws(0, 32, 4096, 8192, 256) == 16 * 32 * 256 * 4
 
 def test_noalloc_forward_validation():
     """qlora_linear_fwd_noalloc validates like qlora_linear_fwd, and rejects a
