@@ -124,7 +124,7 @@ struct FwdWs {
   size_t gpart;  // fp32 partials of the fused GEMM's schedule (0: none)
   bool decode;   // few tokens: split-K decode path
 };
-// decode: the few-token decode path may run (NF4 weight, bf16, no dropout);
+// decode: the few-token decode path may run (NF4 weight, bf16 compute);
 // nf4w: the weight is the NF4 one (the fused GEMM may then take its narrow
 // tile, which sizes the partials differently)
 FwdWs fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool decode = true,
@@ -257,8 +257,9 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
     if (!aligned16(x) || !aligned16(y) || (r > 0 && (!aligned16(A) || !aligned16(B))) ||
         (keep && !aligned16(keep)))
       return QLORA_EALIGN;
-    // the few-token decode kernel has no dropout: the tiled path then runs
-    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !keep && !drop && !f16, w->nf4());
+    // the few-token decode kernel computes in bf16 only: with fp16 the
+    // tiled path runs
+    const FwdWs ws = fwd_layout(M, N, K, r, w->nf4() && !f16, w->nf4());
     const size_t ny = (size_t)M * N * 2;
     if (overlap(y, ny, x, (size_t)M * K * 2) || overlap(y, ny, w->data(), w->bytes()) ||
         (r > 0 && (overlap(y, ny, A, (size_t)r * K * 2) || overlap(y, ny, B, (size_t)N * r * 2))) ||
@@ -286,7 +287,7 @@ int fwd_impl(const Wref* w, const uint16_t* x, int64_t M, const uint16_t* A, con
       return hip_status(qlora::launch_decode_fwd(
           w->codes, w->qscale, w->step, w->mean, x, A, B, r, scale,
           ws.total > 0 ? at<float>(workspace, ws.part_off) : nullptr, ws.dsplits, y, M, N, K, L,
-          s));
+          s, keep, drop));
     }
     uint16_t* xs = nullptr;
     if (r > 0) {
@@ -477,9 +478,10 @@ size_t qlora_linear_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
   if (op == 1) return bwd_layout(M, N, K, r).total;
   if (op == 3) return bwd_layout(M, N, K, r, false).total;
   if (op == 2) return fwd_layout(M, N, K, r, false, false).total;
-  if (op == 4 || op == 6) return fwd_layout(M, N, K, r, false, true).total;
+  if (op == 4) return fwd_layout(M, N, K, r, true, true).total;
+  if (op == 6) return fwd_layout(M, N, K, r, false, true).total;
   if (op == 5 || op == 7) return bwd_layout(M, N, K, r).total;
-  if (op == 8) return fwd_layout(M, N, K, r, false, true).total;
+  if (op == 8) return fwd_layout(M, N, K, r, true, true).total;
   if (op == 9) return bwd_layout(M, N, K, r, true, true).total;
   return 0;
 }

@@ -188,6 +188,19 @@ __device__ __forceinline__ u32x4_t philox4x32_10(u32x4_t x, uint32_t k0, uint32_
   return x;
 }
 
+// LoRA dropout: the 8 bf16 of a 16-byte chunk (consecutive k, value i in
+// halfword i) keep their bits where bit i of the chunk's keep byte is set
+// and become +0 where it is clear.
+__device__ __forceinline__ u32x4_t keep8(const u32x4_t v, uint32_t kb) {
+  u32x4_t o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t b = kb >> (2 * d);
+    o[d] = v[d] & (((b & 1u) ? 0x0000FFFFu : 0u) | ((b & 2u) ? 0xFFFF0000u : 0u));
+  }
+  return o;
+}
+
 // The keep byte of mask byte `chunk` (bit j set where element 8 chunk + j
 // of the flattened [M, K] activation is kept).
 __device__ __forceinline__ uint32_t philox_keep_byte(const PhiloxDrop& d, uint32_t chunk) {

@@ -98,6 +98,9 @@ struct DecodeParams {
   float scale;         // alpha / r
   uint16_t* y;         // bf16 output of the weight tiles
   int sa;              // k splits of the A tiles
+  const uint8_t* keep; // LoRA dropout keep mask [M, K / 8] on x . A^T's x (or null)
+  PhiloxDrop drop;     // ... or keep bits drawn from Philox4x32-10 (rng != 0)
+  int rng;
   int64_t w_blocks;    // weight tiles (they come first)
   int64_t blocks;      // w_blocks + A tiles x sa
   Nf4Levels L;
@@ -537,6 +540,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_main_kernel(DecodeParams p)
 #pragma unroll
       for (int j = 0; j < 8; ++j) xb[j] = zero;
       load_x(kb < K ? kb : 0, xb);
+      if (p.keep || p.rng) {
+        // LoRA dropout on the adapter's input: piece j of the lane's token
+        // row is mask byte (m, k / 8) with k = kb + 8 j (lanes past the M
+        // tokens read token 0's row and bytes; their columns are never
+        // stored)
+        const uint32_t c0 = (uint32_t)((tok_ok ? lr : 0) * (K / 8) + (kb < K ? kb : 0) / 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t kbyte = p.rng ? philox_keep_byte(p.drop, c0 + (uint32_t)j)
+                                       : (uint32_t)p.keep[c0 + j];
+          xb[j] = keep8(xb[j], kbyte);
+        }
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         av[j] = ok ? *reinterpret_cast<const u32x4_t*>(arow + kb + 8 * j) : zero;
@@ -681,8 +697,12 @@ hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const 
                              const float* dq_mean, const uint16_t* x, const uint16_t* A,
                              const uint16_t* B, int r,
                              float scale, float* part, int splits, uint16_t* y, int64_t M,
-                             int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s) {
+                             int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s,
+                             const uint8_t* keep, const PhiloxDrop* drop) {
   DecodeParams p;
+  p.keep = keep;
+  p.drop = drop ? *drop : PhiloxDrop{};
+  p.rng = drop != nullptr;
   p.codes = codes;
   p.qscale = qscale;
   p.step = step;

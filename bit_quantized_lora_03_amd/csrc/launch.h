@@ -144,14 +144,16 @@ hipError_t launch_gemm_reduce(const GemmConfig& c, const float* part, int64_t M,
 // writes y.  With one, a first launch of k-split A tiles writes the
 // partials of x . A^T to part[z][m][j] ([S][M][r] fp32), then the weight
 // tiles write y = bf16(x . W'^T + scale . (sum_z part[z]) . B^T);
-// decode_splits is the number of partial planes S (0: none).
+// decode_splits is the number of partial planes S (0: none).  keep or drop
+// (or neither): LoRA dropout on the adapter's input, as in lora_proj.
 constexpr int kDecodeMaxM = 32;
 int decode_splits(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_decode_fwd(const uint8_t* codes, const uint8_t* qscale, const float* step,
                              const float* dq_mean, const uint16_t* x, const uint16_t* A,
                              const uint16_t* B, int r,
                              float scale, float* part, int splits, uint16_t* y, int64_t M,
-                             int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s);
+                             int64_t N, int64_t K, const Nf4Levels& L, hipStream_t s,
+                             const uint8_t* keep = nullptr, const PhiloxDrop* drop = nullptr);
 
 // gemm_bwd.hip -- dx = dy . deq(W) + gs . [A ; A]; scheduled by
 // gemm_config(M, K, N) (output M x K, reduction N)

@@ -63,19 +63,6 @@ __device__ __forceinline__ uint32_t ldb8(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 
-// LoRA dropout: the 8 bf16 of a 16-byte chunk (consecutive k, value i in
-// halfword i) keep their bits where bit i of the chunk's keep byte is set
-// and become +0 where it is clear.
-__device__ __forceinline__ u32x4_t keep8(const u32x4_t v, uint32_t kb) {
-  u32x4_t o;
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    const uint32_t b = kb >> (2 * d);
-    o[d] = v[d] & (((b & 1u) ? 0x0000FFFFu : 0u) | ((b & 2u) ? 0xFFFF0000u : 0u));
-  }
-  return o;
-}
-
 // The keep-mask of a job, [rows, cols / 8] bytes, through a descriptor;
 // `all` is ORed into every loaded byte (0xFF: the job has no mask, so
 // every bit reads as kept).

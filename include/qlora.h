@@ -266,10 +266,11 @@ int qlora_linear_bwd_f16(const qlora_nf4_weight* w, const uint16_t* x, const uin
  *        folded into the fp32 scale alpha/r.
  * Other arguments, rounding (y and dx still rounded once), errors and size
  * limits as qlora_linear_fwd / qlora_linear_bwd; keep must not overlap an
- * output (EINVAL).  The forward always runs the tiled GEMMs (no few-token
- * path); its workspace is qlora_linear_workspace_bytes(4, ...), the
- * backward's qlora_linear_workspace_bytes(5, ...).  With r = 0 there is no
- * adapter and keep is ignored.                                             */
+ * output (EINVAL).  The forward takes the same paths as qlora_linear_fwd
+ * (the few-token one for M <= 32); its workspace is
+ * qlora_linear_workspace_bytes(4, ...), the backward's
+ * qlora_linear_workspace_bytes(5, ...).  With r = 0 there is no adapter and
+ * keep is ignored.                                                         */
 int qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, int64_t M,
                              const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                              const uint8_t* keep, float p, uint16_t* y, void* workspace,
@@ -304,7 +305,7 @@ int qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, const
  *   qlora_linear_fwd_dropout_rng / qlora_linear_bwd_dropout_rng: the
  *     layer of qlora_linear_fwd_dropout / qlora_linear_bwd_dropout with
  *     the drawn bits; other arguments, rounding, errors and size limits
- *     alike; the forward always runs the tiled GEMMs; workspace
+ *     alike; the forward takes qlora_linear_fwd's paths; workspace
  *     qlora_linear_workspace_bytes(8 (forward) or 9 (backward), ...); the
  *     backward keeps the drawn mask in its workspace.                     */
 int qlora_dropout_keep_mask(int64_t M, int64_t K, float p, uint64_t seed, uint64_t offset,

@@ -86,9 +86,13 @@ def test_workspace_sizes():
     assert ws(0, 16, 4096, 4096, 12) == 0         # r % 8
     assert ws(0, 16, 4096, 4096, 264) == 0        # r > 256
     assert ws(10, 16, 4096, 4096, 16) == 0        # bad op
-    # fp16 compute type and dropout: the tiled forward at every M (never the
-    # few-token path), both on the NF4 weight, so laid out alike
-    assert ws(6, 16, 8192, 8192, 64) == ws(4, 16, 8192, 8192, 64)
+    # fp16 compute type: the tiled forward at every M (never the few-token
+    # path); dropout (passed or drawn bits): the same paths as the plain
+    # forward, the few-token one included
+    assert ws(6, 16, 8192, 8192, 64) != ws(4, 16, 8192, 8192, 64)
+    assert ws(4, 16, 8192, 8192, 64) == ws(0, 16, 8192, 8192, 64)
+    assert ws(8, 16, 8192, 8192, 64) == ws(0, 16, 8192, 8192, 64)
+    assert ws(4, 512, 4096, 4096, 16) == ws(0, 512, 4096, 4096, 16)
     assert ws(6, 512, 4096, 4096, 16) == ws(0, 512, 4096, 4096, 16)
     assert ws(7, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
     assert ws(5, 512, 4096, 4096, 16) == ws(1, 512, 4096, 4096, 16)
@@ -101,10 +105,10 @@ def test_workspace_sizes():
     for op_b, op_n in ((2, 0), (3, 1)):
         assert ws(op_b, 512, 4096, 4096, 16) >= 4 * P
         assert 2 * P <= ws(op_n, 512, 4096, 4096, 16) < 3 * P
-    # at 16 tokens the NF4 forward's 64 narrow tiles split 4 ways, the bf16
+    # at 16 tokens the NF4 weight's tiled forward (fp16) takes 64 narrow tiles split 4 ways, the bf16
     # weight's 32 tiles of 256 x 256 8 ways
     part = lambda s: s * 16 * 8192 * 4
-    assert ws(4, 16, 8192, 8192, 64) >= part(4) and ws(4, 16, 8192, 8192, 64) < part(8)
+    assert ws(6, 16, 8192, 8192, 64) >= part(4) and ws(6, 16, 8192, 8192, 64) < part(8)
     assert ws(2, 16, 8192, 8192, 64) >= part(8)
 
 
@@ -408,11 +412,11 @@ def test_decode_partials_stay_small_at_any_output_width():
     """The few-token path's workspace holds only the k-split partials of
     x . A^T, [S][M][r] fp32 (S <= 16), whatever N is: even an output of 2^24
     columns keeps the decode path and its small layout, not the tiled GEMM's
-    (the dropout forward's layout)."""
+    (the fp16 forward's layout)."""
     ws = q.workspace_bytes
     N = 1 << 24
     assert ws(0, 32, N, 64, 8) == 1 * 32 * 8 * 4      # K = 64: one split
-    assert ws(0, 32, N, 64, 8) != ws(4, 32, N, 64, 8)
+    assert ws(0, 32, N, 64, 8) != ws(6, 32, N, 64, 8)
     assert ws(0, 32, 4096, 4096, 8) == 8 * 32 * 8 * 4  # K = 4096: 8 splits of 512
     assert ws(0, 32, 4096, 8192, 256) == 16 * 32 * 256 * 4
 

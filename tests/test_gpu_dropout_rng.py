@@ -48,6 +48,8 @@ def test_drawn_mask_is_bit_exact(cuda, M, K, p, seed, offset):
 # store the drawn bytes), the three gradient kernels, ragged tails
 SHAPES = [
     (1, 64, 64, 8, 16.0, 0.05),
+    (16, 512, 4096, 64, 16.0, 0.05),     # few tokens: x by DMA ring, 8 A splits
+    (29, 320, 1024, 32, 64.0, 0.1),      # few tokens: x in registers, ragged M
     (300, 320, 448, 16, 32.0, 0.05),
     (257, 512, 320, 24, 48.0, 0.1),
     (513, 384, 256, 64, 16.0, 0.05),
@@ -130,14 +132,15 @@ def test_drawn_dropout_65b_layer(cuda):
         assert torch.equal(a, b), name
 
 
-def test_no_dropout_limit_equals_the_plain_layer(cuda):
+@pytest.mark.parametrize("M", [16, 300])
+def test_no_dropout_limit_equals_the_plain_layer(cuda, M):
     """p = 0 keeps every element: the drawn forward equals the layer without
-    dropout bit for bit (same tiled kernels, same scale).  The backward's
+    dropout bit for bit (same kernels, same scale).  The backward's
     masked dX kernel adds the adapter rows before the base (so its rounding
     order differs): dX, dA and dB are checked against the oracle without
     dropout."""
     import torch
-    M, N, K, r, alpha = 300, 320, 448, 16, 32.0
+    N, K, r, alpha = 320, 448, 16, 32.0
     L = _layer(M, N, K, r, alpha)
     ol = OracleLayer(L.w)
     pw = ol.to_device()
