@@ -42,14 +42,20 @@ constexpr int RT = 64;  // reduction rows per stage
 constexpr int ROW_CHUNKS = RT / 8;
 // W slab row stride in LDS, bytes: 512 of data plus 64 of pad (144 dwords,
 // 16 mod 64 banks), with the 16-byte pieces of row r XOR-swizzled by
-// (r / 4) mod 4 within each 64-byte window (slab_swz).  A 16-byte store
-// serves 16 lanes (16 rows at one column) per LDS cycle and a transpose
-// read 32 lanes (4 rows x 64 contiguous bytes); with this layout both touch
-// each of the 64 banks once.  (A plain 12-mod-64 stride, conflict-free for
-// the stores, made the four rows of a transpose read overlap by 4 banks:
-// about half the dX kernel's LDS cycles were bank conflicts.)
+// (r / 2) mod 4 within each 64-byte window (slab_swz).  Reads and writes
+// see the banks differently (measured with the LDS bank-conflict counter
+// on the exact access patterns): a transpose read serves 32 lanes (4 rows
+// x 64 contiguous bytes) per cycle across all 64 banks, a 16-byte store
+// 8 lanes (8 rows at one column) per cycle across 32 banks, i.e. banks
+// taken mod 32.  With the 144-dword stride rows r and r + 2 coincide mod
+// 32, so the swizzle has to tell them apart: (r / 2) mod 4 gives the 8
+// rows of a store cycle 8 distinct 16-byte bank groups, and the 4 rows of
+// a transpose read stay in their own 16-bank quarters.  (The former
+// (r / 4) mod 4 swizzle left the stores 2-way conflicted -- half of the dX
+// kernel's LDS cycles were conflict cycles; a plain 12-mod-64 stride,
+// before that, made the four rows of a transpose read overlap.)
 constexpr int WROW = 576;
-__device__ __forceinline__ int slab_swz(int row) { return ((row >> 2) & 3) << 4; }
+__device__ __forceinline__ int slab_swz(int row) { return ((row >> 1) & 3) << 4; }
 
 struct DxParams {
   const uint8_t* codes;   // NF4 weight (WF = kWeightNf4 or kWeightNf4Centred)
@@ -268,7 +274,7 @@ void dx_gemm_kernel(DxParams p) {
   // 16-lane group g points at row 8 (g / 2) + j / 4 (+ 4 for the second
   // read), column 16 (g % 2) + 4 (j % 4).
   // (The swizzle term of a row does not change with kk, as 16 kk is a
-  // multiple of 4 rows, nor with i, which moves by whole 64-byte windows.)
+  // multiple of 8 rows, nor with i, which moves by whole 64-byte windows.)
   const int tg = lane >> 4, tj = lane & 15;
   const int a_row = 8 * (tg >> 1) + (tj >> 2);
   const int a_col = ((KW / 2) * wk + 16 * (tg & 1) + 4 * (tj & 3)) * 2;
